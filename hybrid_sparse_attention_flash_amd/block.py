@@ -1,0 +1,121 @@
+"""Sequencing of the C-ABI calls into hybrid blocks (host logic only).
+
+HySparse block (QbitAI HySparse article, method section): the full layer runs
+causal attention and emits block scores; one top-k per query picks the blocks;
+every sparse layer attends over those blocks of the shared KV and over its own
+128-token window, merged by the sigmoid gate.
+
+HySparse2 block (airebao HySparse2 news, inner KV Reuse / token-level selection /
+forced recent window): the full layer emits per-tile token scores; one top-k
+per 64-query tile picks tokens; every sparse layer attends over them united
+with the recent window, over the one shared KV.
+
+All buffers are allocated once per runner so repeated steps launch kernels
+only.
+"""
+from dataclasses import dataclass
+from typing import List, Optional
+
+import torch
+
+from . import ops
+
+
+class HySparseBlock:
+    """One HySparse hybrid block: 1 full layer + N gated sparse layers."""
+
+    def __init__(self, B, L, Hq, Hkv, D, n_sparse, topk, window=128, block=64, device="cuda",
+                 out_dtype=torch.float32, softmax_scale=None):
+        self.B, self.L, self.Hq, self.Hkv, self.D = B, L, Hq, Hkv, D
+        self.n_sparse, self.topk, self.window, self.block = n_sparse, topk, window, block
+        self.scale = softmax_scale
+        nblk = (L + block - 1) // block
+        f32 = dict(dtype=torch.float32, device=device)
+        self.o_full = torch.empty(B, L, Hq, D, dtype=out_dtype, device=device)
+        self.lse = torch.empty(B, Hq, L, **f32)
+        self.scores = torch.empty(B, L, nblk, **f32)
+        self.idx = torch.empty(B, L, topk, dtype=torch.int32, device=device)
+        self.count = torch.empty(B * L, dtype=torch.int32, device=device)
+        self.o_sp = torch.empty(B, L, Hq, D, **f32)
+        self.lse_sp = torch.empty(B, Hq, L, **f32)
+        self.o_layers = [torch.empty(B, L, Hq, D, dtype=out_dtype, device=device) for _ in range(n_sparse)]
+
+    def full(self, q0, k, v):
+        ops.hys_full_attn_fwd(q0, k, v, self.o_full, self.lse, "block", self.scores, softmax_scale=self.scale)
+
+    def select(self):
+        B, L = self.B, self.L
+        ops.hys_select_topk(self.scores.view(B * L, -1), self.topk, self.idx.view(B * L, self.topk), self.count)
+
+    def sparse_layer(self, l, q, k, v, kw, vw, gate_w):
+        ops.hys_sparse_attn_fwd(q, k, v, self.idx, self.o_sp, self.lse_sp, granularity=self.block,
+                                topk=self.topk, q_tile=1, softmax_scale=self.scale)
+        ops.hys_swa_gate_fwd(q, kw, vw, self.window, self.o_sp, self.lse_sp, gate_w, self.o_layers[l],
+                             softmax_scale=self.scale)
+
+    def run(self, q_layers, k, v, kw_layers, vw_layers, gate_layers):
+        self.full(q_layers[0], k, v)
+        self.select()
+        for l in range(self.n_sparse):
+            self.sparse_layer(l, q_layers[l + 1], k, v, kw_layers[l], vw_layers[l], gate_layers[l])
+        return self
+
+
+class HySparse2Block:
+    """One HySparse2 hybrid block (prefill): 1 full layer + N token-sparse layers."""
+
+    def __init__(self, B, L, Hq, Hkv, D, n_sparse, topk=1024, window=128, tile=64, device="cuda",
+                 out_dtype=torch.float32, softmax_scale=None):
+        self.B, self.L, self.Hq, self.Hkv, self.D = B, L, Hq, Hkv, D
+        self.n_sparse, self.topk, self.window, self.tile = n_sparse, topk, window, tile
+        self.scale = softmax_scale
+        ntile = (L + tile - 1) // tile
+        f32 = dict(dtype=torch.float32, device=device)
+        self.o_full = torch.empty(B, L, Hq, D, dtype=out_dtype, device=device)
+        self.lse = torch.empty(B, Hq, L, **f32)
+        self.scores = torch.empty(B, ntile, L, **f32)
+        self.idx = torch.empty(B, ntile, topk, dtype=torch.int32, device=device)
+        self.count = torch.empty(B * ntile, dtype=torch.int32, device=device)
+        self.lse_sp = torch.empty(B, Hq, L, **f32)
+        self.o_layers = [torch.empty(B, L, Hq, D, dtype=out_dtype, device=device) for _ in range(n_sparse)]
+
+    def full(self, q0, k, v, k_scale=1.0, v_scale=1.0):
+        ops.hys_full_attn_fwd(q0, k, v, self.o_full, self.lse, "tile_token", self.scores,
+                              softmax_scale=self.scale, k_scale=k_scale, v_scale=v_scale)
+
+    def select(self):
+        B, nt = self.B, self.scores.shape[1]
+        ops.hys_select_topk(self.scores.view(B * nt, -1), self.topk, self.idx.view(B * nt, self.topk), self.count)
+
+    def sparse_layer(self, l, q, k, v, k_scale=1.0, v_scale=1.0):
+        ops.hys_sparse_attn_fwd(q, k, v, self.idx, self.o_layers[l], self.lse_sp, granularity=1, topk=self.topk,
+                                q_tile=self.tile, forced_window=self.window, softmax_scale=self.scale,
+                                k_scale=k_scale, v_scale=v_scale)
+
+    def run(self, q_layers, k, v, k_scale=1.0, v_scale=1.0):
+        self.full(q_layers[0], k, v, k_scale, v_scale)
+        self.select()
+        for l in range(self.n_sparse):
+            self.sparse_layer(l, q_layers[l + 1], k, v, k_scale, v_scale)
+        return self
+
+
+class HySparse2Decode:
+    """One HySparse2 decode step (full layer + top-k + N sparse layers) over an fp8 cache."""
+
+    def __init__(self, B, Nmax, Hq, D, n_sparse, topk=1024, window=128, device="cuda", out_dtype=torch.float32,
+                 softmax_scale=None):
+        self.B, self.Nmax, self.Hq, self.D = B, Nmax, Hq, D
+        self.n_sparse, self.topk, self.window = n_sparse, topk, window
+        self.scale = softmax_scale
+        self.o_full = torch.empty(B, 1, Hq, D, dtype=out_dtype, device=device)
+        self.scores = torch.empty(B, Nmax, dtype=torch.float32, device=device)
+        self.idx = torch.empty(B, topk, dtype=torch.int32, device=device)
+        self.o_layers = [torch.empty(B, 1, Hq, D, dtype=out_dtype, device=device) for _ in range(n_sparse)]
+        self.ws = None
+
+    def run(self, q_full, k_cache, v_cache, cache_len, q_sparse, k_scale=1.0, v_scale=1.0):
+        self.ws = ops.hys_decode_step(q_full, k_cache, v_cache, cache_len, self.o_full, self.scores, self.idx,
+                                      q_sparse, self.o_layers, self.topk, self.window, softmax_scale=self.scale,
+                                      k_scale=k_scale, v_scale=v_scale, workspace=self.ws)
+        return self

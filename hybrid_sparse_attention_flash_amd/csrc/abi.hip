@@ -1,0 +1,480 @@
+// C ABI of libhys: argument validation, launch configuration and dispatch.
+// Every check runs on the host before any GPU work; failures return a status
+// and leave a thread-local message (see include/hys.h for the contract).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "../../include/hys.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hys_status fail(hys_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+hys_status ok() {
+  g_last_error.clear();
+  return HYS_OK;
+}
+
+hys_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(HYS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t elem_size(int32_t dt) { return dt == HYS_F32 ? 4 : (dt == HYS_BF16 ? 2 : 1); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape/stride sanity of one [B, T, H, D] tensor.
+hys_status check_tensor(const hys_tensor4& t, const char* name, bool allow_fp8) {
+  if (!t.ptr) return fail(HYS_ERR_INVALID_ARG, "%s: null pointer", name);
+  if (t.dtype != HYS_F32 && t.dtype != HYS_BF16 && t.dtype != HYS_FP8_E4M3)
+    return fail(HYS_ERR_INVALID_ARG, "%s: unknown dtype %d", name, (int)t.dtype);
+  if (t.dtype == HYS_FP8_E4M3 && !allow_fp8) return fail(HYS_ERR_UNSUPPORTED, "%s: fp8 not accepted here", name);
+  for (int i = 0; i < 4; ++i) {
+    if (t.shape[i] < 0) return fail(HYS_ERR_INVALID_ARG, "%s: negative shape[%d]", name, i);
+    if (t.stride[i] < 0) return fail(HYS_ERR_INVALID_ARG, "%s: negative stride[%d]", name, i);
+  }
+  if (t.shape[0] < 1 || t.shape[2] < 1) return fail(HYS_ERR_INVALID_ARG, "%s: batch and heads must be >= 1", name);
+  if (t.shape[3] != 64 && t.shape[3] != 128)
+    return fail(HYS_ERR_UNSUPPORTED, "%s: head dim %lld not in {64, 128}", name, (long long)t.shape[3]);
+  if (t.stride[3] != 1) return fail(HYS_ERR_INVALID_ARG, "%s: head-dim stride must be 1", name);
+  if (t.shape[1] >= (1ll << 30)) return fail(HYS_ERR_UNSUPPORTED, "%s: more than 2^30 tokens", name);
+  const size_t es = elem_size(t.dtype);
+  if (!aligned16(t.ptr)) return fail(HYS_ERR_INVALID_ARG, "%s: pointer not 16-byte aligned", name);
+  for (int i = 0; i < 3; ++i)
+    if (((size_t)t.stride[i] * es) % 16 != 0 && t.shape[i] > 1)
+      return fail(HYS_ERR_INVALID_ARG, "%s: stride[%d] not a multiple of 16 bytes", name, i);
+  return HYS_OK;
+}
+
+hys::ElemType et(int32_t dt) {
+  return dt == HYS_F32 ? hys::ET_F32 : (dt == HYS_BF16 ? hys::ET_BF16 : hys::ET_FP8);
+}
+
+// q [B,L,Hq,D], k/v [B,L,Hkv,D] consistency and type rule
+hys_status check_qkv(const hys_tensor4& q, const hys_tensor4& k, const hys_tensor4& v, bool same_len) {
+  hys_status s;
+  if ((s = check_tensor(q, "q", false)) != HYS_OK) return s;
+  if ((s = check_tensor(k, "k", true)) != HYS_OK) return s;
+  if ((s = check_tensor(v, "v", true)) != HYS_OK) return s;
+  if (k.dtype != v.dtype) return fail(HYS_ERR_INVALID_ARG, "k and v dtypes differ");
+  if (q.dtype == HYS_F32 && k.dtype != HYS_F32) return fail(HYS_ERR_UNSUPPORTED, "fp32 q needs fp32 k/v");
+  if (q.dtype == HYS_BF16 && k.dtype == HYS_F32) return fail(HYS_ERR_UNSUPPORTED, "bf16 q needs bf16 or fp8 k/v");
+  if (k.shape[0] != q.shape[0] || v.shape[0] != q.shape[0]) return fail(HYS_ERR_INVALID_ARG, "batch sizes differ");
+  if (k.shape[3] != q.shape[3] || v.shape[3] != q.shape[3]) return fail(HYS_ERR_INVALID_ARG, "head dims differ");
+  if (k.shape[2] != v.shape[2]) return fail(HYS_ERR_INVALID_ARG, "k and v head counts differ");
+  if (k.shape[1] != v.shape[1]) return fail(HYS_ERR_INVALID_ARG, "k and v lengths differ");
+  if (q.shape[2] % k.shape[2] != 0)
+    return fail(HYS_ERR_INVALID_ARG, "query heads (%lld) not a multiple of KV heads (%lld)", (long long)q.shape[2],
+                (long long)k.shape[2]);
+  if (same_len && q.shape[1] != k.shape[1])
+    return fail(HYS_ERR_UNSUPPORTED, "prefill self-attention needs equal query and key lengths");
+  return HYS_OK;
+}
+
+hys_status check_out(const hys_tensor4& o, const hys_tensor4& q, const char* name) {
+  hys_status s;
+  if ((s = check_tensor(o, name, false)) != HYS_OK) return s;
+  for (int i = 0; i < 4; ++i)
+    if (o.shape[i] != q.shape[i]) return fail(HYS_ERR_INVALID_ARG, "%s: shape differs from q", name);
+  return HYS_OK;
+}
+
+hys::AttnArgs base_args(const hys_attn_params* p, const hys_tensor4& q, const hys_tensor4& k, const hys_tensor4& v,
+                        const hys_tensor4& o, float* lse) {
+  hys::AttnArgs a{};
+  a.q = q.ptr; a.q_sb = q.stride[0]; a.q_st = q.stride[1]; a.q_sh = q.stride[2];
+  a.k = k.ptr; a.k_sb = k.stride[0]; a.k_st = k.stride[1]; a.k_sh = k.stride[2];
+  a.v = v.ptr; a.v_sb = v.stride[0]; a.v_st = v.stride[1]; a.v_sh = v.stride[2];
+  a.o = o.ptr; a.o_sb = o.stride[0]; a.o_st = o.stride[1]; a.o_sh = o.stride[2];
+  a.o_f32 = o.dtype == HYS_F32 ? 1 : 0;
+  a.lse = lse;
+  a.B = (int)q.shape[0]; a.Lq = (int)q.shape[1]; a.Lk = (int)k.shape[1];
+  a.Hq = (int)q.shape[2]; a.Hkv = (int)k.shape[2]; a.G = a.Hq / a.Hkv;
+  a.logit_scale = p->softmax_scale * p->k_scale;
+  a.scale_log2 = a.logit_scale * 1.4426950408889634f;
+  a.v_scale = p->v_scale;
+  return a;
+}
+
+hys_status check_params(const hys_attn_params* p) {
+  if (!p) return fail(HYS_ERR_INVALID_ARG, "null params");
+  if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.f))
+    return fail(HYS_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (!std::isfinite(p->k_scale) || !(p->k_scale > 0.f) || !std::isfinite(p->v_scale) || !(p->v_scale > 0.f))
+    return fail(HYS_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0");
+  return HYS_OK;
+}
+
+// Launch the top-k kernels; arguments already validated, ws holds topk_workspace_bytes.
+hys_status topk_launch(const float* scores, int64_t rows, int64_t cols, int64_t row_stride, int32_t k, int32_t* idx,
+                       int32_t* count, void* ws, hipStream_t st) {
+  if (rows == 0) return ok();
+  if (k == 0 || cols == 0) {
+    hipError_t e = hipSuccess;
+    if (k > 0) e = hys::launch_fill_i32(idx, -1, rows * (int64_t)k, st);
+    if (e == hipSuccess && count) e = hys::launch_fill_i32(count, 0, rows, st);
+    return hip_status(e, "empty top-k fill");
+  }
+  hys::TopkArgs a{};
+  a.scores = scores; a.rows = rows; a.cols = cols; a.row_stride = row_stride; a.k = k;
+  a.idx = idx; a.count = count;
+  if (cols > 65536) {
+    const int64_t nchunk = (cols + 65535) / 65536;
+    a.cand_idx = (int32_t*)ws;
+    a.cand_val = (float*)((char*)ws + (size_t)(rows * nchunk * k) * sizeof(int32_t));
+    a.nchunk = (int)nchunk; a.chunk_cols = 65536;
+  }
+  return hip_status(hys::launch_topk(a, st), "top-k launch");
+}
+
+int env_int(const char* name, int dflt) {
+  const char* e = std::getenv(name);
+  if (!e || !*e) return dflt;
+  return std::atoi(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hys_last_error(void) { return g_last_error.c_str(); }
+
+const char* hys_status_string(hys_status s) {
+  switch (s) {
+    case HYS_OK: return "HYS_OK";
+    case HYS_ERR_INVALID_ARG: return "HYS_ERR_INVALID_ARG";
+    case HYS_ERR_UNSUPPORTED: return "HYS_ERR_UNSUPPORTED";
+    case HYS_ERR_WORKSPACE: return "HYS_ERR_WORKSPACE";
+    case HYS_ERR_HIP: return "HYS_ERR_HIP";
+    case HYS_ERR_INTERNAL: return "HYS_ERR_INTERNAL";
+  }
+  return "HYS_ERR_UNKNOWN";
+}
+
+int hys_abi_version(void) { return HYS_ABI_VERSION; }
+
+// ---------------------------------------------------------------------------
+hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v, hys_tensor4 o,
+                             float* lse, const hys_score_params* sp, float* scores, void* ws, size_t* ws_bytes,
+                             void* stream) {
+  try {
+    hys_status s;
+    if ((s = check_params(p)) != HYS_OK) return s;
+    if ((s = check_qkv(q, k, v, true)) != HYS_OK) return s;
+    if ((s = check_out(o, q, "o")) != HYS_OK) return s;
+    if (!ws_bytes) return fail(HYS_ERR_INVALID_ARG, "ws_bytes must not be null");
+    const int mode_in = sp ? sp->mode : HYS_SCORE_NONE;
+    if (mode_in != HYS_SCORE_NONE && mode_in != HYS_SCORE_BLOCK && mode_in != HYS_SCORE_TILE_TOKEN)
+      return fail(HYS_ERR_INVALID_ARG, "unknown score mode %d", mode_in);
+    if (mode_in != HYS_SCORE_NONE) {
+      if (sp->size != 64) return fail(HYS_ERR_UNSUPPORTED, "score size must be 64 (got %d)", sp->size);
+      if (!scores) return fail(HYS_ERR_INVALID_ARG, "scores must not be null when a score mode is set");
+    }
+    const int64_t B = q.shape[0], L = q.shape[1], Hq = q.shape[2], Hkv = k.shape[2], D = q.shape[3];
+    const int64_t G = Hq / Hkv;
+    if (G > 256 && mode_in != HYS_SCORE_TILE_TOKEN)
+      return fail(HYS_ERR_UNSUPPORTED, "more than 256 query heads per KV head");
+    const int64_t nblk = (L + 63) / 64;
+    size_t need = 0;
+    if (mode_in == HYS_SCORE_BLOCK && Hkv > 1) need = (size_t)(Hkv * B * L * nblk) * sizeof(float);
+    if (!ws) { *ws_bytes = need; return ok(); }
+    if (*ws_bytes < need) return fail(HYS_ERR_WORKSPACE, "workspace %zu < required %zu bytes", *ws_bytes, need);
+    if (need > 0 && !aligned16(ws)) return fail(HYS_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+    if (L == 0) return ok();
+
+    hys::AttnArgs a = base_args(p, q, k, v, o, lse);
+    hipStream_t st = (hipStream_t)stream;
+    int mode, grid;
+    if (mode_in == HYS_SCORE_TILE_TOKEN) {
+      mode = hys::M_FULL_TILE;
+      a.BQ = 64;
+      a.HC = (int)(G < 4 ? G : 4);
+      a.nhc = (int)((G + a.HC - 1) / a.HC);
+      a.ntq = (int)((L + 63) / 64);
+      a.scores = scores; a.sc_sb = (int64_t)a.ntq * L; a.sc_sr = L; a.sc_sg = 0;
+      grid = (int)(B * a.ntq);
+    } else {
+      mode = mode_in == HYS_SCORE_BLOCK ? hys::M_FULL_BLOCK : hys::M_FULL;
+      a.HC = (int)G;
+      a.BQ = (int)(256 / G);
+      a.nhc = 1;
+      a.ntq = (int)((L + a.BQ - 1) / a.BQ);
+      if (mode == hys::M_FULL_BLOCK) {
+        a.nblk = (int)nblk;
+        a.sc_sb = L * nblk; a.sc_sr = nblk;
+        if (Hkv > 1) { a.scores = (float*)ws; a.sc_sg = B * L * nblk; }
+        else { a.scores = scores; a.sc_sg = 0; }
+      }
+      grid = (int)(B * a.ntq * Hkv);
+    }
+    a.grid_used = grid;
+    hipError_t e = hys::launch_attn(mode, et(q.dtype), et(k.dtype), (int)D, a, grid, st);
+    if (e != hipSuccess) return hip_status(e, "full attention launch");
+    if (mode == hys::M_FULL_BLOCK && Hkv > 1) {
+      e = hys::launch_reduce_max((const float*)ws, (int)Hkv, B * L * nblk, scores, B * L * nblk, st);
+      if (e != hipSuccess) return hip_status(e, "score reduction launch");
+    }
+    return ok();
+  } catch (...) {
+    return fail(HYS_ERR_INTERNAL, "internal error");
+  }
+}
+
+// ---------------------------------------------------------------------------
+hys_status hys_select_topk(const float* scores, int64_t rows, int64_t cols, int64_t row_stride, int32_t k,
+                           int32_t* idx, int32_t* count, void* ws, size_t* ws_bytes, void* stream) {
+  try {
+    if (!ws_bytes) return fail(HYS_ERR_INVALID_ARG, "ws_bytes must not be null");
+    if (rows < 0 || cols < 0) return fail(HYS_ERR_INVALID_ARG, "negative rows/cols");
+    if (k < 0) return fail(HYS_ERR_INVALID_ARG, "k must be >= 0");
+    if (k > 4096) return fail(HYS_ERR_UNSUPPORTED, "k > 4096");
+    if (cols >= (1ll << 31)) return fail(HYS_ERR_UNSUPPORTED, "cols >= 2^31");
+    if (rows > 0 && row_stride < cols) return fail(HYS_ERR_INVALID_ARG, "row_stride < cols");
+    if (rows > (1ll << 31) - 1) return fail(HYS_ERR_UNSUPPORTED, "rows >= 2^31");
+    if (cols > 65536 && ((cols + 65535) / 65536) * (int64_t)k > 65536)
+      return fail(HYS_ERR_UNSUPPORTED, "ceil(cols/65536) * k exceeds 65536");
+    const size_t need = hys::topk_workspace_bytes(rows, cols, k);
+    if (!ws) { *ws_bytes = need; return ok(); }
+    if (*ws_bytes < need) return fail(HYS_ERR_WORKSPACE, "workspace %zu < required %zu bytes", *ws_bytes, need);
+    if (rows > 0 && k > 0 && (!idx || (cols > 0 && !scores))) return fail(HYS_ERR_INVALID_ARG, "null scores or idx");
+    if (rows > 0 && k == 0 && count == nullptr) return ok();
+    return topk_launch(scores, rows, cols, row_stride, k, idx, count, ws, (hipStream_t)stream);
+  } catch (...) {
+    return fail(HYS_ERR_INTERNAL, "internal error");
+  }
+}
+
+// ---------------------------------------------------------------------------
+hys_status hys_sparse_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v,
+                               const hys_sparse_params* sp, const int32_t* idx, hys_tensor4 o, float* lse, void* ws,
+                               size_t* ws_bytes, void* stream) {
+  (void)ws;
+  try {
+    hys_status s;
+    if ((s = check_params(p)) != HYS_OK) return s;
+    if ((s = check_qkv(q, k, v, true)) != HYS_OK) return s;
+    if ((s = check_out(o, q, "o")) != HYS_OK) return s;
+    if (!sp) return fail(HYS_ERR_INVALID_ARG, "null sparse params");
+    if (ws_bytes && !ws) { *ws_bytes = 0; return ok(); }
+    if (sp->k < 0) return fail(HYS_ERR_INVALID_ARG, "k must be >= 0");
+    if (sp->k > 0 && !idx) return fail(HYS_ERR_INVALID_ARG, "null idx");
+    if (sp->idx_row_stride < sp->k || sp->idx_batch_stride < 0)
+      return fail(HYS_ERR_INVALID_ARG, "idx strides too small");
+    const int64_t B = q.shape[0], L = q.shape[1], Hq = q.shape[2], Hkv = k.shape[2], D = q.shape[3];
+    const int64_t G = Hq / Hkv;
+    hys::AttnArgs a = base_args(p, q, k, v, o, lse);
+    a.idx = idx; a.idx_sb = sp->idx_batch_stride; a.idx_sr = sp->idx_row_stride; a.topk = sp->k;
+    int mode, grid;
+    if (sp->granularity == 64) {
+      if (sp->q_tile != 1) return fail(HYS_ERR_UNSUPPORTED, "granularity 64 needs q_tile 1");
+      if (sp->forced_window != 0) return fail(HYS_ERR_UNSUPPORTED, "granularity 64 has no forced window");
+      if (sp->k > 64) return fail(HYS_ERR_UNSUPPORTED, "granularity 64 needs k <= 64");
+      if (G > 256) return fail(HYS_ERR_UNSUPPORTED, "more than 256 query heads per KV head");
+      const int64_t nblk = (L + 63) / 64;
+      if (nblk > 16384) return fail(HYS_ERR_UNSUPPORTED, "more than 16384 key blocks");
+      mode = hys::M_SPARSE_BLOCK;
+      a.HC = (int)G;
+      int bq = (int)(256 / G);
+      if (bq > 64) bq = 64;
+      if (sp->k > 0 && bq > 1024 / sp->k) bq = 1024 / sp->k;
+      const int bq_env = env_int("HYS_SPARSE_BQ", 0);       // tuning override
+      if (bq_env > 0 && bq_env < bq) bq = bq_env;
+      if (bq < 1) bq = 1;
+      a.BQ = bq; a.nhc = 1; a.nblk = (int)nblk;
+      a.ntq = (int)((L + a.BQ - 1) / a.BQ);
+      grid = (int)(B * a.ntq * Hkv);
+      if (sp->k == 0) {
+        // empty selection: every row's set is empty
+        a.topk = 0;
+      }
+    } else if (sp->granularity == 1) {
+      if (sp->q_tile != 64) return fail(HYS_ERR_UNSUPPORTED, "granularity 1 needs q_tile 64");
+      if (sp->k > 2048) return fail(HYS_ERR_UNSUPPORTED, "granularity 1 needs k <= 2048");
+      if (sp->forced_window < 0 || sp->forced_window > 1984)
+        return fail(HYS_ERR_UNSUPPORTED, "forced_window must be in [0, 1984]");
+      mode = hys::M_SPARSE_TOKEN;
+      a.BQ = 64;
+      a.HC = (int)(G < 4 ? G : 4);
+      a.nhc = (int)((G + a.HC - 1) / a.HC);
+      a.ntq = (int)((L + 63) / 64);
+      a.window = sp->forced_window;
+      const int64_t tiles = B * a.ntq;
+      grid = (int)(((tiles + 7) / 8) * 8 * (Hkv * a.nhc));
+    } else {
+      return fail(HYS_ERR_UNSUPPORTED, "granularity must be 64 or 1");
+    }
+    if (L == 0) return ok();
+    a.grid_used = grid;
+    return hip_status(hys::launch_attn(mode, et(q.dtype), et(k.dtype), (int)D, a, grid, (hipStream_t)stream),
+                      "sparse attention launch");
+  } catch (...) {
+    return fail(HYS_ERR_INTERNAL, "internal error");
+  }
+}
+
+// ---------------------------------------------------------------------------
+hys_status hys_swa_gate_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k_win, hys_tensor4 v_win,
+                            int32_t window, hys_tensor4 o_sparse, const float* lse_sparse, const float* gate_w,
+                            const float* gate_b, hys_tensor4 o, void* stream) {
+  try {
+    hys_status s;
+    if ((s = check_params(p)) != HYS_OK) return s;
+    if ((s = check_qkv(q, k_win, v_win, true)) != HYS_OK) return s;
+    if (k_win.dtype != q.dtype) return fail(HYS_ERR_UNSUPPORTED, "window K/V must have q's dtype");
+    if ((s = check_out(o, q, "o")) != HYS_OK) return s;
+    if ((s = check_out(o_sparse, q, "o_sparse")) != HYS_OK) return s;
+    if (o_sparse.dtype != HYS_F32) return fail(HYS_ERR_UNSUPPORTED, "o_sparse must be fp32");
+    if (!lse_sparse || !gate_w) return fail(HYS_ERR_INVALID_ARG, "null lse_sparse or gate_w");
+    if (window < 1) return fail(HYS_ERR_INVALID_ARG, "window must be >= 1");
+    const int64_t B = q.shape[0], L = q.shape[1], Hq = q.shape[2], Hkv = k_win.shape[2], D = q.shape[3];
+    const int64_t G = Hq / Hkv;
+    if (G > 256) return fail(HYS_ERR_UNSUPPORTED, "more than 256 query heads per KV head");
+    if (L == 0) return ok();
+    hys::AttnArgs a = base_args(p, q, k_win, v_win, o, nullptr);
+    a.window = window;
+    a.HC = (int)G; a.BQ = (int)(256 / G); a.nhc = 1;
+    a.ntq = (int)((L + a.BQ - 1) / a.BQ);
+    a.o_sp = (const float*)o_sparse.ptr;
+    a.osp_sb = o_sparse.stride[0]; a.osp_st = o_sparse.stride[1]; a.osp_sh = o_sparse.stride[2];
+    a.lse_sp = lse_sparse; a.gate_w = gate_w; a.gate_b = gate_b;
+    const int grid = (int)(B * a.ntq * Hkv);
+    a.grid_used = grid;
+    return hip_status(hys::launch_attn(hys::M_SWA_GATE, et(q.dtype), et(k_win.dtype), (int)D, a, grid,
+                                       (hipStream_t)stream),
+                      "window+gate launch");
+  } catch (...) {
+    return fail(HYS_ERR_INTERNAL, "internal error");
+  }
+}
+
+// ---------------------------------------------------------------------------
+hys_status hys_decode_step(const hys_decode_params* p, hys_tensor4 q_full, hys_tensor4 k_cache, hys_tensor4 v_cache,
+                           const int64_t* cache_len, hys_tensor4 o_full, float* token_scores, int32_t* idx,
+                           int32_t n_sparse, const hys_tensor4* q_sparse, const hys_tensor4* o_sparse, void* ws,
+                           size_t* ws_bytes, void* stream) {
+  try {
+    if (!p) return fail(HYS_ERR_INVALID_ARG, "null params");
+    if (!ws_bytes) return fail(HYS_ERR_INVALID_ARG, "ws_bytes must not be null");
+    hys_attn_params ap{p->softmax_scale, p->k_scale, p->v_scale};
+    hys_status s;
+    if ((s = check_params(&ap)) != HYS_OK) return s;
+    if ((s = check_qkv(q_full, k_cache, v_cache, false)) != HYS_OK) return s;
+    if (q_full.dtype != HYS_BF16) return fail(HYS_ERR_UNSUPPORTED, "decode queries must be bf16");
+    const int64_t B = q_full.shape[0], Hq = q_full.shape[2], D = q_full.shape[3], Nmax = k_cache.shape[1];
+    if (q_full.shape[1] != 1) return fail(HYS_ERR_INVALID_ARG, "decode takes one query token per sequence");
+    if (k_cache.shape[2] != 1) return fail(HYS_ERR_UNSUPPORTED, "decode needs an MQA cache (one KV head)");
+    if (Hq > 64) return fail(HYS_ERR_UNSUPPORTED, "decode supports at most 64 query heads");
+    if (B > hys::kMaxDecodeBatch) return fail(HYS_ERR_UNSUPPORTED, "decode batch > %d", hys::kMaxDecodeBatch);
+    if (n_sparse < 0 || n_sparse > hys::kMaxDecodeLayers)
+      return fail(HYS_ERR_UNSUPPORTED, "n_sparse must be in [0, %d]", hys::kMaxDecodeLayers);
+    if (p->topk < 1 || p->topk > 2048) return fail(HYS_ERR_UNSUPPORTED, "topk must be in [1, 2048]");
+    if (p->window < 0) return fail(HYS_ERR_INVALID_ARG, "window must be >= 0");
+    if (Nmax < 1) return fail(HYS_ERR_INVALID_ARG, "empty cache");
+    if (Nmax > 65536 && ((Nmax + 65535) / 65536) * (int64_t)p->topk > 65536)
+      return fail(HYS_ERR_UNSUPPORTED, "cache too long for top-%d", p->topk);
+    if ((s = check_out(o_full, q_full, "o_full")) != HYS_OK) return s;
+    if (!cache_len || !token_scores || !idx) return fail(HYS_ERR_INVALID_ARG, "null cache_len, token_scores or idx");
+    if (n_sparse > 0 && (!q_sparse || !o_sparse)) return fail(HYS_ERR_INVALID_ARG, "null q_sparse or o_sparse");
+    for (int64_t b = 0; b < B; ++b)
+      if (cache_len[b] < 1 || cache_len[b] > Nmax)
+        return fail(HYS_ERR_INVALID_ARG, "cache_len[%lld] = %lld outside [1, %lld]", (long long)b,
+                    (long long)cache_len[b], (long long)Nmax);
+    for (int l = 0; l < n_sparse; ++l) {
+      if ((s = check_out(q_sparse[l], q_full, "q_sparse")) != HYS_OK) return s;
+      if (q_sparse[l].dtype != HYS_BF16) return fail(HYS_ERR_UNSUPPORTED, "q_sparse must be bf16");
+      if (q_sparse[l].stride[0] != q_sparse[0].stride[0] || q_sparse[l].stride[2] != q_sparse[0].stride[2])
+        return fail(HYS_ERR_UNSUPPORTED, "all q_sparse must share strides");
+      if ((s = check_out(o_sparse[l], q_full, "o_sparse")) != HYS_OK) return s;
+      if (o_sparse[l].dtype != o_sparse[0].dtype || o_sparse[l].stride[0] != o_sparse[0].stride[0] ||
+          o_sparse[l].stride[2] != o_sparse[0].stride[2])
+        return fail(HYS_ERR_UNSUPPORTED, "all o_sparse must share dtype and strides");
+    }
+    const int64_t ntiles = (Nmax + 63) / 64;
+    int nsplit = (int)(256 / B);
+    if (nsplit < 1) nsplit = 1;
+    if ((int64_t)nsplit * 4 > ntiles) nsplit = (int)((ntiles + 3) / 4);
+    const int nsplit_env = env_int("HYS_DECODE_SPLIT", 0);
+    if (nsplit_env > 0) nsplit = nsplit_env;
+    const int nsplit_sp = 4;
+    const size_t part_full = (size_t)(B * nsplit * Hq) * (size_t)(D + 2) * sizeof(float);
+    const size_t part_sp = (size_t)((int64_t)n_sparse * B * nsplit_sp * Hq) * (size_t)(D + 2) * sizeof(float);
+    const size_t tk = hys::topk_workspace_bytes(B, Nmax, p->topk);
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t need = up(part_full) + up(part_sp) + up(tk);
+    if (!ws) { *ws_bytes = need; return ok(); }
+    if (*ws_bytes < need) return fail(HYS_ERR_WORKSPACE, "workspace %zu < required %zu bytes", *ws_bytes, need);
+    if (!aligned16(ws)) return fail(HYS_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+    char* w = (char*)ws;
+    float* pf_o = (float*)w;
+    float* pf_ml = pf_o + (size_t)(B * nsplit * Hq) * D;
+    w += up(part_full);
+    float* ps_o = (float*)w;
+    float* ps_ml = ps_o + (size_t)((int64_t)n_sparse * B * nsplit_sp * Hq) * D;
+    w += up(part_sp);
+    void* tkws = w;
+
+    hipStream_t st = (hipStream_t)stream;
+    const float logit_scale = p->softmax_scale * p->k_scale;
+    hys::DecArgs d{};
+    d.k = k_cache.ptr; d.k_sb = k_cache.stride[0]; d.k_st = k_cache.stride[1];
+    d.v = v_cache.ptr; d.v_sb = v_cache.stride[0]; d.v_st = v_cache.stride[1];
+    for (int64_t b = 0; b < B; ++b) d.lens[b] = (int)cache_len[b];
+    d.B = (int)B; d.Hq = (int)Hq; d.Nmax = (int)Nmax;
+    d.scale_log2 = logit_scale * 1.4426950408889634f; d.logit_scale = logit_scale;
+    // 1. full layer, split over the cache
+    d.q[0] = q_full.ptr; d.q_sb = q_full.stride[0]; d.q_sh = q_full.stride[2];
+    d.nsplit = nsplit; d.nlayer = 1;
+    d.scores = token_scores; d.sc_sb = Nmax;
+    d.part_o = pf_o; d.part_ml = pf_ml;
+    hipError_t e = hys::launch_decode(0, et(k_cache.dtype), (int)D, d, st);
+    if (e != hipSuccess) return hip_status(e, "decode split launch");
+    hys::MergeArgs m{};
+    m.B = (int)B; m.Hq = (int)Hq; m.logit_scale = logit_scale; m.v_scale = p->v_scale;
+    m.scale_log2 = d.scale_log2;
+    m.part_o = pf_o; m.part_ml = pf_ml; m.nsplit = nsplit; m.nlayer = 1;
+    m.o[0] = o_full.ptr; m.o_sb = o_full.stride[0]; m.o_sh = o_full.stride[2]; m.o_f32 = o_full.dtype == HYS_F32;
+    e = hys::launch_decode_merge((int)D, m, st);
+    if (e != hipSuccess) return hip_status(e, "decode merge launch");
+    // 2. selection over the token scores
+    hys_status ts = topk_launch(token_scores, B, Nmax, Nmax, p->topk, idx, nullptr, tkws, st);
+    if (ts != HYS_OK) return ts;
+    // 3. all sparse layers in one launch
+    if (n_sparse > 0) {
+      for (int l = 0; l < n_sparse; ++l) d.q[l] = q_sparse[l].ptr;
+      d.q_sb = q_sparse[0].stride[0]; d.q_sh = q_sparse[0].stride[2];
+      d.nsplit = nsplit_sp; d.nlayer = n_sparse;
+      d.scores = nullptr;
+      d.idx = idx; d.idx_sb = p->topk; d.topk = p->topk; d.window = p->window;
+      d.part_o = ps_o; d.part_ml = ps_ml;
+      e = hys::launch_decode(1, et(k_cache.dtype), (int)D, d, st);
+      if (e != hipSuccess) return hip_status(e, "decode sparse launch");
+      m.part_o = ps_o; m.part_ml = ps_ml; m.nsplit = nsplit_sp; m.nlayer = n_sparse;
+      for (int l = 0; l < n_sparse; ++l) { m.o[l] = o_sparse[l].ptr; m.lse[l] = nullptr; }
+      m.o_sb = o_sparse[0].stride[0]; m.o_sh = o_sparse[0].stride[2]; m.o_f32 = o_sparse[0].dtype == HYS_F32;
+      e = hys::launch_decode_merge((int)D, m, st);
+      if (e != hipSuccess) return hip_status(e, "decode sparse merge launch");
+    }
+    return ok();
+  } catch (...) {
+    return fail(HYS_ERR_INTERNAL, "internal error");
+  }
+}
+
+}  // extern "C"

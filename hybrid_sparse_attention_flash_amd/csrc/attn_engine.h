@@ -1,0 +1,693 @@
+// Tiled MFMA attention engine for the HySparse / HySparse2 prefill path (gfx950).
+//
+// One workgroup = 4 waves = 256 threads.  It owns a "row set": BQ consecutive
+// queries x HC query heads that share one KV head (GQA/MQA), laid out
+// query-major (row r = query r/HC, head r%HC), 32*NB rows per wave.  It walks a
+// sequence of 64-key tiles -- contiguous (causal / window) or gathered (selected
+// blocks / selected tokens) -- staging each tile through LDS:
+//   K   as [64 keys][D]   (row padded), read as MFMA A fragments, and
+//   V^T as [D][64 keys]   (row padded), transposed in registers on the way in,
+// with fp8 e4m3 K/V decoded to bf16 while staging.  The logits are formed
+// transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16, or 32x32x2_f32 for fp32),
+// so each lane holds one row's logits for 32 of the 64 keys and the row
+// softmax needs a single cross-lane exchange; O^T = V^T P^T then consumes the
+// probabilities straight from the logit registers.  Online softmax runs in the
+// base-2 domain on raw dot products; the natural-unit scaled logit is recovered
+// exactly where scores are emitted.
+//
+// Score emission (the full layer's byproduct, TechWalker HySparse write-up,
+// paragraph on the modified FlashAttention kernel): the per-row tile maximum
+// that the online softmax needs anyway is the block maximum when tiles are the
+// 64-key blocks; the max over the query heads of a KV group is taken in LDS.
+// For HySparse2 token scores the per-key maximum over a tile's rows is reduced
+// across lanes and waves and accumulated over head chunks by the one thread
+// that owns each key column, so no atomics are used and results are
+// deterministic.
+#pragma once
+#include "common.h"
+#include "kernels.h"
+#include <type_traits>
+
+namespace hys {
+
+template <typename QT> struct Compute;
+template <> struct Compute<float> { using CT = float; static constexpr int KPAD = 4; static constexpr int VPAD = 4; };
+template <> struct Compute<uint16_t> { using CT = uint16_t; static constexpr int KPAD = 8; static constexpr int VPAD = 4; };
+
+// ---------------------------------------------------------------------------
+// the engine
+// ---------------------------------------------------------------------------
+
+template <int MODE, typename QT, typename KT, int D, int NB>
+__global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
+  using CT = typename Compute<QT>::CT;
+  constexpr bool F32 = sizeof(CT) == 4;
+  constexpr int KROW = D + Compute<QT>::KPAD;      // LDS row stride of K (elements)
+  constexpr int VROW = 64 + Compute<QT>::VPAD;     // LDS row stride of V^T (elements)
+  constexpr int ROWS = 4 * 32 * NB;                // rows per workgroup
+  constexpr int KUN = 64 * (D / 8);                // K staging units (8 elements each)
+  constexpr int KU = KUN / 256;
+  constexpr int VUN = 16 * (D / 8);                // V staging units (4 keys x 8 d)
+  constexpr int VU = (VUN + 255) / 256;
+  constexpr int NDB = D / 32;                      // 32-wide d blocks of O^T
+  constexpr int NQC = F32 ? D / 2 : D / 16;        // Q fragments per row (k-steps of S^T)
+  constexpr int UMAX = 1024;                       // max union entries (block mode)
+  constexpr int NBWMAX = 512;                      // max bitmap words (block mode)
+  constexpr int TLMAX = 2048;                      // max token-list length (token mode)
+  static_assert(KUN % 256 == 0, "D must be 64 or 128");
+
+  __shared__ __attribute__((aligned(16))) CT Klds[64 * KROW];
+  __shared__ __attribute__((aligned(16))) CT VTlds[D * VROW];
+  __shared__ __attribute__((aligned(16))) int kinfo[64];
+  __shared__ float red[2 * ROWS];
+  __shared__ int s_misc[4];
+  // block-sparse lists
+  __shared__ uint32_t s_bitmap[(MODE == M_SPARSE_BLOCK) ? NBWMAX : 1];
+  __shared__ int s_wpre[(MODE == M_SPARSE_BLOCK) ? NBWMAX : 1];
+  __shared__ int s_ulist[(MODE == M_SPARSE_BLOCK) ? UMAX : 1];
+  __shared__ unsigned long long s_member[(MODE == M_SPARSE_BLOCK) ? UMAX : 1];
+  // token-sparse lists
+  __shared__ int s_tlist[(MODE == M_SPARSE_TOKEN) ? TLMAX : 1];
+  __shared__ unsigned char s_selw[(MODE == M_SPARSE_TOKEN) ? 2048 : 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, hh = lane >> 5, ln = lane & 31;
+
+  int bid = blockIdx.x;
+  if (bid >= a.grid_used) return;
+
+  // ---- work decomposition ------------------------------------------------
+  int b, qt, g = 0, ch_begin = 0, ch_end = 1;
+  if (MODE == M_FULL_TILE) {
+    b = bid % a.B;
+    qt = a.ntq - 1 - bid / a.B;                    // longest rows first
+    ch_end = a.Hkv * a.nhc;
+  } else if (MODE == M_SPARSE_TOKEN) {
+    // the head chunks of one query tile run back to back on one XCD
+    // (workgroups are dealt to the 8 XCDs round robin), sharing its gathered KV in L2
+    const int nch = a.Hkv * a.nhc;
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int ch = slot % nch;
+    const int tile_rank = (slot / nch) * 8 + xcd;
+    b = tile_rank % a.B;
+    qt = tile_rank / a.B;
+    if (qt >= a.ntq) return;
+    ch_begin = ch; ch_end = ch + 1;
+  } else {
+    g = bid % a.Hkv;                               // KV group fastest: XCD x sees groups x mod Hkv
+    const int rest = bid / a.Hkv;
+    b = rest % a.B;
+    qt = a.ntq - 1 - rest / a.B;
+  }
+  const int q0 = qt * a.BQ;
+  const int q_last = min(q0 + a.BQ, a.Lq) - 1;
+  const int HC = a.HC;
+
+  // ---- per-WG selection lists ----------------------------------------------
+  int ntiles = 0;
+  int kbase = 0;            // contiguous modes: first key
+  int kend = 0;             // contiguous modes: last key (inclusive)
+  int npre = 0, wstart = 0, wend = 0;
+  if (MODE == M_FULL || MODE == M_FULL_BLOCK || MODE == M_FULL_TILE) {
+    kbase = 0; kend = min(q_last, a.Lk - 1);
+    ntiles = kend / 64 + 1;
+  } else if (MODE == M_SWA_GATE) {
+    kbase = max(0, q0 - a.window + 1); kend = min(q_last, a.Lk - 1);
+    ntiles = (kend - kbase + 1 + 63) / 64;
+  } else if (MODE == M_SPARSE_BLOCK) {
+    const int nbw = (a.nblk + 31) >> 5;
+    for (int w = tid; w < nbw; w += 256) s_bitmap[w] = 0u;
+    for (int u = tid; u < UMAX; u += 256) s_member[u] = 0ull;
+    __syncthreads();
+    const int nent = a.BQ * a.topk;
+    const int32_t* ib = a.idx + (int64_t)b * a.idx_sb;
+    for (int e = tid; e < nent; e += 256) {
+      const int qi = e / a.topk, s = e - qi * a.topk;
+      const int q = q0 + qi;
+      if (q < a.Lq) {
+        const int c = ib[(int64_t)q * a.idx_sr + s];
+        if (c >= 0 && c < a.nblk) atomicOr(&s_bitmap[c >> 5], 1u << (c & 31));
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int carry = 0;
+      for (int w0 = 0; w0 < nbw; w0 += 64) {
+        const int w = w0 + lane;
+        const int cnt = (w < nbw) ? __popc(s_bitmap[w]) : 0;
+        int x = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) { const int y = __shfl_up(x, o); if (lane >= o) x += y; }
+        if (w < nbw) s_wpre[w] = carry + x - cnt;
+        carry += __shfl(x, 63);
+      }
+      if (lane == 0) s_misc[0] = carry;
+    }
+    __syncthreads();
+    for (int w = tid; w < nbw; w += 256) {
+      uint32_t bits = s_bitmap[w];
+      int pos = s_wpre[w];
+      while (bits) {
+        const int bit = __ffs(bits) - 1;
+        bits &= bits - 1;
+        s_ulist[pos++] = w * 32 + bit;
+      }
+    }
+    for (int e = tid; e < nent; e += 256) {
+      const int qi = e / a.topk, s = e - qi * a.topk;
+      const int q = q0 + qi;
+      if (q < a.Lq) {
+        const int c = ib[(int64_t)q * a.idx_sr + s];
+        if (c >= 0 && c < a.nblk) {
+          const int u = s_wpre[c >> 5] + __popc(s_bitmap[c >> 5] & ((1u << (c & 31)) - 1u));
+          atomicOr(&s_member[u], 1ull << qi);
+        }
+      }
+    }
+    __syncthreads();
+    ntiles = s_misc[0];
+  } else if (MODE == M_SPARSE_TOKEN) {
+    wstart = max(0, q0 - a.window + 1);
+    wend = min(q_last, a.Lk - 1);
+    const int nw = wend - wstart + 1;
+    for (int x = tid; x < nw; x += 256) s_selw[x] = 0;
+    __syncthreads();
+    const int32_t* sel = a.idx + (int64_t)b * a.idx_sb + (int64_t)qt * a.idx_sr;
+    // order-preserving compaction of the selected tokens that precede the window
+    int carry = 0;
+    for (int e0 = 0; e0 < a.topk; e0 += 256) {
+      const int e = e0 + tid;
+      const int s = (e < a.topk) ? sel[e] : -1;
+      const bool pre = s >= 0 && s < wstart;
+      if (s >= wstart && s <= wend) s_selw[s - wstart] = 1;
+      const unsigned long long bal = __ballot(pre);
+      if (lane == 0) s_misc[wave] = __popcll(bal);
+      __syncthreads();
+      int before = carry;
+      for (int w = 0; w < wave; ++w) before += s_misc[w];
+      const int mypos = before + __popcll(bal & ((1ull << lane) - 1ull));
+      if (pre && mypos < TLMAX) s_tlist[mypos] = s;
+      carry += s_misc[0] + s_misc[1] + s_misc[2] + s_misc[3];
+      __syncthreads();
+    }
+    npre = min(carry, TLMAX);
+    ntiles = (npre + nw + 63) / 64;
+  }
+
+  // ---- staging helpers -----------------------------------------------------
+  const KT* kb = (const KT*)a.k + (int64_t)b * a.k_sb;
+  const KT* vb = (const KT*)a.v + (int64_t)b * a.v_sb;
+
+  // key position of tile slot t of tile n; -1 when the slot is empty.
+  // For the token mode, bit 30 flags a selected (as opposed to window-only) token.
+  auto keypos = [&](int n, int t) -> int {
+    if (MODE == M_SPARSE_BLOCK) {
+      const int j = s_ulist[n] * 64 + t;
+      return j < a.Lk ? j : -1;
+    } else if (MODE == M_SPARSE_TOKEN) {
+      const int p = n * 64 + t;
+      if (p < npre) return s_tlist[p] | (1 << 30);
+      const int j = wstart + (p - npre);
+      if (j > wend) return -1;
+      return s_selw[j - wstart] ? (j | (1 << 30)) : j;
+    } else {
+      const int j = kbase + n * 64 + t;
+      return j <= kend ? j : -1;
+    }
+  };
+
+  Raw8<KT> kreg[KU];
+  Raw8<KT> vreg[VU][4];
+  int my_kinfo = 0;
+
+  auto stage_load = [&](int n, int g_) {
+    const int kvh = g_;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int unit = tid + 256 * u;
+      const int key = unit / (D / 8), c8 = unit % (D / 8);
+      const int j = keypos(n, key) & ~(1 << 30);
+      const bool ok = keypos(n, key) >= 0;
+      kreg[u] = ok ? load8<KT>(kb + (int64_t)j * a.k_st + (int64_t)kvh * a.k_sh + c8 * 8) : zero8<KT>();
+    }
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      const int unit = tid + 256 * u;
+      if (unit < VUN) {
+        const int kg = unit / (D / 8), dc = unit % (D / 8);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kp = keypos(n, kg * 4 + r);
+          const int j = kp & ~(1 << 30);
+          vreg[u][r] = kp >= 0 ? load8<KT>(vb + (int64_t)j * a.v_st + (int64_t)kvh * a.v_sh + dc * 8) : zero8<KT>();
+        }
+      }
+    }
+    if (tid < 64) {
+      const int kp = keypos(n, tid);
+      my_kinfo = kp >= 0 ? kp : 0x3fffffff;   // empty slots are later than every query
+    }
+  };
+
+  auto stage_store = [&]() {
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int unit = tid + 256 * u;
+      const int key = unit / (D / 8), c8 = unit % (D / 8);
+      Cvt8<CT> c = to_ct(kreg[u]);
+      CT* dst = &Klds[key * KROW + c8 * 8];
+      *(uint4*)dst = c.a;
+      if constexpr (F32) *(uint4*)(dst + 4) = c.b;
+    }
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      const int unit = tid + 256 * u;
+      if (unit < VUN) {
+        const int kg = unit / (D / 8), dc = unit % (D / 8);
+        Cvt8<CT> r0 = to_ct(vreg[u][0]), r1 = to_ct(vreg[u][1]), r2 = to_ct(vreg[u][2]), r3 = to_ct(vreg[u][3]);
+        if constexpr (!F32) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const uint32_t w0 = u4get(r0.a, p), w1 = u4get(r1.a, p), w2 = u4get(r2.a, p), w3 = u4get(r3.a, p);
+            uint2 e, o;
+            e.x = __builtin_amdgcn_perm(w1, w0, 0x05040100u); e.y = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
+            o.x = __builtin_amdgcn_perm(w1, w0, 0x07060302u); o.y = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
+            *(uint2*)&VTlds[(dc * 8 + 2 * p) * VROW + kg * 4] = e;
+            *(uint2*)&VTlds[(dc * 8 + 2 * p + 1) * VROW + kg * 4] = o;
+          }
+        } else {
+#pragma unroll
+          for (int d = 0; d < 8; ++d) {
+            uint4 t;
+            t.x = d < 4 ? u4get(r0.a, d) : u4get(r0.b, d - 4);
+            t.y = d < 4 ? u4get(r1.a, d) : u4get(r1.b, d - 4);
+            t.z = d < 4 ? u4get(r2.a, d) : u4get(r2.b, d - 4);
+            t.w = d < 4 ? u4get(r3.a, d) : u4get(r3.b, d - 4);
+            *(uint4*)&VTlds[(dc * 8 + d) * VROW + kg * 4] = t;
+          }
+        }
+      }
+    }
+    if (tid < 64) kinfo[tid] = my_kinfo;
+  };
+
+  const QT* qbase = (const QT*)a.q + (int64_t)b * a.q_sb;
+
+  for (int ch = ch_begin; ch < ch_end; ++ch) {
+    int h0 = 0;
+    if (MODE == M_FULL_TILE || MODE == M_SPARSE_TOKEN) { g = ch / a.nhc; h0 = (ch % a.nhc) * HC; }
+
+    // ---- rows owned by this lane -------------------------------------------
+    int qpos[NB], head[NB], qiv[NB];
+    bool valid[NB];
+    bool wave_full = true;
+    int wave_qmin = 0x7fffffff, wave_qmax = -1;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int r = wave * 32 * NB + nb * 32 + ln;
+      const int qi = r / HC, hl = r - qi * HC;
+      qiv[nb] = qi;
+      qpos[nb] = q0 + qi;
+      head[nb] = g * a.G + h0 + hl;
+      valid[nb] = qi < a.BQ && qpos[nb] < a.Lq && (h0 + hl) < a.G;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      int qv = valid[nb] ? qpos[nb] : 0x7fffffff;
+      int qx = valid[nb] ? qpos[nb] : -1;
+      for (int o = 32; o >= 1; o >>= 1) { qv = min(qv, __shfl_xor(qv, o)); qx = max(qx, __shfl_xor(qx, o)); }
+      wave_qmin = min(wave_qmin, qv);
+      wave_qmax = max(wave_qmax, qx);
+      wave_full = wave_full && (__ballot(!valid[nb]) == 0ull);
+    }
+    const bool wave_any = wave_qmax >= 0;
+    unsigned long long wave_qmask = 0ull;
+    if (MODE == M_SPARSE_BLOCK) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        unsigned long long m = valid[nb] ? (1ull << qiv[nb]) : 0ull;
+        for (int o = 32; o >= 1; o >>= 1) m |= __shfl_xor(m, o);
+        wave_qmask |= m;
+      }
+    }
+
+    // ---- Q fragments (B operand of S^T) ------------------------------------
+    typedef typename std::conditional<F32, float, bf16x8>::type QFrag;
+    QFrag qf[NB][NQC];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const QT* qr = qbase + (int64_t)qpos[nb] * a.q_st + (int64_t)head[nb] * a.q_sh;
+#pragma unroll
+      for (int c = 0; c < NQC; ++c) {
+        if constexpr (F32) {
+          qf[nb][c] = valid[nb] ? qr[2 * c + hh] : 0.0f;
+        } else {
+          uint4 z = {0u, 0u, 0u, 0u};
+          qf[nb][c] = as_bf16x8(valid[nb] ? *(const uint4*)(qr + 16 * c + 8 * hh) : z);
+        }
+      }
+    }
+
+    float m_run[NB], l_run[NB];
+    f32x16 acc[NB][NDB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      m_run[nb] = kNegInf; l_run[nb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[nb][db][i] = 0.f;
+    }
+
+    const float c2 = a.scale_log2;
+
+    // score emission for tile n (reads red[n & 1]); called by all threads after a barrier
+    auto emit_scores = [&](int n) {
+      if (MODE == M_FULL_BLOCK) {
+        const float* rb = red + (n & 1) * ROWS;
+        float* sc = a.scores + (int64_t)g * a.sc_sg + (int64_t)b * a.sc_sb;
+        for (int t = tid; t < a.BQ; t += 256) {
+          const int q = q0 + t;
+          if (q < a.Lq) {
+            float mx = kNegInf;
+            for (int hl = 0; hl < HC; ++hl) mx = fmaxf(mx, rb[t * HC + hl]);
+            sc[(int64_t)q * a.sc_sr + n] = mx * a.logit_scale;
+          }
+        }
+      } else if (MODE == M_FULL_TILE) {
+        if (tid < 64) {
+          const float* rb = red + (n & 1) * ROWS;
+          float mx = fmaxf(fmaxf(rb[tid], rb[64 + tid]), fmaxf(rb[128 + tid], rb[192 + tid]));
+          const int j = n * 64 + tid;
+          if (j < a.Lk) {
+            float* dst = a.scores + (int64_t)b * a.sc_sb + (int64_t)qt * a.sc_sr + j;
+            const float v = mx * a.logit_scale;
+            *dst = (ch == 0) ? v : fmaxf(*dst, v);
+          }
+        }
+      }
+    };
+
+    // ---- tile loop ---------------------------------------------------------
+    if (ntiles > 0) stage_load(0, g);
+    for (int n = 0; n < ntiles; ++n) {
+      __syncthreads();
+      if (n > 0) emit_scores(n - 1);
+      stage_store();
+      __syncthreads();
+      if (n + 1 < ntiles) stage_load(n + 1, g);
+
+      // wave-level skip: nothing of this tile is visible to any row of the wave
+      bool active = wave_any;
+      if (MODE == M_SPARSE_BLOCK) active = active && ((s_member[n] & wave_qmask) != 0ull);
+      const unsigned long long memb = (MODE == M_SPARSE_BLOCK) ? s_member[n] : 0ull;
+
+      if (!active) {
+        if (MODE == M_FULL_BLOCK && hh == 0) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) red[(n & 1) * ROWS + wave * 32 * NB + nb * 32 + ln] = kNegInf;
+        }
+        if (MODE == M_FULL_TILE) red[(n & 1) * ROWS + wave * 64 + lane] = kNegInf;
+        continue;
+      }
+
+      // S^T = K Q^T  (M = 64 keys as two 32-blocks, N = rows, K = D)
+      f32x16 s[2][NB];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[mb][nb][i] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NQC; ++c) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          if constexpr (F32) {
+            const float ka = Klds[(mb * 32 + ln) * KROW + 2 * c + hh];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(ka, qf[nb][c], s[mb][nb], 0, 0, 0);
+          } else {
+            const bf16x8 ka = as_bf16x8(*(const uint4*)&Klds[(mb * 32 + ln) * KROW + 16 * c + 8 * hh]);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[nb][c], s[mb][nb], 0, 0, 0);
+          }
+        }
+      }
+
+      // masking
+      bool need_mask = true;
+      if (MODE == M_FULL || MODE == M_FULL_BLOCK || MODE == M_FULL_TILE)
+        need_mask = !(wave_full && (n * 64 + 63 <= wave_qmin) && (n * 64 + 63 <= kend));
+      if (need_mask) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int off = mb * 32 + 8 * i4 + 4 * hh;
+            const int4 ki = *(const int4*)&kinfo[off];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int kinf = e == 0 ? ki.x : (e == 1 ? ki.y : (e == 2 ? ki.z : ki.w));
+              const int j = kinf & 0x3fffffff;
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb) {
+                bool ok = valid[nb] && j <= qpos[nb];
+                if (MODE == M_SWA_GATE) ok = ok && (j > qpos[nb] - a.window);
+                if (MODE == M_SPARSE_BLOCK) ok = ok && ((memb >> qiv[nb]) & 1ull);
+                if (MODE == M_SPARSE_TOKEN) ok = ok && ((kinf >> 30) || (j > qpos[nb] - a.window));
+                if (!ok) s[mb][nb][4 * i4 + e] = kNegInf;
+              }
+            }
+          }
+        }
+      }
+
+      // token scores: per-key max over this workgroup's rows
+      if (MODE == M_FULL_TILE) {
+        float cm[32];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float v = s[mb][0][i];
+#pragma unroll
+            for (int nb = 1; nb < NB; ++nb) v = fmaxf(v, s[mb][nb][i]);
+            cm[mb * 16 + i] = v;
+          }
+        // reduce-scatter over the 32 lanes of each half: after 5 halvings lane ln
+        // holds the max of one of the 32 values
+#pragma unroll
+        for (int st = 0; st < 5; ++st) {
+          const int half = 16 >> st;                 // values kept after this step
+          const int bit = 16 >> st;                  // lane bit exchanged
+          const bool upper = (ln & bit) != 0;
+#pragma unroll
+          for (int x = 0; x < half; ++x) {
+            const float send = upper ? cm[x] : cm[x + half];
+            const float keep = upper ? cm[x + half] : cm[x];
+            const float got = __shfl_xor(send, bit);
+            cm[x] = fmaxf(keep, got);
+          }
+        }
+        // lane ln now owns value index vi = bitrev5-style mapping: bits of ln pick the upper halves
+        int vi = 0;
+#pragma unroll
+        for (int st = 0; st < 5; ++st) if (ln & (16 >> st)) vi += (16 >> st);
+        const int mb = vi >> 4, i = vi & 15;
+        const int off = mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        red[(n & 1) * ROWS + wave * 64 + off] = cm[0];
+      }
+
+      // online softmax (base 2 on raw dot products)
+      float alpha[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        float mt = kNegInf;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[mb][nb][i]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        if (MODE == M_FULL_BLOCK && hh == 0) red[(n & 1) * ROWS + wave * 32 * NB + nb * 32 + ln] = mt;
+        const float mnew = fmaxf(m_run[nb], mt);
+        const float muse = (mnew == kNegInf) ? 0.f : mnew;
+        alpha[nb] = __builtin_amdgcn_exp2f((m_run[nb] - muse) * c2);
+        m_run[nb] = mnew;
+        const float mc = muse * c2;
+        float ps = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][nb][i], c2, -mc));
+            s[mb][nb][i] = p;
+            ps += p;
+          }
+        l_run[nb] = fmaf(l_run[nb], alpha[nb], ps);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[nb][db][i] *= alpha[nb];
+      }
+
+      // O^T += V^T P^T  (M = D, N = rows, K = 64 keys)
+      if constexpr (F32) {
+#pragma unroll
+        for (int kk = 0; kk < 32; ++kk) {
+          const int mb = kk >> 4, i = kk & 15;
+          const int key = mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const float va = VTlds[(db * 32 + ln) * VROW + key];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              acc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, s[mb][nb][i], acc[nb][db], 0, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          const int mb = kc >> 1, i0 = 8 * (kc & 1);
+          bf16x8 pf[NB];
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            uint4 pk;
+            pk.x = pack_bf16x2(s[mb][nb][i0 + 0], s[mb][nb][i0 + 1]);
+            pk.y = pack_bf16x2(s[mb][nb][i0 + 2], s[mb][nb][i0 + 3]);
+            pk.z = pack_bf16x2(s[mb][nb][i0 + 4], s[mb][nb][i0 + 5]);
+            pk.w = pack_bf16x2(s[mb][nb][i0 + 6], s[mb][nb][i0 + 7]);
+            pf[nb] = as_bf16x8(pk);
+          }
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const CT* vr = &VTlds[(db * 32 + ln) * VROW + 16 * kc + 4 * hh];
+            uint4 va;
+            const uint2 lo = *(const uint2*)vr;
+            const uint2 hi = *(const uint2*)(vr + 8);
+            va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
+            const bf16x8 vf = as_bf16x8(va);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              acc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb], acc[nb][db], 0, 0, 0);
+          }
+        }
+      }
+    }  // tile loop
+
+    __syncthreads();
+    if (ntiles > 0) emit_scores(ntiles - 1);
+
+    // -inf for blocks / keys after the diagonal
+    if (MODE == M_FULL_BLOCK) {
+      float* sc = a.scores + (int64_t)g * a.sc_sg + (int64_t)b * a.sc_sb;
+      const int c0 = ntiles, ncol = a.nblk - c0;
+      if (ncol > 0)
+        for (int e = tid; e < a.BQ * ncol; e += 256) {
+          const int t = e / ncol, c = c0 + (e - t * ncol);
+          if (q0 + t < a.Lq) sc[(int64_t)(q0 + t) * a.sc_sr + c] = kNegInf;
+        }
+    }
+    if (MODE == M_FULL_TILE && ch == 0) {
+      float* sc = a.scores + (int64_t)b * a.sc_sb + (int64_t)qt * a.sc_sr;
+      for (int j = ntiles * 64 + tid; j < a.Lk; j += 256) sc[j] = kNegInf;
+    }
+
+    // ---- epilogue ------------------------------------------------------------
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float lsum = l_run[nb] + __shfl_xor(l_run[nb], 32);
+      const bool live = m_run[nb] != kNegInf;
+      const float inv = live ? a.v_scale / lsum : 0.f;
+      const float lse_v = live ? (m_run[nb] * a.logit_scale + __logf(lsum)) : kNegInf;
+      if (!valid[nb]) continue;
+      const int64_t row_off_o = (int64_t)b * a.o_sb + (int64_t)qpos[nb] * a.o_st + (int64_t)head[nb] * a.o_sh;
+      float gate = 1.f;
+      bool sp_live = true;
+      const float* osp = nullptr;
+      if (MODE == M_SWA_GATE) {
+        // g = sigmoid(<q, w_h> + b_h): each lane holds half of the row's d values
+        const float* w = a.gate_w + (int64_t)head[nb] * D;
+        float z = 0.f;
+        const QT* qr = qbase + (int64_t)qpos[nb] * a.q_st + (int64_t)head[nb] * a.q_sh;
+#pragma unroll
+        for (int c = 0; c < NQC; ++c) {
+          if constexpr (F32) {
+            z = fmaf(qr[2 * c + hh], w[2 * c + hh], z);
+          } else {
+            const uint4 qv = *(const uint4*)(qr + 16 * c + 8 * hh);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const uint32_t wv = u4get(qv, p);
+              z = fmaf(bf16_to_f32((uint16_t)(wv & 0xffffu)), w[16 * c + 8 * hh + 2 * p], z);
+              z = fmaf(bf16_to_f32((uint16_t)(wv >> 16)), w[16 * c + 8 * hh + 2 * p + 1], z);
+            }
+          }
+        }
+        z += __shfl_xor(z, 32);
+        if (a.gate_b) z += a.gate_b[head[nb]];
+        gate = 1.f / (1.f + __expf(-z));
+        const float lsp = a.lse_sp[((int64_t)b * a.Hq + head[nb]) * a.Lq + qpos[nb]];
+        sp_live = lsp != kNegInf;
+        osp = a.o_sp + (int64_t)b * a.osp_sb + (int64_t)qpos[nb] * a.osp_st + (int64_t)head[nb] * a.osp_sh;
+      } else if (a.lse && hh == 0) {
+        a.lse[((int64_t)b * a.Hq + head[nb]) * a.Lq + qpos[nb]] = lse_v;
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = db * 32 + 8 * i4 + 4 * hh;
+          float r[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[e] = acc[nb][db][4 * i4 + e] * inv;
+          if (MODE == M_SWA_GATE) {
+            if (sp_live) {
+              const float4 sp = *(const float4*)(osp + d);
+              const float spv[4] = {sp.x, sp.y, sp.z, sp.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) r[e] = gate * spv[e] + (1.f - gate) * r[e];
+            }
+          }
+          if (a.o_f32) {
+            float4 out = {r[0], r[1], r[2], r[3]};
+            *(float4*)((float*)a.o + row_off_o + d) = out;
+          } else {
+            uint2 out;
+            out.x = pack_bf16x2(r[0], r[1]);
+            out.y = pack_bf16x2(r[2], r[3]);
+            *(uint2*)((uint16_t*)a.o + row_off_o + d) = out;
+          }
+        }
+      }
+    }
+  }  // chunk loop
+}
+
+// ---------------------------------------------------------------------------
+// per-mode launch (instantiated in one translation unit per mode)
+// ---------------------------------------------------------------------------
+template <int MODE, typename QT, typename KT, int D>
+static hipError_t launch_one(const AttnArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((attn_tile_kernel<MODE, QT, KT, D, 2>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(int qt, int kt, int D, const AttnArgs& a, int grid, hipStream_t s) {
+  if (qt == ET_F32 && kt == ET_F32) {
+    if (D == 64) return launch_one<MODE, float, float, 64>(a, grid, s);
+    if (D == 128) return launch_one<MODE, float, float, 128>(a, grid, s);
+  } else if (qt == ET_BF16 && kt == ET_BF16) {
+    if (D == 64) return launch_one<MODE, uint16_t, uint16_t, 64>(a, grid, s);
+    if (D == 128) return launch_one<MODE, uint16_t, uint16_t, 128>(a, grid, s);
+  } else if (qt == ET_BF16 && kt == ET_FP8) {
+    if (D == 64) return launch_one<MODE, uint16_t, uint8_t, 64>(a, grid, s);
+    if (D == 128) return launch_one<MODE, uint16_t, uint8_t, 128>(a, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hys

@@ -1,0 +1,130 @@
+// Shared device helpers for the gfx950 kernels of the HySparse hot path.
+//
+// Element storage types:
+//   float     - fp32
+//   uint16_t  - bf16 bits
+//   uint8_t   - OCP fp8 e4m3fn bits (value = decode(byte) * per-tensor scale)
+//
+// MFMA lane layouts used throughout (wave64, checked on gfx950):
+//   v_mfma_f32_32x32x16_bf16: lane l holds A[m=l%32][k=8*(l/32)+j], B[k=8*(l/32)+j][n=l%32]
+//                             (j = 0..7) and C[m=8*(i/4)+4*(l/32)+i%4][n=l%32] (i = 0..15)
+//   v_mfma_f32_32x32x2_f32:   lane l holds A[m=l%32][k=l/32], B[k=l/32][n=l%32], same C
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hys {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+  return __builtin_bit_cast(float, (uint32_t)x << 16);
+}
+
+// round-to-nearest-even fp32 -> bf16 bits (NaN kept quiet)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Two fp32 -> packed bf16x2, round to nearest even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// OCP e4m3fn -> bf16, exact.  v_cvt_pk_f32_fp8 decodes two e4m3fn bytes of a
+// dword to fp32 (checked against the format definition for all 256 codes on
+// gfx950); every finite e4m3 value has at most 4 significant bits, so the
+// round-to-nearest bf16 conversion that follows is exact.  (The pair goes
+// through __builtin_convertvector: extracting the two fp32 lanes as integers
+// and splicing their upper halves by hand was miscompiled by this toolchain,
+// which read the first lane twice.)
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi_word) {
+  const f32x2 f = hi_word ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// Four fp8 bytes (one dword) -> four bf16 (two dwords).
+__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = fp8x2_to_bf16x2(w, false);
+  hi = fp8x2_to_bf16x2(w, true);
+}
+
+// Four fp8 bytes -> four fp32.
+__device__ __forceinline__ f32x4 fp8x4_to_f32x4(uint32_t w) {
+  f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  f32x4 r = {a[0], a[1], b[0], b[1]};
+  return r;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger key).
+// -inf maps below every finite value; NaN is handled by callers.
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 8 consecutive stored elements as raw registers
+template <typename KT> struct Raw8;
+template <> struct Raw8<float> { uint4 a, b; };
+template <> struct Raw8<uint16_t> { uint4 a; };
+template <> struct Raw8<uint8_t> { uint2 a; };
+
+template <typename KT> __device__ __forceinline__ Raw8<KT> load8(const KT* p);
+template <> __device__ __forceinline__ Raw8<float> load8<float>(const float* p) {
+  Raw8<float> r; r.a = *(const uint4*)p; r.b = *(const uint4*)(p + 4); return r;
+}
+template <> __device__ __forceinline__ Raw8<uint16_t> load8<uint16_t>(const uint16_t* p) {
+  Raw8<uint16_t> r; r.a = *(const uint4*)p; return r;
+}
+template <> __device__ __forceinline__ Raw8<uint8_t> load8<uint8_t>(const uint8_t* p) {
+  Raw8<uint8_t> r; r.a = *(const uint2*)p; return r;
+}
+template <typename KT> __device__ __forceinline__ Raw8<KT> zero8() { Raw8<KT> r; __builtin_memset(&r, 0, sizeof(r)); return r; }
+
+// 8 elements in compute layout: bf16 -> one uint4, fp32 -> two uint4
+template <typename CT> struct Cvt8;
+template <> struct Cvt8<uint16_t> { uint4 a; };
+template <> struct Cvt8<float> { uint4 a, b; };
+
+__device__ __forceinline__ Cvt8<uint16_t> to_ct(const Raw8<uint16_t>& r) { Cvt8<uint16_t> c; c.a = r.a; return c; }
+__device__ __forceinline__ Cvt8<uint16_t> to_ct(const Raw8<uint8_t>& r) {
+  Cvt8<uint16_t> c;
+  fp8x4_to_bf16x4(r.a.x, c.a.x, c.a.y);
+  fp8x4_to_bf16x4(r.a.y, c.a.z, c.a.w);
+  return c;
+}
+__device__ __forceinline__ Cvt8<float> to_ct(const Raw8<float>& r) { Cvt8<float> c; c.a = r.a; c.b = r.b; return c; }
+
+__device__ __forceinline__ uint32_t u4get(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+}  // namespace hys

@@ -1,0 +1,93 @@
+// Internal launch interface between the C-ABI layer and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hys {
+
+enum ElemType { ET_F32 = 0, ET_BF16 = 1, ET_FP8 = 2 };
+
+// Prefill attention modes, all served by one tiled MFMA engine.
+enum AttnMode {
+  M_FULL = 0,          // causal attention, no scores
+  M_FULL_BLOCK = 1,    // causal attention + per-(query, key-block) max logit
+  M_FULL_TILE = 2,     // causal attention + per-(query-tile, key) max logit
+  M_SPARSE_BLOCK = 3,  // attention over selected key blocks (per-query selection)
+  M_SPARSE_TOKEN = 4,  // attention over selected tokens of a query tile + forced recent window
+  M_SWA_GATE = 5,      // sliding-window attention fused with the sigmoid gate merge
+};
+
+struct AttnArgs {
+  const void* q; int64_t q_sb, q_st, q_sh;
+  const void* k; int64_t k_sb, k_st, k_sh;
+  const void* v; int64_t v_sb, v_st, v_sh;
+  void* o; int64_t o_sb, o_st, o_sh;
+  int o_f32;                 // 1: fp32 output, 0: bf16 output
+  float* lse;                // [B, Hq, Lq] or null
+  int B, Lq, Lk, Hq, Hkv, G;
+  float scale_log2;          // softmax scale * k scale * log2(e)
+  float logit_scale;         // softmax scale * k scale
+  float v_scale;             // V dequantisation scale applied to O
+  int BQ;                    // queries per workgroup row set
+  int HC;                    // query heads per row set
+  int nhc;                   // head chunks per KV group = ceil(G / HC)
+  int ntq;                   // number of query tiles = ceil(Lq / BQ)
+  // importance scores (M_FULL_BLOCK: [B, Lq, nblk] per KV group slab; M_FULL_TILE: [B, ntq, Lk])
+  float* scores; int64_t sc_sb, sc_sr, sc_sg;
+  int nblk;
+  // sparse selection
+  const int32_t* idx; int64_t idx_sb, idx_sr;
+  int topk;
+  int window;
+  // gate inputs (M_SWA_GATE)
+  const float* o_sp; int64_t osp_sb, osp_st, osp_sh;
+  const float* lse_sp;       // [B, Hq, Lq]
+  const float* gate_w;       // [Hq, D]
+  const float* gate_b;       // [Hq] or null
+  int grid_used;             // work items; extra workgroups exit
+};
+
+hipError_t launch_attn(int mode, int qt, int kt, int D, const AttnArgs& a, int grid, hipStream_t s);
+
+hipError_t launch_reduce_max(const float* part, int nparts, int64_t part_stride, float* out, int64_t n,
+                             hipStream_t s);
+
+struct TopkArgs {
+  const float* scores; int64_t rows, cols, row_stride;
+  int k;
+  int32_t* idx; int32_t* count;
+  // two-stage path workspace
+  float* cand_val; int32_t* cand_idx; int nchunk; int64_t chunk_cols;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+size_t topk_workspace_bytes(int64_t rows, int64_t cols, int k);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+
+// HySparse2 decode (one query per sequence, MQA cache).
+constexpr int kMaxDecodeLayers = 16;
+constexpr int kMaxDecodeBatch = 64;
+
+struct DecArgs {
+  const void* q[kMaxDecodeLayers]; int64_t q_sb, q_sh;   // per layer [B, 1, Hq, D] bf16
+  const void* k; int64_t k_sb, k_st;                     // [B, Nmax, 1, D]
+  const void* v; int64_t v_sb, v_st;
+  int lens[kMaxDecodeBatch];                             // valid cache length per sequence
+  int B, Hq, Nmax, nsplit, nlayer;
+  float scale_log2, logit_scale;
+  float* scores; int64_t sc_sb;                          // full mode: [B, Nmax] token scores
+  const int32_t* idx; int64_t idx_sb; int topk; int window;   // sparse mode: [B, topk]
+  float* part_o; float* part_ml;                         // [(layer*B + b)*nsplit + s][Hq][D], [..][Hq][2]
+};
+
+struct MergeArgs {
+  const float* part_o; const float* part_ml;
+  int B, Hq, nsplit, nlayer;
+  float logit_scale, v_scale, scale_log2;
+  void* o[kMaxDecodeLayers]; int64_t o_sb, o_sh; int o_f32;
+  float* lse[kMaxDecodeLayers];                          // [B, Hq] per layer or null
+};
+
+hipError_t launch_decode(int sparse, int kt, int D, const DecArgs& a, hipStream_t s);
+hipError_t launch_decode_merge(int D, const MergeArgs& a, hipStream_t s);
+
+}  // namespace hys

@@ -1,0 +1,285 @@
+// Exact per-row top-k selection on gfx950.
+//
+// Order: score descending, then column ascending (the lowest index wins a
+// tie); entries that are -inf or NaN are never chosen.  The output row holds
+// the chosen columns in ascending order, padded with -1, plus their count.
+// (TopK over the full layer's importance scores: QbitAI HySparse article,
+// method section; TechWalker HySparse write-up, kernel paragraph.)
+//
+// Method: each score becomes an order-preserving 32-bit key (0 for -inf/NaN).
+// The threshold T = the k-th largest key is found by bisection over the 32 key
+// bits, each step counting keys >= candidate across the row (no atomics, no
+// sorting).  Keys above T are taken; of the keys equal to T the ones with the
+// lowest columns fill the remaining slots.  Each thread owns a contiguous
+// segment of columns, so an exclusive scan of per-thread counts places every
+// chosen column directly at its ascending position.
+//
+//   short rows (cols <= 2048): one wave per row, up to 32 keys per lane
+//   long rows  (cols <= 65536): one 1024-thread workgroup per row, up to 64 keys per thread
+//   longer rows: each 65536-column chunk keeps its own top-k (exact superset of
+//   the row's top-k), then a second pass selects among the chunk winners.
+#include "common.h"
+#include "kernels.h"
+
+namespace hys {
+
+__device__ __forceinline__ uint32_t score_key(float x) {
+  // valid iff x > -inf (NaN fails the comparison); valid keys are >= 0x00800000
+  return (x > kNegInf) ? f32_order_key(x) : 0u;
+}
+
+// ---------------------------------------------------------------------------
+// one wave per row
+// ---------------------------------------------------------------------------
+template <int V>
+__global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict__ scores, int64_t rows, int64_t cols,
+                                                        int64_t row_stride, int k, int32_t* __restrict__ idx,
+                                                        int32_t* __restrict__ count) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* sr = scores + row * row_stride;
+  const int seg = (int)((cols + 63) / 64);           // columns per lane (<= V)
+  const int c0 = lane * seg;
+  uint32_t key[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int c = c0 + v;
+    key[v] = (v < seg && c < cols) ? score_key(sr[c]) : 0u;
+  }
+  auto count_ge = [&](uint32_t t) {
+    int n = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) n += (key[v] >= t) ? 1 : 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o);
+    return n;
+  };
+  const int nvalid = count_ge(1u);
+  uint32_t T = 1u;
+  int need = k;   // number of keys equal to T to take (when nvalid > k)
+  if (nvalid > k && k > 0) {
+    uint32_t t = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = t | (1u << bit);
+      if (count_ge(cand) >= k) t = cand;
+    }
+    T = t;
+    need = k - count_ge(T + 1u);
+  } else {
+    need = 0x7fffffff;
+  }
+  const bool all = !(nvalid > k && k > 0);
+  // ties at T in column order
+  int nt = 0;
+  if (!all) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) nt += (key[v] == T) ? 1 : 0;
+  }
+  int tpre = nt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) { const int y = __shfl_up(tpre, o); if (lane >= o) tpre += y; }
+  tpre -= nt;
+  // flags and placement
+  int cnt = 0;
+  uint32_t take = 0u;
+  {
+    int tr = tpre;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      bool f;
+      if (k <= 0) f = false;
+      else if (all) f = key[v] != 0u;
+      else if (key[v] > T) f = true;
+      else if (key[v] == T) { f = tr < need; ++tr; }
+      else f = false;
+      if (f) { take |= 1u << v; ++cnt; }
+    }
+  }
+  int pre = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) { const int y = __shfl_up(pre, o); if (lane >= o) pre += y; }
+  const int total = __shfl(pre, 63);
+  pre -= cnt;
+  int32_t* out = idx + row * (int64_t)k;
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+    if (take & (1u << v)) out[pre++] = c0 + v;
+  for (int p = total + lane; p < k; p += 64) out[p] = -1;
+  if (count && lane == 0) count[row] = total;
+}
+
+// ---------------------------------------------------------------------------
+// one 1024-thread workgroup per (row, chunk)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int block_sum_1024(int v, int* sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) t += sh[i];
+  return t;
+}
+
+// exclusive scan over the 1024 threads in thread order; returns (prefix, total)
+__device__ __forceinline__ int block_excl_scan_1024(int v, int* sh, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) { const int y = __shfl_up(x, o); if (lane >= o) x += y; }
+  __syncthreads();
+  if (lane == 63) sh[w] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { const int s = sh[i]; before += (i < w) ? s : 0; tot += s; }
+  total = tot;
+  return before + x - v;
+}
+
+// vals: row r, position p at vals[r*row_stride + p] (p < cols)
+// cmap: if non-null, the original column of position p is cmap[r*row_stride + p]
+//       (positions with cmap == -1 are empty); else the column is chunk_base + p.
+// Output for (row, chunk): out_idx[(r*nchunk + chunk)*k ...], out_val likewise (if non-null).
+__global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restrict__ vals,
+                                                          const int32_t* __restrict__ cmap, int64_t rows,
+                                                          int64_t cols, int64_t row_stride, int64_t chunk_cols,
+                                                          int nchunk, int k, int32_t* __restrict__ out_idx,
+                                                          float* __restrict__ out_val, int32_t* __restrict__ count) {
+  __shared__ int sh[16];
+  const int tid = threadIdx.x;
+  const int64_t r = blockIdx.x / nchunk;
+  const int chunk = blockIdx.x % nchunk;
+  const int64_t cbase = (int64_t)chunk * chunk_cols;
+  const int64_t ccols = min(chunk_cols, cols - cbase);
+  const int seg = (int)((ccols + 1023) / 1024);        // <= 64
+  const int64_t p0 = cbase + (int64_t)tid * seg;
+  const float* vr = vals + r * row_stride;
+  const int32_t* mr = cmap ? cmap + r * row_stride : nullptr;
+  uint32_t key[64];
+#pragma unroll
+  for (int v = 0; v < 64; ++v) {
+    const int64_t p = p0 + v;
+    uint32_t kk = 0u;
+    if (v < seg && p < cbase + ccols) {
+      const bool present = mr ? (mr[p] >= 0) : true;
+      kk = present ? score_key(vr[p]) : 0u;
+    }
+    key[v] = kk;
+  }
+  auto count_ge = [&](uint32_t t) {
+    int n = 0;
+#pragma unroll
+    for (int v = 0; v < 64; ++v) n += (key[v] >= t) ? 1 : 0;
+    return block_sum_1024(n, sh);
+  };
+  const int nvalid = count_ge(1u);
+  const bool all = !(nvalid > k && k > 0);
+  uint32_t T = 1u;
+  int need = 0;
+  if (!all) {
+    uint32_t t = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = t | (1u << bit);
+      if (count_ge(cand) >= k) t = cand;
+    }
+    T = t;
+    need = k - count_ge(T + 1u);
+  }
+  int nt = 0;
+  if (!all) {
+#pragma unroll
+    for (int v = 0; v < 64; ++v) nt += (key[v] == T) ? 1 : 0;
+  }
+  int ttot;
+  const int tpre = block_excl_scan_1024(nt, sh, ttot);
+  uint64_t take = 0ull;
+  int cnt = 0;
+  {
+    int tr = tpre;
+#pragma unroll
+    for (int v = 0; v < 64; ++v) {
+      bool f;
+      if (k <= 0) f = false;
+      else if (all) f = key[v] != 0u;
+      else if (key[v] > T) f = true;
+      else if (key[v] == T) { f = tr < need; ++tr; }
+      else f = false;
+      if (f) { take |= 1ull << v; ++cnt; }
+    }
+  }
+  int total;
+  int pre = block_excl_scan_1024(cnt, sh, total);
+  const int64_t ob = (r * nchunk + chunk) * (int64_t)k;
+#pragma unroll
+  for (int v = 0; v < 64; ++v) {
+    if (take & (1ull << v)) {
+      const int64_t p = p0 + v;
+      out_idx[ob + pre] = mr ? mr[p] : (int32_t)p;
+      if (out_val) out_val[ob + pre] = vr[p];
+      ++pre;
+    }
+  }
+  for (int p = total + tid; p < k; p += 1024) {
+    out_idx[ob + p] = -1;
+    if (out_val) out_val[ob + p] = kNegInf;
+  }
+  if (count && tid == 0) count[r * nchunk + chunk] = total;
+}
+
+// ---------------------------------------------------------------------------
+// int32 fill (used instead of hipMemsetAsync so that captured graphs replay correctly)
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+size_t topk_workspace_bytes(int64_t rows, int64_t cols, int k) {
+  if (cols <= 65536) return 0;
+  const int64_t nchunk = (cols + 65535) / 65536;
+  return (size_t)(rows * nchunk * (int64_t)k) * (sizeof(float) + sizeof(int32_t));
+}
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
+  if (a.rows == 0) return hipSuccess;
+  if (a.cols <= 2048 && a.k <= 2048) {
+    const unsigned grid = (unsigned)((a.rows + 3) / 4);
+    const int64_t seg = (a.cols + 63) / 64;
+    if (seg <= 8)
+      hipLaunchKernelGGL(topk_wave_kernel<8>, dim3(grid), dim3(256), 0, s, a.scores, a.rows, a.cols, a.row_stride, a.k, a.idx, a.count);
+    else
+      hipLaunchKernelGGL(topk_wave_kernel<32>, dim3(grid), dim3(256), 0, s, a.scores, a.rows, a.cols, a.row_stride, a.k, a.idx, a.count);
+    return hipGetLastError();
+  }
+  if (a.cols <= 65536) {
+    hipLaunchKernelGGL(topk_block_kernel, dim3((unsigned)a.rows), dim3(1024), 0, s, a.scores, (const int32_t*)nullptr,
+                       a.rows, a.cols, a.row_stride, (int64_t)65536, 1, a.k, a.idx, (float*)nullptr, a.count);
+    return hipGetLastError();
+  }
+  // two passes: per-chunk winners, then the winners' winners
+  const int nchunk = (int)((a.cols + 65535) / 65536);
+  hipLaunchKernelGGL(topk_block_kernel, dim3((unsigned)(a.rows * nchunk)), dim3(1024), 0, s, a.scores,
+                     (const int32_t*)nullptr, a.rows, a.cols, a.row_stride, (int64_t)65536, nchunk, a.k, a.cand_idx,
+                     a.cand_val, (int32_t*)nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t ccols = (int64_t)nchunk * a.k;       // <= 65536 by validation
+  hipLaunchKernelGGL(topk_block_kernel, dim3((unsigned)a.rows), dim3(1024), 0, s, (const float*)a.cand_val,
+                     (const int32_t*)a.cand_idx, a.rows, ccols, ccols, (int64_t)65536, 1, a.k, a.idx, (float*)nullptr,
+                     a.count);
+  return hipGetLastError();
+}
+
+}  // namespace hys

@@ -1,0 +1,122 @@
+"""Python binding of the five C-ABI calls (argument marshalling only).
+
+PyTorch supplies device memory and the current stream; every computation runs
+in libhys.so.  Workspace, when a call needs one, is queried from the library
+and allocated with torch on the same device.
+"""
+import ctypes
+import math
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import (HYS_BF16, HYS_F32, HYS_FP8_E4M3, HYS_SCORE_BLOCK, HYS_SCORE_NONE, HYS_SCORE_TILE_TOKEN,
+                   HysAttnParams, HysDecodeParams, HysScoreParams, HysSparseParams, HysTensor4, check)
+
+_DT = {torch.float32: HYS_F32, torch.bfloat16: HYS_BF16, torch.uint8: HYS_FP8_E4M3,
+       torch.float8_e4m3fn: HYS_FP8_E4M3}
+_SCORE = {"none": HYS_SCORE_NONE, "block": HYS_SCORE_BLOCK, "tile_token": HYS_SCORE_TILE_TOKEN}
+
+
+def tensor4(t: torch.Tensor) -> HysTensor4:
+    """Describe a [B, T, H, D] torch tensor (fp8 given as uint8 or float8_e4m3fn)."""
+    if t.dim() != 4:
+        raise ValueError(f"expected a 4-D [B, T, H, D] tensor, got shape {tuple(t.shape)}")
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    d = HysTensor4()
+    d.ptr = t.data_ptr()
+    d.dtype = _DT[t.dtype]
+    for i in range(4):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # ws == NULL means "size query", so a run always passes a real buffer
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def hys_full_attn_fwd(q, k, v, o, lse=None, score_mode: str = "none", scores=None, softmax_scale: float = None,
+                      k_scale: float = 1.0, v_scale: float = 1.0, score_size: int = 64):
+    lib = _lib.load()
+    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), k_scale, v_scale)
+    sp = HysScoreParams(_SCORE[score_mode], score_size)
+    args = [ctypes.byref(p), tensor4(q), tensor4(k), tensor4(v), tensor4(o), _ptr(lse), ctypes.byref(sp),
+            _ptr(scores)]
+    nb = ctypes.c_size_t(0)
+    check(lib.hys_full_attn_fwd(*args, None, ctypes.byref(nb), None))
+    ws = _workspace(nb.value, q.device)
+    nb = ctypes.c_size_t(ws.numel())
+    check(lib.hys_full_attn_fwd(*args, _ptr(ws), ctypes.byref(nb), _stream(q.device)))
+    return ws
+
+
+def hys_select_topk(scores: torch.Tensor, k: int, idx: torch.Tensor, count: Optional[torch.Tensor] = None):
+    """scores: 2-D fp32 [rows, cols] (row stride from the tensor); idx [rows, k] int32 contiguous."""
+    lib = _lib.load()
+    rows, cols = scores.shape
+    args = [_ptr(scores), rows, cols, scores.stride(0) if rows > 0 else cols, k, _ptr(idx), _ptr(count)]
+    nb = ctypes.c_size_t(0)
+    check(lib.hys_select_topk(*args, None, ctypes.byref(nb), None))
+    ws = _workspace(nb.value, scores.device)
+    nb = ctypes.c_size_t(ws.numel())
+    check(lib.hys_select_topk(*args, _ptr(ws), ctypes.byref(nb), _stream(scores.device)))
+    return ws
+
+
+def hys_sparse_attn_fwd(q, k, v, idx, o, lse=None, granularity: int = 64, topk: int = None, q_tile: int = 1,
+                        forced_window: int = 0, softmax_scale: float = None, k_scale: float = 1.0,
+                        v_scale: float = 1.0):
+    """idx: [B, R, topk] int32 (R = L for q_tile 1, ceil(L/64) for q_tile 64)."""
+    lib = _lib.load()
+    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), k_scale, v_scale)
+    kk = idx.shape[-1] if topk is None else topk
+    sp = HysSparseParams(granularity, kk, q_tile, forced_window, idx.stride(0), idx.stride(1))
+    check(lib.hys_sparse_attn_fwd(ctypes.byref(p), tensor4(q), tensor4(k), tensor4(v), ctypes.byref(sp), _ptr(idx),
+                                  tensor4(o), _ptr(lse), None, None, _stream(q.device)))
+
+
+def hys_swa_gate_fwd(q, k_win, v_win, window: int, o_sparse, lse_sparse, gate_w, o, gate_b=None,
+                     softmax_scale: float = None):
+    lib = _lib.load()
+    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), 1.0, 1.0)
+    check(lib.hys_swa_gate_fwd(ctypes.byref(p), tensor4(q), tensor4(k_win), tensor4(v_win), window,
+                               tensor4(o_sparse), _ptr(lse_sparse), _ptr(gate_w), _ptr(gate_b), tensor4(o),
+                               _stream(q.device)))
+
+
+def hys_decode_step(q_full, k_cache, v_cache, cache_len: Sequence[int], o_full, token_scores, idx,
+                    q_sparse: Sequence[torch.Tensor], o_sparse: Sequence[torch.Tensor], topk: int, window: int,
+                    softmax_scale: float = None, k_scale: float = 1.0, v_scale: float = 1.0,
+                    workspace: Optional[torch.Tensor] = None):
+    """Returns the workspace tensor so callers can reuse it across steps."""
+    lib = _lib.load()
+    p = HysDecodeParams(softmax_scale or 1.0 / math.sqrt(q_full.shape[-1]), k_scale, v_scale, topk, window)
+    lens = (ctypes.c_int64 * len(cache_len))(*[int(x) for x in cache_len])
+    n = len(q_sparse)
+    qs = (HysTensor4 * max(n, 1))(*[tensor4(t) for t in q_sparse])
+    os_ = (HysTensor4 * max(n, 1))(*[tensor4(t) for t in o_sparse])
+    args = [ctypes.byref(p), tensor4(q_full), tensor4(k_cache), tensor4(v_cache), lens, tensor4(o_full),
+            _ptr(token_scores), _ptr(idx), n, qs, os_]
+    nb = ctypes.c_size_t(0)
+    check(lib.hys_decode_step(*args, None, ctypes.byref(nb), None))
+    if workspace is None or workspace.numel() < nb.value:
+        workspace = _workspace(nb.value, q_full.device)
+    nb2 = ctypes.c_size_t(workspace.numel())
+    check(lib.hys_decode_step(*args, _ptr(workspace), ctypes.byref(nb2), _stream(q_full.device)))
+    return workspace
+
+
+def abi_version() -> int:
+    return _lib.load().hys_abi_version()

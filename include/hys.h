@@ -1,0 +1,246 @@
+/*
+ * hys.h - C ABI of the HySparse / HySparse2 hybrid-block attention hot path
+ *         for AMD Instinct MI355X (gfx950).
+ *
+ * A hybrid block is one causal full-attention layer followed by N sparse
+ * layers that reuse the full layer's KV cache and its top-k indices
+ * (QbitAI HySparse article, method section; airebao HySparse2 news, inner
+ * KV Reuse paragraph).  The five entry points below are the steps of that
+ * block:
+ *
+ *   hys_full_attn_fwd   - the full layer: exact causal attention that also
+ *                         emits importance scores as a byproduct
+ *   hys_select_topk     - top-k of each importance row
+ *   hys_sparse_attn_fwd - a sparse layer's attention over the selected blocks
+ *                         or tokens of the shared KV (HySparse2: plus the
+ *                         forced recent window)
+ *   hys_swa_gate_fwd    - HySparse's sliding-window branch fused with the
+ *                         sigmoid gate that merges it with the sparse branch
+ *   hys_decode_step     - one HySparse2 decode step against a long fp8 cache
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Memory:   every tensor pointer is device memory owned by the caller (for
+ *           example allocated by PyTorch).  The library allocates nothing,
+ *           keeps no pointer after returning and holds no global mutable state.
+ *           Inputs are only read; outputs are fully overwritten.
+ * Streams:  work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *           stream) and the call returns without waiting.  Keep every buffer
+ *           alive until the stream has finished the work.
+ * Layout:   hys_tensor4 describes a [B, T, H, D] tensor (batch, token, head,
+ *           head dim) with strides in elements; the head-dim stride must be
+ *           1, and D must be 64 or 128.
+ * Types:    Q is fp32 or bf16.  K/V are of Q's type, or OCP fp8 e4m3fn when Q
+ *           is bf16 (the stored value is decode(byte) * k_scale / v_scale).
+ *           Arithmetic is fp32 accumulation on MFMA: fp32 x fp32 for fp32
+ *           inputs; bf16 x bf16 otherwise, with softmax probabilities rounded
+ *           to bf16 before the P*V product.
+ * Workspace:calls that take (ws, ws_bytes) follow one rule: a call with
+ *           ws == NULL is a size query - it stores the required size in
+ *           *ws_bytes and returns HYS_OK without touching the GPU.  To run,
+ *           pass ws != NULL (16-byte aligned device memory) with *ws_bytes at
+ *           least the required size; when that size is 0 any non-NULL ws
+ *           will do.  hys_sparse_attn_fwd needs no workspace and also runs
+ *           with ws == NULL and ws_bytes == NULL.
+ * Errors:   arguments are validated before any GPU work.  A failing call
+ *           returns a non-zero hys_status, enqueues nothing, and
+ *           hys_last_error() returns a message for the calling thread.  It
+ *           never aborts and never throws.  Faults inside kernels surface at
+ *           the caller's next stream synchronisation.
+ * Threads:  the library is stateless; concurrent calls on different streams
+ *           are safe.
+ */
+#ifndef HYS_H_
+#define HYS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HYS_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define HYS_API __attribute__((visibility("default")))
+#else
+#define HYS_API
+#endif
+
+typedef enum {
+  HYS_OK = 0,
+  HYS_ERR_INVALID_ARG = 1,  /* null pointer, bad shape/stride/size, inconsistent tensors */
+  HYS_ERR_UNSUPPORTED = 2,  /* valid request outside what the kernels implement */
+  HYS_ERR_WORKSPACE = 3,    /* *ws_bytes smaller than required */
+  HYS_ERR_HIP = 4,          /* a HIP launch failed */
+  HYS_ERR_INTERNAL = 5
+} hys_status;
+
+typedef enum { HYS_F32 = 0, HYS_BF16 = 1, HYS_FP8_E4M3 = 2 } hys_dtype;
+
+typedef struct {
+  void* ptr;          /* device pointer to element [0,0,0,0] */
+  int32_t dtype;      /* hys_dtype */
+  int64_t shape[4];   /* [B, T, H, D] */
+  int64_t stride[4];  /* element strides; stride[3] must be 1 */
+} hys_tensor4;
+
+typedef struct {
+  float softmax_scale;  /* multiplies q.k, normally 1/sqrt(D) */
+  float k_scale;        /* fp8 K dequantisation scale (1 for fp32/bf16) */
+  float v_scale;        /* fp8 V dequantisation scale (1 for fp32/bf16) */
+} hys_attn_params;
+
+typedef enum {
+  HYS_SCORE_NONE = 0,
+  HYS_SCORE_BLOCK = 1,      /* HySparse: per (query, key block) */
+  HYS_SCORE_TILE_TOKEN = 2  /* HySparse2: per (query tile, key token) */
+} hys_score_mode;
+
+typedef struct {
+  int32_t mode;  /* hys_score_mode */
+  int32_t size;  /* key-block size (BLOCK) or query-tile size (TILE_TOKEN); must be 64 */
+} hys_score_params;
+
+typedef struct {
+  int32_t granularity;    /* 64: idx holds key-block ids; 1: idx holds token positions */
+  int32_t k;              /* entries per idx row */
+  int32_t q_tile;         /* queries sharing one idx row: 1 (with granularity 64) or 64 (with granularity 1) */
+  int32_t forced_window;  /* granularity 1 only: the recent-token window forced into every query's set (0 = none) */
+  int64_t idx_batch_stride;  /* elements between batches of idx */
+  int64_t idx_row_stride;    /* elements between idx rows */
+} hys_sparse_params;
+
+typedef struct {
+  float softmax_scale;
+  float k_scale, v_scale;
+  int32_t topk;    /* tokens selected from the full layer's token scores */
+  int32_t window;  /* recent tokens forced into every sparse layer's set */
+} hys_decode_params;
+
+/*
+ * hys_full_attn_fwd - the full-attention layer of a hybrid block.
+ *
+ * Computes exact causal scaled dot-product attention
+ *   O[b,i,h,:] = sum_{j<=i} softmax_j(S[b,h,i,:]) V[b,j,h/G,:],
+ *   S[b,h,i,j] = softmax_scale * k_scale * <Q[b,i,h,:], K[b,j,h/G,:]>,
+ * with G = Hq/Hkv query heads per KV head, and LSE[b,h,i] = ln sum_{j<=i} exp(S).
+ * As its byproduct it emits importance scores taken from the same logits, the
+ * maxima the online softmax already tracks (TechWalker HySparse write-up,
+ * paragraph on the modified FlashAttention kernel):
+ *   HYS_SCORE_BLOCK:      scores[b,i,c] = max_h max_{j in block c, j<=i} S[b,h,i,j]
+ *                         (64-key blocks: airebao HySparse2 news, token-level
+ *                         selection paragraph), -inf for blocks after i;
+ *                         layout [B, Lq, ceil(Lk/64)] contiguous.
+ *   HYS_SCORE_TILE_TOKEN: scores[b,t,j] = max_h max_{i in tile t, i>=j} S[b,h,i,j]
+ *                         (token-level importance of HySparse2, one row per
+ *                         64-query tile), -inf for keys after the tile;
+ *                         layout [B, ceil(Lq/64), Lk] contiguous.
+ * The max over heads spans all query heads, so one index set serves every KV
+ * head.
+ *
+ * q [B, L, Hq, D]; k, v [B, L, Hkv, D] (self-attention: Lq = Lk = L).
+ * o [B, L, Hq, D] fp32 or bf16.  lse [B, Hq, L] fp32 or NULL.
+ * sp may be NULL (no scores); scores must be non-NULL when sp->mode != NONE.
+ * Workspace: BLOCK mode with Hkv > 1 needs Hkv * B * L * ceil(L/64) floats.
+ */
+HYS_API hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v,
+                             hys_tensor4 o, float* lse, const hys_score_params* sp, float* scores,
+                             void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * hys_select_topk - the k largest entries of each row of a score matrix.
+ *
+ * The sparse layers attend to the top-k blocks/tokens of the full layer's
+ * importance (QbitAI HySparse article, method section; TechWalker write-up).
+ * Order: score descending, then column ascending (the lowest column wins a
+ * tie).  Only entries > -inf are candidates (NaN and -inf are never chosen).
+ * idx[r, 0..k) receives the chosen columns in ascending order, padded with
+ * -1; count[r] (if non-NULL) the number chosen.  Selection is exact.
+ *
+ * scores: rows x cols fp32 with row_stride (elements, >= cols).
+ * idx: rows x k int32, contiguous.  Limits: cols < 2^31; k <= 4096; rows with
+ * more than 65536 columns are split into 65536-column chunks, requiring
+ * ceil(cols/65536) * k <= 65536, and need workspace.
+ */
+HYS_API hys_status hys_select_topk(const float* scores, int64_t rows, int64_t cols, int64_t row_stride, int32_t k,
+                           int32_t* idx, int32_t* count, void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * hys_sparse_attn_fwd - a sparse layer's global attention over the shared KV.
+ *
+ * The sparse layer attends with its own query q to the full layer's K/V at the
+ * selected positions (QbitAI HySparse article, method section; TechWalker
+ * write-up: the selected KV blocks form a sparse KV matrix).
+ *   granularity 64 (HySparse): idx[b,i,:] lists key-block ids for query i;
+ *       J(i) = { j <= i : j/64 in idx[b,i,:] }.
+ *   granularity 1, q_tile 64 (HySparse2): idx[b,t,:] lists token positions for
+ *       the 64 queries of tile t, and the most recent forced_window tokens are
+ *       added (airebao HySparse2 news, forced recent window paragraph):
+ *       J(i) = { j in idx[b,i/64,:] : j <= i }  U  [max(0, i-forced_window+1), i].
+ * O[b,i,h,:] = softmax over J(i) of S, applied to V; lse[b,h,i] likewise
+ * (-inf when J(i) is empty, with O = 0).  Entries < 0 are ignored; entries of
+ * a row must be distinct (hys_select_topk guarantees this).
+ * o [B, L, Hq, D] fp32 or bf16; lse [B, Hq, L] fp32 or NULL.
+ * Limits: granularity 64 needs k <= 64 and ceil(L/64) <= 16384; granularity 1
+ * needs k <= 2048 and forced_window <= 1984.  No workspace is used.
+ */
+HYS_API hys_status hys_sparse_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v,
+                               const hys_sparse_params* sp, const int32_t* idx, hys_tensor4 o, float* lse,
+                               void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * hys_swa_gate_fwd - HySparse's local branch and the gate.
+ *
+ * Sliding-window attention of q over the layer's own window cache
+ * (k_win, v_win), window [max(0,i-window+1), i] (QbitAI HySparse article:
+ * window 128; TechWalker write-up: the most recent 128 tokens, own KV), fused
+ * with the sigmoid gate that merges it with the sparse branch:
+ *   z = <q[b,i,h,:], gate_w[h,:]> (+ gate_b[h]),  g = 1/(1+exp(-z)),
+ *   o = g * o_sparse + (1-g) * O_window,
+ * and o = O_window where lse_sparse = -inf (empty sparse set).
+ * q [B, L, Hq, D]; k_win, v_win [B, L, Hkv, D] of q's type; o_sparse fp32
+ * [B, L, Hq, D]; lse_sparse [B, Hq, L]; gate_w [Hq, D] fp32; gate_b [Hq] or
+ * NULL; o [B, L, Hq, D] fp32 or bf16.
+ */
+HYS_API hys_status hys_swa_gate_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k_win, hys_tensor4 v_win,
+                            int32_t window, hys_tensor4 o_sparse, const float* lse_sparse, const float* gate_w,
+                            const float* gate_b, hys_tensor4 o, void* stream);
+
+/*
+ * hys_decode_step - one HySparse2 decode step (airebao HySparse2 news:
+ * token-level selection, forced recent window, MQA, 1M-token FP8 cache).
+ *
+ * For each sequence b with valid cache length n = cache_len[b] (the cache
+ * already holds the new token at position n-1):
+ *   full layer:   o_full[b,0,h,:] = attention of q_full[b,0,h,:] over keys [0, n);
+ *                 token_scores[b,j] = max_h S[b,h,j] for j < n, -inf for j >= n;
+ *   selection:    idx[b,:] = top-topk of token_scores[b,:] (ascending, -1 padded);
+ *   sparse layers l = 0..n_sparse-1:
+ *                 o_sparse[l][b,0,h,:] = attention of q_sparse[l][b,0,h,:] over
+ *                 idx[b,:] U [max(0, n-window), n-1], all over the same cache.
+ * q_full and q_sparse[l]: [B, 1, Hq, D] bf16, all q_sparse with equal strides.
+ * k_cache, v_cache: [B, Nmax, 1, D] fp8 e4m3fn or bf16 (MQA: one KV head).
+ * cache_len: HOST array of B lengths, 1 <= n <= Nmax.
+ * o_full, o_sparse[l]: [B, 1, Hq, D] fp32 or bf16 (all of one type).
+ * token_scores: [B, Nmax] fp32 (required).  idx: [B, topk] int32.
+ * Limits: Hq <= 64, B <= 64, n_sparse <= 16, topk <= 2048.
+ * Workspace: split partials, top-k candidates (query with ws == NULL).
+ */
+HYS_API hys_status hys_decode_step(const hys_decode_params* p, hys_tensor4 q_full, hys_tensor4 k_cache,
+                           hys_tensor4 v_cache, const int64_t* cache_len, hys_tensor4 o_full, float* token_scores,
+                           int32_t* idx, int32_t n_sparse, const hys_tensor4* q_sparse,
+                           const hys_tensor4* o_sparse, void* ws, size_t* ws_bytes, void* stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+HYS_API const char* hys_last_error(void);
+/* Static name of a status code. */
+HYS_API const char* hys_status_string(hys_status s);
+/* HYS_ABI_VERSION of the built library. */
+HYS_API int hys_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HYS_H_ */

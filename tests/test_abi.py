@@ -1,0 +1,125 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and
+rejects invalid arguments with the documented status before any GPU work.
+
+No call here reaches a kernel launch: every case fails validation or is a
+workspace-size query, so the tests run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hybrid_sparse_attention_flash_amd import _lib
+from hybrid_sparse_attention_flash_amd._lib import (HysAttnParams, HysDecodeParams, HysScoreParams, HysSparseParams,
+                                                    HysTensor4)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+FAKE = 0x7f0000000000          # 16-byte aligned, never dereferenced (validation fails first)
+
+
+def lib():
+    return _lib.load()
+
+
+def t4(shape, dtype=1, strides=None, ptr=FAKE):
+    t = HysTensor4()
+    t.ptr = ptr
+    t.dtype = dtype
+    if strides is None:
+        strides = [shape[1] * shape[2] * shape[3], shape[2] * shape[3], shape[3], 1]
+    for i in range(4):
+        t.shape[i] = shape[i]
+        t.stride[i] = strides[i]
+    return t
+
+
+def test_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "hys.h")).read()
+    declared = set(re.findall(r"HYS_API[^;]*?\b(hys_\w+)\(", hdr))
+    assert declared == set(_lib.EXPORTED)
+    for name in declared:
+        assert hasattr(lib(), name)
+    assert lib().hys_abi_version() == 1
+    assert lib().hys_status_string(3) == b"HYS_ERR_WORKSPACE"
+
+
+def _full(p, q, k, v, o, sp=None, scores=None, ws=None, nb=None):
+    nb = nb if nb is not None else ctypes.c_size_t(0)
+    return lib().hys_full_attn_fwd(ctypes.byref(p), q, k, v, o, None, ctypes.byref(sp) if sp else None,
+                                   scores, ws, ctypes.byref(nb), None)
+
+
+def test_full_attn_validation():
+    p = HysAttnParams(0.125, 1.0, 1.0)
+    q, kv = t4([1, 128, 8, 128]), t4([1, 128, 2, 128])
+    o = t4([1, 128, 8, 128], dtype=0)
+    assert _full(p, HysTensor4(), kv, kv, o) == INVALID
+    assert b"null" in lib().hys_last_error()
+    assert _full(p, t4([1, 128, 8, 96]), t4([1, 128, 2, 96]), t4([1, 128, 2, 96]), t4([1, 128, 8, 96])) == UNSUPPORTED
+    assert _full(p, q, t4([1, 128, 3, 128]), t4([1, 128, 3, 128]), o) == INVALID          # Hq % Hkv
+    assert _full(p, q, t4([1, 128, 2, 128], strides=[0, 0, 128, 2]), kv, o) == INVALID   # d stride
+    assert _full(p, q, kv, kv, t4([1, 127, 8, 128], dtype=0)) == INVALID                 # o shape
+    assert _full(p, t4([1, 128, 8, 128], ptr=FAKE + 4), kv, kv, o) == INVALID            # alignment
+    assert _full(p, q, t4([1, 128, 2, 128], dtype=0), t4([1, 128, 2, 128], dtype=0), o) == UNSUPPORTED  # bf16 q, f32 kv
+    assert _full(HysAttnParams(float("nan"), 1, 1), q, kv, kv, o) == INVALID
+    sp = HysScoreParams(1, 32)
+    assert _full(p, q, kv, kv, o, sp, ctypes.c_void_p(FAKE)) == UNSUPPORTED               # block size 32
+    sp = HysScoreParams(1, 64)
+    assert _full(p, q, kv, kv, o, sp, None) == INVALID                                    # scores missing
+    # workspace query: 2 KV groups x B x L x nblk floats
+    nb = ctypes.c_size_t(0)
+    assert _full(p, q, kv, kv, o, sp, ctypes.c_void_p(FAKE), None, nb) == 0
+    assert nb.value == 2 * 1 * 128 * 2 * 4
+    nb = ctypes.c_size_t(16)
+    assert _full(p, q, kv, kv, o, sp, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), nb) == WORKSPACE
+
+
+def test_topk_validation():
+    L = lib()
+    nb = ctypes.c_size_t(0)
+    assert L.hys_select_topk(None, 4, 10, 10, -1, None, None, None, ctypes.byref(nb), None) == INVALID
+    assert L.hys_select_topk(None, 4, 10, 5, 3, None, None, None, ctypes.byref(nb), None) == INVALID
+    assert L.hys_select_topk(None, 4, 10, 10, 5000, None, None, None, ctypes.byref(nb), None) == UNSUPPORTED
+    assert L.hys_select_topk(None, 4, 1 << 20, 1 << 20, 1024, None, None, None, ctypes.byref(nb), None) == 0
+    assert nb.value == 4 * 16 * 1024 * 8          # chunk winners: index + value
+    assert L.hys_select_topk(None, 4, 1 << 20, 1 << 20, 8192, None, None, None, ctypes.byref(nb), None) == UNSUPPORTED
+    nb = ctypes.c_size_t(0)
+    assert L.hys_select_topk(None, 4, 100, 100, 8, None, None, ctypes.c_void_p(FAKE), ctypes.byref(nb), None) == INVALID
+
+
+def test_sparse_validation():
+    p = HysAttnParams(0.125, 1.0, 1.0)
+    q, kv, o = t4([1, 128, 8, 128]), t4([1, 128, 1, 128]), t4([1, 128, 8, 128], dtype=0)
+
+    def call(sp, idx=FAKE):
+        return lib().hys_sparse_attn_fwd(ctypes.byref(p), q, kv, kv, ctypes.byref(sp), ctypes.c_void_p(idx), o,
+                                         None, None, None, None)
+    assert call(HysSparseParams(32, 4, 1, 0, 512, 4)) == UNSUPPORTED
+    assert call(HysSparseParams(64, 4, 64, 0, 512, 4)) == UNSUPPORTED
+    assert call(HysSparseParams(64, 65, 1, 0, 512 * 65, 65)) == UNSUPPORTED
+    assert call(HysSparseParams(64, 4, 1, 0, 512, 2)) == INVALID
+    assert call(HysSparseParams(1, 4096, 64, 128, 8192, 4096)) == UNSUPPORTED
+    assert call(HysSparseParams(1, 16, 64, 4000, 32, 16)) == UNSUPPORTED
+    assert call(HysSparseParams(64, 4, 1, 0, 512, 4), idx=0) == INVALID
+
+
+def test_decode_validation():
+    p = HysDecodeParams(0.088, 0.01, 0.01, 1024, 128)
+    qf = t4([4, 1, 64, 128])
+    kc = t4([4, 1 << 20, 1, 128], dtype=2)
+    o = t4([4, 1, 64, 128], dtype=0)
+    lens = (ctypes.c_int64 * 4)(1 << 20, 1 << 20, 5, 1 << 20)
+    nb = ctypes.c_size_t(0)
+
+    def call(pp=p, q=qf, k=kc, ln=lens, n_sparse=0):
+        return lib().hys_decode_step(ctypes.byref(pp), q, k, k, ln, o, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                                     n_sparse, None, None, None, ctypes.byref(nb), None)
+    assert call() == 0 and nb.value > 0
+    assert call(k=t4([4, 1 << 20, 2, 128], dtype=2)) == UNSUPPORTED          # not MQA
+    assert call(q=t4([4, 1, 128, 128])) == INVALID or call(q=t4([4, 1, 128, 128])) == UNSUPPORTED
+    bad = (ctypes.c_int64 * 4)(0, 1, 2, 3)
+    assert call(ln=bad) == INVALID
+    assert call(pp=HysDecodeParams(0.088, 0.01, 0.01, 4096, 128)) == UNSUPPORTED
+    assert call(n_sparse=3) == INVALID                                        # null q_sparse
