@@ -1,0 +1,303 @@
+"""Benchmark of the HySparse hybrid-block hot path on one MI355X.
+
+Timed step: one HySparse hybrid block on the 80B-MoE-like 32k workload
+(B=1, L=32768, 32 query heads, 4 KV heads, head dim 128, bf16; 1 full layer +
+11 sparse layers; top-16 of 64-token blocks; window 128; 32 needle keys x4):
+  full attention + block scores -> top-k -> 11 x (block-sparse attention,
+  window attention + sigmoid gate).
+Value: prefill tokens/s of that block (L / step time).  Also reported: the
+HySparse2 1M-token decode step (B=4, fp8 MQA cache, top-1024 + recent 128,
+11 sparse layers) in microseconds per step, per-kernel times from HIP events
+on the launch stream, the roofline of the dominant kernel, and the CPU oracle
+timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from hybrid_sparse_attention_flash_amd import ops  # noqa: E402
+from hybrid_sparse_attention_flash_amd.block import HySparse2Decode, HySparseBlock  # noqa: E402
+
+METRIC = ("hybrid-block prefill tokens/s at 32k (TFLOP/s, GB/s % peak); decode us/token at 1M")
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work
+# ---------------------------------------------------------------------------
+
+def full_attention_flops(w):
+    L = w.L
+    return 4.0 * w.D * w.Hq * L * (L + 1) / 2 * w.B
+
+
+def sparse_keys_per_query(idx, L, block):
+    """Number of visible selected keys per query from the returned block ids."""
+    i = torch.arange(L, device=idx.device, dtype=torch.int64).view(1, L, 1)
+    c = idx.to(torch.int64)
+    valid = c >= 0
+    start = c * block
+    n = torch.clamp(torch.minimum(i + 1 - start, torch.full_like(start, block)), min=0)
+    return (n * valid).sum().item()
+
+
+# ---------------------------------------------------------------------------
+# timing helpers
+# ---------------------------------------------------------------------------
+
+class Timer:
+    """Accumulates HIP-event intervals per stage on the current stream."""
+
+    def __init__(self):
+        self.events = {}
+
+    def span(self, name):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        self.events.setdefault(name, []).append((s, e))
+        return s, e
+
+    def totals_ms(self):
+        torch.cuda.synchronize()
+        return {k: sum(s.elapsed_time(e) for s, e in v) for k, v in self.events.items()}
+
+    def counts(self):
+        return {k: len(v) for k, v in self.events.items()}
+
+
+def run_block(blk, inp, timer=None):
+    def rec(name, fn):
+        if timer is None:
+            fn()
+        else:
+            s, e = timer.span(name)
+            s.record()
+            fn()
+            e.record()
+    q, k, v, kw, vw, gw = inp
+    rec("full_attn+scores", lambda: blk.full(q[0], k, v))
+    rec("select_topk", blk.select)
+    for l in range(blk.n_sparse):
+        rec("sparse_attn", lambda: ops.hys_sparse_attn_fwd(q[l + 1], k, v, blk.idx, blk.o_sp, blk.lse_sp,
+                                                           granularity=64, topk=blk.topk, q_tile=1))
+        rec("swa_gate", lambda: ops.hys_swa_gate_fwd(q[l + 1], kw[l], vw[l], blk.window, blk.o_sp, blk.lse_sp,
+                                                     gw[l], blk.o_layers[l]))
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+
+class _RowView:
+    """Array stand-in that converts only the indexed query rows to float64."""
+
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, rows):
+        return self.t[torch.as_tensor(np.asarray(rows))].to(torch.float64).numpy()
+
+
+def cpu_baseline(w, host, nrows, seed=0):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    q, k, v, kw, vw, gw = host
+    f = lambda t: t[0].to(torch.float64).numpy()
+    kf, vf = f(k), f(v)
+    kwf = [f(x) for x in kw]
+    vwf = [f(x) for x in vw]
+    gwf = [x.numpy().astype(np.float64) for x in gw]
+    qv = [_RowView(x[0]) for x in q]
+    rows = np.linspace(0, w.L - 1, nrows).round().astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.hysparse_block(qv, kf, vf, kwf, vwf, gwf, w.scale, w.block, w.topk, w.window, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": nrows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{nrows} query rows spread evenly over L={w.L} of the same block "
+                      f"(full layer row + block scores + top-{w.topk} + {w.n_sparse} gated sparse layers), "
+                      f"{dt:.1f} s wall"}
+
+
+# ---------------------------------------------------------------------------
+
+def bench_prefill(args, dev):
+    w = synth.WORKLOADS["moe80b_32k"]
+    log(f"[bench] generating {w.name} inputs (L={w.L}, {w.n_sparse + 1} layers)")
+    t0 = time.time()
+    q_h = [synth.gen_q(w, l) for l in range(w.n_sparse + 1)]
+    k_h, _ = synth.gen_kv(w, "k")
+    v_h, _ = synth.gen_kv(w, "v")
+    kw_h = [synth.gen_window_kv(w, l + 1, "kw")[0] for l in range(w.n_sparse)]
+    vw_h = [synth.gen_window_kv(w, l + 1, "vw")[0] for l in range(w.n_sparse)]
+    gw_h = [synth.gen_gate_w(w, l + 1) for l in range(w.n_sparse)]
+    log(f"[bench] inputs generated in {time.time() - t0:.1f} s; uploading")
+    inp = ([x.to(dev) for x in q_h], k_h.to(dev), v_h.to(dev), [x.to(dev) for x in kw_h],
+           [x.to(dev) for x in vw_h], [x.to(dev) for x in gw_h])
+    blk = HySparseBlock(w.B, w.L, w.Hq, w.Hkv, w.D, w.n_sparse, w.topk, w.window, device=dev,
+                        out_dtype=torch.bfloat16)
+    for i in range(args.warmup):
+        run_block(blk, inp)
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+    timer = Timer()
+    torch.cuda.synchronize()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    g0.record()
+    for i in range(args.steps):
+        run_block(blk, inp, timer)
+    g1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = g0.elapsed_time(g1) / args.steps
+    log(f"[bench] {args.steps} steps: {step_ms:.3f} ms/step (wall {wall * 1000 / args.steps:.3f})")
+    tot = timer.totals_ms()
+    per_step = {k: v / args.steps for k, v in tot.items()}
+    launches = {k: c // args.steps for k, c in timer.counts().items()}
+
+    # algorithmic work of the step
+    fl_full = full_attention_flops(w)
+    keys_sel = sparse_keys_per_query(blk.idx, w.L, w.block) * w.Hq      # per sparse layer, all heads
+    fl_sparse = 4.0 * w.D * keys_sel
+    win_keys = sum(min(i + 1, w.window) for i in range(w.L)) * w.Hq * w.B
+    fl_swa = 4.0 * w.D * win_keys
+    tflops = {
+        "full_attn+scores": fl_full / (per_step["full_attn+scores"] * 1e-3) / 1e12,
+        "sparse_attn": w.n_sparse * fl_sparse / (per_step["sparse_attn"] * 1e-3) / 1e12,
+        "swa_gate": w.n_sparse * fl_swa / (per_step["swa_gate"] * 1e-3) / 1e12,
+    }
+    # logical gathered K/V bytes of the sparse branch per layer (per KV head reading of each query's keys)
+    gather_bytes = keys_sel / w.G * w.D * 2 * 2
+    stages = {k: {"ms_per_step": round(per_step[k], 4), "launches_per_step": launches[k]} for k in per_step}
+    for k, v in tflops.items():
+        stages[k]["tflops"] = round(v, 2)
+        stages[k]["frac_mfma_bf16"] = round(v / PEAK_BF16_TFLOPS, 4)
+    stages["sparse_attn"]["logical_gather_GBs"] = round(
+        w.n_sparse * gather_bytes / (per_step["sparse_attn"] * 1e-3) / 1e9, 1)
+
+    # roofline of the dominant kernel (largest share of the step)
+    dom = max(["full_attn+scores", "sparse_attn", "swa_gate"], key=lambda k: per_step[k])
+    if dom == "full_attn+scores":
+        ach = tflops[dom]
+        roof = {"kernel": "full_attn (causal + block scores)", "bound": "mfma", "achieved": round(ach, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "avg_launch_ms": round(per_step[dom] / launches[dom], 4),
+                "work_per_launch": f"{fl_full:.4g} FLOP", "traffic": None}
+    elif dom == "sparse_attn":
+        ach = gather_bytes / (per_step[dom] / launches[dom] * 1e-3) / 1e9
+        roof = {"kernel": "sparse_attn (block gather)", "bound": "hbm", "achieved": round(ach, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                "avg_launch_ms": round(per_step[dom] / launches[dom], 4),
+                "work_per_launch": f"{gather_bytes:.4g} logical gathered bytes", "traffic": None}
+    else:
+        byts = (w.L * w.Hq * w.D * (2 + 4 + 2) + 2 * w.L * w.Hkv * w.D * 2)
+        ach = byts / (per_step[dom] / launches[dom] * 1e-3) / 1e9
+        roof = {"kernel": "swa_gate", "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                "avg_launch_ms": round(per_step[dom] / launches[dom], 4),
+                "work_per_launch": f"{byts:.4g} bytes", "traffic": None}
+    res = {"w": w, "step_ms": step_ms, "stages": stages, "roofline": roof,
+           "host": (q_h, k_h, v_h, kw_h, vw_h, gw_h)}
+    del inp, blk
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(args, dev):
+    w = synth.WORKLOADS["decode_1m"]
+    log(f"[bench] generating {w.name} inputs (B={w.B}, N={w.L}, fp8 cache)")
+    qf = synth.gen_q(w, 0).to(dev)
+    qs = [synth.gen_q(w, l + 1).to(dev) for l in range(w.n_sparse)]
+    kc, ks = synth.gen_kv(w, "k")
+    kc = kc.to(dev)
+    vc, vs = synth.gen_kv(w, "v")
+    vc = vc.to(dev)
+    dec = HySparse2Decode(w.B, w.L, w.Hq, w.D, w.n_sparse, w.topk, w.window, device=dev)
+    lens = w.lens()
+    for _ in range(max(3, args.warmup)):
+        dec.run(qf, kc, vc, lens, qs, ks, vs)
+    torch.cuda.synchronize()
+    steps = max(20, args.steps * 5)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dec.run(qf, kc, vc, lens, qs, ks, vs)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000 / steps
+    kv_bytes = 2.0 * sum(lens) * w.D          # fp8 K + V streamed by the full layer
+    gbs = kv_bytes / (us * 1e-6) / 1e9
+    log(f"[bench] decode: {us:.1f} us/step, full-layer KV stream {gbs:.0f} GB/s equivalent")
+    return {"workload": w.name, "us_per_step": round(us, 2), "us_per_token": round(us / w.B, 2),
+            "batch": w.B, "cache_tokens": w.L, "kv_stream_GBs_step_equiv": round(gbs, 1),
+            "frac_hbm_step_equiv": round(gbs / PEAK_HBM_GBS, 4), "steps": steps}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=64)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the hot path is built for a single MI355X and has no "
+              "multi-GPU mode (see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda:0"
+    ops.abi_version()      # fail loudly if libhys.so is missing
+    pre = bench_prefill(args, dev)
+    w = pre["w"]
+    dec = None if args.no_decode else bench_decode(args, dev)
+    cpu = None
+    if not args.no_cpu:
+        log(f"[bench] timing the CPU oracle on {args.cpu_rows} sampled rows")
+        cpu = cpu_baseline(w, pre["host"], args.cpu_rows)
+        log(f"[bench] oracle: {cpu['value']:.2f} tokens/s on {cpu['cores']} threads")
+    tok_s = w.L * w.B / (pre["step_ms"] * 1e-3)
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(pre["step_ms"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16; 32 needle keys x4)",
+        "config": {"workload": w.name, "batch": w.B, "seq_len": w.L, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.D, "layers": f"1 full + {w.n_sparse} sparse", "topk_blocks": w.topk,
+                   "block": w.block, "window": w.window},
+        "roofline": pre["roofline"],
+        "cpu_baseline": cpu,
+        "stages": pre["stages"],
+        "decode": dec,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

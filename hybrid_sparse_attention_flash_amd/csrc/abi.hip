@@ -406,13 +406,14 @@ hys_status hys_decode_step(const hys_decode_params* p, hys_tensor4 q_full, hys_t
           o_sparse[l].stride[2] != o_sparse[0].stride[2])
         return fail(HYS_ERR_UNSUPPORTED, "all o_sparse must share dtype and strides");
     }
+    // split-K: about 4 two-wave workgroups per CU, at least 8 key tiles each
     const int64_t ntiles = (Nmax + 63) / 64;
-    int nsplit = (int)(256 / B);
+    int nsplit = (int)(1024 / B);
     if (nsplit < 1) nsplit = 1;
-    if ((int64_t)nsplit * 4 > ntiles) nsplit = (int)((ntiles + 3) / 4);
+    if ((int64_t)nsplit * 8 > ntiles) nsplit = (int)((ntiles + 7) / 8);
     const int nsplit_env = env_int("HYS_DECODE_SPLIT", 0);
     if (nsplit_env > 0) nsplit = nsplit_env;
-    const int nsplit_sp = 4;
+    const int nsplit_sp = 8;
     const size_t part_full = (size_t)(B * nsplit * Hq) * (size_t)(D + 2) * sizeof(float);
     const size_t part_sp = (size_t)((int64_t)n_sparse * B * nsplit_sp * Hq) * (size_t)(D + 2) * sizeof(float);
     const size_t tk = hys::topk_workspace_bytes(B, Nmax, p->topk);

@@ -218,17 +218,20 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
 
   Raw8<KT> kreg[KU];
   Raw8<KT> vreg[VU][4];
+  uint32_t kmask = 0u, vmask = 0u;     // staged units whose slot holds a key
   int my_kinfo = 0;
 
   auto stage_load = [&](int n, int g_) {
     const int kvh = g_;
+    kmask = 0u; vmask = 0u;
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
       const int unit = tid + 256 * u;
       const int key = unit / (D / 8), c8 = unit % (D / 8);
-      const int j = keypos(n, key) & ~(1 << 30);
-      const bool ok = keypos(n, key) >= 0;
-      kreg[u] = ok ? load8<KT>(kb + (int64_t)j * a.k_st + (int64_t)kvh * a.k_sh + c8 * 8) : zero8<KT>();
+      const int kp = keypos(n, key);
+      const int j = kp >= 0 ? (kp & ~(1 << 30)) : 0;
+      kmask |= (kp >= 0 ? 1u : 0u) << u;
+      kreg[u] = load8<KT>(kb + (int64_t)j * a.k_st + (int64_t)kvh * a.k_sh + c8 * 8);
     }
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
@@ -238,8 +241,9 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int kp = keypos(n, kg * 4 + r);
-          const int j = kp & ~(1 << 30);
-          vreg[u][r] = kp >= 0 ? load8<KT>(vb + (int64_t)j * a.v_st + (int64_t)kvh * a.v_sh + dc * 8) : zero8<KT>();
+          const int j = kp >= 0 ? (kp & ~(1 << 30)) : 0;
+          vmask |= (kp >= 0 ? 1u : 0u) << (4 * u + r);
+          vreg[u][r] = load8<KT>(vb + (int64_t)j * a.v_st + (int64_t)kvh * a.v_sh + dc * 8);
         }
       }
     }
@@ -254,6 +258,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
     for (int u = 0; u < KU; ++u) {
       const int unit = tid + 256 * u;
       const int key = unit / (D / 8), c8 = unit % (D / 8);
+      keep_if(kreg[u], (kmask >> u) & 1u);
       Cvt8<CT> c = to_ct(kreg[u]);
       CT* dst = &Klds[key * KROW + c8 * 8];
       *(uint4*)dst = c.a;
@@ -264,6 +269,8 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
       const int unit = tid + 256 * u;
       if (unit < VUN) {
         const int kg = unit / (D / 8), dc = unit % (D / 8);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) keep_if(vreg[u][r], (vmask >> (4 * u + r)) & 1u);
         Cvt8<CT> r0 = to_ct(vreg[u][0]), r1 = to_ct(vreg[u][1]), r2 = to_ct(vreg[u][2]), r3 = to_ct(vreg[u][3]);
         if constexpr (!F32) {
 #pragma unroll
@@ -336,14 +343,17 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
     QFrag qf[NB][NQC];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const QT* qr = qbase + (int64_t)qpos[nb] * a.q_st + (int64_t)head[nb] * a.q_sh;
+      // unconditional loads from a clamped row (see keep_if), zeroed for padding rows
+      const QT* qr = qbase + (valid[nb] ? (int64_t)qpos[nb] * a.q_st + (int64_t)head[nb] * a.q_sh : 0);
 #pragma unroll
       for (int c = 0; c < NQC; ++c) {
         if constexpr (F32) {
-          qf[nb][c] = valid[nb] ? qr[2 * c + hh] : 0.0f;
+          const float x = qr[2 * c + hh];
+          qf[nb][c] = valid[nb] ? x : 0.0f;
         } else {
-          uint4 z = {0u, 0u, 0u, 0u};
-          qf[nb][c] = as_bf16x8(valid[nb] ? *(const uint4*)(qr + 16 * c + 8 * hh) : z);
+          const uint4 x = *(const uint4*)(qr + 16 * c + 8 * hh);
+          const uint4 z = {0u, 0u, 0u, 0u};
+          qf[nb][c] = as_bf16x8(valid[nb] ? x : z);
         }
       }
     }

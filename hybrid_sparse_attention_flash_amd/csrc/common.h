@@ -109,6 +109,21 @@ template <> __device__ __forceinline__ Raw8<uint8_t> load8<uint8_t>(const uint8_
 }
 template <typename KT> __device__ __forceinline__ Raw8<KT> zero8() { Raw8<KT> r; __builtin_memset(&r, 0, sizeof(r)); return r; }
 
+// Zero a staged unit whose slot is empty.  Staging loads are issued
+// unconditionally from a clamped, in-bounds address (a branch around each
+// load makes the compiler wait for every earlier load before issuing the
+// next, which serialises the whole prefetch); the select happens when the
+// data is consumed.
+__device__ __forceinline__ void keep_if(Raw8<float>& r, bool ok) {
+  if (!ok) { r.a = make_uint4(0u, 0u, 0u, 0u); r.b = r.a; }
+}
+__device__ __forceinline__ void keep_if(Raw8<uint16_t>& r, bool ok) {
+  if (!ok) r.a = make_uint4(0u, 0u, 0u, 0u);
+}
+__device__ __forceinline__ void keep_if(Raw8<uint8_t>& r, bool ok) {
+  if (!ok) r.a = make_uint2(0u, 0u);
+}
+
 // 8 elements in compute layout: bf16 -> one uint4, fp32 -> two uint4
 template <typename CT> struct Cvt8;
 template <> struct Cvt8<uint16_t> { uint4 a; };

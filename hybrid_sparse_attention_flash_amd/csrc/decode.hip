@@ -26,22 +26,26 @@
 namespace hys {
 
 template <int SPARSE, typename KT, int D>
-__global__ __launch_bounds__(256) void decode_kernel(const DecArgs a) {
+__global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
+  // Workgroup = 2 waves; wave w owns query heads [32w, 32w+32) (one MFMA N-block).
+  // Both waves consume the same staged 64-key tile, so every cache byte is read
+  // once per workgroup; with at most ~256 registers per wave two workgroups'
+  // waves share each SIMD and hide each other's latency.
   constexpr int KROW = D + 8;                 // bf16 LDS row stride of K
   constexpr int VROW = 68;                    // bf16 LDS row stride of V^T
-  constexpr int WSLICE = 64 * KROW + D * VROW;
   constexpr int NDB = D / 32;
   constexpr int NQC = D / 16;
   constexpr int KUN = 64 * (D / 8);           // K units (8 elements) per tile
-  constexpr int KU = KUN / 64;                // per lane
+  constexpr int KU = KUN / 128;               // per thread
   constexpr int VUN = 16 * (D / 8);           // V units (4 keys x 8 d)
-  constexpr int VU = VUN / 64;
+  constexpr int VU = VUN / 128;
   constexpr int TLMAX = 2048;
-  static_assert(4 * WSLICE * 2 >= 4 * 64 * D * 4 + 2 * 4 * 64 * 4, "combine scratch must fit");
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * WSLICE];
+  __shared__ __attribute__((aligned(16))) uint16_t Kl[64 * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Vl[D * VROW];
+  __shared__ float red[2][2][64];
   __shared__ int s_tlist[SPARSE ? TLMAX : 1];
-  __shared__ int s_misc[8];
+  __shared__ int s_misc[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, ln = lane & 31;
   const int bid = blockIdx.x;
@@ -50,37 +54,35 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecArgs a) {
   const int b = rest % a.B;
   const int layer = rest / a.B;
   const int n = a.lens[b];
-  uint16_t* Kl = lds + wave * WSLICE;
-  uint16_t* Vl = Kl + 64 * KROW;
 
   // ---- key list ------------------------------------------------------------
-  int npre = 0, wstart = 0, nkeys = 0, ntiles_all = 0;
+  int npre = 0, wstart = 0, nkeys = 0;
   if (!SPARSE) {
     nkeys = n;
-    ntiles_all = (a.Nmax + 63) / 64;
   } else {
     wstart = max(0, n - a.window);
     const int32_t* sel = a.idx + (int64_t)b * a.idx_sb;
     int carry = 0;
-    for (int e0 = 0; e0 < a.topk; e0 += 256) {
+    for (int e0 = 0; e0 < a.topk; e0 += 128) {
       const int e = e0 + tid;
       const int sv = (e < a.topk) ? sel[e] : -1;
       const bool pre = sv >= 0 && sv < wstart;
       const unsigned long long bal = __ballot(pre);
       if (lane == 0) s_misc[wave] = __popcll(bal);
       __syncthreads();
-      int before = carry;
-      for (int w = 0; w < wave; ++w) before += s_misc[w];
+      const int before = carry + (wave ? s_misc[0] : 0);
       const int pos = before + __popcll(bal & ((1ull << lane) - 1ull));
       if (pre && pos < TLMAX) s_tlist[pos] = sv;
-      carry += s_misc[0] + s_misc[1] + s_misc[2] + s_misc[3];
+      carry += s_misc[0] + s_misc[1];
       __syncthreads();
     }
     npre = min(carry, TLMAX);
     nkeys = npre + (n - wstart);
-    ntiles_all = (nkeys + 63) / 64;
   }
-  const int ntiles_valid = (nkeys + 63) / 64;
+  const int ntiles = (nkeys + 63) / 64;
+  // this workgroup's contiguous share of the tiles
+  const int per = (ntiles + a.nsplit - 1) / a.nsplit;
+  const int t0 = s * per, t1 = min(ntiles, t0 + per);
 
   auto keyof = [&](int t, int x) -> int {     // key position of list slot 64t+x, or -1
     const int p = t * 64 + x;
@@ -89,65 +91,69 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecArgs a) {
     return p < nkeys ? wstart + (p - npre) : -1;
   };
 
-  // ---- query fragments: heads are the 64 rows (2 N-blocks of 32) -----------
+  // ---- query fragments (this wave's 32 heads) --------------------------------
   const uint16_t* qb = (const uint16_t*)a.q[layer] + (int64_t)b * a.q_sb;
-  bf16x8 qf[2][NQC];
-  bool hvalid[2];
+  const int head = wave * 32 + ln;
+  const bool hvalid = head < a.Hq;
+  bf16x8 qf[NQC];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int h = nb * 32 + ln;
-    hvalid[nb] = h < a.Hq;
-#pragma unroll
-    for (int c = 0; c < NQC; ++c) {
-      uint4 z = {0u, 0u, 0u, 0u};
-      qf[nb][c] = as_bf16x8(hvalid[nb] ? *(const uint4*)(qb + (int64_t)h * a.q_sh + 16 * c + 8 * hh) : z);
-    }
+  for (int c = 0; c < NQC; ++c) {
+    const uint4 x = *(const uint4*)(qb + (int64_t)(hvalid ? head : 0) * a.q_sh + 16 * c + 8 * hh);
+    const uint4 z = {0u, 0u, 0u, 0u};
+    qf[c] = as_bf16x8(hvalid ? x : z);
   }
 
-  float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
-  f32x16 acc[2][NDB];
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16 acc[NDB];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[nb][db][i] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
   const KT* kb = (const KT*)a.k + (int64_t)b * a.k_sb;
   const KT* vb = (const KT*)a.v + (int64_t)b * a.v_sb;
   Raw8<KT> kreg[KU];
   Raw8<KT> vreg[VU][4];
+  uint32_t kmask = 0u, vmask = 0u;
 
+  // loads are unconditional from a clamped in-bounds key (key 0); empty slots
+  // are zeroed when staged (see keep_if)
   auto stage_load = [&](int t) {
+    kmask = 0u; vmask = 0u;
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
-      const int unit = lane + 64 * u;
+      const int unit = tid + 128 * u;
       const int key = unit / (D / 8), c8 = unit % (D / 8);
       const int j = keyof(t, key);
-      kreg[u] = j >= 0 ? load8<KT>(kb + (int64_t)j * a.k_st + c8 * 8) : zero8<KT>();
+      kmask |= (j >= 0 ? 1u : 0u) << u;
+      kreg[u] = load8<KT>(kb + (int64_t)(j >= 0 ? j : 0) * a.k_st + c8 * 8);
     }
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
-      const int unit = lane + 64 * u;
+      const int unit = tid + 128 * u;
       const int kg = unit / (D / 8), dc = unit % (D / 8);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = keyof(t, kg * 4 + r);
-        vreg[u][r] = j >= 0 ? load8<KT>(vb + (int64_t)j * a.v_st + dc * 8) : zero8<KT>();
+        vmask |= (j >= 0 ? 1u : 0u) << (4 * u + r);
+        vreg[u][r] = load8<KT>(vb + (int64_t)(j >= 0 ? j : 0) * a.v_st + dc * 8);
       }
     }
   };
   auto stage_store = [&]() {
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
-      const int unit = lane + 64 * u;
+      const int unit = tid + 128 * u;
       const int key = unit / (D / 8), c8 = unit % (D / 8);
+      keep_if(kreg[u], (kmask >> u) & 1u);
       *(uint4*)&Kl[key * KROW + c8 * 8] = to_ct(kreg[u]).a;
     }
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
-      const int unit = lane + 64 * u;
+      const int unit = tid + 128 * u;
       const int kg = unit / (D / 8), dc = unit % (D / 8);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) keep_if(vreg[u][r], (vmask >> (4 * u + r)) & 1u);
       const uint4 r0 = to_ct(vreg[u][0]).a, r1 = to_ct(vreg[u][1]).a, r2 = to_ct(vreg[u][2]).a, r3 = to_ct(vreg[u][3]).a;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -160,52 +166,60 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecArgs a) {
       }
     }
   };
+  // token scores of tile t: max over the two waves' per-key maxima
+  auto emit_scores = [&](int t) {
+    if (!SPARSE && tid < 64) {
+      const int j = t * 64 + tid;
+      const float v = fmaxf(red[t & 1][0][tid], red[t & 1][1][tid]);
+      if (j < a.Nmax) a.scores[(int64_t)b * a.sc_sb + j] = (j < n) ? v * a.logit_scale : kNegInf;
+    }
+  };
 
   const float c2 = a.scale_log2;
-  const int gw = s * 4 + wave, gstride = a.nsplit * 4;
-  int t = gw;
-  if (t < ntiles_valid) stage_load(t);
-  for (; t < ntiles_valid; t += gstride) {
+  if (t0 < t1) stage_load(t0);
+  for (int t = t0; t < t1; ++t) {
+    __syncthreads();
+    if (t > t0) emit_scores(t - 1);
     stage_store();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (t + gstride < ntiles_valid) stage_load(t + gstride);
+    __syncthreads();
+    if (t + 1 < t1) stage_load(t + 1);
 
-    f32x16 sacc[2][2];
+    // S^T = K q^T: 64 keys (2 M-blocks) x this wave's 32 heads; fragments read one step ahead
+    f32x16 sacc[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int i = 0; i < 16; ++i) sacc[mb][i] = 0.f;
+    uint4 kf0 = *(const uint4*)&Kl[ln * KROW + 8 * hh];
+    uint4 kf1 = *(const uint4*)&Kl[(32 + ln) * KROW + 8 * hh];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[mb][nb][i] = 0.f;
-#pragma unroll
-    for (int c = 0; c < NQC; ++c)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 ka = as_bf16x8(*(const uint4*)&Kl[(mb * 32 + ln) * KROW + 16 * c + 8 * hh]);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          sacc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[nb][c], sacc[mb][nb], 0, 0, 0);
+    for (int c = 0; c < NQC; ++c) {
+      const uint4 a0 = kf0, a1 = kf1;
+      if (c + 1 < NQC) {
+        kf0 = *(const uint4*)&Kl[ln * KROW + 16 * (c + 1) + 8 * hh];
+        kf1 = *(const uint4*)&Kl[(32 + ln) * KROW + 16 * (c + 1) + 8 * hh];
       }
-    // mask: empty list slots and invalid heads
-    const int rem = nkeys - t * 64;             // valid slots in this tile
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), qf[c], sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), qf[c], sacc[1], 0, 0, 0);
+    }
+    // mask empty list slots and padding heads
+    const int rem = nkeys - t * 64;
+    if (rem < 64 || !hvalid) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int off = mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          if (off >= rem || !hvalid[nb]) sacc[mb][nb][i] = kNegInf;
-      }
+        for (int i = 0; i < 16; ++i) {
+          const int off = mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          if (off >= rem || !hvalid) sacc[mb][i] = kNegInf;
+        }
+    }
     if (!SPARSE) {
-      // token score = max over heads; reduce-scatter so lane ln owns value index ln
+      // per-key max over this wave's heads; reduce-scatter leaves lane ln owning value ln
       float cm[32];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) cm[mb * 16 + i] = fmaxf(sacc[mb][0][i], sacc[mb][1][i]);
+        for (int i = 0; i < 16; ++i) cm[mb * 16 + i] = sacc[mb][i];
 #pragma unroll
       for (int st = 0; st < 5; ++st) {
         const int half = 16 >> st;
@@ -218,120 +232,89 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecArgs a) {
         }
       }
       const int mb = ln >> 4, i = ln & 15;
-      const int j = t * 64 + mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-      if (j < a.Nmax) a.scores[(int64_t)b * a.sc_sb + j] = (j < n) ? cm[0] * a.logit_scale : kNegInf;
+      red[t & 1][wave][mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3)] = cm[0];
     }
-    // online softmax
+    // online softmax (base 2); the rescale of O is skipped when no row max moved
+    float mt = kNegInf;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      float mt = kNegInf;
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[mb][i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mnew = fmaxf(m_run, mt);
+    const float muse = (mnew == kNegInf) ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - muse) * c2);
+    const bool moved = mnew != m_run;
+    m_run = mnew;
+    const float mc = muse * c2;
+    float ps = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[mb][nb][i]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mnew = fmaxf(m_run[nb], mt);
-      const float muse = (mnew == kNegInf) ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f((m_run[nb] - muse) * c2);
-      m_run[nb] = mnew;
-      const float mc = muse * c2;
-      float ps = 0.f;
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mb][nb][i], c2, -mc));
-          sacc[mb][nb][i] = p;
-          ps += p;
-        }
-      l_run[nb] = fmaf(l_run[nb], alpha, ps);
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[mb][i], c2, -mc));
+        sacc[mb][i] = p;
+        ps += p;
+      }
+    l_run = fmaf(l_run, alpha, ps);
+    if (__ballot(moved) != 0ull) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[nb][db][i] *= alpha;
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
     }
-    // O^T += V^T P^T
+    // O^T += V^T P^T, V^T fragments read one step ahead
+    bf16x8 pf[4];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const int mb = kc >> 1, i0 = 8 * (kc & 1);
-      bf16x8 pf[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        uint4 pk;
-        pk.x = pack_bf16x2(sacc[mb][nb][i0 + 0], sacc[mb][nb][i0 + 1]);
-        pk.y = pack_bf16x2(sacc[mb][nb][i0 + 2], sacc[mb][nb][i0 + 3]);
-        pk.z = pack_bf16x2(sacc[mb][nb][i0 + 4], sacc[mb][nb][i0 + 5]);
-        pk.w = pack_bf16x2(sacc[mb][nb][i0 + 6], sacc[mb][nb][i0 + 7]);
-        pf[nb] = as_bf16x8(pk);
-      }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const uint16_t* vr = &Vl[(db * 32 + ln) * VROW + 16 * kc + 4 * hh];
-        const uint2 lo = *(const uint2*)vr;
-        const uint2 hi = *(const uint2*)(vr + 8);
-        uint4 va; va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
-        const bf16x8 vf = as_bf16x8(va);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          acc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb], acc[nb][db], 0, 0, 0);
-      }
+      uint4 pk;
+      pk.x = pack_bf16x2(sacc[mb][i0 + 0], sacc[mb][i0 + 1]);
+      pk.y = pack_bf16x2(sacc[mb][i0 + 2], sacc[mb][i0 + 3]);
+      pk.z = pack_bf16x2(sacc[mb][i0 + 4], sacc[mb][i0 + 5]);
+      pk.w = pack_bf16x2(sacc[mb][i0 + 6], sacc[mb][i0 + 7]);
+      pf[kc] = as_bf16x8(pk);
     }
-    __builtin_amdgcn_wave_barrier();
+    auto vfrag = [&](int db, int kc) {
+      const uint16_t* vr = &Vl[(db * 32 + ln) * VROW + 16 * kc + 4 * hh];
+      const uint2 lo = *(const uint2*)vr;
+      const uint2 hi = *(const uint2*)(vr + 8);
+      uint4 va; va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
+      return va;
+    };
+    uint4 vn = vfrag(0, 0);
+#pragma unroll
+    for (int st = 0; st < NDB * 4; ++st) {
+      const int db = st >> 2, kc = st & 3;
+      const uint4 va = vn;
+      if (st + 1 < NDB * 4) vn = vfrag((st + 1) >> 2, (st + 1) & 3);
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), pf[kc], acc[db], 0, 0, 0);
+    }
   }
-  // tiles past the valid length: token scores are -inf
-  if (!SPARSE) {
-    for (int tt = t; tt < ntiles_all; tt += gstride) {   // t: this wave's first tile past the valid ones
-      const int j = tt * 64 + lane;
-      if (j < a.Nmax) a.scores[(int64_t)b * a.sc_sb + j] = kNegInf;
-    }
+  __syncthreads();
+  if (t0 < t1) emit_scores(t1 - 1);
+  // keys past the valid length: token scores are -inf (the workgroups of the
+  // last split cover the tail of the score row)
+  if (!SPARSE && s == a.nsplit - 1) {
+    for (int j = ntiles * 64 + tid; j < a.Nmax; j += 128) a.scores[(int64_t)b * a.sc_sb + j] = kNegInf;
   }
 
-  // ---- merge the 4 waves' partials in LDS, emit one partial ----------------
-  __syncthreads();
-  float* Ow = (float*)lds;                       // [4][64 rows][D]
-  float* Mw = Ow + 4 * 64 * D;                   // [4][64]
-  float* Lw = Mw + 4 * 64;                       // [4][64]
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int row = nb * 32 + ln;
-    const float lsum = l_run[nb] + __shfl_xor(l_run[nb], 32);
-    if (hh == 0) { Mw[wave * 64 + row] = m_run[nb]; Lw[wave * 64 + row] = lsum; }
+  // ---- this wave's partial (m, l, unnormalised O) ------------------------------
+  if (hvalid) {
+    const float lsum = l_run + __shfl_xor(l_run, 32);
+    const int64_t pidx = ((int64_t)(layer * a.B + b) * a.nsplit + s) * a.Hq + head;
+    float* po = a.part_o + pidx * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d = db * 32 + 8 * i4 + 4 * hh;
-        float4 v4 = {acc[nb][db][4 * i4], acc[nb][db][4 * i4 + 1], acc[nb][db][4 * i4 + 2], acc[nb][db][4 * i4 + 3]};
-        *(float4*)&Ow[(wave * 64 + row) * D + d] = v4;
+        const float4 v4 = {acc[db][4 * i4], acc[db][4 * i4 + 1], acc[db][4 * i4 + 2], acc[db][4 * i4 + 3]};
+        *(float4*)(po + d) = v4;
       }
-  }
-  __syncthreads();
-  {
-    const int row = tid >> 2, dq = (tid & 3) * (D / 4);
-    if (row < a.Hq) {
-      float m = kNegInf;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) m = fmaxf(m, Mw[w * 64 + row]);
-      float sc[4], l = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = Mw[w * 64 + row];
-        sc[w] = (mw == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((mw - m) * c2);
-        l += Lw[w * 64 + row] * sc[w];
-      }
-      const int64_t pidx = ((int64_t)(layer * a.B + b) * a.nsplit + s) * a.Hq + row;
-      float* po = a.part_o + pidx * D + dq;
-      for (int d = 0; d < D / 4; d += 4) {
-        float4 r = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float4 x = *(const float4*)&Ow[(w * 64 + row) * D + dq + d];
-          r.x += x.x * sc[w]; r.y += x.y * sc[w]; r.z += x.z * sc[w]; r.w += x.w * sc[w];
-        }
-        *(float4*)(po + d) = r;
-      }
-      if ((tid & 3) == 0) { a.part_ml[pidx * 2] = m; a.part_ml[pidx * 2 + 1] = l; }
-    }
+    if (hh == 0) { a.part_ml[pidx * 2] = m_run; a.part_ml[pidx * 2 + 1] = lsum; }
+  } else {
+    // (a wave whose lanes are all padding heads still joined every barrier)
   }
 }
 
@@ -367,7 +350,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const MergeArgs a) {
 
 hipError_t launch_decode(int sparse, int kt, int D, const DecArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)(a.nlayer * a.B * a.nsplit);
-#define HYS_DEC(SP, KT, DD) hipLaunchKernelGGL((decode_kernel<SP, KT, DD>), dim3(grid), dim3(256), 0, s, a)
+#define HYS_DEC(SP, KT, DD) hipLaunchKernelGGL((decode_kernel<SP, KT, DD>), dim3(grid), dim3(128), 0, s, a)
   if (kt == ET_FP8) {
     if (D == 128) { if (sparse) HYS_DEC(1, uint8_t, 128); else HYS_DEC(0, uint8_t, 128); }
     else if (D == 64) { if (sparse) HYS_DEC(1, uint8_t, 64); else HYS_DEC(0, uint8_t, 64); }
