@@ -135,11 +135,12 @@ hys_status topk_launch(const float* scores, int64_t rows, int64_t cols, int64_t 
   hys::TopkArgs a{};
   a.scores = scores; a.rows = rows; a.cols = cols; a.row_stride = row_stride; a.k = k;
   a.idx = idx; a.count = count;
-  if (cols > 65536) {
-    const int64_t nchunk = (cols + 65535) / 65536;
+  const int64_t ch = hys::topk_chunk_cols();
+  if (cols > ch) {
+    const int64_t nchunk = (cols + ch - 1) / ch;
     a.cand_idx = (int32_t*)ws;
     a.cand_val = (float*)((char*)ws + (size_t)(rows * nchunk * k) * sizeof(int32_t));
-    a.nchunk = (int)nchunk; a.chunk_cols = 65536;
+    a.nchunk = (int)nchunk; a.chunk_cols = ch;
   }
   return hip_status(hys::launch_topk(a, st), "top-k launch");
 }
@@ -202,18 +203,21 @@ hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
     hys::AttnArgs a = base_args(p, q, k, v, o, lse);
     hipStream_t st = (hipStream_t)stream;
     int mode, grid;
+    a.nb = env_int("HYS_NB_FULL", 1) == 2 ? 2 : 1;
+    const int rows = 128 * a.nb;                 // rows per workgroup
     if (mode_in == HYS_SCORE_TILE_TOKEN) {
       mode = hys::M_FULL_TILE;
       a.BQ = 64;
-      a.HC = (int)(G < 4 ? G : 4);
+      a.HC = (int)(G < rows / 64 ? G : rows / 64);
       a.nhc = (int)((G + a.HC - 1) / a.HC);
       a.ntq = (int)((L + 63) / 64);
       a.scores = scores; a.sc_sb = (int64_t)a.ntq * L; a.sc_sr = L; a.sc_sg = 0;
       grid = (int)(B * a.ntq);
     } else {
       mode = mode_in == HYS_SCORE_BLOCK ? hys::M_FULL_BLOCK : hys::M_FULL;
+      if (G > rows) return fail(HYS_ERR_UNSUPPORTED, "more than %d query heads per KV head", rows);
       a.HC = (int)G;
-      a.BQ = (int)(256 / G);
+      a.BQ = (int)(rows / G);
       a.nhc = 1;
       a.ntq = (int)((L + a.BQ - 1) / a.BQ);
       if (mode == hys::M_FULL_BLOCK) {
@@ -248,8 +252,12 @@ hys_status hys_select_topk(const float* scores, int64_t rows, int64_t cols, int6
     if (cols >= (1ll << 31)) return fail(HYS_ERR_UNSUPPORTED, "cols >= 2^31");
     if (rows > 0 && row_stride < cols) return fail(HYS_ERR_INVALID_ARG, "row_stride < cols");
     if (rows > (1ll << 31) - 1) return fail(HYS_ERR_UNSUPPORTED, "rows >= 2^31");
-    if (cols > 65536 && ((cols + 65535) / 65536) * (int64_t)k > 65536)
-      return fail(HYS_ERR_UNSUPPORTED, "ceil(cols/65536) * k exceeds 65536");
+    {
+      const int64_t ch = hys::topk_chunk_cols();
+      if (cols > ch && ((cols + ch - 1) / ch) * (int64_t)k > hys::topk_max_candidates())
+        return fail(HYS_ERR_UNSUPPORTED, "ceil(cols/%lld) * k exceeds %lld", (long long)ch,
+                    (long long)hys::topk_max_candidates());
+    }
     const size_t need = hys::topk_workspace_bytes(rows, cols, k);
     if (!ws) { *ws_bytes = need; return ok(); }
     if (*ws_bytes < need) return fail(HYS_ERR_WORKSPACE, "workspace %zu < required %zu bytes", *ws_bytes, need);
@@ -290,10 +298,13 @@ hys_status hys_sparse_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tens
       const int64_t nblk = (L + 63) / 64;
       if (nblk > 16384) return fail(HYS_ERR_UNSUPPORTED, "more than 16384 key blocks");
       mode = hys::M_SPARSE_BLOCK;
+      a.nb = env_int("HYS_NB_SPARSE", 1) == 2 ? 2 : 1;
+      const int rows = 128 * a.nb;
+      if (G > rows) return fail(HYS_ERR_UNSUPPORTED, "more than %d query heads per KV head", rows);
       a.HC = (int)G;
-      int bq = (int)(256 / G);
+      int bq = (int)(rows / G);
       if (bq > 64) bq = 64;
-      if (sp->k > 0 && bq > 1024 / sp->k) bq = 1024 / sp->k;
+      if (sp->k > 0 && bq > 4 * rows / sp->k) bq = 4 * rows / sp->k;
       const int bq_env = env_int("HYS_SPARSE_BQ", 0);       // tuning override
       if (bq_env > 0 && bq_env < bq) bq = bq_env;
       if (bq < 1) bq = 1;
@@ -310,8 +321,10 @@ hys_status hys_sparse_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tens
       if (sp->forced_window < 0 || sp->forced_window > 1984)
         return fail(HYS_ERR_UNSUPPORTED, "forced_window must be in [0, 1984]");
       mode = hys::M_SPARSE_TOKEN;
+      a.nb = env_int("HYS_NB_TOKEN", 1) == 2 ? 2 : 1;
+      const int hcmax = 2 * a.nb;                // 64 queries x hcmax heads = the workgroup's rows
       a.BQ = 64;
-      a.HC = (int)(G < 4 ? G : 4);
+      a.HC = (int)(G < hcmax ? G : hcmax);
       a.nhc = (int)((G + a.HC - 1) / a.HC);
       a.ntq = (int)((L + 63) / 64);
       a.window = sp->forced_window;
@@ -345,11 +358,12 @@ hys_status hys_swa_gate_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4
     if (window < 1) return fail(HYS_ERR_INVALID_ARG, "window must be >= 1");
     const int64_t B = q.shape[0], L = q.shape[1], Hq = q.shape[2], Hkv = k_win.shape[2], D = q.shape[3];
     const int64_t G = Hq / Hkv;
-    if (G > 256) return fail(HYS_ERR_UNSUPPORTED, "more than 256 query heads per KV head");
     if (L == 0) return ok();
     hys::AttnArgs a = base_args(p, q, k_win, v_win, o, nullptr);
     a.window = window;
-    a.HC = (int)G; a.BQ = (int)(256 / G); a.nhc = 1;
+    a.nb = env_int("HYS_NB_SWA", 1) == 2 ? 2 : 1;
+    if (G > 128 * a.nb) return fail(HYS_ERR_UNSUPPORTED, "more than %d query heads per KV head", 128 * a.nb);
+    a.HC = (int)G; a.BQ = (int)(128 * a.nb / G); a.nhc = 1;
     a.ntq = (int)((L + a.BQ - 1) / a.BQ);
     a.o_sp = (const float*)o_sparse.ptr;
     a.osp_sb = o_sparse.stride[0]; a.osp_st = o_sparse.stride[1]; a.osp_sh = o_sparse.stride[2];
@@ -387,8 +401,11 @@ hys_status hys_decode_step(const hys_decode_params* p, hys_tensor4 q_full, hys_t
     if (p->topk < 1 || p->topk > 2048) return fail(HYS_ERR_UNSUPPORTED, "topk must be in [1, 2048]");
     if (p->window < 0) return fail(HYS_ERR_INVALID_ARG, "window must be >= 0");
     if (Nmax < 1) return fail(HYS_ERR_INVALID_ARG, "empty cache");
-    if (Nmax > 65536 && ((Nmax + 65535) / 65536) * (int64_t)p->topk > 65536)
-      return fail(HYS_ERR_UNSUPPORTED, "cache too long for top-%d", p->topk);
+    {
+      const int64_t ch = hys::topk_chunk_cols();
+      if (Nmax > ch && ((Nmax + ch - 1) / ch) * (int64_t)p->topk > hys::topk_max_candidates())
+        return fail(HYS_ERR_UNSUPPORTED, "cache too long for top-%d", p->topk);
+    }
     if ((s = check_out(o_full, q_full, "o_full")) != HYS_OK) return s;
     if (!cache_len || !token_scores || !idx) return fail(HYS_ERR_INVALID_ARG, "null cache_len, token_scores or idx");
     if (n_sparse > 0 && (!q_sparse || !o_sparse)) return fail(HYS_ERR_INVALID_ARG, "null q_sparse or o_sparse");

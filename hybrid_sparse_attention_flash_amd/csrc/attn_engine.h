@@ -39,7 +39,7 @@ template <> struct Compute<uint16_t> { using CT = uint16_t; static constexpr int
 // ---------------------------------------------------------------------------
 
 template <int MODE, typename QT, typename KT, int D, int NB>
-__global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const AttnArgs a) {
   using CT = typename Compute<QT>::CT;
   constexpr bool F32 = sizeof(CT) == 4;
   constexpr int KROW = D + Compute<QT>::KPAD;      // LDS row stride of K (elements)
@@ -51,15 +51,17 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
   constexpr int VU = (VUN + 255) / 256;
   constexpr int NDB = D / 32;                      // 32-wide d blocks of O^T
   constexpr int NQC = F32 ? D / 2 : D / 16;        // Q fragments per row (k-steps of S^T)
-  constexpr int UMAX = 1024;                       // max union entries (block mode)
+  constexpr int UMAX = 4 * ROWS;                   // max union entries (block mode)
   constexpr int NBWMAX = 512;                      // max bitmap words (block mode)
   constexpr int TLMAX = 2048;                      // max token-list length (token mode)
   static_assert(KUN % 256 == 0, "D must be 64 or 128");
 
-  __shared__ __attribute__((aligned(16))) CT Klds[64 * KROW];
-  __shared__ __attribute__((aligned(16))) CT VTlds[D * VROW];
-  __shared__ __attribute__((aligned(16))) int kinfo[64];
-  __shared__ float red[2 * ROWS];
+  // two stages: tile n is consumed from one while tile n+1 is written to the other
+  __shared__ __attribute__((aligned(16))) CT Klds[2 * 64 * KROW];
+  __shared__ __attribute__((aligned(16))) CT VTlds[2 * D * VROW];
+  __shared__ __attribute__((aligned(16))) int kinfo[2 * 64];
+  constexpr int RS = ROWS > 256 ? ROWS : 256;      // stride of the two score-reduction halves
+  __shared__ float red[2 * RS];
   __shared__ int s_misc[4];
   // block-sparse lists
   __shared__ uint32_t s_bitmap[(MODE == M_SPARSE_BLOCK) ? NBWMAX : 1];
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
       const int unit = tid + 256 * u;
-      if (unit < VUN) {
+      if (VUN % 256 == 0 || unit < VUN) {
         const int kg = unit / (D / 8), dc = unit % (D / 8);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -253,21 +255,23 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
     }
   };
 
-  auto stage_store = [&]() {
+  auto stage_store = [&](int buf) {
+    CT* Kb = Klds + buf * (64 * KROW);
+    CT* Vb = VTlds + buf * (D * VROW);
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
       const int unit = tid + 256 * u;
       const int key = unit / (D / 8), c8 = unit % (D / 8);
       keep_if(kreg[u], (kmask >> u) & 1u);
       Cvt8<CT> c = to_ct(kreg[u]);
-      CT* dst = &Klds[key * KROW + c8 * 8];
+      CT* dst = &Kb[key * KROW + c8 * 8];
       *(uint4*)dst = c.a;
       if constexpr (F32) *(uint4*)(dst + 4) = c.b;
     }
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
       const int unit = tid + 256 * u;
-      if (unit < VUN) {
+      if (VUN % 256 == 0 || unit < VUN) {
         const int kg = unit / (D / 8), dc = unit % (D / 8);
 #pragma unroll
         for (int r = 0; r < 4; ++r) keep_if(vreg[u][r], (vmask >> (4 * u + r)) & 1u);
@@ -279,8 +283,8 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
             uint2 e, o;
             e.x = __builtin_amdgcn_perm(w1, w0, 0x05040100u); e.y = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
             o.x = __builtin_amdgcn_perm(w1, w0, 0x07060302u); o.y = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
-            *(uint2*)&VTlds[(dc * 8 + 2 * p) * VROW + kg * 4] = e;
-            *(uint2*)&VTlds[(dc * 8 + 2 * p + 1) * VROW + kg * 4] = o;
+            *(uint2*)&Vb[(dc * 8 + 2 * p) * VROW + kg * 4] = e;
+            *(uint2*)&Vb[(dc * 8 + 2 * p + 1) * VROW + kg * 4] = o;
           }
         } else {
 #pragma unroll
@@ -290,12 +294,12 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
             t.y = d < 4 ? u4get(r1.a, d) : u4get(r1.b, d - 4);
             t.z = d < 4 ? u4get(r2.a, d) : u4get(r2.b, d - 4);
             t.w = d < 4 ? u4get(r3.a, d) : u4get(r3.b, d - 4);
-            *(uint4*)&VTlds[(dc * 8 + d) * VROW + kg * 4] = t;
+            *(uint4*)&Vb[(dc * 8 + d) * VROW + kg * 4] = t;
           }
         }
       }
     }
-    if (tid < 64) kinfo[tid] = my_kinfo;
+    if (tid < 64) kinfo[buf * 64 + tid] = my_kinfo;
   };
 
   const QT* qbase = (const QT*)a.q + (int64_t)b * a.q_sb;
@@ -374,7 +378,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
     // score emission for tile n (reads red[n & 1]); called by all threads after a barrier
     auto emit_scores = [&](int n) {
       if (MODE == M_FULL_BLOCK) {
-        const float* rb = red + (n & 1) * ROWS;
+        const float* rb = red + (n & 1) * RS;
         float* sc = a.scores + (int64_t)g * a.sc_sg + (int64_t)b * a.sc_sb;
         for (int t = tid; t < a.BQ; t += 256) {
           const int q = q0 + t;
@@ -386,7 +390,7 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
         }
       } else if (MODE == M_FULL_TILE) {
         if (tid < 64) {
-          const float* rb = red + (n & 1) * ROWS;
+          const float* rb = red + (n & 1) * RS;
           float mx = fmaxf(fmaxf(rb[tid], rb[64 + tid]), fmaxf(rb[128 + tid], rb[192 + tid]));
           const int j = n * 64 + tid;
           if (j < a.Lk) {
@@ -399,13 +403,20 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
     };
 
     // ---- tile loop ---------------------------------------------------------
-    if (ntiles > 0) stage_load(0, g);
+    // One barrier per tile: tile n is read from stage n&1 while the registers
+    // holding tile n+1 are written to the other stage and tile n+2 is fetched.
+    if (ntiles > 0) {
+      stage_load(0, g);
+      stage_store(0);
+      if (ntiles > 1) stage_load(1, g);
+    }
+    __syncthreads();
     for (int n = 0; n < ntiles; ++n) {
-      __syncthreads();
+      const int cur = n & 1;
+      const CT* Kc = Klds + cur * (64 * KROW);
+      const CT* Vc = VTlds + cur * (D * VROW);
+      const int* kic = kinfo + cur * 64;
       if (n > 0) emit_scores(n - 1);
-      stage_store();
-      __syncthreads();
-      if (n + 1 < ntiles) stage_load(n + 1, g);
 
       // wave-level skip: nothing of this tile is visible to any row of the wave
       bool active = wave_any;
@@ -415,179 +426,204 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
       if (!active) {
         if (MODE == M_FULL_BLOCK && hh == 0) {
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) red[(n & 1) * ROWS + wave * 32 * NB + nb * 32 + ln] = kNegInf;
+          for (int nb = 0; nb < NB; ++nb) red[(n & 1) * RS + wave * 32 * NB + nb * 32 + ln] = kNegInf;
         }
-        if (MODE == M_FULL_TILE) red[(n & 1) * ROWS + wave * 64 + lane] = kNegInf;
-        continue;
-      }
-
-      // S^T = K Q^T  (M = 64 keys as two 32-blocks, N = rows, K = D)
-      f32x16 s[2][NB];
+        if (MODE == M_FULL_TILE) red[(n & 1) * RS + wave * 64 + lane] = kNegInf;
+      } else {
+        // S^T = K Q^T  (M = 64 keys as two 32-blocks, N = rows, K = D); the K
+        // fragments of step c+1 are read while the MFMAs of step c issue
+        f32x16 s[2][NB];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+          for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) s[mb][nb][i] = 0.f;
+            for (int i = 0; i < 16; ++i) s[mb][nb][i] = 0.f;
+        if constexpr (F32) {
+          float kn0 = Kc[ln * KROW + hh], kn1 = Kc[(32 + ln) * KROW + hh];
 #pragma unroll
-      for (int c = 0; c < NQC; ++c) {
+          for (int c = 0; c < NQC; ++c) {
+            const float k0 = kn0, k1 = kn1;
+            if (c + 1 < NQC) { kn0 = Kc[ln * KROW + 2 * (c + 1) + hh]; kn1 = Kc[(32 + ln) * KROW + 2 * (c + 1) + hh]; }
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          if constexpr (F32) {
-            const float ka = Klds[(mb * 32 + ln) * KROW + 2 * c + hh];
+            for (int nb = 0; nb < NB; ++nb) {
+              s[0][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k0, qf[nb][c], s[0][nb], 0, 0, 0);
+              s[1][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k1, qf[nb][c], s[1][nb], 0, 0, 0);
+            }
+          }
+        } else {
+          uint4 kn0 = *(const uint4*)&Kc[ln * KROW + 8 * hh];
+          uint4 kn1 = *(const uint4*)&Kc[(32 + ln) * KROW + 8 * hh];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-              s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(ka, qf[nb][c], s[mb][nb], 0, 0, 0);
-          } else {
-            const bf16x8 ka = as_bf16x8(*(const uint4*)&Klds[(mb * 32 + ln) * KROW + 16 * c + 8 * hh]);
+          for (int c = 0; c < NQC; ++c) {
+            const uint4 k0 = kn0, k1 = kn1;
+            if (c + 1 < NQC) {
+              kn0 = *(const uint4*)&Kc[ln * KROW + 16 * (c + 1) + 8 * hh];
+              kn1 = *(const uint4*)&Kc[(32 + ln) * KROW + 16 * (c + 1) + 8 * hh];
+            }
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-              s[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[nb][c], s[mb][nb], 0, 0, 0);
+            for (int nb = 0; nb < NB; ++nb) {
+              s[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), qf[nb][c], s[0][nb], 0, 0, 0);
+              s[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), qf[nb][c], s[1][nb], 0, 0, 0);
+            }
           }
         }
-      }
 
-      // masking
-      bool need_mask = true;
-      if (MODE == M_FULL || MODE == M_FULL_BLOCK || MODE == M_FULL_TILE)
-        need_mask = !(wave_full && (n * 64 + 63 <= wave_qmin) && (n * 64 + 63 <= kend));
-      if (need_mask) {
+        // masking
+        bool need_mask = true;
+        if (MODE == M_FULL || MODE == M_FULL_BLOCK || MODE == M_FULL_TILE)
+          need_mask = !(wave_full && (n * 64 + 63 <= wave_qmin) && (n * 64 + 63 <= kend));
+        if (need_mask) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+          for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            const int off = mb * 32 + 8 * i4 + 4 * hh;
-            const int4 ki = *(const int4*)&kinfo[off];
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const int off = mb * 32 + 8 * i4 + 4 * hh;
+              const int4 ki = *(const int4*)&kic[off];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int kinf = e == 0 ? ki.x : (e == 1 ? ki.y : (e == 2 ? ki.z : ki.w));
-              const int j = kinf & 0x3fffffff;
+              for (int e = 0; e < 4; ++e) {
+                const int kinf = e == 0 ? ki.x : (e == 1 ? ki.y : (e == 2 ? ki.z : ki.w));
+                const int j = kinf & 0x3fffffff;
 #pragma unroll
-              for (int nb = 0; nb < NB; ++nb) {
-                bool ok = valid[nb] && j <= qpos[nb];
-                if (MODE == M_SWA_GATE) ok = ok && (j > qpos[nb] - a.window);
-                if (MODE == M_SPARSE_BLOCK) ok = ok && ((memb >> qiv[nb]) & 1ull);
-                if (MODE == M_SPARSE_TOKEN) ok = ok && ((kinf >> 30) || (j > qpos[nb] - a.window));
-                if (!ok) s[mb][nb][4 * i4 + e] = kNegInf;
+                for (int nb = 0; nb < NB; ++nb) {
+                  bool ok = valid[nb] && j <= qpos[nb];
+                  if (MODE == M_SWA_GATE) ok = ok && (j > qpos[nb] - a.window);
+                  if (MODE == M_SPARSE_BLOCK) ok = ok && ((memb >> qiv[nb]) & 1ull);
+                  if (MODE == M_SPARSE_TOKEN) ok = ok && ((kinf >> 30) || (j > qpos[nb] - a.window));
+                  if (!ok) s[mb][nb][4 * i4 + e] = kNegInf;
+                }
               }
             }
           }
         }
-      }
 
-      // token scores: per-key max over this workgroup's rows
-      if (MODE == M_FULL_TILE) {
-        float cm[32];
+        // token scores: per-key max over this workgroup's rows
+        if (MODE == M_FULL_TILE) {
+          float cm[32];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+          for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float v = s[mb][0][i];
+            for (int i = 0; i < 16; ++i) {
+              float v = s[mb][0][i];
 #pragma unroll
-            for (int nb = 1; nb < NB; ++nb) v = fmaxf(v, s[mb][nb][i]);
-            cm[mb * 16 + i] = v;
+              for (int nb = 1; nb < NB; ++nb) v = fmaxf(v, s[mb][nb][i]);
+              cm[mb * 16 + i] = v;
+            }
+          // reduce-scatter over the 32 lanes of each half: after 5 halvings lane
+          // ln holds the max of value index ln
+#pragma unroll
+          for (int st = 0; st < 5; ++st) {
+            const int half = 16 >> st;
+            const bool upper = (ln & half) != 0;
+#pragma unroll
+            for (int x = 0; x < half; ++x) {
+              const float send = upper ? cm[x] : cm[x + half];
+              const float keep = upper ? cm[x + half] : cm[x];
+              cm[x] = fmaxf(keep, __shfl_xor(send, half));
+            }
           }
-        // reduce-scatter over the 32 lanes of each half: after 5 halvings lane ln
-        // holds the max of one of the 32 values
-#pragma unroll
-        for (int st = 0; st < 5; ++st) {
-          const int half = 16 >> st;                 // values kept after this step
-          const int bit = 16 >> st;                  // lane bit exchanged
-          const bool upper = (ln & bit) != 0;
-#pragma unroll
-          for (int x = 0; x < half; ++x) {
-            const float send = upper ? cm[x] : cm[x + half];
-            const float keep = upper ? cm[x + half] : cm[x];
-            const float got = __shfl_xor(send, bit);
-            cm[x] = fmaxf(keep, got);
-          }
+          const int mb = ln >> 4, i = ln & 15;
+          const int off = mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          red[(n & 1) * RS + wave * 64 + off] = cm[0];
         }
-        // lane ln now owns value index vi = bitrev5-style mapping: bits of ln pick the upper halves
-        int vi = 0;
-#pragma unroll
-        for (int st = 0; st < 5; ++st) if (ln & (16 >> st)) vi += (16 >> st);
-        const int mb = vi >> 4, i = vi & 15;
-        const int off = mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-        red[(n & 1) * ROWS + wave * 64 + off] = cm[0];
-      }
 
-      // online softmax (base 2 on raw dot products)
-      float alpha[NB];
+        // online softmax (base 2 on raw dot products); O is rescaled only when
+        // some row's running max moved
+        float alpha[NB];
+        bool moved = false;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float mt = kNegInf;
+        for (int nb = 0; nb < NB; ++nb) {
+          float mt = kNegInf;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+          for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[mb][nb][i]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        if (MODE == M_FULL_BLOCK && hh == 0) red[(n & 1) * ROWS + wave * 32 * NB + nb * 32 + ln] = mt;
-        const float mnew = fmaxf(m_run[nb], mt);
-        const float muse = (mnew == kNegInf) ? 0.f : mnew;
-        alpha[nb] = __builtin_amdgcn_exp2f((m_run[nb] - muse) * c2);
-        m_run[nb] = mnew;
-        const float mc = muse * c2;
-        float ps = 0.f;
+            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[mb][nb][i]);
+          mt = fmaxf(mt, __shfl_xor(mt, 32));
+          if (MODE == M_FULL_BLOCK && hh == 0) red[(n & 1) * RS + wave * 32 * NB + nb * 32 + ln] = mt;
+          const float mnew = fmaxf(m_run[nb], mt);
+          const float muse = (mnew == kNegInf) ? 0.f : mnew;
+          alpha[nb] = __builtin_amdgcn_exp2f((m_run[nb] - muse) * c2);
+          moved = moved || (mnew != m_run[nb]);
+          m_run[nb] = mnew;
+          const float mc = muse * c2;
+          float ps = 0.f;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+          for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][nb][i], c2, -mc));
-            s[mb][nb][i] = p;
-            ps += p;
-          }
-        l_run[nb] = fmaf(l_run[nb], alpha[nb], ps);
+            for (int i = 0; i < 16; ++i) {
+              const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][nb][i], c2, -mc));
+              s[mb][nb][i] = p;
+              ps += p;
+            }
+          l_run[nb] = fmaf(l_run[nb], alpha[nb], ps);
+        }
+        if (__ballot(moved) != 0ull) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+          for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[nb][db][i] *= alpha[nb];
-      }
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) acc[nb][db][i] *= alpha[nb];
+        }
 
-      // O^T += V^T P^T  (M = D, N = rows, K = 64 keys)
-      if constexpr (F32) {
+        // O^T += V^T P^T  (M = D, N = rows, K = 64 keys); V^T fragments read one step ahead
+        if constexpr (F32) {
+          float vn = Vc[ln * VROW + 4 * hh];
 #pragma unroll
-        for (int kk = 0; kk < 32; ++kk) {
-          const int mb = kk >> 4, i = kk & 15;
-          const int key = mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const float va = VTlds[(db * 32 + ln) * VROW + key];
+          for (int st = 0; st < 32 * NDB; ++st) {
+            const int kk = st / NDB, db = st % NDB;
+            const int mb = kk >> 4, i = kk & 15;
+            const float va = vn;
+            if (st + 1 < 32 * NDB) {
+              const int kk2 = (st + 1) / NDB, db2 = (st + 1) % NDB;
+              const int key2 = (kk2 >> 4) * 32 + 8 * ((kk2 & 15) >> 2) + 4 * hh + (kk2 & 3);
+              vn = Vc[(db2 * 32 + ln) * VROW + key2];
+            }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
               acc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, s[mb][nb][i], acc[nb][db], 0, 0, 0);
           }
-        }
-      } else {
+        } else {
+          bf16x8 pf[4][NB];
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const int mb = kc >> 1, i0 = 8 * (kc & 1);
-          bf16x8 pf[NB];
+          for (int kc = 0; kc < 4; ++kc) {
+            const int mb = kc >> 1, i0 = 8 * (kc & 1);
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            uint4 pk;
-            pk.x = pack_bf16x2(s[mb][nb][i0 + 0], s[mb][nb][i0 + 1]);
-            pk.y = pack_bf16x2(s[mb][nb][i0 + 2], s[mb][nb][i0 + 3]);
-            pk.z = pack_bf16x2(s[mb][nb][i0 + 4], s[mb][nb][i0 + 5]);
-            pk.w = pack_bf16x2(s[mb][nb][i0 + 6], s[mb][nb][i0 + 7]);
-            pf[nb] = as_bf16x8(pk);
+            for (int nb = 0; nb < NB; ++nb) {
+              uint4 pk;
+              pk.x = pack_bf16x2(s[mb][nb][i0 + 0], s[mb][nb][i0 + 1]);
+              pk.y = pack_bf16x2(s[mb][nb][i0 + 2], s[mb][nb][i0 + 3]);
+              pk.z = pack_bf16x2(s[mb][nb][i0 + 4], s[mb][nb][i0 + 5]);
+              pk.w = pack_bf16x2(s[mb][nb][i0 + 6], s[mb][nb][i0 + 7]);
+              pf[kc][nb] = as_bf16x8(pk);
+            }
           }
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const CT* vr = &VTlds[(db * 32 + ln) * VROW + 16 * kc + 4 * hh];
-            uint4 va;
+          auto vfrag = [&](int db, int kc) {
+            const CT* vr = &Vc[(db * 32 + ln) * VROW + 16 * kc + 4 * hh];
             const uint2 lo = *(const uint2*)vr;
             const uint2 hi = *(const uint2*)(vr + 8);
-            va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
-            const bf16x8 vf = as_bf16x8(va);
+            uint4 va; va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
+            return va;
+          };
+          uint4 vn = vfrag(0, 0);
+#pragma unroll
+          for (int st = 0; st < NDB * 4; ++st) {
+            const int db = st >> 2, kc = st & 3;
+            const uint4 va = vn;
+            if (st + 1 < NDB * 4) vn = vfrag((st + 1) >> 2, (st + 1) & 3);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-              acc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb], acc[nb][db], 0, 0, 0);
+              acc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), pf[kc][nb], acc[nb][db], 0, 0, 0);
           }
         }
       }
+
+      // stage tile n+1 into the other buffer, fetch tile n+2
+      if (n + 1 < ntiles) stage_store((n + 1) & 1);
+      if (n + 2 < ntiles) stage_load(n + 2, g);
+      __syncthreads();
     }  // tile loop
 
-    __syncthreads();
     if (ntiles > 0) emit_scores(ntiles - 1);
 
     // -inf for blocks / keys after the diagonal
@@ -681,7 +717,10 @@ __global__ __launch_bounds__(256) void attn_tile_kernel(const AttnArgs a) {
 // ---------------------------------------------------------------------------
 template <int MODE, typename QT, typename KT, int D>
 static hipError_t launch_one(const AttnArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_tile_kernel<MODE, QT, KT, D, 2>), dim3(grid), dim3(256), 0, s, a);
+  if (a.nb == 1)
+    hipLaunchKernelGGL((attn_tile_kernel<MODE, QT, KT, D, 1>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_tile_kernel<MODE, QT, KT, D, 2>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -318,34 +318,69 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
   }
 }
 
-// One workgroup per (layer, sequence, head); thread d combines the partials of
-// output column d in split order.
+// One workgroup per (layer, sequence, head).  Thread (g, q) folds the partials
+// s = g, g + NG, g + 2 NG, ... of output columns [4q, 4q+4) with the exact LSE
+// rule, then the NG group results are folded in group order in LDS, so the
+// result does not depend on scheduling.
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(const MergeArgs a) {
+__global__ __launch_bounds__(256) void decode_merge_kernel(const MergeArgs a) {
+  constexpr int NQ = D / 4;          // float4 column groups
+  constexpr int NG = 256 / NQ;       // split groups
+  __shared__ float sm[NG], sl[NG];
+  __shared__ float4 so[NG][NQ];
   const int bid = blockIdx.x;
   const int h = bid % a.Hq;
   const int b = (bid / a.Hq) % a.B;
   const int layer = bid / (a.Hq * a.B);
-  const int d = threadIdx.x;
+  const int q = threadIdx.x % NQ, g = threadIdx.x / NQ;
   const int64_t base = (int64_t)(layer * a.B + b) * a.nsplit;
-  float m = kNegInf;
-  for (int s = 0; s < a.nsplit; ++s) m = fmaxf(m, a.part_ml[((base + s) * a.Hq + h) * 2]);
-  float l = 0.f, o = 0.f;
-  if (m != kNegInf) {
-    for (int s = 0; s < a.nsplit; ++s) {
-      const int64_t p = (base + s) * a.Hq + h;
-      const float ms = a.part_ml[p * 2];
-      const float w = (ms == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((ms - m) * a.scale_log2);
-      l += a.part_ml[p * 2 + 1] * w;
-      o += a.part_o[p * D + d] * w;
-    }
+  const float c2 = a.scale_log2;
+  float m = kNegInf, l = 0.f;
+  float4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int s = g; s < a.nsplit; s += NG) {
+    const int64_t p = (base + s) * a.Hq + h;
+    const float ms = a.part_ml[p * 2], ls = a.part_ml[p * 2 + 1];
+    const float4 os = *(const float4*)(a.part_o + p * D + 4 * q);
+    if (ms == kNegInf) continue;
+    const float mn = fmaxf(m, ms);
+    const float wo = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);
+    const float wn = __builtin_amdgcn_exp2f((ms - mn) * c2);
+    l = l * wo + ls * wn;
+    o.x = o.x * wo + os.x * wn; o.y = o.y * wo + os.y * wn;
+    o.z = o.z * wo + os.z * wn; o.w = o.w * wo + os.w * wn;
+    m = mn;
   }
-  const float out = (m != kNegInf) ? o / l * a.v_scale : 0.f;
-  const int64_t off = (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + d;
-  if (a.o_f32) ((float*)a.o[layer])[off] = out;
-  else ((uint16_t*)a.o[layer])[off] = f32_to_bf16(out);
-  if (a.lse[layer] && d == 0)
-    a.lse[layer][(int64_t)b * a.Hq + h] = (m != kNegInf) ? m * a.logit_scale + __logf(l) : kNegInf;
+  if (q == 0) { sm[g] = m; sl[g] = l; }
+  so[g][q] = o;
+  __syncthreads();
+  if (g == 0) {
+    float M = kNegInf;
+    for (int x = 0; x < NG; ++x) M = fmaxf(M, sm[x]);
+    float L = 0.f;
+    float4 O = {0.f, 0.f, 0.f, 0.f};
+    if (M != kNegInf) {
+      for (int x = 0; x < NG; ++x) {
+        if (sm[x] == kNegInf) continue;
+        const float w = __builtin_amdgcn_exp2f((sm[x] - M) * c2);
+        L += sl[x] * w;
+        const float4 v = so[x][q];
+        O.x += v.x * w; O.y += v.y * w; O.z += v.z * w; O.w += v.w * w;
+      }
+    }
+    const float inv = (M != kNegInf) ? a.v_scale / L : 0.f;
+    const int64_t off = (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + 4 * q;
+    if (a.o_f32) {
+      const float4 r = {O.x * inv, O.y * inv, O.z * inv, O.w * inv};
+      *(float4*)((float*)a.o[layer] + off) = r;
+    } else {
+      uint2 r;
+      r.x = pack_bf16x2(O.x * inv, O.y * inv);
+      r.y = pack_bf16x2(O.z * inv, O.w * inv);
+      *(uint2*)((uint16_t*)a.o[layer] + off) = r;
+    }
+    if (a.lse[layer] && q == 0)
+      a.lse[layer][(int64_t)b * a.Hq + h] = (M != kNegInf) ? M * a.logit_scale + __logf(L) : kNegInf;
+  }
 }
 
 hipError_t launch_decode(int sparse, int kt, int D, const DecArgs& a, hipStream_t s) {
@@ -368,8 +403,8 @@ hipError_t launch_decode(int sparse, int kt, int D, const DecArgs& a, hipStream_
 
 hipError_t launch_decode_merge(int D, const MergeArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)(a.nlayer * a.B * a.Hq);
-  if (D == 128) hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(grid), dim3(128), 0, s, a);
-  else if (D == 64) hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(grid), dim3(64), 0, s, a);
+  if (D == 128) hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(grid), dim3(256), 0, s, a);
+  else if (D == 64) hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(grid), dim3(256), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -45,6 +45,7 @@ struct AttnArgs {
   const float* gate_w;       // [Hq, D]
   const float* gate_b;       // [Hq] or null
   int grid_used;             // work items; extra workgroups exit
+  int nb;                    // 32-row MFMA blocks per wave: 2 (256 rows per workgroup) or 1 (128 rows)
 };
 
 hipError_t launch_attn(int mode, int qt, int kt, int D, const AttnArgs& a, int grid, hipStream_t s);
@@ -61,6 +62,8 @@ struct TopkArgs {
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 size_t topk_workspace_bytes(int64_t rows, int64_t cols, int k);
+int64_t topk_max_candidates();
+int64_t topk_chunk_cols();
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 
 // HySparse2 decode (one query per sequence, MQA cache).

@@ -15,8 +15,8 @@
 // chosen column directly at its ascending position.
 //
 //   short rows (cols <= 2048): one wave per row, up to 32 keys per lane
-//   long rows  (cols <= 65536): one 1024-thread workgroup per row, up to 64 keys per thread
-//   longer rows: each 65536-column chunk keeps its own top-k (exact superset of
+//   long rows  (cols <= 32768): one 1024-thread workgroup per row, up to 32 keys per thread
+//   longer rows: each 32768-column chunk keeps its own top-k (exact superset of
 //   the row's top-k), then a second pass selects among the chunk winners.
 #include "common.h"
 #include "kernels.h"
@@ -41,12 +41,17 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
   const float* sr = scores + row * row_stride;
   const int seg = (int)((cols + 63) / 64);           // columns per lane (<= V)
   const int c0 = lane * seg;
-  uint32_t key[V];
+  // unconditional loads from clamped columns (a branch per load would make every
+  // load wait for the previous ones), masked afterwards
+  float x[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const int c = c0 + v;
-    key[v] = (v < seg && c < cols) ? score_key(sr[c]) : 0u;
+    const int c = min(c0 + v, (int)cols - 1);
+    x[v] = sr[c];
   }
+  uint32_t key[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) key[v] = (v < seg && c0 + v < cols) ? score_key(x[v]) : 0u;
   auto count_ge = [&](uint32_t t) {
     int n = 0;
 #pragma unroll
@@ -145,6 +150,7 @@ __device__ __forceinline__ int block_excl_scan_1024(int v, int* sh, int& total) 
 // cmap: if non-null, the original column of position p is cmap[r*row_stride + p]
 //       (positions with cmap == -1 are empty); else the column is chunk_base + p.
 // Output for (row, chunk): out_idx[(r*nchunk + chunk)*k ...], out_val likewise (if non-null).
+template <int VPT>
 __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restrict__ vals,
                                                           const int32_t* __restrict__ cmap, int64_t rows,
                                                           int64_t cols, int64_t row_stride, int64_t chunk_cols,
@@ -156,25 +162,55 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
   const int chunk = blockIdx.x % nchunk;
   const int64_t cbase = (int64_t)chunk * chunk_cols;
   const int64_t ccols = min(chunk_cols, cols - cbase);
-  const int seg = (int)((ccols + 1023) / 1024);        // <= 64
+  const int seg = (int)((ccols + 1023) / 1024);        // <= VPT
   const int64_t p0 = cbase + (int64_t)tid * seg;
   const float* vr = vals + r * row_stride;
   const int32_t* mr = cmap ? cmap + r * row_stride : nullptr;
-  uint32_t key[64];
+  // loads are straight-line (no branch per element, which would serialise
+  // them); the row tail is handled by clamping and masking
+  const int64_t plast = cbase + ccols - 1;
+  uint32_t key[VPT];
+  const float* src = vr + p0;
+  const bool fast = seg == VPT && p0 + VPT - 1 <= plast && (((uintptr_t)src) & 15u) == 0 &&
+                    (mr == nullptr || (((uintptr_t)(mr + p0)) & 15u) == 0);
+  if (fast) {
 #pragma unroll
-  for (int v = 0; v < 64; ++v) {
-    const int64_t p = p0 + v;
-    uint32_t kk = 0u;
-    if (v < seg && p < cbase + ccols) {
-      const bool present = mr ? (mr[p] >= 0) : true;
-      kk = present ? score_key(vr[p]) : 0u;
+    for (int v4 = 0; v4 < VPT / 4; ++v4) {
+      const float4 f = ((const float4*)src)[v4];
+      key[4 * v4 + 0] = __builtin_bit_cast(uint32_t, f.x);
+      key[4 * v4 + 1] = __builtin_bit_cast(uint32_t, f.y);
+      key[4 * v4 + 2] = __builtin_bit_cast(uint32_t, f.z);
+      key[4 * v4 + 3] = __builtin_bit_cast(uint32_t, f.w);
     }
-    key[v] = kk;
+    if (mr) {
+#pragma unroll
+      for (int v4 = 0; v4 < VPT / 4; ++v4) {
+        const int4 c = ((const int4*)(mr + p0))[v4];
+        if (c.x < 0) key[4 * v4 + 0] = 0xff800000u;     // -inf: an empty candidate slot
+        if (c.y < 0) key[4 * v4 + 1] = 0xff800000u;
+        if (c.z < 0) key[4 * v4 + 2] = 0xff800000u;
+        if (c.w < 0) key[4 * v4 + 3] = 0xff800000u;
+      }
+    }
+  } else {
+    // the row tail (at most one thread of a chunk): element-wise
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      uint32_t kk = 0xff800000u;
+      if (v < seg && p0 + v <= plast) {
+        kk = __builtin_bit_cast(uint32_t, vr[p0 + v]);
+        if (mr && mr[p0 + v] < 0) kk = 0xff800000u;
+      }
+      key[v] = kk;
+    }
   }
+#pragma unroll
+  for (int v = 0; v < VPT; ++v)
+    key[v] = (v < seg && p0 + v <= plast) ? score_key(__builtin_bit_cast(float, key[v])) : 0u;
   auto count_ge = [&](uint32_t t) {
     int n = 0;
 #pragma unroll
-    for (int v = 0; v < 64; ++v) n += (key[v] >= t) ? 1 : 0;
+    for (int v = 0; v < VPT; ++v) n += (key[v] >= t) ? 1 : 0;
     return block_sum_1024(n, sh);
   };
   const int nvalid = count_ge(1u);
@@ -193,31 +229,31 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
   int nt = 0;
   if (!all) {
 #pragma unroll
-    for (int v = 0; v < 64; ++v) nt += (key[v] == T) ? 1 : 0;
+    for (int v = 0; v < VPT; ++v) nt += (key[v] == T) ? 1 : 0;
   }
   int ttot;
   const int tpre = block_excl_scan_1024(nt, sh, ttot);
-  uint64_t take = 0ull;
+  uint32_t take = 0u;
   int cnt = 0;
   {
     int tr = tpre;
 #pragma unroll
-    for (int v = 0; v < 64; ++v) {
+    for (int v = 0; v < VPT; ++v) {
       bool f;
       if (k <= 0) f = false;
       else if (all) f = key[v] != 0u;
       else if (key[v] > T) f = true;
       else if (key[v] == T) { f = tr < need; ++tr; }
       else f = false;
-      if (f) { take |= 1ull << v; ++cnt; }
+      if (f) { take |= 1u << v; ++cnt; }
     }
   }
   int total;
   int pre = block_excl_scan_1024(cnt, sh, total);
   const int64_t ob = (r * nchunk + chunk) * (int64_t)k;
 #pragma unroll
-  for (int v = 0; v < 64; ++v) {
-    if (take & (1ull << v)) {
+  for (int v = 0; v < VPT; ++v) {
+    if (take & (1u << v)) {
       const int64_t p = p0 + v;
       out_idx[ob + pre] = mr ? mr[p] : (int32_t)p;
       if (out_val) out_val[ob + pre] = vr[p];
@@ -246,11 +282,17 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+constexpr int kTopkVPT = 32;
+constexpr int64_t kTopkChunk = 1024 * kTopkVPT;      // columns per workgroup pass
+
 size_t topk_workspace_bytes(int64_t rows, int64_t cols, int k) {
-  if (cols <= 65536) return 0;
-  const int64_t nchunk = (cols + 65535) / 65536;
+  if (cols <= kTopkChunk) return 0;
+  const int64_t nchunk = (cols + kTopkChunk - 1) / kTopkChunk;
   return (size_t)(rows * nchunk * (int64_t)k) * (sizeof(float) + sizeof(int32_t));
 }
+
+int64_t topk_max_candidates() { return kTopkChunk; }
+int64_t topk_chunk_cols() { return kTopkChunk; }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
@@ -263,21 +305,24 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
       hipLaunchKernelGGL(topk_wave_kernel<32>, dim3(grid), dim3(256), 0, s, a.scores, a.rows, a.cols, a.row_stride, a.k, a.idx, a.count);
     return hipGetLastError();
   }
-  if (a.cols <= 65536) {
-    hipLaunchKernelGGL(topk_block_kernel, dim3((unsigned)a.rows), dim3(1024), 0, s, a.scores, (const int32_t*)nullptr,
-                       a.rows, a.cols, a.row_stride, (int64_t)65536, 1, a.k, a.idx, (float*)nullptr, a.count);
+  if (a.cols <= kTopkChunk) {
+    hipLaunchKernelGGL(topk_block_kernel<kTopkVPT>, dim3((unsigned)a.rows), dim3(1024), 0, s, a.scores,
+                       (const int32_t*)nullptr, a.rows, a.cols, a.row_stride, kTopkChunk, 1, a.k, a.idx,
+                       (float*)nullptr, a.count);
     return hipGetLastError();
   }
-  // two passes: per-chunk winners, then the winners' winners
-  const int nchunk = (int)((a.cols + 65535) / 65536);
-  hipLaunchKernelGGL(topk_block_kernel, dim3((unsigned)(a.rows * nchunk)), dim3(1024), 0, s, a.scores,
-                     (const int32_t*)nullptr, a.rows, a.cols, a.row_stride, (int64_t)65536, nchunk, a.k, a.cand_idx,
+  // two passes: per-chunk winners (an exact superset of the row's top-k), then
+  // the winners' winners; chunk winners are in ascending column order, so the
+  // concatenation is too and ties still resolve by column
+  const int nchunk = (int)((a.cols + kTopkChunk - 1) / kTopkChunk);
+  hipLaunchKernelGGL(topk_block_kernel<kTopkVPT>, dim3((unsigned)(a.rows * nchunk)), dim3(1024), 0, s, a.scores,
+                     (const int32_t*)nullptr, a.rows, a.cols, a.row_stride, kTopkChunk, nchunk, a.k, a.cand_idx,
                      a.cand_val, (int32_t*)nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t ccols = (int64_t)nchunk * a.k;       // <= 65536 by validation
-  hipLaunchKernelGGL(topk_block_kernel, dim3((unsigned)a.rows), dim3(1024), 0, s, (const float*)a.cand_val,
-                     (const int32_t*)a.cand_idx, a.rows, ccols, ccols, (int64_t)65536, 1, a.k, a.idx, (float*)nullptr,
+  const int64_t ccols = (int64_t)nchunk * a.k;       // <= kTopkChunk by validation
+  hipLaunchKernelGGL(topk_block_kernel<kTopkVPT>, dim3((unsigned)a.rows), dim3(1024), 0, s, (const float*)a.cand_val,
+                     (const int32_t*)a.cand_idx, a.rows, ccols, ccols, kTopkChunk, 1, a.k, a.idx, (float*)nullptr,
                      a.count);
   return hipGetLastError();
 }

@@ -161,8 +161,9 @@ HYS_API hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hy
  *
  * scores: rows x cols fp32 with row_stride (elements, >= cols).
  * idx: rows x k int32, contiguous.  Limits: cols < 2^31; k <= 4096; rows with
- * more than 65536 columns are split into 65536-column chunks, requiring
- * ceil(cols/65536) * k <= 65536, and need workspace.
+ * more than 32768 columns are split into 32768-column chunks whose winners
+ * are selected again, requiring ceil(cols/32768) * k <= 32768, and need
+ * workspace.
  */
 HYS_API hys_status hys_select_topk(const float* scores, int64_t rows, int64_t cols, int64_t row_stride, int32_t k,
                            int32_t* idx, int32_t* count, void* ws, size_t* ws_bytes, void* stream);

@@ -83,7 +83,7 @@ def test_topk_validation():
     assert L.hys_select_topk(None, 4, 10, 5, 3, None, None, None, ctypes.byref(nb), None) == INVALID
     assert L.hys_select_topk(None, 4, 10, 10, 5000, None, None, None, ctypes.byref(nb), None) == UNSUPPORTED
     assert L.hys_select_topk(None, 4, 1 << 20, 1 << 20, 1024, None, None, None, ctypes.byref(nb), None) == 0
-    assert nb.value == 4 * 16 * 1024 * 8          # chunk winners: index + value
+    assert nb.value == 4 * 32 * 1024 * 8          # chunk winners (32768-column chunks): index + value
     assert L.hys_select_topk(None, 4, 1 << 20, 1 << 20, 8192, None, None, None, ctypes.byref(nb), None) == UNSUPPORTED
     nb = ctypes.c_size_t(0)
     assert L.hys_select_topk(None, 4, 100, 100, 8, None, None, ctypes.c_void_p(FAKE), ctypes.byref(nb), None) == INVALID

@@ -92,7 +92,8 @@ def test_full_attention_tile_token_scores(name, L, Hq, Hkv, D):
 
 
 @pytest.mark.parametrize("rows,cols,k", [(300, 16, 4), (257, 512, 16), (64, 2048, 64), (33, 3000, 100),
-                                         (5, 65536, 1024), (3, 200001, 1024), (7, 100, 0), (9, 40, 50)])
+                                         (5, 65536, 1024), (3, 200001, 1024), (4, 32768, 1000), (2, 1048576, 1024),
+                                         (7, 100, 0), (9, 40, 50)])
 def test_select_topk_exact(rows, cols, k):
     """Same fp32 scores on both sides -> the index sets must be identical."""
     r = np.random.default_rng(rows * 7 + cols)
