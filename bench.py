@@ -198,26 +198,29 @@ def bench_prefill(args, dev):
     stages["sparse_attn"]["logical_gather_GBs"] = round(
         w.n_sparse * gather_bytes / (per_step["sparse_attn"] * 1e-3) / 1e9, 1)
 
-    # roofline of the dominant kernel (largest share of the step)
+    # roofline of the dominant kernel (largest share of the step).  Work is
+    # algorithmic: only causal (full layer) or selected-and-causal (sparse)
+    # (query, key) pairs, 4*D FLOP each, or the compulsory bytes of the window
+    # kernel.  The sparse kernel processes each query tile's union of selected
+    # blocks on MFMA, so its binding roof is MFMA; its logical gathered bytes
+    # (each query reading its own blocks) are reported beside it as context.
     dom = max(["full_attn+scores", "sparse_attn", "swa_gate"], key=lambda k: per_step[k])
-    if dom == "full_attn+scores":
-        ach = tflops[dom]
-        roof = {"kernel": "full_attn (causal + block scores)", "bound": "mfma", "achieved": round(ach, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "avg_launch_ms": round(per_step[dom] / launches[dom], 4),
-                "work_per_launch": f"{fl_full:.4g} FLOP", "traffic": None}
-    elif dom == "sparse_attn":
-        ach = gather_bytes / (per_step[dom] / launches[dom] * 1e-3) / 1e9
-        roof = {"kernel": "sparse_attn (block gather)", "bound": "hbm", "achieved": round(ach, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                "avg_launch_ms": round(per_step[dom] / launches[dom], 4),
-                "work_per_launch": f"{gather_bytes:.4g} logical gathered bytes", "traffic": None}
+    avg = per_step[dom] / launches[dom]
+    if dom in ("full_attn+scores", "sparse_attn"):
+        work = fl_full if dom == "full_attn+scores" else fl_sparse
+        ach = work / (avg * 1e-3) / 1e12
+        roof = {"kernel": "full_attn (causal + block scores)" if dom == "full_attn+scores"
+                else "sparse_attn (selected 64-key blocks, query-tile union)",
+                "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(avg, 4),
+                "work_per_launch": f"{work:.4g} FLOP (4*D per visible (query, head, key) pair)", "traffic": None}
+        if dom == "sparse_attn":
+            roof["logical_gather_GBs"] = round(gather_bytes / (avg * 1e-3) / 1e9, 1)
     else:
         byts = (w.L * w.Hq * w.D * (2 + 4 + 2) + 2 * w.L * w.Hkv * w.D * 2)
-        ach = byts / (per_step[dom] / launches[dom] * 1e-3) / 1e9
+        ach = byts / (avg * 1e-3) / 1e9
         roof = {"kernel": "swa_gate", "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                "avg_launch_ms": round(per_step[dom] / launches[dom], 4),
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "avg_launch_ms": round(avg, 4),
                 "work_per_launch": f"{byts:.4g} bytes", "traffic": None}
     res = {"w": w, "step_ms": step_ms, "stages": stages, "roofline": roof,
            "host": (q_h, k_h, v_h, kw_h, vw_h, gw_h)}

@@ -54,6 +54,8 @@ hys_status check_tensor(const hys_tensor4& t, const char* name, bool allow_fp8) 
   if (t.shape[3] != 64 && t.shape[3] != 128)
     return fail(HYS_ERR_UNSUPPORTED, "%s: head dim %lld not in {64, 128}", name, (long long)t.shape[3]);
   if (t.stride[3] != 1) return fail(HYS_ERR_INVALID_ARG, "%s: head-dim stride must be 1", name);
+  if (t.stride[1] >= (1ll << 24) || t.stride[2] >= (1ll << 24))
+    return fail(HYS_ERR_UNSUPPORTED, "%s: token/head strides must be below 2^24 elements", name);
   if (t.shape[1] >= (1ll << 30)) return fail(HYS_ERR_UNSUPPORTED, "%s: more than 2^30 tokens", name);
   const size_t es = elem_size(t.dtype);
   if (!aligned16(t.ptr)) return fail(HYS_ERR_INVALID_ARG, "%s: pointer not 16-byte aligned", name);

@@ -223,8 +223,48 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
   uint32_t kmask = 0u, vmask = 0u;     // staged units whose slot holds a key
   int my_kinfo = 0;
 
+  // First key of tile n when its 64 slots are the consecutive keys j0..j0+63
+  // (a full contiguous tile or a whole selected block): then one wave-uniform
+  // base pointer serves every load and no slot needs masking.
+  auto full_tile = [&](int n, int& j0) -> bool {
+    if (MODE == M_SPARSE_TOKEN) { j0 = 0; return false; }
+    if (MODE == M_SPARSE_BLOCK) { j0 = s_ulist[n] * 64; return j0 + 63 < a.Lk; }
+    j0 = kbase + n * 64;
+    return j0 + 63 <= kend;
+  };
+  // per-thread element offsets inside a tile (independent of the tile)
+  int koff[KU], voff[VU][4];
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int unit = tid + 256 * u;
+    koff[u] = (unit / (D / 8)) * (int)a.k_st + (unit % (D / 8)) * 8;
+  }
+#pragma unroll
+  for (int u = 0; u < VU; ++u) {
+    const int unit = tid + 256 * u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) voff[u][r] = ((unit / (D / 8)) * 4 + r) * (int)a.v_st + (unit % (D / 8)) * 8;
+  }
+  bool staged_full = true;
+
   auto stage_load = [&](int n, int g_) {
     const int kvh = g_;
+    int j0;
+    staged_full = full_tile(n, j0);
+    if (staged_full) {
+      const KT* kt = kb + (int64_t)j0 * a.k_st + (int64_t)kvh * a.k_sh;
+      const KT* vt = vb + (int64_t)j0 * a.v_st + (int64_t)kvh * a.v_sh;
+#pragma unroll
+      for (int u = 0; u < KU; ++u) kreg[u] = load8<KT>(kt + koff[u]);
+#pragma unroll
+      for (int u = 0; u < VU; ++u)
+        if (VUN % 256 == 0 || tid + 256 * u < VUN) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vreg[u][r] = load8<KT>(vt + voff[u][r]);
+        }
+      if (tid < 64) my_kinfo = j0 + tid;
+      return;
+    }
     kmask = 0u; vmask = 0u;
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
@@ -262,7 +302,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     for (int u = 0; u < KU; ++u) {
       const int unit = tid + 256 * u;
       const int key = unit / (D / 8), c8 = unit % (D / 8);
-      keep_if(kreg[u], (kmask >> u) & 1u);
+      if (!staged_full) keep_if(kreg[u], (kmask >> u) & 1u);
       Cvt8<CT> c = to_ct(kreg[u]);
       CT* dst = &Kb[key * KROW + c8 * 8];
       *(uint4*)dst = c.a;
@@ -274,7 +314,8 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
       if (VUN % 256 == 0 || unit < VUN) {
         const int kg = unit / (D / 8), dc = unit % (D / 8);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) keep_if(vreg[u][r], (vmask >> (4 * u + r)) & 1u);
+        for (int r = 0; r < 4; ++r)
+          if (!staged_full) keep_if(vreg[u][r], (vmask >> (4 * u + r)) & 1u);
         Cvt8<CT> r0 = to_ct(vreg[u][0]), r1 = to_ct(vreg[u][1]), r2 = to_ct(vreg[u][2]), r3 = to_ct(vreg[u][3]);
         if constexpr (!F32) {
 #pragma unroll
@@ -433,12 +474,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
         // S^T = K Q^T  (M = 64 keys as two 32-blocks, N = rows, K = D); the K
         // fragments of step c+1 are read while the MFMAs of step c issue
         f32x16 s[2][NB];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[mb][nb][i] = 0.f;
+        const f32x16 zero16 = {};
         if constexpr (F32) {
           float kn0 = Kc[ln * KROW + hh], kn1 = Kc[(32 + ln) * KROW + hh];
 #pragma unroll
@@ -447,8 +483,8 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
             if (c + 1 < NQC) { kn0 = Kc[ln * KROW + 2 * (c + 1) + hh]; kn1 = Kc[(32 + ln) * KROW + 2 * (c + 1) + hh]; }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-              s[0][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k0, qf[nb][c], s[0][nb], 0, 0, 0);
-              s[1][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k1, qf[nb][c], s[1][nb], 0, 0, 0);
+              s[0][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k0, qf[nb][c], c == 0 ? zero16 : s[0][nb], 0, 0, 0);
+              s[1][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k1, qf[nb][c], c == 0 ? zero16 : s[1][nb], 0, 0, 0);
             }
           }
         } else {
@@ -463,8 +499,8 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
             }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-              s[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), qf[nb][c], s[0][nb], 0, 0, 0);
-              s[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), qf[nb][c], s[1][nb], 0, 0, 0);
+              s[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), qf[nb][c], c == 0 ? zero16 : s[0][nb], 0, 0, 0);
+              s[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), qf[nb][c], c == 0 ? zero16 : s[1][nb], 0, 0, 0);
             }
           }
         }
@@ -474,12 +510,16 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
         if (MODE == M_FULL || MODE == M_FULL_BLOCK || MODE == M_FULL_TILE)
           need_mask = !(wave_full && (n * 64 + 63 <= wave_qmin) && (n * 64 + 63 <= kend));
         if (need_mask) {
+          int jt0 = 0;
+          if (MODE != M_SPARSE_TOKEN) full_tile(n, jt0);   // consecutive keys from jt0
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
               const int off = mb * 32 + 8 * i4 + 4 * hh;
-              const int4 ki = *(const int4*)&kic[off];
+              int4 ki;
+              if (MODE == M_SPARSE_TOKEN) ki = *(const int4*)&kic[off];
+              else ki = make_int4(jt0 + off, jt0 + off + 1, jt0 + off + 2, jt0 + off + 3);
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int kinf = e == 0 ? ki.x : (e == 1 ? ki.y : (e == 2 ? ki.z : ki.w));

@@ -118,7 +118,35 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
 
   // loads are unconditional from a clamped in-bounds key (key 0); empty slots
   // are zeroed when staged (see keep_if)
+  // per-thread element offsets inside a tile (independent of the tile)
+  int koff[KU], voff[VU][4];
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int unit = tid + 128 * u;
+    koff[u] = (unit / (D / 8)) * (int)a.k_st + (unit % (D / 8)) * 8;
+  }
+#pragma unroll
+  for (int u = 0; u < VU; ++u) {
+    const int unit = tid + 128 * u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) voff[u][r] = ((unit / (D / 8)) * 4 + r) * (int)a.v_st + (unit % (D / 8)) * 8;
+  }
+  bool staged_full = true;
+
   auto stage_load = [&](int t) {
+    // a contiguous tile of 64 valid keys: one uniform base, no masking
+    staged_full = !SPARSE && t * 64 + 63 < n;
+    if (staged_full) {
+      const KT* kt = kb + (int64_t)t * 64 * a.k_st;
+      const KT* vt = vb + (int64_t)t * 64 * a.v_st;
+#pragma unroll
+      for (int u = 0; u < KU; ++u) kreg[u] = load8<KT>(kt + koff[u]);
+#pragma unroll
+      for (int u = 0; u < VU; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vreg[u][r] = load8<KT>(vt + voff[u][r]);
+      return;
+    }
     kmask = 0u; vmask = 0u;
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
@@ -145,7 +173,7 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
     for (int u = 0; u < KU; ++u) {
       const int unit = tid + 128 * u;
       const int key = unit / (D / 8), c8 = unit % (D / 8);
-      keep_if(kreg[u], (kmask >> u) & 1u);
+      if (!staged_full) keep_if(kreg[u], (kmask >> u) & 1u);
       *(uint4*)&Kl[key * KROW + c8 * 8] = to_ct(kreg[u]).a;
     }
 #pragma unroll
@@ -153,7 +181,8 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
       const int unit = tid + 128 * u;
       const int kg = unit / (D / 8), dc = unit % (D / 8);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) keep_if(vreg[u][r], (vmask >> (4 * u + r)) & 1u);
+      for (int r = 0; r < 4; ++r)
+        if (!staged_full) keep_if(vreg[u][r], (vmask >> (4 * u + r)) & 1u);
       const uint4 r0 = to_ct(vreg[u][0]).a, r1 = to_ct(vreg[u][1]).a, r2 = to_ct(vreg[u][2]).a, r3 = to_ct(vreg[u][3]).a;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
@@ -186,10 +215,7 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
 
     // S^T = K q^T: 64 keys (2 M-blocks) x this wave's 32 heads; fragments read one step ahead
     f32x16 sacc[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[mb][i] = 0.f;
+    const f32x16 zero16 = {};
     uint4 kf0 = *(const uint4*)&Kl[ln * KROW + 8 * hh];
     uint4 kf1 = *(const uint4*)&Kl[(32 + ln) * KROW + 8 * hh];
 #pragma unroll
@@ -199,8 +225,8 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
         kf0 = *(const uint4*)&Kl[ln * KROW + 16 * (c + 1) + 8 * hh];
         kf1 = *(const uint4*)&Kl[(32 + ln) * KROW + 16 * (c + 1) + 8 * hh];
       }
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), qf[c], sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), qf[c], sacc[1], 0, 0, 0);
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), qf[c], c == 0 ? zero16 : sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), qf[c], c == 0 ? zero16 : sacc[1], 0, 0, 0);
     }
     // mask empty list slots and padding heads
     const int rem = nkeys - t * 64;
