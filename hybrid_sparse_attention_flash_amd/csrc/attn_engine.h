@@ -104,6 +104,8 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
   const int q0 = qt * a.BQ;
   const int q_last = min(q0 + a.BQ, a.Lq) - 1;
   const int HC = a.HC;
+  // block scores reduced inside each wave when a query's heads are adjacent lanes
+  const bool lane_scores = (MODE == M_FULL_BLOCK) && (32 % HC == 0);
 
   // ---- per-WG selection lists ----------------------------------------------
   int ntiles = 0;
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
   for (int u = 0; u < VU; ++u) {
     const int unit = tid + 256 * u;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) voff[u][r] = ((unit / (D / 8)) * 4 + r) * (int)a.v_st + (unit % (D / 8)) * 8;
+    for (int r = 0; r < 4; ++r) voff[u][r] = ((unit % 16) * 4 + r) * (int)a.v_st + (unit / 16) * 8;
   }
   bool staged_full = true;
 
@@ -279,7 +281,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     for (int u = 0; u < VU; ++u) {
       const int unit = tid + 256 * u;
       if (VUN % 256 == 0 || unit < VUN) {
-        const int kg = unit / (D / 8), dc = unit % (D / 8);
+        const int kg = unit % 16, dc = unit / 16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int kp = keypos(n, kg * 4 + r);
@@ -312,7 +314,9 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     for (int u = 0; u < VU; ++u) {
       const int unit = tid + 256 * u;
       if (VUN % 256 == 0 || unit < VUN) {
-        const int kg = unit / (D / 8), dc = unit % (D / 8);
+        // the 16 lanes of one write cover the 16 key groups of one V^T row:
+        // consecutive 8-byte slots, no bank conflicts
+        const int kg = unit % 16, dc = unit / 16;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (!staged_full) keep_if(vreg[u][r], (vmask >> (4 * u + r)) & 1u);
@@ -418,7 +422,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
 
     // score emission for tile n (reads red[n & 1]); called by all threads after a barrier
     auto emit_scores = [&](int n) {
-      if (MODE == M_FULL_BLOCK) {
+      if (MODE == M_FULL_BLOCK && !lane_scores) {
         const float* rb = red + (n & 1) * RS;
         float* sc = a.scores + (int64_t)g * a.sc_sg + (int64_t)b * a.sc_sb;
         for (int t = tid; t < a.BQ; t += 256) {
@@ -467,7 +471,14 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
       if (!active) {
         if (MODE == M_FULL_BLOCK && hh == 0) {
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) red[(n & 1) * RS + wave * 32 * NB + nb * 32 + ln] = kNegInf;
+          for (int nb = 0; nb < NB; ++nb) {
+            if (lane_scores) {
+              if (valid[nb] && (ln % HC) == 0)
+                a.scores[(int64_t)g * a.sc_sg + (int64_t)b * a.sc_sb + (int64_t)qpos[nb] * a.sc_sr + n] = kNegInf;
+            } else {
+              red[(n & 1) * RS + wave * 32 * NB + nb * 32 + ln] = kNegInf;
+            }
+          }
         }
         if (MODE == M_FULL_TILE) red[(n & 1) * RS + wave * 64 + lane] = kNegInf;
       } else {
@@ -578,8 +589,19 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[mb][nb][i]);
-          mt = fmaxf(mt, __shfl_xor(mt, 32));
-          if (MODE == M_FULL_BLOCK && hh == 0) red[(n & 1) * RS + wave * 32 * NB + nb * 32 + ln] = mt;
+          mt = xor32_max(mt);
+          if (MODE == M_FULL_BLOCK) {
+            if (lane_scores) {
+              // heads of a query are HC adjacent lanes: reduce them in-wave and
+              // let the group's first lane store the block score
+              const float gm = group_max(mt, HC);
+              if (hh == 0 && valid[nb] && (ln % HC) == 0)
+                a.scores[(int64_t)g * a.sc_sg + (int64_t)b * a.sc_sb + (int64_t)qpos[nb] * a.sc_sr + n] =
+                    gm * a.logit_scale;
+            } else if (hh == 0) {
+              red[(n & 1) * RS + wave * 32 * NB + nb * 32 + ln] = mt;
+            }
+          }
           const float mnew = fmaxf(m_run[nb], mt);
           const float muse = (mnew == kNegInf) ? 0.f : mnew;
           alpha[nb] = __builtin_amdgcn_exp2f((m_run[nb] - muse) * c2);

@@ -70,6 +70,26 @@ __device__ __forceinline__ f32x4 fp8x4_to_f32x4(uint32_t w) {
   return r;
 }
 
+// max(v[l], v[l ^ 32]) for every lane l.
+__device__ __forceinline__ float xor32_max(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+
+// max over aligned groups of `width` consecutive lanes (width in {1,2,4,8,16,32},
+// wave-uniform), every lane of a group receiving the group max.  Lane pairs
+// are exchanged with DPP (quad_perm, row_half_mirror, row_mirror) inside a
+// 16-lane row; the 32-wide step crosses rows with a shuffle.
+__device__ __forceinline__ float group_max(float v, int width) {
+  if (width >= 2)
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+  if (width >= 4)
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+  if (width >= 8)
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+  if (width >= 16)
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+  if (width >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -129,7 +129,7 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
   for (int u = 0; u < VU; ++u) {
     const int unit = tid + 128 * u;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) voff[u][r] = ((unit / (D / 8)) * 4 + r) * (int)a.v_st + (unit % (D / 8)) * 8;
+    for (int r = 0; r < 4; ++r) voff[u][r] = ((unit % 16) * 4 + r) * (int)a.v_st + (unit / 16) * 8;
   }
   bool staged_full = true;
 
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
       const int unit = tid + 128 * u;
-      const int kg = unit / (D / 8), dc = unit % (D / 8);
+      const int kg = unit % 16, dc = unit / 16;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = keyof(t, kg * 4 + r);
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
       const int unit = tid + 128 * u;
-      const int kg = unit / (D / 8), dc = unit % (D / 8);
+      const int kg = unit % 16, dc = unit / 16;     // one write covers a V^T row's 16 key groups
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (!staged_full) keep_if(vreg[u][r], (vmask >> (4 * u + r)) & 1u);
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[mb][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = xor32_max(mt);
     const float mnew = fmaxf(m_run, mt);
     const float muse = (mnew == kNegInf) ? 0.f : mnew;
     const float alpha = __builtin_amdgcn_exp2f((m_run - muse) * c2);
