@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
 
   // key position of tile slot t of tile n; -1 when the slot is empty.
   // For the token mode, bit 30 flags a selected (as opposed to window-only) token.
-  auto keypos = [&](int n, int t) -> int {
+  auto keypos = [&](int n, int t) __attribute__((always_inline)) -> int {
     if (MODE == M_SPARSE_BLOCK) {
       const int j = s_ulist[n] * 64 + t;
       return j < a.Lk ? j : -1;
@@ -228,41 +228,35 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
   // First key of tile n when its 64 slots are the consecutive keys j0..j0+63
   // (a full contiguous tile or a whole selected block): then one wave-uniform
   // base pointer serves every load and no slot needs masking.
-  auto full_tile = [&](int n, int& j0) -> bool {
+  auto full_tile = [&](int n, int& j0) __attribute__((always_inline)) -> bool {
     if (MODE == M_SPARSE_TOKEN) { j0 = 0; return false; }
     if (MODE == M_SPARSE_BLOCK) { j0 = s_ulist[n] * 64; return j0 + 63 < a.Lk; }
     j0 = kbase + n * 64;
     return j0 + 63 <= kend;
   };
-  // per-thread element offsets inside a tile (independent of the tile)
-  int koff[KU], voff[VU][4];
-#pragma unroll
-  for (int u = 0; u < KU; ++u) {
-    const int unit = tid + 256 * u;
-    koff[u] = (unit / (D / 8)) * (int)a.k_st + (unit % (D / 8)) * 8;
-  }
-#pragma unroll
-  for (int u = 0; u < VU; ++u) {
-    const int unit = tid + 256 * u;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) voff[u][r] = ((unit % 16) * 4 + r) * (int)a.v_st + (unit / 16) * 8;
-  }
+  // per-thread element offsets inside a tile (independent of the tile): unit
+  // tid + 256u covers key tid/(D/8) + u*256/(D/8) (K) and, for V, key group
+  // (tid%16) with d chunk tid/16 + 16u, so one base register per operand and
+  // wave-uniform strides address every unit
+  const int koff0 = (tid / (D / 8)) * (int)a.k_st + (tid % (D / 8)) * 8;
+  const int kstep = (256 / (D / 8)) * (int)a.k_st;
+  const int voff0 = ((tid % 16) * 4) * (int)a.v_st + (tid / 16) * 8;
   bool staged_full = true;
 
-  auto stage_load = [&](int n, int g_) {
+  auto stage_load = [&](int n, int g_) __attribute__((always_inline)) {
     const int kvh = g_;
     int j0;
-    staged_full = full_tile(n, j0);
+    staged_full = __builtin_amdgcn_readfirstlane((int)full_tile(n, j0)) != 0;
     if (staged_full) {
       const KT* kt = kb + (int64_t)j0 * a.k_st + (int64_t)kvh * a.k_sh;
       const KT* vt = vb + (int64_t)j0 * a.v_st + (int64_t)kvh * a.v_sh;
 #pragma unroll
-      for (int u = 0; u < KU; ++u) kreg[u] = load8<KT>(kt + koff[u]);
+      for (int u = 0; u < KU; ++u) kreg[u] = load8<KT>(kt + koff0 + u * kstep);
 #pragma unroll
       for (int u = 0; u < VU; ++u)
         if (VUN % 256 == 0 || tid + 256 * u < VUN) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) vreg[u][r] = load8<KT>(vt + voff[u][r]);
+          for (int r = 0; r < 4; ++r) vreg[u][r] = load8<KT>(vt + voff0 + r * (int)a.v_st + u * 128);
         }
       if (tid < 64) my_kinfo = j0 + tid;
       return;
@@ -297,14 +291,18 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     }
   };
 
-  auto stage_store = [&](int buf) {
+  // Registers of the staged tile -> LDS stage `buf` (K row-major, V transposed).
+  // Instantiated twice so that whole contiguous tiles store without any
+  // per-unit masking; the choice is wave-uniform.
+  auto stage_store_impl = [&](int buf, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     CT* Kb = Klds + buf * (64 * KROW);
     CT* Vb = VTlds + buf * (D * VROW);
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
       const int unit = tid + 256 * u;
       const int key = unit / (D / 8), c8 = unit % (D / 8);
-      if (!staged_full) keep_if(kreg[u], (kmask >> u) & 1u);
+      if constexpr (MASKED) keep_if(kreg[u], (kmask >> u) & 1u);
       Cvt8<CT> c = to_ct(kreg[u]);
       CT* dst = &Kb[key * KROW + c8 * 8];
       *(uint4*)dst = c.a;
@@ -317,9 +315,10 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
         // the 16 lanes of one write cover the 16 key groups of one V^T row:
         // consecutive 8-byte slots, no bank conflicts
         const int kg = unit % 16, dc = unit / 16;
+        if constexpr (MASKED) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (!staged_full) keep_if(vreg[u][r], (vmask >> (4 * u + r)) & 1u);
+          for (int r = 0; r < 4; ++r) keep_if(vreg[u][r], (vmask >> (4 * u + r)) & 1u);
+        }
         Cvt8<CT> r0 = to_ct(vreg[u][0]), r1 = to_ct(vreg[u][1]), r2 = to_ct(vreg[u][2]), r3 = to_ct(vreg[u][3]);
         if constexpr (!F32) {
 #pragma unroll
@@ -345,6 +344,10 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
       }
     }
     if (tid < 64) kinfo[buf * 64 + tid] = my_kinfo;
+  };
+  auto stage_store = [&](int buf) __attribute__((always_inline)) {
+    if (staged_full) stage_store_impl(buf, std::false_type{});
+    else stage_store_impl(buf, std::true_type{});
   };
 
   const QT* qbase = (const QT*)a.q + (int64_t)b * a.q_sb;
@@ -419,9 +422,10 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     }
 
     const float c2 = a.scale_log2;
+    const float lazy_raw = kLazyLog2 / c2;    // the slack in raw dot-product units
 
     // score emission for tile n (reads red[n & 1]); called by all threads after a barrier
-    auto emit_scores = [&](int n) {
+    auto emit_scores = [&](int n) __attribute__((always_inline)) {
       if (MODE == M_FULL_BLOCK && !lane_scores) {
         const float* rb = red + (n & 1) * RS;
         float* sc = a.scores + (int64_t)g * a.sc_sg + (int64_t)b * a.sc_sb;
@@ -499,21 +503,44 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
             }
           }
         } else {
-          uint4 kn0 = *(const uint4*)&Kc[ln * KROW + 8 * hh];
-          uint4 kn1 = *(const uint4*)&Kc[(32 + ln) * KROW + 8 * hh];
+          // K fragments are read two k-steps ahead of the MFMAs that use them
+          uint4 kf[NQC][2];
+          auto kfrag = [&](int c) __attribute__((always_inline)) {
+            kf[c][0] = *(const uint4*)&Kc[ln * KROW + 16 * c + 8 * hh];
+            kf[c][1] = *(const uint4*)&Kc[(32 + ln) * KROW + 16 * c + 8 * hh];
+          };
+          kfrag(0);
+          kfrag(1);
 #pragma unroll
           for (int c = 0; c < NQC; ++c) {
-            const uint4 k0 = kn0, k1 = kn1;
-            if (c + 1 < NQC) {
-              kn0 = *(const uint4*)&Kc[ln * KROW + 16 * (c + 1) + 8 * hh];
-              kn1 = *(const uint4*)&Kc[(32 + ln) * KROW + 16 * (c + 1) + 8 * hh];
-            }
+            if (c + 2 < NQC) kfrag(c + 2);
+            // keep the reads ahead: the scheduler would otherwise sink each
+            // read next to its MFMA and expose the full LDS latency per step
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-              s[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), qf[nb][c], c == 0 ? zero16 : s[0][nb], 0, 0, 0);
-              s[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), qf[nb][c], c == 0 ? zero16 : s[1][nb], 0, 0, 0);
+              s[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[c][0]), qf[nb][c], c == 0 ? zero16 : s[0][nb], 0, 0, 0);
+              s[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[c][1]), qf[nb][c], c == 0 ? zero16 : s[1][nb], 0, 0, 0);
             }
           }
+        }
+
+        // V^T fragments (A operand of O^T): the first d block is read now so
+        // that its LDS latency hides under the softmax; later blocks are read
+        // one d block ahead of their MFMAs
+        typedef typename std::conditional<F32, float, uint4>::type VFrag;
+        VFrag vf[F32 ? 1 : NDB][4];
+        auto vfrag = [&](int db, int kc) __attribute__((always_inline)) {
+          const CT* vr = &Vc[(db * 32 + ln) * VROW + 16 * kc + 4 * hh];
+          const uint2 lo = *(const uint2*)vr;
+          const uint2 hi = *(const uint2*)(vr + 8);
+          uint4 va; va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
+          return va;
+        };
+        if constexpr (!F32) {
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) vf[0][kc] = vfrag(0, kc);
+          __builtin_amdgcn_sched_barrier(0);
         }
 
         // masking
@@ -578,8 +605,12 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
           red[(n & 1) * RS + wave * 64 + off] = cm[0];
         }
 
-        // online softmax (base 2 on raw dot products); O is rescaled only when
-        // some row's running max moved
+        // online softmax (base 2 on raw dot products) with a lazily updated
+        // reference maximum: a row's reference moves only when the tile max
+        // exceeds it by more than kLazyLog2 (probabilities then stay below
+        // 2^kLazyLog2), so O and l are rescaled in few tiles.  The final
+        // normalisation and the LSE use the same reference, so the result is
+        // exact up to rounding.
         float alpha[NB];
         bool moved = false;
 #pragma unroll
@@ -594,7 +625,15 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
             if (lane_scores) {
               // heads of a query are HC adjacent lanes: reduce them in-wave and
               // let the group's first lane store the block score
-              const float gm = group_max(mt, HC);
+              float gm = mt;
+              switch (HC) {
+                case 2: gm = group_max<2>(mt); break;
+                case 4: gm = group_max<4>(mt); break;
+                case 8: gm = group_max<8>(mt); break;
+                case 16: gm = group_max<16>(mt); break;
+                case 32: gm = group_max<32>(mt); break;
+                default: break;
+              }
               if (hh == 0 && valid[nb] && (ln % HC) == 0)
                 a.scores[(int64_t)g * a.sc_sg + (int64_t)b * a.sc_sb + (int64_t)qpos[nb] * a.sc_sr + n] =
                     gm * a.logit_scale;
@@ -602,21 +641,24 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
               red[(n & 1) * RS + wave * 32 * NB + nb * 32 + ln] = mt;
             }
           }
-          const float mnew = fmaxf(m_run[nb], mt);
-          const float muse = (mnew == kNegInf) ? 0.f : mnew;
-          alpha[nb] = __builtin_amdgcn_exp2f((m_run[nb] - muse) * c2);
-          moved = moved || (mnew != m_run[nb]);
-          m_run[nb] = mnew;
-          const float mc = muse * c2;
+          // true when the reference is -inf and mt finite; false when both are -inf
+          const bool need = mt > m_run[nb] + lazy_raw;
+          const float mref = need ? mt : m_run[nb];
+          alpha[nb] = need ? __builtin_amdgcn_exp2f((m_run[nb] - mref) * c2) : 1.f;
+          moved = moved || need;
+          m_run[nb] = mref;
+          const float mc = (mref == kNegInf) ? 0.f : mref * c2;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[mb][nb][i] = __builtin_amdgcn_exp2f(fmaf(s[mb][nb][i], c2, -mc));
+          // the row sum is taken over the fp32 probabilities, so the LSE is
+          // the exact log-sum-exp up to fp32 rounding
           float ps = 0.f;
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][nb][i], c2, -mc));
-              s[mb][nb][i] = p;
-              ps += p;
-            }
+            for (int i = 0; i < 16; ++i) ps += s[mb][nb][i];
           l_run[nb] = fmaf(l_run[nb], alpha[nb], ps);
         }
         if (__ballot(moved) != 0ull) {
@@ -660,22 +702,18 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
               pf[kc][nb] = as_bf16x8(pk);
             }
           }
-          auto vfrag = [&](int db, int kc) {
-            const CT* vr = &Vc[(db * 32 + ln) * VROW + 16 * kc + 4 * hh];
-            const uint2 lo = *(const uint2*)vr;
-            const uint2 hi = *(const uint2*)(vr + 8);
-            uint4 va; va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
-            return va;
-          };
-          uint4 vn = vfrag(0, 0);
 #pragma unroll
-          for (int st = 0; st < NDB * 4; ++st) {
-            const int db = st >> 2, kc = st & 3;
-            const uint4 va = vn;
-            if (st + 1 < NDB * 4) vn = vfrag((st + 1) >> 2, (st + 1) & 3);
+          for (int db = 0; db < NDB; ++db) {
+            if (db + 1 < NDB) {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-              acc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), pf[kc][nb], acc[nb][db], 0, 0, 0);
+              for (int kc = 0; kc < 4; ++kc) vf[db + 1][kc] = vfrag(db + 1, kc);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb)
+                acc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[db][kc]), pf[kc][nb], acc[nb][db], 0, 0, 0);
           }
         }
       }

@@ -22,6 +22,10 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// Slack of the online softmax's reference maximum, in base-2 exponent units:
+// a row's reference moves only when a tile maximum exceeds it by more than
+// this, so probabilities stay below 2^kLazyLog2 and O is rescaled rarely.
+constexpr float kLazyLog2 = 8.0f;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
   return __builtin_bit_cast(float, (uint32_t)x << 16);
@@ -73,20 +77,20 @@ __device__ __forceinline__ f32x4 fp8x4_to_f32x4(uint32_t w) {
 // max(v[l], v[l ^ 32]) for every lane l.
 __device__ __forceinline__ float xor32_max(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
 
-// max over aligned groups of `width` consecutive lanes (width in {1,2,4,8,16,32},
-// wave-uniform), every lane of a group receiving the group max.  Lane pairs
-// are exchanged with DPP (quad_perm, row_half_mirror, row_mirror) inside a
-// 16-lane row; the 32-wide step crosses rows with a shuffle.
-__device__ __forceinline__ float group_max(float v, int width) {
-  if (width >= 2)
+// max over aligned groups of W consecutive lanes (W in {2,4,8,16,32}), every
+// lane of a group receiving the group max.  Lane pairs are exchanged with DPP
+// (quad_perm, row_half_mirror, row_mirror) inside a 16-lane row; the 32-wide
+// step crosses rows with a shuffle.
+template <int W> __device__ __forceinline__ float group_max(float v) {
+  if (W >= 2)
     v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
-  if (width >= 4)
+  if (W >= 4)
     v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
-  if (width >= 8)
+  if (W >= 8)
     v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
-  if (width >= 16)
+  if (W >= 16)
     v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
-  if (width >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  if (W >= 32) v = fmaxf(v, __shfl_xor(v, 16));
   return v;
 }
 
@@ -134,14 +138,16 @@ template <typename KT> __device__ __forceinline__ Raw8<KT> zero8() { Raw8<KT> r;
 // load makes the compiler wait for every earlier load before issuing the
 // next, which serialises the whole prefetch); the select happens when the
 // data is consumed.
+__device__ __forceinline__ uint32_t sel0(uint32_t x, bool ok) { return ok ? x : 0u; }
 __device__ __forceinline__ void keep_if(Raw8<float>& r, bool ok) {
-  if (!ok) { r.a = make_uint4(0u, 0u, 0u, 0u); r.b = r.a; }
+  r.a = make_uint4(sel0(r.a.x, ok), sel0(r.a.y, ok), sel0(r.a.z, ok), sel0(r.a.w, ok));
+  r.b = make_uint4(sel0(r.b.x, ok), sel0(r.b.y, ok), sel0(r.b.z, ok), sel0(r.b.w, ok));
 }
 __device__ __forceinline__ void keep_if(Raw8<uint16_t>& r, bool ok) {
-  if (!ok) r.a = make_uint4(0u, 0u, 0u, 0u);
+  r.a = make_uint4(sel0(r.a.x, ok), sel0(r.a.y, ok), sel0(r.a.z, ok), sel0(r.a.w, ok));
 }
 __device__ __forceinline__ void keep_if(Raw8<uint8_t>& r, bool ok) {
-  if (!ok) r.a = make_uint2(0u, 0u);
+  r.a = make_uint2(sel0(r.a.x, ok), sel0(r.a.y, ok));
 }
 
 // 8 elements in compute layout: bf16 -> one uint4, fp32 -> two uint4
