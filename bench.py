@@ -95,10 +95,10 @@ def run_block(blk, inp, timer=None):
     rec("full_attn+scores", lambda: blk.full(q[0], k, v))
     rec("select_topk", blk.select)
     for l in range(blk.n_sparse):
-        rec("sparse_attn", lambda: ops.hys_sparse_attn_fwd(q[l + 1], k, v, blk.idx, blk.o_sp, blk.lse_sp,
-                                                           granularity=64, topk=blk.topk, q_tile=1))
-        rec("swa_gate", lambda: ops.hys_swa_gate_fwd(q[l + 1], kw[l], vw[l], blk.window, blk.o_sp, blk.lse_sp,
-                                                     gw[l], blk.o_layers[l]))
+        # one pass per sparse layer: selected blocks of the shared KV, the
+        # layer's own window, and the gate
+        rec("sparse_layer", lambda: ops.hys_sparse_layer_fwd(q[l + 1], k, v, blk.idx, kw[l], vw[l], blk.window,
+                                                             gw[l], blk.o_layers[l], topk=blk.topk))
 
 
 # ---------------------------------------------------------------------------
@@ -184,10 +184,10 @@ def bench_prefill(args, dev):
     fl_sparse = 4.0 * w.D * keys_sel
     win_keys = sum(min(i + 1, w.window) for i in range(w.L)) * w.Hq * w.B
     fl_swa = 4.0 * w.D * win_keys
+    fl_layer = fl_sparse + fl_swa
     tflops = {
         "full_attn+scores": fl_full / (per_step["full_attn+scores"] * 1e-3) / 1e12,
-        "sparse_attn": w.n_sparse * fl_sparse / (per_step["sparse_attn"] * 1e-3) / 1e12,
-        "swa_gate": w.n_sparse * fl_swa / (per_step["swa_gate"] * 1e-3) / 1e12,
+        "sparse_layer": w.n_sparse * fl_layer / (per_step["sparse_layer"] * 1e-3) / 1e12,
     }
     # logical gathered K/V bytes of the sparse branch per layer (per KV head reading of each query's keys)
     gather_bytes = keys_sel / w.G * w.D * 2 * 2
@@ -195,33 +195,26 @@ def bench_prefill(args, dev):
     for k, v in tflops.items():
         stages[k]["tflops"] = round(v, 2)
         stages[k]["frac_mfma_bf16"] = round(v / PEAK_BF16_TFLOPS, 4)
-    stages["sparse_attn"]["logical_gather_GBs"] = round(
-        w.n_sparse * gather_bytes / (per_step["sparse_attn"] * 1e-3) / 1e9, 1)
+    stages["sparse_layer"]["logical_gather_GBs"] = round(
+        w.n_sparse * gather_bytes / (per_step["sparse_layer"] * 1e-3) / 1e9, 1)
 
     # roofline of the dominant kernel (largest share of the step).  Work is
-    # algorithmic: only causal (full layer) or selected-and-causal (sparse)
-    # (query, key) pairs, 4*D FLOP each, or the compulsory bytes of the window
-    # kernel.  The sparse kernel processes each query tile's union of selected
-    # blocks on MFMA, so its binding roof is MFMA; its logical gathered bytes
-    # (each query reading its own blocks) are reported beside it as context.
-    dom = max(["full_attn+scores", "sparse_attn", "swa_gate"], key=lambda k: per_step[k])
+    # algorithmic: only causal (full layer), or selected-and-causal plus
+    # in-window (sparse layer) (query, key) pairs, 4*D FLOP each.  The sparse
+    # layer processes each query tile's union of selected blocks on MFMA, so
+    # its binding roof is MFMA; its logical gathered bytes (each query reading
+    # its own blocks) are reported beside it as context.
+    dom = max(["full_attn+scores", "sparse_layer"], key=lambda k: per_step[k])
     avg = per_step[dom] / launches[dom]
-    if dom in ("full_attn+scores", "sparse_attn"):
-        work = fl_full if dom == "full_attn+scores" else fl_sparse
-        ach = work / (avg * 1e-3) / 1e12
-        roof = {"kernel": "full_attn (causal + block scores)" if dom == "full_attn+scores"
-                else "sparse_attn (selected 64-key blocks, query-tile union)",
-                "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(avg, 4),
-                "work_per_launch": f"{work:.4g} FLOP (4*D per visible (query, head, key) pair)", "traffic": None}
-        if dom == "sparse_attn":
-            roof["logical_gather_GBs"] = round(gather_bytes / (avg * 1e-3) / 1e9, 1)
-    else:
-        byts = (w.L * w.Hq * w.D * (2 + 4 + 2) + 2 * w.L * w.Hkv * w.D * 2)
-        ach = byts / (avg * 1e-3) / 1e9
-        roof = {"kernel": "swa_gate", "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "avg_launch_ms": round(avg, 4),
-                "work_per_launch": f"{byts:.4g} bytes", "traffic": None}
+    work = fl_full if dom == "full_attn+scores" else fl_layer
+    ach = work / (avg * 1e-3) / 1e12
+    roof = {"kernel": "full_attn (causal + block scores)" if dom == "full_attn+scores"
+            else "sparse_layer (selected 64-key blocks, query-tile union; own 128-key window; gate)",
+            "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(avg, 4),
+            "work_per_launch": f"{work:.4g} FLOP (4*D per visible (query, head, key) pair)", "traffic": None}
+    if dom == "sparse_layer":
+        roof["logical_gather_GBs"] = round(gather_bytes / (avg * 1e-3) / 1e9, 1)
     res = {"w": w, "step_ms": step_ms, "stages": stages, "roofline": roof,
            "host": (q_h, k_h, v_h, kw_h, vw_h, gw_h)}
     del inp, blk

@@ -16,7 +16,7 @@ HYS_SCORE_NONE, HYS_SCORE_BLOCK, HYS_SCORE_TILE_TOKEN = 0, 1, 2
 # every symbol include/hys.h declares
 EXPORTED = (
     "hys_full_attn_fwd", "hys_select_topk", "hys_sparse_attn_fwd", "hys_swa_gate_fwd",
-    "hys_decode_step", "hys_last_error", "hys_status_string", "hys_abi_version",
+    "hys_decode_step", "hys_sparse_layer_fwd", "hys_last_error", "hys_status_string", "hys_abi_version",
 )
 
 
@@ -70,8 +70,10 @@ def load(path: str = LIB_PATH):
     lib.hys_swa_gate_fwd.argtypes = [P(HysAttnParams), T4, T4, T4, ctypes.c_int32, T4, vp, vp, vp, T4, vp]
     lib.hys_decode_step.argtypes = [P(HysDecodeParams), T4, T4, T4, P(ctypes.c_int64), T4, vp, vp, ctypes.c_int32,
                                     P(T4), P(T4), vp, P(sz), vp]
+    lib.hys_sparse_layer_fwd.argtypes = [P(HysAttnParams), T4, T4, T4, P(HysSparseParams), vp, T4, T4,
+                                         ctypes.c_int32, vp, vp, T4, vp]
     for name in ("hys_full_attn_fwd", "hys_select_topk", "hys_sparse_attn_fwd", "hys_swa_gate_fwd",
-                 "hys_decode_step"):
+                 "hys_decode_step", "hys_sparse_layer_fwd"):
         getattr(lib, name).restype = ctypes.c_int
     lib.hys_last_error.restype = ctypes.c_char_p
     lib.hys_last_error.argtypes = []

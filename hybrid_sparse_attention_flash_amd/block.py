@@ -3,7 +3,8 @@
 HySparse block (QbitAI HySparse article, method section): the full layer runs
 causal attention and emits block scores; one top-k per query picks the blocks;
 every sparse layer attends over those blocks of the shared KV and over its own
-128-token window, merged by the sigmoid gate.
+128-token window, merged by the sigmoid gate (one fused call per layer, or the
+sparse and window+gate calls separately).
 
 HySparse2 block (airebao HySparse2 news, inner KV Reuse / token-level selection /
 forced recent window): the full layer emits per-tile token scores; one top-k
@@ -25,10 +26,11 @@ class HySparseBlock:
     """One HySparse hybrid block: 1 full layer + N gated sparse layers."""
 
     def __init__(self, B, L, Hq, Hkv, D, n_sparse, topk, window=128, block=64, device="cuda",
-                 out_dtype=torch.float32, softmax_scale=None):
+                 out_dtype=torch.float32, softmax_scale=None, fused=True):
         self.B, self.L, self.Hq, self.Hkv, self.D = B, L, Hq, Hkv, D
         self.n_sparse, self.topk, self.window, self.block = n_sparse, topk, window, block
         self.scale = softmax_scale
+        self.fused = fused
         nblk = (L + block - 1) // block
         f32 = dict(dtype=torch.float32, device=device)
         self.o_full = torch.empty(B, L, Hq, D, dtype=out_dtype, device=device)
@@ -36,8 +38,9 @@ class HySparseBlock:
         self.scores = torch.empty(B, L, nblk, **f32)
         self.idx = torch.empty(B, L, topk, dtype=torch.int32, device=device)
         self.count = torch.empty(B * L, dtype=torch.int32, device=device)
-        self.o_sp = torch.empty(B, L, Hq, D, **f32)
-        self.lse_sp = torch.empty(B, Hq, L, **f32)
+        # the two-call form's intermediate sparse branch
+        self.o_sp = None if fused else torch.empty(B, L, Hq, D, **f32)
+        self.lse_sp = None if fused else torch.empty(B, Hq, L, **f32)
         self.o_layers = [torch.empty(B, L, Hq, D, dtype=out_dtype, device=device) for _ in range(n_sparse)]
 
     def full(self, q0, k, v):
@@ -48,6 +51,10 @@ class HySparseBlock:
         ops.hys_select_topk(self.scores.view(B * L, -1), self.topk, self.idx.view(B * L, self.topk), self.count)
 
     def sparse_layer(self, l, q, k, v, kw, vw, gate_w):
+        if self.fused:
+            ops.hys_sparse_layer_fwd(q, k, v, self.idx, kw, vw, self.window, gate_w, self.o_layers[l], topk=self.topk,
+                                     softmax_scale=self.scale)
+            return
         ops.hys_sparse_attn_fwd(q, k, v, self.idx, self.o_sp, self.lse_sp, granularity=self.block,
                                 topk=self.topk, q_tile=1, softmax_scale=self.scale)
         ops.hys_swa_gate_fwd(q, kw, vw, self.window, self.o_sp, self.lse_sp, gate_w, self.o_layers[l],

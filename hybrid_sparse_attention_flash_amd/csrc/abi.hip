@@ -271,6 +271,33 @@ hys_status hys_select_topk(const float* scores, int64_t rows, int64_t cols, int6
   }
 }
 
+// Row sets of the block-selection modes (granularity 64, per-query selection):
+// BQ queries x G heads per workgroup, BQ * k <= 4 * rows so the union of the
+// row set's selected blocks fits the per-workgroup list.
+hys_status setup_block_selection(hys::AttnArgs& a, const hys_sparse_params* sp, int64_t G, int64_t L, int64_t B,
+                                 int64_t Hkv, int& grid) {
+  if (sp->q_tile != 1) return fail(HYS_ERR_UNSUPPORTED, "granularity 64 needs q_tile 1");
+  if (sp->forced_window != 0) return fail(HYS_ERR_UNSUPPORTED, "granularity 64 has no forced window");
+  if (sp->k > 64) return fail(HYS_ERR_UNSUPPORTED, "granularity 64 needs k <= 64");
+  if (G > 256) return fail(HYS_ERR_UNSUPPORTED, "more than 256 query heads per KV head");
+  const int64_t nblk = (L + 63) / 64;
+  if (nblk > 16384) return fail(HYS_ERR_UNSUPPORTED, "more than 16384 key blocks");
+  a.nb = env_int("HYS_NB_SPARSE", 1) == 2 ? 2 : 1;
+  const int rows = 128 * a.nb;
+  if (G > rows) return fail(HYS_ERR_UNSUPPORTED, "more than %d query heads per KV head", rows);
+  a.HC = (int)G;
+  int bq = (int)(rows / G);
+  if (bq > 64) bq = 64;
+  if (sp->k > 0 && bq > 4 * rows / sp->k) bq = 4 * rows / sp->k;
+  const int bq_env = env_int("HYS_SPARSE_BQ", 0);       // tuning override
+  if (bq_env > 0 && bq_env < bq) bq = bq_env;
+  if (bq < 1) bq = 1;
+  a.BQ = bq; a.nhc = 1; a.nblk = (int)nblk;
+  a.ntq = (int)((L + a.BQ - 1) / a.BQ);
+  grid = (int)(B * a.ntq * Hkv);
+  return HYS_OK;
+}
+
 // ---------------------------------------------------------------------------
 hys_status hys_sparse_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v,
                                const hys_sparse_params* sp, const int32_t* idx, hys_tensor4 o, float* lse, void* ws,
@@ -293,30 +320,9 @@ hys_status hys_sparse_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tens
     a.idx = idx; a.idx_sb = sp->idx_batch_stride; a.idx_sr = sp->idx_row_stride; a.topk = sp->k;
     int mode, grid;
     if (sp->granularity == 64) {
-      if (sp->q_tile != 1) return fail(HYS_ERR_UNSUPPORTED, "granularity 64 needs q_tile 1");
-      if (sp->forced_window != 0) return fail(HYS_ERR_UNSUPPORTED, "granularity 64 has no forced window");
-      if (sp->k > 64) return fail(HYS_ERR_UNSUPPORTED, "granularity 64 needs k <= 64");
-      if (G > 256) return fail(HYS_ERR_UNSUPPORTED, "more than 256 query heads per KV head");
-      const int64_t nblk = (L + 63) / 64;
-      if (nblk > 16384) return fail(HYS_ERR_UNSUPPORTED, "more than 16384 key blocks");
+      hys_status bs = setup_block_selection(a, sp, G, L, B, Hkv, grid);
+      if (bs != HYS_OK) return bs;
       mode = hys::M_SPARSE_BLOCK;
-      a.nb = env_int("HYS_NB_SPARSE", 1) == 2 ? 2 : 1;
-      const int rows = 128 * a.nb;
-      if (G > rows) return fail(HYS_ERR_UNSUPPORTED, "more than %d query heads per KV head", rows);
-      a.HC = (int)G;
-      int bq = (int)(rows / G);
-      if (bq > 64) bq = 64;
-      if (sp->k > 0 && bq > 4 * rows / sp->k) bq = 4 * rows / sp->k;
-      const int bq_env = env_int("HYS_SPARSE_BQ", 0);       // tuning override
-      if (bq_env > 0 && bq_env < bq) bq = bq_env;
-      if (bq < 1) bq = 1;
-      a.BQ = bq; a.nhc = 1; a.nblk = (int)nblk;
-      a.ntq = (int)((L + a.BQ - 1) / a.BQ);
-      grid = (int)(B * a.ntq * Hkv);
-      if (sp->k == 0) {
-        // empty selection: every row's set is empty
-        a.topk = 0;
-      }
     } else if (sp->granularity == 1) {
       if (sp->q_tile != 64) return fail(HYS_ERR_UNSUPPORTED, "granularity 1 needs q_tile 64");
       if (sp->k > 2048) return fail(HYS_ERR_UNSUPPORTED, "granularity 1 needs k <= 2048");
@@ -375,6 +381,53 @@ hys_status hys_swa_gate_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4
     return hip_status(hys::launch_attn(hys::M_SWA_GATE, et(q.dtype), et(k_win.dtype), (int)D, a, grid,
                                        (hipStream_t)stream),
                       "window+gate launch");
+  } catch (...) {
+    return fail(HYS_ERR_INTERNAL, "internal error");
+  }
+}
+
+// ---------------------------------------------------------------------------
+hys_status hys_sparse_layer_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v,
+                                const hys_sparse_params* sp, const int32_t* idx, hys_tensor4 k_win,
+                                hys_tensor4 v_win, int32_t window, const float* gate_w, const float* gate_b,
+                                hys_tensor4 o, void* stream) {
+  try {
+    hys_status s;
+    if ((s = check_params(p)) != HYS_OK) return s;
+    if (p->k_scale != 1.f || p->v_scale != 1.f)
+      return fail(HYS_ERR_UNSUPPORTED, "k_scale and v_scale must be 1 (K/V of q's type)");
+    if ((s = check_qkv(q, k, v, true)) != HYS_OK) return s;
+    if (k.dtype != q.dtype) return fail(HYS_ERR_UNSUPPORTED, "k/v must have q's dtype");
+    if ((s = check_qkv(q, k_win, v_win, true)) != HYS_OK) return s;
+    if (k_win.dtype != q.dtype) return fail(HYS_ERR_UNSUPPORTED, "window K/V must have q's dtype");
+    for (int i = 0; i < 4; ++i) {
+      if (k_win.shape[i] != k.shape[i] || v_win.shape[i] != v.shape[i])
+        return fail(HYS_ERR_INVALID_ARG, "window K/V shapes differ from k/v");
+      if (k_win.stride[i] != k.stride[i] || v_win.stride[i] != v.stride[i])
+        return fail(HYS_ERR_UNSUPPORTED, "window K/V strides must equal those of k/v");
+    }
+    if ((s = check_out(o, q, "o")) != HYS_OK) return s;
+    if (!sp) return fail(HYS_ERR_INVALID_ARG, "null sparse params");
+    if (sp->granularity != 64) return fail(HYS_ERR_UNSUPPORTED, "granularity must be 64");
+    if (sp->k < 0) return fail(HYS_ERR_INVALID_ARG, "k must be >= 0");
+    if (sp->k > 0 && !idx) return fail(HYS_ERR_INVALID_ARG, "null idx");
+    if (sp->idx_row_stride < sp->k || sp->idx_batch_stride < 0)
+      return fail(HYS_ERR_INVALID_ARG, "idx strides too small");
+    if (!gate_w) return fail(HYS_ERR_INVALID_ARG, "null gate_w");
+    if (window < 1) return fail(HYS_ERR_INVALID_ARG, "window must be >= 1");
+    const int64_t B = q.shape[0], L = q.shape[1], Hq = q.shape[2], Hkv = k.shape[2], D = q.shape[3];
+    const int64_t G = Hq / Hkv;
+    hys::AttnArgs a = base_args(p, q, k, v, o, nullptr);
+    a.idx = idx; a.idx_sb = sp->idx_batch_stride; a.idx_sr = sp->idx_row_stride; a.topk = sp->k;
+    a.kw = k_win.ptr; a.vw = v_win.ptr; a.window = window;
+    a.gate_w = gate_w; a.gate_b = gate_b;
+    int grid = 0;
+    if ((s = setup_block_selection(a, sp, G, L, B, Hkv, grid)) != HYS_OK) return s;
+    if (L == 0) return ok();
+    a.grid_used = grid;
+    return hip_status(hys::launch_attn(hys::M_SPARSE_SWA, et(q.dtype), et(k.dtype), (int)D, a, grid,
+                                       (hipStream_t)stream),
+                      "sparse layer launch");
   } catch (...) {
     return fail(HYS_ERR_INTERNAL, "internal error");
   }

@@ -36,6 +36,7 @@ hipError_t launch_attn(int mode, int qt, int kt, int D, const AttnArgs& a, int g
     case M_SPARSE_BLOCK: return launch_mode<M_SPARSE_BLOCK>(qt, kt, D, a, grid, s);
     case M_SPARSE_TOKEN: return launch_mode<M_SPARSE_TOKEN>(qt, kt, D, a, grid, s);
     case M_SWA_GATE: return launch_mode<M_SWA_GATE>(qt, kt, D, a, grid, s);
+    case M_SPARSE_SWA: return launch_mode<M_SPARSE_SWA>(qt, kt, D, a, grid, s);
   }
   return hipErrorInvalidValue;
 }

@@ -55,6 +55,8 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
   constexpr int NBWMAX = 512;                      // max bitmap words (block mode)
   constexpr int TLMAX = 2048;                      // max token-list length (token mode)
   static_assert(KUN % 256 == 0, "D must be 64 or 128");
+  // modes whose tiles include selected key blocks
+  constexpr bool BLOCKSEL = MODE == M_SPARSE_BLOCK || MODE == M_SPARSE_SWA;
 
   // two stages: tile n is consumed from one while tile n+1 is written to the other
   __shared__ __attribute__((aligned(16))) CT Klds[2 * 64 * KROW];
@@ -64,10 +66,10 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
   __shared__ float red[2 * RS];
   __shared__ int s_misc[4];
   // block-sparse lists
-  __shared__ uint32_t s_bitmap[(MODE == M_SPARSE_BLOCK) ? NBWMAX : 1];
-  __shared__ int s_wpre[(MODE == M_SPARSE_BLOCK) ? NBWMAX : 1];
-  __shared__ int s_ulist[(MODE == M_SPARSE_BLOCK) ? UMAX : 1];
-  __shared__ unsigned long long s_member[(MODE == M_SPARSE_BLOCK) ? UMAX : 1];
+  __shared__ uint32_t s_bitmap[BLOCKSEL ? NBWMAX : 1];
+  __shared__ int s_wpre[BLOCKSEL ? NBWMAX : 1];
+  __shared__ int s_ulist[BLOCKSEL ? UMAX : 1];
+  __shared__ unsigned long long s_member[BLOCKSEL ? UMAX : 1];
   // token-sparse lists
   __shared__ int s_tlist[(MODE == M_SPARSE_TOKEN) ? TLMAX : 1];
   __shared__ unsigned char s_selw[(MODE == M_SPARSE_TOKEN) ? 2048 : 1];
@@ -112,13 +114,14 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
   int kbase = 0;            // contiguous modes: first key
   int kend = 0;             // contiguous modes: last key (inclusive)
   int npre = 0, wstart = 0, wend = 0;
+  int nsp = 0;              // M_SPARSE_SWA: tiles [0, nsp) are selected blocks, the rest the window
   if (MODE == M_FULL || MODE == M_FULL_BLOCK || MODE == M_FULL_TILE) {
     kbase = 0; kend = min(q_last, a.Lk - 1);
     ntiles = kend / 64 + 1;
   } else if (MODE == M_SWA_GATE) {
     kbase = max(0, q0 - a.window + 1); kend = min(q_last, a.Lk - 1);
     ntiles = (kend - kbase + 1 + 63) / 64;
-  } else if (MODE == M_SPARSE_BLOCK) {
+  } else if (BLOCKSEL) {
     const int nbw = (a.nblk + 31) >> 5;
     for (int w = tid; w < nbw; w += 256) s_bitmap[w] = 0u;
     for (int u = tid; u < UMAX; u += 256) s_member[u] = 0ull;
@@ -170,6 +173,13 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     }
     __syncthreads();
     ntiles = s_misc[0];
+    if (MODE == M_SPARSE_SWA) {
+      // then the window [q0 - window + 1, q_last] of the layer's own K/V
+      nsp = ntiles;
+      wstart = max(0, q0 - a.window + 1);
+      wend = min(q_last, a.Lk - 1);
+      ntiles = nsp + (wend - wstart + 1 + 63) / 64;
+    }
   } else if (MODE == M_SPARSE_TOKEN) {
     wstart = max(0, q0 - a.window + 1);
     wend = min(q_last, a.Lk - 1);
@@ -201,11 +211,17 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
   // ---- staging helpers -----------------------------------------------------
   const KT* kb = (const KT*)a.k + (int64_t)b * a.k_sb;
   const KT* vb = (const KT*)a.v + (int64_t)b * a.v_sb;
+  // the layer's own window K/V (same strides as k, v)
+  const KT* kwb = (MODE == M_SPARSE_SWA) ? (const KT*)a.kw + (int64_t)b * a.k_sb : kb;
+  const KT* vwb = (MODE == M_SPARSE_SWA) ? (const KT*)a.vw + (int64_t)b * a.v_sb : vb;
 
   // key position of tile slot t of tile n; -1 when the slot is empty.
   // For the token mode, bit 30 flags a selected (as opposed to window-only) token.
   auto keypos = [&](int n, int t) __attribute__((always_inline)) -> int {
-    if (MODE == M_SPARSE_BLOCK) {
+    if (MODE == M_SPARSE_SWA && n >= nsp) {
+      const int j = wstart + (n - nsp) * 64 + t;
+      return j <= wend ? j : -1;
+    } else if (BLOCKSEL) {
       const int j = s_ulist[n] * 64 + t;
       return j < a.Lk ? j : -1;
     } else if (MODE == M_SPARSE_TOKEN) {
@@ -230,7 +246,8 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
   // base pointer serves every load and no slot needs masking.
   auto full_tile = [&](int n, int& j0) __attribute__((always_inline)) -> bool {
     if (MODE == M_SPARSE_TOKEN) { j0 = 0; return false; }
-    if (MODE == M_SPARSE_BLOCK) { j0 = s_ulist[n] * 64; return j0 + 63 < a.Lk; }
+    if (MODE == M_SPARSE_SWA && n >= nsp) { j0 = wstart + (n - nsp) * 64; return j0 + 63 <= wend; }
+    if (BLOCKSEL) { j0 = s_ulist[n] * 64; return j0 + 63 < a.Lk; }
     j0 = kbase + n * 64;
     return j0 + 63 <= kend;
   };
@@ -245,11 +262,14 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
 
   auto stage_load = [&](int n, int g_) __attribute__((always_inline)) {
     const int kvh = g_;
+    const bool own = MODE == M_SPARSE_SWA && n >= nsp;
+    const KT* ksrc = own ? kwb : kb;
+    const KT* vsrc = own ? vwb : vb;
     int j0;
     staged_full = __builtin_amdgcn_readfirstlane((int)full_tile(n, j0)) != 0;
     if (staged_full) {
-      const KT* kt = kb + (int64_t)j0 * a.k_st + (int64_t)kvh * a.k_sh;
-      const KT* vt = vb + (int64_t)j0 * a.v_st + (int64_t)kvh * a.v_sh;
+      const KT* kt = ksrc + (int64_t)j0 * a.k_st + (int64_t)kvh * a.k_sh;
+      const KT* vt = vsrc + (int64_t)j0 * a.v_st + (int64_t)kvh * a.v_sh;
 #pragma unroll
       for (int u = 0; u < KU; ++u) kreg[u] = load8<KT>(kt + koff0 + u * kstep);
 #pragma unroll
@@ -269,7 +289,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
       const int kp = keypos(n, key);
       const int j = kp >= 0 ? (kp & ~(1 << 30)) : 0;
       kmask |= (kp >= 0 ? 1u : 0u) << u;
-      kreg[u] = load8<KT>(kb + (int64_t)j * a.k_st + (int64_t)kvh * a.k_sh + c8 * 8);
+      kreg[u] = load8<KT>(ksrc + (int64_t)j * a.k_st + (int64_t)kvh * a.k_sh + c8 * 8);
     }
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
@@ -281,7 +301,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
           const int kp = keypos(n, kg * 4 + r);
           const int j = kp >= 0 ? (kp & ~(1 << 30)) : 0;
           vmask |= (kp >= 0 ? 1u : 0u) << (4 * u + r);
-          vreg[u][r] = load8<KT>(vb + (int64_t)j * a.v_st + (int64_t)kvh * a.v_sh + dc * 8);
+          vreg[u][r] = load8<KT>(vsrc + (int64_t)j * a.v_st + (int64_t)kvh * a.v_sh + dc * 8);
         }
       }
     }
@@ -381,7 +401,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     }
     const bool wave_any = wave_qmax >= 0;
     unsigned long long wave_qmask = 0ull;
-    if (MODE == M_SPARSE_BLOCK) {
+    if (BLOCKSEL) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         unsigned long long m = valid[nb] ? (1ull << qiv[nb]) : 0ull;
@@ -424,6 +444,45 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     const float c2 = a.scale_log2;
     const float lazy_raw = kLazyLog2 / c2;    // the slack in raw dot-product units
 
+    // M_SPARSE_SWA: at the first window tile, the sparse branch is finished.
+    // Its normalised output goes to this row's output slot (read back by the
+    // same lane in the epilogue) and the softmax state restarts for the window.
+    bool sp_live[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) sp_live[nb] = false;
+    auto finish_sparse_branch = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float lsum = l_run[nb] + __shfl_xor(l_run[nb], 32);
+        sp_live[nb] = m_run[nb] != kNegInf;
+        const float inv = sp_live[nb] ? a.v_scale / lsum : 0.f;
+        if (valid[nb]) {
+          const int64_t row_off_o = (int64_t)b * a.o_sb + (int64_t)qpos[nb] * a.o_st + (int64_t)head[nb] * a.o_sh;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const int d = db * 32 + 8 * i4 + 4 * hh;
+              const f32x16& ac = acc[nb][db];
+              if (a.o_f32) {
+                float4 out = {ac[4 * i4] * inv, ac[4 * i4 + 1] * inv, ac[4 * i4 + 2] * inv, ac[4 * i4 + 3] * inv};
+                *(float4*)((float*)a.o + row_off_o + d) = out;
+              } else {
+                uint2 out;
+                out.x = pack_bf16x2(ac[4 * i4] * inv, ac[4 * i4 + 1] * inv);
+                out.y = pack_bf16x2(ac[4 * i4 + 2] * inv, ac[4 * i4 + 3] * inv);
+                *(uint2*)((uint16_t*)a.o + row_off_o + d) = out;
+              }
+            }
+        }
+        m_run[nb] = kNegInf; l_run[nb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[nb][db][i] = 0.f;
+      }
+    };
+
     // score emission for tile n (reads red[n & 1]); called by all threads after a barrier
     auto emit_scores = [&](int n) __attribute__((always_inline)) {
       if (MODE == M_FULL_BLOCK && !lane_scores) {
@@ -461,6 +520,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     }
     __syncthreads();
     for (int n = 0; n < ntiles; ++n) {
+      if (MODE == M_SPARSE_SWA && n == nsp) finish_sparse_branch();
       const int cur = n & 1;
       const CT* Kc = Klds + cur * (64 * KROW);
       const CT* Vc = VTlds + cur * (D * VROW);
@@ -469,8 +529,9 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
 
       // wave-level skip: nothing of this tile is visible to any row of the wave
       bool active = wave_any;
-      if (MODE == M_SPARSE_BLOCK) active = active && ((s_member[n] & wave_qmask) != 0ull);
-      const unsigned long long memb = (MODE == M_SPARSE_BLOCK) ? s_member[n] : 0ull;
+      const bool sel_tile = BLOCKSEL && !(MODE == M_SPARSE_SWA && n >= nsp);
+      const unsigned long long memb = sel_tile ? s_member[n] : 0ull;
+      if (sel_tile) active = active && ((memb & wave_qmask) != 0ull);
 
       if (!active) {
         if (MODE == M_FULL_BLOCK && hh == 0) {
@@ -543,31 +604,57 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
           __builtin_amdgcn_sched_barrier(0);
         }
 
-        // masking
-        bool need_mask = true;
-        if (MODE == M_FULL || MODE == M_FULL_BLOCK || MODE == M_FULL_TILE)
-          need_mask = !(wave_full && (n * 64 + 63 <= wave_qmin) && (n * 64 + 63 <= kend));
-        if (need_mask) {
+        // Visibility.  Each lane's row sees the keys [lo, hi] of this tile
+        // (causal, window), or none (invalid row, block not selected by its
+        // query).  Rows that see nothing are excluded through the softmax
+        // reference below, not element by element; element masks are applied
+        // only when some row of the wave sees part of the tile.
+        bool row_on[NB];
+        unsigned vbase[NB], vspan[NB];
+        bool elem_mask = MODE == M_SPARSE_TOKEN;
+        {
           int jt0 = 0;
           if (MODE != M_SPARSE_TOKEN) full_tile(n, jt0);   // consecutive keys from jt0
+          bool part = false, off_row = false;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const bool win = MODE == M_SWA_GATE || (MODE == M_SPARSE_SWA && !sel_tile);
+            const int hi = qpos[nb];
+            const int lo = win ? qpos[nb] - a.window + 1 : 0;
+            bool on = valid[nb];
+            if (BLOCKSEL && sel_tile) on = on && ((memb >> qiv[nb]) & 1ull) != 0ull;
+            row_on[nb] = on;
+            vbase[nb] = (unsigned)(jt0 - lo);
+            vspan[nb] = (unsigned)(hi - lo);
+            part = part || (on && !(jt0 >= lo && jt0 + 63 <= hi));
+            off_row = off_row || !on;
+          }
+          // token scores take a max over every row of the tile, so there rows
+          // that see nothing must hold -inf as well
+          if (MODE != M_SPARSE_TOKEN)
+            elem_mask = __ballot(part || (MODE == M_FULL_TILE && off_row)) != 0ull;
+        }
+        if (elem_mask) {
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
               const int off = mb * 32 + 8 * i4 + 4 * hh;
-              int4 ki;
+              int4 ki = make_int4(0, 0, 0, 0);
               if (MODE == M_SPARSE_TOKEN) ki = *(const int4*)&kic[off];
-              else ki = make_int4(jt0 + off, jt0 + off + 1, jt0 + off + 2, jt0 + off + 3);
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                const int kinf = e == 0 ? ki.x : (e == 1 ? ki.y : (e == 2 ? ki.z : ki.w));
-                const int j = kinf & 0x3fffffff;
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                  bool ok = valid[nb] && j <= qpos[nb];
-                  if (MODE == M_SWA_GATE) ok = ok && (j > qpos[nb] - a.window);
-                  if (MODE == M_SPARSE_BLOCK) ok = ok && ((memb >> qiv[nb]) & 1ull);
-                  if (MODE == M_SPARSE_TOKEN) ok = ok && ((kinf >> 30) || (j > qpos[nb] - a.window));
+                  bool ok;
+                  if (MODE == M_SPARSE_TOKEN) {
+                    const int kinf = e == 0 ? ki.x : (e == 1 ? ki.y : (e == 2 ? ki.z : ki.w));
+                    const int j = kinf & 0x3fffffff;
+                    ok = row_on[nb] && j <= qpos[nb] && ((kinf >> 30) || (j > qpos[nb] - a.window));
+                  } else {
+                    // key jt0 + off + e lies in [lo, hi]
+                    ok = row_on[nb] && (vbase[nb] + (unsigned)(off + e)) <= vspan[nb];
+                  }
                   if (!ok) s[mb][nb][4 * i4 + e] = kNegInf;
                 }
               }
@@ -621,6 +708,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
 #pragma unroll
             for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[mb][nb][i]);
           mt = xor32_max(mt);
+          if (!row_on[nb]) mt = kNegInf;
           if (MODE == M_FULL_BLOCK) {
             if (lane_scores) {
               // heads of a query are HC adjacent lanes: reduce them in-wave and
@@ -647,7 +735,8 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
           alpha[nb] = need ? __builtin_amdgcn_exp2f((m_run[nb] - mref) * c2) : 1.f;
           moved = moved || need;
           m_run[nb] = mref;
-          const float mc = (mref == kNegInf) ? 0.f : mref * c2;
+          // rows that see nothing in this tile get probability 0 everywhere
+          const float mc = !row_on[nb] ? __builtin_huge_valf() : ((mref == kNegInf) ? 0.f : mref * c2);
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -725,6 +814,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     }  // tile loop
 
     if (ntiles > 0) emit_scores(ntiles - 1);
+    if (MODE == M_SPARSE_SWA && nsp == ntiles) finish_sparse_branch();
 
     // -inf for blocks / keys after the diagonal
     if (MODE == M_FULL_BLOCK) {
@@ -751,9 +841,9 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
       if (!valid[nb]) continue;
       const int64_t row_off_o = (int64_t)b * a.o_sb + (int64_t)qpos[nb] * a.o_st + (int64_t)head[nb] * a.o_sh;
       float gate = 1.f;
-      bool sp_live = true;
+      bool sp_on = true;
       const float* osp = nullptr;
-      if (MODE == M_SWA_GATE) {
+      if (MODE == M_SWA_GATE || MODE == M_SPARSE_SWA) {
         // g = sigmoid(<q, w_h> + b_h): each lane holds half of the row's d values
         const float* w = a.gate_w + (int64_t)head[nb] * D;
         float z = 0.f;
@@ -775,9 +865,13 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
         z += __shfl_xor(z, 32);
         if (a.gate_b) z += a.gate_b[head[nb]];
         gate = 1.f / (1.f + __expf(-z));
-        const float lsp = a.lse_sp[((int64_t)b * a.Hq + head[nb]) * a.Lq + qpos[nb]];
-        sp_live = lsp != kNegInf;
-        osp = a.o_sp + (int64_t)b * a.osp_sb + (int64_t)qpos[nb] * a.osp_st + (int64_t)head[nb] * a.osp_sh;
+        if (MODE == M_SWA_GATE) {
+          const float lsp = a.lse_sp[((int64_t)b * a.Hq + head[nb]) * a.Lq + qpos[nb]];
+          sp_on = lsp != kNegInf;
+          osp = a.o_sp + (int64_t)b * a.osp_sb + (int64_t)qpos[nb] * a.osp_st + (int64_t)head[nb] * a.osp_sh;
+        } else {
+          sp_on = sp_live[nb];
+        }
       } else if (a.lse && hh == 0) {
         a.lse[((int64_t)b * a.Hq + head[nb]) * a.Lq + qpos[nb]] = lse_v;
       }
@@ -789,13 +883,22 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
           float r[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) r[e] = acc[nb][db][4 * i4 + e] * inv;
-          if (MODE == M_SWA_GATE) {
-            if (sp_live) {
+          if ((MODE == M_SWA_GATE || MODE == M_SPARSE_SWA) && sp_on) {
+            float spv[4];
+            if (MODE == M_SWA_GATE) {
               const float4 sp = *(const float4*)(osp + d);
-              const float spv[4] = {sp.x, sp.y, sp.z, sp.w};
-#pragma unroll
-              for (int e = 0; e < 4; ++e) r[e] = gate * spv[e] + (1.f - gate) * r[e];
+              spv[0] = sp.x; spv[1] = sp.y; spv[2] = sp.z; spv[3] = sp.w;
+            } else if (a.o_f32) {
+              // the sparse branch this lane stored at the branch switch
+              const float4 sp = *(const float4*)((const float*)a.o + row_off_o + d);
+              spv[0] = sp.x; spv[1] = sp.y; spv[2] = sp.z; spv[3] = sp.w;
+            } else {
+              const uint2 sp = *(const uint2*)((const uint16_t*)a.o + row_off_o + d);
+              spv[0] = bf16_to_f32((uint16_t)(sp.x & 0xffffu)); spv[1] = bf16_to_f32((uint16_t)(sp.x >> 16));
+              spv[2] = bf16_to_f32((uint16_t)(sp.y & 0xffffu)); spv[3] = bf16_to_f32((uint16_t)(sp.y >> 16));
             }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = gate * spv[e] + (1.f - gate) * r[e];
           }
           if (a.o_f32) {
             float4 out = {r[0], r[1], r[2], r[3]};

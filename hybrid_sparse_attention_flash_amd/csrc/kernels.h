@@ -15,6 +15,7 @@ enum AttnMode {
   M_SPARSE_BLOCK = 3,  // attention over selected key blocks (per-query selection)
   M_SPARSE_TOKEN = 4,  // attention over selected tokens of a query tile + forced recent window
   M_SWA_GATE = 5,      // sliding-window attention fused with the sigmoid gate merge
+  M_SPARSE_SWA = 6,    // selected key blocks, then the layer's own window, merged by the gate
 };
 
 struct AttnArgs {
@@ -39,7 +40,9 @@ struct AttnArgs {
   const int32_t* idx; int64_t idx_sb, idx_sr;
   int topk;
   int window;
-  // gate inputs (M_SWA_GATE)
+  // the layer's own window K/V (M_SPARSE_SWA; same strides as k, v)
+  const void* kw; const void* vw;
+  // gate inputs (M_SWA_GATE, M_SPARSE_SWA)
   const float* o_sp; int64_t osp_sb, osp_st, osp_sh;
   const float* lse_sp;       // [B, Hq, Lq]
   const float* gate_w;       // [Hq, D]

@@ -96,6 +96,19 @@ def hys_swa_gate_fwd(q, k_win, v_win, window: int, o_sparse, lse_sparse, gate_w,
                                _stream(q.device)))
 
 
+def hys_sparse_layer_fwd(q, k, v, idx, k_win, v_win, window: int, gate_w, o, gate_b=None, topk: int = None,
+                         softmax_scale: float = None):
+    """One HySparse sparse layer (selected blocks of k/v, own window k_win/v_win, sigmoid gate) in one call.
+    idx: [B, L, topk] int32 block ids."""
+    lib = _lib.load()
+    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), 1.0, 1.0)
+    kk = idx.shape[-1] if topk is None else topk
+    sp = HysSparseParams(64, kk, 1, 0, idx.stride(0), idx.stride(1))
+    check(lib.hys_sparse_layer_fwd(ctypes.byref(p), tensor4(q), tensor4(k), tensor4(v), ctypes.byref(sp), _ptr(idx),
+                                   tensor4(k_win), tensor4(v_win), window, _ptr(gate_w), _ptr(gate_b), tensor4(o),
+                                   _stream(q.device)))
+
+
 def hys_decode_step(q_full, k_cache, v_cache, cache_len: Sequence[int], o_full, token_scores, idx,
                     q_sparse: Sequence[torch.Tensor], o_sparse: Sequence[torch.Tensor], topk: int, window: int,
                     softmax_scale: float = None, k_scale: float = 1.0, v_scale: float = 1.0,

@@ -18,6 +18,11 @@
  *                         sigmoid gate that merges it with the sparse branch
  *   hys_decode_step     - one HySparse2 decode step against a long fp8 cache
  *
+ * and one fused form of two of them:
+ *
+ *   hys_sparse_layer_fwd - a whole HySparse sparse layer (sparse branch,
+ *                          window branch and gate) in one pass
+ *
  * Conventions shared by every call
  * --------------------------------
  * Memory:   every tensor pointer is device memory owned by the caller (for
@@ -208,6 +213,33 @@ HYS_API hys_status hys_sparse_attn_fwd(const hys_attn_params* p, hys_tensor4 q, 
 HYS_API hys_status hys_swa_gate_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k_win, hys_tensor4 v_win,
                             int32_t window, hys_tensor4 o_sparse, const float* lse_sparse, const float* gate_w,
                             const float* gate_b, hys_tensor4 o, void* stream);
+
+/*
+ * hys_sparse_layer_fwd - one HySparse sparse layer in one pass.
+ *
+ * Computes what hys_sparse_attn_fwd (granularity 64, q_tile 1) followed by
+ * hys_swa_gate_fwd computes (QbitAI HySparse article, method section: the
+ * sparse layer's global branch over the selected blocks of the shared KV and
+ * its local window branch over its own KV, merged by a sigmoid gate;
+ * TechWalker write-up: window 128, independent window KV):
+ *   O_sparse = attention of q over J(i) = { j <= i : j/64 in idx[b,i,:] } of k, v
+ *   O_window = attention of q over [max(0, i-window+1), i] of k_win, v_win
+ *   o = g * O_sparse + (1-g) * O_window,  g = sigmoid(<q, gate_w[h]> (+ gate_b[h])),
+ *   o = O_window where J(i) is empty.
+ * The sparse branch is never materialised separately: its normalised output
+ * is held in o's storage type between the branches (so with a bf16 o it is
+ * rounded to bf16 before the gate; with fp32 o the result matches the
+ * two-call form up to fp32 rounding).
+ * q [B, L, Hq, D] bf16 or fp32; k, v, k_win, v_win [B, L, Hkv, D] of q's type,
+ * the window tensors with the same strides as k and v; idx and sp as for
+ * hys_sparse_attn_fwd with granularity 64 (k <= 64); gate_w [Hq, D] fp32;
+ * gate_b [Hq] fp32 or NULL; o [B, L, Hq, D] fp32 or bf16.  p->k_scale and
+ * p->v_scale must be 1.  No workspace.
+ */
+HYS_API hys_status hys_sparse_layer_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v,
+                                const hys_sparse_params* sp, const int32_t* idx, hys_tensor4 k_win,
+                                hys_tensor4 v_win, int32_t window, const float* gate_w, const float* gate_b,
+                                hys_tensor4 o, void* stream);
 
 /*
  * hys_decode_step - one HySparse2 decode step (airebao HySparse2 news:

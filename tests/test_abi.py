@@ -105,6 +105,27 @@ def test_sparse_validation():
     assert call(HysSparseParams(64, 4, 1, 0, 512, 4), idx=0) == INVALID
 
 
+def test_sparse_layer_validation():
+    p = HysAttnParams(0.125, 1.0, 1.0)
+    q, kv, o = t4([1, 128, 8, 128]), t4([1, 128, 2, 128]), t4([1, 128, 8, 128], dtype=0)
+    sp = HysSparseParams(64, 4, 1, 0, 512, 4)
+
+    def call(q=q, k=kv, v=kv, kw=kv, vw=kv, sp=sp, idx=FAKE, window=128, gate=FAKE, o=o, p=p):
+        return lib().hys_sparse_layer_fwd(ctypes.byref(p), q, k, v, ctypes.byref(sp), ctypes.c_void_p(idx), kw, vw,
+                                          window, ctypes.c_void_p(gate), None, o, None)
+    assert call(p=HysAttnParams(0.125, 2.0, 1.0)) == UNSUPPORTED                          # k_scale != 1
+    assert call(k=t4([1, 128, 2, 128], dtype=2), v=t4([1, 128, 2, 128], dtype=2)) == UNSUPPORTED   # fp8 k/v
+    assert call(kw=t4([1, 128, 2, 128], dtype=0), vw=t4([1, 128, 2, 128], dtype=0)) == UNSUPPORTED  # f32 window
+    assert call(kw=t4([1, 128, 4, 64]), vw=t4([1, 128, 4, 64])) == INVALID               # head dims differ
+    assert call(kw=t4([1, 128, 2, 128], strides=[2 * 128 * 128 + 128, 256, 128, 1])) == UNSUPPORTED  # strides
+    assert call(sp=HysSparseParams(1, 16, 64, 128, 32, 16)) == UNSUPPORTED               # granularity 1
+    assert call(sp=HysSparseParams(64, 65, 1, 0, 512 * 65, 65)) == UNSUPPORTED           # k > 64
+    assert call(idx=0) == INVALID
+    assert call(gate=0) == INVALID
+    assert call(window=0) == INVALID
+    assert call(o=t4([1, 128, 8, 64], dtype=0)) == INVALID                               # o shape
+
+
 def test_decode_validation():
     p = HysDecodeParams(0.088, 0.01, 0.01, 1024, 128)
     qf = t4([4, 1, 64, 128])

@@ -204,6 +204,42 @@ def test_swa_gate(name, L, Hq, Hkv, D, W):
     assert max_abs(o[0].cpu().numpy(), ref) <= TOL_OUT[w.q_dtype]
 
 
+@pytest.mark.parametrize("name,L,Hq,Hkv,D,k,W,out", [
+    ("tiny_fp32", 1024, 8, 1, 64, 4, 128, "f32"),
+    ("dense7b_16k", 333, 8, 2, 128, 3, 128, "f32"),
+    ("moe80b_32k", 512, 16, 2, 128, 6, 77, "f32"),
+    ("moe80b_32k", 300, 8, 1, 128, 16, 128, "bf16"),
+    ("dense7b_16k", 200, 4, 4, 64, 0, 1, "f32"),
+])
+def test_sparse_layer_fused(name, L, Hq, Hkv, D, k, W, out):
+    """The one-pass sparse layer against the oracle's sparse branch, window branch and gate."""
+    w = _wl(name, L=L, Hq=Hq, Hkv=Hkv, D=D, needles=0)
+    q = synth.gen_q(w, 1)
+    kk, _ = synth.gen_kv(w, "k")
+    vv, _ = synth.gen_kv(w, "v")
+    kw, _ = synth.gen_window_kv(w, 1, "kw")
+    vw, _ = synth.gen_window_kv(w, 1, "vw")
+    gw = synth.gen_gate_w(w, 1)
+    sel = _rand_block_sel(L, k, np.random.default_rng(L + 7))
+    if k > 0:
+        sel[::9] = -1                                  # rows with an empty selection
+    print(f"sparse-layer {name} L={L} Hq={Hq} Hkv={Hkv} D={D} k={k} W={W} out={out}", flush=True)
+    odt = torch.float32 if out == "f32" else torch.bfloat16
+    o = _nan_like((1, L, Hq, D), odt)
+    idx = torch.from_numpy(sel).reshape(1, L, k).cuda() if k > 0 else torch.zeros((1, L, 1), dtype=torch.int32,
+                                                                                  device="cuda")
+    ops.hys_sparse_layer_fwd(dev(q), dev(kk), dev(vv), idx, dev(kw), dev(vw), W, dev(gw), o, topk=k)
+    torch.cuda.synchronize()
+    qf = f64(q[0], w.q_dtype)
+    Osp, LSEsp = oracle.sparse_block_attention(qf, f64(kk[0], w.kv_dtype), f64(vv[0], w.kv_dtype), w.scale,
+                                               sel if k > 0 else np.zeros((L, 0), int), 64)
+    Ow, _ = oracle.window_attention(qf, f64(kw[0], w.q_dtype), f64(vw[0], w.q_dtype), w.scale, W)
+    ref = oracle.gate_merge(qf, gw.numpy().astype(np.float64), Osp, LSEsp, Ow)
+    got = o[0].float().cpu().numpy()
+    assert np.isfinite(got).all()
+    assert max_abs(got, ref) <= TOL_OUT[w.q_dtype if out == "f32" else "bf16"]
+
+
 @pytest.mark.parametrize("B,N,lens,Hq,D,topk,W,nsp,kv", [
     (2, 5000, (5000, 3001), 64, 128, 256, 128, 3, "fp8"),
     (3, 700, (1, 64, 700), 16, 128, 64, 32, 2, "fp8"),
