@@ -118,19 +118,12 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
 
   // loads are unconditional from a clamped in-bounds key (key 0); empty slots
   // are zeroed when staged (see keep_if)
-  // per-thread element offsets inside a tile (independent of the tile)
-  int koff[KU], voff[VU][4];
-#pragma unroll
-  for (int u = 0; u < KU; ++u) {
-    const int unit = tid + 128 * u;
-    koff[u] = (unit / (D / 8)) * (int)a.k_st + (unit % (D / 8)) * 8;
-  }
-#pragma unroll
-  for (int u = 0; u < VU; ++u) {
-    const int unit = tid + 128 * u;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) voff[u][r] = ((unit % 16) * 4 + r) * (int)a.v_st + (unit / 16) * 8;
-  }
+  // per-thread element offsets inside a tile (independent of the tile): unit
+  // tid + 128u is key tid/(D/8) + u*128/(D/8) (K) or key group tid%16 with d
+  // chunk tid/16 + 8u (V), so one base register and uniform strides suffice
+  const int koff0 = (tid / (D / 8)) * (int)a.k_st + (tid % (D / 8)) * 8;
+  const int kstep = (128 / (D / 8)) * (int)a.k_st;
+  const int voff0 = ((tid % 16) * 4) * (int)a.v_st + (tid / 16) * 8;
   bool staged_full = true;
 
   auto stage_load = [&](int t) {
@@ -140,11 +133,11 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
       const KT* kt = kb + (int64_t)t * 64 * a.k_st;
       const KT* vt = vb + (int64_t)t * 64 * a.v_st;
 #pragma unroll
-      for (int u = 0; u < KU; ++u) kreg[u] = load8<KT>(kt + koff[u]);
+      for (int u = 0; u < KU; ++u) kreg[u] = load8<KT>(kt + koff0 + u * kstep);
 #pragma unroll
       for (int u = 0; u < VU; ++u)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vreg[u][r] = load8<KT>(vt + voff[u][r]);
+        for (int r = 0; r < 4; ++r) vreg[u][r] = load8<KT>(vt + voff0 + r * (int)a.v_st + u * 64);
       return;
     }
     kmask = 0u; vmask = 0u;
