@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 import synth  # noqa: E402
 from hybrid_sparse_attention_flash_amd import ops  # noqa: E402
-from hybrid_sparse_attention_flash_amd.block import HySparse2Decode, HySparseBlock  # noqa: E402
+from hybrid_sparse_attention_flash_amd.block import HySparse2Block, HySparse2Decode, HySparseBlock  # noqa: E402
 
 METRIC = ("hybrid-block prefill tokens/s at 32k (TFLOP/s, GB/s % peak); decode us/token at 1M")
 
@@ -171,8 +171,85 @@ def calibrate_copy(dev, mib=512, reps=3):
     del src, dst
 
 
+def token_sparse_keys(idx, L, window):
+    """Visible keys of the HySparse2 sparse layer, summed over queries: the
+    selected tokens j <= i of the query's tile united with [i-window+1, i]."""
+    nt, k = idx.shape[1], idx.shape[2]
+    sel = torch.where(idx[0] >= 0, idx[0].to(torch.int64), torch.full_like(idx[0], 1 << 40, dtype=torch.int64))
+    sel = torch.sort(sel, dim=1).values                                  # [nt, k]
+    i = torch.arange(L, device=idx.device, dtype=torch.int64)
+    t = i // 64
+    rows = sel[t]                                                        # [L, k]
+    le_i = torch.searchsorted(rows, i.view(-1, 1), right=True).view(-1)
+    lo = torch.clamp(i - window + 1, min=0)
+    below_lo = torch.searchsorted(rows, lo.view(-1, 1), right=False).view(-1)
+    in_win = le_i - below_lo
+    return int((le_i - in_win + torch.clamp(i + 1, max=window)).sum().item())
+
+
+def bench_prefill2(args, dev, name):
+    """HySparse2 block (fp8 MQA KV): full layer + tile-token scores, top-k per
+    64-query tile, token-sparse layers with the forced window."""
+    w = synth.WORKLOADS[name]
+    log(f"[bench] generating {w.name} inputs (L={w.L}, {w.n_sparse + 1} layers)")
+    q = [synth.gen_q(w, l).to(dev) for l in range(w.n_sparse + 1)]
+    k, ks = synth.gen_kv(w, "k")
+    v, vs = synth.gen_kv(w, "v")
+    k, v = k.to(dev), v.to(dev)
+    blk = HySparse2Block(w.B, w.L, w.Hq, w.Hkv, w.D, w.n_sparse, w.topk, w.window, tile=w.block, device=dev,
+                         out_dtype=torch.bfloat16)
+
+    def run(timer=None):
+        def rec(nm, fn):
+            if timer is None:
+                fn()
+            else:
+                a, b = timer.span(nm)
+                a.record(); fn(); b.record()
+        rec("full_attn+scores", lambda: blk.full(q[0], k, v, ks, vs))
+        rec("select_topk", blk.select)
+        for l in range(w.n_sparse):
+            rec("sparse_layer", lambda: blk.sparse_layer(l, q[l + 1], k, v, ks, vs))
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    timer = Timer()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(args.steps):
+        run(timer)
+    g1.record()
+    torch.cuda.synchronize()
+    step_ms = g0.elapsed_time(g1) / args.steps
+    tot = timer.totals_ms()
+    per_step = {kk: vv / args.steps for kk, vv in tot.items()}
+    launches = {kk: c // args.steps for kk, c in timer.counts().items()}
+    fl_full = full_attention_flops(w)
+    fl_layer = 4.0 * w.D * w.Hq * token_sparse_keys(blk.idx, w.L, w.window)
+    stages = {kk: {"ms_per_step": round(per_step[kk], 4), "launches_per_step": launches[kk]} for kk in per_step}
+    for kk, fl in (("full_attn+scores", fl_full), ("sparse_layer", w.n_sparse * fl_layer)):
+        tf = fl / (per_step[kk] * 1e-3) / 1e12
+        stages[kk]["tflops"] = round(tf, 2)
+        stages[kk]["frac_mfma_bf16"] = round(tf / PEAK_BF16_TFLOPS, 4)
+    dom = max(["full_attn+scores", "sparse_layer"], key=lambda kk: per_step[kk])
+    avg = per_step[dom] / launches[dom]
+    work = fl_full if dom == "full_attn+scores" else fl_layer
+    ach = work / (avg * 1e-3) / 1e12
+    roof = {"kernel": "full_attn (causal + tile-token scores)" if dom == "full_attn+scores"
+            else "sparse_layer (selected tokens U forced window, fp8 KV)", "bound": "mfma",
+            "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(avg, 4),
+            "work_per_launch": f"{work:.4g} FLOP (4*D per visible (query, head, key) pair)", "traffic": None}
+    log(f"[bench] {w.name}: {step_ms:.3f} ms/step")
+    return {"w": w, "step_ms": step_ms, "stages": stages, "roofline": roof, "host": None}
+
+
 def bench_prefill(args, dev):
-    w = synth.WORKLOADS["moe80b_32k"]
+    name = args.workload
+    if synth.WORKLOADS[name].variant == "hysparse2":
+        return bench_prefill2(args, dev, name)
+    w = synth.WORKLOADS[name]
     log(f"[bench] generating {w.name} inputs (L={w.L}, {w.n_sparse + 1} layers)")
     t0 = time.time()
     q_h = [synth.gen_q(w, l) for l in range(w.n_sparse + 1)]
@@ -291,6 +368,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--workload", default="moe80b_32k",
+                    choices=["moe80b_32k", "dense7b_16k", "hysparse2_64k", "tiny_fp32"],
+                    help="prefill block to time (default: the 32k HySparse block the metric is quoted on)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain copy of known size (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -309,7 +389,7 @@ def main():
     w = pre["w"]
     dec = None if args.no_decode else bench_decode(args, dev)
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and pre["host"] is not None:
         log(f"[bench] timing the CPU oracle on {args.cpu_rows} sampled rows")
         cpu = cpu_baseline(w, pre["host"], args.cpu_rows)
         log(f"[bench] oracle: {cpu['value']:.2f} tokens/s on {cpu['cores']} threads")
@@ -317,11 +397,14 @@ def main():
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(pre["step_ms"], 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1), bf16; 32 needle keys x4)",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.q_dtype,
+        "data": f"synthetic (seeded N(0,1); {w.q_dtype} Q, {w.kv_dtype} K/V"
+                + (f"; {w.needles} needle keys x{w.needle_scale:g})" if w.needles else ")"),
         "config": {"workload": w.name, "batch": w.B, "seq_len": w.L, "q_heads": w.Hq, "kv_heads": w.Hkv,
-                   "head_dim": w.D, "layers": f"1 full + {w.n_sparse} sparse", "topk_blocks": w.topk,
-                   "block": w.block, "window": w.window},
+                   "head_dim": w.D, "layers": f"1 full + {w.n_sparse} sparse",
+                   "selection": (f"top-{w.topk} of {w.block}-token blocks per query" if w.variant == "hysparse"
+                                 else f"top-{w.topk} tokens per {w.block}-query tile"),
+                   "window": w.window},
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,
         "stages": pre["stages"],

@@ -214,7 +214,10 @@ hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
       a.nhc = (int)((G + a.HC - 1) / a.HC);
       a.ntq = (int)((L + 63) / 64);
       a.scores = scores; a.sc_sb = (int64_t)a.ntq * L; a.sc_sr = L; a.sc_sg = 0;
-      grid = (int)(B * a.ntq);
+      // one workgroup per (query tile, head chunk), tiles padded to the 8 XCDs
+      const int64_t wgs = ((B * a.ntq + 7) / 8) * 8 * Hkv * a.nhc;
+      if (wgs > 0x7fffffff) return fail(HYS_ERR_UNSUPPORTED, "too many query tiles x head chunks (%lld)", (long long)wgs);
+      grid = (int)wgs;
     } else {
       mode = mode_in == HYS_SCORE_BLOCK ? hys::M_FULL_BLOCK : hys::M_FULL;
       if (G > rows) return fail(HYS_ERR_UNSUPPORTED, "more than %d query heads per KV head", rows);
@@ -231,8 +234,17 @@ hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
       grid = (int)(B * a.ntq * Hkv);
     }
     a.grid_used = grid;
-    hipError_t e = hys::launch_attn(mode, et(q.dtype), et(k.dtype), (int)D, a, grid, st);
+    hipError_t e;
+    if (mode == hys::M_FULL_TILE) {
+      e = hys::launch_tile_scores(a.scores, (int)B, a.ntq, a.BQ, (int)L, (int)L, a.sc_sb, a.sc_sr, 0, st);
+      if (e != hipSuccess) return hip_status(e, "score clear launch");
+    }
+    e = hys::launch_attn(mode, et(q.dtype), et(k.dtype), (int)D, a, grid, st);
     if (e != hipSuccess) return hip_status(e, "full attention launch");
+    if (mode == hys::M_FULL_TILE) {
+      e = hys::launch_tile_scores(a.scores, (int)B, a.ntq, a.BQ, (int)L, (int)L, a.sc_sb, a.sc_sr, 1, st);
+      if (e != hipSuccess) return hip_status(e, "score decode launch");
+    }
     if (mode == hys::M_FULL_BLOCK && Hkv > 1) {
       e = hys::launch_reduce_max((const float*)ws, (int)Hkv, B * L * nblk, scores, B * L * nblk, st);
       if (e != hipSuccess) return hip_status(e, "score reduction launch");

@@ -28,6 +28,39 @@ hipError_t launch_reduce_max(const float* part, int nparts, int64_t part_stride,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// tile-token score rows: before the attention launch, the keys each query
+// tile's workgroups will max into are set to 0 (below the key of any float)
+// and the keys past the tile's last key block to -inf; afterwards the keys are
+// decoded back to fp32 in place
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void tile_scores_kernel(float* sc, int ntq, int BQ, int Lq, int Lk, int64_t sb,
+                                                          int64_t sr, int decode) {
+  const int row = blockIdx.x;
+  const int b = row / ntq, qt = row - b * ntq;
+  const int last = min(min(qt * BQ + BQ, Lq) - 1, Lk - 1);
+  const int touched = min((last / 64 + 1) * 64, Lk);
+  float* p = sc + (int64_t)b * sb + (int64_t)qt * sr;
+  uint32_t* u = (uint32_t*)p;
+  if (!decode) {
+    for (int j = threadIdx.x; j < Lk; j += 256) u[j] = j < touched ? 0u : 0xff800000u;
+  } else {
+    for (int j = threadIdx.x; j < touched; j += 256) {
+      const uint32_t k = u[j];
+      const uint32_t f = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+      u[j] = k == 0u ? 0xff800000u : f;
+    }
+  }
+}
+
+hipError_t launch_tile_scores(float* sc, int B, int ntq, int BQ, int Lq, int Lk, int64_t sb, int64_t sr,
+                              int decode, hipStream_t s) {
+  const int64_t rows = (int64_t)B * ntq;
+  if (rows <= 0 || Lk <= 0) return hipSuccess;
+  hipLaunchKernelGGL(tile_scores_kernel, dim3((unsigned)rows), dim3(256), 0, s, sc, ntq, BQ, Lq, Lk, sb, sr, decode);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn(int mode, int qt, int kt, int D, const AttnArgs& a, int grid, hipStream_t s) {
   switch (mode) {
     case M_FULL: return launch_mode<M_FULL>(qt, kt, D, a, grid, s);

@@ -19,10 +19,12 @@
 // paragraph on the modified FlashAttention kernel): the per-row tile maximum
 // that the online softmax needs anyway is the block maximum when tiles are the
 // 64-key blocks; the max over the query heads of a KV group is taken in LDS.
-// For HySparse2 token scores the per-key maximum over a tile's rows is reduced
-// across lanes and waves and accumulated over head chunks by the one thread
-// that owns each key column, so no atomics are used and results are
-// deterministic.
+// For HySparse2 token scores the per-key maximum over a workgroup's rows is
+// reduced across lanes (in registers) and waves (in LDS); the head chunks of a
+// query tile run as separate workgroups and combine their maxima with an
+// atomic max on order-preserving integer keys, which is exact and order
+// independent, so results are deterministic.  The key array is cleared
+// before and decoded to fp32 after the attention launch.
 #pragma once
 #include "common.h"
 #include "kernels.h"
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
   __shared__ __attribute__((aligned(16))) CT VTlds[2 * D * VROW];
   __shared__ __attribute__((aligned(16))) int kinfo[2 * 64];
   constexpr int RS = ROWS > 256 ? ROWS : 256;      // stride of the two score-reduction halves
-  __shared__ float red[2 * RS];
+  __shared__ __attribute__((aligned(16))) float red[2 * RS];
   __shared__ int s_misc[4];
   // block-sparse lists
   __shared__ uint32_t s_bitmap[BLOCKSEL ? NBWMAX : 1];
@@ -82,13 +84,10 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
 
   // ---- work decomposition ------------------------------------------------
   int b, qt, g = 0, ch_begin = 0, ch_end = 1;
-  if (MODE == M_FULL_TILE) {
-    b = bid % a.B;
-    qt = a.ntq - 1 - bid / a.B;                    // longest rows first
-    ch_end = a.Hkv * a.nhc;
-  } else if (MODE == M_SPARSE_TOKEN) {
+  if (MODE == M_FULL_TILE || MODE == M_SPARSE_TOKEN) {
     // the head chunks of one query tile run back to back on one XCD
-    // (workgroups are dealt to the 8 XCDs round robin), sharing its gathered KV in L2
+    // (workgroups are dealt to the 8 XCDs round robin), so they stream the
+    // same K/V tiles through its L2 at about the same time
     const int nch = a.Hkv * a.nhc;
     const int xcd = bid & 7, slot = bid >> 3;
     const int ch = slot % nch;
@@ -96,6 +95,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     b = tile_rank % a.B;
     qt = tile_rank / a.B;
     if (qt >= a.ntq) return;
+    if (MODE == M_FULL_TILE) qt = a.ntq - 1 - qt;  // causal: longest rows first
     ch_begin = ch; ch_end = ch + 1;
   } else {
     g = bid % a.Hkv;                               // KV group fastest: XCD x sees groups x mod Hkv
@@ -502,9 +502,10 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
           float mx = fmaxf(fmaxf(rb[tid], rb[64 + tid]), fmaxf(rb[128 + tid], rb[192 + tid]));
           const int j = n * 64 + tid;
           if (j < a.Lk) {
-            float* dst = a.scores + (int64_t)b * a.sc_sb + (int64_t)qt * a.sc_sr + j;
-            const float v = mx * a.logit_scale;
-            *dst = (ch == 0) ? v : fmaxf(*dst, v);
+            // head chunks of the tile combine through an atomic max of
+            // order-preserving keys: exact, and independent of their order
+            uint32_t* dst = (uint32_t*)(a.scores + (int64_t)b * a.sc_sb + (int64_t)qt * a.sc_sr) + j;
+            atomicMax(dst, f32_order_key(mx * a.logit_scale));
           }
         }
       }
@@ -611,7 +612,10 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
         // only when some row of the wave sees part of the tile.
         bool row_on[NB];
         unsigned vbase[NB], vspan[NB];
-        bool elem_mask = MODE == M_SPARSE_TOKEN;
+        // token mode: list slots before npre hold selected tokens that precede
+        // the window start, hence every query of the tile; a tile made only of
+        // them needs no element mask
+        bool elem_mask = MODE == M_SPARSE_TOKEN && !(n * 64 + 63 < npre);
         {
           int jt0 = 0;
           if (MODE != M_SPARSE_TOKEN) full_tile(n, jt0);   // consecutive keys from jt0
@@ -662,7 +666,10 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
           }
         }
 
-        // token scores: per-key max over this workgroup's rows
+        // token scores: per-key max over this workgroup's rows.  Register
+        // x = 16 mb + i of lane (ln, hh) holds key mb*32 + 8(i/4) + 4hh + i%4
+        // of row ln; colmax32 leaves the maxima of keys off .. off+3 in every
+        // lane of a quad and the quad's first lane stores them.
         if (MODE == M_FULL_TILE) {
           float cm[32];
 #pragma unroll
@@ -671,25 +678,12 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
             for (int i = 0; i < 16; ++i) {
               float v = s[mb][0][i];
 #pragma unroll
-              for (int nb = 1; nb < NB; ++nb) v = fmaxf(v, s[mb][nb][i]);
+              for (int nb = 1; nb < NB; ++nb) v = fmax_nc(v, s[mb][nb][i]);
               cm[mb * 16 + i] = v;
             }
-          // reduce-scatter over the 32 lanes of each half: after 5 halvings lane
-          // ln holds the max of value index ln
-#pragma unroll
-          for (int st = 0; st < 5; ++st) {
-            const int half = 16 >> st;
-            const bool upper = (ln & half) != 0;
-#pragma unroll
-            for (int x = 0; x < half; ++x) {
-              const float send = upper ? cm[x] : cm[x + half];
-              const float keep = upper ? cm[x + half] : cm[x];
-              cm[x] = fmaxf(keep, __shfl_xor(send, half));
-            }
-          }
-          const int mb = ln >> 4, i = ln & 15;
-          const int off = mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          red[(n & 1) * RS + wave * 64 + off] = cm[0];
+          const f32x4 m4 = colmax32(cm);
+          const int off = (ln >> 4) * 32 + 8 * ((ln >> 2) & 3) + 4 * hh;
+          if ((ln & 3) == 0) *(f32x4*)&red[(n & 1) * RS + wave * 64 + off] = m4;
         }
 
         // online softmax (base 2 on raw dot products) with a lazily updated
@@ -825,10 +819,6 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
           const int t = e / ncol, c = c0 + (e - t * ncol);
           if (q0 + t < a.Lq) sc[(int64_t)(q0 + t) * a.sc_sr + c] = kNegInf;
         }
-    }
-    if (MODE == M_FULL_TILE && ch == 0) {
-      float* sc = a.scores + (int64_t)b * a.sc_sb + (int64_t)qt * a.sc_sr;
-      for (int j = ntiles * 64 + tid; j < a.Lk; j += 256) sc[j] = kNegInf;
     }
 
     // ---- epilogue ------------------------------------------------------------

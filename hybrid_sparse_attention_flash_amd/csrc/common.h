@@ -74,13 +74,89 @@ __device__ __forceinline__ f32x4 fp8x4_to_f32x4(uint32_t w) {
   return r;
 }
 
-// max(v[l], v[l ^ 32]) for every lane l.
-__device__ __forceinline__ float xor32_max(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+// IEEE maximum of two floats in one instruction.  Values that crossed lanes
+// come back as integers, and fmaxf on them would first quiet them (an extra
+// v_max per operand); the logits handled here are never NaN.
+__device__ __forceinline__ float fmax_nc(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// max(v[l], v[l ^ 32]) for every lane l: v_permlane32_swap of v with itself
+// leaves the two 32-lane halves exchanged between its two results.
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmax_nc(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// max(v[l], v[l ^ 16]) for every lane l (v_permlane16_swap exchanges odd and
+// even 16-lane rows).
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmax_nc(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Column maxima of a 32 x 32 block held one column value per register:
+// lane l (l = 32h + r) holds v[x] = M_h[r][x] for a 32 x 32 matrix M_h per
+// half h, and the result is max over r of M_h[r][x] for the four columns
+// x = (r & 28) + c, c = 0..3, returned in element c (all four lanes of a quad
+// receive the same four maxima).  A reduce-scatter: the row bit 4 step pairs
+// registers x and x + 16 through v_permlane16_swap; the bit 3 and bit 2 steps
+// use DPP row_mirror / row_half_mirror with bank masks, so each lane half of a
+// bank pair updates only the register range it keeps; bits 1 and 0 are then
+// all-reduced with quad permutes.  32 VALU operations and no LDS traffic.
+__device__ __forceinline__ f32x4 colmax32(const float (&v)[32]) {
+  float w[16];
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[x]), __float_as_uint(v[x + 16]), false, false);
+    w[x] = fmax_nc(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  // One block so the ordering below holds: every DPP read is at least two
+  // instructions after the write of its source (the s_nop covers the VALU
+  // writes before the block).  A disabled bank keeps its destination value.
+  asm("s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %0, %8, %8 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %1, %1, %1 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %1, %9, %9 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %2, %2, %2 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %2, %10, %10 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %3, %3, %3 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %3, %11, %11 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %4, %4, %4 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %4, %12, %12 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %5, %5, %5 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %5, %13, %13 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %6, %6, %6 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %6, %14, %14 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      "v_max_f32_dpp %7, %7, %7 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+      "v_max_f32_dpp %7, %15, %15 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+      // bit 2: banks 0, 2 keep registers 0..3, banks 1, 3 take 4..7
+      "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_max_f32_dpp %0, %4, %4 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_max_f32_dpp %1, %1, %1 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_max_f32_dpp %1, %5, %5 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_max_f32_dpp %2, %2, %2 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_max_f32_dpp %2, %6, %6 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_max_f32_dpp %3, %3, %3 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_max_f32_dpp %3, %7, %7 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      // bits 1 and 0: all-reduce inside each quad
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %2, %2, %2 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %3, %3, %3 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %2, %2, %2 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %3, %3, %3 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+      : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]), "+v"(w[6]), "+v"(w[7])
+      : "v"(w[8]), "v"(w[9]), "v"(w[10]), "v"(w[11]), "v"(w[12]), "v"(w[13]), "v"(w[14]), "v"(w[15]));
+  const f32x4 o = {w[0], w[1], w[2], w[3]};
+  return o;
+}
 
 // max over aligned groups of W consecutive lanes (W in {2,4,8,16,32}), every
 // lane of a group receiving the group max.  Lane pairs are exchanged with DPP
 // (quad_perm, row_half_mirror, row_mirror) inside a 16-lane row; the 32-wide
-// step crosses rows with a shuffle.
+// step crosses rows with v_permlane16_swap.
 template <int W> __device__ __forceinline__ float group_max(float v) {
   if (W >= 2)
     v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
@@ -90,8 +166,28 @@ template <int W> __device__ __forceinline__ float group_max(float v) {
     v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
   if (W >= 16)
     v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
-  if (W >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  if (W >= 32) v = xor16_max(v);
   return v;
+}
+
+// Inclusive prefix sum of an int over the 64 lanes of a wave, by DPP:
+// row_shr 1, 2, 3 (from the original values), 4 and 8 within each 16-lane
+// row, then row_bcast 15 / 31 across rows.  Invalid DPP sources read 0.
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+  int x = v + __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);       // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);              // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, v, 0x113, 0xF, 0xF, true);              // row_shr:3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xE, true);              // row_shr:4, banks 1-3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xC, true);              // row_shr:8, banks 2-3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, true);              // row_bcast:15, rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, true);              // row_bcast:31, rows 2, 3
+  return x;
+}
+
+// Sum of an int over the 64 lanes of a wave (wave-uniform): the last lane of
+// the inclusive scan.
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_scan_i32(v), 63);
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -53,6 +53,11 @@ struct AttnArgs {
 
 hipError_t launch_attn(int mode, int qt, int kt, int D, const AttnArgs& a, int grid, hipStream_t s);
 
+// M_FULL_TILE score rows [B, ntq, Lk] (row stride sr, batch stride sb):
+// decode = 0 clears them to atomic-max keys, decode = 1 turns keys into fp32
+hipError_t launch_tile_scores(float* sc, int B, int ntq, int BQ, int Lq, int Lk, int64_t sb, int64_t sr,
+                              int decode, hipStream_t s);
+
 hipError_t launch_reduce_max(const float* part, int nparts, int64_t part_stride, float* out, int64_t n,
                              hipStream_t s);
 

@@ -52,13 +52,12 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
   uint32_t key[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) key[v] = (v < seg && c0 + v < cols) ? score_key(x[v]) : 0u;
+  // keys >= t in the row: per-lane counts, wave total by DPP
   auto count_ge = [&](uint32_t t) {
     int n = 0;
 #pragma unroll
     for (int v = 0; v < V; ++v) n += (key[v] >= t) ? 1 : 0;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o);
-    return n;
+    return wave_sum_i32(n);
   };
   const int nvalid = count_ge(1u);
   uint32_t T = 1u;
@@ -207,24 +206,66 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
 #pragma unroll
   for (int v = 0; v < VPT; ++v)
     key[v] = (v < seg && p0 + v <= plast) ? score_key(__builtin_bit_cast(float, key[v])) : 0u;
+  // keys >= t in the chunk: per-lane counts, wave totals by DPP, the 16 wave
+  // totals through LDS
+  __shared__ int shc[16];
   auto count_ge = [&](uint32_t t) {
     int n = 0;
 #pragma unroll
     for (int v = 0; v < VPT; ++v) n += (key[v] >= t) ? 1 : 0;
-    return block_sum_1024(n, sh);
+    n = wave_sum_i32(n);
+    if ((tid & 63) == 0) shc[tid >> 6] = n;
+    __syncthreads();
+    int tot = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tot += shc[i];
+    __syncthreads();
+    return tot;
   };
   const int nvalid = count_ge(1u);
   const bool all = !(nvalid > k && k > 0);
+  // ---- the k-th largest key T by radix selection: four rounds over the 8-bit
+  // digits from the top; each round histograms the digit of the keys that
+  // share the digits chosen so far and picks, scanning digits downward, the
+  // one whose bin holds the remaining rank.  need = how many keys equal to T
+  // are taken (the rest of k after all keys > T).
+  __shared__ int hist[256];
+  __shared__ int s_pick[2];
   uint32_t T = 1u;
   int need = 0;
   if (!all) {
-    uint32_t t = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = t | (1u << bit);
-      if (count_ge(cand) >= k) t = cand;
+    uint32_t prefix = 0u, pmask = 0u;
+    int krem = k;
+    for (int round = 0; round < 4; ++round) {
+      const int shift = 24 - 8 * round;
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int v = 0; v < VPT; ++v)
+        if (key[v] != 0u && (key[v] & pmask) == prefix) atomicAdd(&hist[(key[v] >> shift) & 255u], 1);
+      __syncthreads();
+      // thread t < 256 takes digit 255 - t; an inclusive scan over t counts
+      // the keys with that digit or a larger one
+      int c = 0, incl = 0;
+      if (tid < 256) {
+        c = hist[255 - tid];
+        incl = wave_incl_scan_i32(c);
+        if ((tid & 63) == 63) shc[tid >> 6] = incl;
+      }
+      __syncthreads();
+      if (tid < 256) {
+        const int w = tid >> 6;
+        for (int i = 0; i < w; ++i) incl += shc[i];
+        if (incl - c < krem && krem <= incl) { s_pick[0] = 255 - tid; s_pick[1] = incl - c; }
+      }
+      __syncthreads();
+      prefix |= (uint32_t)s_pick[0] << shift;
+      pmask |= 0xFFu << shift;
+      krem -= s_pick[1];
+      __syncthreads();                          // s_pick, shc and hist are rewritten next round
     }
-    T = t;
-    need = k - count_ge(T + 1u);
+    T = prefix;
+    need = krem;
   }
   int nt = 0;
   if (!all) {

@@ -103,6 +103,8 @@ def test_select_topk_exact(rows, cols, k):
     if rows > 2:
         x[1, :] = -np.inf                       # a row with no candidate
         x[2, : cols // 2] = -np.inf             # causal-like row
+    if rows > 3:
+        x[3, :] = 0.5                           # one value everywhere: every candidate ties
     print(f"topk rows={rows} cols={cols} k={k}", flush=True)
     s = torch.from_numpy(x).cuda()
     idx = torch.full((rows, max(k, 1)), -7, dtype=torch.int32, device="cuda")[:, :k].contiguous()
