@@ -7,9 +7,11 @@
 // method section; TechWalker HySparse write-up, kernel paragraph.)
 //
 // Method: each score becomes an order-preserving 32-bit key (0 for -inf/NaN).
-// The threshold T = the k-th largest key is found by bisection over the 32 key
-// bits, each step counting keys >= candidate across the row (no atomics, no
-// sorting).  Keys above T are taken; of the keys equal to T the ones with the
+// The threshold T = the k-th largest key is found without sorting: the
+// one-wave kernel bisects over the 32 key bits, each step counting keys >=
+// candidate across the row; the workgroup kernel selects T radix-wise, one
+// 8-bit digit per round from the top, from an LDS histogram of the keys that
+// match the digits chosen so far.  Keys above T are taken; of the keys equal to T the ones with the
 // lowest columns fill the remaining slots.  Each thread owns a contiguous
 // segment of columns, so an exclusive scan of per-thread counts places every
 // chosen column directly at its ascending position.
