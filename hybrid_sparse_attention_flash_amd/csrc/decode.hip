@@ -43,7 +43,7 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t Kl[64 * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t Vl[D * VROW];
-  __shared__ float red[2][2][64];
+  __shared__ __attribute__((aligned(16))) float red[2][2][64];
   __shared__ int s_tlist[SPARSE ? TLMAX : 1];
   __shared__ int s_misc[4];
 
@@ -233,25 +233,16 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
         }
     }
     if (!SPARSE) {
-      // per-key max over this wave's heads; reduce-scatter leaves lane ln owning value ln
+      // per-key max over this wave's heads, reduced in registers: every lane
+      // of a quad ends with the maxima of keys off .. off+3
       float cm[32];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) cm[mb * 16 + i] = sacc[mb][i];
-#pragma unroll
-      for (int st = 0; st < 5; ++st) {
-        const int half = 16 >> st;
-        const bool upper = (ln & half) != 0;
-#pragma unroll
-        for (int x = 0; x < half; ++x) {
-          const float send = upper ? cm[x] : cm[x + half];
-          const float keep = upper ? cm[x + half] : cm[x];
-          cm[x] = fmaxf(keep, __shfl_xor(send, half));
-        }
-      }
-      const int mb = ln >> 4, i = ln & 15;
-      red[t & 1][wave][mb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3)] = cm[0];
+      const f32x4 m4 = colmax32(cm);
+      const int off = (ln >> 4) * 32 + 8 * ((ln >> 2) & 3) + 4 * hh;
+      if ((ln & 3) == 0) *(f32x4*)&red[t & 1][wave][off] = m4;
     }
     // online softmax (base 2); the rescale of O is skipped when no row max moved
     float mt = kNegInf;
@@ -337,54 +328,59 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
   }
 }
 
-// One workgroup per (layer, sequence, head).  Thread (g, q) folds the partials
-// s = g, g + NG, g + 2 NG, ... of output columns [4q, 4q+4) with the exact LSE
-// rule, then the NG group results are folded in group order in LDS, so the
-// result does not depend on scheduling.
+// One workgroup per (layer, sequence, head), in two passes.  First the
+// workgroup takes the maximum M of the partials' reference maxima.  Then
+// thread (g, q) sums the partials s = g, g + NG, g + 2 NG, ... of output
+// columns [4q, 4q+4), each weighted by exp2((m_s - M) c) (the exact LSE
+// rule with a common reference, so the sum has no serial dependence and the
+// loads of many partials are in flight together), and the NG group sums are
+// added in group order in LDS, so the result does not depend on scheduling.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const MergeArgs a) {
   constexpr int NQ = D / 4;          // float4 column groups
   constexpr int NG = 256 / NQ;       // split groups
-  __shared__ float sm[NG], sl[NG];
+  __shared__ float sl[NG], smax[4];
   __shared__ float4 so[NG][NQ];
   const int bid = blockIdx.x;
   const int h = bid % a.Hq;
   const int b = (bid / a.Hq) % a.B;
   const int layer = bid / (a.Hq * a.B);
-  const int q = threadIdx.x % NQ, g = threadIdx.x / NQ;
+  const int tid = threadIdx.x;
+  const int q = tid % NQ, g = tid / NQ;
   const int64_t base = (int64_t)(layer * a.B + b) * a.nsplit;
   const float c2 = a.scale_log2;
-  float m = kNegInf, l = 0.f;
+  // pass 1: M = max over the splits' m
+  float mx = kNegInf;
+  for (int s = tid; s < a.nsplit; s += 256) mx = fmaxf(mx, a.part_ml[((base + s) * a.Hq + h) * 2]);
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) smax[tid >> 6] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+  // pass 2: weighted sums (empty partials have m = -inf and weight 0)
+  float l = 0.f;
   float4 o = {0.f, 0.f, 0.f, 0.f};
-  for (int s = g; s < a.nsplit; s += NG) {
-    const int64_t p = (base + s) * a.Hq + h;
-    const float ms = a.part_ml[p * 2], ls = a.part_ml[p * 2 + 1];
-    const float4 os = *(const float4*)(a.part_o + p * D + 4 * q);
-    if (ms == kNegInf) continue;
-    const float mn = fmaxf(m, ms);
-    const float wo = (m == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);
-    const float wn = __builtin_amdgcn_exp2f((ms - mn) * c2);
-    l = l * wo + ls * wn;
-    o.x = o.x * wo + os.x * wn; o.y = o.y * wo + os.y * wn;
-    o.z = o.z * wo + os.z * wn; o.w = o.w * wo + os.w * wn;
-    m = mn;
+  if (M != kNegInf) {
+#pragma unroll 4
+    for (int s = g; s < a.nsplit; s += NG) {
+      const int64_t p = (base + s) * a.Hq + h;
+      const float ms = a.part_ml[p * 2], ls = a.part_ml[p * 2 + 1];
+      const float4 os = *(const float4*)(a.part_o + p * D + 4 * q);
+      const float w = ms == kNegInf ? 0.f : __builtin_amdgcn_exp2f((ms - M) * c2);
+      l = fmaf(ls, w, l);
+      o.x = fmaf(os.x, w, o.x); o.y = fmaf(os.y, w, o.y);
+      o.z = fmaf(os.z, w, o.z); o.w = fmaf(os.w, w, o.w);
+    }
   }
-  if (q == 0) { sm[g] = m; sl[g] = l; }
+  if (q == 0) sl[g] = l;
   so[g][q] = o;
   __syncthreads();
   if (g == 0) {
-    float M = kNegInf;
-    for (int x = 0; x < NG; ++x) M = fmaxf(M, sm[x]);
     float L = 0.f;
     float4 O = {0.f, 0.f, 0.f, 0.f};
-    if (M != kNegInf) {
-      for (int x = 0; x < NG; ++x) {
-        if (sm[x] == kNegInf) continue;
-        const float w = __builtin_amdgcn_exp2f((sm[x] - M) * c2);
-        L += sl[x] * w;
-        const float4 v = so[x][q];
-        O.x += v.x * w; O.y += v.y * w; O.z += v.z * w; O.w += v.w * w;
-      }
+    for (int x = 0; x < NG; ++x) {
+      L += sl[x];
+      const float4 v = so[x][q];
+      O.x += v.x; O.y += v.y; O.z += v.z; O.w += v.w;
     }
     const float inv = (M != kNegInf) ? a.v_scale / L : 0.f;
     const int64_t off = (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + 4 * q;

@@ -134,9 +134,7 @@ __device__ __forceinline__ int block_sum_1024(int v, int* sh) {
 // exclusive scan over the 1024 threads in thread order; returns (prefix, total)
 __device__ __forceinline__ int block_excl_scan_1024(int v, int* sh, int& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) { const int y = __shfl_up(x, o); if (lane >= o) x += y; }
+  const int x = wave_incl_scan_i32(v);
   __syncthreads();
   if (lane == 63) sh[w] = x;
   __syncthreads();
@@ -171,6 +169,7 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
   // them); the row tail is handled by clamping and masking
   const int64_t plast = cbase + ccols - 1;
   uint32_t key[VPT];
+  int cmv[VPT];                 // original columns (cmap) of the thread's positions
   const float* src = vr + p0;
   const bool fast = seg == VPT && p0 + VPT - 1 <= plast && (((uintptr_t)src) & 15u) == 0 &&
                     (mr == nullptr || (((uintptr_t)(mr + p0)) & 15u) == 0);
@@ -187,6 +186,7 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
 #pragma unroll
       for (int v4 = 0; v4 < VPT / 4; ++v4) {
         const int4 c = ((const int4*)(mr + p0))[v4];
+        cmv[4 * v4 + 0] = c.x; cmv[4 * v4 + 1] = c.y; cmv[4 * v4 + 2] = c.z; cmv[4 * v4 + 3] = c.w;
         if (c.x < 0) key[4 * v4 + 0] = 0xff800000u;     // -inf: an empty candidate slot
         if (c.y < 0) key[4 * v4 + 1] = 0xff800000u;
         if (c.z < 0) key[4 * v4 + 2] = 0xff800000u;
@@ -198,11 +198,14 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
       uint32_t kk = 0xff800000u;
+      int cv = -1;
       if (v < seg && p0 + v <= plast) {
         kk = __builtin_bit_cast(uint32_t, vr[p0 + v]);
-        if (mr && mr[p0 + v] < 0) kk = 0xff800000u;
+        if (mr) cv = mr[p0 + v];
+        if (mr && cv < 0) kk = 0xff800000u;
       }
       key[v] = kk;
+      cmv[v] = cv;
     }
   }
 #pragma unroll
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
   // share the digits chosen so far and picks, scanning digits downward, the
   // one whose bin holds the remaining rank.  need = how many keys equal to T
   // are taken (the rest of k after all keys > T).
-  __shared__ int hist[256];
+  __shared__ __attribute__((aligned(16))) int histc[256 * 32];
   __shared__ int s_pick[2];
   uint32_t T = 1u;
   int need = 0;
@@ -240,17 +243,23 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
     int krem = k;
     for (int round = 0; round < 4; ++round) {
       const int shift = 24 - 8 * round;
-      if (tid < 256) hist[tid] = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) histc[tid + 1024 * i] = 0;
       __syncthreads();
+      // 32 copies of each bin, lane l adding to copy l % 32, so lanes that
+      // share a digit (often all of them: the top digit is sign and
+      // exponent) do not serialise on one LDS address
 #pragma unroll
       for (int v = 0; v < VPT; ++v)
-        if (key[v] != 0u && (key[v] & pmask) == prefix) atomicAdd(&hist[(key[v] >> shift) & 255u], 1);
+        if (key[v] != 0u && (key[v] & pmask) == prefix) atomicAdd(&histc[((key[v] >> shift) & 255u) * 32 + (tid & 31)], 1);
       __syncthreads();
       // thread t < 256 takes digit 255 - t; an inclusive scan over t counts
       // the keys with that digit or a larger one
       int c = 0, incl = 0;
       if (tid < 256) {
-        c = hist[255 - tid];
+        const int4* hc = (const int4*)&histc[(255 - tid) * 32];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { const int4 x = hc[i]; c += x.x + x.y + x.z + x.w; }
         incl = wave_incl_scan_i32(c);
         if ((tid & 63) == 63) shc[tid >> 6] = incl;
       }
@@ -264,7 +273,7 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
       prefix |= (uint32_t)s_pick[0] << shift;
       pmask |= 0xFFu << shift;
       krem -= s_pick[1];
-      __syncthreads();                          // s_pick, shc and hist are rewritten next round
+      __syncthreads();                          // s_pick, shc and histc are rewritten next round
     }
     T = prefix;
     need = krem;
@@ -297,9 +306,11 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     if (take & (1u << v)) {
-      const int64_t p = p0 + v;
-      out_idx[ob + pre] = mr ? mr[p] : (int32_t)p;
-      if (out_val) out_val[ob + pre] = vr[p];
+      // the score back from its (valid, hence nonzero) order key
+      const uint32_t kk = key[v];
+      const uint32_t bits = (kk & 0x80000000u) ? (kk & 0x7fffffffu) : ~kk;
+      out_idx[ob + pre] = mr ? cmv[v] : (int32_t)(p0 + v);
+      if (out_val) out_val[ob + pre] = __builtin_bit_cast(float, bits);
       ++pre;
     }
   }
