@@ -131,86 +131,47 @@ __device__ __forceinline__ int block_sum_1024(int v, int* sh) {
   return t;
 }
 
-// exclusive scan over the 1024 threads in thread order; returns (prefix, total)
-__device__ __forceinline__ int block_excl_scan_1024(int v, int* sh, int& total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int x = wave_incl_scan_i32(v);
-  __syncthreads();
-  if (lane == 63) sh[w] = x;
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) { const int s = sh[i]; before += (i < w) ? s : 0; tot += s; }
-  total = tot;
-  return before + x - v;
-}
-
 // vals: row r, position p at vals[r*row_stride + p] (p < cols)
 // cmap: if non-null, the original column of position p is cmap[r*row_stride + p]
 //       (positions with cmap == -1 are empty); else the column is chunk_base + p.
 // Output for (row, chunk): out_idx[(r*nchunk + chunk)*k ...], out_val likewise (if non-null).
-template <int VPT>
+//
+// Wave w owns positions [2048 w, 2048 w + 2048) of the chunk; lane L holds, in
+// slot v, position 2048 w + 64 v + L, so every load instruction reads 256
+// contiguous bytes and position order is (wave, slot, lane) order.
+template <int VPT, bool CMAP>
 __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restrict__ vals,
                                                           const int32_t* __restrict__ cmap, int64_t rows,
                                                           int64_t cols, int64_t row_stride, int64_t chunk_cols,
                                                           int nchunk, int k, int32_t* __restrict__ out_idx,
                                                           float* __restrict__ out_val, int32_t* __restrict__ count) {
-  __shared__ int sh[16];
+  static_assert(VPT * 64 * 16 == 32768, "a workgroup covers 32768 positions");
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int64_t r = blockIdx.x / nchunk;
   const int chunk = blockIdx.x % nchunk;
   const int64_t cbase = (int64_t)chunk * chunk_cols;
-  const int64_t ccols = min(chunk_cols, cols - cbase);
-  const int seg = (int)((ccols + 1023) / 1024);        // <= VPT
-  const int64_t p0 = cbase + (int64_t)tid * seg;
-  const float* vr = vals + r * row_stride;
-  const int32_t* mr = cmap ? cmap + r * row_stride : nullptr;
-  // loads are straight-line (no branch per element, which would serialise
-  // them); the row tail is handled by clamping and masking
-  const int64_t plast = cbase + ccols - 1;
+  const int ccols = (int)min(chunk_cols, cols - cbase);
+  const float* vr = vals + r * row_stride + cbase;
+  const int32_t* mr = CMAP ? cmap + r * row_stride + cbase : nullptr;
+  const int pos0 = wave * (64 * VPT) + lane;           // position of slot 0
+  // straight-line loads from clamped positions, masked afterwards
   uint32_t key[VPT];
-  int cmv[VPT];                 // original columns (cmap) of the thread's positions
-  const float* src = vr + p0;
-  const bool fast = seg == VPT && p0 + VPT - 1 <= plast && (((uintptr_t)src) & 15u) == 0 &&
-                    (mr == nullptr || (((uintptr_t)(mr + p0)) & 15u) == 0);
-  if (fast) {
+  int cmv[CMAP ? VPT : 1];      // original columns (cmap) of the positions
 #pragma unroll
-    for (int v4 = 0; v4 < VPT / 4; ++v4) {
-      const float4 f = ((const float4*)src)[v4];
-      key[4 * v4 + 0] = __builtin_bit_cast(uint32_t, f.x);
-      key[4 * v4 + 1] = __builtin_bit_cast(uint32_t, f.y);
-      key[4 * v4 + 2] = __builtin_bit_cast(uint32_t, f.z);
-      key[4 * v4 + 3] = __builtin_bit_cast(uint32_t, f.w);
-    }
-    if (mr) {
-#pragma unroll
-      for (int v4 = 0; v4 < VPT / 4; ++v4) {
-        const int4 c = ((const int4*)(mr + p0))[v4];
-        cmv[4 * v4 + 0] = c.x; cmv[4 * v4 + 1] = c.y; cmv[4 * v4 + 2] = c.z; cmv[4 * v4 + 3] = c.w;
-        if (c.x < 0) key[4 * v4 + 0] = 0xff800000u;     // -inf: an empty candidate slot
-        if (c.y < 0) key[4 * v4 + 1] = 0xff800000u;
-        if (c.z < 0) key[4 * v4 + 2] = 0xff800000u;
-        if (c.w < 0) key[4 * v4 + 3] = 0xff800000u;
-      }
-    }
-  } else {
-    // the row tail (at most one thread of a chunk): element-wise
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      uint32_t kk = 0xff800000u;
-      int cv = -1;
-      if (v < seg && p0 + v <= plast) {
-        kk = __builtin_bit_cast(uint32_t, vr[p0 + v]);
-        if (mr) cv = mr[p0 + v];
-        if (mr && cv < 0) kk = 0xff800000u;
-      }
-      key[v] = kk;
-      cmv[v] = cv;
-    }
+  for (int v = 0; v < VPT; ++v) {
+    const int p = pos0 + 64 * v;
+    const int pc = min(p, ccols - 1);
+    key[v] = __builtin_bit_cast(uint32_t, vr[pc]);
+    if constexpr (CMAP) cmv[v] = mr[pc];
   }
 #pragma unroll
-  for (int v = 0; v < VPT; ++v)
-    key[v] = (v < seg && p0 + v <= plast) ? score_key(__builtin_bit_cast(float, key[v])) : 0u;
+  for (int v = 0; v < VPT; ++v) {
+    const int p = pos0 + 64 * v;
+    bool ok = p < ccols;
+    if constexpr (CMAP) ok = ok && cmv[v] >= 0;          // cmap -1: an empty candidate slot
+    key[v] = ok ? score_key(__builtin_bit_cast(float, key[v])) : 0u;
+  }
   // keys >= t in the chunk: per-lane counts, wave totals by DPP, the 16 wave
   // totals through LDS
   __shared__ int shc[16];
@@ -219,7 +180,7 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
 #pragma unroll
     for (int v = 0; v < VPT; ++v) n += (key[v] >= t) ? 1 : 0;
     n = wave_sum_i32(n);
-    if ((tid & 63) == 0) shc[tid >> 6] = n;
+    if (lane == 0) shc[wave] = n;
     __syncthreads();
     int tot = 0;
 #pragma unroll
@@ -236,7 +197,7 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
   // are taken (the rest of k after all keys > T).
   __shared__ __attribute__((aligned(16))) int histc[256 * 32];
   __shared__ int s_pick[2];
-  uint32_t T = 1u;
+  uint32_t T = 0u;
   int need = 0;
   if (!all) {
     uint32_t prefix = 0u, pmask = 0u;
@@ -261,12 +222,11 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
 #pragma unroll
         for (int i = 0; i < 8; ++i) { const int4 x = hc[i]; c += x.x + x.y + x.z + x.w; }
         incl = wave_incl_scan_i32(c);
-        if ((tid & 63) == 63) shc[tid >> 6] = incl;
+        if (lane == 63) shc[wave] = incl;
       }
       __syncthreads();
       if (tid < 256) {
-        const int w = tid >> 6;
-        for (int i = 0; i < w; ++i) incl += shc[i];
+        for (int i = 0; i < wave; ++i) incl += shc[i];
         if (incl - c < krem && krem <= incl) { s_pick[0] = 255 - tid; s_pick[1] = incl - c; }
       }
       __syncthreads();
@@ -278,40 +238,56 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
     T = prefix;
     need = krem;
   }
-  int nt = 0;
-  if (!all) {
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) nt += (key[v] == T) ? 1 : 0;
-  }
-  int ttot;
-  const int tpre = block_excl_scan_1024(nt, sh, ttot);
-  uint32_t take = 0u;
-  int cnt = 0;
+  if (k <= 0) { T = 0xffffffffu; need = 0; }      // nothing is taken
+  // ---- compaction in position order.  Taken: keys > T, and the first `need`
+  // keys equal to T.  (all: T = 0, need = 0 takes every valid key.)
+  __shared__ int s_gt[16], s_eq[16];
   {
-    int tr = tpre;
+    int ngt = 0, neq = 0;
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      bool f;
-      if (k <= 0) f = false;
-      else if (all) f = key[v] != 0u;
-      else if (key[v] > T) f = true;
-      else if (key[v] == T) { f = tr < need; ++tr; }
-      else f = false;
-      if (f) { take |= 1u << v; ++cnt; }
-    }
+    for (int v = 0; v < VPT; ++v) { ngt += key[v] > T ? 1 : 0; neq += key[v] == T ? 1 : 0; }
+    ngt = wave_sum_i32(ngt);
+    neq = wave_sum_i32(neq);
+    if (lane == 0) { s_gt[wave] = ngt; s_eq[wave] = neq; }
   }
-  int total;
-  int pre = block_excl_scan_1024(cnt, sh, total);
+  __syncthreads();
+  // this wave's first tie rank and first output slot, and the chunk total:
+  // wave w takes its keys > T and those of its ties whose rank is below need
+  int tie0 = 0, out0 = 0, total = 0;
+  {
+    int t0 = 0, o0 = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int eq = s_eq[w];
+      if (w == wave) { tie0 = t0; out0 = o0; }
+      o0 += s_gt[w] + min(max(need - t0, 0), eq);
+      t0 += eq;
+    }
+    total = o0;
+  }
   const int64_t ob = (r * nchunk + chunk) * (int64_t)k;
+  int trun = tie0, orun = out0;
+  // tie ranks are needed only in waves that hold keys equal to T (usually one)
+  const bool has_eq = __builtin_amdgcn_readfirstlane(s_eq[wave]) != 0;
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
-    if (take & (1u << v)) {
+    bool tk = key[v] > T;
+    if (has_eq) {
+      const bool eq = key[v] == T;
+      const unsigned long long be = __ballot(eq);
+      const int trank = trun + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+      trun += __popcll(be);
+      tk = tk || (eq && trank < need);
+    }
+    const unsigned long long bt = __ballot(tk);
+    const int slot = orun + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bt >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bt, 0u));
+    orun += __popcll(bt);
+    if (tk) {
       // the score back from its (valid, hence nonzero) order key
       const uint32_t kk = key[v];
       const uint32_t bits = (kk & 0x80000000u) ? (kk & 0x7fffffffu) : ~kk;
-      out_idx[ob + pre] = mr ? cmv[v] : (int32_t)(p0 + v);
-      if (out_val) out_val[ob + pre] = __builtin_bit_cast(float, bits);
-      ++pre;
+      if constexpr (CMAP) out_idx[ob + slot] = cmv[v];
+      else out_idx[ob + slot] = (int32_t)(cbase + pos0 + 64 * v);
+      if (out_val) out_val[ob + slot] = __builtin_bit_cast(float, bits);
     }
   }
   for (int p = total + tid; p < k; p += 1024) {
@@ -360,7 +336,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if (a.cols <= kTopkChunk) {
-    hipLaunchKernelGGL(topk_block_kernel<kTopkVPT>, dim3((unsigned)a.rows), dim3(1024), 0, s, a.scores,
+    hipLaunchKernelGGL((topk_block_kernel<kTopkVPT, false>), dim3((unsigned)a.rows), dim3(1024), 0, s, a.scores,
                        (const int32_t*)nullptr, a.rows, a.cols, a.row_stride, kTopkChunk, 1, a.k, a.idx,
                        (float*)nullptr, a.count);
     return hipGetLastError();
@@ -369,13 +345,13 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   // the winners' winners; chunk winners are in ascending column order, so the
   // concatenation is too and ties still resolve by column
   const int nchunk = (int)((a.cols + kTopkChunk - 1) / kTopkChunk);
-  hipLaunchKernelGGL(topk_block_kernel<kTopkVPT>, dim3((unsigned)(a.rows * nchunk)), dim3(1024), 0, s, a.scores,
+  hipLaunchKernelGGL((topk_block_kernel<kTopkVPT, false>), dim3((unsigned)(a.rows * nchunk)), dim3(1024), 0, s, a.scores,
                      (const int32_t*)nullptr, a.rows, a.cols, a.row_stride, kTopkChunk, nchunk, a.k, a.cand_idx,
                      a.cand_val, (int32_t*)nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t ccols = (int64_t)nchunk * a.k;       // <= kTopkChunk by validation
-  hipLaunchKernelGGL(topk_block_kernel<kTopkVPT>, dim3((unsigned)a.rows), dim3(1024), 0, s, (const float*)a.cand_val,
+  hipLaunchKernelGGL((topk_block_kernel<kTopkVPT, true>), dim3((unsigned)a.rows), dim3(1024), 0, s, (const float*)a.cand_val,
                      (const int32_t*)a.cand_idx, a.rows, ccols, ccols, kTopkChunk, 1, a.k, a.idx, (float*)nullptr,
                      a.count);
   return hipGetLastError();
