@@ -490,9 +490,10 @@ hys_status hys_decode_step(const hys_decode_params* p, hys_tensor4 q_full, hys_t
           o_sparse[l].stride[2] != o_sparse[0].stride[2])
         return fail(HYS_ERR_UNSUPPORTED, "all o_sparse must share dtype and strides");
     }
-    // split-K: about 4 two-wave workgroups per CU, at least 8 key tiles each
+    // split-K: two workgroups (two compute waves and one staging wave each)
+    // per CU, at least 8 key tiles each
     const int64_t ntiles = (Nmax + 63) / 64;
-    int nsplit = (int)(1024 / B);
+    int nsplit = (int)(512 / B);
     if (nsplit < 1) nsplit = 1;
     if ((int64_t)nsplit * 8 > ntiles) nsplit = (int)((ntiles + 7) / 8);
     const int nsplit_env = env_int("HYS_DECODE_SPLIT", 0);

@@ -26,28 +26,34 @@
 namespace hys {
 
 template <int SPARSE, typename KT, int D>
-__global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
-  // Workgroup = 2 waves; wave w owns query heads [32w, 32w+32) (one MFMA N-block).
-  // Both waves consume the same staged 64-key tile, so every cache byte is read
-  // once per workgroup; with at most ~256 registers per wave two workgroups'
-  // waves share each SIMD and hide each other's latency.
+__global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
+  // Workgroup = 4 waves.  Waves 0 and 1 compute: wave w owns query heads
+  // [32w, 32w+32) (one MFMA N-block) and both consume the same staged 64-key
+  // tile, so every cache byte is read once per workgroup.  Waves 2 and 3
+  // stage: they keep the loads of the next NSET tiles in flight in their own
+  // registers and write each tile, converted to bf16 (K row-major, V
+  // transposed), into a two-stage LDS ring one tile ahead of the compute
+  // waves, so these wait on LDS only, never on memory latency.  One barrier
+  // per tile.
   constexpr int KROW = D + 8;                 // bf16 LDS row stride of K
   constexpr int VROW = 68;                    // bf16 LDS row stride of V^T
   constexpr int NDB = D / 32;
   constexpr int NQC = D / 16;
-  constexpr int KUN = 64 * (D / 8);           // K units (8 elements) per tile
-  constexpr int KU = KUN / 128;               // per thread
-  constexpr int VUN = 16 * (D / 8);           // V units (4 keys x 8 d)
-  constexpr int VU = VUN / 128;
+  constexpr int NST = 128;                    // staging threads
+  constexpr int KU = 64 * (D / 8) / NST;      // K units (8 elements) per staging thread
+  constexpr int VU = (16 * (D / 8) + NST - 1) / NST;   // V units (4 keys x 8 d) per staging thread
+  constexpr int NSET = sizeof(KT) == 1 ? 3 : 1;   // tiles of loads in flight
   constexpr int TLMAX = 2048;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Kl[64 * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vl[D * VROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Kl[2][64 * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Vl[2][D * VROW];
   __shared__ __attribute__((aligned(16))) float red[2][2][64];
   __shared__ int s_tlist[SPARSE ? TLMAX : 1];
   __shared__ int s_misc[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, ln = lane & 31;
+  const bool stager = wave >= 2;
+  const int st = tid - 128;                   // staging thread index (stager waves)
   const int bid = blockIdx.x;
   const int s = bid % a.nsplit;
   const int rest = bid / a.nsplit;
@@ -63,17 +69,17 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
     wstart = max(0, n - a.window);
     const int32_t* sel = a.idx + (int64_t)b * a.idx_sb;
     int carry = 0;
-    for (int e0 = 0; e0 < a.topk; e0 += 128) {
+    for (int e0 = 0; e0 < a.topk; e0 += 256) {
       const int e = e0 + tid;
       const int sv = (e < a.topk) ? sel[e] : -1;
       const bool pre = sv >= 0 && sv < wstart;
       const unsigned long long bal = __ballot(pre);
       if (lane == 0) s_misc[wave] = __popcll(bal);
       __syncthreads();
-      const int before = carry + (wave ? s_misc[0] : 0);
+      const int before = carry + (wave > 0 ? s_misc[0] : 0) + (wave > 1 ? s_misc[1] : 0) + (wave > 2 ? s_misc[2] : 0);
       const int pos = before + __popcll(bal & ((1ull << lane) - 1ull));
       if (pre && pos < TLMAX) s_tlist[pos] = sv;
-      carry += s_misc[0] + s_misc[1];
+      carry += s_misc[0] + s_misc[1] + s_misc[2] + s_misc[3];
       __syncthreads();
     }
     npre = min(carry, TLMAX);
@@ -91,10 +97,99 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
     return p < nkeys ? wstart + (p - npre) : -1;
   };
 
-  // ---- query fragments (this wave's 32 heads) --------------------------------
+  // ---- staging (waves 2, 3) ----------------------------------------------------
+  // staging thread x, K unit u: key u*(NST/(D/8)) + x/(D/8), 8 elements from
+  // x%(D/8)*8; V unit u: keys 4(x%16) .. 4(x%16)+3, 8 elements from
+  // (u*NST/16 + x/16)*8
+  const KT* kb = (const KT*)a.k + (int64_t)b * a.k_sb;
+  const KT* vb = (const KT*)a.v + (int64_t)b * a.v_sb;
+  Raw8<KT> kreg[NSET][KU];
+  Raw8<KT> vreg[NSET][VU][4];
+  uint32_t kmask[NSET], vmask[NSET];
+  bool sfull[NSET];
+  const int koff0 = (st / (D / 8)) * (int)a.k_st + (st % (D / 8)) * 8;
+  const int kstep = (NST / (D / 8)) * (int)a.k_st;
+  const int voff0 = ((st % 16) * 4) * (int)a.v_st + (st / 16) * 8;
+  constexpr int VUN = 16 * (D / 8);
+
+  auto stage_load = [&](auto set_tag, int t) __attribute__((always_inline)) {
+    constexpr int S = decltype(set_tag)::value;
+    // a contiguous tile of 64 valid keys: one uniform base, no masking
+    sfull[S] = !SPARSE && t * 64 + 63 < n;
+    if (sfull[S]) {
+      const KT* kt = kb + (int64_t)t * 64 * a.k_st;
+      const KT* vt = vb + (int64_t)t * 64 * a.v_st;
+#pragma unroll
+      for (int u = 0; u < KU; ++u) kreg[S][u] = load8<KT>(kt + koff0 + u * kstep);
+#pragma unroll
+      for (int u = 0; u < VU; ++u)
+        if (VUN % NST == 0 || u * NST + st < VUN) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vreg[S][u][r] = load8<KT>(vt + voff0 + r * (int)a.v_st + u * (NST / 16) * 8);
+        }
+      return;
+    }
+    // loads are unconditional from a clamped in-bounds key (key 0); empty
+    // slots are zeroed when staged (see keep_if)
+    uint32_t km = 0u, vm = 0u;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int unit = u * NST + st;
+      const int key = unit / (D / 8), c8 = unit % (D / 8);
+      const int j = keyof(t, key);
+      km |= (j >= 0 ? 1u : 0u) << u;
+      kreg[S][u] = load8<KT>(kb + (int64_t)(j >= 0 ? j : 0) * a.k_st + c8 * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      const int unit = u * NST + st;
+      if (VUN % NST != 0 && unit >= VUN) continue;
+      const int kg = unit % 16, dc = unit / 16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = keyof(t, kg * 4 + r);
+        vm |= (j >= 0 ? 1u : 0u) << (4 * u + r);
+        vreg[S][u][r] = load8<KT>(vb + (int64_t)(j >= 0 ? j : 0) * a.v_st + dc * 8);
+      }
+    }
+    kmask[S] = km; vmask[S] = vm;
+  };
+  auto stage_store = [&](auto set_tag, int stage) __attribute__((always_inline)) {
+    constexpr int S = decltype(set_tag)::value;
+    const bool full = sfull[S];
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int unit = u * NST + st;
+      const int key = unit / (D / 8), c8 = unit % (D / 8);
+      if (!full) keep_if(kreg[S][u], (kmask[S] >> u) & 1u);
+      *(uint4*)&Kl[stage][key * KROW + c8 * 8] = to_ct(kreg[S][u]).a;
+    }
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      const int unit = u * NST + st;
+      if (VUN % NST != 0 && unit >= VUN) continue;
+      const int kg = unit % 16, dc = unit / 16;     // one write covers a V^T row's 16 key groups
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (!full) keep_if(vreg[S][u][r], (vmask[S] >> (4 * u + r)) & 1u);
+      const uint4 r0 = to_ct(vreg[S][u][0]).a, r1 = to_ct(vreg[S][u][1]).a, r2 = to_ct(vreg[S][u][2]).a,
+                  r3 = to_ct(vreg[S][u][3]).a;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t w0 = u4get(r0, p), w1 = u4get(r1, p), w2 = u4get(r2, p), w3 = u4get(r3, p);
+        uint2 e, o;
+        e.x = __builtin_amdgcn_perm(w1, w0, 0x05040100u); e.y = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
+        o.x = __builtin_amdgcn_perm(w1, w0, 0x07060302u); o.y = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
+        *(uint2*)&Vl[stage][(dc * 8 + 2 * p) * VROW + kg * 4] = e;
+        *(uint2*)&Vl[stage][(dc * 8 + 2 * p + 1) * VROW + kg * 4] = o;
+      }
+    }
+  };
+
+  // ---- query fragments (compute waves: this wave's 32 heads) -------------------
   const uint16_t* qb = (const uint16_t*)a.q[layer] + (int64_t)b * a.q_sb;
   const int head = wave * 32 + ln;
-  const bool hvalid = head < a.Hq;
+  const bool hvalid = !stager && head < a.Hq;
   bf16x8 qf[NQC];
 #pragma unroll
   for (int c = 0; c < NQC; ++c) {
@@ -110,85 +205,7 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  const KT* kb = (const KT*)a.k + (int64_t)b * a.k_sb;
-  const KT* vb = (const KT*)a.v + (int64_t)b * a.v_sb;
-  Raw8<KT> kreg[KU];
-  Raw8<KT> vreg[VU][4];
-  uint32_t kmask = 0u, vmask = 0u;
-
-  // loads are unconditional from a clamped in-bounds key (key 0); empty slots
-  // are zeroed when staged (see keep_if)
-  // per-thread element offsets inside a tile (independent of the tile): unit
-  // tid + 128u is key tid/(D/8) + u*128/(D/8) (K) or key group tid%16 with d
-  // chunk tid/16 + 8u (V), so one base register and uniform strides suffice
-  const int koff0 = (tid / (D / 8)) * (int)a.k_st + (tid % (D / 8)) * 8;
-  const int kstep = (128 / (D / 8)) * (int)a.k_st;
-  const int voff0 = ((tid % 16) * 4) * (int)a.v_st + (tid / 16) * 8;
-  bool staged_full = true;
-
-  auto stage_load = [&](int t) {
-    // a contiguous tile of 64 valid keys: one uniform base, no masking
-    staged_full = !SPARSE && t * 64 + 63 < n;
-    if (staged_full) {
-      const KT* kt = kb + (int64_t)t * 64 * a.k_st;
-      const KT* vt = vb + (int64_t)t * 64 * a.v_st;
-#pragma unroll
-      for (int u = 0; u < KU; ++u) kreg[u] = load8<KT>(kt + koff0 + u * kstep);
-#pragma unroll
-      for (int u = 0; u < VU; ++u)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vreg[u][r] = load8<KT>(vt + voff0 + r * (int)a.v_st + u * 64);
-      return;
-    }
-    kmask = 0u; vmask = 0u;
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int unit = tid + 128 * u;
-      const int key = unit / (D / 8), c8 = unit % (D / 8);
-      const int j = keyof(t, key);
-      kmask |= (j >= 0 ? 1u : 0u) << u;
-      kreg[u] = load8<KT>(kb + (int64_t)(j >= 0 ? j : 0) * a.k_st + c8 * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < VU; ++u) {
-      const int unit = tid + 128 * u;
-      const int kg = unit % 16, dc = unit / 16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = keyof(t, kg * 4 + r);
-        vmask |= (j >= 0 ? 1u : 0u) << (4 * u + r);
-        vreg[u][r] = load8<KT>(vb + (int64_t)(j >= 0 ? j : 0) * a.v_st + dc * 8);
-      }
-    }
-  };
-  auto stage_store = [&]() {
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int unit = tid + 128 * u;
-      const int key = unit / (D / 8), c8 = unit % (D / 8);
-      if (!staged_full) keep_if(kreg[u], (kmask >> u) & 1u);
-      *(uint4*)&Kl[key * KROW + c8 * 8] = to_ct(kreg[u]).a;
-    }
-#pragma unroll
-    for (int u = 0; u < VU; ++u) {
-      const int unit = tid + 128 * u;
-      const int kg = unit % 16, dc = unit / 16;     // one write covers a V^T row's 16 key groups
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (!staged_full) keep_if(vreg[u][r], (vmask >> (4 * u + r)) & 1u);
-      const uint4 r0 = to_ct(vreg[u][0]).a, r1 = to_ct(vreg[u][1]).a, r2 = to_ct(vreg[u][2]).a, r3 = to_ct(vreg[u][3]).a;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t w0 = u4get(r0, p), w1 = u4get(r1, p), w2 = u4get(r2, p), w3 = u4get(r3, p);
-        uint2 e, o;
-        e.x = __builtin_amdgcn_perm(w1, w0, 0x05040100u); e.y = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
-        o.x = __builtin_amdgcn_perm(w1, w0, 0x07060302u); o.y = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
-        *(uint2*)&Vl[(dc * 8 + 2 * p) * VROW + kg * 4] = e;
-        *(uint2*)&Vl[(dc * 8 + 2 * p + 1) * VROW + kg * 4] = o;
-      }
-    }
-  };
-  // token scores of tile t: max over the two waves' per-key maxima
+  // token scores of tile t: max over the two compute waves' per-key maxima
   auto emit_scores = [&](int t) {
     if (!SPARSE && tid < 64) {
       const int j = t * 64 + tid;
@@ -198,29 +215,43 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
   };
 
   const float c2 = a.scale_log2;
-  if (t0 < t1) stage_load(t0);
-  for (int t = t0; t < t1; ++t) {
-    __syncthreads();
-    if (t > t0) emit_scores(t - 1);
-    stage_store();
-    __syncthreads();
-    if (t + 1 < t1) stage_load(t + 1);
-
-    // S^T = K q^T: 64 keys (2 M-blocks) x this wave's 32 heads; fragments read one step ahead
+  const float lazy_raw = kLazyLog2 / c2;      // the reference slack in raw dot-product units
+  // one tile of attention for this compute wave, from LDS stage t & 1
+  auto compute = [&](int t) __attribute__((always_inline)) {
+    const uint16_t* Kc = Kl[t & 1];
+    const uint16_t* Vc = Vl[t & 1];
+    // S^T = K q^T: 64 keys (2 M-blocks) x this wave's 32 heads; K fragments
+    // are read two k-steps ahead of their MFMAs (pinned: the scheduler would
+    // otherwise sink each read next to its MFMA and expose the LDS latency)
     f32x16 sacc[2];
     const f32x16 zero16 = {};
-    uint4 kf0 = *(const uint4*)&Kl[ln * KROW + 8 * hh];
-    uint4 kf1 = *(const uint4*)&Kl[(32 + ln) * KROW + 8 * hh];
+    uint4 kf[NQC][2];
+    auto kfrag = [&](int c) __attribute__((always_inline)) {
+      kf[c][0] = *(const uint4*)&Kc[ln * KROW + 16 * c + 8 * hh];
+      kf[c][1] = *(const uint4*)&Kc[(32 + ln) * KROW + 16 * c + 8 * hh];
+    };
+    kfrag(0);
+    kfrag(1);
 #pragma unroll
     for (int c = 0; c < NQC; ++c) {
-      const uint4 a0 = kf0, a1 = kf1;
-      if (c + 1 < NQC) {
-        kf0 = *(const uint4*)&Kl[ln * KROW + 16 * (c + 1) + 8 * hh];
-        kf1 = *(const uint4*)&Kl[(32 + ln) * KROW + 16 * (c + 1) + 8 * hh];
-      }
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), qf[c], c == 0 ? zero16 : sacc[0], 0, 0, 0);
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), qf[c], c == 0 ? zero16 : sacc[1], 0, 0, 0);
+      if (c + 2 < NQC) kfrag(c + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[c][0]), qf[c], c == 0 ? zero16 : sacc[0], 0, 0, 0);
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[c][1]), qf[c], c == 0 ? zero16 : sacc[1], 0, 0, 0);
     }
+    // V^T fragments (A operand of O^T): the first d block is read now, under
+    // the softmax; later blocks one d block ahead of their MFMAs
+    auto vfrag = [&](int db, int kc) __attribute__((always_inline)) {
+      const uint16_t* vr = &Vc[(db * 32 + ln) * VROW + 16 * kc + 4 * hh];
+      const uint2 lo = *(const uint2*)vr;
+      const uint2 hi = *(const uint2*)(vr + 8);
+      uint4 va; va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
+      return va;
+    };
+    uint4 vf[2][4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) vf[0][kc] = vfrag(0, kc);
+    __builtin_amdgcn_sched_barrier(0);
     // mask empty list slots and padding heads
     const int rem = nkeys - t * 64;
     if (rem < 64 || !hvalid) {
@@ -244,19 +275,23 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
       const int off = (ln >> 4) * 32 + 8 * ((ln >> 2) & 3) + 4 * hh;
       if ((ln & 3) == 0) *(f32x4*)&red[t & 1][wave][off] = m4;
     }
-    // online softmax (base 2); the rescale of O is skipped when no row max moved
+    // online softmax (base 2) with a lazily moved reference maximum: a
+    // head's reference moves only when the tile max exceeds it by more than
+    // kLazyLog2 (so probabilities stay below 2^kLazyLog2 and O is rescaled in
+    // few tiles); O, l and the partial's m all use that reference, so the
+    // merged result is exact up to rounding
     float mt = kNegInf;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[mb][i]);
     mt = xor32_max(mt);
-    const float mnew = fmaxf(m_run, mt);
-    const float muse = (mnew == kNegInf) ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - muse) * c2);
-    const bool moved = mnew != m_run;
-    m_run = mnew;
-    const float mc = muse * c2;
+    // true when the reference is -inf and mt finite; false when both are -inf
+    const bool moved = mt > m_run + lazy_raw;
+    const float mref = moved ? mt : m_run;
+    const float alpha = moved ? __builtin_amdgcn_exp2f((m_run - mref) * c2) : 1.f;
+    m_run = mref;
+    const float mc = (mref == kNegInf) ? 0.f : mref * c2;
     float ps = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -285,28 +320,54 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
       pk.w = pack_bf16x2(sacc[mb][i0 + 6], sacc[mb][i0 + 7]);
       pf[kc] = as_bf16x8(pk);
     }
-    auto vfrag = [&](int db, int kc) {
-      const uint16_t* vr = &Vl[(db * 32 + ln) * VROW + 16 * kc + 4 * hh];
-      const uint2 lo = *(const uint2*)vr;
-      const uint2 hi = *(const uint2*)(vr + 8);
-      uint4 va; va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
-      return va;
-    };
-    uint4 vn = vfrag(0, 0);
 #pragma unroll
-    for (int st = 0; st < NDB * 4; ++st) {
-      const int db = st >> 2, kc = st & 3;
-      const uint4 va = vn;
-      if (st + 1 < NDB * 4) vn = vfrag((st + 1) >> 2, (st + 1) & 3);
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), pf[kc], acc[db], 0, 0, 0);
+    for (int db = 0; db < NDB; ++db) {
+      if (db + 1 < NDB) {
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) vf[(db + 1) & 1][kc] = vfrag(db + 1, kc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[db & 1][kc]), pf[kc], acc[db], 0, 0, 0);
+    }
+  };
+
+  // ---- tile pipeline: iteration i stages tile t0 + i (wave 2) while the
+  // compute waves take tile t0 + i - 1; the stager's loads run NSET tiles
+  // ahead.  The two roles run separate loops with the same barrier count, so
+  // neither keeps the other's registers live.
+  const int niter = (t1 > t0) ? (t1 - t0 + 1) : 0;
+  if (stager) {
+    if (t0 < t1) stage_load(std::integral_constant<int, 0>{}, t0);
+    if (NSET >= 2 && t0 + 1 < t1) stage_load(std::integral_constant<int, NSET >= 2 ? 1 : 0>{}, t0 + 1);
+    if (NSET >= 3 && t0 + 2 < t1) stage_load(std::integral_constant<int, NSET >= 3 ? 2 : 0>{}, t0 + 2);
+    auto step = [&](int i, auto set_tag) __attribute__((always_inline)) {
+      const int t = t0 + i;
+      if (t < t1) {
+        stage_store(set_tag, t & 1);
+        if (t + NSET < t1) stage_load(set_tag, t + NSET);
+      }
+      __syncthreads();
+    };
+    for (int i = 0; i < niter; i += NSET) {
+      step(i, std::integral_constant<int, 0>{});
+      if (NSET >= 2 && i + 1 < niter) step(i + 1, std::integral_constant<int, NSET >= 2 ? 1 : 0>{});
+      if (NSET >= 3 && i + 2 < niter) step(i + 2, std::integral_constant<int, NSET >= 3 ? 2 : 0>{});
+    }
+  } else {
+    for (int i = 0; i < niter; ++i) {
+      const int t = t0 + i;
+      if (i >= 2) emit_scores(t - 2);
+      if (i >= 1) compute(t - 1);
+      __syncthreads();
     }
   }
-  __syncthreads();
   if (t0 < t1) emit_scores(t1 - 1);
   // keys past the valid length: token scores are -inf (the workgroups of the
   // last split cover the tail of the score row)
   if (!SPARSE && s == a.nsplit - 1) {
-    for (int j = ntiles * 64 + tid; j < a.Nmax; j += 128) a.scores[(int64_t)b * a.sc_sb + j] = kNegInf;
+    for (int j = ntiles * 64 + tid; j < a.Nmax; j += 256) a.scores[(int64_t)b * a.sc_sb + j] = kNegInf;
   }
 
   // ---- this wave's partial (m, l, unnormalised O) ------------------------------
@@ -323,8 +384,6 @@ __global__ __launch_bounds__(128, 2) void decode_kernel(const DecArgs a) {
         *(float4*)(po + d) = v4;
       }
     if (hh == 0) { a.part_ml[pidx * 2] = m_run; a.part_ml[pidx * 2 + 1] = lsum; }
-  } else {
-    // (a wave whose lanes are all padding heads still joined every barrier)
   }
 }
 
@@ -400,7 +459,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const MergeArgs a) {
 
 hipError_t launch_decode(int sparse, int kt, int D, const DecArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)(a.nlayer * a.B * a.nsplit);
-#define HYS_DEC(SP, KT, DD) hipLaunchKernelGGL((decode_kernel<SP, KT, DD>), dim3(grid), dim3(128), 0, s, a)
+#define HYS_DEC(SP, KT, DD) hipLaunchKernelGGL((decode_kernel<SP, KT, DD>), dim3(grid), dim3(256), 0, s, a)
   if (kt == ET_FP8) {
     if (D == 128) { if (sparse) HYS_DEC(1, uint8_t, 128); else HYS_DEC(0, uint8_t, 128); }
     else if (D == 64) { if (sparse) HYS_DEC(1, uint8_t, 64); else HYS_DEC(0, uint8_t, 64); }
