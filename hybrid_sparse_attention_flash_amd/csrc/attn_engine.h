@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
   if (bid >= a.grid_used) return;
 
   // ---- work decomposition ------------------------------------------------
-  int b, qt, g = 0, ch_begin = 0, ch_end = 1;
+  int b, qt, g = 0, ch_begin = 0;
   if (MODE == M_FULL_TILE || MODE == M_SPARSE_TOKEN) {
     // the head chunks of one query tile run back to back on one XCD
     // (workgroups are dealt to the 8 XCDs round robin), so they stream the
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     qt = tile_rank / a.B;
     if (qt >= a.ntq) return;
     if (MODE == M_FULL_TILE) qt = a.ntq - 1 - qt;  // causal: longest rows first
-    ch_begin = ch; ch_end = ch + 1;
+    ch_begin = ch;
   } else {
     g = bid % a.Hkv;                               // KV group fastest: XCD x sees groups x mod Hkv
     const int rest = bid / a.Hkv;
@@ -108,6 +108,67 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
   const int HC = a.HC;
   // block scores reduced inside each wave when a query's heads are adjacent lanes
   const bool lane_scores = (MODE == M_FULL_BLOCK) && (32 % HC == 0);
+
+  // the workgroup's head chunk; its Q fragments are loaded first, so their
+  // latency overlaps the selection-list building below
+  const int ch = ch_begin;
+  int h0 = 0;
+  if (MODE == M_FULL_TILE || MODE == M_SPARSE_TOKEN) { g = ch / a.nhc; h0 = (ch % a.nhc) * HC; }
+
+  // ---- rows owned by this lane -------------------------------------------
+  int qpos[NB], head[NB], qiv[NB];
+  bool valid[NB];
+  bool wave_full = true;
+  int wave_qmin = 0x7fffffff, wave_qmax = -1;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int r = wave * 32 * NB + nb * 32 + ln;
+    const int qi = r / HC, hl = r - qi * HC;
+    qiv[nb] = qi;
+    qpos[nb] = q0 + qi;
+    head[nb] = g * a.G + h0 + hl;
+    valid[nb] = qi < a.BQ && qpos[nb] < a.Lq && (h0 + hl) < a.G;
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    int qv = valid[nb] ? qpos[nb] : 0x7fffffff;
+    int qx = valid[nb] ? qpos[nb] : -1;
+    for (int o = 32; o >= 1; o >>= 1) { qv = min(qv, __shfl_xor(qv, o)); qx = max(qx, __shfl_xor(qx, o)); }
+    wave_qmin = min(wave_qmin, qv);
+    wave_qmax = max(wave_qmax, qx);
+    wave_full = wave_full && (__ballot(!valid[nb]) == 0ull);
+  }
+  const bool wave_any = wave_qmax >= 0;
+  unsigned long long wave_qmask = 0ull;
+  if (BLOCKSEL) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      unsigned long long m = valid[nb] ? (1ull << qiv[nb]) : 0ull;
+      for (int o = 32; o >= 1; o >>= 1) m |= __shfl_xor(m, o);
+      wave_qmask |= m;
+    }
+  }
+
+  // ---- Q fragments (B operand of S^T) ------------------------------------
+  const QT* qbase = (const QT*)a.q + (int64_t)b * a.q_sb;
+  typedef typename std::conditional<F32, float, bf16x8>::type QFrag;
+  QFrag qf[NB][NQC];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    // unconditional loads from a clamped row (see keep_if), zeroed for padding rows
+    const QT* qr = qbase + (valid[nb] ? (int64_t)qpos[nb] * a.q_st + (int64_t)head[nb] * a.q_sh : 0);
+#pragma unroll
+    for (int c = 0; c < NQC; ++c) {
+      if constexpr (F32) {
+        const float x = qr[2 * c + hh];
+        qf[nb][c] = valid[nb] ? x : 0.0f;
+      } else {
+        const uint4 x = *(const uint4*)(qr + 16 * c + 8 * hh);
+        const uint4 z = {0u, 0u, 0u, 0u};
+        qf[nb][c] = as_bf16x8(valid[nb] ? x : z);
+      }
+    }
+  }
 
   // ---- per-WG selection lists ----------------------------------------------
   int ntiles = 0;
@@ -187,11 +248,20 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     for (int x = tid; x < nw; x += 256) s_selw[x] = 0;
     __syncthreads();
     const int32_t* sel = a.idx + (int64_t)b * a.idx_sb + (int64_t)qt * a.idx_sr;
+    // all of the tile's selections are loaded up front (one memory latency,
+    // not one per round below); k <= TLMAX = 8 * 256
+    int sv[TLMAX / 256];
+#pragma unroll
+    for (int i = 0; i < TLMAX / 256; ++i) {
+      const int e = i * 256 + tid;
+      sv[i] = (e < a.topk) ? sel[e] : -1;
+    }
     // order-preserving compaction of the selected tokens that precede the window
     int carry = 0;
-    for (int e0 = 0; e0 < a.topk; e0 += 256) {
-      const int e = e0 + tid;
-      const int s = (e < a.topk) ? sel[e] : -1;
+#pragma unroll
+    for (int i = 0; i < TLMAX / 256; ++i) {
+      if (i * 256 >= a.topk) break;
+      const int s = sv[i];
       const bool pre = s >= 0 && s < wstart;
       if (s >= wstart && s <= wend) s_selw[s - wstart] = 1;
       const unsigned long long bal = __ballot(pre);
@@ -370,66 +440,8 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     else stage_store_impl(buf, std::true_type{});
   };
 
-  const QT* qbase = (const QT*)a.q + (int64_t)b * a.q_sb;
 
-  for (int ch = ch_begin; ch < ch_end; ++ch) {
-    int h0 = 0;
-    if (MODE == M_FULL_TILE || MODE == M_SPARSE_TOKEN) { g = ch / a.nhc; h0 = (ch % a.nhc) * HC; }
-
-    // ---- rows owned by this lane -------------------------------------------
-    int qpos[NB], head[NB], qiv[NB];
-    bool valid[NB];
-    bool wave_full = true;
-    int wave_qmin = 0x7fffffff, wave_qmax = -1;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int r = wave * 32 * NB + nb * 32 + ln;
-      const int qi = r / HC, hl = r - qi * HC;
-      qiv[nb] = qi;
-      qpos[nb] = q0 + qi;
-      head[nb] = g * a.G + h0 + hl;
-      valid[nb] = qi < a.BQ && qpos[nb] < a.Lq && (h0 + hl) < a.G;
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      int qv = valid[nb] ? qpos[nb] : 0x7fffffff;
-      int qx = valid[nb] ? qpos[nb] : -1;
-      for (int o = 32; o >= 1; o >>= 1) { qv = min(qv, __shfl_xor(qv, o)); qx = max(qx, __shfl_xor(qx, o)); }
-      wave_qmin = min(wave_qmin, qv);
-      wave_qmax = max(wave_qmax, qx);
-      wave_full = wave_full && (__ballot(!valid[nb]) == 0ull);
-    }
-    const bool wave_any = wave_qmax >= 0;
-    unsigned long long wave_qmask = 0ull;
-    if (BLOCKSEL) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        unsigned long long m = valid[nb] ? (1ull << qiv[nb]) : 0ull;
-        for (int o = 32; o >= 1; o >>= 1) m |= __shfl_xor(m, o);
-        wave_qmask |= m;
-      }
-    }
-
-    // ---- Q fragments (B operand of S^T) ------------------------------------
-    typedef typename std::conditional<F32, float, bf16x8>::type QFrag;
-    QFrag qf[NB][NQC];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      // unconditional loads from a clamped row (see keep_if), zeroed for padding rows
-      const QT* qr = qbase + (valid[nb] ? (int64_t)qpos[nb] * a.q_st + (int64_t)head[nb] * a.q_sh : 0);
-#pragma unroll
-      for (int c = 0; c < NQC; ++c) {
-        if constexpr (F32) {
-          const float x = qr[2 * c + hh];
-          qf[nb][c] = valid[nb] ? x : 0.0f;
-        } else {
-          const uint4 x = *(const uint4*)(qr + 16 * c + 8 * hh);
-          const uint4 z = {0u, 0u, 0u, 0u};
-          qf[nb][c] = as_bf16x8(valid[nb] ? x : z);
-        }
-      }
-    }
-
+  {
     float m_run[NB], l_run[NB];
     f32x16 acc[NB][NDB];
 #pragma unroll
@@ -902,7 +914,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
         }
       }
     }
-  }  // chunk loop
+  }
 }
 
 // ---------------------------------------------------------------------------
