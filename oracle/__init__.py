@@ -14,8 +14,9 @@ It shares no code with the HIP path; both consume the seeded bytes of the
 
 Pins (tests/test_oracle*.py, run with -m "not gpu"): brute force in pure
 Python loops, torch's CPU float64 scaled_dot_product_attention, closed forms,
-invariants, hand-derived golden values under tests/golden/, and the fp8
-decode table against torch.float8_e4m3fn.
+invariants, hand-derived golden values under tests/golden/, the fp8
+decode table against torch.float8_e4m3fn, and the fp8 encoder of the KV
+Bridging projection (bridge.py) against torch's CPU float8 conversion.
 
 Parity unpinned (against the real HySparse/HySparse2, whose pages leave these
 open): the head reduction of importance scores (max over all query heads),
@@ -23,7 +24,7 @@ the gate's form (one sigmoid scalar per token and head, no bias), the empty
 sparse set rule, the per-tile token-score reading and the per-query forced
 window.  They are pinned only to this package's stated readings.
 """
-from . import fp8  # noqa: F401
+from . import bridge, fp8  # noqa: F401
 from .hysparse import (  # noqa: F401
     NEG_INF, attend, block_scores, decode_full, decode_sparse, decode_step,
     full_attention, gate_merge, hysparse2_block, hysparse_block, logits,
