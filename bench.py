@@ -11,7 +11,10 @@ HySparse2 1M-token decode step (B=4, fp8 MQA cache, top-1024 + recent 128,
 on the launch stream, the roofline of the dominant kernel, and the CPU oracle
 timed on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode]
+The HySparse2 KV Bridging projection (64k tokens, d_model 4096, fp8 MQA
+cache) is timed beside them with its own roofline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-bridge]
 """
 import argparse
 import json
@@ -360,6 +363,46 @@ def bench_decode(args, dev):
             "frac_hbm_step_equiv": round(gbs / PEAK_HBM_GBS, 4), "steps": steps}
 
 
+def bench_bridge(args, dev):
+    """HySparse2 KV Bridging: the cross-decoder full layer's K/V projected from
+    the self-decoder's hidden states into the fp8 MQA cache, one call per
+    step (64k tokens, d_model 4096, one 128-wide KV head)."""
+    w = synth.BRIDGE_WORKLOAD
+    B, L, dm, Hkv, D = w["B"], w["L"], w["d_model"], w["Hkv"], w["D"]
+    n = Hkv * D
+    log(f"[bench] generating {w['name']} inputs (L={L}, d_model={dm})")
+    h, wk, wv = synth.gen_bridge(0, w["cfg_id"], B, L, dm, n)
+    h, wk, wv = h.to(dev), wk.to(dev), wv.to(dev)
+    kc = torch.empty((B, L, Hkv, D), dtype=torch.uint8, device=dev)
+    vc = torch.empty_like(kc)
+    amax = torch.empty(2, dtype=torch.float32, device=dev)
+    ks = vs = 8.0 / 448.0
+    for _ in range(max(3, args.warmup)):
+        ops.hys_kv_bridge_fwd(h, wk, wv, kc, vc, ks, vs, amax)
+    torch.cuda.synchronize()
+    calls = max(20, args.steps * 5)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        ops.hys_kv_bridge_fwd(h, wk, wv, kc, vc, ks, vs, amax)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000 / calls
+    nbytes = B * L * dm * 2 + 2 * n * dm * 2 + 2 * B * L * n      # h, W_k + W_v, fp8 K + V
+    flops = 2.0 * B * L * dm * 2 * n
+    gbs = nbytes / (us * 1e-6) / 1e9
+    tf = flops / (us * 1e-6) / 1e12
+    log(f"[bench] kv bridge: {us:.1f} us/call, {gbs:.0f} GB/s, {tf:.0f} TFLOP/s")
+    return {"workload": w["name"], "us_per_call": round(us, 2), "tokens_per_s": round(B * L / (us * 1e-6), 1),
+            "calls": calls,
+            "roofline": {"kernel": "kv_bridge (bf16 projection, fp8 e4m3 epilogue)", "bound": "hbm",
+                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "avg_launch_us": round(us, 2),
+                         "work_per_launch": f"{nbytes:.4g} B (h, both weights, fp8 K and V)",
+                         "mfma_tflops": round(tf, 1), "frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": None}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -367,6 +410,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-bridge", action="store_true")
+    ap.add_argument("--only-bridge", action="store_true", help="time only the KV Bridging projection")
     ap.add_argument("--cpu-rows", type=int, default=64)
     ap.add_argument("--workload", default="moe80b_32k",
                     choices=["moe80b_32k", "dense7b_16k", "hysparse2_64k", "tiny_fp32"],
@@ -385,9 +430,13 @@ def main():
     ops.abi_version()      # fail loudly if libhys.so is missing
     if args.calibrate_copy:
         calibrate_copy(dev)
+    if args.only_bridge:
+        print(json.dumps({"kv_bridge": bench_bridge(args, dev)}), flush=True)
+        return
     pre = bench_prefill(args, dev)
     w = pre["w"]
     dec = None if args.no_decode else bench_decode(args, dev)
+    bridge = None if args.no_bridge else bench_bridge(args, dev)
     cpu = None
     if not args.no_cpu and pre["host"] is not None:
         log(f"[bench] timing the CPU oracle on {args.cpu_rows} sampled rows")
@@ -409,6 +458,7 @@ def main():
         "cpu_baseline": cpu,
         "stages": pre["stages"],
         "decode": dec,
+        "kv_bridge": bridge,
     }
     print(json.dumps(out), flush=True)
 

@@ -16,7 +16,8 @@ HYS_SCORE_NONE, HYS_SCORE_BLOCK, HYS_SCORE_TILE_TOKEN = 0, 1, 2
 # every symbol include/hys.h declares
 EXPORTED = (
     "hys_full_attn_fwd", "hys_select_topk", "hys_sparse_attn_fwd", "hys_swa_gate_fwd",
-    "hys_decode_step", "hys_sparse_layer_fwd", "hys_last_error", "hys_status_string", "hys_abi_version",
+    "hys_decode_step", "hys_sparse_layer_fwd", "hys_kv_bridge_fwd", "hys_last_error", "hys_status_string",
+    "hys_abi_version",
 )
 
 
@@ -42,6 +43,10 @@ class HysSparseParams(ctypes.Structure):
 class HysDecodeParams(ctypes.Structure):
     _fields_ = [("softmax_scale", ctypes.c_float), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
                 ("topk", ctypes.c_int32), ("window", ctypes.c_int32)]
+
+
+class HysBridgeParams(ctypes.Structure):
+    _fields_ = [("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -72,8 +77,9 @@ def load(path: str = LIB_PATH):
                                     P(T4), P(T4), vp, P(sz), vp]
     lib.hys_sparse_layer_fwd.argtypes = [P(HysAttnParams), T4, T4, T4, P(HysSparseParams), vp, T4, T4,
                                          ctypes.c_int32, vp, vp, T4, vp]
+    lib.hys_kv_bridge_fwd.argtypes = [P(HysBridgeParams), T4, vp, vp, T4, T4, vp, vp]
     for name in ("hys_full_attn_fwd", "hys_select_topk", "hys_sparse_attn_fwd", "hys_swa_gate_fwd",
-                 "hys_decode_step", "hys_sparse_layer_fwd"):
+                 "hys_decode_step", "hys_sparse_layer_fwd", "hys_kv_bridge_fwd"):
         getattr(lib, name).restype = ctypes.c_int
     lib.hys_last_error.restype = ctypes.c_char_p
     lib.hys_last_error.argtypes = []

@@ -563,4 +563,76 @@ hys_status hys_decode_step(const hys_decode_params* p, hys_tensor4 q_full, hys_t
   }
 }
 
+// ---------------------------------------------------------------------------
+hys_status hys_kv_bridge_fwd(const hys_bridge_params* p, hys_tensor4 h, const void* w_k, const void* w_v,
+                             hys_tensor4 k_cache, hys_tensor4 v_cache, float* amax, void* stream) {
+  try {
+    if (!p) return fail(HYS_ERR_INVALID_ARG, "null params");
+    if (!std::isfinite(p->k_scale) || !(p->k_scale > 0.f) || !std::isfinite(p->v_scale) || !(p->v_scale > 0.f))
+      return fail(HYS_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0");
+    const float inv_k = 1.0f / p->k_scale, inv_v = 1.0f / p->v_scale;
+    if (!std::isfinite(inv_k) || !std::isfinite(inv_v))
+      return fail(HYS_ERR_INVALID_ARG, "k_scale and v_scale must have finite reciprocals");
+    // with no tokens nothing is read or written: null tensor pointers are
+    // accepted (an empty torch tensor has none) and stand in as an aligned
+    // placeholder for the checks below
+    if (h.shape[1] == 0) {
+      void* const placeholder = (void*)(uintptr_t)256;
+      if (!h.ptr) h.ptr = placeholder;
+      if (!k_cache.ptr) k_cache.ptr = placeholder;
+      if (!v_cache.ptr) v_cache.ptr = placeholder;
+    }
+    // h [B, L, 1, d_model] bf16
+    if (!h.ptr) return fail(HYS_ERR_INVALID_ARG, "h: null pointer");
+    if (h.dtype != HYS_BF16) return fail(HYS_ERR_UNSUPPORTED, "h must be bf16");
+    for (int i = 0; i < 4; ++i)
+      if (h.shape[i] < 0 || h.stride[i] < 0) return fail(HYS_ERR_INVALID_ARG, "h: negative shape or stride");
+    if (h.shape[0] < 1 || h.shape[2] != 1) return fail(HYS_ERR_INVALID_ARG, "h must be [B >= 1, L, 1, d_model]");
+    const int64_t B = h.shape[0], L = h.shape[1], dm = h.shape[3];
+    if (dm < 64 || dm > 32768 || dm % 64 != 0)
+      return fail(HYS_ERR_UNSUPPORTED, "d_model %lld not a multiple of 64 in [64, 32768]", (long long)dm);
+    if (h.stride[3] != 1) return fail(HYS_ERR_INVALID_ARG, "h: d_model stride must be 1");
+    if (!aligned16(h.ptr)) return fail(HYS_ERR_INVALID_ARG, "h: pointer not 16-byte aligned");
+    if ((h.stride[0] % 8 != 0 && B > 1) || (h.stride[1] % 8 != 0 && L > 1))
+      return fail(HYS_ERR_INVALID_ARG, "h: token and batch strides must be multiples of 8 elements");
+    if (L >= (1ll << 30)) return fail(HYS_ERR_UNSUPPORTED, "more than 2^30 tokens");
+    if (B * L >= (1ll << 31) - 256) return fail(HYS_ERR_UNSUPPORTED, "B*L too large");
+    // caches [B, L, Hkv, D] fp8, one shape and one set of strides
+    hys_status s;
+    if ((s = check_tensor(k_cache, "k_cache", true)) != HYS_OK) return s;
+    if ((s = check_tensor(v_cache, "v_cache", true)) != HYS_OK) return s;
+    if (k_cache.dtype != HYS_FP8_E4M3 || v_cache.dtype != HYS_FP8_E4M3)
+      return fail(HYS_ERR_UNSUPPORTED, "k_cache and v_cache must be fp8 e4m3");
+    for (int i = 0; i < 4; ++i)
+      if (k_cache.shape[i] != v_cache.shape[i]) return fail(HYS_ERR_INVALID_ARG, "k_cache and v_cache shapes differ");
+    for (int i = 0; i < 4; ++i)
+      if (k_cache.stride[i] != v_cache.stride[i])
+        return fail(HYS_ERR_UNSUPPORTED, "k_cache and v_cache strides must be equal");
+    if (k_cache.shape[0] != B || k_cache.shape[1] != L)
+      return fail(HYS_ERR_INVALID_ARG, "cache [B, L] differs from h");
+    const int64_t Hkv = k_cache.shape[2], D = k_cache.shape[3];
+    if ((Hkv * D) % 128 != 0) return fail(HYS_ERR_UNSUPPORTED, "Hkv*D must be a multiple of 128");
+    if (Hkv * D > 65536) return fail(HYS_ERR_UNSUPPORTED, "Hkv*D above 65536");
+    if (!w_k || !w_v) return fail(HYS_ERR_INVALID_ARG, "null w_k or w_v");
+    if (!aligned16(w_k) || !aligned16(w_v)) return fail(HYS_ERR_INVALID_ARG, "w_k, w_v not 16-byte aligned");
+    if (amax && ((uintptr_t)amax & 3u)) return fail(HYS_ERR_INVALID_ARG, "amax not 4-byte aligned");
+
+    hipStream_t st = (hipStream_t)stream;
+    if (amax) {
+      hipError_t e = hys::launch_fill_i32((int32_t*)amax, 0, 2, st);
+      if (e != hipSuccess) return hip_status(e, "amax clear");
+    }
+    hys::BridgeArgs a{};
+    a.h = h.ptr; a.h_sb = h.stride[0]; a.h_st = h.stride[1];
+    a.w_k = w_k; a.w_v = w_v;
+    a.k_out = k_cache.ptr; a.v_out = v_cache.ptr;
+    a.o_sb = k_cache.stride[0]; a.o_st = k_cache.stride[1]; a.o_sh = k_cache.stride[2];
+    a.amax = amax; a.inv_k = inv_k; a.inv_v = inv_v;
+    a.B = (int)B; a.L = (int)L; a.d_model = (int)dm; a.Hkv = (int)Hkv; a.D = (int)D;
+    return hip_status(hys::launch_kv_bridge(a, st), "kv bridge launch");
+  } catch (...) {
+    return fail(HYS_ERR_INTERNAL, "internal error");
+  }
+}
+
 }  // extern "C"

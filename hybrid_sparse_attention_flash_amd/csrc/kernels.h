@@ -101,4 +101,16 @@ struct MergeArgs {
 hipError_t launch_decode(int sparse, int kt, int D, const DecArgs& a, hipStream_t s);
 hipError_t launch_decode_merge(int D, const MergeArgs& a, hipStream_t s);
 
+// HySparse2 KV Bridging: K/V of a cross-decoder full layer projected from
+// hidden states straight into the fp8 e4m3 cache.
+struct BridgeArgs {
+  const void* h; int64_t h_sb, h_st;                    // [B, L, 1, d_model] bf16
+  const void* w_k; const void* w_v;                     // [Hkv*D, d_model] bf16, contiguous
+  void* k_out; void* v_out; int64_t o_sb, o_st, o_sh;   // [B, L, Hkv, D] fp8 (one set of strides)
+  float* amax;                                          // [2]: max |K|, max |V| (cleared beforehand) or null
+  float inv_k, inv_v;                                   // fp32 1/k_scale, 1/v_scale
+  int B, L, d_model, Hkv, D;
+};
+hipError_t launch_kv_bridge(const BridgeArgs& a, hipStream_t s);
+
 }  // namespace hys

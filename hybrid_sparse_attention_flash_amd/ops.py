@@ -1,4 +1,4 @@
-"""Python binding of the five C-ABI calls (argument marshalling only).
+"""Python binding of the C-ABI calls (argument marshalling only).
 
 PyTorch supplies device memory and the current stream; every computation runs
 in libhys.so.  Workspace, when a call needs one, is queried from the library
@@ -12,7 +12,7 @@ import torch
 
 from . import _lib
 from ._lib import (HYS_BF16, HYS_F32, HYS_FP8_E4M3, HYS_SCORE_BLOCK, HYS_SCORE_NONE, HYS_SCORE_TILE_TOKEN,
-                   HysAttnParams, HysDecodeParams, HysScoreParams, HysSparseParams, HysTensor4, check)
+                   HysAttnParams, HysBridgeParams, HysDecodeParams, HysScoreParams, HysSparseParams, HysTensor4, check)
 
 _DT = {torch.float32: HYS_F32, torch.bfloat16: HYS_BF16, torch.uint8: HYS_FP8_E4M3,
        torch.float8_e4m3fn: HYS_FP8_E4M3}
@@ -129,6 +129,20 @@ def hys_decode_step(q_full, k_cache, v_cache, cache_len: Sequence[int], o_full, 
     nb2 = ctypes.c_size_t(workspace.numel())
     check(lib.hys_decode_step(*args, _ptr(workspace), ctypes.byref(nb2), _stream(q_full.device)))
     return workspace
+
+
+def hys_kv_bridge_fwd(h, w_k, w_v, k_cache, v_cache, k_scale: float, v_scale: float,
+                      amax: Optional[torch.Tensor] = None):
+    """KV Bridging into the fp8 cache.  h: [B, L, d_model] (or [B, L, 1, d_model]) bf16;
+    w_k, w_v: [Hkv*D, d_model] bf16 contiguous; k_cache, v_cache: [B, L, Hkv, D] fp8 (uint8 or
+    float8_e4m3fn); amax: 2 fp32 (max |K|, max |V|) or None."""
+    lib = _lib.load()
+    h4 = h.unsqueeze(2) if h.dim() == 3 else h
+    if not (w_k.is_contiguous() and w_v.is_contiguous()):
+        raise ValueError("w_k and w_v must be contiguous [Hkv*D, d_model]")
+    p = HysBridgeParams(k_scale, v_scale)
+    check(lib.hys_kv_bridge_fwd(ctypes.byref(p), tensor4(h4), _ptr(w_k), _ptr(w_v), tensor4(k_cache),
+                                tensor4(v_cache), _ptr(amax), _stream(h.device)))
 
 
 def abi_version() -> int:

@@ -23,6 +23,11 @@
  *   hys_sparse_layer_fwd - a whole HySparse sparse layer (sparse branch,
  *                          window branch and gate) in one pass
  *
+ * and the step that fills HySparse2's shared cache:
+ *
+ *   hys_kv_bridge_fwd    - KV Bridging: a cross-decoder full layer's K/V
+ *                          projected from hidden states into the fp8 cache
+ *
  * Conventions shared by every call
  * --------------------------------
  * Memory:   every tensor pointer is device memory owned by the caller (for
@@ -265,6 +270,41 @@ HYS_API hys_status hys_decode_step(const hys_decode_params* p, hys_tensor4 q_ful
                            hys_tensor4 v_cache, const int64_t* cache_len, hys_tensor4 o_full, float* token_scores,
                            int32_t* idx, int32_t n_sparse, const hys_tensor4* q_sparse,
                            const hys_tensor4* o_sparse, void* ws, size_t* ws_bytes, void* stream);
+
+typedef struct {
+  float k_scale;  /* K cache quantisation scale: the stored code is e4m3(K / k_scale) */
+  float v_scale;  /* V cache quantisation scale */
+} hys_bridge_params;
+
+/*
+ * hys_kv_bridge_fwd - HySparse2's KV Bridging projection (airebao HySparse2
+ * news, outer KV Bridging paragraph; demingchina commentary, section 02).
+ *
+ * The cross-decoder's full-attention layers take their K and V from the
+ * hidden states of the self-decoder's full-attention layer, so the shared
+ * MQA cache is written once, in FP8 (airebao key-data table):
+ *   K[b,t,:] = h[b,t,:] W_k^T,  V[b,t,:] = h[b,t,:] W_v^T   (no bias),
+ *   k_cache[b,t,g,d] = e4m3(K[b,t,g*D+d] / k_scale),  v_cache likewise,
+ * with e4m3 the OCP e4m3fn code of the value rounded to nearest (ties to
+ * even) and saturated at +-448; K and V are accumulated in fp32 from bf16
+ * products and multiplied by the fp32 reciprocal of the scale.  Infinite
+ * projections saturate; the codes of NaN projections are unspecified.
+ * amax, when not NULL, receives max |K| and max |V| over the fp32
+ * projections (0 when B*L = 0), so that a caller can set the next scales
+ * (scale = amax / 448); it is overwritten, not accumulated.
+ *
+ * h: [B, L, 1, d_model] bf16, d_model a multiple of 64 in [64, 32768],
+ *    token and batch strides multiples of 8 elements.
+ * w_k, w_v: [Hkv*D, d_model] bf16, contiguous ([out, in] layout), 16-byte
+ *    aligned device memory.
+ * k_cache, v_cache: [B, L, Hkv, D] fp8 e4m3fn with identical shapes and
+ *    strides, D in {64, 128} and Hkv*D a multiple of 128.  Pass a view to
+ *    write positions [t0, t0+L) of a longer cache.
+ * With L = 0 only amax is written, and the h and cache pointers may be NULL.
+ * No workspace.
+ */
+HYS_API hys_status hys_kv_bridge_fwd(const hys_bridge_params* p, hys_tensor4 h, const void* w_k, const void* w_v,
+                                     hys_tensor4 k_cache, hys_tensor4 v_cache, float* amax, void* stream);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 HYS_API const char* hys_last_error(void);

@@ -218,3 +218,31 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.uint8:
         raise TypeError("fp8 bytes must be decoded by the consumer")
     return t.to(torch.float64).numpy()
+
+
+# ----------------------------------------------------------------------------
+# KV Bridging inputs (HySparse2): the self-decoder full layer's hidden states
+# and the cross-decoder full layer's K/V projection weights
+# ----------------------------------------------------------------------------
+
+# The pages name no model width; 4096 is the hidden size taken for the 64k
+# HySparse2 workload (one MQA KV head of dimension 128, as in hysparse2_64k).
+BRIDGE_WORKLOAD = {"name": "kv_bridge_64k", "cfg_id": 6, "B": 1, "L": 65536, "d_model": 4096, "Hkv": 1, "D": 128}
+
+
+def gen_bridge(seed: int, cfg_id: int, B: int, L: int, d_model: int, n_out: int,
+               outlier_frac: float = 0.01, outlier_scale: float = 8.0):
+    """Hidden states h [B, L, d_model] and weights w_k, w_v [n_out, d_model], bf16 CPU tensors.
+
+    h ~ N(0, 1) with a fixed 1% of channels scaled by 8 (the few large
+    channels of normalised transformer activations); weights ~ N(0, 1/d_model)
+    so the projections have unit-order spread.
+    """
+    h = normal(seed, cfg_id, "bridge_h", (B, L, d_model))
+    n_out_ch = max(1, int(round(d_model * outlier_frac)))
+    cols = np.sort(rng_for(seed, cfg_id, "bridge_outliers").choice(d_model, size=n_out_ch, replace=False))
+    h[..., cols] *= np.float32(outlier_scale)
+    std = float(1.0 / np.sqrt(d_model))
+    wk = normal(seed, cfg_id, "bridge_wk", (n_out, d_model), std=std)
+    wv = normal(seed, cfg_id, "bridge_wv", (n_out, d_model), std=std)
+    return to_bf16(h), to_bf16(wk), to_bf16(wv)

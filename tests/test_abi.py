@@ -144,3 +144,44 @@ def test_decode_validation():
     assert call(ln=bad) == INVALID
     assert call(pp=HysDecodeParams(0.088, 0.01, 0.01, 4096, 128)) == UNSUPPORTED
     assert call(n_sparse=3) == INVALID                                        # null q_sparse
+
+
+def test_kv_bridge_validation():
+    from hybrid_sparse_attention_flash_amd._lib import HysBridgeParams
+    p = HysBridgeParams(0.02, 0.02)
+    h = t4([1, 300, 1, 4096])
+    kc = t4([1, 300, 1, 128], dtype=2)
+
+    def call(pp=p, h=h, k=kc, v=kc, wk=FAKE, wv=FAKE, amax=None):
+        return lib().hys_kv_bridge_fwd(ctypes.byref(pp) if pp is not None else None, h, ctypes.c_void_p(wk),
+                                       ctypes.c_void_p(wv), k, v, amax, None)
+    assert call(pp=None) == INVALID
+    assert call(pp=HysBridgeParams(0.0, 0.02)) == INVALID                     # scale 0
+    assert call(pp=HysBridgeParams(float("nan"), 0.02)) == INVALID
+    assert call(pp=HysBridgeParams(1e-45, 0.02)) == INVALID                   # reciprocal overflows
+    assert call(h=t4([1, 300, 1, 4096], dtype=0)) == UNSUPPORTED               # fp32 hidden states
+    assert call(h=t4([1, 300, 2, 4096])) == INVALID                           # H != 1
+    assert call(h=t4([1, 300, 1, 4000])) == UNSUPPORTED                        # d_model % 64
+    assert call(h=t4([1, 300, 1, 4096], strides=[300 * 4100, 4100, 4096, 1])) == INVALID   # token stride % 8
+    assert call(k=t4([1, 300, 1, 128], dtype=1), v=t4([1, 300, 1, 128], dtype=1)) == UNSUPPORTED  # bf16 cache
+    assert call(k=t4([1, 301, 1, 128], dtype=2), v=t4([1, 301, 1, 128], dtype=2)) == INVALID     # L differs
+    assert call(v=t4([1, 300, 2, 128], dtype=2)) == INVALID                   # K/V shapes differ
+    assert call(v=t4([1, 300, 1, 128], dtype=2, strides=[300 * 256, 256, 128, 1])) == UNSUPPORTED  # strides differ
+    assert call(k=t4([1, 300, 1, 64], dtype=2), v=t4([1, 300, 1, 64], dtype=2)) == UNSUPPORTED   # Hkv*D = 64
+    assert call(wk=0) == INVALID
+    assert call(wv=FAKE + 8) == INVALID                                       # misaligned weights
+    assert call(amax=ctypes.c_void_p(FAKE + 2)) == INVALID                    # misaligned amax
+    assert b"amax" in lib().hys_last_error()
+
+
+def test_kv_bridge_empty_accepts_null_tensors():
+    """L = 0 with null tensor pointers and no amax passes validation and launches nothing."""
+    from hybrid_sparse_attention_flash_amd._lib import HysBridgeParams
+    p = HysBridgeParams(0.02, 0.02)
+    h = t4([2, 0, 1, 128], ptr=0)
+    kc = t4([2, 0, 1, 128], dtype=2, ptr=0)
+    assert lib().hys_kv_bridge_fwd(ctypes.byref(p), h, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), kc, kc,
+                                   None, None) == 0
+    h1 = t4([2, 1, 1, 128], ptr=0)
+    assert lib().hys_kv_bridge_fwd(ctypes.byref(p), h1, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), kc, kc,
+                                   None, None) == INVALID

@@ -1,0 +1,151 @@
+"""GPU parity of hys_kv_bridge_fwd (KV Bridging into the fp8 cache) against the oracle.
+
+Comparison rule.  The kernel accumulates K = h W_k^T in fp32 on MFMA, so its
+value differs from the exact (float64) projection by at most the accumulation
+error; the tests take that as bound(x) = 2^-18 * sum_c |h_c w_c| (64 fp32
+ulps of the absolute sum, several times the random-walk error of 4096
+fp32 additions).  Each GPU code must decode to a value between the codes the
+oracle gives for exact - bound and exact + bound (the encoding is monotonic),
+which forces bit equality wherever the exact value is not within the bound of
+an fp8 rounding midpoint.  amax must lie within the bound of the exact
+maximum.  Bytes of the cache outside the written region must be untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from hybrid_sparse_attention_flash_amd import ops
+from oracle.bridge import kv_bridge, quantize_kernel_precision
+from oracle.fp8 import decode_table
+
+pytestmark = pytest.mark.gpu
+
+TAB = decode_table()
+BOUND_REL = 2.0 ** -18
+
+
+def _inputs(B, L, d_model, n_out, seed=0, cfg_id=6):
+    return synth.gen_bridge(seed, cfg_id, B, L, d_model, n_out)
+
+
+def _oracle(h, wk, wv, ks, vs):
+    h64 = h.to(torch.float64).numpy()
+    wk64, wv64 = wk.to(torch.float64).numpy(), wv.to(torch.float64).numpy()
+    kc, vc, kx, vx, ak, av = kv_bridge(h64, wk64, wv64, ks, vs)
+    ah = np.abs(h64)
+    kb = BOUND_REL * (ah @ np.abs(wk64).T)
+    vb = BOUND_REL * (ah @ np.abs(wv64).T)
+    return kc, vc, kx, vx, ak, av, kb, vb
+
+
+def _check_codes(gpu, ref, exact, bound, scale, what):
+    gpu = np.asarray(gpu).reshape(ref.shape)
+    lo = TAB[quantize_kernel_precision(exact - bound, scale)]
+    hi = TAB[quantize_kernel_precision(exact + bound, scale)]
+    gv = TAB[gpu]
+    assert not np.isnan(gv).any(), f"{what}: NaN code written"
+    bad = (gv < lo) | (gv > hi)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} codes outside the accumulation bound, first at "
+                           f"{np.argwhere(bad)[:3].tolist()}: gpu {gpu[bad][:3].tolist()} oracle {ref[bad][:3].tolist()}")
+    return int((gpu != ref).sum())
+
+
+def _run(h, wk, wv, Hkv, D, ks, vs, k_cache=None, v_cache=None, with_amax=True):
+    B, L, _ = h.shape
+    hd, wkd, wvd = h.cuda(), wk.cuda(), wv.cuda()
+    if k_cache is None:
+        k_cache = torch.full((B, L, Hkv, D), 0x55, dtype=torch.uint8, device="cuda")
+        v_cache = torch.full((B, L, Hkv, D), 0x55, dtype=torch.uint8, device="cuda")
+    amax = torch.full((2,), -7.0, dtype=torch.float32, device="cuda") if with_amax else None
+    ops.hys_kv_bridge_fwd(hd, wkd, wvd, k_cache, v_cache, ks, vs, amax)
+    torch.cuda.synchronize()
+    return k_cache, v_cache, amax
+
+
+CASES = [
+    # B, L, d_model, Hkv, D
+    (1, 300, 128, 1, 128),      # two chunks, ragged token tail
+    (2, 77, 256, 2, 64),        # token tile spans both sequences
+    (1, 513, 64, 2, 128),       # one chunk, two output tiles, tail of 1
+    (3, 1, 192, 1, 128),        # odd chunk count, one token per sequence
+    (1, 256, 4096, 1, 128),     # the workload's width, exactly one token tile
+    (2, 1000, 512, 4, 64),      # two output tiles of four 64-wide heads
+]
+
+
+@pytest.mark.parametrize("B,L,d_model,Hkv,D", CASES)
+def test_kv_bridge_parity(B, L, d_model, Hkv, D):
+    n = Hkv * D
+    h, wk, wv = _inputs(B, L, d_model, n, seed=B * 1000 + L)
+    # scales from the exact maxima (amax / 448), so the codes span the format
+    _, _, _, _, ak, av = kv_bridge(h.to(torch.float64).numpy(), wk.to(torch.float64).numpy(),
+                                   wv.to(torch.float64).numpy(), 1.0, 1.0)
+    ks, vs = float(np.float32(ak / 448.0)), float(np.float32(av / 448.0))
+    kc, vc, kx, vx, ak, av, kb, vb = _oracle(h, wk, wv, ks, vs)
+    k_cache, v_cache, amax = _run(h, wk, wv, Hkv, D, ks, vs)
+    g_k = k_cache.cpu().numpy().reshape(B, L, n)
+    g_v = v_cache.cpu().numpy().reshape(B, L, n)
+    mk = _check_codes(g_k, kc, kx, kb, ks, "K")
+    mv = _check_codes(g_v, vc, vx, vb, vs, "V")
+    # a handful of midpoint neighbours at most
+    assert mk + mv <= max(4, (kc.size + vc.size) // 200), (mk, mv)
+    am = amax.cpu().numpy()
+    assert abs(am[0] - ak) <= kb.max() and abs(am[1] - av) <= vb.max(), (am.tolist(), ak, av)
+
+
+def test_kv_bridge_saturation_and_strided_views():
+    """Tiny K scale (most K codes saturate at +-448), h read through a token
+    stride wider than d_model, and the caches written through a view into the
+    middle of a longer cache whose other bytes must stay untouched."""
+    B, L, d_model, Hkv, D, Nmax, t0 = 2, 200, 128, 1, 128, 512, 100
+    h, wk, wv = _inputs(B, L, d_model, Hkv * D, seed=7)
+    wide = torch.zeros(B, L, d_model + 64, dtype=torch.bfloat16)
+    wide[:, :, 32:32 + d_model] = h
+    _, _, _, _, ak, av = kv_bridge(h.to(torch.float64).numpy(), wk.to(torch.float64).numpy(),
+                                   wv.to(torch.float64).numpy(), 1.0, 1.0)
+    ks, vs = float(np.float32(ak / 448.0 / 20.0)), float(np.float32(av / 448.0))
+    kc, vc, kx, vx, ak, av, kb, vb = _oracle(h, wk, wv, ks, vs)
+    kfull = torch.full((B, Nmax, Hkv, D), 0x33, dtype=torch.uint8, device="cuda")
+    vfull = torch.full((B, Nmax, Hkv, D), 0x33, dtype=torch.uint8, device="cuda")
+    hd = wide.cuda()[:, :, 32:32 + d_model]
+    assert hd.stride(1) == d_model + 64
+    amax = torch.zeros(2, dtype=torch.float32, device="cuda")
+    ops.hys_kv_bridge_fwd(hd, wk.cuda(), wv.cuda(), kfull[:, t0:t0 + L], vfull[:, t0:t0 + L], ks, vs, amax)
+    torch.cuda.synchronize()
+    kf, vf = kfull.cpu().numpy(), vfull.cpu().numpy()
+    _check_codes(kf[:, t0:t0 + L].reshape(B, L, -1), kc, kx, kb, ks, "K")
+    _check_codes(vf[:, t0:t0 + L].reshape(B, L, -1), vc, vx, vb, vs, "V")
+    sat = np.isin(kf[:, t0:t0 + L], [0x7E, 0xFE]).mean()
+    assert sat > 0.5, sat
+    for arr in (kf, vf):
+        assert (arr[:, :t0] == 0x33).all() and (arr[:, t0 + L:] == 0x33).all()
+
+
+def test_kv_bridge_empty_and_no_amax():
+    h = torch.zeros(2, 0, 128, dtype=torch.bfloat16)
+    wk = torch.zeros(128, 128, dtype=torch.bfloat16)
+    _, _, amax = _run(h, wk, wk, 1, 128, 1.0, 1.0)
+    assert amax.cpu().tolist() == [0.0, 0.0]
+    # amax omitted: codes still written
+    h, wk, wv = _inputs(1, 70, 64, 128, seed=3)
+    kc, vc, kx, vx, _, _, kb, vb = _oracle(h, wk, wv, 0.02, 0.02)
+    k_cache, v_cache, _ = _run(h, wk, wv, 1, 128, 0.02, 0.02, with_amax=False)
+    _check_codes(k_cache.cpu().numpy().reshape(1, 70, 128), kc, kx, kb, 0.02, "K")
+    _check_codes(v_cache.cpu().numpy().reshape(1, 70, 128), vc, vx, vb, 0.02, "V")
+
+
+def test_kv_bridge_full_size():
+    """The 64k-token workload at its full size (L = 65536, d_model = 4096, one
+    128-wide MQA head), every output checked."""
+    w = synth.BRIDGE_WORKLOAD
+    B, L, dm, Hkv, D = w["B"], w["L"], w["d_model"], w["Hkv"], w["D"]
+    h, wk, wv = synth.gen_bridge(0, w["cfg_id"], B, L, dm, Hkv * D)
+    ks = vs = 8.0 / 448.0
+    kc, vc, kx, vx, ak, av, kb, vb = _oracle(h, wk, wv, ks, vs)
+    k_cache, v_cache, amax = _run(h, wk, wv, Hkv, D, ks, vs)
+    mk = _check_codes(k_cache.cpu().numpy().reshape(B, L, -1), kc, kx, kb, ks, "K")
+    mv = _check_codes(v_cache.cpu().numpy().reshape(B, L, -1), vc, vx, vb, vs, "V")
+    assert mk + mv <= (kc.size + vc.size) // 200, (mk, mv)
+    am = amax.cpu().numpy()
+    assert abs(am[0] - ak) <= kb.max() and abs(am[1] - av) <= vb.max(), (am.tolist(), ak, av)
