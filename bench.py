@@ -42,7 +42,11 @@ METRIC = ("hybrid-block prefill tokens/s at 32k (TFLOP/s, GB/s % peak); decode u
 # profiles directory holds both summaries).  It is reported only while the
 # kernel sources still hash to the value they had when the counters were taken.
 TRAFFIC_SOURCES = ("attn_engine.h", "common.h", "kernels.h", "attn_sparse_swa.hip")
-TRAFFIC = {"sources_sha1": "02cef080f5049c21a8e86345a27a3dee9737f00a", "bytes_per_launch": 2.088e9}
+TRAFFIC = {"sources_sha1": "0d6d5480d7db2273bf15c61e33eeb87d96474d85", "bytes_per_launch": 2.087e9}
+# The same two passes for the KV Bridging kernel, over
+#   python3 bench.py --only-bridge --calibrate-copy --steps 1 --warmup 0
+BRIDGE_TRAFFIC_SOURCES = ("bridge.hip", "common.h", "kernels.h")
+BRIDGE_TRAFFIC = {"sources_sha1": "5bf079ce8145b3307ebe1570a0401330f6c85d38", "bytes_per_launch": 575.9e6}
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
@@ -154,10 +158,10 @@ def cpu_baseline(w, host, nrows, seed=0):
 
 # ---------------------------------------------------------------------------
 
-def kernel_sources_sha1():
+def kernel_sources_sha1(files=TRAFFIC_SOURCES):
     import hashlib
     h = hashlib.sha1()
-    for f in TRAFFIC_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "hybrid_sparse_attention_flash_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -381,26 +385,33 @@ def bench_bridge(args, dev):
         ops.hys_kv_bridge_fwd(h, wk, wv, kc, vc, ks, vs, amax)
     torch.cuda.synchronize()
     calls = max(20, args.steps * 5)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(calls):
-        ops.hys_kv_bridge_fwd(h, wk, wv, kc, vc, ks, vs, amax)
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1000 / calls
+
+    def timed(am):
+        # HIP events on the launch stream (the current stream, which ops uses)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(calls):
+            ops.hys_kv_bridge_fwd(h, wk, wv, kc, vc, ks, vs, am)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000 / calls
+    us_call = timed(amax)      # the call: amax clear + projection kernel
+    us = timed(None)           # the projection kernel alone (no amax, no clear)
     nbytes = B * L * dm * 2 + 2 * n * dm * 2 + 2 * B * L * n      # h, W_k + W_v, fp8 K + V
     flops = 2.0 * B * L * dm * 2 * n
     gbs = nbytes / (us * 1e-6) / 1e9
     tf = flops / (us * 1e-6) / 1e12
-    log(f"[bench] kv bridge: {us:.1f} us/call, {gbs:.0f} GB/s, {tf:.0f} TFLOP/s")
-    return {"workload": w["name"], "us_per_call": round(us, 2), "tokens_per_s": round(B * L / (us * 1e-6), 1),
-            "calls": calls,
+    log(f"[bench] kv bridge: {us_call:.1f} us/call, kernel {us:.1f} us, {gbs:.0f} GB/s, {tf:.0f} TFLOP/s")
+    traffic = (BRIDGE_TRAFFIC["bytes_per_launch"]
+               if BRIDGE_TRAFFIC["sources_sha1"] == kernel_sources_sha1(BRIDGE_TRAFFIC_SOURCES) else None)
+    return {"workload": w["name"], "us_per_call": round(us_call, 2),
+            "tokens_per_s": round(B * L / (us_call * 1e-6), 1), "calls": calls,
             "roofline": {"kernel": "kv_bridge (bf16 projection, fp8 e4m3 epilogue)", "bound": "hbm",
                          "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "avg_launch_us": round(us, 2),
                          "work_per_launch": f"{nbytes:.4g} B (h, both weights, fp8 K and V)",
                          "mfma_tflops": round(tf, 1), "frac_mfma_bf16": round(tf / PEAK_BF16_TFLOPS, 4),
-                         "traffic": None}}
+                         "traffic": traffic}}
 
 
 def main():

@@ -9,6 +9,8 @@ oracle gives for exact - bound and exact + bound (the encoding is monotonic),
 which forces bit equality wherever the exact value is not within the bound of
 an fp8 rounding midpoint.  amax must lie within the bound of the exact
 maximum.  Bytes of the cache outside the written region must be untouched.
+Widths that are and are not multiples of three 64-column chunks exercise the
+zero-padded tail of the chunk loop.
 """
 import numpy as np
 import pytest
@@ -71,6 +73,8 @@ CASES = [
     (3, 1, 192, 1, 128),        # odd chunk count, one token per sequence
     (1, 256, 4096, 1, 128),     # the workload's width, exactly one token tile
     (2, 1000, 512, 4, 64),      # two output tiles of four 64-wide heads
+    (2, 700, 768, 2, 128),      # three 512-token tiles across the batch seam, two output tiles
+    (1, 33, 1280, 1, 128),      # one partial token block, five 256-column super-chunks
 ]
 
 
@@ -94,11 +98,13 @@ def test_kv_bridge_parity(B, L, d_model, Hkv, D):
     assert abs(am[0] - ak) <= kb.max() and abs(am[1] - av) <= vb.max(), (am.tolist(), ak, av)
 
 
-def test_kv_bridge_saturation_and_strided_views():
+@pytest.mark.parametrize("d_model", [192, 256])
+def test_kv_bridge_saturation_and_strided_views(d_model):
     """Tiny K scale (most K codes saturate at +-448), h read through a token
     stride wider than d_model, and the caches written through a view into the
-    middle of a longer cache whose other bytes must stay untouched."""
-    B, L, d_model, Hkv, D, Nmax, t0 = 2, 200, 128, 1, 128, 512, 100
+    middle of a longer cache whose other bytes must stay untouched (192 is a
+    whole group of three 64-column chunks, 256 is not)."""
+    B, L, Hkv, D, Nmax, t0 = 2, 200, 1, 128, 512, 100
     h, wk, wv = _inputs(B, L, d_model, Hkv * D, seed=7)
     wide = torch.zeros(B, L, d_model + 64, dtype=torch.bfloat16)
     wide[:, :, 32:32 + d_model] = h
