@@ -523,6 +523,13 @@ hys_status hys_decode_step(const hys_decode_params* p, hys_tensor4 q_full, hys_t
     d.v = v_cache.ptr; d.v_sb = v_cache.stride[0]; d.v_st = v_cache.stride[1];
     for (int64_t b = 0; b < B; ++b) d.lens[b] = (int)cache_len[b];
     d.B = (int)B; d.Hq = (int)Hq; d.Nmax = (int)Nmax;
+    {
+      int dev = 0, ncu = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+        return fail(HYS_ERR_HIP, "device query failed");
+      d.ncu = ncu;
+    }
     d.scale_log2 = logit_scale * 1.4426950408889634f; d.logit_scale = logit_scale;
     // 1. full layer, split over the cache
     d.q[0] = q_full.ptr; d.q_sb = q_full.stride[0]; d.q_sh = q_full.stride[2];

@@ -6,14 +6,16 @@
 // cache, so memory bandwidth dominates (QbitAI HySparse article, background
 // section).  The full layer therefore streams the cache once:
 //
-//   decode_kernel<full>   - split-K: every wave streams its own 64-key tiles
-//                           through a private LDS slice (K as MFMA A fragments,
-//                           V transposed), computes S^T = K q^T for all query
-//                           heads at once (heads are the MFMA N dimension), and
-//                           keeps an online-softmax partial.  The per-key max
-//                           over heads is the token score, written directly.
-//                           The 4 waves of a workgroup merge their partials in
-//                           LDS, so one (m, l, O) partial per workgroup leaves.
+//   decode_kernel<full>   - split-K: each workgroup takes a contiguous share
+//                           of the 64-key tiles.  Two staging waves load fp8
+//                           tiles several ahead and write them, as bf16 (K
+//                           row-major, V transposed), into a two-stage LDS
+//                           ring; two compute waves (32 query heads each, the
+//                           MFMA N dimension) take S^T = K q^T and O^T = V^T
+//                           P^T from it with an online softmax.  The per-key
+//                           max over heads is the token score, written
+//                           directly; each compute wave leaves one (m, l, O)
+//                           partial per head.
 //   decode_merge_kernel   - combines the partials in a fixed order (exact LSE
 //                           rule, deterministic).
 //   decode_kernel<sparse> - all sparse layers in one launch: each workgroup
@@ -27,9 +29,9 @@ namespace hys {
 
 template <int SPARSE, typename KT, int D>
 __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
-  // Workgroup = 4 waves.  Waves 0 and 1 compute: wave w owns query heads
+  // Workgroup = 4 waves.  Two compute: role w owns query heads
   // [32w, 32w+32) (one MFMA N-block) and both consume the same staged 64-key
-  // tile, so every cache byte is read once per workgroup.  Waves 2 and 3
+  // tile, so every cache byte is read once per workgroup.  The other two
   // stage: they keep the loads of the next NSET tiles in flight in their own
   // registers and write each tile, converted to bf16 (K row-major, V
   // transposed), into a two-stage LDS ring one tile ahead of the compute
@@ -51,10 +53,25 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
   __shared__ int s_tlist[SPARSE ? TLMAX : 1];
   __shared__ int s_misc[4];
 
+  __shared__ int s_simd[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, ln = lane & 31;
-  const bool stager = wave >= 2;
-  const int st = tid - 128;                   // staging thread index (stager waves)
   const int bid = blockIdx.x;
+  // Roles follow the SIMD a wave runs on.  The four waves of a workgroup sit
+  // on four distinct SIMDs, and the two workgroups that share a CU are
+  // dispatched in separate passes over the CUs; taking the compute waves on
+  // SIMDs {0, 2} in one pass and {1, 3} in the other puts one compute wave on
+  // every SIMD (fixed wave roles stacked both workgroups' compute waves on
+  // one SIMD in every CU).  Any other placement keeps the fixed roles.
+  // vw: role index, 0 and 1 compute (heads [32 vw, +32)), 2 and 3 stage.
+  if (lane == 0) s_simd[wave] = (__builtin_amdgcn_s_getreg((31 << 11) | 4) >> 4) & 3;   // HW_REG_HW_ID.SIMD_ID
+  __syncthreads();
+  int vw = wave;
+  if (((1 << s_simd[0]) | (1 << s_simd[1]) | (1 << s_simd[2]) | (1 << s_simd[3])) == 15) {
+    const int my = s_simd[wave], par = (bid / a.ncu) & 1;
+    vw = (((my + par) & 1) == 0 ? 0 : 2) + (my >> 1);
+  }
+  const bool stager = vw >= 2;
+  const int st = (vw - 2) * 64 + lane;        // staging thread index (stager waves)
   const int s = bid % a.nsplit;
   const int rest = bid / a.nsplit;
   const int b = rest % a.B;
@@ -97,7 +114,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
     return p < nkeys ? wstart + (p - npre) : -1;
   };
 
-  // ---- staging (waves 2, 3) ----------------------------------------------------
+  // ---- staging (roles 2, 3) ----------------------------------------------------
   // staging thread x, K unit u: key u*(NST/(D/8)) + x/(D/8), 8 elements from
   // x%(D/8)*8; V unit u: keys 4(x%16) .. 4(x%16)+3, 8 elements from
   // (u*NST/16 + x/16)*8
@@ -188,7 +205,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
 
   // ---- query fragments (compute waves: this wave's 32 heads) -------------------
   const uint16_t* qb = (const uint16_t*)a.q[layer] + (int64_t)b * a.q_sb;
-  const int head = wave * 32 + ln;
+  const int head = vw * 32 + ln;
   const bool hvalid = !stager && head < a.Hq;
   bf16x8 qf[NQC];
 #pragma unroll
@@ -207,9 +224,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
 
   // token scores of tile t: max over the two compute waves' per-key maxima
   auto emit_scores = [&](int t) {
-    if (!SPARSE && tid < 64) {
-      const int j = t * 64 + tid;
-      const float v = fmaxf(red[t & 1][0][tid], red[t & 1][1][tid]);
+    if (!SPARSE && vw == 0) {
+      const int j = t * 64 + lane;
+      const float v = fmaxf(red[t & 1][0][lane], red[t & 1][1][lane]);
       if (j < a.Nmax) a.scores[(int64_t)b * a.sc_sb + j] = (j < n) ? v * a.logit_scale : kNegInf;
     }
   };
@@ -273,7 +290,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
         for (int i = 0; i < 16; ++i) cm[mb * 16 + i] = sacc[mb][i];
       const f32x4 m4 = colmax32(cm);
       const int off = (ln >> 4) * 32 + 8 * ((ln >> 2) & 3) + 4 * hh;
-      if ((ln & 3) == 0) *(f32x4*)&red[t & 1][wave][off] = m4;
+      if ((ln & 3) == 0) *(f32x4*)&red[t & 1][vw][off] = m4;
     }
     // online softmax (base 2) with a lazily moved reference maximum: a
     // head's reference moves only when the tile max exceeds it by more than
@@ -333,7 +350,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
     }
   };
 
-  // ---- tile pipeline: iteration i stages tile t0 + i (wave 2) while the
+  // ---- tile pipeline: iteration i stages tile t0 + i (staging waves) while the
   // compute waves take tile t0 + i - 1; the stager's loads run NSET tiles
   // ahead.  The two roles run separate loops with the same barrier count, so
   // neither keeps the other's registers live.

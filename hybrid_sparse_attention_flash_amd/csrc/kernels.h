@@ -84,6 +84,7 @@ struct DecArgs {
   const void* v; int64_t v_sb, v_st;
   int lens[kMaxDecodeBatch];                             // valid cache length per sequence
   int B, Hq, Nmax, nsplit, nlayer;
+  int ncu;                                               // compute units of the device
   float scale_log2, logit_scale;
   float* scores; int64_t sc_sb;                          // full mode: [B, Nmax] token scores
   const int32_t* idx; int64_t idx_sb; int topk; int window;   // sparse mode: [B, topk]
