@@ -15,16 +15,18 @@ It shares no code with the HIP path; both consume the seeded bytes of the
 Pins (tests/test_oracle*.py, run with -m "not gpu"): brute force in pure
 Python loops, torch's CPU float64 scaled_dot_product_attention, closed forms,
 invariants, hand-derived golden values under tests/golden/, the fp8
-decode table against torch.float8_e4m3fn, and the fp8 encoder of the KV
-Bridging projection (bridge.py) against torch's CPU float8 conversion.
+decode table against torch.float8_e4m3fn, the fp8 encoder of the KV
+Bridging projection (bridge.py) against torch's CPU float8 conversion, and
+the HySparse decode step with ring window caches (hysparse_decode.py)
+against the prefill block evaluated at its last row.
 
 Parity unpinned (against the real HySparse/HySparse2, whose pages leave these
 open): the head reduction of importance scores (max over all query heads),
 the gate's form (one sigmoid scalar per token and head, no bias), the empty
-sparse set rule, the per-tile token-score reading and the per-query forced
-window.  They are pinned only to this package's stated readings.
+sparse set rule, the per-tile token-score reading, the per-query forced
+window and the decode-time ring window cache.  They are pinned only to this package's stated readings.
 """
-from . import bridge, fp8  # noqa: F401
+from . import bridge, fp8, hysparse_decode  # noqa: F401
 from .hysparse import (  # noqa: F401
     NEG_INF, attend, block_scores, decode_full, decode_sparse, decode_step,
     full_attention, gate_merge, hysparse2_block, hysparse_block, logits,
