@@ -12,7 +12,9 @@ on the launch stream, the roofline of the dominant kernel, and the CPU oracle
 timed on a bounded sample of the same workload.
 
 The HySparse2 KV Bridging projection (64k tokens, d_model 4096, fp8 MQA
-cache) is timed beside them with its own roofline.
+cache) and the HySparse block-level decode step (B=4, 128k-token bf16 GQA
+cache, top-16 blocks, 11 sparse layers with ring window caches) are timed
+beside them with their own rooflines.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-bridge]
 """
@@ -367,6 +369,53 @@ def bench_decode(args, dev):
             "frac_hbm_step_equiv": round(gbs / PEAK_HBM_GBS, 4), "steps": steps}
 
 
+def bench_hs_decode(args, dev):
+    """HySparse (block-level) decode step: full layer + block scores over a
+    128k-token bf16 GQA cache per sequence, top-16 blocks, 11 sparse layers
+    (block gather, ring window append, gate)."""
+    w = synth.HS_DECODE_WORKLOAD
+    log(f"[bench] generating {w.name} inputs (B={w.B}, N={w.L}, bf16 cache, {w.n_sparse} sparse layers)")
+    x = synth.gen_hs_decode(w)
+    q_full, k, v = x["q_full"].to(dev), x["k"].to(dev), x["v"].to(dev)
+    qs = [t.to(dev) for t in x["q"]]
+    kn, vn = [t.to(dev) for t in x["k_new"]], [t.to(dev) for t in x["v_new"]]
+    kr, vr = [t.to(dev) for t in x["k_ring"]], [t.to(dev) for t in x["v_ring"]]
+    gw = [t.to(dev) for t in x["gate_w"]]
+    nblk = (w.L + 63) // 64
+    o_full = torch.empty(w.B, 1, w.Hq, w.D, dtype=torch.bfloat16, device=dev)
+    bs = torch.empty(w.B, nblk, dtype=torch.float32, device=dev)
+    idx = torch.empty(w.B, w.topk, dtype=torch.int32, device=dev)
+    o_sp = [torch.empty_like(o_full) for _ in qs]
+    lens = w.lens()
+    ws = None
+
+    def step():
+        nonlocal ws
+        ws = ops.hys_hysparse_decode_step(q_full, k, v, lens, o_full, bs, idx, qs, kn, vn, kr, vr, gw, o_sp,
+                                          w.topk, workspace=ws)
+    for _ in range(max(3, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    steps = max(20, args.steps * 5)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000 / steps
+    kv_bytes = 2.0 * sum(lens) * w.Hkv * w.D * 2           # bf16 K + V streamed by the full layer
+    gathered = 2.0 * w.n_sparse * w.B * w.Hkv * (w.topk * 64 + w.window) * w.D * 2
+    gbs = (kv_bytes + gathered) / (us * 1e-6) / 1e9
+    log(f"[bench] HySparse decode: {us:.1f} us/step, {gbs:.0f} GB/s algorithmic")
+    return {"workload": w.name, "us_per_step": round(us, 2), "us_per_token": round(us / w.B, 2), "batch": w.B,
+            "cache_tokens": w.L, "steps": steps,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "work_per_step": f"{kv_bytes + gathered:.4g} B (full-layer K+V, gathered blocks + windows)",
+                         "traffic": None}}
+
+
 def bench_bridge(args, dev):
     """HySparse2 KV Bridging: the cross-decoder full layer's K/V projected from
     the self-decoder's hidden states into the fp8 MQA cache, one call per
@@ -422,6 +471,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-bridge", action="store_true")
+    ap.add_argument("--no-hs-decode", action="store_true")
+    ap.add_argument("--only-hs-decode", action="store_true", help="time only the HySparse decode step")
     ap.add_argument("--only-bridge", action="store_true", help="time only the KV Bridging projection")
     ap.add_argument("--cpu-rows", type=int, default=64)
     ap.add_argument("--workload", default="moe80b_32k",
@@ -444,10 +495,14 @@ def main():
     if args.only_bridge:
         print(json.dumps({"kv_bridge": bench_bridge(args, dev)}), flush=True)
         return
+    if args.only_hs_decode:
+        print(json.dumps({"hs_decode": bench_hs_decode(args, dev)}), flush=True)
+        return
     pre = bench_prefill(args, dev)
     w = pre["w"]
     dec = None if args.no_decode else bench_decode(args, dev)
     bridge = None if args.no_bridge else bench_bridge(args, dev)
+    hs_dec = None if args.no_hs_decode else bench_hs_decode(args, dev)
     cpu = None
     if not args.no_cpu and pre["host"] is not None:
         log(f"[bench] timing the CPU oracle on {args.cpu_rows} sampled rows")
@@ -470,6 +525,7 @@ def main():
         "stages": pre["stages"],
         "decode": dec,
         "kv_bridge": bridge,
+        "hs_decode": hs_dec,
     }
     print(json.dumps(out), flush=True)
 

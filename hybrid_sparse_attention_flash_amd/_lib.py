@@ -16,7 +16,8 @@ HYS_SCORE_NONE, HYS_SCORE_BLOCK, HYS_SCORE_TILE_TOKEN = 0, 1, 2
 # every symbol include/hys.h declares
 EXPORTED = (
     "hys_full_attn_fwd", "hys_select_topk", "hys_sparse_attn_fwd", "hys_swa_gate_fwd",
-    "hys_decode_step", "hys_sparse_layer_fwd", "hys_kv_bridge_fwd", "hys_last_error", "hys_status_string",
+    "hys_decode_step", "hys_sparse_layer_fwd", "hys_kv_bridge_fwd", "hys_hysparse_decode_step", "hys_last_error",
+    "hys_status_string",
     "hys_abi_version",
 )
 
@@ -43,6 +44,10 @@ class HysSparseParams(ctypes.Structure):
 class HysDecodeParams(ctypes.Structure):
     _fields_ = [("softmax_scale", ctypes.c_float), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
                 ("topk", ctypes.c_int32), ("window", ctypes.c_int32)]
+
+
+class HysHsDecodeParams(ctypes.Structure):
+    _fields_ = [("softmax_scale", ctypes.c_float), ("topk", ctypes.c_int32), ("block", ctypes.c_int32)]
 
 
 class HysBridgeParams(ctypes.Structure):
@@ -78,8 +83,11 @@ def load(path: str = LIB_PATH):
     lib.hys_sparse_layer_fwd.argtypes = [P(HysAttnParams), T4, T4, T4, P(HysSparseParams), vp, T4, T4,
                                          ctypes.c_int32, vp, vp, T4, vp]
     lib.hys_kv_bridge_fwd.argtypes = [P(HysBridgeParams), T4, vp, vp, T4, T4, vp, vp]
+    lib.hys_hysparse_decode_step.argtypes = [P(HysHsDecodeParams), T4, T4, T4, P(ctypes.c_int64), T4, vp, vp,
+                                             ctypes.c_int32, P(T4), P(T4), P(T4), P(T4), P(T4), P(vp), P(T4), vp,
+                                             P(sz), vp]
     for name in ("hys_full_attn_fwd", "hys_select_topk", "hys_sparse_attn_fwd", "hys_swa_gate_fwd",
-                 "hys_decode_step", "hys_sparse_layer_fwd", "hys_kv_bridge_fwd"):
+                 "hys_decode_step", "hys_sparse_layer_fwd", "hys_kv_bridge_fwd", "hys_hysparse_decode_step"):
         getattr(lib, name).restype = ctypes.c_int
     lib.hys_last_error.restype = ctypes.c_char_p
     lib.hys_last_error.argtypes = []

@@ -642,4 +642,159 @@ hys_status hys_kv_bridge_fwd(const hys_bridge_params* p, hys_tensor4 h, const vo
   }
 }
 
+// ---------------------------------------------------------------------------
+hys_status hys_hysparse_decode_step(const hys_hs_decode_params* p, hys_tensor4 q_full, hys_tensor4 k_cache,
+                                    hys_tensor4 v_cache, const int64_t* cache_len, hys_tensor4 o_full,
+                                    float* block_scores, int32_t* idx, int32_t n_sparse, const hys_tensor4* q_sparse,
+                                    const hys_tensor4* k_win_new, const hys_tensor4* v_win_new,
+                                    const hys_tensor4* k_ring, const hys_tensor4* v_ring, const float* const* gate_w,
+                                    const hys_tensor4* o_sparse, void* ws, size_t* ws_bytes, void* stream) {
+  try {
+    if (!p) return fail(HYS_ERR_INVALID_ARG, "null params");
+    if (!ws_bytes) return fail(HYS_ERR_INVALID_ARG, "ws_bytes must not be null");
+    hys_attn_params ap{p->softmax_scale, 1.f, 1.f};
+    hys_status s;
+    if ((s = check_params(&ap)) != HYS_OK) return s;
+    if ((s = check_qkv(q_full, k_cache, v_cache, false)) != HYS_OK) return s;
+    if (q_full.dtype != HYS_BF16 || k_cache.dtype != HYS_BF16)
+      return fail(HYS_ERR_UNSUPPORTED, "HySparse decode takes bf16 queries and a bf16 cache");
+    const int64_t B = q_full.shape[0], Hq = q_full.shape[2], D = q_full.shape[3], Nmax = k_cache.shape[1];
+    const int64_t Hkv = k_cache.shape[2], G = Hq / Hkv;
+    if (q_full.shape[1] != 1) return fail(HYS_ERR_INVALID_ARG, "decode takes one query token per sequence");
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+      return fail(HYS_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4, 8 or 16");
+    if (B > hys::kMaxDecodeBatch) return fail(HYS_ERR_UNSUPPORTED, "decode batch > %d", hys::kMaxDecodeBatch);
+    if (n_sparse < 0 || n_sparse > hys::kMaxDecodeLayers)
+      return fail(HYS_ERR_UNSUPPORTED, "n_sparse must be in [0, %d]", hys::kMaxDecodeLayers);
+    if (p->block != 64) return fail(HYS_ERR_UNSUPPORTED, "block must be 64");
+    if (p->topk < 1 || p->topk > 64) return fail(HYS_ERR_UNSUPPORTED, "topk must be in [1, 64]");
+    if (Nmax < 1) return fail(HYS_ERR_INVALID_ARG, "empty cache");
+    const int64_t nblk = (Nmax + 63) / 64;
+    {
+      const int64_t ch = hys::topk_chunk_cols();
+      if (nblk > ch && ((nblk + ch - 1) / ch) * (int64_t)p->topk > hys::topk_max_candidates())
+        return fail(HYS_ERR_UNSUPPORTED, "cache too long for top-%d", p->topk);
+    }
+    if ((s = check_out(o_full, q_full, "o_full")) != HYS_OK) return s;
+    if (!cache_len || !block_scores || !idx) return fail(HYS_ERR_INVALID_ARG, "null cache_len, block_scores or idx");
+    for (int64_t b = 0; b < B; ++b)
+      if (cache_len[b] < 1 || cache_len[b] > Nmax)
+        return fail(HYS_ERR_INVALID_ARG, "cache_len[%lld] = %lld outside [1, %lld]", (long long)b,
+                    (long long)cache_len[b], (long long)Nmax);
+    int64_t W = 0;
+    if (n_sparse > 0) {
+      if (!q_sparse || !o_sparse || !k_win_new || !v_win_new || !k_ring || !v_ring || !gate_w)
+        return fail(HYS_ERR_INVALID_ARG, "null per-layer array");
+      W = k_ring[0].shape[1];
+      if (W < 1) return fail(HYS_ERR_INVALID_ARG, "ring window must have at least one slot");
+      for (int l = 0; l < n_sparse; ++l) {
+        if ((s = check_out(q_sparse[l], q_full, "q_sparse")) != HYS_OK) return s;
+        if (q_sparse[l].dtype != HYS_BF16) return fail(HYS_ERR_UNSUPPORTED, "q_sparse must be bf16");
+        if (q_sparse[l].stride[0] != q_sparse[0].stride[0] || q_sparse[l].stride[2] != q_sparse[0].stride[2])
+          return fail(HYS_ERR_UNSUPPORTED, "all q_sparse must share strides");
+        if ((s = check_out(o_sparse[l], q_full, "o_sparse")) != HYS_OK) return s;
+        if (o_sparse[l].dtype != o_sparse[0].dtype || o_sparse[l].stride[0] != o_sparse[0].stride[0] ||
+            o_sparse[l].stride[2] != o_sparse[0].stride[2])
+          return fail(HYS_ERR_UNSUPPORTED, "all o_sparse must share dtype and strides");
+        const hys_tensor4* nw[4] = {&k_win_new[l], &v_win_new[l], &k_ring[l], &v_ring[l]};
+        const char* nm[4] = {"k_win_new", "v_win_new", "k_ring", "v_ring"};
+        for (int i = 0; i < 4; ++i) {
+          if ((s = check_tensor(*nw[i], nm[i], false)) != HYS_OK) return s;
+          if (nw[i]->dtype != HYS_BF16) return fail(HYS_ERR_UNSUPPORTED, "%s must be bf16", nm[i]);
+          const int64_t want[4] = {B, i < 2 ? 1 : W, Hkv, D};
+          for (int d = 0; d < 4; ++d)
+            if (nw[i]->shape[d] != want[d]) return fail(HYS_ERR_INVALID_ARG, "%s: shape mismatch", nm[i]);
+        }
+        for (int d = 0; d < 3; ++d) {
+          if (v_win_new[l].stride[d] != k_win_new[0].stride[d] || k_win_new[l].stride[d] != k_win_new[0].stride[d])
+            return fail(HYS_ERR_UNSUPPORTED, "all new-token window tensors must share strides");
+          if (v_ring[l].stride[d] != k_ring[0].stride[d] || k_ring[l].stride[d] != k_ring[0].stride[d])
+            return fail(HYS_ERR_UNSUPPORTED, "all ring tensors must share strides");
+        }
+        if (!gate_w[l]) return fail(HYS_ERR_INVALID_ARG, "null gate_w");
+      }
+    }
+    // the full layer runs once per KV head on the split-K kernel (G heads each)
+    const int64_t ntiles = (Nmax + 63) / 64;
+    int nsplit = (int)(512 / B);
+    if (nsplit < 1) nsplit = 1;
+    if ((int64_t)nsplit * 8 > ntiles) nsplit = (int)((ntiles + 7) / 8);
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t ts_bytes = (size_t)(Hkv * B * Nmax) * sizeof(float);
+    const size_t part_one = (size_t)(B * nsplit * G) * (size_t)(D + 2) * sizeof(float);
+    const size_t tk = hys::topk_workspace_bytes(B, nblk, p->topk);
+    const size_t need = up(ts_bytes) + (size_t)Hkv * up(part_one) + up(tk);
+    if (!ws) { *ws_bytes = need; return ok(); }
+    if (*ws_bytes < need) return fail(HYS_ERR_WORKSPACE, "workspace %zu < required %zu bytes", *ws_bytes, need);
+    if (!aligned16(ws)) return fail(HYS_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+    char* w = (char*)ws;
+    float* ts = (float*)w;
+    w += up(ts_bytes);
+    char* parts = w;
+    w += (size_t)Hkv * up(part_one);
+    void* tkws = w;
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+      return fail(HYS_ERR_HIP, "device query failed");
+
+    hipStream_t st = (hipStream_t)stream;
+    const float logit_scale = p->softmax_scale;
+    const size_t oes = o_full.dtype == HYS_F32 ? 4 : 2;
+    for (int64_t g = 0; g < Hkv; ++g) {
+      float* po = (float*)(parts + (size_t)g * up(part_one));
+      float* pml = po + (size_t)(B * nsplit * G) * D;
+      hys::DecArgs d{};
+      d.q[0] = (const uint16_t*)q_full.ptr + g * G * q_full.stride[2];
+      d.q_sb = q_full.stride[0]; d.q_sh = q_full.stride[2];
+      d.k = (const uint16_t*)k_cache.ptr + g * k_cache.stride[2]; d.k_sb = k_cache.stride[0]; d.k_st = k_cache.stride[1];
+      d.v = (const uint16_t*)v_cache.ptr + g * v_cache.stride[2]; d.v_sb = v_cache.stride[0]; d.v_st = v_cache.stride[1];
+      for (int64_t b = 0; b < B; ++b) d.lens[b] = (int)cache_len[b];
+      d.B = (int)B; d.Hq = (int)G; d.Nmax = (int)Nmax; d.ncu = ncu;
+      d.scale_log2 = logit_scale * 1.4426950408889634f; d.logit_scale = logit_scale;
+      d.nsplit = nsplit; d.nlayer = 1;
+      d.scores = ts + (size_t)g * B * Nmax; d.sc_sb = Nmax;
+      d.part_o = po; d.part_ml = pml;
+      hipError_t e = hys::launch_decode(0, hys::ET_BF16, (int)D, d, st);
+      if (e != hipSuccess) return hip_status(e, "decode split launch");
+      hys::MergeArgs m{};
+      m.B = (int)B; m.Hq = (int)G; m.logit_scale = logit_scale; m.v_scale = 1.f; m.scale_log2 = d.scale_log2;
+      m.part_o = po; m.part_ml = pml; m.nsplit = nsplit; m.nlayer = 1;
+      m.o[0] = (char*)o_full.ptr + (size_t)(g * G * o_full.stride[2]) * oes;
+      m.o_sb = o_full.stride[0]; m.o_sh = o_full.stride[2]; m.o_f32 = o_full.dtype == HYS_F32;
+      e = hys::launch_decode_merge((int)D, m, st);
+      if (e != hipSuccess) return hip_status(e, "decode merge launch");
+    }
+    hipError_t e = hys::launch_hs_block_max(ts, (int)Hkv, B * Nmax, (int)B, (int)Nmax, (int)nblk, block_scores, st);
+    if (e != hipSuccess) return hip_status(e, "block score launch");
+    hys_status ts_status = topk_launch(block_scores, B, nblk, nblk, p->topk, idx, nullptr, tkws, st);
+    if (ts_status != HYS_OK) return ts_status;
+    if (n_sparse > 0) {
+      hys::HsDecArgs h{};
+      h.k = (const uint16_t*)k_cache.ptr; h.k_sb = k_cache.stride[0]; h.k_st = k_cache.stride[1]; h.k_sh = k_cache.stride[2];
+      h.v = (const uint16_t*)v_cache.ptr; h.v_sb = v_cache.stride[0]; h.v_st = v_cache.stride[1]; h.v_sh = v_cache.stride[2];
+      for (int64_t b = 0; b < B; ++b) h.lens[b] = (int)cache_len[b];
+      h.B = (int)B; h.Hkv = (int)Hkv; h.G = (int)G; h.nlayer = n_sparse; h.topk = p->topk; h.W = (int)W;
+      h.scale_log2 = logit_scale * 1.4426950408889634f;
+      h.idx = idx; h.idx_sb = p->topk;
+      h.q_sb = q_sparse[0].stride[0]; h.q_sh = q_sparse[0].stride[2];
+      h.n_sb = k_win_new[0].stride[0]; h.n_sh = k_win_new[0].stride[2];
+      h.r_sb = k_ring[0].stride[0]; h.r_st = k_ring[0].stride[1]; h.r_sh = k_ring[0].stride[2];
+      h.o_sb = o_sparse[0].stride[0]; h.o_sh = o_sparse[0].stride[2]; h.o_f32 = o_sparse[0].dtype == HYS_F32;
+      for (int l = 0; l < n_sparse; ++l) {
+        h.q[l] = (const uint16_t*)q_sparse[l].ptr;
+        h.knew[l] = (const uint16_t*)k_win_new[l].ptr; h.vnew[l] = (const uint16_t*)v_win_new[l].ptr;
+        h.kring[l] = (uint16_t*)k_ring[l].ptr; h.vring[l] = (uint16_t*)v_ring[l].ptr;
+        h.gate_w[l] = gate_w[l];
+        h.o[l] = o_sparse[l].ptr;
+      }
+      e = hys::launch_hs_decode_sparse((int)D, h, st);
+      if (e != hipSuccess) return hip_status(e, "sparse layer launch");
+    }
+    return ok();
+  } catch (...) {
+    return fail(HYS_ERR_INTERNAL, "internal error");
+  }
+}
+
 }  // extern "C"

@@ -102,6 +102,28 @@ struct MergeArgs {
 hipError_t launch_decode(int sparse, int kt, int D, const DecArgs& a, hipStream_t s);
 hipError_t launch_decode_merge(int D, const MergeArgs& a, hipStream_t s);
 
+// HySparse (block-level) decode: block scores from the full layer's per-KV-head
+// token scores, and every sparse layer (block gather, ring window, gate).
+hipError_t launch_hs_block_max(const float* ts, int nparts, int64_t part_stride, int B, int Nmax, int nblk,
+                               float* out, hipStream_t s);
+
+struct HsDecArgs {
+  const uint16_t* k; int64_t k_sb, k_st, k_sh;           // shared cache [B, Nmax, Hkv, D] bf16
+  const uint16_t* v; int64_t v_sb, v_st, v_sh;
+  int lens[kMaxDecodeBatch];
+  int B, Hkv, G, nlayer, topk, W;                        // G query heads per KV head, W ring slots
+  float scale_log2;                                      // softmax scale * log2(e)
+  const int32_t* idx; int64_t idx_sb;                    // [B, topk] selected block ids
+  const uint16_t* q[kMaxDecodeLayers]; int64_t q_sb, q_sh;        // [B, 1, Hq, D] bf16 per layer
+  const uint16_t* knew[kMaxDecodeLayers]; const uint16_t* vnew[kMaxDecodeLayers];
+  int64_t n_sb, n_sh;                                    // new token's window K/V [B, 1, Hkv, D]
+  uint16_t* kring[kMaxDecodeLayers]; uint16_t* vring[kMaxDecodeLayers];
+  int64_t r_sb, r_st, r_sh;                              // rings [B, W, Hkv, D]
+  const float* gate_w[kMaxDecodeLayers];                 // [Hq, D] fp32 per layer
+  void* o[kMaxDecodeLayers]; int64_t o_sb, o_sh; int o_f32;       // [B, 1, Hq, D]
+};
+hipError_t launch_hs_decode_sparse(int D, const HsDecArgs& a, hipStream_t s);
+
 // HySparse2 KV Bridging: K/V of a cross-decoder full layer projected from
 // hidden states straight into the fp8 e4m3 cache.
 struct BridgeArgs {

@@ -12,7 +12,7 @@ import torch
 
 from . import _lib
 from ._lib import (HYS_BF16, HYS_F32, HYS_FP8_E4M3, HYS_SCORE_BLOCK, HYS_SCORE_NONE, HYS_SCORE_TILE_TOKEN,
-                   HysAttnParams, HysBridgeParams, HysDecodeParams, HysScoreParams, HysSparseParams, HysTensor4, check)
+                   HysAttnParams, HysBridgeParams, HysDecodeParams, HysHsDecodeParams, HysScoreParams, HysSparseParams, HysTensor4, check)
 
 _DT = {torch.float32: HYS_F32, torch.bfloat16: HYS_BF16, torch.uint8: HYS_FP8_E4M3,
        torch.float8_e4m3fn: HYS_FP8_E4M3}
@@ -128,6 +128,33 @@ def hys_decode_step(q_full, k_cache, v_cache, cache_len: Sequence[int], o_full, 
         workspace = _workspace(nb.value, q_full.device)
     nb2 = ctypes.c_size_t(workspace.numel())
     check(lib.hys_decode_step(*args, _ptr(workspace), ctypes.byref(nb2), _stream(q_full.device)))
+    return workspace
+
+
+def hys_hysparse_decode_step(q_full, k_cache, v_cache, cache_len: Sequence[int], o_full, block_scores, idx,
+                             q_sparse: Sequence[torch.Tensor], k_win_new: Sequence[torch.Tensor],
+                             v_win_new: Sequence[torch.Tensor], k_ring: Sequence[torch.Tensor],
+                             v_ring: Sequence[torch.Tensor], gate_w: Sequence[torch.Tensor],
+                             o_sparse: Sequence[torch.Tensor], topk: int, softmax_scale: float = None,
+                             workspace: Optional[torch.Tensor] = None):
+    """One HySparse decode step; the rings are updated in place.  Returns the workspace for reuse."""
+    lib = _lib.load()
+    p = HysHsDecodeParams(softmax_scale or 1.0 / math.sqrt(q_full.shape[-1]), topk, 64)
+    lens = (ctypes.c_int64 * len(cache_len))(*[int(x) for x in cache_len])
+    n = len(q_sparse)
+
+    def arr(ts):
+        return (HysTensor4 * max(n, 1))(*[tensor4(t) for t in ts])
+    gw = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in gate_w])
+    args = [ctypes.byref(p), tensor4(q_full), tensor4(k_cache), tensor4(v_cache), lens, tensor4(o_full),
+            _ptr(block_scores), _ptr(idx), n, arr(q_sparse), arr(k_win_new), arr(v_win_new), arr(k_ring),
+            arr(v_ring), gw, arr(o_sparse)]
+    nb = ctypes.c_size_t(0)
+    check(lib.hys_hysparse_decode_step(*args, None, ctypes.byref(nb), None))
+    if workspace is None or workspace.numel() < nb.value:
+        workspace = _workspace(nb.value, q_full.device)
+    nb2 = ctypes.c_size_t(workspace.numel())
+    check(lib.hys_hysparse_decode_step(*args, _ptr(workspace), ctypes.byref(nb2), _stream(q_full.device)))
     return workspace
 
 

@@ -23,6 +23,12 @@
  *   hys_sparse_layer_fwd - a whole HySparse sparse layer (sparse branch,
  *                          window branch and gate) in one pass
  *
+ * the HySparse (block-level) decode step:
+ *
+ *   hys_hysparse_decode_step - full layer with block scores, top-k blocks,
+ *                          and every sparse layer (block gather, ring window
+ *                          cache with append, gate) for one new query
+ *
  * and the step that fills HySparse2's shared cache:
  *
  *   hys_kv_bridge_fwd    - KV Bridging: a cross-decoder full layer's K/V
@@ -270,6 +276,56 @@ HYS_API hys_status hys_decode_step(const hys_decode_params* p, hys_tensor4 q_ful
                            hys_tensor4 v_cache, const int64_t* cache_len, hys_tensor4 o_full, float* token_scores,
                            int32_t* idx, int32_t n_sparse, const hys_tensor4* q_sparse,
                            const hys_tensor4* o_sparse, void* ws, size_t* ws_bytes, void* stream);
+
+typedef struct {
+  float softmax_scale;
+  int32_t topk;   /* key blocks selected from the full layer's block scores (1..64) */
+  int32_t block;  /* key-block size; must be 64 */
+} hys_hs_decode_params;
+
+/*
+ * hys_hysparse_decode_step - one HySparse decode step (block-level selection
+ * with a gated sliding-window branch; QbitAI HySparse article, method section;
+ * TechWalker write-up: 64-token blocks, window 128 over the layer's own K/V).
+ *
+ * For each sequence b with valid cache length n = cache_len[b] (the shared
+ * cache already holds the new token at position n-1):
+ *   full layer:   o_full[b,0,h,:] = attention of q_full[b,0,h,:] over keys
+ *                 [0, n) of KV head h/G (G = Hq/Hkv);
+ *                 block_scores[b,c] = max_h max_{j in block c, j < n} S[b,h,j]
+ *                 (-inf for blocks with no key below n);
+ *   selection:    idx[b,:] = top-topk of block_scores[b,:] (block ids,
+ *                 ascending, -1 padded; the hys_select_topk rule);
+ *   sparse layers l = 0..n_sparse-1, each with a ring window cache of W slots
+ *   (token t in slot t mod W):
+ *                 the new token's window K/V k_win_new[l], v_win_new[l] is
+ *                 written into slot (n-1) mod W of k_ring[l], v_ring[l];
+ *                 O_sp = attention of q_sparse[l] over { j < n : j/64 in idx[b,:] }
+ *                 of the shared cache; O_w = attention over the window tokens
+ *                 [max(0, n-W), n-1] of the ring;
+ *                 o_sparse[l] = g O_sp + (1-g) O_w, g = sigmoid(<q, gate_w[l][h,:]>),
+ *                 and o_sparse[l] = O_w where the selected set is empty.
+ * q_full, q_sparse[l]: [B, 1, Hq, D] bf16 (all q_sparse with equal strides).
+ * k_cache, v_cache: [B, Nmax, Hkv, D] bf16.  cache_len: HOST array of B
+ * lengths, 1 <= n <= Nmax.  o_full, o_sparse[l]: [B, 1, Hq, D] fp32 or bf16
+ * (all o_sparse of one type and strides).  block_scores: [B, ceil(Nmax/64)]
+ * fp32, contiguous.  idx: [B, topk] int32.
+ * k_win_new[l], v_win_new[l]: [B, 1, Hkv, D] bf16; k_ring[l], v_ring[l]:
+ * [B, W, Hkv, D] bf16, updated in place; every new and ring tensor with one
+ * set of strides.  gate_w[l]: [Hq, D] fp32, contiguous.  The window length
+ * is W = k_ring[0].shape[1].
+ * Limits: Hq = Hkv*G with G in {1, 2, 4, 8, 16}, B <= 64, n_sparse <= 16,
+ * topk <= 64.
+ * Workspace: per-KV-head token scores and split partials, top-k candidates
+ * (query with ws == NULL).
+ */
+HYS_API hys_status hys_hysparse_decode_step(const hys_hs_decode_params* p, hys_tensor4 q_full, hys_tensor4 k_cache,
+                                            hys_tensor4 v_cache, const int64_t* cache_len, hys_tensor4 o_full,
+                                            float* block_scores, int32_t* idx, int32_t n_sparse,
+                                            const hys_tensor4* q_sparse, const hys_tensor4* k_win_new,
+                                            const hys_tensor4* v_win_new, const hys_tensor4* k_ring,
+                                            const hys_tensor4* v_ring, const float* const* gate_w,
+                                            const hys_tensor4* o_sparse, void* ws, size_t* ws_bytes, void* stream);
 
 typedef struct {
   float k_scale;  /* K cache quantisation scale: the stored code is e4m3(K / k_scale) */

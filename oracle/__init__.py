@@ -24,7 +24,8 @@ Parity unpinned (against the real HySparse/HySparse2, whose pages leave these
 open): the head reduction of importance scores (max over all query heads),
 the gate's form (one sigmoid scalar per token and head, no bias), the empty
 sparse set rule, the per-tile token-score reading, the per-query forced
-window and the decode-time ring window cache.  They are pinned only to this package's stated readings.
+window and the decode-time ring window cache.  They are pinned only to this
+package's stated readings.
 """
 from . import bridge, fp8, hysparse_decode  # noqa: F401
 from .hysparse import (  # noqa: F401

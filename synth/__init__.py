@@ -107,6 +107,16 @@ WORKLOADS: Dict[str, Workload] = {
 
 WORKLOAD_ORDER = ["tiny_fp32", "dense7b_16k", "moe80b_32k", "hysparse2_64k", "decode_1m"]
 
+# HySparse (block-level) decode: the 80B-like block's attention (32 query /
+# 4 KV heads, bf16, 11 sparse layers, top-16 of 64-token blocks, window 128)
+# one token at a time against a 128k-token cache per sequence.  The pages give
+# no HySparse decode configuration; 128k x 4 sequences is the same KV byte
+# count as the 1M-token fp8 HySparse2 decode workload.
+HS_DECODE_WORKLOAD = Workload(
+    name="hysparse_decode_128k", cfg_id=7, B=4, L=131072, Hq=32, Hkv=4, D=128,
+    q_dtype="bf16", kv_dtype="bf16", n_sparse=11, variant="hsdecode",
+    block=64, topk=16, window=128)
+
 
 # ----------------------------------------------------------------------------
 # seeded draws and storage conversions
@@ -246,3 +256,28 @@ def gen_bridge(seed: int, cfg_id: int, B: int, L: int, d_model: int, n_out: int,
     wk = normal(seed, cfg_id, "bridge_wk", (n_out, d_model), std=std)
     wv = normal(seed, cfg_id, "bridge_wv", (n_out, d_model), std=std)
     return to_bf16(h), to_bf16(wk), to_bf16(wv)
+
+
+def gen_hs_decode(w: Workload, seed: int = 0) -> Dict:
+    """Inputs of one HySparse decode step (bf16 CPU tensors, gate fp32).
+
+    q_full [B,1,Hq,D]; the shared cache k, v [B,N,Hkv,D]; per sparse layer l:
+    q [B,1,Hq,D], the new token's window K/V [B,1,Hkv,D], the ring
+    [B,window,Hkv,D] (window K/V of the earlier tokens; every slot is drawn,
+    including slots that hold no token yet) and gate_w [Hq,D] ~ N(0, gate_std^2).
+    """
+    B, N, Hq, Hkv, D, W = w.B, w.L, w.Hq, w.Hkv, w.D, w.window
+    out = {
+        "q_full": to_bf16(normal(seed, w.cfg_id, "hsd_q0", (B, 1, Hq, D))),
+        "k": to_bf16(normal(seed, w.cfg_id, "hsd_k", (B, N, Hkv, D))),
+        "v": to_bf16(normal(seed, w.cfg_id, "hsd_v", (B, N, Hkv, D))),
+        "q": [], "k_new": [], "v_new": [], "k_ring": [], "v_ring": [], "gate_w": [],
+    }
+    for l in range(1, w.n_sparse + 1):
+        out["q"].append(to_bf16(normal(seed, w.cfg_id, f"hsd_q{l}", (B, 1, Hq, D))))
+        out["k_new"].append(to_bf16(normal(seed, w.cfg_id, f"hsd_kn{l}", (B, 1, Hkv, D))))
+        out["v_new"].append(to_bf16(normal(seed, w.cfg_id, f"hsd_vn{l}", (B, 1, Hkv, D))))
+        out["k_ring"].append(to_bf16(normal(seed, w.cfg_id, f"hsd_kr{l}", (B, W, Hkv, D))))
+        out["v_ring"].append(to_bf16(normal(seed, w.cfg_id, f"hsd_vr{l}", (B, W, Hkv, D))))
+        out["gate_w"].append(torch.from_numpy(normal(seed, w.cfg_id, f"hsd_gate{l}", (Hq, D), std=w.gate_std)))
+    return out

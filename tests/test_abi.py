@@ -185,3 +185,39 @@ def test_kv_bridge_empty_accepts_null_tensors():
     h1 = t4([2, 1, 1, 128], ptr=0)
     assert lib().hys_kv_bridge_fwd(ctypes.byref(p), h1, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), kc, kc,
                                    None, None) == INVALID
+
+
+def test_hysparse_decode_validation():
+    from hybrid_sparse_attention_flash_amd._lib import HysHsDecodeParams
+    B, N, Hq, Hkv, D, W, nl = 2, 4096, 32, 4, 128, 128, 2
+    p = HysHsDecodeParams(0.088, 16, 64)
+    q = t4([B, 1, Hq, D])
+    kc = t4([B, N, Hkv, D])
+    o = t4([B, 1, Hq, D], dtype=0)
+    lens = (ctypes.c_int64 * B)(N, 100)
+    qs = (HysTensor4 * nl)(*[t4([B, 1, Hq, D]) for _ in range(nl)])
+    new = (HysTensor4 * nl)(*[t4([B, 1, Hkv, D]) for _ in range(nl)])
+    ring = (HysTensor4 * nl)(*[t4([B, W, Hkv, D]) for _ in range(nl)])
+    gw = (ctypes.c_void_p * nl)(FAKE, FAKE)
+    nb = ctypes.c_size_t(0)
+
+    def call(pp=p, q=q, k=kc, ln=lens, n_sparse=nl, ring=ring, new=new, gw=gw, scores=FAKE):
+        return lib().hys_hysparse_decode_step(ctypes.byref(pp), q, k, k, ln, o, ctypes.c_void_p(scores),
+                                              ctypes.c_void_p(FAKE), n_sparse, qs, new, new, ring, ring, gw, qs,
+                                              None, ctypes.byref(nb), None)
+    assert call() == 0 and nb.value > 0                                         # size query
+    assert call(k=t4([B, N, Hkv, D], dtype=2)) == UNSUPPORTED                   # fp8 cache
+    assert call(q=t4([B, 1, 64, D]), k=t4([B, N, 2, D])) == UNSUPPORTED          # G = 32 > 16
+    assert call(q=t4([B, 1, 12, D]), k=t4([B, N, 4, D])) == UNSUPPORTED          # G = 3
+    assert call(pp=HysHsDecodeParams(0.088, 65, 64)) == UNSUPPORTED              # topk > 64
+    assert call(pp=HysHsDecodeParams(0.088, 16, 32)) == UNSUPPORTED              # block != 64
+    assert call(ln=(ctypes.c_int64 * B)(0, 5)) == INVALID                       # empty sequence
+    assert call(ln=(ctypes.c_int64 * B)(N + 1, 5)) == INVALID                   # beyond the cache
+    bad_ring = (HysTensor4 * nl)(*[t4([B, W, Hkv, 64]) for _ in range(nl)])
+    assert call(ring=bad_ring) == INVALID                                       # ring head dim
+    bad_new = (HysTensor4 * nl)(*[t4([B, 2, Hkv, D]) for _ in range(nl)])
+    assert call(new=bad_new) == INVALID                                         # two new tokens
+    assert call(gw=(ctypes.c_void_p * nl)(FAKE, 0)) == INVALID                  # null gate
+    assert call(scores=0) == INVALID
+    assert call(n_sparse=17) == UNSUPPORTED
+    assert call(n_sparse=0) == 0                                                # full layer only

@@ -12,7 +12,7 @@ import torch
 import oracle
 import synth
 from hybrid_sparse_attention_flash_amd import ops
-from tests.parity_util import (TOL_OUT, check_scores, check_topk_band, dev, f64, max_abs)
+from tests.parity_util import (TOL_OUT, check_out, check_scores, check_topk_band, dev, f64, max_abs)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,7 @@ def test_full_attention_block_scores(name, L, Hq, Hkv, D):
         qf, kf, vf = f64(q[b], w.q_dtype), f64(k[b], w.kv_dtype), f64(v[b], w.kv_dtype)
         O, LSE = oracle.full_attention(qf, kf, vf, w.scale)
         M = oracle.block_scores(qf, kf, w.scale, 64)
-        assert max_abs(o[b].cpu().numpy(), O) <= tol
+        check_out(o[b].cpu().numpy(), O, w.q_dtype, "o")
         assert max_abs(lse[b].cpu().numpy(), LSE) <= max(tol, 1e-3)
         check_scores(sc[b].cpu().numpy(), M)
 
@@ -86,7 +86,7 @@ def test_full_attention_tile_token_scores(name, L, Hq, Hkv, D):
     qf, kf, vf = f64(q[0]), oracle.as_f64(k[0], w.kv_dtype, ks), oracle.as_f64(v[0], w.kv_dtype, vs)
     O, LSE = oracle.full_attention(qf, kf, vf, w.scale)
     T = oracle.tile_token_scores(qf, kf, w.scale, 64)
-    assert max_abs(o[0].cpu().numpy(), O) <= TOL_OUT["bf16"]
+    check_out(o[0].cpu().numpy(), O, "bf16", "o")
     assert max_abs(lse[0].cpu().numpy(), LSE) <= 1e-3
     check_scores(sc[0].cpu().numpy(), T)
 
@@ -146,7 +146,7 @@ def test_sparse_block_attention(name, L, Hq, Hkv, D, k):
     torch.cuda.synchronize()
     O, LSE = oracle.sparse_block_attention(f64(q[0], w.q_dtype), f64(kk[0], w.kv_dtype), f64(vv[0], w.kv_dtype),
                                            w.scale, sel if k > 0 else np.zeros((L, 0), int), 64)
-    assert max_abs(o[0].cpu().numpy(), O) <= TOL_OUT[w.q_dtype]
+    check_out(o[0].cpu().numpy(), O, w.q_dtype, "o")
     g = lse[0].cpu().numpy()
     assert np.array_equal(np.isneginf(g), np.isneginf(LSE))
     fin = np.isfinite(LSE)
@@ -178,7 +178,7 @@ def test_sparse_token_attention(L, Hq, D, k, W, kv):
     torch.cuda.synchronize()
     O, LSE = oracle.sparse_token_attention(f64(q[0]), oracle.as_f64(kk[0], kv, ks), oracle.as_f64(vv[0], kv, vs),
                                            w.scale, sel, 64, W)
-    assert max_abs(o[0].cpu().numpy(), O) <= TOL_OUT["bf16"]
+    check_out(o[0].cpu().numpy(), O, "bf16", "o")
     assert max_abs(lse[0].cpu().numpy(), LSE) <= 1e-3
 
 
@@ -203,7 +203,7 @@ def test_swa_gate(name, L, Hq, Hkv, D, W):
     Ow, _ = oracle.window_attention(qf, f64(kw[0], w.q_dtype), f64(vw[0], w.q_dtype), w.scale, W)
     ref = oracle.gate_merge(qf, gw.numpy().astype(np.float64), o_sp[0].astype(np.float64),
                             lse_sp[0].astype(np.float64), Ow)
-    assert max_abs(o[0].cpu().numpy(), ref) <= TOL_OUT[w.q_dtype]
+    check_out(o[0].cpu().numpy(), ref, w.q_dtype, "o")
 
 
 @pytest.mark.parametrize("name,L,Hq,Hkv,D,k,W,out", [
@@ -239,7 +239,7 @@ def test_sparse_layer_fused(name, L, Hq, Hkv, D, k, W, out):
     ref = oracle.gate_merge(qf, gw.numpy().astype(np.float64), Osp, LSEsp, Ow)
     got = o[0].float().cpu().numpy()
     assert np.isfinite(got).all()
-    assert max_abs(got, ref) <= TOL_OUT[w.q_dtype if out == "f32" else "bf16"]
+    check_out(got, ref, w.q_dtype if out == "f32" else "bf16", "o")
 
 
 @pytest.mark.parametrize("B,N,lens,Hq,D,topk,W,nsp,kv", [
@@ -267,7 +267,7 @@ def test_decode_step(B, N, lens, Hq, D, topk, W, nsp, kv):
         kf = oracle.as_f64(kc[b, :, 0:1], kv, ks)
         vf = oracle.as_f64(vc[b, :, 0:1], kv, vs)
         res = oracle.decode_step(f64(qf[b, 0]), kf, vf, w.scale, n, [f64(x[b, 0]) for x in qs], topk, W)
-        assert max_abs(o_full[b, 0].cpu().numpy(), res["o_full"]) <= TOL_OUT["bf16"]
+        check_out(o_full[b, 0].cpu().numpy(), res["o_full"], "bf16", "o_full")
         s = scores[b].cpu().numpy()
         check_scores(s[:n], res["scores"])
         assert np.all(np.isneginf(s[n:]))
@@ -275,7 +275,7 @@ def test_decode_step(B, N, lens, Hq, D, topk, W, nsp, kv):
         same, inband = check_topk_band(gi[None], res["sel"][None], res["scores"][None], topk)
         if same:
             for l in range(nsp):
-                assert max_abs(o_sp[l][b, 0].cpu().numpy(), res["o_layers"][l]) <= TOL_OUT["bf16"]
+                check_out(o_sp[l][b, 0].cpu().numpy(), res["o_layers"][l], "bf16", "o_sparse")
 
 
 @pytest.mark.parametrize("half", [0, 1])
