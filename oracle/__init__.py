@@ -29,10 +29,10 @@ package's stated readings.
 """
 from . import bridge, fp8, hysparse_decode  # noqa: F401
 from .hysparse import (  # noqa: F401
-    NEG_INF, attend, block_scores, decode_full, decode_sparse, decode_step,
-    full_attention, gate_merge, hysparse2_block, hysparse_block, logits,
-    sparse_block_attention, sparse_token_attention, tile_token_scores,
-    topk_rows, topk_select, window_attention,
+    NEG_INF, attend, block_scores, block_scores_per_group, decode_full, decode_sparse, decode_step,
+    expand_blocks, full_attention, gate_merge, hysparse2_block, hysparse2_gated_window_layer, hysparse_block,
+    logits, sparse_block_attention, sparse_block_attention_grouped, sparse_token_attention, tile_block_scores,
+    tile_token_scores, topk_rows, topk_select, window_attention,
 )
 
 import numpy as _np

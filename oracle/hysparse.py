@@ -132,6 +132,30 @@ def block_scores(q, k, scale, block, rows=None):
     return pad.reshape(len(rows), nblk, block).max(axis=2)
 
 
+def block_scores_per_group(q, k, scale, block, rows=None):
+    """Per-KV-group block importance, the ablation of the head reduction (R1).
+
+    M[g, i, c] = max over the query heads h of KV group g (h // G == g) of
+    max_{j in block c, j <= i} S[h, i, j]: each KV group selects for itself
+    instead of one index set serving every group.  Returns [Hkv, R, nblk].
+    """
+    L, Hq, _ = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    Lk = k.shape[0]
+    rows = _rows(rows, L)
+    S = logits(q[rows], k, scale, G)
+    S[:, ~_causal_allowed(rows, Lk)] = NEG_INF
+    nblk = (Lk + block - 1) // block
+    out = np.empty((Hkv, len(rows), nblk))
+    for g in range(Hkv):
+        Sg = S[g * G:(g + 1) * G].max(axis=0)       # [R, Lk] max over the group's heads
+        pad = np.full((len(rows), nblk * block), NEG_INF)
+        pad[:, :Lk] = Sg
+        out[g] = pad.reshape(len(rows), nblk, block).max(axis=2)
+    return out
+
+
 def tile_token_scores(q, k, scale, tile, tiles=None):
     """HySparse2 token importance T[t, j] = max_h max_{i in tile t, i >= j} S[h, i, j].
 
@@ -215,6 +239,28 @@ def sparse_block_attention(q, k, v, scale, sel, block, rows=None):
     allowed &= _causal_allowed(rows, Lk)
     S = logits(q[rows], k, scale, G)
     S[:, ~allowed] = NEG_INF
+    return attend(S, v, G)
+
+
+def sparse_block_attention_grouped(q, k, v, scale, sel_g, block, rows=None):
+    """Block-sparse branch with one index set per KV group (per-group variant):
+    head h attends J_{h//G}(i) = {j <= i : j // block in sel_g[h // G, i]}.
+    `sel_g` [Hkv, R, kb] holds block ids for the rows in `rows` (-1 = unused)."""
+    L, Hq, _ = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    Lk = k.shape[0]
+    rows = _rows(rows, L)
+    causal = _causal_allowed(rows, Lk)
+    S = logits(q[rows], k, scale, G)
+    for g in range(Hkv):
+        allowed = np.zeros((len(rows), Lk), dtype=bool)
+        for r in range(len(rows)):
+            for c in np.asarray(sel_g[g][r]):
+                if c >= 0:
+                    allowed[r, c * block:(c + 1) * block] = True
+        allowed &= causal
+        S[g * G:(g + 1) * G][:, ~allowed] = NEG_INF
     return attend(S, v, G)
 
 
@@ -383,3 +429,48 @@ def decode_step(q_full, kc, vc, scale, n, q_sparse, topk, window):
     sel, cnt = topk_select(s, topk)
     outs = [decode_sparse(ql, kc, vc, scale, n, sel, window)[0] for ql in q_sparse]
     return dict(o_full=o_full, lse=lse, scores=s, sel=sel, count=cnt, o_layers=outs)
+
+
+# ----------------------------------------------------------------------------
+# ablation variants (switches on the HySparse2 block)
+# ----------------------------------------------------------------------------
+
+def hysparse2_gated_window_layer(q, k, v, scale, sel_tiles, tile, window, gate_w, rows=None):
+    """HySparse2 sparse layer with a gated sliding-window branch instead of the
+    forced recent window (the ablation of [airebao] forced recent window
+    paragraph, where a gated SWA is compared with forcing the window into the
+    selected set).  Reading: the window branch covers the same 128 recent
+    tokens of the shared cache, and the two branches are fused by the HySparse
+    sigmoid gate:  o = g * O(sel) + (1 - g) * O(window), o = O(window) when the
+    selected set is empty.
+    """
+    L = q.shape[0]
+    rows = _rows(rows, L)
+    o_sp, lse_sp = sparse_token_attention(q, k, v, scale, sel_tiles, tile, 0, rows)
+    o_w, _ = window_attention(q, k, v, scale, window, rows)
+    return gate_merge(q[rows], gate_w, o_sp, lse_sp, o_w)
+
+
+def tile_block_scores(T, block):
+    """Block-level importance per query tile from the tile-token scores:
+    M[t, c] = max over the keys of block c of T[t, j] (-inf when none is
+    visible).  Block-level selection at the token budget of HySparse2 picks
+    the top (budget / block) blocks of these rows ([deming] section 03:
+    token- vs block-level selection at the same 1024 + 128 budget)."""
+    T = np.asarray(T, dtype=np.float64)
+    nt, Lk = T.shape
+    nblk = (Lk + block - 1) // block
+    pad = np.full((nt, nblk * block), NEG_INF)
+    pad[:, :Lk] = T
+    return pad.reshape(nt, nblk, block).max(axis=2)
+
+
+def expand_blocks(sel_blocks, block, Lk):
+    """Token positions of selected blocks (ascending, -1 padded): each block c
+    contributes [c*block, min(Lk, (c+1)*block))."""
+    sel_blocks = np.asarray(sel_blocks)
+    out = np.full((sel_blocks.shape[0], sel_blocks.shape[1] * block), -1, dtype=np.int64)
+    for r in range(sel_blocks.shape[0]):
+        toks = [j for c in sel_blocks[r] if c >= 0 for j in range(c * block, min(Lk, (c + 1) * block))]
+        out[r, :len(toks)] = toks
+    return out
