@@ -115,7 +115,7 @@ def run_block(blk, inp, timer=None):
     for l in range(blk.n_sparse):
         # one pass per sparse layer: selected blocks of the shared KV, the
         # layer's own window, and the gate
-        rec("sparse_layer", lambda: ops.hys_sparse_layer_fwd(q[l + 1], k, v, blk.idx, kw[l], vw[l], blk.window,
+        rec("sparse_layer", lambda: ops.hys_sparse_layer_fwd(q[l + 1], k, v, blk._idx(), kw[l], vw[l], blk.window,
                                                              gw[l], blk.o_layers[l], topk=blk.topk))
 
 
@@ -295,7 +295,7 @@ def bench_prefill(args, dev):
 
     # algorithmic work of the step
     fl_full = full_attention_flops(w)
-    keys_sel = sparse_keys_per_query(blk.idx, w.L, w.block) * w.Hq      # per sparse layer, all heads
+    keys_sel = sparse_keys_per_query(blk.idx[0], w.L, w.block) * w.Hq   # per sparse layer, all heads (one set)
     fl_sparse = 4.0 * w.D * keys_sel
     win_keys = sum(min(i + 1, w.window) for i in range(w.L)) * w.Hq * w.B
     fl_swa = 4.0 * w.D * win_keys

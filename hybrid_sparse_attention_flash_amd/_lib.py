@@ -11,13 +11,13 @@ LIB_PATH = os.path.join(HERE, "libhys.so")
 
 HYS_OK = 0
 HYS_F32, HYS_BF16, HYS_FP8_E4M3 = 0, 1, 2
-HYS_SCORE_NONE, HYS_SCORE_BLOCK, HYS_SCORE_TILE_TOKEN = 0, 1, 2
+HYS_SCORE_NONE, HYS_SCORE_BLOCK, HYS_SCORE_TILE_TOKEN, HYS_SCORE_BLOCK_GROUP = 0, 1, 2, 3
 
 # every symbol include/hys.h declares
 EXPORTED = (
     "hys_full_attn_fwd", "hys_select_topk", "hys_sparse_attn_fwd", "hys_swa_gate_fwd",
-    "hys_decode_step", "hys_sparse_layer_fwd", "hys_kv_bridge_fwd", "hys_hysparse_decode_step", "hys_last_error",
-    "hys_status_string",
+    "hys_decode_step", "hys_sparse_layer_fwd", "hys_kv_bridge_fwd", "hys_hysparse_decode_step",
+    "hys_select_topk_blocks", "hys_last_error", "hys_status_string",
     "hys_abi_version",
 )
 
@@ -38,7 +38,7 @@ class HysScoreParams(ctypes.Structure):
 class HysSparseParams(ctypes.Structure):
     _fields_ = [("granularity", ctypes.c_int32), ("k", ctypes.c_int32), ("q_tile", ctypes.c_int32),
                 ("forced_window", ctypes.c_int32), ("idx_batch_stride", ctypes.c_int64),
-                ("idx_row_stride", ctypes.c_int64)]
+                ("idx_row_stride", ctypes.c_int64), ("idx_group_stride", ctypes.c_int64)]
 
 
 class HysDecodeParams(ctypes.Structure):
@@ -83,11 +83,14 @@ def load(path: str = LIB_PATH):
     lib.hys_sparse_layer_fwd.argtypes = [P(HysAttnParams), T4, T4, T4, P(HysSparseParams), vp, T4, T4,
                                          ctypes.c_int32, vp, vp, T4, vp]
     lib.hys_kv_bridge_fwd.argtypes = [P(HysBridgeParams), T4, vp, vp, T4, T4, vp, vp]
+    lib.hys_select_topk_blocks.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                           ctypes.c_int32, vp, vp, P(sz), vp]
     lib.hys_hysparse_decode_step.argtypes = [P(HysHsDecodeParams), T4, T4, T4, P(ctypes.c_int64), T4, vp, vp,
                                              ctypes.c_int32, P(T4), P(T4), P(T4), P(T4), P(T4), P(vp), P(T4), vp,
                                              P(sz), vp]
     for name in ("hys_full_attn_fwd", "hys_select_topk", "hys_sparse_attn_fwd", "hys_swa_gate_fwd",
-                 "hys_decode_step", "hys_sparse_layer_fwd", "hys_kv_bridge_fwd", "hys_hysparse_decode_step"):
+                 "hys_decode_step", "hys_sparse_layer_fwd", "hys_kv_bridge_fwd", "hys_hysparse_decode_step",
+                 "hys_select_topk_blocks"):
         getattr(lib, name).restype = ctypes.c_int
     lib.hys_last_error.restype = ctypes.c_char_p
     lib.hys_last_error.argtypes = []

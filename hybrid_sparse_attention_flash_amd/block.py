@@ -23,39 +23,52 @@ from . import ops
 
 
 class HySparseBlock:
-    """One HySparse hybrid block: 1 full layer + N gated sparse layers."""
+    """One HySparse hybrid block: 1 full layer + N gated sparse layers.
+
+    selection: "all_heads" (one index set per query from the max over all
+    query heads) or "kv_group" (one index set per query and KV group from the
+    max over that group's heads; the ablation variant of the head reduction)."""
 
     def __init__(self, B, L, Hq, Hkv, D, n_sparse, topk, window=128, block=64, device="cuda",
-                 out_dtype=torch.float32, softmax_scale=None, fused=True):
+                 out_dtype=torch.float32, softmax_scale=None, fused=True, selection="all_heads"):
+        if selection not in ("all_heads", "kv_group"):
+            raise ValueError(f"unknown selection {selection!r}")
         self.B, self.L, self.Hq, self.Hkv, self.D = B, L, Hq, Hkv, D
         self.n_sparse, self.topk, self.window, self.block = n_sparse, topk, window, block
         self.scale = softmax_scale
         self.fused = fused
+        self.selection = selection
         nblk = (L + block - 1) // block
+        ng = Hkv if selection == "kv_group" else 1
         f32 = dict(dtype=torch.float32, device=device)
         self.o_full = torch.empty(B, L, Hq, D, dtype=out_dtype, device=device)
         self.lse = torch.empty(B, Hq, L, **f32)
-        self.scores = torch.empty(B, L, nblk, **f32)
-        self.idx = torch.empty(B, L, topk, dtype=torch.int32, device=device)
-        self.count = torch.empty(B * L, dtype=torch.int32, device=device)
+        self.scores = torch.empty(ng, B, L, nblk, **f32)
+        self.idx = torch.empty(ng, B, L, topk, dtype=torch.int32, device=device)
+        self.count = torch.empty(ng * B * L, dtype=torch.int32, device=device)
         # the two-call form's intermediate sparse branch
         self.o_sp = None if fused else torch.empty(B, L, Hq, D, **f32)
         self.lse_sp = None if fused else torch.empty(B, Hq, L, **f32)
         self.o_layers = [torch.empty(B, L, Hq, D, dtype=out_dtype, device=device) for _ in range(n_sparse)]
 
     def full(self, q0, k, v):
-        ops.hys_full_attn_fwd(q0, k, v, self.o_full, self.lse, "block", self.scores, softmax_scale=self.scale)
+        mode = "block_group" if self.selection == "kv_group" else "block"
+        ops.hys_full_attn_fwd(q0, k, v, self.o_full, self.lse, mode, self.scores, softmax_scale=self.scale)
 
     def select(self):
-        B, L = self.B, self.L
-        ops.hys_select_topk(self.scores.view(B * L, -1), self.topk, self.idx.view(B * L, self.topk), self.count)
+        rows = self.scores.shape[0] * self.B * self.L
+        ops.hys_select_topk(self.scores.view(rows, -1), self.topk, self.idx.view(rows, self.topk), self.count)
+
+    def _idx(self):
+        # per-group index sets as [Hkv, B, L, k]; one set as [B, L, k]
+        return self.idx if self.selection == "kv_group" else self.idx[0]
 
     def sparse_layer(self, l, q, k, v, kw, vw, gate_w):
         if self.fused:
-            ops.hys_sparse_layer_fwd(q, k, v, self.idx, kw, vw, self.window, gate_w, self.o_layers[l], topk=self.topk,
-                                     softmax_scale=self.scale)
+            ops.hys_sparse_layer_fwd(q, k, v, self._idx(), kw, vw, self.window, gate_w, self.o_layers[l],
+                                     topk=self.topk, softmax_scale=self.scale)
             return
-        ops.hys_sparse_attn_fwd(q, k, v, self.idx, self.o_sp, self.lse_sp, granularity=self.block,
+        ops.hys_sparse_attn_fwd(q, k, v, self._idx(), self.o_sp, self.lse_sp, granularity=self.block,
                                 topk=self.topk, q_tile=1, softmax_scale=self.scale)
         ops.hys_swa_gate_fwd(q, kw, vw, self.window, self.o_sp, self.lse_sp, gate_w, self.o_layers[l],
                              softmax_scale=self.scale)
@@ -69,13 +82,25 @@ class HySparseBlock:
 
 
 class HySparse2Block:
-    """One HySparse2 hybrid block (prefill): 1 full layer + N token-sparse layers."""
+    """One HySparse2 hybrid block (prefill): 1 full layer + N token-sparse layers.
+
+    Ablation switches (the comparisons of the HySparse2 pages):
+      window_mode "forced" (the recent window joins the selected set) or
+        "gated" (a sliding-window branch over the same cache fused by the
+        sigmoid gate, as in HySparse; needs gate weights per layer);
+      selection "token" (top-k tokens per 64-query tile) or "block" (the top
+        k/64 blocks of the same scores, expanded to tokens: equal budget)."""
 
     def __init__(self, B, L, Hq, Hkv, D, n_sparse, topk=1024, window=128, tile=64, device="cuda",
-                 out_dtype=torch.float32, softmax_scale=None):
+                 out_dtype=torch.float32, softmax_scale=None, window_mode="forced", selection="token"):
+        if window_mode not in ("forced", "gated") or selection not in ("token", "block"):
+            raise ValueError(f"unknown window_mode {window_mode!r} or selection {selection!r}")
+        if selection == "block" and topk % 64 != 0:
+            raise ValueError("block selection needs a budget that is a multiple of 64 tokens")
         self.B, self.L, self.Hq, self.Hkv, self.D = B, L, Hq, Hkv, D
         self.n_sparse, self.topk, self.window, self.tile = n_sparse, topk, window, tile
         self.scale = softmax_scale
+        self.window_mode, self.selection = window_mode, selection
         ntile = (L + tile - 1) // tile
         f32 = dict(dtype=torch.float32, device=device)
         self.o_full = torch.empty(B, L, Hq, D, dtype=out_dtype, device=device)
@@ -84,6 +109,7 @@ class HySparse2Block:
         self.idx = torch.empty(B, ntile, topk, dtype=torch.int32, device=device)
         self.count = torch.empty(B * ntile, dtype=torch.int32, device=device)
         self.lse_sp = torch.empty(B, Hq, L, **f32)
+        self.o_sp = torch.empty(B, L, Hq, D, **f32) if window_mode == "gated" else None
         self.o_layers = [torch.empty(B, L, Hq, D, dtype=out_dtype, device=device) for _ in range(n_sparse)]
 
     def full(self, q0, k, v, k_scale=1.0, v_scale=1.0):
@@ -92,18 +118,31 @@ class HySparse2Block:
 
     def select(self):
         B, nt = self.B, self.scores.shape[1]
-        ops.hys_select_topk(self.scores.view(B * nt, -1), self.topk, self.idx.view(B * nt, self.topk), self.count)
+        if self.selection == "block":
+            ops.hys_select_topk_blocks(self.scores.view(B * nt, -1), self.topk // 64, self.idx.view(B * nt, self.topk))
+        else:
+            ops.hys_select_topk(self.scores.view(B * nt, -1), self.topk, self.idx.view(B * nt, self.topk), self.count)
 
-    def sparse_layer(self, l, q, k, v, k_scale=1.0, v_scale=1.0):
-        ops.hys_sparse_attn_fwd(q, k, v, self.idx, self.o_layers[l], self.lse_sp, granularity=1, topk=self.topk,
-                                q_tile=self.tile, forced_window=self.window, softmax_scale=self.scale,
+    def sparse_layer(self, l, q, k, v, k_scale=1.0, v_scale=1.0, gate_w=None):
+        if self.window_mode == "forced":
+            ops.hys_sparse_attn_fwd(q, k, v, self.idx, self.o_layers[l], self.lse_sp, granularity=1, topk=self.topk,
+                                    q_tile=self.tile, forced_window=self.window, softmax_scale=self.scale,
+                                    k_scale=k_scale, v_scale=v_scale)
+            return
+        if gate_w is None:
+            raise ValueError("the gated window needs gate weights")
+        ops.hys_sparse_attn_fwd(q, k, v, self.idx, self.o_sp, self.lse_sp, granularity=1, topk=self.topk,
+                                q_tile=self.tile, forced_window=0, softmax_scale=self.scale,
                                 k_scale=k_scale, v_scale=v_scale)
+        ops.hys_swa_gate_fwd(q, k, v, self.window, self.o_sp, self.lse_sp, gate_w, self.o_layers[l],
+                             softmax_scale=self.scale, k_scale=k_scale, v_scale=v_scale)
 
-    def run(self, q_layers, k, v, k_scale=1.0, v_scale=1.0):
+    def run(self, q_layers, k, v, k_scale=1.0, v_scale=1.0, gate_layers=None):
         self.full(q_layers[0], k, v, k_scale, v_scale)
         self.select()
         for l in range(self.n_sparse):
-            self.sparse_layer(l, q_layers[l + 1], k, v, k_scale, v_scale)
+            self.sparse_layer(l, q_layers[l + 1], k, v, k_scale, v_scale,
+                              gate_layers[l] if gate_layers is not None else None)
         return self
 
 

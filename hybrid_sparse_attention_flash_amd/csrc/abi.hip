@@ -184,7 +184,8 @@ hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
     if ((s = check_out(o, q, "o")) != HYS_OK) return s;
     if (!ws_bytes) return fail(HYS_ERR_INVALID_ARG, "ws_bytes must not be null");
     const int mode_in = sp ? sp->mode : HYS_SCORE_NONE;
-    if (mode_in != HYS_SCORE_NONE && mode_in != HYS_SCORE_BLOCK && mode_in != HYS_SCORE_TILE_TOKEN)
+    if (mode_in != HYS_SCORE_NONE && mode_in != HYS_SCORE_BLOCK && mode_in != HYS_SCORE_TILE_TOKEN &&
+        mode_in != HYS_SCORE_BLOCK_GROUP)
       return fail(HYS_ERR_INVALID_ARG, "unknown score mode %d", mode_in);
     if (mode_in != HYS_SCORE_NONE) {
       if (sp->size != 64) return fail(HYS_ERR_UNSUPPORTED, "score size must be 64 (got %d)", sp->size);
@@ -219,7 +220,7 @@ hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
       if (wgs > 0x7fffffff) return fail(HYS_ERR_UNSUPPORTED, "too many query tiles x head chunks (%lld)", (long long)wgs);
       grid = (int)wgs;
     } else {
-      mode = mode_in == HYS_SCORE_BLOCK ? hys::M_FULL_BLOCK : hys::M_FULL;
+      mode = (mode_in == HYS_SCORE_BLOCK || mode_in == HYS_SCORE_BLOCK_GROUP) ? hys::M_FULL_BLOCK : hys::M_FULL;
       if (G > rows) return fail(HYS_ERR_UNSUPPORTED, "more than %d query heads per KV head", rows);
       a.HC = (int)G;
       a.BQ = (int)(rows / G);
@@ -228,7 +229,8 @@ hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
       if (mode == hys::M_FULL_BLOCK) {
         a.nblk = (int)nblk;
         a.sc_sb = L * nblk; a.sc_sr = nblk;
-        if (Hkv > 1) { a.scores = (float*)ws; a.sc_sg = B * L * nblk; }
+        if (mode_in == HYS_SCORE_BLOCK_GROUP) { a.scores = scores; a.sc_sg = B * L * nblk; }   // one matrix per group
+        else if (Hkv > 1) { a.scores = (float*)ws; a.sc_sg = B * L * nblk; }
         else { a.scores = scores; a.sc_sg = 0; }
       }
       grid = (int)(B * a.ntq * Hkv);
@@ -245,7 +247,7 @@ hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
       e = hys::launch_tile_scores(a.scores, (int)B, a.ntq, a.BQ, (int)L, (int)L, a.sc_sb, a.sc_sr, 1, st);
       if (e != hipSuccess) return hip_status(e, "score decode launch");
     }
-    if (mode == hys::M_FULL_BLOCK && Hkv > 1) {
+    if (mode == hys::M_FULL_BLOCK && mode_in == HYS_SCORE_BLOCK && Hkv > 1) {
       e = hys::launch_reduce_max((const float*)ws, (int)Hkv, B * L * nblk, scores, B * L * nblk, st);
       if (e != hipSuccess) return hip_status(e, "score reduction launch");
     }
@@ -311,6 +313,46 @@ hys_status setup_block_selection(hys::AttnArgs& a, const hys_sparse_params* sp, 
 }
 
 // ---------------------------------------------------------------------------
+hys_status hys_select_topk_blocks(const float* scores, int64_t rows, int64_t cols, int64_t row_stride, int32_t block,
+                                  int32_t k_blocks, int32_t* idx, void* ws, size_t* ws_bytes, void* stream) {
+  try {
+    if (!ws_bytes) return fail(HYS_ERR_INVALID_ARG, "ws_bytes must not be null");
+    if (rows < 0 || cols < 1) return fail(HYS_ERR_INVALID_ARG, "rows must be >= 0 and cols >= 1");
+    if (row_stride < cols) return fail(HYS_ERR_INVALID_ARG, "row_stride < cols");
+    if (block != 64) return fail(HYS_ERR_UNSUPPORTED, "block must be 64");
+    if (k_blocks < 1 || k_blocks > 32) return fail(HYS_ERR_UNSUPPORTED, "k_blocks must be in [1, 32]");
+    if (cols >= (1ll << 31)) return fail(HYS_ERR_UNSUPPORTED, "cols must be below 2^31");
+    const int64_t nblk = (cols + 63) / 64;
+    {
+      const int64_t ch = hys::topk_chunk_cols();
+      if (nblk > ch && ((nblk + ch - 1) / ch) * (int64_t)k_blocks > hys::topk_max_candidates())
+        return fail(HYS_ERR_UNSUPPORTED, "rows too long for top-%d blocks", k_blocks);
+    }
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t mb = (size_t)(rows * nblk) * sizeof(float), ib = (size_t)(rows * k_blocks) * sizeof(int32_t);
+    const size_t tk = hys::topk_workspace_bytes(rows, nblk, k_blocks);
+    const size_t need = up(mb) + up(ib) + up(tk);
+    if (!ws) { *ws_bytes = need; return ok(); }
+    if (*ws_bytes < need) return fail(HYS_ERR_WORKSPACE, "workspace %zu < required %zu bytes", *ws_bytes, need);
+    if (!aligned16(ws)) return fail(HYS_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+    if (rows == 0) return ok();
+    if (!scores || !idx) return fail(HYS_ERR_INVALID_ARG, "null scores or idx");
+    char* w = (char*)ws;
+    float* M = (float*)w;
+    int32_t* blk = (int32_t*)(w + up(mb));
+    void* tkws = w + up(mb) + up(ib);
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hys::launch_block_max_rows(scores, rows, cols, row_stride, (int)nblk, M, st);
+    if (e != hipSuccess) return hip_status(e, "block maxima launch");
+    hys_status ts = topk_launch(M, rows, nblk, nblk, k_blocks, blk, nullptr, tkws, st);
+    if (ts != HYS_OK) return ts;
+    return hip_status(hys::launch_expand_blocks(blk, rows, k_blocks, cols, idx, st), "block expansion launch");
+  } catch (...) {
+    return fail(HYS_ERR_INTERNAL, "internal error");
+  }
+}
+
+// ---------------------------------------------------------------------------
 hys_status hys_sparse_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v,
                                const hys_sparse_params* sp, const int32_t* idx, hys_tensor4 o, float* lse, void* ws,
                                size_t* ws_bytes, void* stream) {
@@ -324,12 +366,15 @@ hys_status hys_sparse_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tens
     if (ws_bytes && !ws) { *ws_bytes = 0; return ok(); }
     if (sp->k < 0) return fail(HYS_ERR_INVALID_ARG, "k must be >= 0");
     if (sp->k > 0 && !idx) return fail(HYS_ERR_INVALID_ARG, "null idx");
-    if (sp->idx_row_stride < sp->k || sp->idx_batch_stride < 0)
+    if (sp->idx_row_stride < sp->k || sp->idx_batch_stride < 0 || sp->idx_group_stride < 0)
       return fail(HYS_ERR_INVALID_ARG, "idx strides too small");
+    if (sp->idx_group_stride != 0 && sp->granularity != 64)
+      return fail(HYS_ERR_UNSUPPORTED, "per-KV-group index sets need granularity 64");
     const int64_t B = q.shape[0], L = q.shape[1], Hq = q.shape[2], Hkv = k.shape[2], D = q.shape[3];
     const int64_t G = Hq / Hkv;
     hys::AttnArgs a = base_args(p, q, k, v, o, lse);
     a.idx = idx; a.idx_sb = sp->idx_batch_stride; a.idx_sr = sp->idx_row_stride; a.topk = sp->k;
+    a.idx_sg = sp->idx_group_stride;
     int mode, grid;
     if (sp->granularity == 64) {
       hys_status bs = setup_block_selection(a, sp, G, L, B, Hkv, grid);
@@ -370,7 +415,8 @@ hys_status hys_swa_gate_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4
     hys_status s;
     if ((s = check_params(p)) != HYS_OK) return s;
     if ((s = check_qkv(q, k_win, v_win, true)) != HYS_OK) return s;
-    if (k_win.dtype != q.dtype) return fail(HYS_ERR_UNSUPPORTED, "window K/V must have q's dtype");
+    if (k_win.dtype != q.dtype && !(q.dtype == HYS_BF16 && k_win.dtype == HYS_FP8_E4M3))
+      return fail(HYS_ERR_UNSUPPORTED, "window K/V must have q's dtype or be fp8 with bf16 q");
     if ((s = check_out(o, q, "o")) != HYS_OK) return s;
     if ((s = check_out(o_sparse, q, "o_sparse")) != HYS_OK) return s;
     if (o_sparse.dtype != HYS_F32) return fail(HYS_ERR_UNSUPPORTED, "o_sparse must be fp32");
@@ -423,7 +469,7 @@ hys_status hys_sparse_layer_fwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     if (sp->granularity != 64) return fail(HYS_ERR_UNSUPPORTED, "granularity must be 64");
     if (sp->k < 0) return fail(HYS_ERR_INVALID_ARG, "k must be >= 0");
     if (sp->k > 0 && !idx) return fail(HYS_ERR_INVALID_ARG, "null idx");
-    if (sp->idx_row_stride < sp->k || sp->idx_batch_stride < 0)
+    if (sp->idx_row_stride < sp->k || sp->idx_batch_stride < 0 || sp->idx_group_stride < 0)
       return fail(HYS_ERR_INVALID_ARG, "idx strides too small");
     if (!gate_w) return fail(HYS_ERR_INVALID_ARG, "null gate_w");
     if (window < 1) return fail(HYS_ERR_INVALID_ARG, "window must be >= 1");
@@ -431,6 +477,7 @@ hys_status hys_sparse_layer_fwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     const int64_t G = Hq / Hkv;
     hys::AttnArgs a = base_args(p, q, k, v, o, nullptr);
     a.idx = idx; a.idx_sb = sp->idx_batch_stride; a.idx_sr = sp->idx_row_stride; a.topk = sp->k;
+    a.idx_sg = sp->idx_group_stride;
     a.kw = k_win.ptr; a.vw = v_win.ptr; a.window = window;
     a.gate_w = gate_w; a.gate_b = gate_b;
     int grid = 0;

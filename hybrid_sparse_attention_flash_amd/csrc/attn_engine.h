@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     for (int u = tid; u < UMAX; u += 256) s_member[u] = 0ull;
     __syncthreads();
     const int nent = a.BQ * a.topk;
-    const int32_t* ib = a.idx + (int64_t)b * a.idx_sb;
+    const int32_t* ib = a.idx + (int64_t)b * a.idx_sb + (int64_t)g * a.idx_sg;
     for (int e = tid; e < nent; e += 256) {
       const int qi = e / a.topk, s = e - qi * a.topk;
       const int q = q0 + qi;

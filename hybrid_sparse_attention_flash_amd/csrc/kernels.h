@@ -38,6 +38,7 @@ struct AttnArgs {
   int nblk;
   // sparse selection
   const int32_t* idx; int64_t idx_sb, idx_sr;
+  int64_t idx_sg;            // between KV groups' index rows (0: one selection for every group)
   int topk;
   int window;
   // the layer's own window K/V (M_SPARSE_SWA; same strides as k, v)
@@ -73,6 +74,13 @@ size_t topk_workspace_bytes(int64_t rows, int64_t cols, int k);
 int64_t topk_max_candidates();
 int64_t topk_chunk_cols();
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+
+// block-level selection over token-score rows: block maxima, then the chosen
+// blocks expanded to token positions
+hipError_t launch_block_max_rows(const float* scores, int64_t rows, int64_t cols, int64_t row_stride, int nblk,
+                                 float* out, hipStream_t s);
+hipError_t launch_expand_blocks(const int32_t* blocks, int64_t rows, int kb, int64_t cols, int32_t* idx,
+                                hipStream_t s);
 
 // HySparse2 decode (one query per sequence, MQA cache).
 constexpr int kMaxDecodeLayers = 16;

@@ -11,12 +11,14 @@ from typing import List, Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import (HYS_BF16, HYS_F32, HYS_FP8_E4M3, HYS_SCORE_BLOCK, HYS_SCORE_NONE, HYS_SCORE_TILE_TOKEN,
+from ._lib import (HYS_BF16, HYS_F32, HYS_FP8_E4M3, HYS_SCORE_BLOCK, HYS_SCORE_BLOCK_GROUP, HYS_SCORE_NONE,
+                   HYS_SCORE_TILE_TOKEN,
                    HysAttnParams, HysBridgeParams, HysDecodeParams, HysHsDecodeParams, HysScoreParams, HysSparseParams, HysTensor4, check)
 
 _DT = {torch.float32: HYS_F32, torch.bfloat16: HYS_BF16, torch.uint8: HYS_FP8_E4M3,
        torch.float8_e4m3fn: HYS_FP8_E4M3}
-_SCORE = {"none": HYS_SCORE_NONE, "block": HYS_SCORE_BLOCK, "tile_token": HYS_SCORE_TILE_TOKEN}
+_SCORE = {"none": HYS_SCORE_NONE, "block": HYS_SCORE_BLOCK, "tile_token": HYS_SCORE_TILE_TOKEN,
+          "block_group": HYS_SCORE_BLOCK_GROUP}
 
 
 def tensor4(t: torch.Tensor) -> HysTensor4:
@@ -75,22 +77,38 @@ def hys_select_topk(scores: torch.Tensor, k: int, idx: torch.Tensor, count: Opti
     return ws
 
 
+def hys_select_topk_blocks(scores: torch.Tensor, k_blocks: int, idx: torch.Tensor, block: int = 64):
+    """scores: 2-D fp32 [rows, cols]; idx [rows, 64 * k_blocks] int32 contiguous: the top k_blocks blocks'
+    token positions (ascending, -1 padded)."""
+    lib = _lib.load()
+    rows, cols = scores.shape
+    args = [_ptr(scores), rows, cols, scores.stride(0) if rows > 0 else cols, block, k_blocks, _ptr(idx)]
+    nb = ctypes.c_size_t(0)
+    check(lib.hys_select_topk_blocks(*args, None, ctypes.byref(nb), None))
+    ws = _workspace(nb.value, scores.device)
+    nb = ctypes.c_size_t(ws.numel())
+    check(lib.hys_select_topk_blocks(*args, _ptr(ws), ctypes.byref(nb), _stream(scores.device)))
+    return ws
+
+
 def hys_sparse_attn_fwd(q, k, v, idx, o, lse=None, granularity: int = 64, topk: int = None, q_tile: int = 1,
                         forced_window: int = 0, softmax_scale: float = None, k_scale: float = 1.0,
                         v_scale: float = 1.0):
-    """idx: [B, R, topk] int32 (R = L for q_tile 1, ceil(L/64) for q_tile 64)."""
+    """idx: [B, R, topk] int32 (R = L for q_tile 1, ceil(L/64) for q_tile 64), or
+    [Hkv, B, L, topk] for per-KV-group index sets (granularity 64)."""
     lib = _lib.load()
     p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), k_scale, v_scale)
     kk = idx.shape[-1] if topk is None else topk
-    sp = HysSparseParams(granularity, kk, q_tile, forced_window, idx.stride(0), idx.stride(1))
+    gs, ib = (idx.stride(0), idx[0]) if idx.dim() == 4 else (0, idx)
+    sp = HysSparseParams(granularity, kk, q_tile, forced_window, ib.stride(0), ib.stride(1), gs)
     check(lib.hys_sparse_attn_fwd(ctypes.byref(p), tensor4(q), tensor4(k), tensor4(v), ctypes.byref(sp), _ptr(idx),
                                   tensor4(o), _ptr(lse), None, None, _stream(q.device)))
 
 
 def hys_swa_gate_fwd(q, k_win, v_win, window: int, o_sparse, lse_sparse, gate_w, o, gate_b=None,
-                     softmax_scale: float = None):
+                     softmax_scale: float = None, k_scale: float = 1.0, v_scale: float = 1.0):
     lib = _lib.load()
-    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), 1.0, 1.0)
+    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), k_scale, v_scale)
     check(lib.hys_swa_gate_fwd(ctypes.byref(p), tensor4(q), tensor4(k_win), tensor4(v_win), window,
                                tensor4(o_sparse), _ptr(lse_sparse), _ptr(gate_w), _ptr(gate_b), tensor4(o),
                                _stream(q.device)))
@@ -99,11 +117,12 @@ def hys_swa_gate_fwd(q, k_win, v_win, window: int, o_sparse, lse_sparse, gate_w,
 def hys_sparse_layer_fwd(q, k, v, idx, k_win, v_win, window: int, gate_w, o, gate_b=None, topk: int = None,
                          softmax_scale: float = None):
     """One HySparse sparse layer (selected blocks of k/v, own window k_win/v_win, sigmoid gate) in one call.
-    idx: [B, L, topk] int32 block ids."""
+    idx: [B, L, topk] int32 block ids, or [Hkv, B, L, topk] for per-KV-group index sets."""
     lib = _lib.load()
     p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), 1.0, 1.0)
     kk = idx.shape[-1] if topk is None else topk
-    sp = HysSparseParams(64, kk, 1, 0, idx.stride(0), idx.stride(1))
+    gs, ib = (idx.stride(0), idx[0]) if idx.dim() == 4 else (0, idx)
+    sp = HysSparseParams(64, kk, 1, 0, ib.stride(0), ib.stride(1), gs)
     check(lib.hys_sparse_layer_fwd(ctypes.byref(p), tensor4(q), tensor4(k), tensor4(v), ctypes.byref(sp), _ptr(idx),
                                    tensor4(k_win), tensor4(v_win), window, _ptr(gate_w), _ptr(gate_b), tensor4(o),
                                    _stream(q.device)))

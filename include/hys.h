@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define HYS_ABI_VERSION 1
+#define HYS_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define HYS_API __attribute__((visibility("default")))
@@ -111,7 +111,8 @@ typedef struct {
 typedef enum {
   HYS_SCORE_NONE = 0,
   HYS_SCORE_BLOCK = 1,      /* HySparse: per (query, key block) */
-  HYS_SCORE_TILE_TOKEN = 2  /* HySparse2: per (query tile, key token) */
+  HYS_SCORE_TILE_TOKEN = 2, /* HySparse2: per (query tile, key token) */
+  HYS_SCORE_BLOCK_GROUP = 3 /* per (KV group, query, key block): the max over each KV group's heads */
 } hys_score_mode;
 
 typedef struct {
@@ -126,6 +127,7 @@ typedef struct {
   int32_t forced_window;  /* granularity 1 only: the recent-token window forced into every query's set (0 = none) */
   int64_t idx_batch_stride;  /* elements between batches of idx */
   int64_t idx_row_stride;    /* elements between idx rows */
+  int64_t idx_group_stride;  /* granularity 64: elements between KV groups' index sets; 0 = one set for all */
 } hys_sparse_params;
 
 typedef struct {
@@ -154,7 +156,10 @@ typedef struct {
  *                         64-query tile), -inf for keys after the tile;
  *                         layout [B, ceil(Lq/64), Lk] contiguous.
  * The max over heads spans all query heads, so one index set serves every KV
- * head.
+ * head.  HYS_SCORE_BLOCK_GROUP instead keeps one score matrix per KV group,
+ *   scores[g,b,i,c] = max_{h in group g} max_{j in block c, j<=i} S[b,h,i,j],
+ * layout [Hkv, B, Lq, ceil(Lk/64)] contiguous (per-KV-group selection, an
+ * ablation variant of the head reduction; no workspace).
  *
  * q [B, L, Hq, D]; k, v [B, L, Hkv, D] (self-attention: Lq = Lk = L).
  * o [B, L, Hq, D] fp32 or bf16.  lse [B, Hq, L] fp32 or NULL.
@@ -185,6 +190,24 @@ HYS_API hys_status hys_select_topk(const float* scores, int64_t rows, int64_t co
                            int32_t* idx, int32_t* count, void* ws, size_t* ws_bytes, void* stream);
 
 /*
+ * hys_select_topk_blocks - block-level selection over token-score rows at a
+ * token budget (the block- vs token-level comparison at equal budget:
+ * demingchina commentary, section 03).
+ *
+ * For each row r of the fp32 score matrix (rows x cols, row_stride):
+ *   M[r,c] = max_{j in [64c, 64c+64), j < cols} scores[r,j],
+ *   the k_blocks highest M[r,:] are chosen by the hys_select_topk rule, and
+ *   idx[r,:] (rows x 64*k_blocks int32, contiguous) receives the chosen
+ *   blocks' token positions [64c, min(cols, 64c+64)) in ascending block
+ *   order, then -1.  The rows can feed hys_sparse_attn_fwd with granularity 1.
+ * block must be 64; 1 <= k_blocks <= 32.  Workspace: the block maxima, the
+ * block ids and top-k candidates (query with ws == NULL).
+ */
+HYS_API hys_status hys_select_topk_blocks(const float* scores, int64_t rows, int64_t cols, int64_t row_stride,
+                                          int32_t block, int32_t k_blocks, int32_t* idx, void* ws, size_t* ws_bytes,
+                                          void* stream);
+
+/*
  * hys_sparse_attn_fwd - a sparse layer's global attention over the shared KV.
  *
  * The sparse layer attends with its own query q to the full layer's K/V at the
@@ -196,6 +219,9 @@ HYS_API hys_status hys_select_topk(const float* scores, int64_t rows, int64_t co
  *       the 64 queries of tile t, and the most recent forced_window tokens are
  *       added (airebao HySparse2 news, forced recent window paragraph):
  *       J(i) = { j in idx[b,i/64,:] : j <= i }  U  [max(0, i-forced_window+1), i].
+ * With idx_group_stride != 0 (granularity 64 only), KV group g reads its own
+ * index set at idx + g*idx_group_stride (per-KV-group selection):
+ *       J_g(i) = { j <= i : j/64 in idx[g,b,i,:] } for the heads of group g.
  * O[b,i,h,:] = softmax over J(i) of S, applied to V; lse[b,h,i] likewise
  * (-inf when J(i) is empty, with O = 0).  Entries < 0 are ignored; entries of
  * a row must be distinct (hys_select_topk guarantees this).
@@ -217,7 +243,9 @@ HYS_API hys_status hys_sparse_attn_fwd(const hys_attn_params* p, hys_tensor4 q, 
  *   z = <q[b,i,h,:], gate_w[h,:]> (+ gate_b[h]),  g = 1/(1+exp(-z)),
  *   o = g * o_sparse + (1-g) * O_window,
  * and o = O_window where lse_sparse = -inf (empty sparse set).
- * q [B, L, Hq, D]; k_win, v_win [B, L, Hkv, D] of q's type; o_sparse fp32
+ * q [B, L, Hq, D]; k_win, v_win [B, L, Hkv, D] of q's type, or fp8 e4m3 with
+ * bf16 q (dequantised by p->k_scale, p->v_scale: a gated window over an fp8
+ * shared cache, the HySparse2 ablation of the forced window); o_sparse fp32
  * [B, L, Hq, D]; lse_sparse [B, Hq, L]; gate_w [Hq, D] fp32; gate_b [Hq] or
  * NULL; o [B, L, Hq, D] fp32 or bf16.
  */
@@ -243,7 +271,8 @@ HYS_API hys_status hys_swa_gate_fwd(const hys_attn_params* p, hys_tensor4 q, hys
  * two-call form up to fp32 rounding).
  * q [B, L, Hq, D] bf16 or fp32; k, v, k_win, v_win [B, L, Hkv, D] of q's type,
  * the window tensors with the same strides as k and v; idx and sp as for
- * hys_sparse_attn_fwd with granularity 64 (k <= 64); gate_w [Hq, D] fp32;
+ * hys_sparse_attn_fwd with granularity 64 (k <= 64; per-KV-group index sets
+ * through idx_group_stride as there); gate_w [Hq, D] fp32;
  * gate_b [Hq] fp32 or NULL; o [B, L, Hq, D] fp32 or bf16.  p->k_scale and
  * p->v_scale must be 1.  No workspace.
  */

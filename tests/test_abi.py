@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol():
     assert declared == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(lib(), name)
-    assert lib().hys_abi_version() == 1
+    assert lib().hys_abi_version() == 2
     assert lib().hys_status_string(3) == b"HYS_ERR_WORKSPACE"
 
 
@@ -87,6 +87,44 @@ def test_topk_validation():
     assert L.hys_select_topk(None, 4, 1 << 20, 1 << 20, 8192, None, None, None, ctypes.byref(nb), None) == UNSUPPORTED
     nb = ctypes.c_size_t(0)
     assert L.hys_select_topk(None, 4, 100, 100, 8, None, None, ctypes.c_void_p(FAKE), ctypes.byref(nb), None) == INVALID
+
+
+def test_select_topk_blocks_validation():
+    L = lib()
+    nb = ctypes.c_size_t(0)
+
+    def call(rows=4, cols=1000, stride=1000, block=64, kb=3, ws=None, idx=None):
+        return L.hys_select_topk_blocks(None, rows, cols, stride, block, kb, idx, ws, ctypes.byref(nb), None)
+    assert call(rows=-1) == INVALID
+    assert call(cols=0) == INVALID
+    assert call(stride=999) == INVALID
+    assert call(block=32) == UNSUPPORTED
+    assert call(kb=0) == UNSUPPORTED
+    assert call(kb=33) == UNSUPPORTED
+    # workspace: block maxima [rows, nblk] + block ids [rows, kb] + the top-k scratch, each 256-byte aligned
+    assert call() == 0
+    assert nb.value >= 256 + 256
+    need = nb.value
+    nb.value = need - 1
+    assert call(ws=ctypes.c_void_p(FAKE)) == WORKSPACE
+    nb.value = need
+    assert call(ws=ctypes.c_void_p(FAKE)) == INVALID                  # null scores / idx
+
+
+def test_group_stride_validation():
+    p = HysAttnParams(0.125, 1.0, 1.0)
+    q, kv, o = t4([1, 128, 8, 128]), t4([1, 128, 2, 128]), t4([1, 128, 8, 128], dtype=0)
+
+    def sparse(sp):
+        return lib().hys_sparse_attn_fwd(ctypes.byref(p), q, kv, kv, ctypes.byref(sp), ctypes.c_void_p(FAKE), o,
+                                         None, None, None, None)
+
+    def layer(sp):
+        return lib().hys_sparse_layer_fwd(ctypes.byref(p), q, kv, kv, ctypes.byref(sp), ctypes.c_void_p(FAKE), kv, kv,
+                                          128, ctypes.c_void_p(FAKE), None, o, None)
+    assert sparse(HysSparseParams(64, 4, 1, 0, 512, 4, -1)) == INVALID
+    assert sparse(HysSparseParams(1, 16, 64, 128, 32, 16, 64)) == UNSUPPORTED          # per-group sets need blocks
+    assert layer(HysSparseParams(64, 4, 1, 0, 512, 4, -1)) == INVALID
 
 
 def test_sparse_validation():

@@ -62,8 +62,8 @@ def _hysparse_case(name, nrows, seed=0):
     r = torch.as_tensor(rows)
     check_out(blk.o_full[0][r].cpu().numpy(), ref["o_full"], w.q_dtype, "o_full")
     assert max_abs(blk.lse[0][:, r].cpu().numpy(), ref["lse"]) <= max(tol, 1e-3)
-    check_scores(blk.scores[0][r].cpu().numpy(), ref["scores"])
-    gidx = blk.idx[0][r].cpu().numpy()
+    check_scores(blk.scores[0, 0][r].cpu().numpy(), ref["scores"])
+    gidx = blk.idx[0, 0][r].cpu().numpy()
     same, inband = check_topk_band(gidx, ref["sel"], ref["scores"], w.topk)
     eq = np.array([np.array_equal(gidx[i], ref["sel"][i]) for i in range(len(rows))])
     print(f"workload {name}: top-k rows identical {same}, inside the tie band {inband}", flush=True)

@@ -38,7 +38,7 @@ def test_per_group_scores_brute_force():
                     for j in range(c * blk, min(L, (c + 1) * blk)):
                         if j <= i:
                             best = max(best, 0.7 * sum(q[i, h, d] * k[j, g, d] for d in range(D)))
-                assert abs(Mg[g, i, c] - best) < 1e-12 or (best == -math.inf and Mg[g, i, c] == -math.inf)
+                assert (best == -math.inf and Mg[g, i, c] == -math.inf) or abs(Mg[g, i, c] - best) < 1e-12
 
 
 def test_grouped_sparse_with_equal_sets_is_the_shared_branch():
