@@ -205,8 +205,11 @@ def bench_prefill2(args, dev, name):
     k, ks = synth.gen_kv(w, "k")
     v, vs = synth.gen_kv(w, "v")
     k, v = k.to(dev), v.to(dev)
+    wmode = args.window_mode
+    sel = "block" if args.selection == "block" else "token"
     blk = HySparse2Block(w.B, w.L, w.Hq, w.Hkv, w.D, w.n_sparse, w.topk, w.window, tile=w.block, device=dev,
-                         out_dtype=torch.bfloat16)
+                         out_dtype=torch.bfloat16, window_mode=wmode, selection=sel)
+    gw = [synth.gen_gate_w(w, l + 1).to(dev) for l in range(w.n_sparse)] if wmode == "gated" else None
 
     def run(timer=None):
         def rec(nm, fn):
@@ -218,7 +221,7 @@ def bench_prefill2(args, dev, name):
         rec("full_attn+scores", lambda: blk.full(q[0], k, v, ks, vs))
         rec("select_topk", blk.select)
         for l in range(w.n_sparse):
-            rec("sparse_layer", lambda: blk.sparse_layer(l, q[l + 1], k, v, ks, vs))
+            rec("sparse_layer", lambda: blk.sparse_layer(l, q[l + 1], k, v, ks, vs, gw[l] if gw else None))
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
@@ -235,7 +238,12 @@ def bench_prefill2(args, dev, name):
     per_step = {kk: vv / args.steps for kk, vv in tot.items()}
     launches = {kk: c // args.steps for kk, c in timer.counts().items()}
     fl_full = full_attention_flops(w)
-    fl_layer = 4.0 * w.D * w.Hq * token_sparse_keys(blk.idx, w.L, w.window)
+    if wmode == "gated":
+        # selected tokens only in the sparse branch, plus the gated window branch's pairs
+        win_pairs = sum(min(i + 1, w.window) for i in range(w.L)) * w.B
+        fl_layer = 4.0 * w.D * w.Hq * (token_sparse_keys(blk.idx, w.L, 0) + win_pairs)
+    else:
+        fl_layer = 4.0 * w.D * w.Hq * token_sparse_keys(blk.idx, w.L, w.window)
     stages = {kk: {"ms_per_step": round(per_step[kk], 4), "launches_per_step": launches[kk]} for kk in per_step}
     for kk, fl in (("full_attn+scores", fl_full), ("sparse_layer", w.n_sparse * fl_layer)):
         tf = fl / (per_step[kk] * 1e-3) / 1e12
@@ -246,7 +254,8 @@ def bench_prefill2(args, dev, name):
     work = fl_full if dom == "full_attn+scores" else fl_layer
     ach = work / (avg * 1e-3) / 1e12
     roof = {"kernel": "full_attn (causal + tile-token scores)" if dom == "full_attn+scores"
-            else "sparse_layer (selected tokens U forced window, fp8 KV)", "bound": "mfma",
+            else ("sparse_layer (selected tokens U forced window, fp8 KV)" if wmode == "forced" else
+                  "sparse_layer (selected tokens, then gated window branch: 2 launches, fp8 KV)"), "bound": "mfma",
             "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(ach / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(avg, 4),
             "work_per_launch": f"{work:.4g} FLOP (4*D per visible (query, head, key) pair)", "traffic": None}
@@ -271,7 +280,7 @@ def bench_prefill(args, dev):
     inp = ([x.to(dev) for x in q_h], k_h.to(dev), v_h.to(dev), [x.to(dev) for x in kw_h],
            [x.to(dev) for x in vw_h], [x.to(dev) for x in gw_h])
     blk = HySparseBlock(w.B, w.L, w.Hq, w.Hkv, w.D, w.n_sparse, w.topk, w.window, device=dev,
-                        out_dtype=torch.bfloat16)
+                        out_dtype=torch.bfloat16, selection="kv_group" if args.selection == "kv_group" else "all_heads")
     for i in range(args.warmup):
         run_block(blk, inp)
         torch.cuda.synchronize()
@@ -295,7 +304,10 @@ def bench_prefill(args, dev):
 
     # algorithmic work of the step
     fl_full = full_attention_flops(w)
-    keys_sel = sparse_keys_per_query(blk.idx[0], w.L, w.block) * w.Hq   # per sparse layer, all heads (one set)
+    # visible selected keys per sparse layer over all heads: one set for every
+    # head, or one set per KV group serving that group's G heads
+    ng = blk.idx.shape[0]
+    keys_sel = sum(sparse_keys_per_query(blk.idx[g], w.L, w.block) for g in range(ng)) * (w.Hq // ng)
     fl_sparse = 4.0 * w.D * keys_sel
     win_keys = sum(min(i + 1, w.window) for i in range(w.L)) * w.Hq * w.B
     fl_swa = 4.0 * w.D * win_keys
@@ -328,7 +340,8 @@ def bench_prefill(args, dev):
             "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(ach / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(avg, 4),
             "work_per_launch": f"{work:.4g} FLOP (4*D per visible (query, head, key) pair)", "traffic": None}
-    if dom == "sparse_layer" and TRAFFIC and TRAFFIC["sources_sha1"] == kernel_sources_sha1():
+    if (dom == "sparse_layer" and args.selection == "default" and TRAFFIC
+            and TRAFFIC["sources_sha1"] == kernel_sources_sha1()):
         roof["traffic"] = TRAFFIC["bytes_per_launch"]
     if dom == "sparse_layer":
         roof["logical_gather_GBs"] = round(gather_bytes / (avg * 1e-3) / 1e9, 1)
@@ -478,9 +491,20 @@ def main():
     ap.add_argument("--workload", default="moe80b_32k",
                     choices=["moe80b_32k", "dense7b_16k", "hysparse2_64k", "tiny_fp32"],
                     help="prefill block to time (default: the 32k HySparse block the metric is quoted on)")
+    ap.add_argument("--selection", default="default", choices=["default", "kv_group", "block"],
+                    help="ablation: per-KV-group block selection (HySparse) or block-level selection at the "
+                         "token budget (HySparse2)")
+    ap.add_argument("--window-mode", default="forced", choices=["forced", "gated"],
+                    help="HySparse2 ablation: gated window branch instead of the forced recent window")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain copy of known size (for scaling HBM byte counters)")
     args = ap.parse_args()
+    v2 = synth.WORKLOADS[args.workload].variant == "hysparse2"
+    if (args.selection == "kv_group" and v2) or ((args.selection == "block" or args.window_mode == "gated")
+                                                 and not v2):
+        print("--selection kv_group applies to the HySparse workloads; --selection block and --window-mode gated "
+              "to the HySparse2 workload", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the hot path is built for a single MI355X and has no "
               "multi-GPU mode (see DESIGN.md for how it would shard).", file=sys.stderr)
@@ -504,7 +528,8 @@ def main():
     bridge = None if args.no_bridge else bench_bridge(args, dev)
     hs_dec = None if args.no_hs_decode else bench_hs_decode(args, dev)
     cpu = None
-    if not args.no_cpu and pre["host"] is not None:
+    ablation = args.selection != "default" or args.window_mode != "forced"
+    if not args.no_cpu and not ablation and pre["host"] is not None:
         log(f"[bench] timing the CPU oracle on {args.cpu_rows} sampled rows")
         cpu = cpu_baseline(w, pre["host"], args.cpu_rows)
         log(f"[bench] oracle: {cpu['value']:.2f} tokens/s on {cpu['cores']} threads")
@@ -519,7 +544,9 @@ def main():
                    "head_dim": w.D, "layers": f"1 full + {w.n_sparse} sparse",
                    "selection": (f"top-{w.topk} of {w.block}-token blocks per query" if w.variant == "hysparse"
                                  else f"top-{w.topk} tokens per {w.block}-query tile"),
-                   "window": w.window},
+                   "window": w.window,
+                   **({"ablation": {"selection": args.selection, "window_mode": args.window_mode}}
+                      if args.selection != "default" or args.window_mode != "forced" else {})},
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,
         "stages": pre["stages"],

@@ -86,6 +86,22 @@ def test_gated_window_special_cases():
     assert live.any() and (~live).any()
     np.testing.assert_allclose(o[live], 0.5 * (o_sp + o_w)[live], rtol=0, atol=1e-12)
     np.testing.assert_allclose(o[~live], o_w[~live], rtol=0, atol=1e-12)
+    # a saturated gate picks one branch: with q[..., 0] = 1 and w = +-60 e_0,
+    # g = sigmoid(+-60) is 1 (sparse branch) or 0 (window branch) to 1e-26
+    q1 = q.copy()
+    q1[:, :, 0] = 1.0
+    T1 = hs.tile_token_scores(q1, k, 0.25, tile)
+    sel1, _ = hs.topk_rows(T1, 32)
+    o_sp1, lse_sp1 = hs.sparse_token_attention(q1, k, v, 0.25, sel1, tile, 0)
+    o_w1, _ = hs.window_attention(q1, k, v, 0.25, W)
+    live1 = np.isfinite(lse_sp1.T)
+    e0 = np.zeros((Hq, D))
+    e0[:, 0] = 60.0
+    o = hs.hysparse2_gated_window_layer(q1, k, v, 0.25, sel1, tile, W, e0)
+    np.testing.assert_allclose(o[live1], o_sp1[live1], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o[~live1], o_w1[~live1], rtol=0, atol=1e-12)
+    o = hs.hysparse2_gated_window_layer(q1, k, v, 0.25, sel1, tile, W, -e0)
+    np.testing.assert_allclose(o, o_w1, rtol=0, atol=1e-12)
     # nothing selected: the window branch alone
     none = np.full_like(sel, -1)
     o = hs.hysparse2_gated_window_layer(q, k, v, 0.25, none, tile, W, np.ones((Hq, D)))
