@@ -18,7 +18,9 @@ invariants, hand-derived golden values under tests/golden/, the fp8
 decode table against torch.float8_e4m3fn, the fp8 encoder of the KV
 Bridging projection (bridge.py) against torch's CPU float8 conversion, and
 the HySparse decode step with ring window caches (hysparse_decode.py)
-against the prefill block evaluated at its last row.
+against the prefill block evaluated at its last row, and the backward pass
+(hysparse_bwd.py) against central finite differences of the forward
+definitions.
 
 Parity unpinned (against the real HySparse/HySparse2, whose pages leave these
 open): the head reduction of importance scores (max over all query heads),
@@ -27,7 +29,7 @@ sparse set rule, the per-tile token-score reading, the per-query forced
 window and the decode-time ring window cache.  They are pinned only to this
 package's stated readings.
 """
-from . import bridge, fp8, hysparse_decode  # noqa: F401
+from . import bridge, fp8, hysparse_bwd, hysparse_decode  # noqa: F401
 from .hysparse import (  # noqa: F401
     NEG_INF, attend, block_scores, block_scores_per_group, decode_full, decode_sparse, decode_step,
     expand_blocks, full_attention, gate_merge, hysparse2_block, hysparse2_gated_window_layer, hysparse_block,
