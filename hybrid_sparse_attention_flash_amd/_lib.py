@@ -17,8 +17,8 @@ HYS_SCORE_NONE, HYS_SCORE_BLOCK, HYS_SCORE_TILE_TOKEN, HYS_SCORE_BLOCK_GROUP = 0
 EXPORTED = (
     "hys_full_attn_fwd", "hys_select_topk", "hys_sparse_attn_fwd", "hys_swa_gate_fwd",
     "hys_decode_step", "hys_sparse_layer_fwd", "hys_kv_bridge_fwd", "hys_hysparse_decode_step",
-    "hys_select_topk_blocks", "hys_last_error", "hys_status_string",
-    "hys_abi_version",
+    "hys_select_topk_blocks", "hys_window_attn_fwd", "hys_full_attn_bwd", "hys_sparse_layer_bwd",
+    "hys_last_error", "hys_status_string", "hys_abi_version",
 )
 
 
@@ -88,9 +88,15 @@ def load(path: str = LIB_PATH):
     lib.hys_hysparse_decode_step.argtypes = [P(HysHsDecodeParams), T4, T4, T4, P(ctypes.c_int64), T4, vp, vp,
                                              ctypes.c_int32, P(T4), P(T4), P(T4), P(T4), P(T4), P(vp), P(T4), vp,
                                              P(sz), vp]
+    lib.hys_window_attn_fwd.argtypes = [P(HysAttnParams), T4, T4, T4, ctypes.c_int32, T4, vp, vp]
+    lib.hys_full_attn_bwd.argtypes = [P(HysAttnParams), T4, T4, T4, T4, vp, T4, T4, T4, T4, ctypes.c_int32, vp,
+                                      P(sz), vp]
+    lib.hys_sparse_layer_bwd.argtypes = [P(HysAttnParams), T4, T4, T4, P(HysSparseParams), vp, T4, T4,
+                                         ctypes.c_int32, vp, vp, T4, vp, T4, vp, T4, T4, T4, T4, ctypes.c_int32, T4,
+                                         T4, vp, vp, P(sz), vp]
     for name in ("hys_full_attn_fwd", "hys_select_topk", "hys_sparse_attn_fwd", "hys_swa_gate_fwd",
                  "hys_decode_step", "hys_sparse_layer_fwd", "hys_kv_bridge_fwd", "hys_hysparse_decode_step",
-                 "hys_select_topk_blocks"):
+                 "hys_select_topk_blocks", "hys_window_attn_fwd", "hys_full_attn_bwd", "hys_sparse_layer_bwd"):
         getattr(lib, name).restype = ctypes.c_int
     lib.hys_last_error.restype = ctypes.c_char_p
     lib.hys_last_error.argtypes = []

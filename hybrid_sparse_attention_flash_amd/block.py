@@ -81,6 +81,61 @@ class HySparseBlock:
         return self
 
 
+class HySparseTrainer:
+    """Forward and backward of one HySparse block for training.
+
+    The forward keeps what the backward needs: the full layer's O and LSE,
+    the selection, and per sparse layer the two branches' O (fp32) and LSE
+    (the sparse branch from hys_sparse_attn_fwd, the window branch from
+    hys_window_attn_fwd), then merges them with hys_swa_gate_fwd.  The
+    backward runs the full layer's gradient first (it writes dK, dV of the
+    shared cache) and every sparse layer's after it (each adds its sparse
+    branch's share), so dk, dv hold the block's total gradient."""
+
+    def __init__(self, B, L, Hq, Hkv, D, n_sparse, topk, window=128, device="cuda", softmax_scale=None,
+                 selection="all_heads"):
+        self.fwd = HySparseBlock(B, L, Hq, Hkv, D, n_sparse, topk, window, device=device, out_dtype=torch.bfloat16,
+                                 softmax_scale=softmax_scale, fused=True, selection=selection)
+        self.scale = softmax_scale
+        self.window = window
+        f32 = dict(dtype=torch.float32, device=device)
+        self.o_sp = [torch.empty(B, L, Hq, D, **f32) for _ in range(n_sparse)]
+        self.lse_sp = [torch.empty(B, Hq, L, **f32) for _ in range(n_sparse)]
+        self.o_w = [torch.empty(B, L, Hq, D, **f32) for _ in range(n_sparse)]
+        self.lse_w = [torch.empty(B, Hq, L, **f32) for _ in range(n_sparse)]
+        self.dq = [torch.empty(B, L, Hq, D, **f32) for _ in range(n_sparse + 1)]
+        self.dk = torch.empty(B, L, Hkv, D, **f32)
+        self.dv = torch.empty(B, L, Hkv, D, **f32)
+        self.dkw = [torch.empty(B, L, Hkv, D, **f32) for _ in range(n_sparse)]
+        self.dvw = [torch.empty(B, L, Hkv, D, **f32) for _ in range(n_sparse)]
+        self.dgate_w = [torch.empty(Hq, D, **f32) for _ in range(n_sparse)]
+
+    def forward(self, q_layers, k, v, kw_layers, vw_layers, gate_layers):
+        f = self.fwd
+        f.full(q_layers[0], k, v)
+        f.select()
+        for l in range(f.n_sparse):
+            q = q_layers[l + 1]
+            ops.hys_sparse_attn_fwd(q, k, v, f._idx(), self.o_sp[l], self.lse_sp[l], granularity=64, topk=f.topk,
+                                    softmax_scale=self.scale)
+            ops.hys_window_attn_fwd(q, kw_layers[l], vw_layers[l], self.window, self.o_w[l], self.lse_w[l],
+                                    softmax_scale=self.scale)
+            ops.hys_swa_gate_fwd(q, kw_layers[l], vw_layers[l], self.window, self.o_sp[l], self.lse_sp[l],
+                                 gate_layers[l], f.o_layers[l], softmax_scale=self.scale)
+        return self
+
+    def backward(self, q_layers, k, v, kw_layers, vw_layers, gate_layers, do_full, do_layers):
+        f = self.fwd
+        ops.hys_full_attn_bwd(q_layers[0], k, v, f.o_full, f.lse, do_full, self.dq[0], self.dk, self.dv,
+                              accumulate_kv=False, softmax_scale=self.scale)
+        for l in range(f.n_sparse):
+            ops.hys_sparse_layer_bwd(q_layers[l + 1], k, v, f._idx(), kw_layers[l], vw_layers[l], self.window,
+                                     gate_layers[l], self.o_sp[l], self.lse_sp[l], self.o_w[l], self.lse_w[l],
+                                     do_layers[l], self.dq[l + 1], self.dk, self.dv, self.dkw[l], self.dvw[l],
+                                     self.dgate_w[l], accumulate_kv=True, topk=f.topk, softmax_scale=self.scale)
+        return self
+
+
 class HySparse2Block:
     """One HySparse2 hybrid block (prefill): 1 full layer + N token-sparse layers.
 

@@ -10,6 +10,7 @@
 #include <string>
 
 #include "../../include/hys.h"
+#include "bwd.h"
 #include "kernels.h"
 
 namespace {
@@ -839,6 +840,239 @@ hys_status hys_hysparse_decode_step(const hys_hs_decode_params* p, hys_tensor4 q
       if (e != hipSuccess) return hip_status(e, "sparse layer launch");
     }
     return ok();
+  } catch (...) {
+    return fail(HYS_ERR_INTERNAL, "internal error");
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// backward pass
+// ---------------------------------------------------------------------------
+hys_status hys_window_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k_win, hys_tensor4 v_win,
+                               int32_t window, hys_tensor4 o, float* lse, void* stream) {
+  try {
+    hys_status s;
+    if ((s = check_params(p)) != HYS_OK) return s;
+    if ((s = check_qkv(q, k_win, v_win, true)) != HYS_OK) return s;
+    if (k_win.dtype != q.dtype && !(q.dtype == HYS_BF16 && k_win.dtype == HYS_FP8_E4M3))
+      return fail(HYS_ERR_UNSUPPORTED, "window K/V must have q's dtype or be fp8 with bf16 q");
+    if ((s = check_out(o, q, "o")) != HYS_OK) return s;
+    if (window < 1) return fail(HYS_ERR_INVALID_ARG, "window must be >= 1");
+    const int64_t B = q.shape[0], L = q.shape[1], Hq = q.shape[2], Hkv = k_win.shape[2], D = q.shape[3];
+    const int64_t G = Hq / Hkv;
+    if (L == 0) return ok();
+    hys::AttnArgs a = base_args(p, q, k_win, v_win, o, lse);
+    a.window = window;
+    a.nb = 1;
+    if (G > 128) return fail(HYS_ERR_UNSUPPORTED, "more than 128 query heads per KV head");
+    a.HC = (int)G; a.BQ = (int)(128 / G); a.nhc = 1;
+    a.ntq = (int)((L + a.BQ - 1) / a.BQ);
+    a.gate_w = nullptr;                       // no gate: the window branch alone, with its LSE
+    const int grid = (int)(B * a.ntq * Hkv);
+    a.grid_used = grid;
+    return hip_status(hys::launch_attn(hys::M_SWA_GATE, et(q.dtype), et(k_win.dtype), (int)D, a, grid,
+                                       (hipStream_t)stream),
+                      "window launch");
+  } catch (...) {
+    return fail(HYS_ERR_INTERNAL, "internal error");
+  }
+}
+
+}  // extern "C"
+
+namespace {
+
+hys_status check_grad(const hys_tensor4& g, const hys_tensor4& like, const char* name) {
+  hys_status s;
+  if ((s = check_tensor(g, name, false)) != HYS_OK) return s;
+  if (g.dtype != HYS_F32) return fail(HYS_ERR_UNSUPPORTED, "%s must be fp32", name);
+  for (int i = 0; i < 4; ++i)
+    if (g.shape[i] != like.shape[i]) return fail(HYS_ERR_INVALID_ARG, "%s: shape differs from its input", name);
+  return HYS_OK;
+}
+
+bool same_strides(const hys_tensor4& x, const hys_tensor4& y) {
+  for (int i = 0; i < 3; ++i)
+    if (x.stride[i] != y.stride[i] && x.shape[i] > 1) return false;
+  return true;
+}
+
+// q, k, v bf16 self-attention inputs of a backward call, k and v sharing strides
+hys_status check_bwd_inputs(const hys_attn_params* p, const hys_tensor4& q, const hys_tensor4& k,
+                            const hys_tensor4& v, const char* what) {
+  hys_status s;
+  if ((s = check_params(p)) != HYS_OK) return s;
+  if (p->k_scale != 1.f || p->v_scale != 1.f) return fail(HYS_ERR_UNSUPPORTED, "k_scale and v_scale must be 1");
+  if ((s = check_qkv(q, k, v, true)) != HYS_OK) return s;
+  if (q.dtype != HYS_BF16 || k.dtype != HYS_BF16)
+    return fail(HYS_ERR_UNSUPPORTED, "%s: the backward pass takes bf16 q, k, v", what);
+  if (!same_strides(k, v)) return fail(HYS_ERR_UNSUPPORTED, "%s: k and v must share strides", what);
+  return HYS_OK;
+}
+
+hys::BwdArgs bwd_args(const hys_attn_params* p, const hys_tensor4& q, const hys_tensor4& k, const hys_tensor4& v,
+                      const hys_tensor4& dq, const hys_tensor4& dk, float* dv) {
+  hys::BwdArgs a{};
+  a.q = (const uint16_t*)q.ptr; a.q_sb = q.stride[0]; a.q_st = q.stride[1]; a.q_sh = q.stride[2];
+  a.k = (const uint16_t*)k.ptr; a.v = (const uint16_t*)v.ptr;
+  a.k_sb = k.stride[0]; a.k_st = k.stride[1]; a.k_sh = k.stride[2];
+  a.dq = (float*)dq.ptr; a.dq_sb = dq.stride[0]; a.dq_st = dq.stride[1]; a.dq_sh = dq.stride[2];
+  a.dk = (float*)dk.ptr; a.dv = dv; a.dk_sb = dk.stride[0]; a.dk_st = dk.stride[1]; a.dk_sh = dk.stride[2];
+  a.B = (int)q.shape[0]; a.L = (int)q.shape[1]; a.Lk = (int)k.shape[1];
+  a.Hq = (int)q.shape[2]; a.Hkv = (int)k.shape[2]; a.G = a.Hq / a.Hkv;
+  a.scale = p->softmax_scale;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.ng = 1;
+  return a;
+}
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+hys_status hys_full_attn_bwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v, hys_tensor4 o,
+                             const float* lse, hys_tensor4 d_o, hys_tensor4 dq, hys_tensor4 dk, hys_tensor4 dv,
+                             int32_t accumulate_kv, void* ws, size_t* ws_bytes, void* stream) {
+  try {
+    hys_status s;
+    if (!ws_bytes) return fail(HYS_ERR_INVALID_ARG, "ws_bytes must not be null");
+    if ((s = check_bwd_inputs(p, q, k, v, "full layer")) != HYS_OK) return s;
+    if ((s = check_out(o, q, "o")) != HYS_OK) return s;
+    if ((s = check_out(d_o, q, "d_o")) != HYS_OK) return s;
+    if (d_o.dtype != HYS_BF16) return fail(HYS_ERR_UNSUPPORTED, "d_o must be bf16");
+    if ((s = check_grad(dq, q, "dq")) != HYS_OK) return s;
+    if ((s = check_grad(dk, k, "dk")) != HYS_OK) return s;
+    if ((s = check_grad(dv, v, "dv")) != HYS_OK) return s;
+    if (!same_strides(dk, dv)) return fail(HYS_ERR_UNSUPPORTED, "dk and dv must share strides");
+    if (!lse) return fail(HYS_ERR_INVALID_ARG, "null lse");
+    if (accumulate_kv != 0 && accumulate_kv != 1) return fail(HYS_ERR_INVALID_ARG, "accumulate_kv must be 0 or 1");
+    const int64_t B = q.shape[0], L = q.shape[1], Hq = q.shape[2], D = q.shape[3];
+    const size_t need = (size_t)(B * Hq * L) * sizeof(float);
+    if (!ws) { *ws_bytes = need; return ok(); }
+    if (*ws_bytes < need) return fail(HYS_ERR_WORKSPACE, "workspace %zu < required %zu bytes", *ws_bytes, need);
+    if (!aligned16(ws)) return fail(HYS_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+    if (L == 0) return ok();
+    hipStream_t st = (hipStream_t)stream;
+    float* Dd = (float*)ws;
+    hys::BwdPrepArgs pa{};
+    pa.dO = d_o.ptr; pa.do_sb = d_o.stride[0]; pa.do_st = d_o.stride[1]; pa.do_sh = d_o.stride[2]; pa.do_f32 = 0;
+    pa.o = o.ptr; pa.o_sb = o.stride[0]; pa.o_st = o.stride[1]; pa.o_sh = o.stride[2];
+    pa.o_f32 = o.dtype == HYS_F32;
+    pa.Dd = Dd; pa.B = (int)B; pa.L = (int)L; pa.Hq = (int)Hq; pa.D = (int)D;
+    hipError_t e = hys::launch_bwd_prep_full(pa, st);
+    if (e != hipSuccess) return hip_status(e, "backward preparation launch");
+    hys::BwdArgs a = bwd_args(p, q, k, v, dq, dk, (float*)dv.ptr);
+    a.dO = (const uint16_t*)d_o.ptr; a.do_sb = d_o.stride[0]; a.do_st = d_o.stride[1]; a.do_sh = d_o.stride[2];
+    a.lse = lse; a.Dd = Dd;
+    a.acc_q = 0; a.acc_kv = accumulate_kv;
+    if ((e = hys::launch_bwd_dq(hys::BW_CAUSAL, (int)D, a, st)) != hipSuccess) return hip_status(e, "dq launch");
+    return hip_status(hys::launch_bwd_dkdv(hys::BW_CAUSAL, (int)D, a, st), "dk/dv launch");
+  } catch (...) {
+    return fail(HYS_ERR_INTERNAL, "internal error");
+  }
+}
+
+hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v,
+                                const hys_sparse_params* sp, const int32_t* idx, hys_tensor4 k_win, hys_tensor4 v_win,
+                                int32_t window, const float* gate_w, const float* gate_b, hys_tensor4 o_sparse,
+                                const float* lse_sparse, hys_tensor4 o_win, const float* lse_win, hys_tensor4 d_o,
+                                hys_tensor4 dq, hys_tensor4 dk, hys_tensor4 dv, int32_t accumulate_kv,
+                                hys_tensor4 dk_win, hys_tensor4 dv_win, float* dgate_w, void* ws, size_t* ws_bytes,
+                                void* stream) {
+  try {
+    hys_status s;
+    if (!ws_bytes) return fail(HYS_ERR_INVALID_ARG, "ws_bytes must not be null");
+    if ((s = check_bwd_inputs(p, q, k, v, "shared K/V")) != HYS_OK) return s;
+    if ((s = check_bwd_inputs(p, q, k_win, v_win, "window K/V")) != HYS_OK) return s;
+    for (int i = 0; i < 4; ++i)
+      if (k_win.shape[i] != k.shape[i]) return fail(HYS_ERR_INVALID_ARG, "window K/V shapes differ from k/v");
+    if ((s = check_out(o_sparse, q, "o_sparse")) != HYS_OK) return s;
+    if ((s = check_out(o_win, q, "o_win")) != HYS_OK) return s;
+    if ((s = check_out(d_o, q, "d_o")) != HYS_OK) return s;
+    if ((s = check_grad(dq, q, "dq")) != HYS_OK) return s;
+    if ((s = check_grad(dk, k, "dk")) != HYS_OK) return s;
+    if ((s = check_grad(dv, v, "dv")) != HYS_OK) return s;
+    if ((s = check_grad(dk_win, k_win, "dk_win")) != HYS_OK) return s;
+    if ((s = check_grad(dv_win, v_win, "dv_win")) != HYS_OK) return s;
+    if (!same_strides(dk, dv) || !same_strides(dk_win, dv_win))
+      return fail(HYS_ERR_UNSUPPORTED, "dk and dv (dk_win and dv_win) must share strides");
+    if (!lse_sparse || !lse_win || !gate_w || !dgate_w)
+      return fail(HYS_ERR_INVALID_ARG, "null lse_sparse, lse_win, gate_w or dgate_w");
+    if (window < 1) return fail(HYS_ERR_INVALID_ARG, "window must be >= 1");
+    if (accumulate_kv != 0 && accumulate_kv != 1) return fail(HYS_ERR_INVALID_ARG, "accumulate_kv must be 0 or 1");
+    if (!sp) return fail(HYS_ERR_INVALID_ARG, "null sparse params");
+    if (sp->granularity != 64 || sp->q_tile != 1 || sp->forced_window != 0)
+      return fail(HYS_ERR_UNSUPPORTED, "granularity 64, q_tile 1 and no forced window");
+    if (sp->k < 0 || sp->k > 64) return fail(HYS_ERR_UNSUPPORTED, "k must be in [0, 64]");
+    if (sp->k > 0 && !idx) return fail(HYS_ERR_INVALID_ARG, "null idx");
+    if (sp->idx_row_stride < sp->k || sp->idx_batch_stride < 0 || sp->idx_group_stride < 0)
+      return fail(HYS_ERR_INVALID_ARG, "idx strides too small");
+    const int64_t B = q.shape[0], L = q.shape[1], Hq = q.shape[2], Hkv = k.shape[2], D = q.shape[3];
+    const int64_t nblk = (L + 63) / 64;
+    if (nblk > 16384) return fail(HYS_ERR_UNSUPPORTED, "more than 16384 key blocks");
+    const int64_t nwords = (nblk + 31) / 32, nrb = (L + 31) / 32;
+    const int64_t ng = sp->idx_group_stride > 0 ? Hkv : 1;
+    const size_t n_do = (size_t)(B * L * Hq * D) * 2, n_row = (size_t)(B * Hq * L) * 4;
+    const size_t n_rb = (size_t)(ng * B * L * nwords) * 4, n_tb = (size_t)(ng * B * nrb * nwords) * 4;
+    const size_t n_gp = hys::bwd_gate_partial_floats((int)Hq, (int)D) * 4;
+    const size_t need = 2 * up256(n_do) + 3 * up256(n_row) + up256(n_rb) + up256(n_tb) + up256(n_gp);
+    if (!ws) { *ws_bytes = need; return ok(); }
+    if (*ws_bytes < need) return fail(HYS_ERR_WORKSPACE, "workspace %zu < required %zu bytes", *ws_bytes, need);
+    if (!aligned16(ws)) return fail(HYS_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+    if (L == 0) return ok();
+    char* w = (char*)ws;
+    uint16_t* do_sp = (uint16_t*)w; w += up256(n_do);
+    uint16_t* do_w = (uint16_t*)w; w += up256(n_do);
+    float* Dd_sp = (float*)w; w += up256(n_row);
+    float* Dd_w = (float*)w; w += up256(n_row);
+    float* dz = (float*)w; w += up256(n_row);
+    uint32_t* rowbits = (uint32_t*)w; w += up256(n_rb);
+    uint32_t* tilebits = (uint32_t*)w; w += up256(n_tb);
+    float* gpart = (float*)w;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+
+    hys::BwdGateArgs ga{};
+    ga.q = (const uint16_t*)q.ptr; ga.q_sb = q.stride[0]; ga.q_st = q.stride[1]; ga.q_sh = q.stride[2];
+    ga.dO = d_o.ptr; ga.do_sb = d_o.stride[0]; ga.do_st = d_o.stride[1]; ga.do_sh = d_o.stride[2];
+    ga.do_f32 = d_o.dtype == HYS_F32;
+    ga.osp = o_sparse.ptr; ga.osp_sb = o_sparse.stride[0]; ga.osp_st = o_sparse.stride[1];
+    ga.osp_sh = o_sparse.stride[2]; ga.osp_f32 = o_sparse.dtype == HYS_F32;
+    ga.ow = o_win.ptr; ga.ow_sb = o_win.stride[0]; ga.ow_st = o_win.stride[1]; ga.ow_sh = o_win.stride[2];
+    ga.ow_f32 = o_win.dtype == HYS_F32;
+    ga.lse_sp = lse_sparse; ga.gate_w = gate_w; ga.gate_b = gate_b;
+    ga.do_sp = do_sp; ga.do_w = do_w; ga.Dd_sp = Dd_sp; ga.Dd_w = Dd_w; ga.dz = dz;
+    ga.dq = (float*)dq.ptr; ga.dq_sb = dq.stride[0]; ga.dq_st = dq.stride[1]; ga.dq_sh = dq.stride[2];
+    ga.B = (int)B; ga.L = (int)L; ga.Hq = (int)Hq; ga.D = (int)D;
+    if ((e = hys::launch_bwd_prep_gate(ga, st)) != hipSuccess) return hip_status(e, "gate preparation launch");
+    if ((e = hys::launch_bwd_gate_grad(dz, (const uint16_t*)q.ptr, q.stride[0], q.stride[1], q.stride[2], (int)B,
+                                       (int)L, (int)Hq, (int)D, gpart, dgate_w, st)) != hipSuccess)
+      return hip_status(e, "gate gradient launch");
+    if ((e = hys::launch_bwd_selbits(idx, sp->idx_group_stride, sp->idx_batch_stride, sp->idx_row_stride, sp->k,
+                                     (int)ng, (int)B, (int)L, (int)nblk, (int)nwords, rowbits, tilebits, st)) !=
+        hipSuccess)
+      return hip_status(e, "selection bitmap launch");
+
+    // block-sparse branch over the shared K/V
+    const int64_t do_st = Hq * D, do_sb = L * Hq * D;
+    hys::BwdArgs a = bwd_args(p, q, k, v, dq, dk, (float*)dv.ptr);
+    a.dO = do_sp; a.do_sb = do_sb; a.do_st = do_st; a.do_sh = D;
+    a.lse = lse_sparse; a.Dd = Dd_sp;
+    a.rowbits = rowbits; a.tilebits = tilebits; a.nwords = (int)nwords; a.ng = (int)ng;
+    a.acc_q = 1; a.acc_kv = accumulate_kv;
+    if ((e = hys::launch_bwd_dq(hys::BW_BLOCK, (int)D, a, st)) != hipSuccess) return hip_status(e, "sparse dq launch");
+    if ((e = hys::launch_bwd_dkdv(hys::BW_BLOCK, (int)D, a, st)) != hipSuccess)
+      return hip_status(e, "sparse dk/dv launch");
+    // window branch over the layer's own K/V
+    hys::BwdArgs wa = bwd_args(p, q, k_win, v_win, dq, dk_win, (float*)dv_win.ptr);
+    wa.dO = do_w; wa.do_sb = do_sb; wa.do_st = do_st; wa.do_sh = D;
+    wa.lse = lse_win; wa.Dd = Dd_w; wa.window = window;
+    wa.acc_q = 1; wa.acc_kv = 0;
+    if ((e = hys::launch_bwd_dq(hys::BW_WINDOW, (int)D, wa, st)) != hipSuccess) return hip_status(e, "window dq launch");
+    return hip_status(hys::launch_bwd_dkdv(hys::BW_WINDOW, (int)D, wa, st), "window dk/dv launch");
   } catch (...) {
     return fail(HYS_ERR_INTERNAL, "internal error");
   }

@@ -845,7 +845,9 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
       float gate = 1.f;
       bool sp_on = true;
       const float* osp = nullptr;
-      if (MODE == M_SWA_GATE || MODE == M_SPARSE_SWA) {
+      // M_SWA_GATE without gate weights is the window branch alone (O and LSE)
+      const bool gated = MODE == M_SPARSE_SWA || (MODE == M_SWA_GATE && a.gate_w != nullptr);
+      if (gated) {
         // g = sigmoid(<q, w_h> + b_h): each lane holds half of the row's d values
         const float* w = a.gate_w + (int64_t)head[nb] * D;
         float z = 0.f;
@@ -885,7 +887,7 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
           float r[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) r[e] = acc[nb][db][4 * i4 + e] * inv;
-          if ((MODE == M_SWA_GATE || MODE == M_SPARSE_SWA) && sp_on) {
+          if (gated && sp_on) {
             float spv[4];
             if (MODE == M_SWA_GATE) {
               const float4 sp = *(const float4*)(osp + d);

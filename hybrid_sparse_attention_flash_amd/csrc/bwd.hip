@@ -1,0 +1,672 @@
+// Backward pass of the HySparse hybrid block on gfx950 (v_mfma_f32_32x32x16_bf16).
+//
+// HySparse is trained directly (QbitAI HySparse article, opening summary;
+// demingchina HySparse2 commentary, section 06).  With the selection held
+// fixed, each attention branch's gradients are those of softmax attention over
+// a visible set:
+//   P = exp(S - LSE),  dV = P^T dO,  dP = dO V^T,  dS = P (dP - rowsum(dO O)),
+//   dQ = scale dS K,   dK = scale dS^T Q,
+// summed over the G query heads of a KV head for dK, dV.  Two kernels per
+// branch, neither with atomics:
+//   bwd_dkdv_kernel - key-stationary: a workgroup owns 128 keys of one KV head
+//     (32 per wave, held in registers as MFMA operands) and walks the 32-row
+//     query blocks of every head of the group that can see them, staging Q and
+//     dO through LDS both row-major (A operands of S and dP) and transposed
+//     (B operands of dK and dV); dK and dV stay in registers and are written
+//     once.
+//   bwd_dq_kernel - query-stationary: a workgroup owns 4 x 32 query rows
+//     (heads of one KV group over the same rows, or consecutive row blocks)
+//     and walks the 64-key tiles they see, staging K (row-major and
+//     transposed) and V through LDS; dQ stays in registers.
+// P and dS come back from the forward's LSE in both kernels.  P and dS leave
+// the MFMA in its C layout (lane = one column, rows spread over the 16
+// values); they feed the next MFMA as A operands directly, with the other
+// operand read in the same permuted row order, so no transpose of P or dS is
+// needed.  The block-sparse branch reads per-row selection bitmaps and skips
+// whole row blocks (dK/dV) or key tiles (dQ) that no row selected.
+
+#include "bwd.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace hys {
+namespace {
+
+typedef unsigned int bw_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int bw_u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x8 bwf(bw_u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bw_u32x4 cat2(bw_u32x2 lo, bw_u32x2 hi) { return bw_u32x4{lo.x, lo.y, hi.x, hi.y}; }
+__device__ __forceinline__ bw_u32x4 zero4() { return bw_u32x4{0u, 0u, 0u, 0u}; }
+
+// eight consecutive values of one 16-byte-aligned chunk packed as MFMA A fragment
+__device__ __forceinline__ bw_u32x4 pack8(const float* x) {
+  return bw_u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+}
+
+template <int MODE>
+__device__ __forceinline__ bool bw_visible(int i, int j, int L, int Lk, int window, bool bit) {
+  bool ok = i < L && j < Lk && j <= i;
+  if (MODE == BW_WINDOW) ok = ok && j > i - window;
+  if (MODE == BW_BLOCK) ok = ok && bit;
+  return ok;
+}
+
+// transposed LDS copy of one 16-byte chunk (8 bf16 of row `row`, columns 8ch..8ch+7)
+template <int TS>
+__device__ __forceinline__ void store_t8(uint16_t* t, int row, int ch, bw_u32x4 v) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[(8 * ch + e) * TS + row] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+}
+
+// Next row block of a dK/dV workgroup: blocks [base, rb_hi) in chunks of 64,
+// in block mode only those whose rows selected one of the tile's two 64-key
+// blocks (both bits sit in one word: the tile starts on an even block).
+template <int MODE>
+__device__ __forceinline__ bool next_row_block(const BwdArgs& a, int lane, int gs, int b, int nrb, int k0, int rb_hi,
+                                               uint64_t& mask, int& base, int& rb) {
+  while (mask == 0ull) {
+    base += 64;
+    if (base >= rb_hi) return false;
+    const int r = base + lane;
+    bool on = r < rb_hi;
+    if (MODE == BW_BLOCK && on) {
+      const uint32_t w = a.tilebits[((int64_t)(gs * a.B + b) * nrb + r) * a.nwords + (k0 >> 11)];
+      on = ((w >> ((k0 >> 6) & 31)) & 3u) != 0u;
+    }
+    mask = __ballot(on);
+  }
+  rb = base + __builtin_ctzll(mask);
+  mask &= mask - 1ull;
+  return true;
+}
+
+template <int MODE, int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NC = D / 16;              // 16-wide d chunks of the S and dP contractions
+  constexpr int NT = D / 32;              // 32-wide d tiles of dK and dV
+  constexpr int RS = D + 8;               // row-major LDS row stride (elements)
+  constexpr int TS = 40;                  // transposed LDS row stride: 32 rows + 8
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int NPASS = 32 * CPR / 256;   // staging passes per tensor
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[32 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t s_do[32 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t s_qt[D * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t s_dot[D * TS];
+  __shared__ __attribute__((aligned(16))) float s_lse[32];
+  __shared__ __attribute__((aligned(16))) float s_dd[32];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 31, hh = lane >> 5;
+  // key tiles slowest, so the long causal tiles (small k0) are dispatched first
+  const int nbh = a.Hkv * a.B;
+  const int kt = blockIdx.x / nbh, gb = blockIdx.x - kt * nbh;
+  const int g = gb % a.Hkv, b = gb / a.Hkv;
+  const int k0 = kt * 128, kw0 = k0 + 32 * wave;
+  const int gs = a.ng > 1 ? g : 0;
+  const int nrb = (a.L + 31) / 32;
+  const int cw = kw0 >> 6;                // this wave's 64-key block
+
+  // this wave's 32 keys and values as B operands: lane (ln, hh) holds key ln, d = 16c + 8hh + [0, 8)
+  bw_u32x4 kf[NC], vf[NC];
+  {
+    const int key = kw0 + ln;
+    const bool ok = key < a.Lk;
+    const int64_t off = (int64_t)b * a.k_sb + (int64_t)(ok ? key : 0) * a.k_st + (int64_t)g * a.k_sh + 8 * hh;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kf[c] = ok ? *(const bw_u32x4*)(a.k + off + 16 * c) : zero4();
+      vf[c] = ok ? *(const bw_u32x4*)(a.v + off + 16 * c) : zero4();
+    }
+  }
+  f32x16 dk_acc[NT], dv_acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { dk_acc[t][i] = 0.f; dv_acc[t][i] = 0.f; }
+
+  int rb_hi = nrb;
+  if (MODE == BW_WINDOW) rb_hi = min(nrb, (k0 + 127 + a.window - 1) / 32 + 1);
+  uint64_t mask = 0ull;
+  int base = k0 / 32 - 64, rb = 0, h = 0;
+  bool have = next_row_block<MODE>(a, lane, gs, b, nrb, k0, rb_hi, mask, base, rb);
+
+  bw_u32x4 pq[NPASS], pdo[NPASS];
+  float plse = kNegInf, pdd = 0.f;
+  uint32_t pbits = 0u;
+  auto issue = [&](int rbi, int hq) {
+    const int r0 = rbi * 32;
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const int e = tid + 256 * p, row = e / CPR, ch = e - row * CPR, i = r0 + row;
+      const bool ok = i < a.L;
+      const int ii = ok ? i : 0;
+      pq[p] = ok ? *(const bw_u32x4*)(a.q + (int64_t)b * a.q_sb + (int64_t)ii * a.q_st + (int64_t)hq * a.q_sh + 8 * ch)
+                 : zero4();
+      pdo[p] = ok ? *(const bw_u32x4*)(a.dO + (int64_t)b * a.do_sb + (int64_t)ii * a.do_st + (int64_t)hq * a.do_sh +
+                                       8 * ch)
+                  : zero4();
+    }
+    if (tid < 32) {
+      const int i = r0 + tid;
+      const bool ok = i < a.L;
+      const int64_t o = ((int64_t)b * a.Hq + hq) * a.L + (ok ? i : 0);
+      plse = ok ? a.lse[o] : kNegInf;
+      pdd = ok ? a.Dd[o] : 0.f;
+    }
+    if (MODE == BW_BLOCK) {
+      const int i = r0 + ln;
+      pbits = i < a.L ? a.rowbits[((int64_t)(gs * a.B + b) * a.L + i) * a.nwords + (cw >> 5)] : 0u;
+    }
+  };
+  if (have) issue(rb, a.G > 0 ? g * a.G : 0);
+
+  while (have) {
+    const int cur_r0 = rb * 32;
+    __syncthreads();                      // the previous step's LDS reads are done
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const int e = tid + 256 * p, row = e / CPR, ch = e - row * CPR;
+      *(bw_u32x4*)&s_q[row * RS + 8 * ch] = pq[p];
+      *(bw_u32x4*)&s_do[row * RS + 8 * ch] = pdo[p];
+      store_t8<TS>(s_qt, row, ch, pq[p]);
+      store_t8<TS>(s_dot, row, ch, pdo[p]);
+    }
+    if (tid < 32) { s_lse[tid] = plse * kLog2e; s_dd[tid] = pdd; }
+    uint32_t selmask = 0xffffffffu;
+    if (MODE == BW_BLOCK) selmask = (uint32_t)__ballot(hh == 0 && ((pbits >> (cw & 31)) & 1u));
+    __syncthreads();
+    // advance and prefetch the next step while this one computes
+    if (++h >= a.G) {
+      h = 0;
+      have = next_row_block<MODE>(a, lane, gs, b, nrb, k0, rb_hi, mask, base, rb);
+    }
+    if (have) issue(rb, g * a.G + h);
+
+    bool any = kw0 <= cur_r0 + 31 && kw0 < a.Lk;
+    if (MODE == BW_WINDOW) any = any && kw0 + 31 > cur_r0 - a.window;
+    if (MODE == BW_BLOCK) any = any && selmask != 0u;
+    if (any) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { s[i] = 0.f; dp[i] = 0.f; }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const bw_u32x4 aq = *(const bw_u32x4*)&s_q[ln * RS + 16 * c + 8 * hh];
+        const bw_u32x4 ad = *(const bw_u32x4*)&s_do[ln * RS + 16 * c + 8 * hh];
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(aq), bwf(kf[c]), s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(ad), bwf(vf[c]), dp, 0, 0, 0);
+      }
+      // element i: query row 8(i/4) + 4hh + i%4 of the block, key kw0 + ln
+      float p[16], ds[16];
+      const int key = kw0 + ln;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const f32x4 l4 = *(const f32x4*)&s_lse[8 * i4 + 4 * hh];
+        const f32x4 d4 = *(const f32x4*)&s_dd[8 * i4 + 4 * hh];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * i4 + e, row = 8 * i4 + 4 * hh + e;
+          const bool vis = bw_visible<MODE>(cur_r0 + row, key, a.L, a.Lk, a.window, (selmask >> row) & 1u) &&
+                           l4[e] != kNegInf;
+          const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -l4[e])) : 0.f;
+          p[i] = pv;
+          ds[i] = pv * (dp[i] - d4[e]);
+        }
+      }
+      // A fragments: k-slot 8hh + j of chunk kc is row 16kc + 8(j/4) + 4hh + j%4, i.e. value 8kc + j
+      const bw_u32x4 pa0 = pack8(p), pa1 = pack8(p + 8);
+      const bw_u32x4 da0 = pack8(ds), da1 = pack8(ds + 8);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint16_t* td = &s_dot[(32 * t + ln) * TS + 4 * hh];
+        const uint16_t* tq = &s_qt[(32 * t + ln) * TS + 4 * hh];
+        const bw_u32x4 bd0 = cat2(*(const bw_u32x2*)(td), *(const bw_u32x2*)(td + 8));
+        const bw_u32x4 bd1 = cat2(*(const bw_u32x2*)(td + 16), *(const bw_u32x2*)(td + 24));
+        const bw_u32x4 bq0 = cat2(*(const bw_u32x2*)(tq), *(const bw_u32x2*)(tq + 8));
+        const bw_u32x4 bq1 = cat2(*(const bw_u32x2*)(tq + 16), *(const bw_u32x2*)(tq + 24));
+        dv_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(pa0), bwf(bd0), dv_acc[t], 0, 0, 0);
+        dv_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(pa1), bwf(bd1), dv_acc[t], 0, 0, 0);
+        dk_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(da0), bwf(bq0), dk_acc[t], 0, 0, 0);
+        dk_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(da1), bwf(bq1), dk_acc[t], 0, 0, 0);
+      }
+    }
+  }
+
+  // dK, dV in C layout: lane (ln, hh) holds d = 32t + ln of keys kw0 + 8(i/4) + 4hh + i%4
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = kw0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+      if (key >= a.Lk) continue;
+      const int64_t o = (int64_t)b * a.dk_sb + (int64_t)key * a.dk_st + (int64_t)g * a.dk_sh + 32 * t + ln;
+      const float kv = dk_acc[t][i] * a.scale, vv = dv_acc[t][i];
+      if (a.acc_kv) { a.dk[o] += kv; a.dv[o] += vv; }
+      else { a.dk[o] = kv; a.dv[o] = vv; }
+    }
+}
+
+// Next 64-key tile of a dQ workgroup (block mode: the union of its rows' selections).
+template <int MODE>
+__device__ __forceinline__ bool next_key_tile(const BwdArgs& a, int gs, int b, int nrb, int rb0, int nrbw, int c_hi,
+                                              uint32_t& bits, int& wi, int& c) {
+  if (MODE != BW_BLOCK) { ++c; return c <= c_hi; }
+  while (bits == 0u) {
+    ++wi;
+    if (wi * 32 > c_hi) return false;
+    uint32_t u = 0u;
+    for (int r = 0; r < nrbw; ++r) u |= a.tilebits[((int64_t)(gs * a.B + b) * nrb + rb0 + r) * a.nwords + wi];
+    const int n = c_hi - wi * 32;
+    if (n < 31) u &= (2u << n) - 1u;
+    bits = u;
+  }
+  c = wi * 32 + __builtin_ctz(bits);
+  bits &= bits - 1u;
+  return true;
+}
+
+template <int MODE, int D>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int NC = D / 16;
+  constexpr int NT = D / 32;
+  constexpr int RS = D + 8;               // row-major K, V row stride
+  constexpr int TS = 72;                  // transposed K row stride: 64 keys + 8
+  constexpr int CPR = D / 8;
+  constexpr int NPASS = 64 * CPR / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[64 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[64 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t s_kt[D * TS];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 31, hh = lane >> 5;
+  const int HW = a.G < 4 ? a.G : 4;       // heads per workgroup
+  const int RB = 4 / HW;                  // 32-row blocks per workgroup
+  const int nhc = (a.G + HW - 1) / HW;
+  const int nrb = (a.L + 31) / 32;
+  const int nqg = (nrb + RB - 1) / RB;
+  const int per = a.B * a.Hkv * nhc;
+  const int qg = nqg - 1 - (int)(blockIdx.x / per);    // the long (late) query groups first
+  int rem = blockIdx.x % per;
+  const int hc = rem % nhc;
+  rem /= nhc;
+  const int g = rem % a.Hkv, b = rem / a.Hkv;
+  const int gs = a.ng > 1 ? g : 0;
+  const int hl = wave % HW, rbl = wave / HW;
+  const int rb0 = qg * RB;
+  const int nrbw = min(RB, nrb - rb0);
+  const int hq = g * a.G + hc * HW + hl;
+  const int r0 = (rb0 + rbl) * 32;
+  const bool active = rbl < RB && hc * HW + hl < a.G && r0 < a.L;
+  const int qi = r0 + ln;
+  const bool rowok = active && qi < a.L;
+
+  // this lane's query row as B operand of S^T = K Q^T and dP^T = V dO^T
+  bw_u32x4 qf[NC], dof[NC];
+  float lse2 = kNegInf, dd = 0.f;
+  {
+    const int ii = rowok ? qi : 0, hh2 = active ? hq : 0;
+    const int64_t oq = (int64_t)b * a.q_sb + (int64_t)ii * a.q_st + (int64_t)hh2 * a.q_sh + 8 * hh;
+    const int64_t od = (int64_t)b * a.do_sb + (int64_t)ii * a.do_st + (int64_t)hh2 * a.do_sh + 8 * hh;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      qf[c] = rowok ? *(const bw_u32x4*)(a.q + oq + 16 * c) : zero4();
+      dof[c] = rowok ? *(const bw_u32x4*)(a.dO + od + 16 * c) : zero4();
+    }
+    if (rowok) {
+      const int64_t o = ((int64_t)b * a.Hq + hq) * a.L + qi;
+      lse2 = a.lse[o] * kLog2e;
+      dd = a.Dd[o];
+    }
+  }
+  f32x16 dq_acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq_acc[t][i] = 0.f;
+
+  const int wr0 = rb0 * 32;
+  const int wr1 = min(a.L, wr0 + RB * 32) - 1;           // last row of the workgroup
+  const int c_hi = min(wr1 / 64, (a.Lk - 1) / 64);
+  int c = -1, wi = -1;
+  uint32_t bits = 0u;
+  if (MODE == BW_WINDOW) c = max(0, wr0 - a.window + 1) / 64 - 1;
+  bool have = next_key_tile<MODE>(a, gs, b, nrb, rb0, nrbw, c_hi, bits, wi, c);
+
+  bw_u32x4 pk[NPASS], pv[NPASS];
+  uint32_t pbits = 0u;
+  auto issue = [&](int ct) {
+    const int kc0 = ct * 64;
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const int e = tid + 256 * p, row = e / CPR, ch = e - row * CPR, key = kc0 + row;
+      const bool ok = key < a.Lk;
+      const int64_t o = (int64_t)b * a.k_sb + (int64_t)(ok ? key : 0) * a.k_st + (int64_t)g * a.k_sh + 8 * ch;
+      pk[p] = ok ? *(const bw_u32x4*)(a.k + o) : zero4();
+      pv[p] = ok ? *(const bw_u32x4*)(a.v + o) : zero4();
+    }
+    if (MODE == BW_BLOCK)
+      pbits = rowok ? a.rowbits[((int64_t)(gs * a.B + b) * a.L + qi) * a.nwords + (ct >> 5)] : 0u;
+  };
+  if (have) issue(c);
+
+  while (have) {
+    const int cur = c;
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const int e = tid + 256 * p, row = e / CPR, ch = e - row * CPR;
+      *(bw_u32x4*)&s_k[row * RS + 8 * ch] = pk[p];
+      *(bw_u32x4*)&s_v[row * RS + 8 * ch] = pv[p];
+      store_t8<TS>(s_kt, row, ch, pk[p]);
+    }
+    const bool selbit = MODE == BW_BLOCK ? ((pbits >> (cur & 31)) & 1u) != 0u : true;
+    __syncthreads();
+    have = next_key_tile<MODE>(a, gs, b, nrb, rb0, nrbw, c_hi, bits, wi, c);
+    if (have) issue(c);
+
+    const int kc0 = cur * 64;
+    bool any = active && kc0 <= r0 + 31;
+    if (MODE == BW_WINDOW) any = any && kc0 + 63 > r0 - a.window;
+    if (MODE == BW_BLOCK) any = any && __ballot(selbit && rowok) != 0ull;
+    if (any) {
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { s[kh][i] = 0.f; dp[kh][i] = 0.f; }
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int c2 = 0; c2 < NC; ++c2) {
+          const bw_u32x4 ak = *(const bw_u32x4*)&s_k[(32 * kh + ln) * RS + 16 * c2 + 8 * hh];
+          const bw_u32x4 av = *(const bw_u32x4*)&s_v[(32 * kh + ln) * RS + 16 * c2 + 8 * hh];
+          s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(ak), bwf(qf[c2]), s[kh], 0, 0, 0);
+          dp[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(av), bwf(dof[c2]), dp[kh], 0, 0, 0);
+        }
+      // element (kh, i): key kc0 + 32kh + 8(i/4) + 4hh + i%4, query row qi (this lane)
+      float ds[32];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kc0 + 32 * kh + 8 * (i >> 2) + 4 * hh + (i & 3);
+          const bool vis = bw_visible<MODE>(qi, key, a.L, a.Lk, a.window, selbit) && lse2 != kNegInf;
+          const float pvv = vis ? __builtin_amdgcn_exp2f(fmaf(s[kh][i], a.scale_log2, -lse2)) : 0.f;
+          ds[16 * kh + i] = pvv * (dp[kh][i] - dd);
+        }
+      // dQ += dS K: k-slot 8hh + j of chunk kc is key 16kc + 8(j/4) + 4hh + j%4, i.e. value 8kc + j
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const bw_u32x4 da = pack8(ds + 8 * kc);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const uint16_t* tk = &s_kt[(32 * t + ln) * TS + 16 * kc + 4 * hh];
+          const bw_u32x4 bk = cat2(*(const bw_u32x2*)(tk), *(const bw_u32x2*)(tk + 8));
+          dq_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(da), bwf(bk), dq_acc[t], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // dQ in C layout: lane (ln, hh) holds d = 32t + ln of rows r0 + 8(i/4) + 4hh + i%4
+  if (active) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = r0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if (row >= a.L) continue;
+        const int64_t o = (int64_t)b * a.dq_sb + (int64_t)row * a.dq_st + (int64_t)hq * a.dq_sh + 32 * t + ln;
+        const float v = dq_acc[t][i] * a.scale;
+        if (a.acc_q) a.dq[o] += v;
+        else a.dq[o] = v;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// per-row preparation kernels (16 lanes per (b, i, h) row, 8 values per lane)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void load8f(const void* p, int64_t off, int f32, float (&x)[8]) {
+  if (f32) {
+    const f32x4 u = *(const f32x4*)((const float*)p + off);
+    const f32x4 w = *(const f32x4*)((const float*)p + off + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { x[j] = u[j]; x[4 + j] = w[j]; }
+  } else {
+    const bw_u32x4 u = *(const bw_u32x4*)((const uint16_t*)p + off);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = bf16_to_f32((uint16_t)(u[j] & 0xffffu));
+      x[2 * j + 1] = bf16_to_f32((uint16_t)(u[j] >> 16));
+    }
+  }
+}
+
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 8);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 1);
+  return v;
+}
+
+__global__ __launch_bounds__(256) void bwd_prep_full_kernel(BwdPrepArgs a) {
+  const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int ch = threadIdx.x & 15;
+  const int64_t nrow = (int64_t)a.B * a.L * a.Hq;
+  if (r >= nrow) return;
+  const int h = (int)(r % a.Hq);
+  const int64_t bi = r / a.Hq;
+  const int i = (int)(bi % a.L), b = (int)(bi / a.L);
+  float acc = 0.f;
+  if (8 * ch < a.D) {
+    float x[8], y[8];
+    load8f(a.dO, (int64_t)b * a.do_sb + (int64_t)i * a.do_st + (int64_t)h * a.do_sh + 8 * ch, a.do_f32, x);
+    load8f(a.o, (int64_t)b * a.o_sb + (int64_t)i * a.o_st + (int64_t)h * a.o_sh + 8 * ch, a.o_f32, y);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = fmaf(x[j], y[j], acc);
+  }
+  acc = sum16(acc);
+  if (ch == 0) a.Dd[((int64_t)b * a.Hq + h) * a.L + i] = acc;
+}
+
+__global__ __launch_bounds__(256) void bwd_prep_gate_kernel(BwdGateArgs a) {
+  const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int ch = threadIdx.x & 15;
+  const int64_t nrow = (int64_t)a.B * a.L * a.Hq;
+  if (r >= nrow) return;
+  const int h = (int)(r % a.Hq);
+  const int64_t bi = r / a.Hq;
+  const int i = (int)(bi % a.L), b = (int)(bi / a.L);
+  const bool lane_on = 8 * ch < a.D;
+  float dov[8], osp[8], ow[8], w[8], qv[8];
+  float z = 0.f, sa = 0.f, sb = 0.f;
+  if (lane_on) {
+    load8f(a.dO, (int64_t)b * a.do_sb + (int64_t)i * a.do_st + (int64_t)h * a.do_sh + 8 * ch, a.do_f32, dov);
+    load8f(a.osp, (int64_t)b * a.osp_sb + (int64_t)i * a.osp_st + (int64_t)h * a.osp_sh + 8 * ch, a.osp_f32, osp);
+    load8f(a.ow, (int64_t)b * a.ow_sb + (int64_t)i * a.ow_st + (int64_t)h * a.ow_sh + 8 * ch, a.ow_f32, ow);
+    load8f(a.q, (int64_t)b * a.q_sb + (int64_t)i * a.q_st + (int64_t)h * a.q_sh + 8 * ch, 0, qv);
+    load8f(a.gate_w, (int64_t)h * a.D + 8 * ch, 1, w);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      z = fmaf(qv[j], w[j], z);
+      sa = fmaf(dov[j], osp[j], sa);
+      sb = fmaf(dov[j], ow[j], sb);
+    }
+  }
+  z = sum16(z);
+  sa = sum16(sa);
+  sb = sum16(sb);
+  if (a.gate_b) z += a.gate_b[h];
+  const float gt = 1.f / (1.f + __expf(-z));
+  const int64_t rl = ((int64_t)b * a.Hq + h) * a.L + i;
+  const bool on = a.lse_sp[rl] != kNegInf;
+  const float ge = on ? gt : 0.f;
+  const float dz = on ? gt * (1.f - gt) * (sa - sb) : 0.f;
+  if (lane_on) {
+    const int64_t oc = (((int64_t)b * a.L + i) * a.Hq + h) * a.D + 8 * ch;
+    bw_u32x4 us, uw;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      us[j] = pack_bf16x2(ge * dov[2 * j], ge * dov[2 * j + 1]);
+      uw[j] = pack_bf16x2((1.f - ge) * dov[2 * j], (1.f - ge) * dov[2 * j + 1]);
+    }
+    *(bw_u32x4*)(a.do_sp + oc) = us;
+    *(bw_u32x4*)(a.do_w + oc) = uw;
+    float* dq = a.dq + (int64_t)b * a.dq_sb + (int64_t)i * a.dq_st + (int64_t)h * a.dq_sh + 8 * ch;
+    const f32x4 lo = {dz * w[0], dz * w[1], dz * w[2], dz * w[3]};
+    const f32x4 hi = {dz * w[4], dz * w[5], dz * w[6], dz * w[7]};
+    *(f32x4*)dq = lo;
+    *(f32x4*)(dq + 4) = hi;
+  }
+  if (ch == 0) {
+    a.Dd_sp[rl] = ge * sa;
+    a.Dd_w[rl] = (1.f - ge) * sb;
+    a.dz[rl] = dz;
+  }
+}
+
+// dgate_w partial sums: workgroup (h, split) sums rows split, split + nsplit, ...
+constexpr int kGateSplit = 64;
+
+__global__ __launch_bounds__(256) void bwd_gate_partial_kernel(const float* dz, const uint16_t* q, int64_t q_sb,
+                                                               int64_t q_st, int64_t q_sh, int B, int L, int Hq,
+                                                               int D, float* part) {
+  __shared__ float red[256];
+  const int h = blockIdx.x % Hq, split = blockIdx.x / Hq;
+  const int d = threadIdx.x % D, rg = threadIdx.x / D, nrg = 256 / D;
+  const int64_t n = (int64_t)B * L;
+  float acc = 0.f;
+  for (int64_t r = (int64_t)split * nrg + rg; r < n; r += (int64_t)kGateSplit * nrg) {
+    const int b = (int)(r / L), i = (int)(r - (int64_t)b * L);
+    const float z = dz[((int64_t)b * Hq + h) * L + i];
+    acc = fmaf(z, bf16_to_f32(q[(int64_t)b * q_sb + (int64_t)i * q_st + (int64_t)h * q_sh + d]), acc);
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (rg == 0) {
+    for (int k = 1; k < nrg; ++k) acc += red[k * D + d];
+    part[((int64_t)split * Hq + h) * D + d] = acc;
+  }
+}
+
+__global__ __launch_bounds__(256) void bwd_gate_reduce_kernel(const float* part, int Hq, int D, float* out) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= Hq * D) return;
+  float s = 0.f;
+  for (int k = 0; k < kGateSplit; ++k) s += part[(int64_t)k * Hq * D + e];
+  out[e] = s;
+}
+
+__global__ __launch_bounds__(256) void bwd_selbits_kernel(const int32_t* idx, int64_t idx_sg, int64_t idx_sb,
+                                                          int64_t idx_sr, int k, int ng, int B, int L, int nblk,
+                                                          int nwords, uint32_t* rowbits, uint32_t* tilebits) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n = (int64_t)ng * B * L * k;
+  if (e >= n) return;
+  const int j = (int)(e % k);
+  int64_t t = e / k;
+  const int i = (int)(t % L);
+  t /= L;
+  const int b = (int)(t % B), gs = (int)(t / B);
+  const int c = idx[gs * idx_sg + b * idx_sb + (int64_t)i * idx_sr + j];
+  if (c < 0 || c >= nblk) return;
+  const uint32_t bit = 1u << (c & 31);
+  const int nrb = (L + 31) / 32;
+  atomicOr(&rowbits[((int64_t)(gs * B + b) * L + i) * nwords + (c >> 5)], bit);
+  atomicOr(&tilebits[((int64_t)(gs * B + b) * nrb + (i >> 5)) * nwords + (c >> 5)], bit);
+}
+
+template <int MODE, int D>
+hipError_t dkdv_one(const BwdArgs& a, hipStream_t s) {
+  const int64_t grid = (int64_t)((a.Lk + 127) / 128) * a.Hkv * a.B;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<MODE, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int MODE, int D>
+hipError_t dq_one(const BwdArgs& a, hipStream_t s) {
+  const int HW = a.G < 4 ? a.G : 4, RB = 4 / HW;
+  const int nhc = (a.G + HW - 1) / HW, nrb = (a.L + 31) / 32;
+  const int64_t grid = (int64_t)((nrb + RB - 1) / RB) * nhc * a.Hkv * a.B;
+  hipLaunchKernelGGL((bwd_dq_kernel<MODE, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dkdv(int mode, int D, const BwdArgs& a, hipStream_t s) {
+  if (a.L == 0 || a.Lk == 0) return hipSuccess;
+  if (D == 128) {
+    if (mode == BW_CAUSAL) return dkdv_one<BW_CAUSAL, 128>(a, s);
+    if (mode == BW_WINDOW) return dkdv_one<BW_WINDOW, 128>(a, s);
+    if (mode == BW_BLOCK) return dkdv_one<BW_BLOCK, 128>(a, s);
+  } else if (D == 64) {
+    if (mode == BW_CAUSAL) return dkdv_one<BW_CAUSAL, 64>(a, s);
+    if (mode == BW_WINDOW) return dkdv_one<BW_WINDOW, 64>(a, s);
+    if (mode == BW_BLOCK) return dkdv_one<BW_BLOCK, 64>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dq(int mode, int D, const BwdArgs& a, hipStream_t s) {
+  if (a.L == 0 || a.Lk == 0) return hipSuccess;
+  if (D == 128) {
+    if (mode == BW_CAUSAL) return dq_one<BW_CAUSAL, 128>(a, s);
+    if (mode == BW_WINDOW) return dq_one<BW_WINDOW, 128>(a, s);
+    if (mode == BW_BLOCK) return dq_one<BW_BLOCK, 128>(a, s);
+  } else if (D == 64) {
+    if (mode == BW_CAUSAL) return dq_one<BW_CAUSAL, 64>(a, s);
+    if (mode == BW_WINDOW) return dq_one<BW_WINDOW, 64>(a, s);
+    if (mode == BW_BLOCK) return dq_one<BW_BLOCK, 64>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_prep_full(const BwdPrepArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.B * a.L * a.Hq;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_prep_full_kernel, dim3((unsigned)((n + 15) / 16)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep_gate(const BwdGateArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.B * a.L * a.Hq;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_prep_gate_kernel, dim3((unsigned)((n + 15) / 16)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+size_t bwd_gate_partial_floats(int Hq, int D) { return (size_t)kGateSplit * Hq * D; }
+
+hipError_t launch_bwd_gate_grad(const float* dz, const uint16_t* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
+                                int B, int L, int Hq, int D, float* part, float* dgate_w, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_gate_partial_kernel, dim3((unsigned)(Hq * kGateSplit)), dim3(256), 0, s, dz, q, q_sb, q_st,
+                     q_sh, B, L, Hq, D, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_gate_reduce_kernel, dim3((unsigned)((Hq * D + 255) / 256)), dim3(256), 0, s, part, Hq, D,
+                     dgate_w);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_selbits(const int32_t* idx, int64_t idx_sg, int64_t idx_sb, int64_t idx_sr, int k, int ng,
+                              int B, int L, int nblk, int nwords, uint32_t* rowbits, uint32_t* tilebits,
+                              hipStream_t s) {
+  const int nrb = (L + 31) / 32;
+  hipError_t e = launch_fill_i32((int32_t*)rowbits, 0, (int64_t)ng * B * L * nwords, s);
+  if (e != hipSuccess) return e;
+  e = launch_fill_i32((int32_t*)tilebits, 0, (int64_t)ng * B * nrb * nwords, s);
+  if (e != hipSuccess) return e;
+  const int64_t n = (int64_t)ng * B * L * k;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_selbits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, idx_sg, idx_sb,
+                     idx_sr, k, ng, B, L, nblk, nwords, rowbits, tilebits);
+  return hipGetLastError();
+}
+
+}  // namespace hys

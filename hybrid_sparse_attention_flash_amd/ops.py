@@ -191,5 +191,50 @@ def hys_kv_bridge_fwd(h, w_k, w_v, k_cache, v_cache, k_scale: float, v_scale: fl
                                 tensor4(v_cache), _ptr(amax), _stream(h.device)))
 
 
+def hys_window_attn_fwd(q, k_win, v_win, window: int, o, lse=None, softmax_scale: float = None, k_scale: float = 1.0,
+                        v_scale: float = 1.0):
+    """The window branch alone (no gate): o and its natural-log lse [B, Hq, L]."""
+    lib = _lib.load()
+    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), k_scale, v_scale)
+    check(lib.hys_window_attn_fwd(ctypes.byref(p), tensor4(q), tensor4(k_win), tensor4(v_win), window, tensor4(o),
+                                  _ptr(lse), _stream(q.device)))
+
+
+def hys_full_attn_bwd(q, k, v, o, lse, d_o, dq, dk, dv, accumulate_kv: bool = False, softmax_scale: float = None):
+    """Gradients of the full layer's causal attention: dq (fp32) overwritten; dk, dv (fp32) overwritten or,
+    with accumulate_kv, added to."""
+    lib = _lib.load()
+    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), 1.0, 1.0)
+    args = [ctypes.byref(p), tensor4(q), tensor4(k), tensor4(v), tensor4(o), _ptr(lse), tensor4(d_o), tensor4(dq),
+            tensor4(dk), tensor4(dv), int(bool(accumulate_kv))]
+    nb = ctypes.c_size_t(0)
+    check(lib.hys_full_attn_bwd(*args, None, ctypes.byref(nb), None))
+    ws = _workspace(nb.value, q.device)
+    nb = ctypes.c_size_t(ws.numel())
+    check(lib.hys_full_attn_bwd(*args, _ptr(ws), ctypes.byref(nb), _stream(q.device)))
+    return ws
+
+
+def hys_sparse_layer_bwd(q, k, v, idx, k_win, v_win, window: int, gate_w, o_sparse, lse_sparse, o_win, lse_win, d_o,
+                         dq, dk, dv, dk_win, dv_win, dgate_w, accumulate_kv: bool = False, gate_b=None,
+                         topk: int = None, softmax_scale: float = None):
+    """Gradients of one HySparse sparse layer.  idx: [B, L, topk] block ids, or [Hkv, B, L, topk] per KV group."""
+    lib = _lib.load()
+    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), 1.0, 1.0)
+    kk = idx.shape[-1] if topk is None else topk
+    gs, ib = (idx.stride(0), idx[0]) if idx.dim() == 4 else (0, idx)
+    sp = HysSparseParams(64, kk, 1, 0, ib.stride(0), ib.stride(1), gs)
+    args = [ctypes.byref(p), tensor4(q), tensor4(k), tensor4(v), ctypes.byref(sp), _ptr(idx), tensor4(k_win),
+            tensor4(v_win), window, _ptr(gate_w), _ptr(gate_b), tensor4(o_sparse), _ptr(lse_sparse), tensor4(o_win),
+            _ptr(lse_win), tensor4(d_o), tensor4(dq), tensor4(dk), tensor4(dv), int(bool(accumulate_kv)),
+            tensor4(dk_win), tensor4(dv_win), _ptr(dgate_w)]
+    nb = ctypes.c_size_t(0)
+    check(lib.hys_sparse_layer_bwd(*args, None, ctypes.byref(nb), None))
+    ws = _workspace(nb.value, q.device)
+    nb = ctypes.c_size_t(ws.numel())
+    check(lib.hys_sparse_layer_bwd(*args, _ptr(ws), ctypes.byref(nb), _stream(q.device)))
+    return ws
+
+
 def abi_version() -> int:
     return _lib.load().hys_abi_version()

@@ -29,17 +29,26 @@
  *                          and every sparse layer (block gather, ring window
  *                          cache with append, gate) for one new query
  *
- * and the step that fills HySparse2's shared cache:
+ * the step that fills HySparse2's shared cache:
  *
  *   hys_kv_bridge_fwd    - KV Bridging: a cross-decoder full layer's K/V
  *                          projected from hidden states into the fp8 cache
+ *
+ * and the backward pass of the HySparse block (training):
+ *
+ *   hys_window_attn_fwd  - the window branch alone, with its LSE (the
+ *                          forward quantity the sparse layer's backward needs)
+ *   hys_full_attn_bwd    - gradients of the full layer's causal attention
+ *   hys_sparse_layer_bwd - gradients of one sparse layer (block-sparse
+ *                          branch, window branch, gate)
  *
  * Conventions shared by every call
  * --------------------------------
  * Memory:   every tensor pointer is device memory owned by the caller (for
  *           example allocated by PyTorch).  The library allocates nothing,
  *           keeps no pointer after returning and holds no global mutable state.
- *           Inputs are only read; outputs are fully overwritten.
+ *           Inputs are only read; outputs are fully overwritten (except
+ *           where a call documents an accumulate flag).
  * Streams:  work is enqueued on `stream` (a hipStream_t; NULL = the default
  *           stream) and the call returns without waiting.  Keep every buffer
  *           alive until the stream has finished the work.
@@ -76,7 +85,7 @@
 extern "C" {
 #endif
 
-#define HYS_ABI_VERSION 2
+#define HYS_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define HYS_API __attribute__((visibility("default")))
@@ -390,6 +399,80 @@ typedef struct {
  */
 HYS_API hys_status hys_kv_bridge_fwd(const hys_bridge_params* p, hys_tensor4 h, const void* w_k, const void* w_v,
                                      hys_tensor4 k_cache, hys_tensor4 v_cache, float* amax, void* stream);
+
+/*
+ * Backward pass of the HySparse block.
+ *
+ * The pages say the hybrid structure is trained directly (QbitAI HySparse
+ * article, opening summary; demingchina commentary, section 06).  The
+ * selection is held fixed (top-k passes no gradient), so every branch's
+ * gradients are those of softmax attention over its visible set J(i):
+ *   P = softmax_J(S), S = scale * q k^T:  dV = P^T dO,  dS = P * (dO v^T - rowsum(dO * O)),
+ *   dQ = scale * dS k,  dK = scale * dS^T q,
+ * summed over the G query heads of each KV head.  All gradients are fp32;
+ * q, k, v and their window counterparts must be bf16 with p->k_scale =
+ * p->v_scale = 1.  P and dS are rounded to bf16 before their products (as P
+ * is in the forward).  dK/dV of the shared cache can accumulate (accumulate_kv
+ * = 1 adds into dk, dv instead of overwriting them) so that the full layer and
+ * every sparse layer of a block sum into one buffer, in call order.
+ */
+
+/*
+ * hys_window_attn_fwd - sliding-window attention alone: O and LSE of the
+ * window branch of hys_swa_gate_fwd, without the gate (window [max(0,
+ * i-window+1), i] over k_win, v_win).  q, k_win, v_win as for
+ * hys_swa_gate_fwd; o [B, L, Hq, D] fp32 or bf16; lse [B, Hq, L] fp32
+ * (natural log) or NULL.  No workspace.
+ */
+HYS_API hys_status hys_window_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k_win, hys_tensor4 v_win,
+                                       int32_t window, hys_tensor4 o, float* lse, void* stream);
+
+/*
+ * hys_full_attn_bwd - gradients of the full layer's causal attention.
+ *
+ * q [B, L, Hq, D], k, v [B, L, Hkv, D] bf16 (k and v with one set of
+ * strides); o (fp32 or bf16) and lse [B, Hq, L] from hys_full_attn_fwd; d_o
+ * [B, L, Hq, D] bf16, the upstream gradient.  dq [B, L, Hq, D] fp32 is
+ * overwritten; dk, dv [B, L, Hkv, D] fp32 (one set of strides) are
+ * overwritten, or added to with accumulate_kv = 1.  Workspace: rowsum(dO * O),
+ * 4*B*Hq*L bytes.
+ */
+HYS_API hys_status hys_full_attn_bwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v,
+                                     hys_tensor4 o, const float* lse, hys_tensor4 d_o, hys_tensor4 dq, hys_tensor4 dk,
+                                     hys_tensor4 dv, int32_t accumulate_kv, void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * hys_sparse_layer_bwd - gradients of one HySparse sparse layer
+ * (hys_sparse_layer_fwd's computation: block-sparse branch over the shared
+ * k, v at the selected blocks, window branch over k_win, v_win, sigmoid gate).
+ *
+ * With g = sigmoid(<q, gate_w[h]> + gate_b[h]) and o = g O_sp + (1-g) O_w
+ * (o = O_w where lse_sparse = -inf), the upstream gradient d_o splits into
+ * g d_o for the sparse branch and (1-g) d_o for the window branch, and the
+ * gate adds dz = g (1-g) <d_o, O_sp - O_w> to the layer:
+ *   dq += dz gate_w[h],   dgate_w[h] = sum over (b, i) of dz q[b,i,h,:].
+ * Inputs: q bf16; k, v (shared) and k_win, v_win bf16 of equal shapes (k and
+ * v with one set of strides, k_win and v_win with one set); sp and idx as
+ * for hys_sparse_attn_fwd with granularity 64, q_tile 1, no forced window
+ * (idx_group_stride for per-KV-group sets); o_sparse, lse_sparse from
+ * hys_sparse_attn_fwd and o_win, lse_win from hys_window_attn_fwd (outputs
+ * fp32 or bf16, lse [B, Hq, L]); gate_w [Hq, D] fp32, gate_b [Hq] or NULL;
+ * d_o [B, L, Hq, D] fp32 or bf16.
+ * Outputs (fp32): dq [B, L, Hq, D] overwritten; dk, dv [B, L, Hkv, D] (one
+ * set of strides) overwritten or, with accumulate_kv = 1, added to; dk_win,
+ * dv_win [B, L, Hkv, D] (one set of strides) overwritten; dgate_w [Hq, D]
+ * contiguous, overwritten (the bias gets no gradient here: it is the sum of
+ * dz over rows).  Workspace: the two branch gradients in bf16 (2*B*L*Hq*D
+ * each), three [B, Hq, L] fp32 arrays, the selection bitmaps and the gate's
+ * partial sums (query with ws == NULL).
+ */
+HYS_API hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v,
+                                        const hys_sparse_params* sp, const int32_t* idx, hys_tensor4 k_win,
+                                        hys_tensor4 v_win, int32_t window, const float* gate_w, const float* gate_b,
+                                        hys_tensor4 o_sparse, const float* lse_sparse, hys_tensor4 o_win,
+                                        const float* lse_win, hys_tensor4 d_o, hys_tensor4 dq, hys_tensor4 dk,
+                                        hys_tensor4 dv, int32_t accumulate_kv, hys_tensor4 dk_win, hys_tensor4 dv_win,
+                                        float* dgate_w, void* ws, size_t* ws_bytes, void* stream);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 HYS_API const char* hys_last_error(void);

@@ -3,6 +3,8 @@
 Comparison rules (GPU vs the fp64 oracle):
   outputs   max |gpu - oracle| <= 2e-2 for bf16 inputs, <= 1e-4 for fp32 inputs,
             and <= 1e-2 (bf16) / 1e-5 (fp32) times the oracle's largest |value|
+  gradients max |gpu - oracle| <= 1e-2 times the oracle's largest |value| of
+            the compared tensor (bf16 inputs)
   scores    -inf positions identical; finite entries within 1e-4
   top-k     the index sets agree except inside the oracle's tie band: with s_k
             the oracle's k-th score and band = {c : |x_c - s_k| < 1e-4},
@@ -54,6 +56,25 @@ def check_out(gpu, ref, dtype="bf16", what=""):
     scale = float(np.max(np.abs(np.asarray(ref, dtype=np.float64)))) if np.size(ref) else 0.0
     assert err <= TOL_OUT[dtype], f"{what} error {err} above {TOL_OUT[dtype]}"
     assert err <= REL_OUT[dtype] * scale + 1e-7, f"{what} error {err} above {REL_OUT[dtype]} x {scale}"
+    return err
+
+
+# Gradients sum up to L terms per element (dK, dV over the query rows that see
+# a key, dQ over its visible keys), so their magnitude grows with the sequence
+# and a fixed absolute bound does not fit them.  The backward rounds P and dS
+# to bf16 (relative error up to 2^-9 each, as the forward rounds P) before
+# their products, the upstream gradient's branch split g dO to bf16, and
+# accumulates in fp32; the error of each element is then a few 2^-9 of the sum
+# of its terms' magnitudes, bounded here relative to the tensor's largest
+# magnitude.
+REL_GRAD = 1e-2
+
+
+def check_grad(gpu, ref, what=""):
+    """Gradient parity: max |gpu - ref| within REL_GRAD of the reference's largest magnitude."""
+    err = max_abs(gpu, ref)
+    scale = float(np.max(np.abs(np.asarray(ref, dtype=np.float64)))) if np.size(ref) else 0.0
+    assert err <= REL_GRAD * scale + 1e-7, f"{what} error {err} above {REL_GRAD} x {scale}"
     return err
 
 

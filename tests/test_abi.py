@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol():
     assert declared == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(lib(), name)
-    assert lib().hys_abi_version() == 2
+    assert lib().hys_abi_version() == 3
     assert lib().hys_status_string(3) == b"HYS_ERR_WORKSPACE"
 
 

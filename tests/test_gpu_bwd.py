@@ -1,0 +1,181 @@
+"""GPU parity of the backward pass against the oracle (oracle/hysparse_bwd.py).
+
+Inputs are bf16 (q, k, v, window K/V, upstream gradients) with fp32 gate
+weights; the oracle differentiates the fp64 forward on the same values.
+Gradients follow the gradient rule of tests/parity_util.py (1e-2 of the
+reference's largest magnitude: the GPU rounds P and dS to bf16 before their
+products, as the forward rounds P; gradients are sums over up to L terms, so
+no fixed absolute bound fits them); the window forward follows the output
+rule.  Selections are seeded random block sets (distinct causal blocks per row, some rows empty) given to
+both sides; the block-level test runs the whole training step on the GPU and
+checks its selection bit-exact against the oracle's before comparing
+gradients.  Sizes span several 128-key and 64-query tiles with ragged tails,
+G = 1, 2, 4 and 8, and both head dims.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import hysparse_bwd as hb
+from hybrid_sparse_attention_flash_amd import ops
+from hybrid_sparse_attention_flash_amd.block import HySparseTrainer
+from tests.parity_util import check_grad, check_out
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf(rng, *shape, s=1.0):
+    return torch.from_numpy((s * rng.standard_normal(shape)).astype(np.float32)).to(torch.bfloat16)
+
+
+def _f64(t):
+    return t.to(torch.float64).numpy()
+
+
+def _rand_sel(rng, L, k, empty_every=0):
+    """Per row: up to k distinct blocks among the causal ones, ascending, -1 padded."""
+    sel = np.full((L, k), -1, dtype=np.int32)
+    for i in range(L):
+        if empty_every and i % empty_every == 3:
+            continue
+        nb = i // 64 + 1
+        ch = np.sort(rng.choice(nb, size=min(k, nb), replace=False))
+        sel[i, :len(ch)] = ch
+    return sel
+
+
+FULL_CASES = [
+    # B, L, Hq, Hkv, D
+    (1, 300, 8, 2, 128),
+    (2, 200, 4, 4, 64),
+    (1, 520, 8, 1, 64),
+    (1, 129, 2, 1, 128),
+]
+
+
+@pytest.mark.parametrize("B,L,Hq,Hkv,D", FULL_CASES)
+def test_full_attn_bwd(B, L, Hq, Hkv, D):
+    rng = np.random.default_rng(L + Hq)
+    q, k, v = _bf(rng, B, L, Hq, D), _bf(rng, B, L, Hkv, D), _bf(rng, B, L, Hkv, D)
+    do = _bf(rng, B, L, Hq, D)
+    scale = 1.0 / math.sqrt(D)
+    dev = "cuda"
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    o = torch.empty(B, L, Hq, D, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, Hq, L, dtype=torch.float32, device=dev)
+    ops.hys_full_attn_fwd(qd, kd, vd, o, lse)
+    dq = torch.empty(B, L, Hq, D, dtype=torch.float32, device=dev)
+    dk = torch.full((B, L, Hkv, D), 7.0, dtype=torch.float32, device=dev)     # overwritten
+    dv = torch.full((B, L, Hkv, D), 7.0, dtype=torch.float32, device=dev)
+    ops.hys_full_attn_bwd(qd, kd, vd, o, lse, dod, dq, dk, dv)
+    torch.cuda.synchronize()
+    for b in range(B):
+        rq, rk, rv = hb.full_attention_bwd(_f64(q[b]), _f64(k[b]), _f64(v[b]), scale, _f64(do[b]))
+        check_grad(dq[b].cpu().numpy(), rq, "dq")
+        check_grad(dk[b].cpu().numpy(), rk, "dk")
+        check_grad(dv[b].cpu().numpy(), rv, "dv")
+    # accumulate: a second call adds the same gradient
+    ops.hys_full_attn_bwd(qd, kd, vd, o, lse, dod, dq, dk, dv, accumulate_kv=True)
+    torch.cuda.synchronize()
+    rq, rk, rv = hb.full_attention_bwd(_f64(q[0]), _f64(k[0]), _f64(v[0]), scale, _f64(do[0]))
+    check_grad(dk[0].cpu().numpy(), 2 * rk, "dk accumulated")
+    check_grad(dv[0].cpu().numpy(), 2 * rv, "dv accumulated")
+
+
+@pytest.mark.parametrize("L,Hq,Hkv,D,W", [(300, 8, 2, 128, 128), (200, 4, 1, 64, 37)])
+def test_window_attn_fwd(L, Hq, Hkv, D, W):
+    rng = np.random.default_rng(5)
+    q, kw, vw = _bf(rng, 1, L, Hq, D), _bf(rng, 1, L, Hkv, D), _bf(rng, 1, L, Hkv, D)
+    o = torch.empty(1, L, Hq, D, dtype=torch.float32, device="cuda")
+    lse = torch.empty(1, Hq, L, dtype=torch.float32, device="cuda")
+    ops.hys_window_attn_fwd(q.cuda(), kw.cuda(), vw.cuda(), W, o, lse)
+    torch.cuda.synchronize()
+    O, LSE = oracle.window_attention(_f64(q[0]), _f64(kw[0]), _f64(vw[0]), 1.0 / math.sqrt(D), W)
+    check_out(o[0].cpu().numpy(), O, "bf16", "window o")
+    assert np.abs(lse[0].cpu().numpy() - LSE).max() <= 1e-3
+
+
+SPARSE_CASES = [
+    # B, L, Hq, Hkv, D, k, window, per-group sets, dO fp32
+    (1, 330, 8, 2, 128, 3, 128, False, False),
+    (2, 200, 4, 1, 64, 2, 50, False, True),
+    (1, 300, 16, 4, 128, 2, 128, True, False),
+    (1, 260, 8, 8, 64, 4, 64, True, True),
+]
+
+
+@pytest.mark.parametrize("B,L,Hq,Hkv,D,kb,W,grouped,do32", SPARSE_CASES)
+def test_sparse_layer_bwd(B, L, Hq, Hkv, D, kb, W, grouped, do32):
+    rng = np.random.default_rng(L * 7 + Hq)
+    scale = 1.0 / math.sqrt(D)
+    q, k, v = _bf(rng, B, L, Hq, D), _bf(rng, B, L, Hkv, D), _bf(rng, B, L, Hkv, D)
+    kw, vw = _bf(rng, B, L, Hkv, D), _bf(rng, B, L, Hkv, D)
+    gw = torch.from_numpy((0.3 * rng.standard_normal((Hq, D))).astype(np.float32))
+    do = torch.from_numpy(rng.standard_normal((B, L, Hq, D)).astype(np.float32))
+    do = do if do32 else do.to(torch.bfloat16)
+    ng = Hkv if grouped else 1
+    sel = np.stack([np.stack([_rand_sel(rng, L, kb, empty_every=11) for _ in range(B)]) for _ in range(ng)])
+    dev = "cuda"
+    idx = torch.from_numpy(sel).to(dev)                     # [ng, B, L, kb]
+    idx_arg = idx if grouped else idx[0]
+    qd, kd, vd, kwd, vwd, gwd, dod = (t.to(dev) for t in (q, k, v, kw, vw, gw, do))
+    f32 = dict(dtype=torch.float32, device=dev)
+    o_sp, lse_sp = torch.empty(B, L, Hq, D, **f32), torch.empty(B, Hq, L, **f32)
+    o_w, lse_w = torch.empty(B, L, Hq, D, **f32), torch.empty(B, Hq, L, **f32)
+    ops.hys_sparse_attn_fwd(qd, kd, vd, idx_arg, o_sp, lse_sp, granularity=64, topk=kb)
+    ops.hys_window_attn_fwd(qd, kwd, vwd, W, o_w, lse_w)
+    dq = torch.empty(B, L, Hq, D, **f32)
+    dk, dv = torch.ones(B, L, Hkv, D, **f32), torch.ones(B, L, Hkv, D, **f32)     # accumulated into
+    dkw, dvw = torch.empty(B, L, Hkv, D, **f32), torch.empty(B, L, Hkv, D, **f32)
+    dgw = torch.empty(Hq, D, **f32)
+    ops.hys_sparse_layer_bwd(qd, kd, vd, idx_arg, kwd, vwd, W, gwd, o_sp, lse_sp, o_w, lse_w, dod, dq, dk, dv, dkw,
+                             dvw, dgw, accumulate_kv=True, topk=kb)
+    torch.cuda.synchronize()
+    dgw_ref = np.zeros((Hq, D))
+    for b in range(B):
+        r = hb.sparse_layer_bwd(_f64(q[b]), _f64(k[b]), _f64(v[b]), _f64(kw[b]), _f64(vw[b]),
+                                gw.numpy().astype(np.float64), scale, sel[0, b], 64, W, do[b].double().numpy(),
+                                sel_groups=sel[:, b] if grouped else None)
+        check_grad(dq[b].cpu().numpy(), r["dq"], "dq")
+        check_grad(dk[b].cpu().numpy() - 1.0, r["dk"], "dk")
+        check_grad(dv[b].cpu().numpy() - 1.0, r["dv"], "dv")
+        check_grad(dkw[b].cpu().numpy(), r["dkw"], "dk_win")
+        check_grad(dvw[b].cpu().numpy(), r["dvw"], "dv_win")
+        dgw_ref += r["dgate_w"]
+    check_grad(dgw.cpu().numpy(), dgw_ref, "dgate_w")
+
+
+def test_hysparse_block_training_step():
+    """Forward (saving the branches) and backward of a whole block on the GPU against the oracle."""
+    B, L, Hq, Hkv, D, nsp, kb, W = 1, 384, 8, 2, 128, 2, 2, 128
+    rng = np.random.default_rng(11)
+    scale = 1.0 / math.sqrt(D)
+    ql = [_bf(rng, B, L, Hq, D) for _ in range(nsp + 1)]
+    k, v = _bf(rng, B, L, Hkv, D), _bf(rng, B, L, Hkv, D)
+    kw = [_bf(rng, B, L, Hkv, D) for _ in range(nsp)]
+    vw = [_bf(rng, B, L, Hkv, D) for _ in range(nsp)]
+    gw = [torch.from_numpy((0.3 * rng.standard_normal((Hq, D))).astype(np.float32)) for _ in range(nsp)]
+    do_full = _bf(rng, B, L, Hq, D)
+    do_l = [_bf(rng, B, L, Hq, D) for _ in range(nsp)]
+    dev = "cuda"
+    cu = lambda xs: [x.to(dev) for x in xs]
+    tr = HySparseTrainer(B, L, Hq, Hkv, D, nsp, kb, W, device=dev)
+    args = (cu(ql), k.to(dev), v.to(dev), cu(kw), cu(vw), cu(gw))
+    tr.forward(*args)
+    tr.backward(*args, do_full.to(dev), cu(do_l))
+    torch.cuda.synchronize()
+    r = hb.hysparse_block_bwd([_f64(x[0]) for x in ql], _f64(k[0]), _f64(v[0]), [_f64(x[0]) for x in kw],
+                              [_f64(x[0]) for x in vw], [g.numpy().astype(np.float64) for g in gw], scale, 64, kb, W,
+                              _f64(do_full[0]), [_f64(x[0]) for x in do_l])
+    assert np.array_equal(tr.fwd.idx[0, 0].cpu().numpy(), r["sel"])
+    for l in range(nsp + 1):
+        check_grad(tr.dq[l][0].cpu().numpy(), r["dq"][l], f"dq {l}")
+    check_grad(tr.dk[0].cpu().numpy(), r["dk"], "dk (full + sparse layers)")
+    check_grad(tr.dv[0].cpu().numpy(), r["dv"], "dv (full + sparse layers)")
+    for l in range(nsp):
+        check_grad(tr.dkw[l][0].cpu().numpy(), r["dkw"][l], f"dk_win {l}")
+        check_grad(tr.dvw[l][0].cpu().numpy(), r["dvw"][l], f"dv_win {l}")
+        check_grad(tr.dgate_w[l].cpu().numpy(), r["dgate_w"][l], f"dgate_w {l}")
