@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 
 import synth  # noqa: E402
 from hybrid_sparse_attention_flash_amd import ops  # noqa: E402
-from hybrid_sparse_attention_flash_amd.block import HySparse2Block, HySparse2Decode, HySparseBlock  # noqa: E402
+from hybrid_sparse_attention_flash_amd.block import (HySparse2Block, HySparse2Decode, HySparseBlock,  # noqa: E402
+                                                     HySparseTrainer)
 
 METRIC = ("hybrid-block prefill tokens/s at 32k (TFLOP/s, GB/s % peak); decode us/token at 1M")
 
@@ -476,6 +477,75 @@ def bench_bridge(args, dev):
                          "traffic": traffic}}
 
 
+def bench_bwd(args, dev):
+    """Backward pass of the 32k HySparse block (the training step's attention
+    gradients): the full layer's causal gradient, then the 11 sparse layers'
+    (block-sparse branch, window branch, gate), dK/dV of the shared cache
+    accumulated over all 12 layers.  The forward that saves what the backward
+    needs runs once before the timed region."""
+    w = synth.WORKLOADS["moe80b_32k"]
+    log(f"[bench] backward: generating {w.name} inputs")
+    q = [synth.gen_q(w, l).to(dev) for l in range(w.n_sparse + 1)]
+    k, v = synth.gen_kv(w, "k")[0].to(dev), synth.gen_kv(w, "v")[0].to(dev)
+    kw = [synth.gen_window_kv(w, l + 1, "kw")[0].to(dev) for l in range(w.n_sparse)]
+    vw = [synth.gen_window_kv(w, l + 1, "vw")[0].to(dev) for l in range(w.n_sparse)]
+    gw = [synth.gen_gate_w(w, l + 1).to(dev) for l in range(w.n_sparse)]
+    dout = [synth.gen_grad_out(w, l).to(dev) for l in range(w.n_sparse + 1)]
+    tr = HySparseTrainer(w.B, w.L, w.Hq, w.Hkv, w.D, w.n_sparse, w.topk, w.window, device=dev)
+    inp = (q, k, v, kw, vw, gw)
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    tr.forward(*inp)
+    f1.record()
+    torch.cuda.synchronize()
+    fwd_ms = f0.elapsed_time(f1)
+
+    def step(timer=None):
+        def rec(nm, fn):
+            if timer is None:
+                fn()
+            else:
+                a, b = timer.span(nm)
+                a.record(); fn(); b.record()
+        f = tr.fwd
+        rec("full_bwd", lambda: ops.hys_full_attn_bwd(q[0], k, v, f.o_full, f.lse, dout[0], tr.dq[0], tr.dk, tr.dv))
+        for l in range(w.n_sparse):
+            rec("sparse_layer_bwd", lambda: ops.hys_sparse_layer_bwd(
+                q[l + 1], k, v, f._idx(), kw[l], vw[l], w.window, gw[l], tr.o_sp[l], tr.lse_sp[l], tr.o_w[l],
+                tr.lse_w[l], dout[l + 1], tr.dq[l + 1], tr.dk, tr.dv, tr.dkw[l], tr.dvw[l], tr.dgate_w[l],
+                accumulate_kv=True, topk=w.topk))
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timer = Timer()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(args.steps):
+        step(timer)
+    g1.record()
+    torch.cuda.synchronize()
+    step_ms = g0.elapsed_time(g1) / args.steps
+    per = {kk: vv / args.steps for kk, vv in timer.totals_ms().items()}
+    # algorithmic work: 10*D FLOP per visible (query, head, key) pair (recomputed
+    # QK^T, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q)
+    pairs_full = w.Hq * w.L * (w.L + 1) / 2 * w.B
+    keys_sel = sparse_keys_per_query(tr.fwd.idx[0], w.L, w.block) * w.Hq
+    win = sum(min(i + 1, w.window) for i in range(w.L)) * w.Hq * w.B
+    fl_full = 10.0 * w.D * pairs_full
+    fl_layer = 10.0 * w.D * (keys_sel + win)
+    st = {"full_bwd": {"ms_per_step": round(per["full_bwd"], 4),
+                       "tflops": round(fl_full / (per["full_bwd"] * 1e-3) / 1e12, 2)},
+          "sparse_layer_bwd": {"ms_per_step": round(per["sparse_layer_bwd"], 4), "launches_per_step": w.n_sparse,
+                               "tflops": round(w.n_sparse * fl_layer / (per["sparse_layer_bwd"] * 1e-3) / 1e12, 2)}}
+    for kk in st:
+        st[kk]["frac_mfma_bf16"] = round(st[kk]["tflops"] / PEAK_BF16_TFLOPS, 4)
+    tot = fl_full + w.n_sparse * fl_layer
+    log(f"[bench] backward {w.name}: {step_ms:.3f} ms/step (forward with saved branches {fwd_ms:.3f} ms)")
+    return {"workload": w.name, "ms_per_step": round(step_ms, 4), "tokens_per_s": round(w.L * w.B / (step_ms * 1e-3), 1),
+            "tflops": round(tot / (step_ms * 1e-3) / 1e12, 2), "forward_saving_ms": round(fwd_ms, 4),
+            "work": "10*D FLOP per visible (query, head, key) pair", "stages": st}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -487,6 +557,8 @@ def main():
     ap.add_argument("--no-hs-decode", action="store_true")
     ap.add_argument("--only-hs-decode", action="store_true", help="time only the HySparse decode step")
     ap.add_argument("--only-bridge", action="store_true", help="time only the KV Bridging projection")
+    ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--only-bwd", action="store_true", help="time only the backward pass of the 32k HySparse block")
     ap.add_argument("--cpu-rows", type=int, default=64)
     ap.add_argument("--workload", default="moe80b_32k",
                     choices=["moe80b_32k", "dense7b_16k", "hysparse2_64k", "tiny_fp32"],
@@ -522,11 +594,15 @@ def main():
     if args.only_hs_decode:
         print(json.dumps({"hs_decode": bench_hs_decode(args, dev)}), flush=True)
         return
+    if args.only_bwd:
+        print(json.dumps({"backward": bench_bwd(args, dev)}), flush=True)
+        return
     pre = bench_prefill(args, dev)
     w = pre["w"]
     dec = None if args.no_decode else bench_decode(args, dev)
     bridge = None if args.no_bridge else bench_bridge(args, dev)
     hs_dec = None if args.no_hs_decode else bench_hs_decode(args, dev)
+    bwd = None if args.no_bwd else bench_bwd(args, dev)
     cpu = None
     ablation = args.selection != "default" or args.window_mode != "forced"
     if not args.no_cpu and not ablation and pre["host"] is not None:
@@ -553,6 +629,7 @@ def main():
         "decode": dec,
         "kv_bridge": bridge,
         "hs_decode": hs_dec,
+        "backward": bwd,
     }
     print(json.dumps(out), flush=True)
 

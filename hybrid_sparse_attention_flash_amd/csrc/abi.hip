@@ -949,8 +949,11 @@ hys_status hys_full_attn_bwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
     if (!same_strides(dk, dv)) return fail(HYS_ERR_UNSUPPORTED, "dk and dv must share strides");
     if (!lse) return fail(HYS_ERR_INVALID_ARG, "null lse");
     if (accumulate_kv != 0 && accumulate_kv != 1) return fail(HYS_ERR_INVALID_ARG, "accumulate_kv must be 0 or 1");
-    const int64_t B = q.shape[0], L = q.shape[1], Hq = q.shape[2], D = q.shape[3];
-    const size_t need = (size_t)(B * Hq * L) * sizeof(float);
+    const int64_t B = q.shape[0], L = q.shape[1], Hq = q.shape[2], Hkv = k.shape[2], D = q.shape[3];
+    int srb = 1;
+    const int nsplit = hys::bwd_dkdv_plan(hys::BW_CAUSAL, (int)L, 0, &srb);
+    const size_t n_dd = up256((size_t)(B * Hq * L) * sizeof(float));
+    const size_t need = n_dd + hys::bwd_dkdv_ws_bytes(nsplit, (int)B, (int)L, (int)Hkv, (int)D);
     if (!ws) { *ws_bytes = need; return ok(); }
     if (*ws_bytes < need) return fail(HYS_ERR_WORKSPACE, "workspace %zu < required %zu bytes", *ws_bytes, need);
     if (!aligned16(ws)) return fail(HYS_ERR_INVALID_ARG, "workspace not 16-byte aligned");
@@ -968,6 +971,8 @@ hys_status hys_full_attn_bwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
     a.dO = (const uint16_t*)d_o.ptr; a.do_sb = d_o.stride[0]; a.do_st = d_o.stride[1]; a.do_sh = d_o.stride[2];
     a.lse = lse; a.Dd = Dd;
     a.acc_q = 0; a.acc_kv = accumulate_kv;
+    a.nsplit = nsplit; a.split_rb = srb;
+    hys::bwd_dkdv_bind_ws(a, (char*)ws + n_dd, (int)D);
     if ((e = hys::launch_bwd_dq(hys::BW_CAUSAL, (int)D, a, st)) != hipSuccess) return hip_status(e, "dq launch");
     return hip_status(hys::launch_bwd_dkdv(hys::BW_CAUSAL, (int)D, a, st), "dk/dv launch");
   } catch (...) {
@@ -1018,7 +1023,11 @@ hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     const size_t n_do = (size_t)(B * L * Hq * D) * 2, n_row = (size_t)(B * Hq * L) * 4;
     const size_t n_rb = (size_t)(ng * B * L * nwords) * 4, n_tb = (size_t)(ng * B * nrb * nwords) * 4;
     const size_t n_gp = hys::bwd_gate_partial_floats((int)Hq, (int)D) * 4;
-    const size_t need = 2 * up256(n_do) + 3 * up256(n_row) + up256(n_rb) + up256(n_tb) + up256(n_gp);
+    int srb = 1, wsrb = 1;
+    const int nsplit = hys::bwd_dkdv_plan(hys::BW_BLOCK, (int)L, 0, &srb);
+    hys::bwd_dkdv_plan(hys::BW_WINDOW, (int)L, window, &wsrb);
+    const size_t n_kv = hys::bwd_dkdv_ws_bytes(nsplit, (int)B, (int)L, (int)Hkv, (int)D);
+    const size_t need = 2 * up256(n_do) + 3 * up256(n_row) + up256(n_rb) + up256(n_tb) + up256(n_gp) + n_kv;
     if (!ws) { *ws_bytes = need; return ok(); }
     if (*ws_bytes < need) return fail(HYS_ERR_WORKSPACE, "workspace %zu < required %zu bytes", *ws_bytes, need);
     if (!aligned16(ws)) return fail(HYS_ERR_INVALID_ARG, "workspace not 16-byte aligned");
@@ -1031,7 +1040,8 @@ hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     float* dz = (float*)w; w += up256(n_row);
     uint32_t* rowbits = (uint32_t*)w; w += up256(n_rb);
     uint32_t* tilebits = (uint32_t*)w; w += up256(n_tb);
-    float* gpart = (float*)w;
+    float* gpart = (float*)w; w += up256(n_gp);
+    void* kvws = w;
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
 
@@ -1063,6 +1073,8 @@ hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     a.lse = lse_sparse; a.Dd = Dd_sp;
     a.rowbits = rowbits; a.tilebits = tilebits; a.nwords = (int)nwords; a.ng = (int)ng;
     a.acc_q = 1; a.acc_kv = accumulate_kv;
+    a.nsplit = nsplit; a.split_rb = srb;
+    hys::bwd_dkdv_bind_ws(a, kvws, (int)D);
     if ((e = hys::launch_bwd_dq(hys::BW_BLOCK, (int)D, a, st)) != hipSuccess) return hip_status(e, "sparse dq launch");
     if ((e = hys::launch_bwd_dkdv(hys::BW_BLOCK, (int)D, a, st)) != hipSuccess)
       return hip_status(e, "sparse dk/dv launch");
@@ -1071,6 +1083,7 @@ hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     wa.dO = do_w; wa.do_sb = do_sb; wa.do_st = do_st; wa.do_sh = D;
     wa.lse = lse_win; wa.Dd = Dd_w; wa.window = window;
     wa.acc_q = 1; wa.acc_kv = 0;
+    wa.nsplit = 1; wa.split_rb = wsrb;
     if ((e = hys::launch_bwd_dq(hys::BW_WINDOW, (int)D, wa, st)) != hipSuccess) return hip_status(e, "window dq launch");
     return hip_status(hys::launch_bwd_dkdv(hys::BW_WINDOW, (int)D, wa, st), "window dk/dv launch");
   } catch (...) {

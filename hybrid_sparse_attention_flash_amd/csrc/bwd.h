@@ -29,7 +29,21 @@ struct BwdArgs {
   const uint32_t* tilebits;   // [ng][B][nrb][nwords]: OR over the 32-row blocks, nrb = ceil(L/32)
   int nwords, ng;             // ng = 1 (one set for every KV group) or Hkv
   int acc_q, acc_kv;          // 1: add into dq / dk, dv; 0: overwrite
+  // dK/dV row split: the query rows a key tile sees are cut into nsplit ranges
+  // of split_rb 32-row blocks, one workgroup each; with nsplit > 1 each writes
+  // its partial sums (part_k, part_v: [nsplit][B][Lk][Hkv][D] fp32) and a flag
+  // (flags: one per workgroup), and a reduce pass adds the flagged partials
+  // into dk, dv in split order
+  int nsplit, split_rb;
+  float* part_k; float* part_v; int32_t* flags;
 };
+
+// Row split of the dK/dV pass for a branch: returns nsplit (1 = no split) and
+// the row blocks per split, and the workspace bytes it needs.
+int bwd_dkdv_plan(int mode, int L, int window, int* split_rb);
+size_t bwd_dkdv_ws_bytes(int nsplit, int B, int Lk, int Hkv, int D);
+// points part_k, part_v, flags into ws (bwd_dkdv_ws_bytes bytes, 16-byte aligned)
+void bwd_dkdv_bind_ws(BwdArgs& a, void* ws, int D);
 
 hipError_t launch_bwd_dkdv(int mode, int D, const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dq(int mode, int D, const BwdArgs& a, hipStream_t s);

@@ -52,11 +52,19 @@ __device__ __forceinline__ bool bw_visible(int i, int j, int L, int Lk, int wind
   return ok;
 }
 
-// transposed LDS copy of one 16-byte chunk (8 bf16 of row `row`, columns 8ch..8ch+7)
+// Transposed LDS copy of two rows' 16-byte chunks (8 bf16 each of rows 2rp and
+// 2rp+1, columns 8ch..8ch+7): column d receives one dword holding both rows.
+// With the lanes of a wave on consecutive row pairs and the row strides
+// chosen by the kernels (36, 72 elements), the 64 lanes of each store hit 64
+// distinct banks.
 template <int TS>
-__device__ __forceinline__ void store_t8(uint16_t* t, int row, int ch, bw_u32x4 v) {
+__device__ __forceinline__ void store_t8x2(uint16_t* t, int rp, int ch, bw_u32x4 v0, bw_u32x4 v1) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) t[(8 * ch + e) * TS + row] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t a = v0[e >> 1], b = v1[e >> 1];
+    const uint32_t w = (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    *(uint32_t*)&t[(8 * ch + e) * TS + 2 * rp] = w;
+  }
 }
 
 // Next row block of a dK/dV workgroup: blocks [base, rb_hi) in chunks of 64,
@@ -86,9 +94,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NC = D / 16;              // 16-wide d chunks of the S and dP contractions
   constexpr int NT = D / 32;              // 32-wide d tiles of dK and dV
   constexpr int RS = D + 8;               // row-major LDS row stride (elements)
-  constexpr int TS = 40;                  // transposed LDS row stride: 32 rows + 8
+  constexpr int TS = 36;                  // transposed LDS row stride: 32 rows + 4
   constexpr int CPR = D / 8;              // 16-byte chunks per row
-  constexpr int NPASS = 32 * CPR / 256;   // staging passes per tensor
+  constexpr int NIT = 16 * CPR;           // staging items: (row pair, chunk)
   __shared__ __attribute__((aligned(16))) uint16_t s_q[32 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t s_do[32 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t s_qt[D * TS];
@@ -100,8 +108,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, hh = lane >> 5;
   // key tiles slowest, so the long causal tiles (small k0) are dispatched first
-  const int nbh = a.Hkv * a.B;
-  const int kt = blockIdx.x / nbh, gb = blockIdx.x - kt * nbh;
+  // split slowest: the workgroups running together read the same absolute
+  // range of query rows, so their Q and dO stay in cache; within a split the
+  // key tiles (long causal tiles first) then the (batch, KV head) pairs
+  const int nbh = a.Hkv * a.B, ntk = (a.Lk + 127) / 128;
+  const int split = blockIdx.x / (ntk * nbh), tile = blockIdx.x - split * (ntk * nbh);
+  const int kt = tile / nbh, gb = tile - kt * nbh;
   const int g = gb % a.Hkv, b = gb / a.Hkv;
   const int k0 = kt * 128, kw0 = k0 + 32 * wave;
   const int gs = a.ng > 1 ? g : 0;
@@ -128,24 +140,33 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 
   int rb_hi = nrb;
   if (MODE == BW_WINDOW) rb_hi = min(nrb, (k0 + 127 + a.window - 1) / 32 + 1);
+  // this workgroup's share of the row blocks that can see the tile: absolute
+  // row blocks [split * split_rb, (split + 1) * split_rb)
+  const int rb_first = max(k0 / 32, split * a.split_rb);
+  rb_hi = min(rb_hi, (split + 1) * a.split_rb);
   uint64_t mask = 0ull;
-  int base = k0 / 32 - 64, rb = 0, h = 0;
-  bool have = next_row_block<MODE>(a, lane, gs, b, nrb, k0, rb_hi, mask, base, rb);
+  int base = rb_first - 64, rb = 0, h = 0;
+  bool have = rb_first < rb_hi && next_row_block<MODE>(a, lane, gs, b, nrb, k0, rb_hi, mask, base, rb);
+  const bool did = have;
 
-  bw_u32x4 pq[NPASS], pdo[NPASS];
+  // staging item tid (when tid < NIT): rows 2rp, 2rp+1 of the block, 16-byte chunk ch
+  const int rp = tid & 15, sch = tid >> 4;
+  const bool stager = tid < NIT;
+  bw_u32x4 pq[2], pdo[2];
   float plse = kNegInf, pdd = 0.f;
   uint32_t pbits = 0u;
   auto issue = [&](int rbi, int hq) {
     const int r0 = rbi * 32;
 #pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-      const int e = tid + 256 * p, row = e / CPR, ch = e - row * CPR, i = r0 + row;
-      const bool ok = i < a.L;
+    for (int u = 0; u < 2; ++u) {
+      const int i = r0 + 2 * rp + u;
+      const bool ok = stager && i < a.L;
       const int ii = ok ? i : 0;
-      pq[p] = ok ? *(const bw_u32x4*)(a.q + (int64_t)b * a.q_sb + (int64_t)ii * a.q_st + (int64_t)hq * a.q_sh + 8 * ch)
+      pq[u] = ok ? *(const bw_u32x4*)(a.q + (int64_t)b * a.q_sb + (int64_t)ii * a.q_st + (int64_t)hq * a.q_sh +
+                                      8 * sch)
                  : zero4();
-      pdo[p] = ok ? *(const bw_u32x4*)(a.dO + (int64_t)b * a.do_sb + (int64_t)ii * a.do_st + (int64_t)hq * a.do_sh +
-                                       8 * ch)
+      pdo[u] = ok ? *(const bw_u32x4*)(a.dO + (int64_t)b * a.do_sb + (int64_t)ii * a.do_st + (int64_t)hq * a.do_sh +
+                                       8 * sch)
                   : zero4();
     }
     if (tid < 32) {
@@ -165,13 +186,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   while (have) {
     const int cur_r0 = rb * 32;
     __syncthreads();                      // the previous step's LDS reads are done
+    if (stager) {
 #pragma unroll
-    for (int p = 0; p < NPASS; ++p) {
-      const int e = tid + 256 * p, row = e / CPR, ch = e - row * CPR;
-      *(bw_u32x4*)&s_q[row * RS + 8 * ch] = pq[p];
-      *(bw_u32x4*)&s_do[row * RS + 8 * ch] = pdo[p];
-      store_t8<TS>(s_qt, row, ch, pq[p]);
-      store_t8<TS>(s_dot, row, ch, pdo[p]);
+      for (int u = 0; u < 2; ++u) {
+        *(bw_u32x4*)&s_q[(2 * rp + u) * RS + 8 * sch] = pq[u];
+        *(bw_u32x4*)&s_do[(2 * rp + u) * RS + 8 * sch] = pdo[u];
+      }
+      store_t8x2<TS>(s_qt, rp, sch, pq[0], pq[1]);
+      store_t8x2<TS>(s_dot, rp, sch, pdo[0], pdo[1]);
     }
     if (tid < 32) { s_lse[tid] = plse * kLog2e; s_dd[tid] = pdd; }
     uint32_t selmask = 0xffffffffu;
@@ -235,6 +257,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   // dK, dV in C layout: lane (ln, hh) holds d = 32t + ln of keys kw0 + 8(i/4) + 4hh + i%4
+  if (a.nsplit > 1) {
+    if (tid == 0) a.flags[blockIdx.x] = did ? 1 : 0;
+    if (!did) return;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kw0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if (key >= a.Lk) continue;
+        const int64_t o = ((((int64_t)split * a.B + b) * a.Lk + key) * a.Hkv + g) * D + 32 * t + ln;
+        a.part_k[o] = dk_acc[t][i] * a.scale;
+        a.part_v[o] = dv_acc[t][i];
+      }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -246,6 +283,35 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       if (a.acc_kv) { a.dk[o] += kv; a.dv[o] += vv; }
       else { a.dk[o] = kv; a.dv[o] = vv; }
     }
+}
+
+// dk, dv (+)= the flagged partial sums of the row splits, in split order
+__global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdArgs a, int D) {
+  const int n4 = D / 4;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n = (int64_t)a.B * a.Lk * a.Hkv * n4;
+  if (e >= n) return;
+  const int d4 = (int)(e % n4);
+  int64_t t = e / n4;
+  const int g = (int)(t % a.Hkv);
+  t /= a.Hkv;
+  const int key = (int)(t % a.Lk), b = (int)(t / a.Lk);
+  const int nbh = a.Hkv * a.B, ntk = (a.Lk + 127) / 128;
+  const int64_t f0 = (int64_t)(key / 128) * nbh + (int64_t)b * a.Hkv + g;     // split s at f0 + s * ntk * nbh
+  const int64_t o = (int64_t)b * a.dk_sb + (int64_t)key * a.dk_st + (int64_t)g * a.dk_sh + 4 * d4;
+  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  if (a.acc_kv) {
+    sk = *(const f32x4*)(a.dk + o);
+    sv = *(const f32x4*)(a.dv + o);
+  }
+  for (int s = 0; s < a.nsplit; ++s) {
+    if (!a.flags[f0 + (int64_t)s * ntk * nbh]) continue;
+    const int64_t po = ((((int64_t)s * a.B + b) * a.Lk + key) * a.Hkv + g) * D + 4 * d4;
+    sk += *(const f32x4*)(a.part_k + po);
+    sv += *(const f32x4*)(a.part_v + po);
+  }
+  *(f32x4*)(a.dk + o) = sk;
+  *(f32x4*)(a.dv + o) = sv;
 }
 
 // Next 64-key tile of a dQ workgroup (block mode: the union of its rows' selections).
@@ -274,7 +340,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   constexpr int RS = D + 8;               // row-major K, V row stride
   constexpr int TS = 72;                  // transposed K row stride: 64 keys + 8
   constexpr int CPR = D / 8;
-  constexpr int NPASS = 64 * CPR / 256;
+  constexpr int NPASS = 32 * CPR / 256;   // staging items (key pair, chunk) per thread
   __shared__ __attribute__((aligned(16))) uint16_t s_k[64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[64 * RS];
   __shared__ __attribute__((aligned(16))) uint16_t s_kt[D * TS];
@@ -335,17 +401,22 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   if (MODE == BW_WINDOW) c = max(0, wr0 - a.window + 1) / 64 - 1;
   bool have = next_key_tile<MODE>(a, gs, b, nrb, rb0, nrbw, c_hi, bits, wi, c);
 
-  bw_u32x4 pk[NPASS], pv[NPASS];
+  // staging item e = tid + 256p: keys 2kp, 2kp+1 of the tile (kp = e % 32), 16-byte chunk e / 32
+  bw_u32x4 pk[NPASS][2], pv[NPASS][2];
   uint32_t pbits = 0u;
   auto issue = [&](int ct) {
     const int kc0 = ct * 64;
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
-      const int e = tid + 256 * p, row = e / CPR, ch = e - row * CPR, key = kc0 + row;
-      const bool ok = key < a.Lk;
-      const int64_t o = (int64_t)b * a.k_sb + (int64_t)(ok ? key : 0) * a.k_st + (int64_t)g * a.k_sh + 8 * ch;
-      pk[p] = ok ? *(const bw_u32x4*)(a.k + o) : zero4();
-      pv[p] = ok ? *(const bw_u32x4*)(a.v + o) : zero4();
+      const int e = tid + 256 * p, kp = e & 31, ch = e >> 5;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int key = kc0 + 2 * kp + u;
+        const bool ok = key < a.Lk;
+        const int64_t o = (int64_t)b * a.k_sb + (int64_t)(ok ? key : 0) * a.k_st + (int64_t)g * a.k_sh + 8 * ch;
+        pk[p][u] = ok ? *(const bw_u32x4*)(a.k + o) : zero4();
+        pv[p][u] = ok ? *(const bw_u32x4*)(a.v + o) : zero4();
+      }
     }
     if (MODE == BW_BLOCK)
       pbits = rowok ? a.rowbits[((int64_t)(gs * a.B + b) * a.L + qi) * a.nwords + (ct >> 5)] : 0u;
@@ -357,10 +428,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
-      const int e = tid + 256 * p, row = e / CPR, ch = e - row * CPR;
-      *(bw_u32x4*)&s_k[row * RS + 8 * ch] = pk[p];
-      *(bw_u32x4*)&s_v[row * RS + 8 * ch] = pv[p];
-      store_t8<TS>(s_kt, row, ch, pk[p]);
+      const int e = tid + 256 * p, kp = e & 31, ch = e >> 5;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        *(bw_u32x4*)&s_k[(2 * kp + u) * RS + 8 * ch] = pk[p][u];
+        *(bw_u32x4*)&s_v[(2 * kp + u) * RS + 8 * ch] = pv[p][u];
+      }
+      store_t8x2<TS>(s_kt, kp, ch, pk[p][0], pk[p][1]);
     }
     const bool selbit = MODE == BW_BLOCK ? ((pbits >> (cur & 31)) & 1u) != 0u : true;
     __syncthreads();
@@ -583,8 +657,12 @@ __global__ __launch_bounds__(256) void bwd_selbits_kernel(const int32_t* idx, in
 
 template <int MODE, int D>
 hipError_t dkdv_one(const BwdArgs& a, hipStream_t s) {
-  const int64_t grid = (int64_t)((a.Lk + 127) / 128) * a.Hkv * a.B;
+  const int64_t grid = (int64_t)((a.Lk + 127) / 128) * a.Hkv * a.B * a.nsplit;
   hipLaunchKernelGGL((bwd_dkdv_kernel<MODE, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  const int64_t n = (int64_t)a.B * a.Lk * a.Hkv * (D / 4);
+  hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, D);
   return hipGetLastError();
 }
 
@@ -598,6 +676,37 @@ hipError_t dq_one(const BwdArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Rows per split: 64 row blocks (2048 rows) per workgroup, or more to keep at most 16
+// splits.  The window branch's tiles see at most (127 + window) / 32 + 1 row
+// blocks and are never split.
+int bwd_dkdv_plan(int mode, int L, int window, int* split_rb) {
+  const int nrb = (L + 31) / 32;
+  int srb = 64;
+  if ((nrb + srb - 1) / srb > 16) srb = (nrb + 15) / 16;
+  if (mode == BW_WINDOW || nrb <= srb) { *split_rb = nrb > 0 ? nrb : 1; return 1; }
+  *split_rb = srb;
+  return (nrb + srb - 1) / srb;
+}
+// (splits are absolute row ranges: key tile kt's rows start at row block 4kt,
+// so its first split is the one holding that block and the earlier ones are empty)
+
+size_t bwd_dkdv_ws_bytes(int nsplit, int B, int Lk, int Hkv, int D) {
+  if (nsplit <= 1) return 0;
+  const size_t part = (size_t)nsplit * B * Lk * Hkv * D * sizeof(float);
+  const size_t flags = (size_t)((Lk + 127) / 128) * Hkv * B * nsplit * sizeof(int32_t);
+  return 2 * ((part + 255) & ~(size_t)255) + ((flags + 255) & ~(size_t)255);
+}
+
+void bwd_dkdv_bind_ws(BwdArgs& a, void* ws, int D) {
+  if (a.nsplit <= 1) { a.part_k = a.part_v = nullptr; a.flags = nullptr; return; }
+  const size_t part = (size_t)a.nsplit * a.B * a.Lk * a.Hkv * D * sizeof(float);
+  const size_t pu = (part + 255) & ~(size_t)255;
+  char* w = (char*)ws;
+  a.part_k = (float*)w;
+  a.part_v = (float*)(w + pu);
+  a.flags = (int32_t*)(w + 2 * pu);
+}
 
 hipError_t launch_bwd_dkdv(int mode, int D, const BwdArgs& a, hipStream_t s) {
   if (a.L == 0 || a.Lk == 0) return hipSuccess;

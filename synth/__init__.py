@@ -220,6 +220,13 @@ def gen_gate_w(w: Workload, layer: int, seed: int = 0) -> torch.Tensor:
     return torch.from_numpy(x)
 
 
+def gen_grad_out(w: Workload, layer: int, seed: int = 0) -> torch.Tensor:
+    """Upstream gradient of layer `layer`'s output (0 = the full layer) for the
+    backward pass: [B, L, Hq, D] bf16, N(0, 1)."""
+    x = normal(seed, w.cfg_id, f"dout{layer}", (w.B, w.L, w.Hq, w.D))
+    return to_bf16(x)
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact upcast of a stored fp32 / bf16 tensor to float64 numpy.
 

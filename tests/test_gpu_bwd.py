@@ -10,7 +10,8 @@ rule.  Selections are seeded random block sets (distinct causal blocks per row, 
 both sides; the block-level test runs the whole training step on the GPU and
 checks its selection bit-exact against the oracle's before comparing
 gradients.  Sizes span several 128-key and 64-query tiles with ragged tails,
-G = 1, 2, 4 and 8, and both head dims.
+G = 1, 2, 4 and 8, both head dims, and a length whose dK/dV pass splits the
+query rows of a key tile over several workgroups (more than 64 row blocks).
 """
 import math
 
@@ -53,6 +54,7 @@ FULL_CASES = [
     (2, 200, 4, 4, 64),
     (1, 520, 8, 1, 64),
     (1, 129, 2, 1, 128),
+    (1, 2300, 4, 1, 64),       # more than 64 row blocks: the dK/dV rows split over two workgroups
 ]
 
 
@@ -104,6 +106,7 @@ SPARSE_CASES = [
     (2, 200, 4, 1, 64, 2, 50, False, True),
     (1, 300, 16, 4, 128, 2, 128, True, False),
     (1, 260, 8, 8, 64, 4, 64, True, True),
+    (1, 2300, 4, 2, 64, 3, 128, False, False),     # split dK/dV rows
 ]
 
 
