@@ -25,9 +25,11 @@ g = sigmoid(<q, w_h>), adds
 and a row whose selected set is empty has o = O_w (no gate term, no sparse
 branch).  The shared K/V receive the full layer's gradient plus every
 sparse layer's sparse-branch gradient; each layer's own window K/V only its
-window branch's.  Rows are all L query rows: a key's gradient collects every
-query that sees it.  The functions are pinned by central finite differences
-of the forward definitions (tests/test_oracle_bwd.py).
+window branch's.  A key's gradient collects every query row that sees it;
+the functions can evaluate a subset of the rows, which gives dQ of those rows
+exactly and the key gradients of keys that no other row sees (the last keys
+of a long sequence).  The functions are pinned by central finite
+differences of the forward definitions (tests/test_oracle_bwd.py).
 """
 from __future__ import annotations
 
@@ -36,25 +38,31 @@ import numpy as np
 from .hysparse import NEG_INF, block_scores, logits, topk_rows
 
 
-def _causal(L: int, Lk: int) -> np.ndarray:
-    i = np.arange(L)[:, None]
+def _row_ids(rows, L):
+    return np.arange(L) if rows is None else np.asarray(rows, dtype=np.int64)
+
+
+def _causal(L: int, Lk: int, rows=None) -> np.ndarray:
+    i = _row_ids(rows, L)[:, None]
     j = np.arange(Lk)[None, :]
     return j <= i
 
 
-def block_allowed(sel, block: int, L: int, Lk: int) -> np.ndarray:
-    """Visible set of the block-sparse branch: j <= i and j // block in sel[i]."""
-    allowed = np.zeros((L, Lk), dtype=bool)
-    for i in range(L):
-        for c in np.asarray(sel[i]):
+def block_allowed(sel, block: int, L: int, Lk: int, rows=None) -> np.ndarray:
+    """Visible set of the block-sparse branch: j <= i and j // block in sel[r]
+    for the r-th of the query rows `rows` (all L rows by default)."""
+    ids = _row_ids(rows, L)
+    allowed = np.zeros((len(ids), Lk), dtype=bool)
+    for r in range(len(ids)):
+        for c in np.asarray(sel[r]):
             if c >= 0:
-                allowed[i, c * block:(c + 1) * block] = True
-    return allowed & _causal(L, Lk)
+                allowed[r, c * block:(c + 1) * block] = True
+    return allowed & _causal(L, Lk, rows)
 
 
-def window_allowed(L: int, Lk: int, window: int) -> np.ndarray:
+def window_allowed(L: int, Lk: int, window: int, rows=None) -> np.ndarray:
     """Visible set of the window branch: i - window < j <= i."""
-    i = np.arange(L)[:, None]
+    i = _row_ids(rows, L)[:, None]
     j = np.arange(Lk)[None, :]
     return (j <= i) & (j > i - window)
 
@@ -97,30 +105,40 @@ def masked_attention_bwd(q, k, v, scale, allowed, do):
     return dq, dk, dv, O, lse
 
 
-def full_attention_bwd(q, k, v, scale, do):
-    """Backward of the full layer's causal attention (every query row)."""
-    dq, dk, dv, _, _ = masked_attention_bwd(q, k, v, scale, _causal(q.shape[0], k.shape[0]), do)
+def full_attention_bwd(q, k, v, scale, do, rows=None):
+    """Backward of the full layer's causal attention.
+
+    With `rows`, only those query rows are evaluated: dq is theirs, and dk, dv
+    hold their rows' contributions, which is the whole gradient of every key
+    that only those rows see (for example the last keys when `rows` are the
+    rows from the first of them to the end)."""
+    ids = _row_ids(rows, q.shape[0])
+    dq, dk, dv, _, _ = masked_attention_bwd(q[ids], k, v, scale, _causal(q.shape[0], k.shape[0], rows), do[ids])
     return dq, dk, dv
 
 
-def sparse_layer_bwd(q, k, v, kw, vw, gate_w, scale, sel, block, window, do, sel_groups=None):
+def sparse_layer_bwd(q, k, v, kw, vw, gate_w, scale, sel, block, window, do, sel_groups=None, rows=None):
     """Backward of one HySparse sparse layer (block-sparse branch over the
     shared k/v, window branch over the layer's kw/vw, sigmoid gate).
 
-    sel [L, kb]: the block ids of every query row (one set for all heads), or
-    sel_groups [Hkv, L, kb]: one set per KV group (head h uses h // G).
-    Returns dict(dq, dk, dv, dkw, dvw, dgate_w) with dk, dv the contribution
-    to the shared cache.
+    sel [R, kb]: the block ids of each evaluated query row (one set for all
+    heads), or sel_groups [Hkv, R, kb]: one set per KV group (head h uses
+    h // G).  The rows are all L rows, or those in `rows` (then dq is theirs
+    and the key gradients and dgate_w hold their contributions only, as in
+    full_attention_bwd).  Returns dict(dq, dk, dv, dkw, dvw, dgate_w) with
+    dk, dv the contribution to the shared cache.
     """
     L, Hq, D = q.shape
     Lk = k.shape[0]
+    ids = _row_ids(rows, L)
     if sel_groups is None:
-        allowed_sp = block_allowed(sel, block, L, Lk)
+        allowed_sp = block_allowed(sel, block, L, Lk, rows)
     else:
         Hkv = k.shape[1]
         G = Hq // Hkv
-        allowed_sp = np.stack([block_allowed(sel_groups[h // G], block, L, Lk) for h in range(Hq)])
-    allowed_w = window_allowed(L, kw.shape[0], window)
+        allowed_sp = np.stack([block_allowed(sel_groups[h // G], block, L, Lk, rows) for h in range(Hq)])
+    allowed_w = window_allowed(L, kw.shape[0], window, rows)
+    q, do = q[ids], do[ids]
     # forward of the two branches (their O and LSE are what the gate needs)
     zero = np.zeros_like(do)
     _, _, _, o_sp, lse_sp = masked_attention_bwd(q, k, v, scale, allowed_sp, zero)

@@ -20,6 +20,7 @@ import pytest
 import torch
 
 import oracle
+import synth
 from oracle import hysparse_bwd as hb
 from hybrid_sparse_attention_flash_amd import ops
 from hybrid_sparse_attention_flash_amd.block import HySparseTrainer
@@ -182,3 +183,60 @@ def test_hysparse_block_training_step():
         check_grad(tr.dkw[l][0].cpu().numpy(), r["dkw"][l], f"dk_win {l}")
         check_grad(tr.dvw[l][0].cpu().numpy(), r["dvw"][l], f"dv_win {l}")
         check_grad(tr.dgate_w[l].cpu().numpy(), r["dgate_w"][l], f"dgate_w {l}")
+
+
+class RowView:
+    """Float64 view of a stored [L, H, D] tensor that converts only indexed rows."""
+
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, rows):
+        return self.t[torch.as_tensor(np.asarray(rows))].to(torch.float64).numpy()
+
+
+def test_moe80b_32k_backward_sampled():
+    """The 32k HySparse block (1 full + 11 sparse layers) at its full size, in
+    the launch configuration the bench times (16 row splits in the dK/dV
+    pass): dq of every layer on sampled rows, and on the last 64 keys, which
+    only the last 64 rows see, the shared dK/dV (full layer plus every sparse
+    layer's share) and each layer's window dK/dV."""
+    w = synth.WORKLOADS["moe80b_32k"]
+    print("backward 32k: generating inputs", flush=True)
+    q = [synth.gen_q(w, l) for l in range(w.n_sparse + 1)]
+    k, v = synth.gen_kv(w, "k")[0], synth.gen_kv(w, "v")[0]
+    kw = [synth.gen_window_kv(w, l + 1, "kw")[0] for l in range(w.n_sparse)]
+    vw = [synth.gen_window_kv(w, l + 1, "vw")[0] for l in range(w.n_sparse)]
+    gw = [synth.gen_gate_w(w, l + 1) for l in range(w.n_sparse)]
+    dout = [synth.gen_grad_out(w, l) for l in range(w.n_sparse + 1)]
+    dev = "cuda"
+    cu = lambda xs: [x.to(dev) for x in xs]
+    tr = HySparseTrainer(w.B, w.L, w.Hq, w.Hkv, w.D, w.n_sparse, w.topk, w.window, device=dev)
+    args = (cu(q), k.to(dev), v.to(dev), cu(kw), cu(vw), cu(gw))
+    print("backward 32k: forward and backward on the GPU", flush=True)
+    tr.forward(*args)
+    tr.backward(*args, dout[0].to(dev), cu(dout[1:]))
+    torch.cuda.synchronize()
+    L, W = w.L, w.window
+    last = np.arange(L - 64, L)
+    rows = np.concatenate([np.array([0, 63, 64, 5000, 20000]), last])
+    kf, vf = k[0].to(torch.float64).numpy(), v[0].to(torch.float64).numpy()
+    print("backward 32k: oracle selection and full layer", flush=True)
+    sel, _ = oracle.topk_rows(oracle.block_scores(RowView(q[0][0]), kf, w.scale, 64, rows), w.topk)
+    assert np.array_equal(tr.fwd.idx[0, 0][torch.as_tensor(rows)].cpu().numpy(), sel)
+    r = torch.as_tensor(rows)
+    dq0, dk, dv = hb.full_attention_bwd(RowView(q[0][0]), kf, vf, w.scale, RowView(dout[0][0]), rows=rows)
+    check_grad(tr.dq[0][0][r].cpu().numpy(), dq0, "dq full layer")
+    for l in range(w.n_sparse):
+        print(f"backward 32k: oracle sparse layer {l}", flush=True)
+        res = hb.sparse_layer_bwd(RowView(q[l + 1][0]), kf, vf, kw[l][0].to(torch.float64).numpy(),
+                                  vw[l][0].to(torch.float64).numpy(), gw[l].numpy().astype(np.float64), w.scale,
+                                  sel, 64, W, RowView(dout[l + 1][0]), rows=rows)
+        check_grad(tr.dq[l + 1][0][r].cpu().numpy(), res["dq"], f"dq layer {l}")
+        check_grad(tr.dkw[l][0][L - 64:].cpu().numpy(), res["dkw"][L - 64:], f"dk_win layer {l}")
+        check_grad(tr.dvw[l][0][L - 64:].cpu().numpy(), res["dvw"][L - 64:], f"dv_win layer {l}")
+        dk = dk + res["dk"]
+        dv = dv + res["dv"]
+    check_grad(tr.dk[0][L - 64:].cpu().numpy(), dk[L - 64:], "dk (full + 11 sparse layers)")
+    check_grad(tr.dv[0][L - 64:].cpu().numpy(), dv[L - 64:], "dv (full + 11 sparse layers)")

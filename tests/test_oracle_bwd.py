@@ -140,3 +140,21 @@ def test_all_blocks_and_saturated_gate_is_the_full_gradient():
     np.testing.assert_allclose(r["dv"], dv, rtol=0, atol=1e-12)
     np.testing.assert_allclose(r["dq"], dq, rtol=0, atol=1e-12)
     assert np.abs(r["dkw"]).max() < 1e-12 and np.abs(r["dgate_w"]).max() < 1e-12
+
+
+def test_row_subsets_give_the_same_rows_and_last_keys():
+    # dq of a row subset equals the full dq at those rows; the rows from the
+    # first of the last keys on carry every contribution to those keys
+    q, k, v, kw, vw, gw, do, sel, block, window = _layer_case(80, L=70)
+    L = q.shape[0]
+    full = hb.sparse_layer_bwd(q, k, v, kw, vw, gw, 0.45, sel, block, window, do)
+    rows = np.arange(L - 20, L)
+    part = hb.sparse_layer_bwd(q, k, v, kw, vw, gw, 0.45, sel[rows], block, window, do, rows=rows)
+    np.testing.assert_allclose(part["dq"], full["dq"][rows], rtol=0, atol=1e-12)
+    for name in ("dk", "dv", "dkw", "dvw"):
+        np.testing.assert_allclose(part[name][L - 20:], full[name][L - 20:], rtol=0, atol=1e-12, err_msg=name)
+    dq, dk, dv = hb.full_attention_bwd(q, k, v, 0.45, do)
+    pq, pk, pv = hb.full_attention_bwd(q, k, v, 0.45, do, rows=rows)
+    np.testing.assert_allclose(pq, dq[rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(pk[L - 20:], dk[L - 20:], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(pv[L - 20:], dv[L - 20:], rtol=0, atol=1e-12)
