@@ -259,3 +259,50 @@ def test_hysparse_decode_validation():
     assert call(scores=0) == INVALID
     assert call(n_sparse=17) == UNSUPPORTED
     assert call(n_sparse=0) == 0                                                # full layer only
+
+
+def test_backward_validation():
+    L_ = lib()
+    p = HysAttnParams(0.125, 1.0, 1.0)
+    q, kv = t4([1, 128, 8, 128]), t4([1, 128, 2, 128])
+    o, dq = t4([1, 128, 8, 128], dtype=0), t4([1, 128, 8, 128], dtype=0)
+    dkv = t4([1, 128, 2, 128], dtype=0)
+    nb = ctypes.c_size_t(0)
+
+    def full(q=q, k=kv, v=kv, d_o=q, dq=dq, dk=dkv, dv=dkv, lse=FAKE, acc=0, p=p, ws=None):
+        return L_.hys_full_attn_bwd(ctypes.byref(p), q, k, v, o, ctypes.c_void_p(lse) if lse else None, d_o, dq, dk,
+                                    dv, acc, ws, ctypes.byref(nb), None)
+    assert full() == 0 and nb.value >= 4 * 8 * 128                          # size query: rowsum(dO * O)
+    assert full(p=HysAttnParams(0.125, 2.0, 1.0)) == UNSUPPORTED             # k_scale != 1
+    assert full(q=t4([1, 128, 8, 128], dtype=0), d_o=t4([1, 128, 8, 128], dtype=0)) == UNSUPPORTED  # fp32 q
+    assert full(d_o=t4([1, 128, 8, 128], dtype=0)) == UNSUPPORTED           # d_o must be bf16
+    assert full(dq=t4([1, 128, 8, 128])) == UNSUPPORTED                     # bf16 gradient
+    assert full(dk=t4([1, 127, 2, 128], dtype=0)) == INVALID                # dk shape
+    assert full(dv=t4([1, 128, 2, 128], dtype=0, strides=[128 * 512, 512, 128, 1])) == UNSUPPORTED   # dk, dv strides
+    assert full(lse=0) == INVALID
+    assert full(acc=2) == INVALID
+    need = nb.value
+    nb.value = need - 1
+    assert full(ws=ctypes.c_void_p(FAKE)) == WORKSPACE
+
+    sp = HysSparseParams(64, 4, 1, 0, 512, 4, 0)
+
+    def layer(sp=sp, window=128, gate=FAKE, dgate=FAKE, kw=kv, dkw=dkv, ws=None):
+        nb.value = 0
+        return L_.hys_sparse_layer_bwd(ctypes.byref(p), q, kv, kv, ctypes.byref(sp), ctypes.c_void_p(FAKE), kw, kw,
+                                       window, ctypes.c_void_p(gate) if gate else None, None, o,
+                                       ctypes.c_void_p(FAKE), o, ctypes.c_void_p(FAKE), q, dq, dkv, dkv, 1, dkw, dkw,
+                                       ctypes.c_void_p(dgate) if dgate else None, ws, ctypes.byref(nb), None)
+    assert layer() == 0 and nb.value > 2 * 2 * 128 * 8 * 128                  # two bf16 branch gradients
+    assert layer(sp=HysSparseParams(1, 16, 64, 128, 32, 16, 0)) == UNSUPPORTED   # token granularity
+    assert layer(sp=HysSparseParams(64, 65, 1, 0, 512 * 65, 65, 0)) == UNSUPPORTED
+    assert layer(sp=HysSparseParams(64, 4, 1, 0, 512, 4, -1)) == INVALID
+    assert layer(window=0) == INVALID
+    assert layer(gate=0) == INVALID
+    assert layer(dgate=0) == INVALID
+    assert layer(kw=t4([1, 128, 2, 64]), dkw=t4([1, 128, 2, 64], dtype=0)) == INVALID   # head dims differ
+
+    def window_fwd(window=128, o=o):
+        return L_.hys_window_attn_fwd(ctypes.byref(p), q, kv, kv, window, o, None, None)
+    assert window_fwd(window=0) == INVALID
+    assert window_fwd(o=t4([1, 128, 8, 64], dtype=0)) == INVALID
