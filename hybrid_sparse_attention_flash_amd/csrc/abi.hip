@@ -771,7 +771,9 @@ hys_status hys_hysparse_decode_step(const hys_hs_decode_params* p, hys_tensor4 q
     const size_t ts_bytes = (size_t)(Hkv * B * Nmax) * sizeof(float);
     const size_t part_one = (size_t)(B * nsplit * G) * (size_t)(D + 2) * sizeof(float);
     const size_t tk = hys::topk_workspace_bytes(B, nblk, p->topk);
-    const size_t need = up(ts_bytes) + (size_t)Hkv * up(part_one) + up(tk);
+    const int hs_split = hys::hs_decode_splits(p->topk);
+    const size_t sp_bytes = (size_t)n_sparse * B * Hq * hs_split * (size_t)(D + 2) * sizeof(float);
+    const size_t need = up(ts_bytes) + (size_t)Hkv * up(part_one) + up(tk) + up(sp_bytes);
     if (!ws) { *ws_bytes = need; return ok(); }
     if (*ws_bytes < need) return fail(HYS_ERR_WORKSPACE, "workspace %zu < required %zu bytes", *ws_bytes, need);
     if (!aligned16(ws)) return fail(HYS_ERR_INVALID_ARG, "workspace not 16-byte aligned");
@@ -781,6 +783,8 @@ hys_status hys_hysparse_decode_step(const hys_hs_decode_params* p, hys_tensor4 q
     char* parts = w;
     w += (size_t)Hkv * up(part_one);
     void* tkws = w;
+    w += up(tk);
+    float* sp_part = (float*)w;
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
@@ -823,6 +827,7 @@ hys_status hys_hysparse_decode_step(const hys_hs_decode_params* p, hys_tensor4 q
       h.v = (const uint16_t*)v_cache.ptr; h.v_sb = v_cache.stride[0]; h.v_st = v_cache.stride[1]; h.v_sh = v_cache.stride[2];
       for (int64_t b = 0; b < B; ++b) h.lens[b] = (int)cache_len[b];
       h.B = (int)B; h.Hkv = (int)Hkv; h.G = (int)G; h.nlayer = n_sparse; h.topk = p->topk; h.W = (int)W;
+      h.nsplit = hs_split; h.part = sp_part;
       h.scale_log2 = logit_scale * 1.4426950408889634f;
       h.idx = idx; h.idx_sb = p->topk;
       h.q_sb = q_sparse[0].stride[0]; h.q_sh = q_sparse[0].stride[2];

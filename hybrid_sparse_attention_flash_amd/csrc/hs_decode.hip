@@ -14,13 +14,18 @@
 //
 //   hs_block_max_kernel      - block score M[b, c] = max over the KV heads'
 //                              token scores of block c (one wave per block)
-//   hs_decode_sparse_kernel  - one workgroup per (layer, sequence, KV head,
-//                              group of up to 8 of its query heads):
-//                              appends the new token to the ring, then the
-//                              two branches, each split over the 4 waves in
-//                              64-key chunks (lane = key for the logits and the
-//                              online softmax, lane = head dim for P V) and
-//                              merged in LDS, then the gate.
+//   hs_decode_sparse_kernel  - per (layer, sequence, KV head, group of up to
+//                              8 of its query heads), ceil(topk / 4) + 1
+//                              workgroups: each of the first takes 4 selected
+//                              blocks, one per wave, the last the window (and
+//                              appends the new token to the ring); 64-key
+//                              chunks with lane = key for the logits and the
+//                              online softmax and lane = head dim for P V,
+//                              the waves merged in LDS, and each workgroup's
+//                              (max, sum, O) written per head
+//   hs_decode_gate_kernel    - one wave per (layer, sequence, query head):
+//                              merges the selected-block partials, then the
+//                              gate with the window branch
 #include "common.h"
 #include "kernels.h"
 
@@ -75,16 +80,17 @@ __global__ __launch_bounds__(256) void hs_decode_sparse_kernel(const HsDecArgs a
   __shared__ __attribute__((aligned(16))) float ps[4][kHsGmax][64];
   __shared__ float wm[4][kHsGmax], wl[4][kHsGmax];
   __shared__ __attribute__((aligned(16))) float wo[4][kHsGmax][D];
-  __shared__ __attribute__((aligned(16))) float res[2][kHsGmax][D];
-  __shared__ float res_l[kHsGmax];
   __shared__ int sel[kHsKmax];
 
   // wave index as a wave-uniform value, so chunk and row addresses stay scalar
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nsub = a.G / GQ;
-  const int sg = blockIdx.x % nsub;           // head sub-group
-  const int g = (blockIdx.x / nsub) % a.Hkv;
-  const int rest = blockIdx.x / (nsub * a.Hkv);
+  const int split = blockIdx.x % a.nsplit;    // 0..nsplit-2: selected blocks 4 split.., nsplit-1: window
+  const int wg = blockIdx.x / a.nsplit;
+  const bool win = split == a.nsplit - 1;
+  const int sg = wg % nsub;                   // head sub-group
+  const int g = (wg / nsub) % a.Hkv;
+  const int rest = wg / (nsub * a.Hkv);
   const int b = rest % a.B;
   const int layer = rest / a.B;
   const int n = a.lens[b];
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(256) void hs_decode_sparse_kernel(const HsDecArgs a
   {
     const int slot = (n - 1) % W;
     constexpr int U = D / 8;                 // 16-byte units per row
-    if (sg == 0 && tid < 2 * U) {
+    if (win && sg == 0 && tid < 2 * U) {
       const bool isv = tid >= U;
       const int u = isv ? tid - U : tid;
       const uint16_t* src = (isv ? a.vnew[layer] : a.knew[layer]) + (int64_t)b * a.n_sb + (int64_t)g * a.n_sh;
@@ -123,10 +129,12 @@ __global__ __launch_bounds__(256) void hs_decode_sparse_kernel(const HsDecArgs a
   const int wstart = max(0, n - W);
   const float c2 = a.scale_log2;
 
-  // br 0: the selected blocks of the shared cache (one chunk per block);
-  // br 1: the window (chunks of 64 positions from wstart)
-  for (int br = 0; br < 2; ++br) {
-    const int nchunk = br == 0 ? a.topk : (n - wstart + 63) / 64;
+  // br 0: the selected blocks of the shared cache (one chunk per block, this
+  // workgroup's four); br 1: the window (chunks of 64 positions from wstart)
+  {
+    const int br = win ? 1 : 0;
+    const int c0 = win ? 0 : 4 * split;
+    const int nchunk = win ? (n - wstart + 63) / 64 : min(a.topk, c0 + 4);
     float m[GQ], l[GQ], o[GQ][DP];
 #pragma unroll
     for (int h = 0; h < GQ; ++h) {
@@ -135,7 +143,7 @@ __global__ __launch_bounds__(256) void hs_decode_sparse_kernel(const HsDecArgs a
 #pragma unroll
       for (int e = 0; e < DP; ++e) o[h][e] = 0.f;
     }
-    for (int c = wave; c < nchunk; c += 4) {
+    for (int c = c0 + wave; c < nchunk; c += 4) {
       // keeps the query reads from LDS inside the loop (hoisted, G x D of them
       // would not fit in registers)
       __asm__ volatile("" ::: "memory");
@@ -234,6 +242,8 @@ __global__ __launch_bounds__(256) void hs_decode_sparse_kernel(const HsDecArgs a
       for (int e = 0; e < DP; ++e) wo[wave][h][DP * lane + e] = o[h][e];
     }
     __syncthreads();
+    // this workgroup's partial per head: [M, L, O / L]
+    const int Hq = a.Hkv * a.G;
     for (int i = tid; i < GQ * D; i += 256) {
       const int h = i / D, d = i - h * D;
       const float M = fmaxf(fmaxf(wm[0][h], wm[1][h]), fmaxf(wm[2][h], wm[3][h]));
@@ -246,45 +256,80 @@ __global__ __launch_bounds__(256) void hs_decode_sparse_kernel(const HsDecArgs a
           O += wo[w][h][d] * f;
         }
       }
-      res[br][h][d] = L > 0.f ? O / L : 0.f;
-      if (br == 0 && d == 0) res_l[h] = L;
-    }
-    __syncthreads();
-  }
-
-  // ---- gate: g = sigmoid(<q_h, w_h>); an empty sparse set leaves the window branch
-  for (int h = wave; h < GQ; h += 4) {
-    const float* gw = a.gate_w[layer] + (int64_t)(h0 + h) * D;
-    float z = 0.f;
-    for (int d = lane; d < D; d += 64) {
-      const uint32_t pr = qs[h][d >> 1];
-      z += __builtin_bit_cast(float, (d & 1) ? (pr & 0xffff0000u) : (pr << 16)) * gw[d];
-    }
-    z = wave_sum(z);
-    const float gt = 1.f / (1.f + __expf(-z));
-    const bool empty = !(res_l[h] > 0.f);
-    const int64_t orow = (int64_t)b * a.o_sb + (int64_t)(h0 + h) * a.o_sh;
-    for (int d = lane; d < D; d += 64) {
-      const float ow = res[1][h][d];
-      const float out = empty ? ow : gt * res[0][h][d] + (1.f - gt) * ow;
-      if (a.o_f32) ((float*)a.o[layer])[orow + d] = out;
-      else ((uint16_t*)a.o[layer])[orow + d] = f32_to_bf16(out);
+      float* pp = a.part + ((((int64_t)layer * a.B + b) * Hq + h0 + h) * a.nsplit + split) * (D + 2);
+      pp[2 + d] = L > 0.f ? O / L : 0.f;
+      if (d == 0) { pp[0] = M; pp[1] = L; }
     }
   }
 }
+
+// Merge of the selected-block partials (exact rule with a common reference)
+// and the gate: g = sigmoid(<q_h, w_h>); an empty sparse set leaves the window
+// branch.  One wave per (layer, sequence, query head), lane = head dims.
+template <int D>
+__global__ __launch_bounds__(256) void hs_decode_gate_kernel(const HsDecArgs a) {
+  constexpr int DP = D / 64;
+  const int Hq = a.Hkv * a.G;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (w >= a.nlayer * a.B * Hq) return;
+  const int h = w % Hq, b = (w / Hq) % a.B, layer = w / (Hq * a.B);
+  const int ns = a.nsplit;
+  const float* pp = a.part + (((int64_t)layer * a.B + b) * Hq + h) * ns * (D + 2);
+  float M = kNegInf;
+  for (int s = 0; s < ns - 1; ++s) M = fmaxf(M, pp[s * (D + 2)]);
+  float L = 0.f, O[DP];
+#pragma unroll
+  for (int e = 0; e < DP; ++e) O[e] = 0.f;
+  if (M != kNegInf)
+    for (int s = 0; s < ns - 1; ++s) {
+      const float ms = pp[s * (D + 2)];
+      const float f = ms == kNegInf ? 0.f : exp2f(ms - M) * pp[s * (D + 2) + 1];
+      L += f;
+#pragma unroll
+      for (int e = 0; e < DP; ++e) O[e] += f * pp[s * (D + 2) + 2 + DP * lane + e];
+    }
+  const float* pw = pp + (ns - 1) * (D + 2) + 2;
+  const uint16_t* qr = a.q[layer] + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
+  const float* gw = a.gate_w[layer] + (int64_t)h * D;
+  float z = 0.f;
+#pragma unroll
+  for (int e = 0; e < DP; ++e) z += bf16_to_f32(qr[DP * lane + e]) * gw[DP * lane + e];
+  z = wave_sum(z);
+  const float gt = 1.f / (1.f + __expf(-z));
+  const bool empty = !(L > 0.f);
+  const int64_t orow = (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;
+#pragma unroll
+  for (int e = 0; e < DP; ++e) {
+    const int d = DP * lane + e;
+    const float ow = pw[d];
+    const float out = empty ? ow : gt * (O[e] / L) + (1.f - gt) * ow;
+    if (a.o_f32) ((float*)a.o[layer])[orow + d] = out;
+    else ((uint16_t*)a.o[layer])[orow + d] = f32_to_bf16(out);
+  }
+}
+
+int hs_decode_splits(int topk) { return (topk + 3) / 4 + 1; }
 
 hipError_t launch_hs_decode_sparse(int D, const HsDecArgs& a, hipStream_t s) {
   // at most 8 query heads per workgroup
   const int gq = a.G <= 8 ? a.G : 8;
   if (a.G % gq != 0) return hipErrorInvalidValue;
-  const int64_t grid = (int64_t)a.nlayer * a.B * a.Hkv * (a.G / gq);
+  if (a.nsplit != hs_decode_splits(a.topk)) return hipErrorInvalidValue;
+  const int64_t grid = (int64_t)a.nlayer * a.B * a.Hkv * (a.G / gq) * a.nsplit;
   if (grid == 0) return hipSuccess;
+  hipError_t e = hipErrorInvalidValue;   // group size not a power of two up to 16
 #define HYS_HS_LAUNCH(DD, GG) \
-  if (D == DD && gq == GG) { hipLaunchKernelGGL((hs_decode_sparse_kernel<DD, GG>), dim3((unsigned)grid), dim3(256), 0, s, a); return hipGetLastError(); }
+  if (D == DD && gq == GG) { hipLaunchKernelGGL((hs_decode_sparse_kernel<DD, GG>), dim3((unsigned)grid), dim3(256), 0, s, a); e = hipGetLastError(); }
   HYS_HS_LAUNCH(128, 1) HYS_HS_LAUNCH(128, 2) HYS_HS_LAUNCH(128, 4) HYS_HS_LAUNCH(128, 8)
   HYS_HS_LAUNCH(64, 1) HYS_HS_LAUNCH(64, 2) HYS_HS_LAUNCH(64, 4) HYS_HS_LAUNCH(64, 8)
 #undef HYS_HS_LAUNCH
-  return hipErrorInvalidValue;   // group size not a power of two up to 16
+  if (e != hipSuccess) return e;
+  const int64_t waves = (int64_t)a.nlayer * a.B * a.Hkv * a.G;
+  if (D == 128)
+    hipLaunchKernelGGL((hs_decode_gate_kernel<128>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((hs_decode_gate_kernel<64>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace hys

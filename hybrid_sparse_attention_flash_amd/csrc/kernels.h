@@ -129,7 +129,12 @@ struct HsDecArgs {
   int64_t r_sb, r_st, r_sh;                              // rings [B, W, Hkv, D]
   const float* gate_w[kMaxDecodeLayers];                 // [Hq, D] fp32 per layer
   void* o[kMaxDecodeLayers]; int64_t o_sb, o_sh; int o_f32;       // [B, 1, Hq, D]
+  // split over workgroups: splits 0..nsplit-2 take 4 selected blocks each, the
+  // last the window; part [nlayer][B][Hq][nsplit][2 + D]: base-2 max M, sum L,
+  // normalised O of each split, merged with the gate by a second kernel
+  int nsplit; float* part;
 };
+int hs_decode_splits(int topk);
 hipError_t launch_hs_decode_sparse(int D, const HsDecArgs& a, hipStream_t s);
 
 // HySparse2 KV Bridging: K/V of a cross-decoder full layer projected from
