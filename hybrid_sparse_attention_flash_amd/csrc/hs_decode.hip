@@ -57,33 +57,39 @@ hipError_t launch_hs_block_max(const float* ts, int nparts, int64_t part_stride,
 namespace {
 constexpr int kHsGmax = 8;    // query heads per workgroup
 constexpr int kHsKmax = 64;   // selected blocks
-// native 16-byte vector (register arrays of HIP's uint4 wrapper struct end up in scratch)
+// native vectors (register arrays of HIP's uint4 wrapper struct end up in scratch)
 typedef unsigned int hs_u32x4 __attribute__((ext_vector_type(4)));
-
-// eight bf16 of a key row as fp32
-__device__ __forceinline__ void bf16x8_to_f32(hs_u32x4 r, float (&x)[8]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = __builtin_bit_cast(float, r[i] << 16);
-    x[2 * i + 1] = __builtin_bit_cast(float, r[i] & 0xffff0000u);
-  }
+typedef unsigned int hs_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8 hs_frag(hs_u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ hs_u32x4 hs_pack8(const float* x) {
+  return hs_u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
 }
 }  // namespace
 
-// GQ: query heads per workgroup, a compile-time constant so the per-head
-// softmax state stays in registers; a KV head's a.G query heads are split
-// into a.G / GQ sub-groups, one workgroup each
+// GQ: query heads per workgroup (a KV head's a.G query heads are split into
+// a.G / GQ sub-groups, one workgroup each).  Per 64-key chunk a wave runs
+//   S^T = K Q^T    v_mfma_f32_32x32x16_bf16, A = 32 key rows (loaded straight
+//                  into operand layout), B = the group's queries (columns
+//                  >= GQ zero), two 32-key tiles;
+//   softmax        per head = per lane column, the two half-waves combined;
+//   O += P V       A = P as it leaves the S MFMA (lane = head, keys in the
+//                  C-layout order, read by V in the same permuted order),
+//                  B = V^T staged per wave through LDS, 32 keys at a time.
 template <int D, int GQ>
 __global__ __launch_bounds__(256) void hs_decode_sparse_kernel(const HsDecArgs a) {
-  constexpr int DP = D / 64;                 // head dims per lane in the P V phase
+  constexpr int NC = D / 16;                 // k-steps of S
+  constexpr int NT = D / 32;                 // 32-wide d tiles of O
+  constexpr int VTS = 36;                    // V^T row stride: 32 keys + 4 (conflict-free pair stores)
   __shared__ __attribute__((aligned(16))) uint32_t qs[kHsGmax][D / 2];   // bf16 pairs
-  __shared__ __attribute__((aligned(16))) float ps[4][kHsGmax][64];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[4][D * VTS];
   __shared__ float wm[4][kHsGmax], wl[4][kHsGmax];
   __shared__ __attribute__((aligned(16))) float wo[4][kHsGmax][D];
+  __shared__ float alpha_s[4][32];
   __shared__ int sel[kHsKmax];
 
   // wave index as a wave-uniform value, so chunk and row addresses stay scalar
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 31, hh = lane >> 5;
   const int nsub = a.G / GQ;
   const int split = blockIdx.x % a.nsplit;    // 0..nsplit-2: selected blocks 4 split.., nsplit-1: window
   const int wg = blockIdx.x / a.nsplit;
@@ -111,7 +117,7 @@ __global__ __launch_bounds__(256) void hs_decode_sparse_kernel(const HsDecArgs a
       *(uint4*)(dst + 8 * u) = *(const uint4*)(src + 8 * u);
     }
   }
-  // ---- the group's queries (fp32) and the selected blocks
+  // ---- the group's queries and the selected blocks
   const uint16_t* qb = a.q[layer] + (int64_t)b * a.q_sb;
   for (int i = tid; i < kHsGmax * (D / 2); i += 256) {
     const int h = i / (D / 2), d2 = i - h * (D / 2);
@@ -119,6 +125,12 @@ __global__ __launch_bounds__(256) void hs_decode_sparse_kernel(const HsDecArgs a
   }
   if (tid < kHsKmax) sel[tid] = tid < a.topk ? a.idx[(int64_t)b * a.idx_sb + tid] : -1;
   __syncthreads();
+
+  // queries as B operand: lane (ln, hh) holds head ln, d = 16c + 8hh + [0, 8) (zero past GQ)
+  hs_u32x4 qf[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    qf[c] = ln < GQ ? *(const hs_u32x4*)&qs[ln][8 * c + 4 * hh] : hs_u32x4{0u, 0u, 0u, 0u};
 
   const uint16_t* kc = a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh;
   const uint16_t* vc = a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh;
@@ -131,135 +143,157 @@ __global__ __launch_bounds__(256) void hs_decode_sparse_kernel(const HsDecArgs a
 
   // br 0: the selected blocks of the shared cache (one chunk per block, this
   // workgroup's four); br 1: the window (chunks of 64 positions from wstart)
-  {
-    const int br = win ? 1 : 0;
-    const int c0 = win ? 0 : 4 * split;
-    const int nchunk = win ? (n - wstart + 63) / 64 : min(a.topk, c0 + 4);
-    float m[GQ], l[GQ], o[GQ][DP];
+  const int br = win ? 1 : 0;
+  const int c0 = win ? 0 : 4 * split;
+  const int nchunk = win ? (n - wstart + 63) / 64 : min(a.topk, c0 + 4);
+  float m = kNegInf, l = 0.f;                // softmax state of head ln (both half-waves)
+  f32x16 o[NT];
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      m[h] = kNegInf;
-      l[h] = 0.f;
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int e = 0; e < DP; ++e) o[h][e] = 0.f;
-    }
-    for (int c = c0 + wave; c < nchunk; c += 4) {
-      // keeps the query reads from LDS inside the loop (hoisted, G x D of them
-      // would not fit in registers)
-      __asm__ volatile("" ::: "memory");
-      // key rows of chunk c: position x = 0..63 (uniform per chunk for the P V phase)
-      const int blk = br == 0 ? __builtin_amdgcn_readfirstlane(sel[c]) : 0;   // uniform: scalar row addresses
-      auto krow = [&](int x, bool& valid) -> const uint16_t* {
-        if (br == 0) {
-          const int j = blk * 64 + x;
-          valid = blk >= 0 && j < n;
-          return kc + (int64_t)(valid ? j : 0) * a.k_st;
-        }
-        const int t = wstart + c * 64 + x;
-        valid = t < n;
-        if (t == n - 1) return kn;
-        return kr + (int64_t)((valid ? t : 0) % W) * a.r_st;
-      };
-      auto vrow = [&](int x, bool& valid) -> const uint16_t* {
-        if (br == 0) {
-          const int j = blk * 64 + x;
-          valid = blk >= 0 && j < n;
-          return vc + (int64_t)(valid ? j : 0) * a.v_st;
-        }
-        const int t = wstart + c * 64 + x;
-        valid = t < n;
-        if (t == n - 1) return vn;
-        return vr + (int64_t)((valid ? t : 0) % W) * a.r_st;
-      };
-      // logits, lane = key: the key row's loads are all issued before use
-      bool kvalid;
-      const uint16_t* kp = krow(lane, kvalid);
-      hs_u32x4 kraw[D / 8];
-#pragma unroll
-      for (int p = 0; p < D / 8; ++p) kraw[p] = *(const hs_u32x4*)(kp + 8 * p);
-      float s[GQ];
-#pragma unroll
-      for (int h = 0; h < GQ; ++h) {
-        float acc = 0.f;
-#pragma unroll
-        for (int p = 0; p < D / 8; ++p) {
-          const hs_u32x4 q4 = *(const hs_u32x4*)&qs[h][4 * p];
-          // bf16 pairs widened in place (a bf16 is the upper half of its fp32);
-          // v_dot2c_f32_bf16 gave wrong sums here although it is exact alone
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc += __builtin_bit_cast(float, kraw[p][i] << 16) * __builtin_bit_cast(float, q4[i] << 16) +
-                   __builtin_bit_cast(float, kraw[p][i] & 0xffff0000u) * __builtin_bit_cast(float, q4[i] & 0xffff0000u);
-        }
-        s[h] = acc;
+    for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
+  uint16_t* vtw = vt[wave];
+
+  for (int c = c0 + wave; c < nchunk; c += 4) {
+    const int blk = br == 0 ? __builtin_amdgcn_readfirstlane(sel[c]) : 0;   // uniform: scalar row addresses
+    // position x = 0..63 of the chunk: row pointers and validity
+    auto row = [&](int x, bool isv, bool& valid) -> const uint16_t* {
+      if (br == 0) {
+        const int j = blk * 64 + x;
+        valid = blk >= 0 && j < n;
+        return (isv ? vc : kc) + (int64_t)(valid ? j : 0) * (isv ? a.v_st : a.k_st);
       }
-      // online softmax per head over the chunk (base 2)
+      const int t = wstart + c * 64 + x;
+      valid = t < n;
+      if (t == n - 1) return isv ? vn : kn;
+      return (isv ? vr : kr) + (int64_t)((valid ? t : 0) % W) * a.r_st;
+    };
+    // K rows as A operands (key 32kt + ln, d = 16c + 8hh + [0, 8)) and the V
+    // rows this lane stages (key pairs 2(ln % 16) + {0, 1} of each 32-key tile,
+    // 16-byte chunks ln / 16 + 4u), all loads issued before use
+    hs_u32x4 kf[2][NC];
+    hs_u32x4 vraw[2][NT][2];
+    bool kval[2];
 #pragma unroll
-      for (int h = 0; h < GQ; ++h) {
-        const float sv = kvalid ? s[h] * c2 : kNegInf;
-        const float mn = fmaxf(m[h], wave_max(sv));
-        const float alpha = mn == kNegInf ? 1.f : exp2f(m[h] - mn);
-        const float pv = sv == kNegInf ? 0.f : exp2f(sv - mn);
-        l[h] = l[h] * alpha + wave_sum(pv);
-        m[h] = mn;
+    for (int kt = 0; kt < 2; ++kt) {
+      const uint16_t* kp = row(32 * kt + ln, false, kval[kt]);
 #pragma unroll
-        for (int e = 0; e < DP; ++e) o[h][e] *= alpha;
-        ps[wave][h][lane] = pv;
-      }
-      // P V, lane = head dims [DP lane, +DP), keys in batches of VB whose row
-      // loads are issued together; invalid keys read a clamped row with p = 0.
-      // ps is read by the wave that wrote it.
-      constexpr int VB = 32;                   // keys per batch of V-row loads
-#pragma unroll
-      for (int x0 = 0; x0 < 64; x0 += VB) {
-        uint32_t vraw[VB];
-#pragma unroll
-        for (int i = 0; i < VB; ++i) {
-          bool vvalid;
-          const uint16_t* vp = vrow(x0 + i, vvalid);
-          vraw[i] = DP == 2 ? *(const uint32_t*)(vp + 2 * lane) : (uint32_t)vp[lane];
-        }
-#pragma unroll
-        for (int h = 0; h < GQ; ++h) {
-#pragma unroll
-          for (int i4 = 0; i4 < VB / 4; ++i4) {
-            const f32x4 p4 = *(const f32x4*)&ps[wave][h][x0 + 4 * i4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t vv = vraw[4 * i4 + j];
-              o[h][0] += p4[j] * __builtin_bit_cast(float, vv << 16);
-              if (DP == 2) o[h][DP - 1] += p4[j] * __builtin_bit_cast(float, vv & 0xffff0000u);
-            }
-          }
-        }
-      }
+      for (int cc = 0; cc < NC; ++cc) kf[kt][cc] = *(const hs_u32x4*)(kp + 16 * cc + 8 * hh);
     }
-    // merge the four waves' partials (exact rule with a common reference)
+    const int vkp = lane & 15, vch = lane >> 4;
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      if (lane == 0) { wm[wave][h] = m[h]; wl[wave][h] = l[h]; }
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int e = 0; e < DP; ++e) wo[wave][h][DP * lane + e] = o[h][e];
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          bool vv;
+          const uint16_t* vp = row(32 * kt + 2 * vkp + e, true, vv);
+          vraw[kt][u][e] = *(const hs_u32x4*)(vp + 8 * (vch + 4 * u));
+        }
+    // S^T per 32-key tile: lane (ln, hh) holds head ln, keys 32kt + 8(i/4) + 4hh + i%4
+    f32x16 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc)
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hs_frag(kf[kt][cc]), hs_frag(qf[cc]), s[kt], 0, 0, 0);
     }
-    __syncthreads();
-    // this workgroup's partial per head: [M, L, O / L]
-    const int Hq = a.Hkv * a.G;
-    for (int i = tid; i < GQ * D; i += 256) {
-      const int h = i / D, d = i - h * D;
-      const float M = fmaxf(fmaxf(wm[0][h], wm[1][h]), fmaxf(wm[2][h], wm[3][h]));
-      float L = 0.f, O = 0.f;
-      if (M != kNegInf) {
+    // online softmax of head ln over the chunk (base 2); invalid keys are -inf
+    float cmax = kNegInf;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float f = wm[w][h] == kNegInf ? 0.f : exp2f(wm[w][h] - M);
-          L += wl[w][h] * f;
-          O += wo[w][h][d] * f;
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int x = 32 * kt + 8 * (i >> 2) + 4 * hh + (i & 3);
+        const bool ok = br == 0 ? (blk >= 0 && blk * 64 + x < n) : (wstart + c * 64 + x < n);
+        s[kt][i] = ok ? s[kt][i] * c2 : kNegInf;
+        cmax = fmaxf(cmax, s[kt][i]);
+      }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float mn = fmaxf(m, cmax);
+    const float alpha = mn == kNegInf ? 1.f : exp2f(m - mn);
+    float psum = 0.f;
+    float p[2][16];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[kt][i] = s[kt][i] == kNegInf ? 0.f : exp2f(s[kt][i] - mn);
+        psum += p[kt][i];
+      }
+    psum += __shfl_xor(psum, 32);
+    l = l * alpha + psum;
+    m = mn;
+    // rescale O: its rows are heads 8(i/4) + 4hh + i%4, whose factors lane ln = head published
+    if (hh == 0) alpha_s[wave][ln] = alpha;
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float f = alpha_s[wave][8 * (i >> 2) + 4 * hh + (i & 3)];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) o[t][i] *= f;
+    }
+    // O += P V, one 32-key tile at a time through this wave's V^T buffer
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the previous tile's V^T reads are done
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        const hs_u32x4 v0 = vraw[kt][u][0], v1 = vraw[kt][u][1];
+        const int dch = vch + 4 * u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t x0 = v0[e >> 1], x1 = v1[e >> 1];
+          const uint32_t wv = (e & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+          *(uint32_t*)&vtw[(8 * dch + e) * VTS + 2 * vkp] = wv;
         }
       }
-      float* pp = a.part + ((((int64_t)layer * a.B + b) * Hq + h0 + h) * a.nsplit + split) * (D + 2);
-      pp[2 + d] = L > 0.f ? O / L : 0.f;
-      if (d == 0) { pp[0] = M; pp[1] = L; }
+      __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const hs_u32x4 pa0 = hs_pack8(&p[kt][0]), pa1 = hs_pack8(&p[kt][8]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint16_t* tv = &vtw[(32 * t + ln) * VTS + 4 * hh];
+        const hs_u32x4 b0 = {((const hs_u32x2*)tv)[0].x, ((const hs_u32x2*)tv)[0].y,
+                             ((const hs_u32x2*)(tv + 8))[0].x, ((const hs_u32x2*)(tv + 8))[0].y};
+        const hs_u32x4 b1 = {((const hs_u32x2*)(tv + 16))[0].x, ((const hs_u32x2*)(tv + 16))[0].y,
+                             ((const hs_u32x2*)(tv + 24))[0].x, ((const hs_u32x2*)(tv + 24))[0].y};
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hs_frag(pa0), hs_frag(b0), o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hs_frag(pa1), hs_frag(b1), o[t], 0, 0, 0);
+      }
     }
+  }
+  // this wave's (max, sum, O) per head: O in C layout, lane (ln, hh) holds d =
+  // 32t + ln of heads 8(i/4) + 4hh + i%4; only heads < GQ (i < 4) are real
+  if (hh == 0 && ln < GQ) { wm[wave][ln] = m; wl[wave][ln] = l; }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * hh + i;
+    if (h < GQ)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) wo[wave][h][32 * t + ln] = o[t][i];
+  }
+  __syncthreads();
+  // the four waves merged (exact rule with a common reference); this
+  // workgroup's partial per head: [M, L, O / L]
+  const int Hq = a.Hkv * a.G;
+  for (int i = tid; i < GQ * D; i += 256) {
+    const int h = i / D, d = i - h * D;
+    const float M = fmaxf(fmaxf(wm[0][h], wm[1][h]), fmaxf(wm[2][h], wm[3][h]));
+    float L = 0.f, O = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = wm[w][h] == kNegInf ? 0.f : exp2f(wm[w][h] - M);
+        L += wl[w][h] * f;
+        O += wo[w][h][d] * f;
+      }
+    }
+    float* pp = a.part + ((((int64_t)layer * a.B + b) * Hq + h0 + h) * a.nsplit + split) * (D + 2);
+    pp[2 + d] = L > 0.f ? O / L : 0.f;
+    if (d == 0) { pp[0] = M; pp[1] = L; }
   }
 }
 
