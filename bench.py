@@ -579,7 +579,7 @@ def main():
         sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the hot path is built for a single MI355X and has no "
-              "multi-GPU mode (see DESIGN.md for how it would shard).", file=sys.stderr)
+              "multi-GPU mode; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
