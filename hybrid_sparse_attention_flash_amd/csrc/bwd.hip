@@ -220,21 +220,42 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(aq), bwf(kf[c]), s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(ad), bwf(vf[c]), dp, 0, 0, 0);
       }
-      // element i: query row 8(i/4) + 4hh + i%4 of the block, key kw0 + ln
+      // element i: query row 8(i/4) + 4hh + i%4 of the block, key kw0 + ln.
+      // A block every one of whose rows sees all 32 keys skips the
+      // per-element test (wave-uniform: away from the diagonal, the window
+      // edges, partly selected blocks and the ragged ends).
+      bool full = kw0 + 31 <= cur_r0 && cur_r0 + 31 < a.L && kw0 + 31 < a.Lk;
+      if (MODE == BW_WINDOW) full = full && kw0 > cur_r0 + 31 - a.window;
+      if (MODE == BW_BLOCK) full = full && selmask == 0xffffffffu;
       float p[16], ds[16];
       const int key = kw0 + ln;
+      if (full) {
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const f32x4 l4 = *(const f32x4*)&s_lse[8 * i4 + 4 * hh];
-        const f32x4 d4 = *(const f32x4*)&s_dd[8 * i4 + 4 * hh];
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 l4 = *(const f32x4*)&s_lse[8 * i4 + 4 * hh];
+          const f32x4 d4 = *(const f32x4*)&s_dd[8 * i4 + 4 * hh];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * i4 + e, row = 8 * i4 + 4 * hh + e;
-          const bool vis = bw_visible<MODE>(cur_r0 + row, key, a.L, a.Lk, a.window, (selmask >> row) & 1u) &&
-                           l4[e] != kNegInf;
-          const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -l4[e])) : 0.f;
-          p[i] = pv;
-          ds[i] = pv * (dp[i] - d4[e]);
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e;
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -l4[e]));
+            p[i] = pv;
+            ds[i] = pv * (dp[i] - d4[e]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 l4 = *(const f32x4*)&s_lse[8 * i4 + 4 * hh];
+          const f32x4 d4 = *(const f32x4*)&s_dd[8 * i4 + 4 * hh];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * i4 + e, row = 8 * i4 + 4 * hh + e;
+            const bool vis = bw_visible<MODE>(cur_r0 + row, key, a.L, a.Lk, a.window, (selmask >> row) & 1u) &&
+                             l4[e] != kNegInf;
+            const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -l4[e])) : 0.f;
+            p[i] = pv;
+            ds[i] = pv * (dp[i] - d4[e]);
+          }
         }
       }
       // A fragments: k-slot 8hh + j of chunk kc is row 16kc + 8(j/4) + 4hh + j%4, i.e. value 8kc + j
@@ -461,16 +482,30 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
           dp[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(av), bwf(dof[c2]), dp[kh], 0, 0, 0);
         }
       // element (kh, i): key kc0 + 32kh + 8(i/4) + 4hh + i%4, query row qi (this lane)
+      // a tile every row of the wave sees whole skips the per-element test
+      bool full = kc0 + 63 <= r0 && r0 + 31 < a.L && kc0 + 63 < a.Lk;
+      if (MODE == BW_WINDOW) full = full && kc0 > r0 + 31 - a.window;
+      if (MODE == BW_BLOCK) full = full && __ballot(!selbit) == 0ull;
       float ds[32];
+      if (full) {
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kc0 + 32 * kh + 8 * (i >> 2) + 4 * hh + (i & 3);
-          const bool vis = bw_visible<MODE>(qi, key, a.L, a.Lk, a.window, selbit) && lse2 != kNegInf;
-          const float pvv = vis ? __builtin_amdgcn_exp2f(fmaf(s[kh][i], a.scale_log2, -lse2)) : 0.f;
-          ds[16 * kh + i] = pvv * (dp[kh][i] - dd);
-        }
+          for (int i = 0; i < 16; ++i) {
+            const float pvv = __builtin_amdgcn_exp2f(fmaf(s[kh][i], a.scale_log2, -lse2));
+            ds[16 * kh + i] = pvv * (dp[kh][i] - dd);
+          }
+      } else {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kc0 + 32 * kh + 8 * (i >> 2) + 4 * hh + (i & 3);
+            const bool vis = bw_visible<MODE>(qi, key, a.L, a.Lk, a.window, selbit) && lse2 != kNegInf;
+            const float pvv = vis ? __builtin_amdgcn_exp2f(fmaf(s[kh][i], a.scale_log2, -lse2)) : 0.f;
+            ds[16 * kh + i] = pvv * (dp[kh][i] - dd);
+          }
+      }
       // dQ += dS K: k-slot 8hh + j of chunk kc is key 16kc + 8(j/4) + 4hh + j%4, i.e. value 8kc + j
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
