@@ -26,8 +26,9 @@
 namespace hys {
 
 __device__ __forceinline__ uint32_t score_key(float x) {
-  // valid iff x > -inf (NaN fails the comparison); valid keys are >= 0x00800000
-  return (x > kNegInf) ? f32_order_key(x) : 0u;
+  // valid iff x > -inf (NaN fails the comparison); valid keys are >= 0x00800000.
+  // -0 and +0 are equal scores, so both take +0's key (a tie, broken by column).
+  return (x > kNegInf) ? f32_order_key(x == 0.f ? 0.f : x) : 0u;
 }
 
 // ---------------------------------------------------------------------------

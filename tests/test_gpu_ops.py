@@ -93,7 +93,8 @@ def test_full_attention_tile_token_scores(name, L, Hq, Hkv, D):
 
 @pytest.mark.parametrize("rows,cols,k", [(300, 16, 4), (257, 512, 16), (64, 2048, 64), (33, 3000, 100),
                                          (5, 65536, 1024), (3, 200001, 1024), (4, 32768, 1000), (2, 1048576, 1024),
-                                         (7, 100, 0), (9, 40, 50)])
+                                         (7, 100, 0), (9, 40, 50), (6, 2048, 16), (6, 1000, 65), (5, 64, 64),
+                                         (8, 700, 33)])
 def test_select_topk_exact(rows, cols, k):
     """Same fp32 scores on both sides -> the index sets must be identical."""
     r = np.random.default_rng(rows * 7 + cols)
@@ -105,6 +106,10 @@ def test_select_topk_exact(rows, cols, k):
         x[2, : cols // 2] = -np.inf             # causal-like row
     if rows > 3:
         x[3, :] = 0.5                           # one value everywhere: every candidate ties
+    if rows > 4:
+        x[4, :] = -1.0
+        x[4, 1::2] = -0.0                       # -0 and +0 are equal scores: they tie, the lower column wins
+        x[4, ::4] = 0.0
     print(f"topk rows={rows} cols={cols} k={k}", flush=True)
     s = torch.from_numpy(x).cuda()
     idx = torch.full((rows, max(k, 1)), -7, dtype=torch.int32, device="cuda")[:, :k].contiguous()
