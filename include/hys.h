@@ -434,8 +434,10 @@ HYS_API hys_status hys_window_attn_fwd(const hys_attn_params* p, hys_tensor4 q, 
  * strides); o (fp32 or bf16) and lse [B, Hq, L] from hys_full_attn_fwd; d_o
  * [B, L, Hq, D] bf16, the upstream gradient.  dq [B, L, Hq, D] fp32 is
  * overwritten; dk, dv [B, L, Hkv, D] fp32 (one set of strides) are
- * overwritten, or added to with accumulate_kv = 1.  Workspace: rowsum(dO * O),
- * 4*B*Hq*L bytes.
+ * overwritten, or added to with accumulate_kv = 1.  Workspace (query with
+ * ws == NULL): rowsum(dO * O) (4*B*Hq*L bytes) and, for L above 2048, the
+ * dK/dV row splits' partial sums (up to 16 copies of dk and dv) with their
+ * flags.
  */
 HYS_API hys_status hys_full_attn_bwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v,
                                      hys_tensor4 o, const float* lse, hys_tensor4 d_o, hys_tensor4 dq, hys_tensor4 dk,
@@ -462,9 +464,10 @@ HYS_API hys_status hys_full_attn_bwd(const hys_attn_params* p, hys_tensor4 q, hy
  * set of strides) overwritten or, with accumulate_kv = 1, added to; dk_win,
  * dv_win [B, L, Hkv, D] (one set of strides) overwritten; dgate_w [Hq, D]
  * contiguous, overwritten (the bias gets no gradient here: it is the sum of
- * dz over rows).  Workspace: the two branch gradients in bf16 (2*B*L*Hq*D
- * each), three [B, Hq, L] fp32 arrays, the selection bitmaps and the gate's
- * partial sums (query with ws == NULL).
+ * dz over rows).  Workspace (query with ws == NULL): the two branch
+ * gradients in bf16 (2*B*L*Hq*D bytes each), three [B, Hq, L] fp32 arrays,
+ * the selection bitmaps, the gate's partial sums and, for L above 2048, the
+ * shared dK/dV row splits' partial sums (up to 16 copies of dk and dv).
  */
 HYS_API hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v,
                                         const hys_sparse_params* sp, const int32_t* idx, hys_tensor4 k_win,
