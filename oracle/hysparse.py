@@ -312,17 +312,20 @@ def window_attention(q, kw, vw, scale, window, rows=None):
     return attend(S, vw, G)
 
 
-def gate_merge(q_rows, gate_w, o_sp, lse_sp, o_w):
+def gate_merge(q_rows, gate_w, o_sp, lse_sp, o_w, gate_b=None):
     """Sigmoid-gated fusion of the global (sparse) and local (window) branches.
 
     [QbitAI]: the two branch outputs are fused by a lightweight sigmoid gate;
     [TechWalker]: both branches use the same query and are weighted by a
     sigmoid gate.  Reading: one scalar gate per (token, head),
-      g = 1 / (1 + exp(-<q[i,h,:], w[h,:]>)),  O = g * O_sp + (1 - g) * O_w,
-    and when the sparse set is empty (LSE_sp = -inf) the branch is absent: O = O_w.
-    q_rows [R, Hq, D]; gate_w [Hq, D]; o_sp, o_w [R, Hq, D]; lse_sp [Hq, R].
+      g = 1 / (1 + exp(-(<q[i,h,:], w[h,:]> + b[h]))),  O = g * O_sp + (1 - g) * O_w,
+    with the optional per-head bias b absent (0) in the plain reading, and
+    when the sparse set is empty (LSE_sp = -inf) the branch is absent: O = O_w.
+    q_rows [R, Hq, D]; gate_w [Hq, D]; o_sp, o_w [R, Hq, D]; lse_sp [Hq, R]; gate_b [Hq] or None.
     """
     z = np.einsum("rhd,hd->rh", q_rows, gate_w)
+    if gate_b is not None:
+        z = z + np.asarray(gate_b)[None, :]
     g = 1.0 / (1.0 + np.exp(-z))
     out = g[:, :, None] * o_sp + (1.0 - g)[:, :, None] * o_w
     empty = ~np.isfinite(np.asarray(lse_sp).T)

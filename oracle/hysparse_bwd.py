@@ -19,9 +19,9 @@ the derivatives of a loss with upstream gradient dO are
   dQ   = scale * dS k,   dK = scale * dS^T q,
 with the sums over the G query heads of a KV head collected in that head's
 dK, dV.  The sparse layer's gate o = g O_sp + (1 - g) O_w,
-g = sigmoid(<q, w_h>), adds
+g = sigmoid(<q, w_h> + b_h), adds
   dO_sp = g dO,  dO_w = (1 - g) dO,  dz = g (1 - g) <dO, O_sp - O_w>,
-  dq += dz w_h,  dw_h = sum over rows of dz q,
+  dq += dz w_h,  dw_h = sum over rows of dz q,  db_h = sum over rows of dz,
 and a row whose selected set is empty has o = O_w (no gate term, no sparse
 branch).  The shared K/V receive the full layer's gradient plus every
 sparse layer's sparse-branch gradient; each layer's own window K/V only its
@@ -117,7 +117,8 @@ def full_attention_bwd(q, k, v, scale, do, rows=None):
     return dq, dk, dv
 
 
-def sparse_layer_bwd(q, k, v, kw, vw, gate_w, scale, sel, block, window, do, sel_groups=None, rows=None):
+def sparse_layer_bwd(q, k, v, kw, vw, gate_w, scale, sel, block, window, do, sel_groups=None, rows=None,
+                     gate_b=None):
     """Backward of one HySparse sparse layer (block-sparse branch over the
     shared k/v, window branch over the layer's kw/vw, sigmoid gate).
 
@@ -125,8 +126,9 @@ def sparse_layer_bwd(q, k, v, kw, vw, gate_w, scale, sel, block, window, do, sel
     heads), or sel_groups [Hkv, R, kb]: one set per KV group (head h uses
     h // G).  The rows are all L rows, or those in `rows` (then dq is theirs
     and the key gradients and dgate_w hold their contributions only, as in
-    full_attention_bwd).  Returns dict(dq, dk, dv, dkw, dvw, dgate_w) with
-    dk, dv the contribution to the shared cache.
+    full_attention_bwd).  gate_b: the gate's optional per-head bias.  Returns
+    dict(dq, dk, dv, dkw, dvw, dgate_w, dgate_b) with dk, dv the contribution
+    to the shared cache and dgate_b the row sum of dz per head.
     """
     L, Hq, D = q.shape
     Lk = k.shape[0]
@@ -144,6 +146,8 @@ def sparse_layer_bwd(q, k, v, kw, vw, gate_w, scale, sel, block, window, do, sel
     _, _, _, o_sp, lse_sp = masked_attention_bwd(q, k, v, scale, allowed_sp, zero)
     _, _, _, o_w, _ = masked_attention_bwd(q, kw, vw, scale, allowed_w, zero)
     z = np.einsum("lhd,hd->lh", q, gate_w)
+    if gate_b is not None:
+        z = z + np.asarray(gate_b)[None, :]
     g = 1.0 / (1.0 + np.exp(-z))
     on = np.isfinite(lse_sp.T)                                   # [L, Hq]: the sparse branch exists
     g_eff = np.where(on, g, 0.0)
@@ -152,7 +156,7 @@ def sparse_layer_bwd(q, k, v, kw, vw, gate_w, scale, sel, block, window, do, sel
     dq_w, dkw, dvw, _, _ = masked_attention_bwd(q, kw, vw, scale, allowed_w, (1.0 - g_eff)[:, :, None] * do)
     dq = dq_sp + dq_w + dz[:, :, None] * gate_w[None, :, :]
     dgate_w = np.einsum("lh,lhd->hd", dz, q)
-    return dict(dq=dq, dk=dk, dv=dv, dkw=dkw, dvw=dvw, dgate_w=dgate_w)
+    return dict(dq=dq, dk=dk, dv=dv, dkw=dkw, dvw=dvw, dgate_w=dgate_w, dgate_b=dz.sum(axis=0))
 
 
 def hysparse_block_bwd(q_layers, k, v, kw_layers, vw_layers, gate_layers, scale, block, topk, window,

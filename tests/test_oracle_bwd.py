@@ -158,3 +158,28 @@ def test_row_subsets_give_the_same_rows_and_last_keys():
     np.testing.assert_allclose(pq, dq[rows], rtol=0, atol=1e-12)
     np.testing.assert_allclose(pk[L - 20:], dk[L - 20:], rtol=0, atol=1e-12)
     np.testing.assert_allclose(pv[L - 20:], dv[L - 20:], rtol=0, atol=1e-12)
+
+
+def test_sparse_layer_bwd_with_gate_bias_finite_differences():
+    q, k, v, kw, vw, gw, do, sel, block, window = _layer_case(90)
+    gb = _rand(96, q.shape[1], s=0.7)
+    scale = 0.45
+    r = hb.sparse_layer_bwd(q, k, v, kw, vw, gw, scale, sel, block, window, do, gate_b=gb)
+
+    def loss():
+        o_sp, lse_sp = hs.sparse_block_attention(q, k, v, scale, sel, block)
+        o_w, _ = hs.window_attention(q, kw, vw, scale, window)
+        return float((do * hs.gate_merge(q, gw, o_sp, lse_sp, o_w, gate_b=gb)).sum())
+    for name, x in (("dgate_b", gb), ("dq", q), ("dgate_w", gw)):
+        np.testing.assert_allclose(r[name], _fd(loss, x), rtol=0, atol=TOL, err_msg=name)
+
+
+def test_gate_bias_saturates_the_gate():
+    # a bias of +-60 gives g = 1 (sparse branch where it exists) or g = 0 (window branch)
+    q, k, v, kw, vw, gw, do, sel, block, window = _layer_case(91)
+    o_sp, lse_sp = hs.sparse_block_attention(q, k, v, 0.45, sel, block)
+    o_w, _ = hs.window_attention(q, kw, vw, 0.45, window)
+    live = np.isfinite(lse_sp.T)
+    b = np.full(q.shape[1], 60.0)
+    np.testing.assert_allclose(hs.gate_merge(q, 0 * gw, o_sp, lse_sp, o_w, gate_b=b)[live], o_sp[live], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(hs.gate_merge(q, 0 * gw, o_sp, lse_sp, o_w, gate_b=-b), o_w, rtol=0, atol=1e-12)
