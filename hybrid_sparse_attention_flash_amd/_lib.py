@@ -93,7 +93,7 @@ def load(path: str = LIB_PATH):
                                       P(sz), vp]
     lib.hys_sparse_layer_bwd.argtypes = [P(HysAttnParams), T4, T4, T4, P(HysSparseParams), vp, T4, T4,
                                          ctypes.c_int32, vp, vp, T4, vp, T4, vp, T4, T4, T4, T4, ctypes.c_int32, T4,
-                                         T4, vp, vp, P(sz), vp]
+                                         T4, vp, vp, vp, P(sz), vp]
     for name in ("hys_full_attn_fwd", "hys_select_topk", "hys_sparse_attn_fwd", "hys_swa_gate_fwd",
                  "hys_decode_step", "hys_sparse_layer_fwd", "hys_kv_bridge_fwd", "hys_hysparse_decode_step",
                  "hys_select_topk_blocks", "hys_window_attn_fwd", "hys_full_attn_bwd", "hys_sparse_layer_bwd"):

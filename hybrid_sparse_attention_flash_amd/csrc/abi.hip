@@ -990,8 +990,8 @@ hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
                                 int32_t window, const float* gate_w, const float* gate_b, hys_tensor4 o_sparse,
                                 const float* lse_sparse, hys_tensor4 o_win, const float* lse_win, hys_tensor4 d_o,
                                 hys_tensor4 dq, hys_tensor4 dk, hys_tensor4 dv, int32_t accumulate_kv,
-                                hys_tensor4 dk_win, hys_tensor4 dv_win, float* dgate_w, void* ws, size_t* ws_bytes,
-                                void* stream) {
+                                hys_tensor4 dk_win, hys_tensor4 dv_win, float* dgate_w, float* dgate_b, void* ws,
+                                size_t* ws_bytes, void* stream) {
   try {
     hys_status s;
     if (!ws_bytes) return fail(HYS_ERR_INVALID_ARG, "ws_bytes must not be null");
@@ -1064,7 +1064,7 @@ hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     ga.B = (int)B; ga.L = (int)L; ga.Hq = (int)Hq; ga.D = (int)D;
     if ((e = hys::launch_bwd_prep_gate(ga, st)) != hipSuccess) return hip_status(e, "gate preparation launch");
     if ((e = hys::launch_bwd_gate_grad(dz, (const uint16_t*)q.ptr, q.stride[0], q.stride[1], q.stride[2], (int)B,
-                                       (int)L, (int)Hq, (int)D, gpart, dgate_w, st)) != hipSuccess)
+                                       (int)L, (int)Hq, (int)D, gpart, dgate_w, dgate_b, st)) != hipSuccess)
       return hip_status(e, "gate gradient launch");
     if ((e = hys::launch_bwd_selbits(idx, sp->idx_group_stride, sp->idx_batch_stride, sp->idx_row_stride, sp->k,
                                      (int)ng, (int)B, (int)L, (int)nblk, (int)nwords, rowbits, tilebits, st)) !=

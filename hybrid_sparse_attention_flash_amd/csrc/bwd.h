@@ -75,11 +75,14 @@ struct BwdGateArgs {
 };
 hipError_t launch_bwd_prep_gate(const BwdGateArgs& a, hipStream_t s);
 
-// dgate_w[h][d] = sum over (b, i) of dz[b, h, i] * q[b, i, h, d], in fixed order:
-// partial sums over row splits into `part` (bwd_gate_partial_floats floats), then their sum
+// dgate_w[h][d] = sum over (b, i) of dz[b, h, i] * q[b, i, h, d] and, when
+// dgate_b is not null, dgate_b[h] = sum over (b, i) of dz[b, h, i], in fixed
+// order: partial sums over row splits into `part` (bwd_gate_partial_floats
+// floats), then their sum
 size_t bwd_gate_partial_floats(int Hq, int D);
 hipError_t launch_bwd_gate_grad(const float* dz, const uint16_t* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
-                                int B, int L, int Hq, int D, float* part, float* dgate_w, hipStream_t s);
+                                int B, int L, int Hq, int D, float* part, float* dgate_w, float* dgate_b,
+                                hipStream_t s);
 
 // selection bitmaps from block ids idx[g*idx_sg + b*idx_sb + i*idx_sr + j] (j < k; -1 = unused)
 hipError_t launch_bwd_selbits(const int32_t* idx, int64_t idx_sg, int64_t idx_sb, int64_t idx_sr, int k, int ng,

@@ -639,7 +639,9 @@ __global__ __launch_bounds__(256) void bwd_prep_gate_kernel(BwdGateArgs a) {
   }
 }
 
-// dgate_w partial sums: workgroup (h, split) sums rows split, split + nsplit, ...
+// dgate_w and dgate_b partial sums: workgroup (h, split) sums rows split,
+// split + nsplit, ...; part holds [kGateSplit][Hq][D] for w, then
+// [kGateSplit][Hq] for the bias (the row sum of dz)
 constexpr int kGateSplit = 64;
 
 __global__ __launch_bounds__(256) void bwd_gate_partial_kernel(const float* dz, const uint16_t* q, int64_t q_sb,
@@ -648,27 +650,42 @@ __global__ __launch_bounds__(256) void bwd_gate_partial_kernel(const float* dz, 
   __shared__ float red[256];
   const int h = blockIdx.x % Hq, split = blockIdx.x / Hq;
   const int d = threadIdx.x % D, rg = threadIdx.x / D, nrg = 256 / D;
+  __shared__ float redz[256];
   const int64_t n = (int64_t)B * L;
-  float acc = 0.f;
+  float acc = 0.f, zs = 0.f;
   for (int64_t r = (int64_t)split * nrg + rg; r < n; r += (int64_t)kGateSplit * nrg) {
     const int b = (int)(r / L), i = (int)(r - (int64_t)b * L);
     const float z = dz[((int64_t)b * Hq + h) * L + i];
     acc = fmaf(z, bf16_to_f32(q[(int64_t)b * q_sb + (int64_t)i * q_st + (int64_t)h * q_sh + d]), acc);
+    zs += z;
   }
   red[threadIdx.x] = acc;
+  redz[threadIdx.x] = zs;
   __syncthreads();
   if (rg == 0) {
     for (int k = 1; k < nrg; ++k) acc += red[k * D + d];
     part[((int64_t)split * Hq + h) * D + d] = acc;
+    if (d == 0) {
+      for (int k = 1; k < nrg; ++k) zs += redz[k * D];
+      part[(int64_t)kGateSplit * Hq * D + (int64_t)split * Hq + h] = zs;
+    }
   }
 }
 
-__global__ __launch_bounds__(256) void bwd_gate_reduce_kernel(const float* part, int Hq, int D, float* out) {
+__global__ __launch_bounds__(256) void bwd_gate_reduce_kernel(const float* part, int Hq, int D, float* out_w,
+                                                              float* out_b) {
   const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= Hq * D) return;
-  float s = 0.f;
-  for (int k = 0; k < kGateSplit; ++k) s += part[(int64_t)k * Hq * D + e];
-  out[e] = s;
+  if (e < Hq * D) {
+    float s = 0.f;
+    for (int k = 0; k < kGateSplit; ++k) s += part[(int64_t)k * Hq * D + e];
+    out_w[e] = s;
+  } else if (out_b && e < Hq * D + Hq) {
+    const int h = e - Hq * D;
+    const float* pb = part + (int64_t)kGateSplit * Hq * D;
+    float s = 0.f;
+    for (int k = 0; k < kGateSplit; ++k) s += pb[(int64_t)k * Hq + h];
+    out_b[h] = s;
+  }
 }
 
 __global__ __launch_bounds__(256) void bwd_selbits_kernel(const int32_t* idx, int64_t idx_sg, int64_t idx_sb,
@@ -785,16 +802,17 @@ hipError_t launch_bwd_prep_gate(const BwdGateArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-size_t bwd_gate_partial_floats(int Hq, int D) { return (size_t)kGateSplit * Hq * D; }
+size_t bwd_gate_partial_floats(int Hq, int D) { return (size_t)kGateSplit * Hq * (D + 1); }
 
 hipError_t launch_bwd_gate_grad(const float* dz, const uint16_t* q, int64_t q_sb, int64_t q_st, int64_t q_sh,
-                                int B, int L, int Hq, int D, float* part, float* dgate_w, hipStream_t s) {
+                                int B, int L, int Hq, int D, float* part, float* dgate_w, float* dgate_b,
+                                hipStream_t s) {
   hipLaunchKernelGGL(bwd_gate_partial_kernel, dim3((unsigned)(Hq * kGateSplit)), dim3(256), 0, s, dz, q, q_sb, q_st,
                      q_sh, B, L, Hq, D, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_gate_reduce_kernel, dim3((unsigned)((Hq * D + 255) / 256)), dim3(256), 0, s, part, Hq, D,
-                     dgate_w);
+  hipLaunchKernelGGL(bwd_gate_reduce_kernel, dim3((unsigned)((Hq * D + Hq + 255) / 256)), dim3(256), 0, s, part, Hq,
+                     D, dgate_w, dgate_b);
   return hipGetLastError();
 }
 

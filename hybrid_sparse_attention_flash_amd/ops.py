@@ -217,8 +217,9 @@ def hys_full_attn_bwd(q, k, v, o, lse, d_o, dq, dk, dv, accumulate_kv: bool = Fa
 
 def hys_sparse_layer_bwd(q, k, v, idx, k_win, v_win, window: int, gate_w, o_sparse, lse_sparse, o_win, lse_win, d_o,
                          dq, dk, dv, dk_win, dv_win, dgate_w, accumulate_kv: bool = False, gate_b=None,
-                         topk: int = None, softmax_scale: float = None):
-    """Gradients of one HySparse sparse layer.  idx: [B, L, topk] block ids, or [Hkv, B, L, topk] per KV group."""
+                         topk: int = None, softmax_scale: float = None, dgate_b=None):
+    """Gradients of one HySparse sparse layer.  idx: [B, L, topk] block ids, or [Hkv, B, L, topk] per KV group.
+    dgate_b: [Hq] fp32 for the gate bias's gradient, or None."""
     lib = _lib.load()
     p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), 1.0, 1.0)
     kk = idx.shape[-1] if topk is None else topk
@@ -227,7 +228,7 @@ def hys_sparse_layer_bwd(q, k, v, idx, k_win, v_win, window: int, gate_w, o_spar
     args = [ctypes.byref(p), tensor4(q), tensor4(k), tensor4(v), ctypes.byref(sp), _ptr(idx), tensor4(k_win),
             tensor4(v_win), window, _ptr(gate_w), _ptr(gate_b), tensor4(o_sparse), _ptr(lse_sparse), tensor4(o_win),
             _ptr(lse_win), tensor4(d_o), tensor4(dq), tensor4(dk), tensor4(dv), int(bool(accumulate_kv)),
-            tensor4(dk_win), tensor4(dv_win), _ptr(dgate_w)]
+            tensor4(dk_win), tensor4(dv_win), _ptr(dgate_w), _ptr(dgate_b)]
     nb = ctypes.c_size_t(0)
     check(lib.hys_sparse_layer_bwd(*args, None, ctypes.byref(nb), None))
     ws = _workspace(nb.value, q.device)

@@ -85,7 +85,7 @@
 extern "C" {
 #endif
 
-#define HYS_ABI_VERSION 3
+#define HYS_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define HYS_API __attribute__((visibility("default")))
@@ -452,7 +452,8 @@ HYS_API hys_status hys_full_attn_bwd(const hys_attn_params* p, hys_tensor4 q, hy
  * (o = O_w where lse_sparse = -inf), the upstream gradient d_o splits into
  * g d_o for the sparse branch and (1-g) d_o for the window branch, and the
  * gate adds dz = g (1-g) <d_o, O_sp - O_w> to the layer:
- *   dq += dz gate_w[h],   dgate_w[h] = sum over (b, i) of dz q[b,i,h,:].
+ *   dq += dz gate_w[h],   dgate_w[h] = sum over (b, i) of dz q[b,i,h,:],
+ *   dgate_b[h] = sum over (b, i) of dz.
  * Inputs: q bf16; k, v (shared) and k_win, v_win bf16 of equal shapes (k and
  * v with one set of strides, k_win and v_win with one set); sp and idx as
  * for hys_sparse_attn_fwd with granularity 64, q_tile 1, no forced window
@@ -463,8 +464,8 @@ HYS_API hys_status hys_full_attn_bwd(const hys_attn_params* p, hys_tensor4 q, hy
  * Outputs (fp32): dq [B, L, Hq, D] overwritten; dk, dv [B, L, Hkv, D] (one
  * set of strides) overwritten or, with accumulate_kv = 1, added to; dk_win,
  * dv_win [B, L, Hkv, D] (one set of strides) overwritten; dgate_w [Hq, D]
- * contiguous, overwritten (the bias gets no gradient here: it is the sum of
- * dz over rows).  Workspace (query with ws == NULL): the two branch
+ * contiguous, overwritten; dgate_b [Hq] (the bias's gradient, the row sum of
+ * dz) overwritten, or NULL when not wanted.  Workspace (query with ws == NULL): the two branch
  * gradients in bf16 (2*B*L*Hq*D bytes each), three [B, Hq, L] fp32 arrays,
  * the selection bitmaps, the gate's partial sums and, for L above 2048, the
  * shared dK/dV row splits' partial sums (up to 16 copies of dk and dv).
@@ -475,7 +476,7 @@ HYS_API hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q,
                                         hys_tensor4 o_sparse, const float* lse_sparse, hys_tensor4 o_win,
                                         const float* lse_win, hys_tensor4 d_o, hys_tensor4 dq, hys_tensor4 dk,
                                         hys_tensor4 dv, int32_t accumulate_kv, hys_tensor4 dk_win, hys_tensor4 dv_win,
-                                        float* dgate_w, void* ws, size_t* ws_bytes, void* stream);
+                                        float* dgate_w, float* dgate_b, void* ws, size_t* ws_bytes, void* stream);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 HYS_API const char* hys_last_error(void);

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol():
     assert declared == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(lib(), name)
-    assert lib().hys_abi_version() == 3
+    assert lib().hys_abi_version() == 4
     assert lib().hys_status_string(3) == b"HYS_ERR_WORKSPACE"
 
 
@@ -292,7 +292,7 @@ def test_backward_validation():
         return L_.hys_sparse_layer_bwd(ctypes.byref(p), q, kv, kv, ctypes.byref(sp), ctypes.c_void_p(FAKE), kw, kw,
                                        window, ctypes.c_void_p(gate) if gate else None, None, o,
                                        ctypes.c_void_p(FAKE), o, ctypes.c_void_p(FAKE), q, dq, dkv, dkv, 1, dkw, dkw,
-                                       ctypes.c_void_p(dgate) if dgate else None, ws, ctypes.byref(nb), None)
+                                       ctypes.c_void_p(dgate) if dgate else None, None, ws, ctypes.byref(nb), None)
     assert layer() == 0 and nb.value > 2 * 2 * 128 * 8 * 128                  # two bf16 branch gradients
     assert layer(sp=HysSparseParams(1, 16, 64, 128, 32, 16, 0)) == UNSUPPORTED   # token granularity
     assert layer(sp=HysSparseParams(64, 65, 1, 0, 512 * 65, 65, 0)) == UNSUPPORTED

@@ -240,3 +240,37 @@ def test_moe80b_32k_backward_sampled():
         dv = dv + res["dv"]
     check_grad(tr.dk[0][L - 64:].cpu().numpy(), dk[L - 64:], "dk (full + 11 sparse layers)")
     check_grad(tr.dv[0][L - 64:].cpu().numpy(), dv[L - 64:], "dv (full + 11 sparse layers)")
+
+
+def test_sparse_layer_bwd_gate_bias():
+    """The gate with a per-head bias: dq, dgate_w and the bias gradient dgate_b."""
+    B, L, Hq, Hkv, D, kb, W = 1, 330, 8, 2, 128, 3, 128
+    rng = np.random.default_rng(1234)
+    scale = 1.0 / math.sqrt(D)
+    q, k, v = _bf(rng, B, L, Hq, D), _bf(rng, B, L, Hkv, D), _bf(rng, B, L, Hkv, D)
+    kw, vw = _bf(rng, B, L, Hkv, D), _bf(rng, B, L, Hkv, D)
+    gw = torch.from_numpy((0.3 * rng.standard_normal((Hq, D))).astype(np.float32))
+    gb = torch.from_numpy((0.8 * rng.standard_normal(Hq)).astype(np.float32))
+    do = _bf(rng, B, L, Hq, D)
+    sel = _rand_sel(rng, L, kb, empty_every=11)
+    dev = "cuda"
+    idx = torch.from_numpy(sel)[None].to(dev)
+    qd, kd, vd, kwd, vwd = (t.to(dev) for t in (q, k, v, kw, vw))
+    f32 = dict(dtype=torch.float32, device=dev)
+    o_sp, lse_sp = torch.empty(B, L, Hq, D, **f32), torch.empty(B, Hq, L, **f32)
+    o_w, lse_w = torch.empty(B, L, Hq, D, **f32), torch.empty(B, Hq, L, **f32)
+    ops.hys_sparse_attn_fwd(qd, kd, vd, idx, o_sp, lse_sp, granularity=64, topk=kb)
+    ops.hys_window_attn_fwd(qd, kwd, vwd, W, o_w, lse_w)
+    dq = torch.empty(B, L, Hq, D, **f32)
+    dk, dv = torch.empty(B, L, Hkv, D, **f32), torch.empty(B, L, Hkv, D, **f32)
+    dkw, dvw = torch.empty(B, L, Hkv, D, **f32), torch.empty(B, L, Hkv, D, **f32)
+    dgw, dgb = torch.empty(Hq, D, **f32), torch.full((Hq,), 7.0, **f32)
+    ops.hys_sparse_layer_bwd(qd, kd, vd, idx, kwd, vwd, W, gw.to(dev), o_sp, lse_sp, o_w, lse_w, do.to(dev), dq, dk,
+                             dv, dkw, dvw, dgw, gate_b=gb.to(dev), topk=kb, dgate_b=dgb)
+    torch.cuda.synchronize()
+    r = hb.sparse_layer_bwd(_f64(q[0]), _f64(k[0]), _f64(v[0]), _f64(kw[0]), _f64(vw[0]), gw.numpy().astype(np.float64),
+                            scale, sel, 64, W, _f64(do[0]), gate_b=gb.numpy().astype(np.float64))
+    check_grad(dq[0].cpu().numpy(), r["dq"], "dq (biased gate)")
+    check_grad(dk[0].cpu().numpy(), r["dk"], "dk (biased gate)")
+    check_grad(dgw.cpu().numpy(), r["dgate_w"], "dgate_w (biased gate)")
+    check_grad(dgb.cpu().numpy(), r["dgate_b"], "dgate_b")
