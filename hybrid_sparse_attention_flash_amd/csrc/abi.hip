@@ -3,6 +3,7 @@
 // and leave a thread-local message (see include/hys.h for the contract).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -769,19 +770,22 @@ hys_status hys_hysparse_decode_step(const hys_hs_decode_params* p, hys_tensor4 q
     if ((int64_t)nsplit * 8 > ntiles) nsplit = (int)((ntiles + 7) / 8);
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t ts_bytes = (size_t)(Hkv * B * Nmax) * sizeof(float);
-    const size_t part_one = (size_t)(B * nsplit * G) * (size_t)(D + 2) * sizeof(float);
     const size_t tk = hys::topk_workspace_bytes(B, nblk, p->topk);
     const int hs_split = hys::hs_decode_splits(p->topk);
     const size_t sp_bytes = (size_t)n_sparse * B * Hq * hs_split * (size_t)(D + 2) * sizeof(float);
-    const size_t need = up(ts_bytes) + (size_t)Hkv * up(part_one) + up(tk) + up(sp_bytes);
+    // every KV head's split partials in one layout, [(g*B + b)*nsplit + s][G][D] then
+    // [..][G][2], so one merge launch serves up to kMaxDecodeLayers heads
+    const size_t po_floats = (size_t)(Hkv * B * nsplit * G) * D, pml_floats = (size_t)(Hkv * B * nsplit * G) * 2;
+    const size_t need = up(ts_bytes) + up((po_floats + pml_floats) * sizeof(float)) + up(tk) + up(sp_bytes);
     if (!ws) { *ws_bytes = need; return ok(); }
     if (*ws_bytes < need) return fail(HYS_ERR_WORKSPACE, "workspace %zu < required %zu bytes", *ws_bytes, need);
     if (!aligned16(ws)) return fail(HYS_ERR_INVALID_ARG, "workspace not 16-byte aligned");
     char* w = (char*)ws;
     float* ts = (float*)w;
     w += up(ts_bytes);
-    char* parts = w;
-    w += (size_t)Hkv * up(part_one);
+    float* po_all = (float*)w;
+    float* pml_all = po_all + po_floats;
+    w += up((po_floats + pml_floats) * sizeof(float));
     void* tkws = w;
     w += up(tk);
     float* sp_part = (float*)w;
@@ -794,8 +798,8 @@ hys_status hys_hysparse_decode_step(const hys_hs_decode_params* p, hys_tensor4 q
     const float logit_scale = p->softmax_scale;
     const size_t oes = o_full.dtype == HYS_F32 ? 4 : 2;
     for (int64_t g = 0; g < Hkv; ++g) {
-      float* po = (float*)(parts + (size_t)g * up(part_one));
-      float* pml = po + (size_t)(B * nsplit * G) * D;
+      float* po = po_all + (size_t)(g * B * nsplit * G) * D;
+      float* pml = pml_all + (size_t)(g * B * nsplit * G) * 2;
       hys::DecArgs d{};
       d.q[0] = (const uint16_t*)q_full.ptr + g * G * q_full.stride[2];
       d.q_sb = q_full.stride[0]; d.q_sh = q_full.stride[2];
@@ -809,12 +813,19 @@ hys_status hys_hysparse_decode_step(const hys_hs_decode_params* p, hys_tensor4 q
       d.part_o = po; d.part_ml = pml;
       hipError_t e = hys::launch_decode(0, hys::ET_BF16, (int)D, d, st);
       if (e != hipSuccess) return hip_status(e, "decode split launch");
+    }
+    // the KV heads' merges, as the "layers" of one merge launch (up to kMaxDecodeLayers at a time)
+    for (int64_t g0 = 0; g0 < Hkv; g0 += hys::kMaxDecodeLayers) {
+      const int nl = (int)std::min<int64_t>(hys::kMaxDecodeLayers, Hkv - g0);
       hys::MergeArgs m{};
-      m.B = (int)B; m.Hq = (int)G; m.logit_scale = logit_scale; m.v_scale = 1.f; m.scale_log2 = d.scale_log2;
-      m.part_o = po; m.part_ml = pml; m.nsplit = nsplit; m.nlayer = 1;
-      m.o[0] = (char*)o_full.ptr + (size_t)(g * G * o_full.stride[2]) * oes;
+      m.B = (int)B; m.Hq = (int)G; m.logit_scale = logit_scale; m.v_scale = 1.f;
+      m.scale_log2 = logit_scale * 1.4426950408889634f;
+      m.part_o = po_all + (size_t)(g0 * B * nsplit * G) * D;
+      m.part_ml = pml_all + (size_t)(g0 * B * nsplit * G) * 2;
+      m.nsplit = nsplit; m.nlayer = nl;
+      for (int l = 0; l < nl; ++l) m.o[l] = (char*)o_full.ptr + (size_t)((g0 + l) * G * o_full.stride[2]) * oes;
       m.o_sb = o_full.stride[0]; m.o_sh = o_full.stride[2]; m.o_f32 = o_full.dtype == HYS_F32;
-      e = hys::launch_decode_merge((int)D, m, st);
+      hipError_t e = hys::launch_decode_merge((int)D, m, st);
       if (e != hipSuccess) return hip_status(e, "decode merge launch");
     }
     hipError_t e = hys::launch_hs_block_max(ts, (int)Hkv, B * Nmax, (int)B, (int)Nmax, (int)nblk, block_scores, st);
