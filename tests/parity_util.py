@@ -4,7 +4,7 @@ Comparison rules (GPU vs the fp64 oracle):
   outputs   max |gpu - oracle| <= 2e-2 for bf16 inputs, <= 1e-4 for fp32 inputs,
             and <= 1e-2 (bf16) / 1e-5 (fp32) times the oracle's largest |value|
   gradients max |gpu - oracle| <= 1e-2 times the oracle's largest |value| of
-            the compared tensor (bf16 inputs)
+            the compared tensor, plus 1e-5 (bf16 inputs)
   scores    -inf positions identical; finite entries within 1e-4
   top-k     the index sets agree except inside the oracle's tie band: with s_k
             the oracle's k-th score and band = {c : |x_c - s_k| < 1e-4},
@@ -68,13 +68,18 @@ def check_out(gpu, ref, dtype="bf16", what=""):
 # of its terms' magnitudes, bounded here relative to the tensor's largest
 # magnitude.
 REL_GRAD = 1e-2
+# Floor for references that vanish exactly (one visible key: dS = dP - rowsum(dO O)
+# = 0): the GPU's dP and rowsum are fp32 sums of D products of order one, whose
+# difference keeps a cancellation residual of order D * 2^-24.
+ABS_GRAD_FLOOR = 1e-5
 
 
 def check_grad(gpu, ref, what=""):
-    """Gradient parity: max |gpu - ref| within REL_GRAD of the reference's largest magnitude."""
+    """Gradient parity: max |gpu - ref| within REL_GRAD of the reference's largest
+    magnitude, plus ABS_GRAD_FLOOR."""
     err = max_abs(gpu, ref)
     scale = float(np.max(np.abs(np.asarray(ref, dtype=np.float64)))) if np.size(ref) else 0.0
-    assert err <= REL_GRAD * scale + 1e-7, f"{what} error {err} above {REL_GRAD} x {scale}"
+    assert err <= REL_GRAD * scale + ABS_GRAD_FLOOR, f"{what} error {err} above {REL_GRAD} x {scale} + {ABS_GRAD_FLOOR}"
     return err
 
 

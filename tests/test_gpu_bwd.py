@@ -56,6 +56,8 @@ FULL_CASES = [
     (1, 520, 8, 1, 64),
     (1, 129, 2, 1, 128),
     (1, 2300, 4, 1, 64),       # more than 64 row blocks: the dK/dV rows split over two workgroups
+    (2, 1, 4, 2, 128),         # one token
+    (1, 64, 8, 1, 64),         # exactly one key block
 ]
 
 
@@ -274,3 +276,42 @@ def test_sparse_layer_bwd_gate_bias():
     check_grad(dk[0].cpu().numpy(), r["dk"], "dk (biased gate)")
     check_grad(dgw.cpu().numpy(), r["dgate_w"], "dgate_w (biased gate)")
     check_grad(dgb.cpu().numpy(), r["dgate_b"], "dgate_b")
+
+
+@pytest.mark.parametrize("L", [64, 200])
+def test_sparse_layer_bwd_empty_selection(L):
+    """k = 0: no sparse branch anywhere, so every gradient is the window branch's
+    and the shared K/V receive nothing (accumulated into, so they stay as given)."""
+    B, Hq, Hkv, D, W = 1, 4, 2, 64, 50
+    rng = np.random.default_rng(L)
+    scale = 1.0 / math.sqrt(D)
+    q, k, v = _bf(rng, B, L, Hq, D), _bf(rng, B, L, Hkv, D), _bf(rng, B, L, Hkv, D)
+    kw, vw = _bf(rng, B, L, Hkv, D), _bf(rng, B, L, Hkv, D)
+    gw = torch.from_numpy((0.3 * rng.standard_normal((Hq, D))).astype(np.float32))
+    do = _bf(rng, B, L, Hq, D)
+    dev = "cuda"
+    idx = torch.empty(B, L, 0, dtype=torch.int32, device=dev)
+    qd, kd, vd, kwd, vwd = (t.to(dev) for t in (q, k, v, kw, vw))
+    f32 = dict(dtype=torch.float32, device=dev)
+    o_sp, lse_sp = torch.empty(B, L, Hq, D, **f32), torch.empty(B, Hq, L, **f32)
+    o_w, lse_w = torch.empty(B, L, Hq, D, **f32), torch.empty(B, Hq, L, **f32)
+    ops.hys_sparse_attn_fwd(qd, kd, vd, idx, o_sp, lse_sp, granularity=64, topk=0)
+    ops.hys_window_attn_fwd(qd, kwd, vwd, W, o_w, lse_w)
+    torch.cuda.synchronize()
+    assert torch.isneginf(lse_sp).all()
+    dq = torch.empty(B, L, Hq, D, **f32)
+    dk, dv = torch.full((B, L, Hkv, D), 3.0, **f32), torch.full((B, L, Hkv, D), 3.0, **f32)
+    dkw, dvw = torch.empty(B, L, Hkv, D, **f32), torch.empty(B, L, Hkv, D, **f32)
+    dgw = torch.empty(Hq, D, **f32)
+    ops.hys_sparse_layer_bwd(qd, kd, vd, idx, kwd, vwd, W, gw.to(dev), o_sp, lse_sp, o_w, lse_w, do.to(dev), dq, dk,
+                             dv, dkw, dvw, dgw, accumulate_kv=True, topk=0)
+    torch.cuda.synchronize()
+    none = np.full((L, 1), -1)
+    r = hb.sparse_layer_bwd(_f64(q[0]), _f64(k[0]), _f64(v[0]), _f64(kw[0]), _f64(vw[0]),
+                            gw.numpy().astype(np.float64), scale, none, 64, W, _f64(do[0]))
+    assert not r["dk"].any() and not r["dgate_w"].any()
+    assert torch.equal(dk, torch.full_like(dk, 3.0)) and torch.equal(dv, torch.full_like(dv, 3.0))
+    assert not dgw.any()
+    check_grad(dq[0].cpu().numpy(), r["dq"], "dq (window only)")
+    check_grad(dkw[0].cpu().numpy(), r["dkw"], "dk_win (window only)")
+    check_grad(dvw[0].cpu().numpy(), r["dvw"], "dv_win (window only)")
