@@ -1038,12 +1038,14 @@ hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     const int64_t ng = sp->idx_group_stride > 0 ? Hkv : 1;
     const size_t n_do = (size_t)(B * L * Hq * D) * 2, n_row = (size_t)(B * Hq * L) * 4;
     const size_t n_rb = (size_t)(ng * B * L * nwords) * 4, n_tb = (size_t)(ng * B * nrb * nwords) * 4;
+    const size_t n_tb16 = (size_t)(ng * B * ((L + 15) / 16) * nwords) * 4;
     const size_t n_gp = hys::bwd_gate_partial_floats((int)Hq, (int)D) * 4;
     int srb = 1, wsrb = 1;
     const int nsplit = hys::bwd_dkdv_plan(hys::BW_BLOCK, (int)L, 0, &srb);
     hys::bwd_dkdv_plan(hys::BW_WINDOW, (int)L, window, &wsrb);
     const size_t n_kv = hys::bwd_dkdv_ws_bytes(nsplit, (int)B, (int)L, (int)Hkv, (int)D);
-    const size_t need = 2 * up256(n_do) + 3 * up256(n_row) + up256(n_rb) + up256(n_tb) + up256(n_gp) + n_kv;
+    const size_t need = 2 * up256(n_do) + 3 * up256(n_row) + up256(n_rb) + up256(n_tb) + up256(n_tb16) +
+                        up256(n_gp) + n_kv;
     if (!ws) { *ws_bytes = need; return ok(); }
     if (*ws_bytes < need) return fail(HYS_ERR_WORKSPACE, "workspace %zu < required %zu bytes", *ws_bytes, need);
     if (!aligned16(ws)) return fail(HYS_ERR_INVALID_ARG, "workspace not 16-byte aligned");
@@ -1056,6 +1058,7 @@ hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     float* dz = (float*)w; w += up256(n_row);
     uint32_t* rowbits = (uint32_t*)w; w += up256(n_rb);
     uint32_t* tilebits = (uint32_t*)w; w += up256(n_tb);
+    uint32_t* tilebits16 = (uint32_t*)w; w += up256(n_tb16);
     float* gpart = (float*)w; w += up256(n_gp);
     void* kvws = w;
     hipStream_t st = (hipStream_t)stream;
@@ -1078,7 +1081,8 @@ hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
                                        (int)L, (int)Hq, (int)D, gpart, dgate_w, dgate_b, st)) != hipSuccess)
       return hip_status(e, "gate gradient launch");
     if ((e = hys::launch_bwd_selbits(idx, sp->idx_group_stride, sp->idx_batch_stride, sp->idx_row_stride, sp->k,
-                                     (int)ng, (int)B, (int)L, (int)nblk, (int)nwords, rowbits, tilebits, st)) !=
+                                     (int)ng, (int)B, (int)L, (int)nblk, (int)nwords, rowbits, tilebits, tilebits16,
+                                     st)) !=
         hipSuccess)
       return hip_status(e, "selection bitmap launch");
 
@@ -1087,7 +1091,7 @@ hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     hys::BwdArgs a = bwd_args(p, q, k, v, dq, dk, (float*)dv.ptr);
     a.dO = do_sp; a.do_sb = do_sb; a.do_st = do_st; a.do_sh = D;
     a.lse = lse_sparse; a.Dd = Dd_sp;
-    a.rowbits = rowbits; a.tilebits = tilebits; a.nwords = (int)nwords; a.ng = (int)ng;
+    a.rowbits = rowbits; a.tilebits = tilebits; a.tilebits16 = tilebits16; a.nwords = (int)nwords; a.ng = (int)ng;
     a.acc_q = 1; a.acc_kv = accumulate_kv;
     a.nsplit = nsplit; a.split_rb = srb;
     hys::bwd_dkdv_bind_ws(a, kvws, (int)D);

@@ -27,6 +27,7 @@ struct BwdArgs {
   // BW_BLOCK: selection bitmaps (bit c of word c/32 = block c selected)
   const uint32_t* rowbits;    // [ng][B][L][nwords]: per query row
   const uint32_t* tilebits;   // [ng][B][nrb][nwords]: OR over the 32-row blocks, nrb = ceil(L/32)
+  const uint32_t* tilebits16; // [ng][B][ceil(L/16)][nwords]: OR over the 16-row blocks
   int nwords, ng;             // ng = 1 (one set for every KV group) or Hkv
   int acc_q, acc_kv;          // 1: add into dq / dk, dv; 0: overwrite
   // dK/dV row split: the query rows a key tile sees are cut into nsplit ranges
@@ -87,6 +88,6 @@ hipError_t launch_bwd_gate_grad(const float* dz, const uint16_t* q, int64_t q_sb
 // selection bitmaps from block ids idx[g*idx_sg + b*idx_sb + i*idx_sr + j] (j < k; -1 = unused)
 hipError_t launch_bwd_selbits(const int32_t* idx, int64_t idx_sg, int64_t idx_sb, int64_t idx_sr, int k, int ng,
                               int B, int L, int nblk, int nwords, uint32_t* rowbits, uint32_t* tilebits,
-                              hipStream_t s);
+                              uint32_t* tilebits16, hipStream_t s);
 
 }  // namespace hys

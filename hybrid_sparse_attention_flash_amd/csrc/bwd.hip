@@ -14,16 +14,19 @@
 //     dO through LDS both row-major (A operands of S and dP) and transposed
 //     (B operands of dK and dV); dK and dV stay in registers and are written
 //     once.
-//   bwd_dq_kernel - query-stationary: a workgroup owns 4 x 32 query rows
-//     (heads of one KV group over the same rows, or consecutive row blocks)
-//     and walks the 64-key tiles they see, staging K (row-major and
-//     transposed) and V through LDS; dQ stays in registers.
+//   bwd_dq_kernel - query-stationary: a workgroup owns 128 (query row, head)
+//     columns of one KV group (16 rows x 8 heads when the group has 8 or more
+//     heads, else 32-row blocks of up to 4 heads) and walks the 64-key tiles
+//     they see, staging K (row-major and transposed) and V through LDS once
+//     for all of them; dQ stays in registers.
 // P and dS come back from the forward's LSE in both kernels.  P and dS leave
 // the MFMA in its C layout (lane = one column, rows spread over the 16
 // values); they feed the next MFMA as A operands directly, with the other
 // operand read in the same permuted row order, so no transpose of P or dS is
 // needed.  The block-sparse branch reads per-row selection bitmaps and skips
 // whole row blocks (dK/dV) or key tiles (dQ) that no row selected.
+
+#include <algorithm>
 
 #include "bwd.h"
 #include "common.h"
@@ -335,16 +338,17 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdArgs a, int D) {
   *(f32x4*)(a.dv + o) = sv;
 }
 
-// Next 64-key tile of a dQ workgroup (block mode: the union of its rows' selections).
+// Next 64-key tile of a dQ workgroup (block mode: the union of its rows'
+// selections, from the 16-row union bitmaps of its row blocks rb0 .. rb0+nrbw-1).
 template <int MODE>
-__device__ __forceinline__ bool next_key_tile(const BwdArgs& a, int gs, int b, int nrb, int rb0, int nrbw, int c_hi,
+__device__ __forceinline__ bool next_key_tile(const BwdArgs& a, int gs, int b, int nrb16, int rb0, int nrbw, int c_hi,
                                               uint32_t& bits, int& wi, int& c) {
   if (MODE != BW_BLOCK) { ++c; return c <= c_hi; }
   while (bits == 0u) {
     ++wi;
     if (wi * 32 > c_hi) return false;
     uint32_t u = 0u;
-    for (int r = 0; r < nrbw; ++r) u |= a.tilebits[((int64_t)(gs * a.B + b) * nrb + rb0 + r) * a.nwords + wi];
+    for (int r = 0; r < nrbw; ++r) u |= a.tilebits16[((int64_t)(gs * a.B + b) * nrb16 + rb0 + r) * a.nwords + wi];
     const int n = c_hi - wi * 32;
     if (n < 31) u &= (2u << n) - 1u;
     bits = u;
@@ -369,11 +373,19 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, hh = lane >> 5;
-  const int HW = a.G < 4 ? a.G : 4;       // heads per workgroup
-  const int RB = 4 / HW;                  // 32-row blocks per workgroup
+  // A wave's 32 MFMA columns are HPW heads x RW rows: with G >= 8, two heads
+  // of 16 rows, so a workgroup holds 16 rows of 8 heads (their K/V tiles are
+  // staged once for all 8, and the selection union spans 16 rows); otherwise
+  // one head of 32 rows per wave, the waves over the group's heads and then
+  // over consecutive row blocks.
+  const int HPW = a.G >= 8 ? 2 : 1;       // heads per wave
+  const int RW = 32 / HPW;                // rows per wave
+  const int HW = min(a.G, 4 * HPW);       // heads per workgroup
+  const int WPH = HW / HPW;               // waves across the heads
+  const int RB = 4 / WPH;                 // RW-row blocks per workgroup
+  const int WROWS = RB * RW;              // rows per workgroup
   const int nhc = (a.G + HW - 1) / HW;
-  const int nrb = (a.L + 31) / 32;
-  const int nqg = (nrb + RB - 1) / RB;
+  const int nqg = (a.L + WROWS - 1) / WROWS;
   const int per = a.B * a.Hkv * nhc;
   const int qg = nqg - 1 - (int)(blockIdx.x / per);    // the long (late) query groups first
   int rem = blockIdx.x % per;
@@ -381,20 +393,25 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   rem /= nhc;
   const int g = rem % a.Hkv, b = rem / a.Hkv;
   const int gs = a.ng > 1 ? g : 0;
-  const int hl = wave % HW, rbl = wave / HW;
-  const int rb0 = qg * RB;
-  const int nrbw = min(RB, nrb - rb0);
-  const int hq = g * a.G + hc * HW + hl;
-  const int r0 = (rb0 + rbl) * 32;
-  const bool active = rbl < RB && hc * HW + hl < a.G && r0 < a.L;
-  const int qi = r0 + ln;
-  const bool rowok = active && qi < a.L;
+  const int wh = wave % WPH, wr = wave / WPH;
+  const int wr0 = qg * WROWS;                           // first row of the workgroup
+  const int r0 = wr0 + wr * RW;                         // first row of the wave
+  const int hbase = hc * HW + wh * HPW;                 // the wave's first head within the group
+  const bool active = wr < RB && hbase < a.G && r0 < a.L;
+  // this lane's column: head hbase + ln / RW, row r0 + ln % RW
+  const int hlane = hbase + ln / RW;
+  const int hq = g * a.G + hlane;
+  const int qi = r0 + ln % RW;
+  const bool rowok = active && hlane < a.G && qi < a.L;
+  const int nrb16 = (a.L + 15) / 16;
+  const int rb0 = wr0 / 16;
+  const int nrbw = min(WROWS / 16, nrb16 - rb0);
 
   // this lane's query row as B operand of S^T = K Q^T and dP^T = V dO^T
   bw_u32x4 qf[NC], dof[NC];
   float lse2 = kNegInf, dd = 0.f;
   {
-    const int ii = rowok ? qi : 0, hh2 = active ? hq : 0;
+    const int ii = rowok ? qi : 0, hh2 = rowok ? hq : 0;
     const int64_t oq = (int64_t)b * a.q_sb + (int64_t)ii * a.q_st + (int64_t)hh2 * a.q_sh + 8 * hh;
     const int64_t od = (int64_t)b * a.do_sb + (int64_t)ii * a.do_st + (int64_t)hh2 * a.do_sh + 8 * hh;
 #pragma unroll
@@ -414,13 +431,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dq_acc[t][i] = 0.f;
 
-  const int wr0 = rb0 * 32;
-  const int wr1 = min(a.L, wr0 + RB * 32) - 1;           // last row of the workgroup
+  const int wr1 = min(a.L, wr0 + WROWS) - 1;             // last row of the workgroup
   const int c_hi = min(wr1 / 64, (a.Lk - 1) / 64);
   int c = -1, wi = -1;
   uint32_t bits = 0u;
   if (MODE == BW_WINDOW) c = max(0, wr0 - a.window + 1) / 64 - 1;
-  bool have = next_key_tile<MODE>(a, gs, b, nrb, rb0, nrbw, c_hi, bits, wi, c);
+  bool have = next_key_tile<MODE>(a, gs, b, nrb16, rb0, nrbw, c_hi, bits, wi, c);
 
   // staging item e = tid + 256p: keys 2kp, 2kp+1 of the tile (kp = e % 32), 16-byte chunk e / 32
   bw_u32x4 pk[NPASS][2], pv[NPASS][2];
@@ -459,11 +475,11 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     }
     const bool selbit = MODE == BW_BLOCK ? ((pbits >> (cur & 31)) & 1u) != 0u : true;
     __syncthreads();
-    have = next_key_tile<MODE>(a, gs, b, nrb, rb0, nrbw, c_hi, bits, wi, c);
+    have = next_key_tile<MODE>(a, gs, b, nrb16, rb0, nrbw, c_hi, bits, wi, c);
     if (have) issue(c);
 
     const int kc0 = cur * 64;
-    bool any = active && kc0 <= r0 + 31;
+    bool any = active && kc0 <= r0 + RW - 1;
     if (MODE == BW_WINDOW) any = any && kc0 + 63 > r0 - a.window;
     if (MODE == BW_BLOCK) any = any && __ballot(selbit && rowok) != 0ull;
     if (any) {
@@ -483,8 +499,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
         }
       // element (kh, i): key kc0 + 32kh + 8(i/4) + 4hh + i%4, query row qi (this lane)
       // a tile every row of the wave sees whole skips the per-element test
-      bool full = kc0 + 63 <= r0 && r0 + 31 < a.L && kc0 + 63 < a.Lk;
-      if (MODE == BW_WINDOW) full = full && kc0 > r0 + 31 - a.window;
+      bool full = kc0 + 63 <= r0 && r0 + RW - 1 < a.L && kc0 + 63 < a.Lk && __ballot(!rowok) == 0ull;
+      if (MODE == BW_WINDOW) full = full && kc0 > r0 + RW - 1 - a.window;
       if (MODE == BW_BLOCK) full = full && __ballot(!selbit) == 0ull;
       float ds[32];
       if (full) {
@@ -520,15 +536,17 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     }
   }
 
-  // dQ in C layout: lane (ln, hh) holds d = 32t + ln of rows r0 + 8(i/4) + 4hh + i%4
+  // dQ in C layout: lane (ln, hh) holds d = 32t + ln of columns m = 8(i/4) + 4hh + i%4,
+  // i.e. head hbase + m / RW, row r0 + m % RW
   if (active) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int row = r0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-        if (row >= a.L) continue;
-        const int64_t o = (int64_t)b * a.dq_sb + (int64_t)row * a.dq_st + (int64_t)hq * a.dq_sh + 32 * t + ln;
+        const int m = 8 * (i >> 2) + 4 * hh + (i & 3);
+        const int row = r0 + m % RW, hm = hbase + m / RW;
+        if (row >= a.L || hm >= a.G) continue;
+        const int64_t o = (int64_t)b * a.dq_sb + (int64_t)row * a.dq_st + (int64_t)(g * a.G + hm) * a.dq_sh + 32 * t + ln;
         const float v = dq_acc[t][i] * a.scale;
         if (a.acc_q) a.dq[o] += v;
         else a.dq[o] = v;
@@ -690,7 +708,8 @@ __global__ __launch_bounds__(256) void bwd_gate_reduce_kernel(const float* part,
 
 __global__ __launch_bounds__(256) void bwd_selbits_kernel(const int32_t* idx, int64_t idx_sg, int64_t idx_sb,
                                                           int64_t idx_sr, int k, int ng, int B, int L, int nblk,
-                                                          int nwords, uint32_t* rowbits, uint32_t* tilebits) {
+                                                          int nwords, uint32_t* rowbits, uint32_t* tilebits,
+                                                          uint32_t* tilebits16) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t n = (int64_t)ng * B * L * k;
   if (e >= n) return;
@@ -705,6 +724,7 @@ __global__ __launch_bounds__(256) void bwd_selbits_kernel(const int32_t* idx, in
   const int nrb = (L + 31) / 32;
   atomicOr(&rowbits[((int64_t)(gs * B + b) * L + i) * nwords + (c >> 5)], bit);
   atomicOr(&tilebits[((int64_t)(gs * B + b) * nrb + (i >> 5)) * nwords + (c >> 5)], bit);
+  atomicOr(&tilebits16[((int64_t)(gs * B + b) * ((L + 15) / 16) + (i >> 4)) * nwords + (c >> 5)], bit);
 }
 
 template <int MODE, int D>
@@ -720,9 +740,9 @@ hipError_t dkdv_one(const BwdArgs& a, hipStream_t s) {
 
 template <int MODE, int D>
 hipError_t dq_one(const BwdArgs& a, hipStream_t s) {
-  const int HW = a.G < 4 ? a.G : 4, RB = 4 / HW;
-  const int nhc = (a.G + HW - 1) / HW, nrb = (a.L + 31) / 32;
-  const int64_t grid = (int64_t)((nrb + RB - 1) / RB) * nhc * a.Hkv * a.B;
+  const int HPW = a.G >= 8 ? 2 : 1, HW = std::min(a.G, 4 * HPW), WROWS = (4 / (HW / HPW)) * (32 / HPW);
+  const int nhc = (a.G + HW - 1) / HW;
+  const int64_t grid = (int64_t)((a.L + WROWS - 1) / WROWS) * nhc * a.Hkv * a.B;
   hipLaunchKernelGGL((bwd_dq_kernel<MODE, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -818,16 +838,18 @@ hipError_t launch_bwd_gate_grad(const float* dz, const uint16_t* q, int64_t q_sb
 
 hipError_t launch_bwd_selbits(const int32_t* idx, int64_t idx_sg, int64_t idx_sb, int64_t idx_sr, int k, int ng,
                               int B, int L, int nblk, int nwords, uint32_t* rowbits, uint32_t* tilebits,
-                              hipStream_t s) {
-  const int nrb = (L + 31) / 32;
+                              uint32_t* tilebits16, hipStream_t s) {
+  const int nrb = (L + 31) / 32, nrb16 = (L + 15) / 16;
   hipError_t e = launch_fill_i32((int32_t*)rowbits, 0, (int64_t)ng * B * L * nwords, s);
   if (e != hipSuccess) return e;
   e = launch_fill_i32((int32_t*)tilebits, 0, (int64_t)ng * B * nrb * nwords, s);
   if (e != hipSuccess) return e;
+  e = launch_fill_i32((int32_t*)tilebits16, 0, (int64_t)ng * B * nrb16 * nwords, s);
+  if (e != hipSuccess) return e;
   const int64_t n = (int64_t)ng * B * L * k;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(bwd_selbits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, idx_sg, idx_sb,
-                     idx_sr, k, ng, B, L, nblk, nwords, rowbits, tilebits);
+                     idx_sr, k, ng, B, L, nblk, nwords, rowbits, tilebits, tilebits16);
   return hipGetLastError();
 }
 

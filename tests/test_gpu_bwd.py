@@ -58,6 +58,8 @@ FULL_CASES = [
     (1, 2300, 4, 1, 64),       # more than 64 row blocks: the dK/dV rows split over two workgroups
     (2, 1, 4, 2, 128),         # one token
     (1, 64, 8, 1, 64),         # exactly one key block
+    (1, 333, 12, 1, 128),      # G = 12: dQ workgroups of 16 rows x 8 heads, the second head chunk half empty
+    (2, 150, 16, 1, 64),       # G = 16: two full head chunks
 ]
 
 
@@ -110,6 +112,8 @@ SPARSE_CASES = [
     (1, 300, 16, 4, 128, 2, 128, True, False),
     (1, 260, 8, 8, 64, 4, 64, True, True),
     (1, 2300, 4, 2, 64, 3, 128, False, False),     # split dK/dV rows
+    (1, 270, 16, 2, 128, 3, 128, True, False),     # G = 8: 16-row dQ workgroups, per-group unions
+    (1, 150, 12, 1, 64, 2, 64, False, True),       # G = 12: a partly empty head chunk
 ]
 
 
