@@ -60,6 +60,7 @@ FULL_CASES = [
     (1, 64, 8, 1, 64),         # exactly one key block
     (1, 333, 12, 1, 128),      # G = 12: dQ workgroups of 16 rows x 8 heads, the second head chunk half empty
     (2, 150, 16, 1, 64),       # G = 16: two full head chunks
+    (2, 77, 8, 2, 128),        # G = 8, two sequences, 16-row blocks with a ragged tail
 ]
 
 
@@ -114,6 +115,7 @@ SPARSE_CASES = [
     (1, 2300, 4, 2, 64, 3, 128, False, False),     # split dK/dV rows
     (1, 270, 16, 2, 128, 3, 128, True, False),     # G = 8: 16-row dQ workgroups, per-group unions
     (1, 150, 12, 1, 64, 2, 64, False, True),       # G = 12: a partly empty head chunk
+    (2, 100, 8, 1, 64, 2, 32, False, True),        # G = 8, two sequences, L not a multiple of 16
 ]
 
 
