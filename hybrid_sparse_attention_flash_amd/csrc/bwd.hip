@@ -152,62 +152,98 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   bool have = rb_first < rb_hi && next_row_block<MODE>(a, lane, gs, b, nrb, k0, rb_hi, mask, base, rb);
   const bool did = have;
 
-  // staging item tid (when tid < NIT): rows 2rp, 2rp+1 of the block, 16-byte chunk ch
+  // staging item tid (when tid < NIT): rows 2rp, 2rp+1 of the block, 16-byte chunk ch.
+  // Two register sets alternate (the loop is unrolled by two), so the loads of
+  // a step are issued two steps before it is staged into LDS.
   const int rp = tid & 15, sch = tid >> 4;
   const bool stager = tid < NIT;
-  bw_u32x4 pq[2], pdo[2];
-  float plse = kNegInf, pdd = 0.f;
-  uint32_t pbits = 0u;
-  auto issue = [&](int rbi, int hq) {
+  bw_u32x4 pq[2][2], pdo[2][2];
+  float plse[2] = {kNegInf, kNegInf}, pdd[2] = {0.f, 0.f};
+  uint32_t pbits[2] = {0u, 0u};
+  uint32_t pok[2] = {0u, 0u};             // bit u: staging row u in range; 4: lse row; 8: bitmap row
+  int srb[2] = {0, 0};
+  bool shave[2] = {false, false};
+  auto issue = [&](auto set_tag, int rbi, int hq) __attribute__((always_inline)) {
+    constexpr int S = decltype(set_tag)::value;
+    // every load is issued unconditionally from a clamped, in-bounds address
+    // and the out-of-range values are replaced when the set is staged: with
+    // no load under a branch and no use before then, the wait before a set is
+    // staged covers that set's loads only
     const int r0 = rbi * 32;
+    const int ch = stager ? sch : 0;
+    uint32_t okm = 0u;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i = r0 + 2 * rp + u;
       const bool ok = stager && i < a.L;
       const int ii = ok ? i : 0;
-      pq[u] = ok ? *(const bw_u32x4*)(a.q + (int64_t)b * a.q_sb + (int64_t)ii * a.q_st + (int64_t)hq * a.q_sh +
-                                      8 * sch)
-                 : zero4();
-      pdo[u] = ok ? *(const bw_u32x4*)(a.dO + (int64_t)b * a.do_sb + (int64_t)ii * a.do_st + (int64_t)hq * a.do_sh +
-                                       8 * sch)
-                  : zero4();
+      okm |= (ok ? 1u : 0u) << u;
+      pq[S][u] = *(const bw_u32x4*)(a.q + (int64_t)b * a.q_sb + (int64_t)ii * a.q_st + (int64_t)hq * a.q_sh + 8 * ch);
+      pdo[S][u] = *(const bw_u32x4*)(a.dO + (int64_t)b * a.do_sb + (int64_t)ii * a.do_st + (int64_t)hq * a.do_sh +
+                                     8 * ch);
     }
-    if (tid < 32) {
-      const int i = r0 + tid;
+    {
+      const int i = r0 + (tid & 31);
       const bool ok = i < a.L;
+      okm |= (ok ? 4u : 0u);
       const int64_t o = ((int64_t)b * a.Hq + hq) * a.L + (ok ? i : 0);
-      plse = ok ? a.lse[o] : kNegInf;
-      pdd = ok ? a.Dd[o] : 0.f;
+      plse[S] = a.lse[o];
+      pdd[S] = a.Dd[o];
     }
     if (MODE == BW_BLOCK) {
       const int i = r0 + ln;
-      pbits = i < a.L ? a.rowbits[((int64_t)(gs * a.B + b) * a.L + i) * a.nwords + (cw >> 5)] : 0u;
+      okm |= (i < a.L ? 8u : 0u);
+      pbits[S] = a.rowbits[((int64_t)(gs * a.B + b) * a.L + (i < a.L ? i : 0)) * a.nwords + (cw >> 5)];
     }
+    pok[S] = okm;
   };
-  if (have) issue(rb, a.G > 0 ? g * a.G : 0);
-
-  while (have) {
-    const int cur_r0 = rb * 32;
-    __syncthreads();                      // the previous step's LDS reads are done
-    if (stager) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        *(bw_u32x4*)&s_q[(2 * rp + u) * RS + 8 * sch] = pq[u];
-        *(bw_u32x4*)&s_do[(2 * rp + u) * RS + 8 * sch] = pdo[u];
-      }
-      store_t8x2<TS>(s_qt, rp, sch, pq[0], pq[1]);
-      store_t8x2<TS>(s_dot, rp, sch, pdo[0], pdo[1]);
-    }
-    if (tid < 32) { s_lse[tid] = plse * kLog2e; s_dd[tid] = pdd; }
-    uint32_t selmask = 0xffffffffu;
-    if (MODE == BW_BLOCK) selmask = (uint32_t)__ballot(hh == 0 && ((pbits >> (cw & 31)) & 1u));
-    __syncthreads();
-    // advance and prefetch the next step while this one computes
+  // the step after the current (row block, head): heads fastest
+  auto advance = [&]() __attribute__((always_inline)) {
+    if (!have) return;
     if (++h >= a.G) {
       h = 0;
       have = next_row_block<MODE>(a, lane, gs, b, nrb, k0, rb_hi, mask, base, rb);
     }
-    if (have) issue(rb, g * a.G + h);
+  };
+  // take the next step into set S and issue its loads (after finding the
+  // step that follows, whose rare bitmap read would otherwise wait for them)
+  auto fill = [&](auto set_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(set_tag)::value;
+    const int hs = h;
+    shave[S] = have;
+    srb[S] = rb;
+    advance();
+    if (shave[S]) issue(set_tag, srb[S], g * a.G + hs);
+  };
+
+  auto step = [&](auto set_tag) __attribute__((always_inline)) {
+    constexpr int S = decltype(set_tag)::value;
+    const int cur_r0 = srb[S] * 32;
+    __syncthreads();                      // the previous step's LDS reads are done
+    const uint32_t okm = pok[S];
+    if (stager) {
+      bw_u32x4 xq[2], xd[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bool ok = (okm >> u) & 1u;
+        xq[u] = ok ? pq[S][u] : zero4();
+        xd[u] = ok ? pdo[S][u] : zero4();
+        *(bw_u32x4*)&s_q[(2 * rp + u) * RS + 8 * sch] = xq[u];
+        *(bw_u32x4*)&s_do[(2 * rp + u) * RS + 8 * sch] = xd[u];
+      }
+      store_t8x2<TS>(s_qt, rp, sch, xq[0], xq[1]);
+      store_t8x2<TS>(s_dot, rp, sch, xd[0], xd[1]);
+    }
+    if (tid < 32) {
+      s_lse[tid] = (okm & 4u) ? plse[S] * kLog2e : kNegInf;
+      s_dd[tid] = (okm & 4u) ? pdd[S] : 0.f;
+    }
+    uint32_t selmask = 0xffffffffu;
+    if (MODE == BW_BLOCK)
+      selmask = (uint32_t)__ballot(hh == 0 && (okm & 8u) && ((pbits[S] >> (cw & 31)) & 1u));
+    __syncthreads();
+    // this set now takes the step two ahead, whose loads overlap two steps of compute
+    fill(set_tag);
 
     bool any = kw0 <= cur_r0 + 31 && kw0 < a.Lk;
     if (MODE == BW_WINDOW) any = any && kw0 + 31 > cur_r0 - a.window;
@@ -278,6 +314,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         dk_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(da1), bwf(bq1), dk_acc[t], 0, 0, 0);
       }
     }
+  };
+
+  fill(std::integral_constant<int, 0>{});
+  fill(std::integral_constant<int, 1>{});
+  while (shave[0]) {
+    step(std::integral_constant<int, 0>{});
+    if (!shave[1]) break;
+    step(std::integral_constant<int, 1>{});
   }
 
   // dK, dV in C layout: lane (ln, hh) holds d = 32t + ln of keys kw0 + 8(i/4) + 4hh + i%4
