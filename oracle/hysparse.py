@@ -14,15 +14,17 @@ full-size workloads.  No blocking, fusion or reordering is used beyond
 computing rows independently: each row's logits are formed explicitly and
 passed through an explicit softmax.
 
-Sources (the pages; citations name page and passage):
-  [QbitAI]     QbitAI article on HySparse, section "HySparse: leave selection
-               and caching to Full Attention"
-  [TechWalker] TechWalker HySparse write-up, paragraphs on the modified
-               FlashAttention kernel and on the apprentice (sparse) layers
-  [airebao]    airebao HySparse2 news: core mechanism, inner KV Reuse,
-               token-level selection, forced recent window, MQA detail,
-               key-data table
-  [deming]     demingchina HySparse2 commentary, sections 03 and 05
+Sources (the pages; each citation below names the page and the passage):
+  [QbitAI]     = QbitAI HySparse article, method section (the full-attention
+               layer does the selection and keeps the cache)
+  [TechWalker] = TechWalker HySparse write-up, paragraphs on the modified
+               FlashAttention kernel and on the sparse layers
+  [airebao]    = airebao HySparse2 news, paragraphs "core mechanism", "inner
+               KV Reuse", "token-level selection", "forced recent window",
+               "MQA detail" and the key-data table
+  [deming]     = demingchina HySparse2 commentary, sections 03 and 05
+A bracketed tag in a docstring abbreviates that page; the passage is named
+next to it.
 """
 from __future__ import annotations
 
@@ -267,10 +269,11 @@ def sparse_block_attention_grouped(q, k, v, scale, sel_g, block, rows=None):
 def sparse_token_attention(q, k, v, scale, sel_tiles, tile, window, rows=None):
     """HySparse2 sparse layer: selected tokens united with a forced recent window.
 
-    [airebao] token-level selection and forced recent window: the sparse
-    layer attends to single selected tokens and the most recent 128 tokens
-    are forced into the selected set, so local and global tokens share one
-    KV cache and there is no separate window branch ([deming] section 03).
+    airebao HySparse2 news, token-level selection and forced recent window
+    paragraphs: a sparse layer attends to individually chosen tokens, and the
+    128 newest tokens are always added to that choice; the window therefore
+    reads the same cache as the chosen tokens and no second (window) branch
+    exists (demingchina HySparse2 commentary, section 03).
     J(i) = {j in sel_{i // tile} : j <= i}  U  [max(0, i-window+1), i]
     (a set union: a token in both counts once).  `sel_tiles` [ntile, kt].
     """

@@ -129,3 +129,17 @@ def check_topk_band(gpu_idx, ref_idx, ref_scores, k):
             bad.append(r)
     assert not bad, f"top-k rows outside the tie band: {bad[:10]}"
     return same, inband
+
+
+def selection_to_compare(gpu_row, ref_row, ref_scores, k):
+    """The index set a sparse-layer comparison recomputes the oracle with.
+
+    The GPU's selection has already passed the band rule (check_topk_band).
+    Where it equals the oracle's, the oracle's own end-to-end result applies;
+    where it differs inside the tie band, both choices are correct and the
+    oracle is re-evaluated on the GPU's choice, so the sparse layers are
+    compared on every row either way.  Returns (selection, same)."""
+    gpu_row = np.asarray(gpu_row)
+    same = np.array_equal(gpu_row, np.asarray(ref_row))
+    assert same or topk_band_ok(gpu_row, ref_row, ref_scores, k)
+    return (np.asarray(ref_row) if same else gpu_row.astype(np.int64)), same

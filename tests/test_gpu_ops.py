@@ -12,7 +12,8 @@ import torch
 import oracle
 import synth
 from hybrid_sparse_attention_flash_amd import ops
-from tests.parity_util import (TOL_OUT, check_out, check_scores, check_topk_band, dev, f64, max_abs)
+from tests.parity_util import (TOL_OUT, check_out, check_scores, check_topk_band, dev, f64, max_abs,
+                               selection_to_compare)
 
 pytestmark = pytest.mark.gpu
 
@@ -267,6 +268,7 @@ def test_decode_step(B, N, lens, Hq, D, topk, W, nsp, kv):
     ops.hys_decode_step(dev(qf), dev(kc), dev(vc), list(lens), o_full, scores, idx, [dev(x) for x in qs], o_sp,
                         topk, W, k_scale=ks, v_scale=vs)
     torch.cuda.synchronize()
+    compared = 0
     for b in range(B):
         n = lens[b]
         kf = oracle.as_f64(kc[b, :, 0:1], kv, ks)
@@ -277,10 +279,15 @@ def test_decode_step(B, N, lens, Hq, D, topk, W, nsp, kv):
         check_scores(s[:n], res["scores"])
         assert np.all(np.isneginf(s[n:]))
         gi = idx[b].cpu().numpy()
-        same, inband = check_topk_band(gi[None], res["sel"][None], res["scores"][None], topk)
-        if same:
-            for l in range(nsp):
-                check_out(o_sp[l][b, 0].cpu().numpy(), res["o_layers"][l], "bf16", "o_sparse")
+        check_topk_band(gi[None], res["sel"][None], res["scores"][None], topk)
+        # every sparse layer is compared: on the oracle's selection, or on the
+        # GPU's where it differs inside the tie band
+        sel, same = selection_to_compare(gi, res["sel"], res["scores"], topk)
+        for l in range(nsp):
+            want = res["o_layers"][l] if same else oracle.decode_sparse(f64(qs[l][b, 0]), kf, vf, w.scale, n, sel, W)[0]
+            check_out(o_sp[l][b, 0].cpu().numpy(), want, "bf16", f"o_sparse layer {l}")
+            compared += 1
+    assert compared == B * nsp
 
 
 @pytest.mark.parametrize("half", [0, 1])

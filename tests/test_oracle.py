@@ -390,3 +390,55 @@ def test_fp8_exact_in_bf16():
     fin = tab[np.isfinite(tab)]
     back = torch.from_numpy(fin).to(torch.bfloat16).to(torch.float64).numpy()
     np.testing.assert_array_equal(back, fin)
+
+
+# ----------------------------------------------------------------------------
+# O9 for HySparse2: the whole block evaluated for chosen query tiles
+# ----------------------------------------------------------------------------
+
+def test_hysparse2_block_brute_force_tiles_out_of_order():
+    """Every field of hysparse2_block against pure-Python loops, for tiles
+    requested out of order and a ragged last tile (L = 43, tile 8: tile 5 has
+    three rows).  The brute force forms the tile-token scores, takes each
+    tile's top-k with the lowest index winning ties, and attends each sparse
+    layer over {selected tokens of the row's tile} U {the last W keys}, so a
+    slip in the tile-to-row bookkeeping (rows out of the tiles' order, one
+    tile's selection given to another, a window off by one) fails here."""
+    q0, k, v, sc = _case(L=43, Hq=2, Hkv=1, D=4, seed=61)
+    q1 = _rand((43, 2, 4), 62)
+    q2 = _rand((43, 2, 4), 63)
+    tile, topk, W = 8, 5, 4
+    tiles = [4, 0, 5, 2]
+    res = oracle.hysparse2_block([q0, q1, q2], k, v, sc, tile, topk, W, tiles=tiles)
+    rows_ref = [i for t in tiles for i in range(t * tile, min(43, (t + 1) * tile))]
+    assert res["rows"].tolist() == rows_ref
+    T = bf.tile_token_scores(_tolist(q0), _tolist(k), sc, tile)
+    for n, t in enumerate(tiles):
+        np.testing.assert_allclose(res["scores"][n], np.array(T[t]), atol=1e-12)
+        sel_t, cnt = bf.topk(T[t], topk)
+        assert res["sel"][n].tolist() == sel_t and res["count"][n] == cnt
+    Of, lse = bf.attention(_tolist(q0), _tolist(k), _tolist(v), sc, lambda i, j: j <= i)
+    np.testing.assert_allclose(res["o_full"], np.array([Of[i] for i in rows_ref]), atol=1e-12)
+    np.testing.assert_allclose(res["lse"], np.array([[lse[h][i] for i in rows_ref] for h in range(2)]), atol=1e-12)
+    sel_of_tile = {t: set(c for c in bf.topk(T[t], topk)[0] if c >= 0) for t in tiles}
+    for l, ql in enumerate((q1, q2)):
+        Ob, _ = bf.attention(_tolist(ql), _tolist(k), _tolist(v), sc,
+                             lambda i, j: j <= i and (j in sel_of_tile.get(i // tile, set()) or j >= i - W + 1))
+        np.testing.assert_allclose(res["o_layers"][l], np.array([Ob[i] for i in rows_ref]), atol=1e-12)
+
+
+def test_hysparse2_block_reductions():
+    """k >= L selects every causal token, so each sparse layer is full causal
+    attention of its own query; k = 0 selects nothing, so it is pure window
+    attention over the shared K/V (both spec invariants, at block level)."""
+    q0, k, v, sc = _case(L=70, Hq=4, Hkv=1, D=8, seed=64)
+    q1 = _rand((70, 4, 8), 65)
+    tile, W = 16, 8
+    tiles = [3, 1, 4]
+    full = oracle.hysparse2_block([q0, q1], k, v, sc, tile, 70, W, tiles=tiles)
+    Of, _ = oracle.full_attention(q1, k, v, sc, rows=full["rows"])
+    np.testing.assert_allclose(full["o_layers"][0], Of, atol=1e-13)
+    none = oracle.hysparse2_block([q0, q1], k, v, sc, tile, 0, W, tiles=tiles)
+    Ow, _ = oracle.window_attention(q1, k, v, sc, W, rows=none["rows"])
+    np.testing.assert_allclose(none["o_layers"][0], Ow, atol=1e-13)
+    assert (none["count"] == 0).all()
