@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 
 #include "../../include/hys.h"
@@ -153,6 +154,40 @@ int env_int(const char* name, int dflt) {
   const char* e = std::getenv(name);
   if (!e || !*e) return dflt;
   return std::atoi(e);
+}
+
+}  // namespace
+
+// Scratch of hys_decode_step_noalloc: a file-scope device array, one copy per
+// GPU, alive until the process ends.  Host code never uses its name as an
+// address (on the host the name is only a stand-in); the device address of
+// each GPU's copy comes from hipGetSymbolAddress, taken once per device with
+// that device current, and is the only pointer passed to kernels.
+static __device__ __align__(256) unsigned char scratch[HYS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (set up on the first
+// call on that device).
+hys_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HYS_ERR_UNSUPPORTED, "device ordinal %d above %d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(HYS_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return HYS_OK;
 }
 
 }  // namespace
@@ -495,10 +530,13 @@ hys_status hys_sparse_layer_fwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
 }
 
 // ---------------------------------------------------------------------------
-hys_status hys_decode_step(const hys_decode_params* p, hys_tensor4 q_full, hys_tensor4 k_cache, hys_tensor4 v_cache,
-                           const int64_t* cache_len, hys_tensor4 o_full, float* token_scores, int32_t* idx,
-                           int32_t n_sparse, const hys_tensor4* q_sparse, const hys_tensor4* o_sparse, void* ws,
-                           size_t* ws_bytes, void* stream) {
+// The HySparse2 decode step; hys_decode_step passes the caller's workspace,
+// hys_decode_step_noalloc the library's fixed scratch array.  With ws == NULL
+// it validates and returns the workspace size without any HIP call.
+static hys_status decode_step_impl(const hys_decode_params* p, hys_tensor4 q_full, hys_tensor4 k_cache,
+                                   hys_tensor4 v_cache, const int64_t* cache_len, hys_tensor4 o_full,
+                                   float* token_scores, int32_t* idx, int32_t n_sparse, const hys_tensor4* q_sparse,
+                                   const hys_tensor4* o_sparse, void* ws, size_t* ws_bytes, void* stream) {
   try {
     if (!p) return fail(HYS_ERR_INVALID_ARG, "null params");
     if (!ws_bytes) return fail(HYS_ERR_INVALID_ARG, "ws_bytes must not be null");
@@ -614,6 +652,37 @@ hys_status hys_decode_step(const hys_decode_params* p, hys_tensor4 q_full, hys_t
       if (e != hipSuccess) return hip_status(e, "decode sparse merge launch");
     }
     return ok();
+  } catch (...) {
+    return fail(HYS_ERR_INTERNAL, "internal error");
+  }
+}
+
+hys_status hys_decode_step(const hys_decode_params* p, hys_tensor4 q_full, hys_tensor4 k_cache, hys_tensor4 v_cache,
+                           const int64_t* cache_len, hys_tensor4 o_full, float* token_scores, int32_t* idx,
+                           int32_t n_sparse, const hys_tensor4* q_sparse, const hys_tensor4* o_sparse, void* ws,
+                           size_t* ws_bytes, void* stream) {
+  return decode_step_impl(p, q_full, k_cache, v_cache, cache_len, o_full, token_scores, idx, n_sparse, q_sparse,
+                          o_sparse, ws, ws_bytes, stream);
+}
+
+hys_status hys_decode_step_noalloc(const hys_decode_params* p, hys_tensor4 q_full, hys_tensor4 k_cache,
+                                   hys_tensor4 v_cache, const int64_t* cache_len, hys_tensor4 o_full,
+                                   float* token_scores, int32_t* idx, int32_t n_sparse, const hys_tensor4* q_sparse,
+                                   const hys_tensor4* o_sparse, void* stream) {
+  try {
+    // validation and the workspace size first: no HIP call yet
+    size_t need = 0;
+    hys_status s = decode_step_impl(p, q_full, k_cache, v_cache, cache_len, o_full, token_scores, idx, n_sparse,
+                                    q_sparse, o_sparse, nullptr, &need, nullptr);
+    if (s != HYS_OK) return s;
+    if (need > HYS_NOALLOC_SCRATCH_BYTES)
+      return fail(HYS_ERR_WORKSPACE, "this decode step needs %zu bytes of scratch; the fixed scratch holds %zu",
+                  need, (size_t)HYS_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if ((s = noalloc_scratch(&ws)) != HYS_OK) return s;
+    size_t have = HYS_NOALLOC_SCRATCH_BYTES;
+    return decode_step_impl(p, q_full, k_cache, v_cache, cache_len, o_full, token_scores, idx, n_sparse, q_sparse,
+                            o_sparse, ws, &have, stream);
   } catch (...) {
     return fail(HYS_ERR_INTERNAL, "internal error");
   }

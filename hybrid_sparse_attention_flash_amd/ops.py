@@ -150,6 +150,22 @@ def hys_decode_step(q_full, k_cache, v_cache, cache_len: Sequence[int], o_full, 
     return workspace
 
 
+def hys_decode_step_noalloc(q_full, k_cache, v_cache, cache_len: Sequence[int], o_full, token_scores, idx,
+                            q_sparse: Sequence[torch.Tensor], o_sparse: Sequence[torch.Tensor], topk: int, window: int,
+                            softmax_scale: float = None, k_scale: float = 1.0, v_scale: float = 1.0):
+    """hys_decode_step on the library's fixed scratch array: no workspace is
+    allocated by the call or by this wrapper."""
+    lib = _lib.load()
+    p = HysDecodeParams(softmax_scale or 1.0 / math.sqrt(q_full.shape[-1]), k_scale, v_scale, topk, window)
+    lens = (ctypes.c_int64 * len(cache_len))(*[int(x) for x in cache_len])
+    n = len(q_sparse)
+    qs = (HysTensor4 * max(n, 1))(*[tensor4(t) for t in q_sparse])
+    os_ = (HysTensor4 * max(n, 1))(*[tensor4(t) for t in o_sparse])
+    check(lib.hys_decode_step_noalloc(ctypes.byref(p), tensor4(q_full), tensor4(k_cache), tensor4(v_cache), lens,
+                                      tensor4(o_full), _ptr(token_scores), _ptr(idx), n, qs, os_,
+                                      _stream(q_full.device)))
+
+
 def hys_hysparse_decode_step(q_full, k_cache, v_cache, cache_len: Sequence[int], o_full, block_scores, idx,
                              q_sparse: Sequence[torch.Tensor], k_win_new: Sequence[torch.Tensor],
                              v_win_new: Sequence[torch.Tensor], k_ring: Sequence[torch.Tensor],

@@ -17,6 +17,8 @@
  *   hys_swa_gate_fwd    - HySparse's sliding-window branch fused with the
  *                         sigmoid gate that merges it with the sparse branch
  *   hys_decode_step     - one HySparse2 decode step against a long fp8 cache
+ *   hys_decode_step_noalloc - the same step on a fixed library-owned scratch
+ *                          array, for callers that cannot allocate
  *
  * and one fused form of two of them:
  *
@@ -46,7 +48,9 @@
  * --------------------------------
  * Memory:   every tensor pointer is device memory owned by the caller (for
  *           example allocated by PyTorch).  The library allocates nothing,
- *           keeps no pointer after returning and holds no global mutable state.
+ *           keeps no pointer after returning and holds no global mutable state
+ *           (the one exception: hys_decode_step_noalloc's fixed per-GPU
+ *           scratch array and its cached device addresses).
  *           Inputs are only read; outputs are fully overwritten (except
  *           where a call documents an accumulate flag).
  * Streams:  work is enqueued on `stream` (a hipStream_t; NULL = the default
@@ -73,7 +77,8 @@
  *           never aborts and never throws.  Faults inside kernels surface at
  *           the caller's next stream synchronisation.
  * Threads:  the library is stateless; concurrent calls on different streams
- *           are safe.
+ *           are safe (except overlapping hys_decode_step_noalloc calls on one
+ *           GPU, which share its scratch array).
  */
 #ifndef HYS_H_
 #define HYS_H_
@@ -85,7 +90,7 @@
 extern "C" {
 #endif
 
-#define HYS_ABI_VERSION 4
+#define HYS_ABI_VERSION 5
 
 #if defined(__GNUC__)
 #define HYS_API __attribute__((visibility("default")))
@@ -314,6 +319,32 @@ HYS_API hys_status hys_decode_step(const hys_decode_params* p, hys_tensor4 q_ful
                            hys_tensor4 v_cache, const int64_t* cache_len, hys_tensor4 o_full, float* token_scores,
                            int32_t* idx, int32_t n_sparse, const hys_tensor4* q_sparse,
                            const hys_tensor4* o_sparse, void* ws, size_t* ws_bytes, void* stream);
+
+/* Size of the fixed device scratch array behind hys_decode_step_noalloc. */
+#define HYS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * hys_decode_step_noalloc - hys_decode_step for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same arguments, outputs and kernels as
+ * hys_decode_step, without (ws, ws_bytes): the workspace is a fixed array
+ * of HYS_NOALLOC_SCRATCH_BYTES (64 MiB) of device memory inside the library,
+ * one copy per GPU, held until the process ends.  The call allocates and
+ * frees nothing (no hipMalloc, hipFree or allocating library routine).
+ * Limit: a step whose workspace (the size hys_decode_step reports for the
+ * same arguments) exceeds the array returns HYS_ERR_WORKSPACE before any GPU
+ * work; the 1,048,576-token, 4-sequence, 11-layer step needs about 30 MiB.
+ * Set-up: the first call on a device looks up that device's copy of the
+ * array (hipGetSymbolAddress, with the device current) and keeps its address.
+ * Sharing: every call on one GPU uses that GPU's one array, and nothing in
+ * it has to start cleared (each step writes every scratch value before
+ * reading it).  Calls that overlap in time on one GPU (other threads, other
+ * streams) race on the array: serialise them, e.g. on one stream.
+ */
+HYS_API hys_status hys_decode_step_noalloc(const hys_decode_params* p, hys_tensor4 q_full, hys_tensor4 k_cache,
+                                           hys_tensor4 v_cache, const int64_t* cache_len, hys_tensor4 o_full,
+                                           float* token_scores, int32_t* idx, int32_t n_sparse,
+                                           const hys_tensor4* q_sparse, const hys_tensor4* o_sparse, void* stream);
 
 typedef struct {
   float softmax_scale;

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol():
     assert declared == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(lib(), name)
-    assert lib().hys_abi_version() == 4
+    assert lib().hys_abi_version() == 5
     assert lib().hys_status_string(3) == b"HYS_ERR_WORKSPACE"
 
 
@@ -306,3 +306,37 @@ def test_backward_validation():
         return L_.hys_window_attn_fwd(ctypes.byref(p), q, kv, kv, window, o, None, None)
     assert window_fwd(window=0) == INVALID
     assert window_fwd(o=t4([1, 128, 8, 64], dtype=0)) == INVALID
+
+
+def test_decode_noalloc_validation_and_scratch_limit():
+    """The entry point without workspace validates like hys_decode_step and
+    refuses a step whose workspace exceeds its fixed scratch, both before any
+    HIP call."""
+    L = lib()
+    p = HysDecodeParams(0.088, 0.01, 0.01, 1024, 128)
+    o = t4([4, 1, 64, 128], dtype=0)
+
+    def call(B, N, lens, n_sparse=0, pp=p):
+        qf = t4([B, 1, 64, 128])
+        kc = t4([B, N, 1, 128], dtype=2)
+        ob = t4([B, 1, 64, 128], dtype=0)
+        arr = (HysTensor4 * max(n_sparse, 1))(*[t4([B, 1, 64, 128]) for _ in range(n_sparse)])
+        arr_o = (HysTensor4 * max(n_sparse, 1))(*[t4([B, 1, 64, 128], dtype=0) for _ in range(n_sparse)])
+        ln = (ctypes.c_int64 * B)(*lens)
+        return L.hys_decode_step_noalloc(ctypes.byref(pp), qf, kc, kc, ln, ob, ctypes.c_void_p(FAKE),
+                                         ctypes.c_void_p(FAKE), n_sparse, arr if n_sparse else None,
+                                         arr_o if n_sparse else None, None)
+    assert call(4, 1 << 20, [0, 1, 2, 3]) == INVALID                           # cache_len 0
+    assert call(4, 1 << 20, [1 << 20] * 4, pp=HysDecodeParams(0.088, 0.01, 0.01, 4096, 128)) == UNSUPPORTED
+    # 64 sequences x 16 sparse layers: the split partials alone exceed 64 MiB
+    big = 16
+    nb = ctypes.c_size_t(0)
+    qf, kc = t4([64, 1, 64, 128]), t4([64, 4096, 1, 128], dtype=2)
+    arr = (HysTensor4 * big)(*[t4([64, 1, 64, 128]) for _ in range(big)])
+    arr_o = (HysTensor4 * big)(*[t4([64, 1, 64, 128], dtype=0) for _ in range(big)])
+    ln = (ctypes.c_int64 * 64)(*([4096] * 64))
+    assert L.hys_decode_step(ctypes.byref(p), qf, kc, kc, ln, t4([64, 1, 64, 128], dtype=0), ctypes.c_void_p(FAKE),
+                             ctypes.c_void_p(FAKE), big, arr, arr_o, None, ctypes.byref(nb), None) == 0
+    assert nb.value > 64 << 20
+    assert call(64, 4096, [4096] * 64, n_sparse=big) == WORKSPACE
+    assert b"scratch" in L.hys_last_error()
