@@ -50,6 +50,11 @@ TRAFFIC = {"sources_sha1": "4c9e9478bc1341f155f1c294d752786d104ce3e7", "bytes_pe
 #   python3 bench.py --only-bridge --calibrate-copy --steps 1 --warmup 0
 BRIDGE_TRAFFIC_SOURCES = ("bridge.hip", "common.h", "kernels.h")
 BRIDGE_TRAFFIC = {"sources_sha1": "0f3200bd622013cb90b006dafe13a157af9fc552", "bytes_per_launch": 575.7e6}
+# The same two passes for the decode step (all kernels of one hys_decode_step
+# call, per step), over
+#   python3 bench.py --only-decode --calibrate-copy --steps 2 --warmup 1
+DECODE_TRAFFIC_SOURCES = ("decode.hip", "topk.hip", "common.h", "kernels.h", "abi.hip")
+DECODE_TRAFFIC = None
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
@@ -101,6 +106,78 @@ class Timer:
         return {k: len(v) for k, v in self.events.items()}
 
 
+def stats_ms(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return {"mean_ms": round(sum(xs) / n, 4), "median_ms": round(med, 4), "min_ms": round(xs[0], 4), "n": n}
+
+
+class CacheFlush:
+    """Writes a 512 MiB buffer, more than the L2s and the 256 MB MALL together,
+    so the next step starts with its inputs in HBM only (cold-cache timing)."""
+
+    def __init__(self, dev, mib=512):
+        self.buf = torch.empty(mib * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        self.buf.fill_(1.0)
+
+
+def per_step_times(step, steps, flush=None):
+    """HIP events around each step on the launch stream; with `flush`, the
+    flush runs before each step, outside the timed interval."""
+    ev = []
+    for _ in range(steps):
+        if flush is not None:
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def clock_state():
+    """The GPU's clock readings as the driver tool reports them (raw text)."""
+    import subprocess
+    for cmd in (["amd-smi", "metric", "--clock"], ["rocm-smi", "--showclocks"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+        except Exception:
+            continue
+        if r.returncode == 0 and r.stdout.strip():
+            lines = [ln.strip() for ln in r.stdout.splitlines() if ln.strip()]
+            keep = [ln for ln in lines if any(t in ln.upper() for t in ("SCLK", "MCLK", "GFX", "MEM", "FCLK", "CLK"))]
+            return {"tool": " ".join(cmd), "lines": (keep or lines)[:24]}
+    return None
+
+
+def measured_peaks(dev):
+    """Measured denominators beside the datasheet ones: a large bf16 GEMM
+    (hipBLASLt through torch) for MFMA, a device copy for HBM."""
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    t = per_step_times(lambda: torch.matmul(a, b), 10)
+    gemm = 2.0 * n ** 3 / (min(t) * 1e-3) / 1e12
+    del a, b
+    src = torch.empty(2 ** 30 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    t = per_step_times(lambda: dst.copy_(src), 10)
+    copy = 2.0 * 2 ** 30 / (min(t) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bf16_gemm_tflops": round(gemm, 1), "hbm_copy_GBs": round(copy, 1),
+            "how": "best of 10: torch.matmul 8192^3 bf16; 1 GiB device copy (read + write bytes)"}
+
+
 def run_block(blk, inp, timer=None):
     def rec(name, fn):
         if timer is None:
@@ -135,13 +212,33 @@ class _RowView:
         return self.t[torch.as_tensor(np.asarray(rows))].to(torch.float64).numpy()
 
 
-def cpu_baseline(w, host, nrows, seed=0):
-    import oracle
+def host_cpu():
+    """Cores this process may run on (capped at the 16 a GPU's share of the
+    host provides) and the CPU model."""
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+        n = len(os.sched_getaffinity(0))
     except Exception:
-        threads = os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except Exception:
+        pass
+    return min(n, 16), n, model
+
+
+def cpu_baseline(w, host, nrows, seed=0):
+    """The oracle as it stands, on a bounded sample of query rows of the same
+    block, spread over the host's cores: the rows are independent, so worker
+    threads each evaluate a contiguous share of them (numpy releases the GIL in
+    its array loops), with BLAS held to one thread per worker."""
+    import concurrent.futures as cf
+    import oracle
+    cores, allowed, model = host_cpu()
     q, k, v, kw, vw, gw = host
     f = lambda t: t[0].to(torch.float64).numpy()
     kf, vf = f(k), f(v)
@@ -150,13 +247,26 @@ def cpu_baseline(w, host, nrows, seed=0):
     gwf = [x.numpy().astype(np.float64) for x in gw]
     qv = [_RowView(x[0]) for x in q]
     rows = np.linspace(0, w.L - 1, nrows).round().astype(np.int64)
+    shares = [r for r in np.array_split(rows, cores) if len(r)]
+
+    def one(r):
+        return oracle.hysparse_block(qv, kf, vf, kwf, vwf, gwf, w.scale, w.block, w.topk, w.window, rows=r)
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(1)
+    except Exception:
+        limit = None
     t0 = time.perf_counter()
-    oracle.hysparse_block(qv, kf, vf, kwf, vwf, gwf, w.scale, w.block, w.topk, w.window, rows=rows)
+    with cf.ThreadPoolExecutor(len(shares)) as ex:
+        list(ex.map(one, shares))
     dt = time.perf_counter() - t0
-    return {"value": nrows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    if limit is not None:
+        limit.restore_original_limits()
+    return {"value": nrows / dt, "unit": "tokens/s", "cores": len(shares), "kind": "oracle",
+            "cpu_model": model, "host_cores_allowed": allowed,
             "sample": f"{nrows} query rows spread evenly over L={w.L} of the same block "
                       f"(full layer row + block scores + top-{w.topk} + {w.n_sparse} gated sparse layers), "
-                      f"{dt:.1f} s wall"}
+                      f"{len(shares)} worker threads x 1 BLAS thread, {dt:.1f} s wall"}
 
 
 # ---------------------------------------------------------------------------
@@ -299,6 +409,14 @@ def bench_prefill(args, dev):
     wall = time.perf_counter() - t0
     step_ms = g0.elapsed_time(g1) / args.steps
     log(f"[bench] {args.steps} steps: {step_ms:.3f} ms/step (wall {wall * 1000 / args.steps:.3f})")
+    # per-step distribution, warm (back to back) and cold (caches flushed before each step)
+    warm = per_step_times(lambda: run_block(blk, inp), args.steps)
+    flush = CacheFlush(dev)
+    cold = per_step_times(lambda: run_block(blk, inp), args.steps, flush)
+    del flush
+    timing = {"warm": stats_ms(warm), "cold_512MiB_flush": stats_ms(cold)}
+    log(f"[bench] per step: warm median {timing['warm']['median_ms']} ms, "
+        f"cold median {timing['cold_512MiB_flush']['median_ms']} ms")
     tot = timer.totals_ms()
     per_step = {k: v / args.steps for k, v in tot.items()}
     launches = {k: c // args.steps for k, c in timer.counts().items()}
@@ -346,7 +464,7 @@ def bench_prefill(args, dev):
         roof["traffic"] = TRAFFIC["bytes_per_launch"]
     if dom == "sparse_layer":
         roof["logical_gather_GBs"] = round(gather_bytes / (avg * 1e-3) / 1e9, 1)
-    res = {"w": w, "step_ms": step_ms, "stages": stages, "roofline": roof,
+    res = {"w": w, "step_ms": step_ms, "stages": stages, "roofline": roof, "timing": timing,
            "host": (q_h, k_h, v_h, kw_h, vw_h, gw_h)}
     del inp, blk
     torch.cuda.empty_cache()
@@ -364,23 +482,46 @@ def bench_decode(args, dev):
     vc = vc.to(dev)
     dec = HySparse2Decode(w.B, w.L, w.Hq, w.D, w.n_sparse, w.topk, w.window, device=dev)
     lens = w.lens()
+    step = lambda: dec.run(qf, kc, vc, lens, qs, ks, vs)
     for _ in range(max(3, args.warmup)):
-        dec.run(qf, kc, vc, lens, qs, ks, vs)
+        step()
     torch.cuda.synchronize()
     steps = max(20, args.steps * 5)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):
-        dec.run(qf, kc, vc, lens, qs, ks, vs)
+        step()
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1000 / steps
-    kv_bytes = 2.0 * sum(lens) * w.D          # fp8 K + V streamed by the full layer
-    gbs = kv_bytes / (us * 1e-6) / 1e9
-    log(f"[bench] decode: {us:.1f} us/step, full-layer KV stream {gbs:.0f} GB/s equivalent")
+    warm = per_step_times(step, steps)
+    flush = CacheFlush(dev)
+    cold = per_step_times(step, steps, flush)
+    del flush
+    # Algorithmic HBM bytes of the step: the full layer streams each cache's
+    # valid fp8 K and V once (2*D bytes per token) and writes one fp32 token
+    # score per cached position; the selection reads the scores once; each
+    # sparse layer gathers its selected tokens and recent window (2*D bytes
+    # each).  Queries and outputs (a few hundred KB) are left out.
+    kv_bytes = 2.0 * sum(lens) * w.D
+    score_bytes = 2.0 * 4 * w.B * w.L
+    gather_bytes = 2.0 * w.D * w.n_sparse * w.B * (w.topk + w.window)
+    step_bytes = kv_bytes + score_bytes + gather_bytes
+    gbs = step_bytes / (us * 1e-6) / 1e9
+    timing = {"warm": stats_ms(warm), "cold_512MiB_flush": stats_ms(cold)}
+    log(f"[bench] decode: {us:.1f} us/step ({gbs:.0f} GB/s algorithmic); per step warm median "
+        f"{timing['warm']['median_ms'] * 1000:.1f} us, cold median {timing['cold_512MiB_flush']['median_ms'] * 1000:.1f} us")
     return {"workload": w.name, "us_per_step": round(us, 2), "us_per_token": round(us / w.B, 2),
-            "batch": w.B, "cache_tokens": w.L, "kv_stream_GBs_step_equiv": round(gbs, 1),
-            "frac_hbm_step_equiv": round(gbs / PEAK_HBM_GBS, 4), "steps": steps}
+            "batch": w.B, "cache_tokens": w.L, "steps": steps, "timing": timing,
+            "roofline": {"kernel": "decode step (split-K full layer with token scores, merge, top-1024, "
+                                   f"{w.n_sparse} sparse layers; one ABI call)",
+                         "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "avg_step_us": round(us, 2),
+                         "work_per_step": f"{step_bytes:.4g} B (fp8 K+V of the valid cache, token scores written "
+                                          "and read, gathered tokens of the sparse layers)",
+                         "traffic": DECODE_TRAFFIC["bytes_per_step"]
+                         if DECODE_TRAFFIC and DECODE_TRAFFIC["sources_sha1"] == kernel_sources_sha1(
+                             DECODE_TRAFFIC_SOURCES) else None}}
 
 
 def bench_hs_decode(args, dev):
@@ -557,9 +698,11 @@ def main():
     ap.add_argument("--no-hs-decode", action="store_true")
     ap.add_argument("--only-hs-decode", action="store_true", help="time only the HySparse decode step")
     ap.add_argument("--only-bridge", action="store_true", help="time only the KV Bridging projection")
+    ap.add_argument("--only-decode", action="store_true", help="time only the HySparse2 1M decode step")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak microbenchmarks")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--only-bwd", action="store_true", help="time only the backward pass of the 32k HySparse block")
-    ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--cpu-rows", type=int, default=192)
     ap.add_argument("--workload", default="moe80b_32k",
                     choices=["moe80b_32k", "dense7b_16k", "hysparse2_64k", "tiny_fp32"],
                     help="prefill block to time (default: the 32k HySparse block the metric is quoted on)")
@@ -597,6 +740,10 @@ def main():
     if args.only_bwd:
         print(json.dumps({"backward": bench_bwd(args, dev)}), flush=True)
         return
+    if args.only_decode:
+        print(json.dumps({"decode": bench_decode(args, dev)}), flush=True)
+        return
+    clocks = clock_state()
     pre = bench_prefill(args, dev)
     w = pre["w"]
     dec = None if args.no_decode else bench_decode(args, dev)
@@ -609,6 +756,16 @@ def main():
         log(f"[bench] timing the CPU oracle on {args.cpu_rows} sampled rows")
         cpu = cpu_baseline(w, pre["host"], args.cpu_rows)
         log(f"[bench] oracle: {cpu['value']:.2f} tokens/s on {cpu['cores']} threads")
+    peaks = None if args.no_peaks else measured_peaks(dev)
+    if peaks:
+        log(f"[bench] measured peaks: bf16 GEMM {peaks['bf16_gemm_tflops']} TFLOP/s, copy {peaks['hbm_copy_GBs']} GB/s")
+        roof = pre["roofline"]
+        mp = peaks["bf16_gemm_tflops"] if roof["unit"] == "TFLOP/s" else peaks["hbm_copy_GBs"]
+        roof["measured_peak"] = mp
+        roof["frac_of_measured_peak"] = round(roof["achieved"] / mp, 4)
+        if dec:
+            dec["roofline"]["measured_peak"] = peaks["hbm_copy_GBs"]
+            dec["roofline"]["frac_of_measured_peak"] = round(dec["roofline"]["achieved"] / peaks["hbm_copy_GBs"], 4)
     tok_s = w.L * w.B / (pre["step_ms"] * 1e-3)
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -626,6 +783,9 @@ def main():
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,
         "stages": pre["stages"],
+        "timing": pre.get("timing"),
+        "measured_peaks": peaks,
+        "clocks": clocks,
         "decode": dec,
         "kv_bridge": bridge,
         "hs_decode": hs_dec,

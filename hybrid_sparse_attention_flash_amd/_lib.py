@@ -28,7 +28,11 @@ class HysTensor4(ctypes.Structure):
 
 
 class HysAttnParams(ctypes.Structure):
-    _fields_ = [("softmax_scale", ctypes.c_float), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+    _fields_ = [("softmax_scale", ctypes.c_float), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                ("causal", ctypes.c_int32), ("q_offset", ctypes.c_int64)]
+
+    def __init__(self, softmax_scale=0.0, k_scale=1.0, v_scale=1.0, causal=1, q_offset=0):
+        super().__init__(softmax_scale, k_scale, v_scale, causal, q_offset)
 
 
 class HysScoreParams(ctypes.Structure):

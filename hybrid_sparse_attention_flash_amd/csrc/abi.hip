@@ -72,8 +72,10 @@ hys::ElemType et(int32_t dt) {
   return dt == HYS_F32 ? hys::ET_F32 : (dt == HYS_BF16 ? hys::ET_BF16 : hys::ET_FP8);
 }
 
-// q [B,L,Hq,D], k/v [B,L,Hkv,D] consistency and type rule
-hys_status check_qkv(const hys_tensor4& q, const hys_tensor4& k, const hys_tensor4& v, bool same_len) {
+// q [B,Lq,Hq,D], k/v [B,Lk,Hkv,D] consistency and type rule.  q_off >= 0: a
+// prefill call whose query rows sit at positions q_off .. q_off + Lq - 1 of
+// the keys (q_off + Lq <= Lk); q_off < 0: no length relation (decode).
+hys_status check_qkv(const hys_tensor4& q, const hys_tensor4& k, const hys_tensor4& v, int64_t q_off) {
   hys_status s;
   if ((s = check_tensor(q, "q", false)) != HYS_OK) return s;
   if ((s = check_tensor(k, "k", true)) != HYS_OK) return s;
@@ -88,8 +90,9 @@ hys_status check_qkv(const hys_tensor4& q, const hys_tensor4& k, const hys_tenso
   if (q.shape[2] % k.shape[2] != 0)
     return fail(HYS_ERR_INVALID_ARG, "query heads (%lld) not a multiple of KV heads (%lld)", (long long)q.shape[2],
                 (long long)k.shape[2]);
-  if (same_len && q.shape[1] != k.shape[1])
-    return fail(HYS_ERR_UNSUPPORTED, "prefill self-attention needs equal query and key lengths");
+  if (q_off >= 0 && q_off + q.shape[1] > k.shape[1])
+    return fail(HYS_ERR_INVALID_ARG, "q_offset (%lld) + query length (%lld) exceeds the key length (%lld)",
+                (long long)q_off, (long long)q.shape[1], (long long)k.shape[1]);
   return HYS_OK;
 }
 
@@ -111,6 +114,7 @@ hys::AttnArgs base_args(const hys_attn_params* p, const hys_tensor4& q, const hy
   a.o_f32 = o.dtype == HYS_F32 ? 1 : 0;
   a.lse = lse;
   a.B = (int)q.shape[0]; a.Lq = (int)q.shape[1]; a.Lk = (int)k.shape[1];
+  a.q_off = (int)p->q_offset;
   a.Hq = (int)q.shape[2]; a.Hkv = (int)k.shape[2]; a.G = a.Hq / a.Hkv;
   a.logit_scale = p->softmax_scale * p->k_scale;
   a.scale_log2 = a.logit_scale * 1.4426950408889634f;
@@ -120,6 +124,10 @@ hys::AttnArgs base_args(const hys_attn_params* p, const hys_tensor4& q, const hy
 
 hys_status check_params(const hys_attn_params* p) {
   if (!p) return fail(HYS_ERR_INVALID_ARG, "null params");
+  if (p->causal != 1)
+    return fail(HYS_ERR_UNSUPPORTED, "causal must be 1: every layer of the hybrid block attends causally");
+  if (p->q_offset < 0 || p->q_offset >= (1ll << 30))
+    return fail(HYS_ERR_INVALID_ARG, "q_offset must be in [0, 2^30)");
   if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.f))
     return fail(HYS_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   if (!std::isfinite(p->k_scale) || !(p->k_scale > 0.f) || !std::isfinite(p->v_scale) || !(p->v_scale > 0.f))
@@ -140,21 +148,23 @@ hys_status topk_launch(const float* scores, int64_t rows, int64_t cols, int64_t 
   hys::TopkArgs a{};
   a.scores = scores; a.rows = rows; a.cols = cols; a.row_stride = row_stride; a.k = k;
   a.idx = idx; a.count = count;
-  const int64_t ch = hys::topk_chunk_cols();
-  if (cols > ch) {
-    const int64_t nchunk = (cols + ch - 1) / ch;
-    a.cand_idx = (int32_t*)ws;
-    a.cand_val = (float*)((char*)ws + (size_t)(rows * nchunk * k) * sizeof(int32_t));
-    a.nchunk = (int)nchunk; a.chunk_cols = ch;
+  if (cols > hys::topk_chunk_cols()) {
+    // buffer 1: values then columns of level 0; buffer 2 likewise of level 1
+    const size_t first = hys::topk_workspace_first_bytes(rows, cols, k);
+    const size_t n1 = first / (sizeof(float) + sizeof(int32_t));
+    const size_t total = hys::topk_workspace_bytes(rows, cols, k);
+    const size_t n2 = (total - first) / (sizeof(float) + sizeof(int32_t));
+    a.cand_val = (float*)ws;
+    a.cand_idx = (int32_t*)((char*)ws + n1 * sizeof(float));
+    a.cand_val2 = (float*)((char*)ws + first);
+    a.cand_idx2 = (int32_t*)((char*)ws + first + n2 * sizeof(float));
   }
   return hip_status(hys::launch_topk(a, st), "top-k launch");
 }
 
-int env_int(const char* name, int dflt) {
-  const char* e = std::getenv(name);
-  if (!e || !*e) return dflt;
-  return std::atoi(e);
-}
+// Largest top-k grid: 1024-thread workgroups, grid x threads below 2^32.
+constexpr int64_t kMaxGrid = (int64_t)1 << 22;
+
 
 }  // namespace
 
@@ -217,7 +227,7 @@ hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
   try {
     hys_status s;
     if ((s = check_params(p)) != HYS_OK) return s;
-    if ((s = check_qkv(q, k, v, true)) != HYS_OK) return s;
+    if ((s = check_qkv(q, k, v, p->q_offset)) != HYS_OK) return s;
     if ((s = check_out(o, q, "o")) != HYS_OK) return s;
     if (!ws_bytes) return fail(HYS_ERR_INVALID_ARG, "ws_bytes must not be null");
     const int mode_in = sp ? sp->mode : HYS_SCORE_NONE;
@@ -228,11 +238,11 @@ hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
       if (sp->size != 64) return fail(HYS_ERR_UNSUPPORTED, "score size must be 64 (got %d)", sp->size);
       if (!scores) return fail(HYS_ERR_INVALID_ARG, "scores must not be null when a score mode is set");
     }
-    const int64_t B = q.shape[0], L = q.shape[1], Hq = q.shape[2], Hkv = k.shape[2], D = q.shape[3];
+    const int64_t B = q.shape[0], L = q.shape[1], Lk = k.shape[1], Hq = q.shape[2], Hkv = k.shape[2], D = q.shape[3];
     const int64_t G = Hq / Hkv;
     if (G > 256 && mode_in != HYS_SCORE_TILE_TOKEN)
       return fail(HYS_ERR_UNSUPPORTED, "more than 256 query heads per KV head");
-    const int64_t nblk = (L + 63) / 64;
+    const int64_t nblk = (Lk + 63) / 64;
     size_t need = 0;
     if (mode_in == HYS_SCORE_BLOCK && Hkv > 1) need = (size_t)(Hkv * B * L * nblk) * sizeof(float);
     if (!ws) { *ws_bytes = need; return ok(); }
@@ -243,15 +253,15 @@ hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
     hys::AttnArgs a = base_args(p, q, k, v, o, lse);
     hipStream_t st = (hipStream_t)stream;
     int mode, grid;
-    a.nb = env_int("HYS_NB_FULL", 1) == 2 ? 2 : 1;
-    const int rows = 128 * a.nb;                 // rows per workgroup
+    a.nb = 1;
+    const int rows = 128;                        // rows per workgroup
     if (mode_in == HYS_SCORE_TILE_TOKEN) {
       mode = hys::M_FULL_TILE;
       a.BQ = 64;
       a.HC = (int)(G < rows / 64 ? G : rows / 64);
       a.nhc = (int)((G + a.HC - 1) / a.HC);
       a.ntq = (int)((L + 63) / 64);
-      a.scores = scores; a.sc_sb = (int64_t)a.ntq * L; a.sc_sr = L; a.sc_sg = 0;
+      a.scores = scores; a.sc_sb = (int64_t)a.ntq * Lk; a.sc_sr = Lk; a.sc_sg = 0;
       // one workgroup per (query tile, head chunk), tiles padded to the 8 XCDs
       const int64_t wgs = ((B * a.ntq + 7) / 8) * 8 * Hkv * a.nhc;
       if (wgs > 0x7fffffff) return fail(HYS_ERR_UNSUPPORTED, "too many query tiles x head chunks (%lld)", (long long)wgs);
@@ -275,13 +285,13 @@ hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
     a.grid_used = grid;
     hipError_t e;
     if (mode == hys::M_FULL_TILE) {
-      e = hys::launch_tile_scores(a.scores, (int)B, a.ntq, a.BQ, (int)L, (int)L, a.sc_sb, a.sc_sr, 0, st);
+      e = hys::launch_tile_scores(a.scores, (int)B, a.ntq, a.BQ, (int)L, (int)Lk, a.q_off, a.sc_sb, a.sc_sr, 0, st);
       if (e != hipSuccess) return hip_status(e, "score clear launch");
     }
     e = hys::launch_attn(mode, et(q.dtype), et(k.dtype), (int)D, a, grid, st);
     if (e != hipSuccess) return hip_status(e, "full attention launch");
     if (mode == hys::M_FULL_TILE) {
-      e = hys::launch_tile_scores(a.scores, (int)B, a.ntq, a.BQ, (int)L, (int)L, a.sc_sb, a.sc_sr, 1, st);
+      e = hys::launch_tile_scores(a.scores, (int)B, a.ntq, a.BQ, (int)L, (int)Lk, a.q_off, a.sc_sb, a.sc_sr, 1, st);
       if (e != hipSuccess) return hip_status(e, "score decode launch");
     }
     if (mode == hys::M_FULL_BLOCK && mode_in == HYS_SCORE_BLOCK && Hkv > 1) {
@@ -305,12 +315,9 @@ hys_status hys_select_topk(const float* scores, int64_t rows, int64_t cols, int6
     if (cols >= (1ll << 31)) return fail(HYS_ERR_UNSUPPORTED, "cols >= 2^31");
     if (rows > 0 && row_stride < cols) return fail(HYS_ERR_INVALID_ARG, "row_stride < cols");
     if (rows > (1ll << 31) - 1) return fail(HYS_ERR_UNSUPPORTED, "rows >= 2^31");
-    {
-      const int64_t ch = hys::topk_chunk_cols();
-      if (cols > ch && ((cols + ch - 1) / ch) * (int64_t)k > hys::topk_max_candidates())
-        return fail(HYS_ERR_UNSUPPORTED, "ceil(cols/%lld) * k exceeds %lld", (long long)ch,
-                    (long long)hys::topk_max_candidates());
-    }
+    if (hys::topk_max_workgroups(rows, cols, k) > kMaxGrid)
+      return fail(HYS_ERR_UNSUPPORTED, "rows x ceil(cols / %lld) above %lld workgroups", (long long)hys::topk_chunk_cols(),
+                  (long long)kMaxGrid);
     const size_t need = hys::topk_workspace_bytes(rows, cols, k);
     if (!ws) { *ws_bytes = need; return ok(); }
     if (*ws_bytes < need) return fail(HYS_ERR_WORKSPACE, "workspace %zu < required %zu bytes", *ws_bytes, need);
@@ -325,23 +332,21 @@ hys_status hys_select_topk(const float* scores, int64_t rows, int64_t cols, int6
 // Row sets of the block-selection modes (granularity 64, per-query selection):
 // BQ queries x G heads per workgroup, BQ * k <= 4 * rows so the union of the
 // row set's selected blocks fits the per-workgroup list.
-hys_status setup_block_selection(hys::AttnArgs& a, const hys_sparse_params* sp, int64_t G, int64_t L, int64_t B,
-                                 int64_t Hkv, int& grid) {
+hys_status setup_block_selection(hys::AttnArgs& a, const hys_sparse_params* sp, int64_t G, int64_t L, int64_t Lk,
+                                 int64_t B, int64_t Hkv, int& grid) {
   if (sp->q_tile != 1) return fail(HYS_ERR_UNSUPPORTED, "granularity 64 needs q_tile 1");
   if (sp->forced_window != 0) return fail(HYS_ERR_UNSUPPORTED, "granularity 64 has no forced window");
   if (sp->k > 64) return fail(HYS_ERR_UNSUPPORTED, "granularity 64 needs k <= 64");
   if (G > 256) return fail(HYS_ERR_UNSUPPORTED, "more than 256 query heads per KV head");
-  const int64_t nblk = (L + 63) / 64;
+  const int64_t nblk = (Lk + 63) / 64;
   if (nblk > 16384) return fail(HYS_ERR_UNSUPPORTED, "more than 16384 key blocks");
-  a.nb = env_int("HYS_NB_SPARSE", 1) == 2 ? 2 : 1;
-  const int rows = 128 * a.nb;
+  a.nb = 1;
+  const int rows = 128;
   if (G > rows) return fail(HYS_ERR_UNSUPPORTED, "more than %d query heads per KV head", rows);
   a.HC = (int)G;
   int bq = (int)(rows / G);
   if (bq > 64) bq = 64;
   if (sp->k > 0 && bq > 4 * rows / sp->k) bq = 4 * rows / sp->k;
-  const int bq_env = env_int("HYS_SPARSE_BQ", 0);       // tuning override
-  if (bq_env > 0 && bq_env < bq) bq = bq_env;
   if (bq < 1) bq = 1;
   a.BQ = bq; a.nhc = 1; a.nblk = (int)nblk;
   a.ntq = (int)((L + a.BQ - 1) / a.BQ);
@@ -360,11 +365,8 @@ hys_status hys_select_topk_blocks(const float* scores, int64_t rows, int64_t col
     if (k_blocks < 1 || k_blocks > 32) return fail(HYS_ERR_UNSUPPORTED, "k_blocks must be in [1, 32]");
     if (cols >= (1ll << 31)) return fail(HYS_ERR_UNSUPPORTED, "cols must be below 2^31");
     const int64_t nblk = (cols + 63) / 64;
-    {
-      const int64_t ch = hys::topk_chunk_cols();
-      if (nblk > ch && ((nblk + ch - 1) / ch) * (int64_t)k_blocks > hys::topk_max_candidates())
-        return fail(HYS_ERR_UNSUPPORTED, "rows too long for top-%d blocks", k_blocks);
-    }
+    if (hys::topk_max_workgroups(rows, nblk, k_blocks) > kMaxGrid)
+      return fail(HYS_ERR_UNSUPPORTED, "too many rows x block chunks for the top-k launch");
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t mb = (size_t)(rows * nblk) * sizeof(float), ib = (size_t)(rows * k_blocks) * sizeof(int32_t);
     const size_t tk = hys::topk_workspace_bytes(rows, nblk, k_blocks);
@@ -397,7 +399,7 @@ hys_status hys_sparse_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tens
   try {
     hys_status s;
     if ((s = check_params(p)) != HYS_OK) return s;
-    if ((s = check_qkv(q, k, v, true)) != HYS_OK) return s;
+    if ((s = check_qkv(q, k, v, p->q_offset)) != HYS_OK) return s;
     if ((s = check_out(o, q, "o")) != HYS_OK) return s;
     if (!sp) return fail(HYS_ERR_INVALID_ARG, "null sparse params");
     if (ws_bytes && !ws) { *ws_bytes = 0; return ok(); }
@@ -414,7 +416,7 @@ hys_status hys_sparse_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tens
     a.idx_sg = sp->idx_group_stride;
     int mode, grid;
     if (sp->granularity == 64) {
-      hys_status bs = setup_block_selection(a, sp, G, L, B, Hkv, grid);
+      hys_status bs = setup_block_selection(a, sp, G, L, k.shape[1], B, Hkv, grid);
       if (bs != HYS_OK) return bs;
       mode = hys::M_SPARSE_BLOCK;
     } else if (sp->granularity == 1) {
@@ -423,8 +425,8 @@ hys_status hys_sparse_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tens
       if (sp->forced_window < 0 || sp->forced_window > 1984)
         return fail(HYS_ERR_UNSUPPORTED, "forced_window must be in [0, 1984]");
       mode = hys::M_SPARSE_TOKEN;
-      a.nb = env_int("HYS_NB_TOKEN", 1) == 2 ? 2 : 1;
-      const int hcmax = 2 * a.nb;                // 64 queries x hcmax heads = the workgroup's rows
+      a.nb = 1;
+      const int hcmax = 2;                       // 64 queries x hcmax heads = the workgroup's rows
       a.BQ = 64;
       a.HC = (int)(G < hcmax ? G : hcmax);
       a.nhc = (int)((G + a.HC - 1) / a.HC);
@@ -451,7 +453,7 @@ hys_status hys_swa_gate_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4
   try {
     hys_status s;
     if ((s = check_params(p)) != HYS_OK) return s;
-    if ((s = check_qkv(q, k_win, v_win, true)) != HYS_OK) return s;
+    if ((s = check_qkv(q, k_win, v_win, p->q_offset)) != HYS_OK) return s;
     if (k_win.dtype != q.dtype && !(q.dtype == HYS_BF16 && k_win.dtype == HYS_FP8_E4M3))
       return fail(HYS_ERR_UNSUPPORTED, "window K/V must have q's dtype or be fp8 with bf16 q");
     if ((s = check_out(o, q, "o")) != HYS_OK) return s;
@@ -464,9 +466,9 @@ hys_status hys_swa_gate_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4
     if (L == 0) return ok();
     hys::AttnArgs a = base_args(p, q, k_win, v_win, o, nullptr);
     a.window = window;
-    a.nb = env_int("HYS_NB_SWA", 1) == 2 ? 2 : 1;
-    if (G > 128 * a.nb) return fail(HYS_ERR_UNSUPPORTED, "more than %d query heads per KV head", 128 * a.nb);
-    a.HC = (int)G; a.BQ = (int)(128 * a.nb / G); a.nhc = 1;
+    a.nb = 1;
+    if (G > 128) return fail(HYS_ERR_UNSUPPORTED, "more than 128 query heads per KV head");
+    a.HC = (int)G; a.BQ = (int)(128 / G); a.nhc = 1;
     a.ntq = (int)((L + a.BQ - 1) / a.BQ);
     a.o_sp = (const float*)o_sparse.ptr;
     a.osp_sb = o_sparse.stride[0]; a.osp_st = o_sparse.stride[1]; a.osp_sh = o_sparse.stride[2];
@@ -491,9 +493,9 @@ hys_status hys_sparse_layer_fwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     if ((s = check_params(p)) != HYS_OK) return s;
     if (p->k_scale != 1.f || p->v_scale != 1.f)
       return fail(HYS_ERR_UNSUPPORTED, "k_scale and v_scale must be 1 (K/V of q's type)");
-    if ((s = check_qkv(q, k, v, true)) != HYS_OK) return s;
+    if ((s = check_qkv(q, k, v, p->q_offset)) != HYS_OK) return s;
     if (k.dtype != q.dtype) return fail(HYS_ERR_UNSUPPORTED, "k/v must have q's dtype");
-    if ((s = check_qkv(q, k_win, v_win, true)) != HYS_OK) return s;
+    if ((s = check_qkv(q, k_win, v_win, p->q_offset)) != HYS_OK) return s;
     if (k_win.dtype != q.dtype) return fail(HYS_ERR_UNSUPPORTED, "window K/V must have q's dtype");
     for (int i = 0; i < 4; ++i) {
       if (k_win.shape[i] != k.shape[i] || v_win.shape[i] != v.shape[i])
@@ -518,7 +520,7 @@ hys_status hys_sparse_layer_fwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     a.kw = k_win.ptr; a.vw = v_win.ptr; a.window = window;
     a.gate_w = gate_w; a.gate_b = gate_b;
     int grid = 0;
-    if ((s = setup_block_selection(a, sp, G, L, B, Hkv, grid)) != HYS_OK) return s;
+    if ((s = setup_block_selection(a, sp, G, L, k.shape[1], B, Hkv, grid)) != HYS_OK) return s;
     if (L == 0) return ok();
     a.grid_used = grid;
     return hip_status(hys::launch_attn(hys::M_SPARSE_SWA, et(q.dtype), et(k.dtype), (int)D, a, grid,
@@ -540,10 +542,10 @@ static hys_status decode_step_impl(const hys_decode_params* p, hys_tensor4 q_ful
   try {
     if (!p) return fail(HYS_ERR_INVALID_ARG, "null params");
     if (!ws_bytes) return fail(HYS_ERR_INVALID_ARG, "ws_bytes must not be null");
-    hys_attn_params ap{p->softmax_scale, p->k_scale, p->v_scale};
+    hys_attn_params ap{p->softmax_scale, p->k_scale, p->v_scale, 1, 0};
     hys_status s;
     if ((s = check_params(&ap)) != HYS_OK) return s;
-    if ((s = check_qkv(q_full, k_cache, v_cache, false)) != HYS_OK) return s;
+    if ((s = check_qkv(q_full, k_cache, v_cache, -1)) != HYS_OK) return s;
     if (q_full.dtype != HYS_BF16) return fail(HYS_ERR_UNSUPPORTED, "decode queries must be bf16");
     const int64_t B = q_full.shape[0], Hq = q_full.shape[2], D = q_full.shape[3], Nmax = k_cache.shape[1];
     if (q_full.shape[1] != 1) return fail(HYS_ERR_INVALID_ARG, "decode takes one query token per sequence");
@@ -555,11 +557,8 @@ static hys_status decode_step_impl(const hys_decode_params* p, hys_tensor4 q_ful
     if (p->topk < 1 || p->topk > 2048) return fail(HYS_ERR_UNSUPPORTED, "topk must be in [1, 2048]");
     if (p->window < 0) return fail(HYS_ERR_INVALID_ARG, "window must be >= 0");
     if (Nmax < 1) return fail(HYS_ERR_INVALID_ARG, "empty cache");
-    {
-      const int64_t ch = hys::topk_chunk_cols();
-      if (Nmax > ch && ((Nmax + ch - 1) / ch) * (int64_t)p->topk > hys::topk_max_candidates())
-        return fail(HYS_ERR_UNSUPPORTED, "cache too long for top-%d", p->topk);
-    }
+    if (hys::topk_max_workgroups(B, Nmax, p->topk) > kMaxGrid)
+      return fail(HYS_ERR_UNSUPPORTED, "cache too long for the top-k launch");
     if ((s = check_out(o_full, q_full, "o_full")) != HYS_OK) return s;
     if (!cache_len || !token_scores || !idx) return fail(HYS_ERR_INVALID_ARG, "null cache_len, token_scores or idx");
     if (n_sparse > 0 && (!q_sparse || !o_sparse)) return fail(HYS_ERR_INVALID_ARG, "null q_sparse or o_sparse");
@@ -583,8 +582,6 @@ static hys_status decode_step_impl(const hys_decode_params* p, hys_tensor4 q_ful
     int nsplit = (int)(512 / B);
     if (nsplit < 1) nsplit = 1;
     if ((int64_t)nsplit * 8 > ntiles) nsplit = (int)((ntiles + 7) / 8);
-    const int nsplit_env = env_int("HYS_DECODE_SPLIT", 0);
-    if (nsplit_env > 0) nsplit = nsplit_env;
     const int nsplit_sp = 8;
     const size_t part_full = (size_t)(B * nsplit * Hq) * (size_t)(D + 2) * sizeof(float);
     const size_t part_sp = (size_t)((int64_t)n_sparse * B * nsplit_sp * Hq) * (size_t)(D + 2) * sizeof(float);
@@ -770,10 +767,10 @@ hys_status hys_hysparse_decode_step(const hys_hs_decode_params* p, hys_tensor4 q
   try {
     if (!p) return fail(HYS_ERR_INVALID_ARG, "null params");
     if (!ws_bytes) return fail(HYS_ERR_INVALID_ARG, "ws_bytes must not be null");
-    hys_attn_params ap{p->softmax_scale, 1.f, 1.f};
+    hys_attn_params ap{p->softmax_scale, 1.f, 1.f, 1, 0};
     hys_status s;
     if ((s = check_params(&ap)) != HYS_OK) return s;
-    if ((s = check_qkv(q_full, k_cache, v_cache, false)) != HYS_OK) return s;
+    if ((s = check_qkv(q_full, k_cache, v_cache, -1)) != HYS_OK) return s;
     if (q_full.dtype != HYS_BF16 || k_cache.dtype != HYS_BF16)
       return fail(HYS_ERR_UNSUPPORTED, "HySparse decode takes bf16 queries and a bf16 cache");
     const int64_t B = q_full.shape[0], Hq = q_full.shape[2], D = q_full.shape[3], Nmax = k_cache.shape[1];
@@ -788,11 +785,8 @@ hys_status hys_hysparse_decode_step(const hys_hs_decode_params* p, hys_tensor4 q
     if (p->topk < 1 || p->topk > 64) return fail(HYS_ERR_UNSUPPORTED, "topk must be in [1, 64]");
     if (Nmax < 1) return fail(HYS_ERR_INVALID_ARG, "empty cache");
     const int64_t nblk = (Nmax + 63) / 64;
-    {
-      const int64_t ch = hys::topk_chunk_cols();
-      if (nblk > ch && ((nblk + ch - 1) / ch) * (int64_t)p->topk > hys::topk_max_candidates())
-        return fail(HYS_ERR_UNSUPPORTED, "cache too long for top-%d", p->topk);
-    }
+    if (hys::topk_max_workgroups(B, nblk, p->topk) > kMaxGrid)
+      return fail(HYS_ERR_UNSUPPORTED, "cache too long for the top-k launch");
     if ((s = check_out(o_full, q_full, "o_full")) != HYS_OK) return s;
     if (!cache_len || !block_scores || !idx) return fail(HYS_ERR_INVALID_ARG, "null cache_len, block_scores or idx");
     for (int64_t b = 0; b < B; ++b)
@@ -939,7 +933,7 @@ hys_status hys_window_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tens
   try {
     hys_status s;
     if ((s = check_params(p)) != HYS_OK) return s;
-    if ((s = check_qkv(q, k_win, v_win, true)) != HYS_OK) return s;
+    if ((s = check_qkv(q, k_win, v_win, p->q_offset)) != HYS_OK) return s;
     if (k_win.dtype != q.dtype && !(q.dtype == HYS_BF16 && k_win.dtype == HYS_FP8_E4M3))
       return fail(HYS_ERR_UNSUPPORTED, "window K/V must have q's dtype or be fp8 with bf16 q");
     if ((s = check_out(o, q, "o")) != HYS_OK) return s;
@@ -989,7 +983,10 @@ hys_status check_bwd_inputs(const hys_attn_params* p, const hys_tensor4& q, cons
   hys_status s;
   if ((s = check_params(p)) != HYS_OK) return s;
   if (p->k_scale != 1.f || p->v_scale != 1.f) return fail(HYS_ERR_UNSUPPORTED, "k_scale and v_scale must be 1");
-  if ((s = check_qkv(q, k, v, true)) != HYS_OK) return s;
+  if (p->q_offset != 0) return fail(HYS_ERR_UNSUPPORTED, "%s: the backward pass takes whole sequences (q_offset 0)", what);
+  if ((s = check_qkv(q, k, v, 0)) != HYS_OK) return s;
+  if (q.shape[1] != k.shape[1])
+    return fail(HYS_ERR_UNSUPPORTED, "%s: the backward pass needs equal query and key lengths", what);
   if (q.dtype != HYS_BF16 || k.dtype != HYS_BF16)
     return fail(HYS_ERR_UNSUPPORTED, "%s: the backward pass takes bf16 q, k, v", what);
   if (!same_strides(k, v)) return fail(HYS_ERR_UNSUPPORTED, "%s: k and v must share strides", what);

@@ -34,11 +34,12 @@ hipError_t launch_reduce_max(const float* part, int nparts, int64_t part_stride,
 // and the keys past the tile's last key block to -inf; afterwards the keys are
 // decoded back to fp32 in place
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void tile_scores_kernel(float* sc, int ntq, int BQ, int Lq, int Lk, int64_t sb,
-                                                          int64_t sr, int decode) {
+__global__ __launch_bounds__(256) void tile_scores_kernel(float* sc, int ntq, int BQ, int Lq, int Lk, int q_off,
+                                                          int64_t sb, int64_t sr, int decode) {
   const int row = blockIdx.x;
   const int b = row / ntq, qt = row - b * ntq;
-  const int last = min(min(qt * BQ + BQ, Lq) - 1, Lk - 1);
+  // the tile's last query, as an absolute position
+  const int last = min(min(qt * BQ + BQ, Lq) - 1 + q_off, Lk - 1);
   const int touched = min((last / 64 + 1) * 64, Lk);
   float* p = sc + (int64_t)b * sb + (int64_t)qt * sr;
   uint32_t* u = (uint32_t*)p;
@@ -53,11 +54,12 @@ __global__ __launch_bounds__(256) void tile_scores_kernel(float* sc, int ntq, in
   }
 }
 
-hipError_t launch_tile_scores(float* sc, int B, int ntq, int BQ, int Lq, int Lk, int64_t sb, int64_t sr,
+hipError_t launch_tile_scores(float* sc, int B, int ntq, int BQ, int Lq, int Lk, int q_off, int64_t sb, int64_t sr,
                               int decode, hipStream_t s) {
   const int64_t rows = (int64_t)B * ntq;
   if (rows <= 0 || Lk <= 0) return hipSuccess;
-  hipLaunchKernelGGL(tile_scores_kernel, dim3((unsigned)rows), dim3(256), 0, s, sc, ntq, BQ, Lq, Lk, sb, sr, decode);
+  hipLaunchKernelGGL(tile_scores_kernel, dim3((unsigned)rows), dim3(256), 0, s, sc, ntq, BQ, Lq, Lk, q_off, sb, sr,
+                     decode);
   return hipGetLastError();
 }
 

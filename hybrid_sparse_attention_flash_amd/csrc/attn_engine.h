@@ -105,6 +105,10 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
   }
   const int q0 = qt * a.BQ;
   const int q_last = min(q0 + a.BQ, a.Lq) - 1;
+  // absolute positions (row r of this call is position q_off + r): every
+  // causal and window range below is in absolute positions, rows address
+  // q, o and lse relative to the call
+  const int qa0 = q0 + a.q_off, qa_last = q_last + a.q_off;
   const int HC = a.HC;
   // block scores reduced inside each wave when a query's heads are adjacent lanes
   const bool lane_scores = (MODE == M_FULL_BLOCK) && (32 % HC == 0);
@@ -177,10 +181,10 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
   int npre = 0, wstart = 0, wend = 0;
   int nsp = 0;              // M_SPARSE_SWA: tiles [0, nsp) are selected blocks, the rest the window
   if (MODE == M_FULL || MODE == M_FULL_BLOCK || MODE == M_FULL_TILE) {
-    kbase = 0; kend = min(q_last, a.Lk - 1);
+    kbase = 0; kend = min(qa_last, a.Lk - 1);
     ntiles = kend / 64 + 1;
   } else if (MODE == M_SWA_GATE) {
-    kbase = max(0, q0 - a.window + 1); kend = min(q_last, a.Lk - 1);
+    kbase = max(0, qa0 - a.window + 1); kend = min(qa_last, a.Lk - 1);
     ntiles = (kend - kbase + 1 + 63) / 64;
   } else if (BLOCKSEL) {
     const int nbw = (a.nblk + 31) >> 5;
@@ -235,15 +239,15 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     __syncthreads();
     ntiles = s_misc[0];
     if (MODE == M_SPARSE_SWA) {
-      // then the window [q0 - window + 1, q_last] of the layer's own K/V
+      // then the window [qa0 - window + 1, qa_last] of the layer's own K/V
       nsp = ntiles;
-      wstart = max(0, q0 - a.window + 1);
-      wend = min(q_last, a.Lk - 1);
+      wstart = max(0, qa0 - a.window + 1);
+      wend = min(qa_last, a.Lk - 1);
       ntiles = nsp + (wend - wstart + 1 + 63) / 64;
     }
   } else if (MODE == M_SPARSE_TOKEN) {
-    wstart = max(0, q0 - a.window + 1);
-    wend = min(q_last, a.Lk - 1);
+    wstart = max(0, qa0 - a.window + 1);
+    wend = min(qa_last, a.Lk - 1);
     const int nw = wend - wstart + 1;
     for (int x = tid; x < nw; x += 256) s_selw[x] = 0;
     __syncthreads();
@@ -635,8 +639,8 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             const bool win = MODE == M_SWA_GATE || (MODE == M_SPARSE_SWA && !sel_tile);
-            const int hi = qpos[nb];
-            const int lo = win ? qpos[nb] - a.window + 1 : 0;
+            const int hi = qpos[nb] + a.q_off;
+            const int lo = win ? hi - a.window + 1 : 0;
             bool on = valid[nb];
             if (BLOCKSEL && sel_tile) on = on && ((memb >> qiv[nb]) & 1ull) != 0ull;
             row_on[nb] = on;
@@ -666,7 +670,8 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
                   if (MODE == M_SPARSE_TOKEN) {
                     const int kinf = e == 0 ? ki.x : (e == 1 ? ki.y : (e == 2 ? ki.z : ki.w));
                     const int j = kinf & 0x3fffffff;
-                    ok = row_on[nb] && j <= qpos[nb] && ((kinf >> 30) || (j > qpos[nb] - a.window));
+                    const int ap = qpos[nb] + a.q_off;
+                    ok = row_on[nb] && j <= ap && ((kinf >> 30) || (j > ap - a.window));
                   } else {
                     // key jt0 + off + e lies in [lo, hi]
                     ok = row_on[nb] && (vbase[nb] + (unsigned)(off + e)) <= vspan[nb];
@@ -922,12 +927,13 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
 // ---------------------------------------------------------------------------
 // per-mode launch (instantiated in one translation unit per mode)
 // ---------------------------------------------------------------------------
+// One 32-row MFMA block per wave (NB = 1): two workgroups per CU.  The engine
+// is written for NB 32-row blocks per wave; NB = 2 (64 rows per wave) measured
+// slower (one wave per SIMD, spills) and is not instantiated.
 template <int MODE, typename QT, typename KT, int D>
 static hipError_t launch_one(const AttnArgs& a, int grid, hipStream_t s) {
-  if (a.nb == 1)
-    hipLaunchKernelGGL((attn_tile_kernel<MODE, QT, KT, D, 1>), dim3(grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((attn_tile_kernel<MODE, QT, KT, D, 2>), dim3(grid), dim3(256), 0, s, a);
+  if (a.nb != 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_tile_kernel<MODE, QT, KT, D, 1>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

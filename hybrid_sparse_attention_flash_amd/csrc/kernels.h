@@ -26,6 +26,7 @@ struct AttnArgs {
   int o_f32;                 // 1: fp32 output, 0: bf16 output
   float* lse;                // [B, Hq, Lq] or null
   int B, Lq, Lk, Hq, Hkv, G;
+  int q_off;                 // absolute position of query row 0 (chunked prefill); masks use q_off + row
   float scale_log2;          // softmax scale * k scale * log2(e)
   float logit_scale;         // softmax scale * k scale
   float v_scale;             // V dequantisation scale applied to O
@@ -49,14 +50,14 @@ struct AttnArgs {
   const float* gate_w;       // [Hq, D]
   const float* gate_b;       // [Hq] or null
   int grid_used;             // work items; extra workgroups exit
-  int nb;                    // 32-row MFMA blocks per wave: 2 (256 rows per workgroup) or 1 (128 rows)
+  int nb;                    // 32-row MFMA blocks per wave: 1 (128 rows per workgroup)
 };
 
 hipError_t launch_attn(int mode, int qt, int kt, int D, const AttnArgs& a, int grid, hipStream_t s);
 
 // M_FULL_TILE score rows [B, ntq, Lk] (row stride sr, batch stride sb):
 // decode = 0 clears them to atomic-max keys, decode = 1 turns keys into fp32
-hipError_t launch_tile_scores(float* sc, int B, int ntq, int BQ, int Lq, int Lk, int64_t sb, int64_t sr,
+hipError_t launch_tile_scores(float* sc, int B, int ntq, int BQ, int Lq, int Lk, int q_off, int64_t sb, int64_t sr,
                               int decode, hipStream_t s);
 
 hipError_t launch_reduce_max(const float* part, int nparts, int64_t part_stride, float* out, int64_t n,
@@ -66,12 +67,18 @@ struct TopkArgs {
   const float* scores; int64_t rows, cols, row_stride;
   int k;
   int32_t* idx; int32_t* count;
-  // two-stage path workspace
-  float* cand_val; int32_t* cand_idx; int nchunk; int64_t chunk_cols;
+  // long rows (cols > topk_chunk_cols()): the two candidate buffers of the
+  // level-by-level reduction (topk_workspace_bytes lays them out)
+  float* cand_val; int32_t* cand_idx;      // level 0's output (and levels 2, 4, ...)
+  float* cand_val2; int32_t* cand_idx2;    // level 1's output (and levels 3, 5, ...)
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+// workspace of launch_topk for [rows, cols] and k; 0 when cols <= topk_chunk_cols()
 size_t topk_workspace_bytes(int64_t rows, int64_t cols, int k);
-int64_t topk_max_candidates();
+// split of that workspace: bytes of the first candidate buffer (values then columns)
+size_t topk_workspace_first_bytes(int64_t rows, int64_t cols, int k);
+// largest grid (workgroups) launch_topk uses
+int64_t topk_max_workgroups(int64_t rows, int64_t cols, int k);
 int64_t topk_chunk_cols();
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 

@@ -315,14 +315,58 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
 // ---------------------------------------------------------------------------
 constexpr int kTopkVPT = 32;
 constexpr int64_t kTopkChunk = 1024 * kTopkVPT;      // columns per workgroup pass
+constexpr int kTopkMaxLevels = 8;
 
-size_t topk_workspace_bytes(int64_t rows, int64_t cols, int k) {
-  if (cols <= kTopkChunk) return 0;
-  const int64_t nchunk = (cols + kTopkChunk - 1) / kTopkChunk;
-  return (size_t)(rows * nchunk * (int64_t)k) * (sizeof(float) + sizeof(int32_t));
+// Long rows are reduced level by level: level i cuts its input row into
+// 32768-column chunks and keeps each chunk's top-k (an exact superset of the
+// row's top-k), so its output row is nchunk_i * k candidates long, at most
+// 1/8 of its input for k <= 4096; the last level (<= 32768 columns) writes
+// the result.  Candidates stay in ascending column order at every level
+// (chunk outputs are ascending and chunks are concatenated in order), so a
+// tie still resolves to the lowest column.
+struct TopkPlan {
+  int nlev = 0;                 // reduction levels before the final one
+  int64_t nchunk[kTopkMaxLevels] = {};
+  int64_t cols[kTopkMaxLevels + 1] = {};   // input columns of each level
+};
+
+static TopkPlan topk_plan(int64_t cols, int k) {
+  TopkPlan p;
+  int64_t c = cols;
+  while (c > kTopkChunk && p.nlev < kTopkMaxLevels) {
+    p.cols[p.nlev] = c;
+    p.nchunk[p.nlev] = (c + kTopkChunk - 1) / kTopkChunk;
+    c = p.nchunk[p.nlev] * (int64_t)k;
+    ++p.nlev;
+  }
+  p.cols[p.nlev] = c;
+  return p;
 }
 
-int64_t topk_max_candidates() { return kTopkChunk; }
+// Two candidate buffers, used alternately by the levels: the first holds
+// level 0's output (the largest), the second level 1's.
+size_t topk_workspace_bytes(int64_t rows, int64_t cols, int k) {
+  if (cols <= kTopkChunk) return 0;
+  const TopkPlan p = topk_plan(cols, k);
+  const size_t per = sizeof(float) + sizeof(int32_t);
+  size_t n = (size_t)(rows * p.cols[1]) * per;
+  if (p.nlev >= 2) n += (size_t)(rows * p.cols[2]) * per;
+  return n;
+}
+
+size_t topk_workspace_first_bytes(int64_t rows, int64_t cols, int k) {
+  if (cols <= kTopkChunk) return 0;
+  const TopkPlan p = topk_plan(cols, k);
+  return (size_t)(rows * p.cols[1]) * (sizeof(float) + sizeof(int32_t));
+}
+
+// Workgroups of the widest launch (rows x chunks of the input row).
+int64_t topk_max_workgroups(int64_t rows, int64_t cols, int k) {
+  if (cols <= kTopkChunk) return rows;
+  const TopkPlan p = topk_plan(cols, k);
+  return rows * p.nchunk[0];
+}
+
 int64_t topk_chunk_cols() { return kTopkChunk; }
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
@@ -342,19 +386,34 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
                        (float*)nullptr, a.count);
     return hipGetLastError();
   }
-  // two passes: per-chunk winners (an exact superset of the row's top-k), then
-  // the winners' winners; chunk winners are in ascending column order, so the
-  // concatenation is too and ties still resolve by column
-  const int nchunk = (int)((a.cols + kTopkChunk - 1) / kTopkChunk);
-  hipLaunchKernelGGL((topk_block_kernel<kTopkVPT, false>), dim3((unsigned)(a.rows * nchunk)), dim3(1024), 0, s, a.scores,
-                     (const int32_t*)nullptr, a.rows, a.cols, a.row_stride, kTopkChunk, nchunk, a.k, a.cand_idx,
-                     a.cand_val, (int32_t*)nullptr);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t ccols = (int64_t)nchunk * a.k;       // <= kTopkChunk by validation
-  hipLaunchKernelGGL((topk_block_kernel<kTopkVPT, true>), dim3((unsigned)a.rows), dim3(1024), 0, s, (const float*)a.cand_val,
-                     (const int32_t*)a.cand_idx, a.rows, ccols, ccols, kTopkChunk, 1, a.k, a.idx, (float*)nullptr,
-                     a.count);
+  const TopkPlan p = topk_plan(a.cols, a.k);
+  if (p.cols[p.nlev] > kTopkChunk) return hipErrorInvalidValue;   // excluded by validation
+  // candidate buffers: level i writes buffer i % 2
+  float* val[2] = {a.cand_val, a.cand_val2};
+  int32_t* col[2] = {a.cand_idx, a.cand_idx2};
+  for (int lev = 0; lev < p.nlev; ++lev) {
+    const int64_t nch = p.nchunk[lev];
+    const int64_t out_cols = nch * (int64_t)a.k;
+    int32_t* oi = col[lev & 1];
+    float* ov = val[lev & 1];
+    if (lev == 0) {
+      hipLaunchKernelGGL((topk_block_kernel<kTopkVPT, false>), dim3((unsigned)(a.rows * nch)), dim3(1024), 0, s,
+                         a.scores, (const int32_t*)nullptr, a.rows, a.cols, a.row_stride, kTopkChunk, (int)nch, a.k,
+                         oi, ov, (int32_t*)nullptr);
+    } else {
+      const int64_t in_cols = p.cols[lev];
+      hipLaunchKernelGGL((topk_block_kernel<kTopkVPT, true>), dim3((unsigned)(a.rows * nch)), dim3(1024), 0, s,
+                         (const float*)val[(lev - 1) & 1], (const int32_t*)col[(lev - 1) & 1], a.rows, in_cols,
+                         in_cols, kTopkChunk, (int)nch, a.k, oi, ov, (int32_t*)nullptr);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    (void)out_cols;
+  }
+  const int64_t fc = p.cols[p.nlev];
+  hipLaunchKernelGGL((topk_block_kernel<kTopkVPT, true>), dim3((unsigned)a.rows), dim3(1024), 0, s,
+                     (const float*)val[(p.nlev - 1) & 1], (const int32_t*)col[(p.nlev - 1) & 1], a.rows, fc, fc,
+                     kTopkChunk, 1, a.k, a.idx, (float*)nullptr, a.count);
   return hipGetLastError();
 }
 

@@ -50,9 +50,11 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def hys_full_attn_fwd(q, k, v, o, lse=None, score_mode: str = "none", scores=None, softmax_scale: float = None,
-                      k_scale: float = 1.0, v_scale: float = 1.0, score_size: int = 64):
+                      k_scale: float = 1.0, v_scale: float = 1.0, score_size: int = 64, q_offset: int = 0):
+    """q_offset: absolute position of q's row 0 (chunked prefill: k, v may be
+    longer than q, with q_offset + Lq <= Lk)."""
     lib = _lib.load()
-    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), k_scale, v_scale)
+    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), k_scale, v_scale, q_offset=q_offset)
     sp = HysScoreParams(_SCORE[score_mode], score_size)
     args = [ctypes.byref(p), tensor4(q), tensor4(k), tensor4(v), tensor4(o), _ptr(lse), ctypes.byref(sp),
             _ptr(scores)]
@@ -93,11 +95,11 @@ def hys_select_topk_blocks(scores: torch.Tensor, k_blocks: int, idx: torch.Tenso
 
 def hys_sparse_attn_fwd(q, k, v, idx, o, lse=None, granularity: int = 64, topk: int = None, q_tile: int = 1,
                         forced_window: int = 0, softmax_scale: float = None, k_scale: float = 1.0,
-                        v_scale: float = 1.0):
+                        v_scale: float = 1.0, q_offset: int = 0):
     """idx: [B, R, topk] int32 (R = L for q_tile 1, ceil(L/64) for q_tile 64), or
     [Hkv, B, L, topk] for per-KV-group index sets (granularity 64)."""
     lib = _lib.load()
-    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), k_scale, v_scale)
+    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), k_scale, v_scale, q_offset=q_offset)
     kk = idx.shape[-1] if topk is None else topk
     gs, ib = (idx.stride(0), idx[0]) if idx.dim() == 4 else (0, idx)
     sp = HysSparseParams(granularity, kk, q_tile, forced_window, ib.stride(0), ib.stride(1), gs)
@@ -106,20 +108,20 @@ def hys_sparse_attn_fwd(q, k, v, idx, o, lse=None, granularity: int = 64, topk: 
 
 
 def hys_swa_gate_fwd(q, k_win, v_win, window: int, o_sparse, lse_sparse, gate_w, o, gate_b=None,
-                     softmax_scale: float = None, k_scale: float = 1.0, v_scale: float = 1.0):
+                     softmax_scale: float = None, k_scale: float = 1.0, v_scale: float = 1.0, q_offset: int = 0):
     lib = _lib.load()
-    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), k_scale, v_scale)
+    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), k_scale, v_scale, q_offset=q_offset)
     check(lib.hys_swa_gate_fwd(ctypes.byref(p), tensor4(q), tensor4(k_win), tensor4(v_win), window,
                                tensor4(o_sparse), _ptr(lse_sparse), _ptr(gate_w), _ptr(gate_b), tensor4(o),
                                _stream(q.device)))
 
 
 def hys_sparse_layer_fwd(q, k, v, idx, k_win, v_win, window: int, gate_w, o, gate_b=None, topk: int = None,
-                         softmax_scale: float = None):
+                         softmax_scale: float = None, q_offset: int = 0):
     """One HySparse sparse layer (selected blocks of k/v, own window k_win/v_win, sigmoid gate) in one call.
     idx: [B, L, topk] int32 block ids, or [Hkv, B, L, topk] for per-KV-group index sets."""
     lib = _lib.load()
-    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), 1.0, 1.0)
+    p = HysAttnParams(softmax_scale or 1.0 / math.sqrt(q.shape[-1]), 1.0, 1.0, q_offset=q_offset)
     kk = idx.shape[-1] if topk is None else topk
     gs, ib = (idx.stride(0), idx[0]) if idx.dim() == 4 else (0, idx)
     sp = HysSparseParams(64, kk, 1, 0, ib.stride(0), ib.stride(1), gs)

@@ -90,7 +90,7 @@
 extern "C" {
 #endif
 
-#define HYS_ABI_VERSION 5
+#define HYS_ABI_VERSION 6
 
 #if defined(__GNUC__)
 #define HYS_API __attribute__((visibility("default")))
@@ -120,6 +120,17 @@ typedef struct {
   float softmax_scale;  /* multiplies q.k, normally 1/sqrt(D) */
   float k_scale;        /* fp8 K dequantisation scale (1 for fp32/bf16) */
   float v_scale;        /* fp8 V dequantisation scale (1 for fp32/bf16) */
+  int32_t causal;       /* must be 1: every layer of the hybrid block attends causally
+                           (QbitAI HySparse article, method section); other values
+                           return HYS_ERR_UNSUPPORTED */
+  int64_t q_offset;     /* absolute position of query row 0 in [0, 2^30): row i of q
+                           is position q_offset + i, so a chunk of queries can
+                           attend to a longer cache (chunked prefill: the sparse
+                           layers reuse the full layer's cache, QbitAI HySparse
+                           article, method section).  Needs q_offset + Lq <= Lk.
+                           Causal and window ranges use absolute positions; rows
+                           of q, o, lse, scores and idx stay relative to the call.
+                           The backward calls need 0. */
 } hys_attn_params;
 
 typedef enum {
@@ -175,10 +186,15 @@ typedef struct {
  * layout [Hkv, B, Lq, ceil(Lk/64)] contiguous (per-KV-group selection, an
  * ablation variant of the head reduction; no workspace).
  *
- * q [B, L, Hq, D]; k, v [B, L, Hkv, D] (self-attention: Lq = Lk = L).
- * o [B, L, Hq, D] fp32 or bf16.  lse [B, Hq, L] fp32 or NULL.
+ * q [B, Lq, Hq, D]; k, v [B, Lk, Hkv, D] with p->q_offset + Lq <= Lk: query
+ * row i is at position q_offset + i and sees keys j <= q_offset + i (a whole
+ * sequence: Lq = Lk, q_offset = 0; a chunk of a longer prefill: its rows and
+ * the cache up to its last row).  "i" in the formulas above is that position;
+ * rows of o, lse and scores are the call's rows (score tile t = rows 64t ..
+ * 64t+63 of the call).
+ * o [B, Lq, Hq, D] fp32 or bf16.  lse [B, Hq, Lq] fp32 or NULL.
  * sp may be NULL (no scores); scores must be non-NULL when sp->mode != NONE.
- * Workspace: BLOCK mode with Hkv > 1 needs Hkv * B * L * ceil(L/64) floats.
+ * Workspace: BLOCK mode with Hkv > 1 needs Hkv * B * Lq * ceil(Lk/64) floats.
  */
 HYS_API hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v,
                              hys_tensor4 o, float* lse, const hys_score_params* sp, float* scores,
@@ -195,10 +211,12 @@ HYS_API hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hy
  * -1; count[r] (if non-NULL) the number chosen.  Selection is exact.
  *
  * scores: rows x cols fp32 with row_stride (elements, >= cols).
- * idx: rows x k int32, contiguous.  Limits: cols < 2^31; k <= 4096; rows with
- * more than 32768 columns are split into 32768-column chunks whose winners
- * are selected again, requiring ceil(cols/32768) * k <= 32768, and need
- * workspace.
+ * idx: rows x k int32, contiguous.  Limits: cols < 2^31; k <= 4096.  Rows
+ * with more than 32768 columns are reduced level by level: each 32768-column
+ * chunk keeps its own top-k (an exact superset of the row's), the winners are
+ * concatenated in column order and reduced again until one chunk remains, so
+ * any length is exact; rows * ceil(cols/32768) must stay below 2^22.  Those
+ * rows need workspace (two candidate buffers).
  */
 HYS_API hys_status hys_select_topk(const float* scores, int64_t rows, int64_t cols, int64_t row_stride, int32_t k,
                            int32_t* idx, int32_t* count, void* ws, size_t* ws_bytes, void* stream);
@@ -239,8 +257,10 @@ HYS_API hys_status hys_select_topk_blocks(const float* scores, int64_t rows, int
  * O[b,i,h,:] = softmax over J(i) of S, applied to V; lse[b,h,i] likewise
  * (-inf when J(i) is empty, with O = 0).  Entries < 0 are ignored; entries of
  * a row must be distinct (hys_select_topk guarantees this).
- * o [B, L, Hq, D] fp32 or bf16; lse [B, Hq, L] fp32 or NULL.
- * Limits: granularity 64 needs k <= 64 and ceil(L/64) <= 16384; granularity 1
+ * q [B, Lq, Hq, D]; k, v [B, Lk, Hkv, D] with p->q_offset + Lq <= Lk: "i"
+ * above is the position q_offset + row; idx rows (and tiles) are the call's.
+ * o [B, Lq, Hq, D] fp32 or bf16; lse [B, Hq, Lq] fp32 or NULL.
+ * Limits: granularity 64 needs k <= 64 and ceil(Lk/64) <= 16384; granularity 1
  * needs k <= 2048 and forced_window <= 1984.  No workspace is used.
  */
 HYS_API hys_status hys_sparse_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v,
@@ -257,11 +277,12 @@ HYS_API hys_status hys_sparse_attn_fwd(const hys_attn_params* p, hys_tensor4 q, 
  *   z = <q[b,i,h,:], gate_w[h,:]> (+ gate_b[h]),  g = 1/(1+exp(-z)),
  *   o = g * o_sparse + (1-g) * O_window,
  * and o = O_window where lse_sparse = -inf (empty sparse set).
- * q [B, L, Hq, D]; k_win, v_win [B, L, Hkv, D] of q's type, or fp8 e4m3 with
+ * q [B, Lq, Hq, D]; k_win, v_win [B, Lk, Hkv, D] (p->q_offset + Lq <= Lk; the
+ * window is taken at position q_offset + row) of q's type, or fp8 e4m3 with
  * bf16 q (dequantised by p->k_scale, p->v_scale: a gated window over an fp8
  * shared cache, the HySparse2 ablation of the forced window); o_sparse fp32
- * [B, L, Hq, D]; lse_sparse [B, Hq, L]; gate_w [Hq, D] fp32; gate_b [Hq] or
- * NULL; o [B, L, Hq, D] fp32 or bf16.
+ * [B, Lq, Hq, D]; lse_sparse [B, Hq, Lq]; gate_w [Hq, D] fp32; gate_b [Hq] or
+ * NULL; o [B, Lq, Hq, D] fp32 or bf16.
  */
 HYS_API hys_status hys_swa_gate_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k_win, hys_tensor4 v_win,
                             int32_t window, hys_tensor4 o_sparse, const float* lse_sparse, const float* gate_w,
@@ -283,11 +304,12 @@ HYS_API hys_status hys_swa_gate_fwd(const hys_attn_params* p, hys_tensor4 q, hys
  * is held in o's storage type between the branches (so with a bf16 o it is
  * rounded to bf16 before the gate; with fp32 o the result matches the
  * two-call form up to fp32 rounding).
- * q [B, L, Hq, D] bf16 or fp32; k, v, k_win, v_win [B, L, Hkv, D] of q's type,
- * the window tensors with the same strides as k and v; idx and sp as for
+ * q [B, Lq, Hq, D] bf16 or fp32; k, v, k_win, v_win [B, Lk, Hkv, D] of q's
+ * type (p->q_offset + Lq <= Lk, positions as for hys_sparse_attn_fwd), the
+ * window tensors with the same strides as k and v; idx and sp as for
  * hys_sparse_attn_fwd with granularity 64 (k <= 64; per-KV-group index sets
  * through idx_group_stride as there); gate_w [Hq, D] fp32;
- * gate_b [Hq] fp32 or NULL; o [B, L, Hq, D] fp32 or bf16.  p->k_scale and
+ * gate_b [Hq] fp32 or NULL; o [B, Lq, Hq, D] fp32 or bf16.  p->k_scale and
  * p->v_scale must be 1.  No workspace.
  */
 HYS_API hys_status hys_sparse_layer_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4 k, hys_tensor4 v,

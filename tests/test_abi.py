@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol():
     assert declared == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(lib(), name)
-    assert lib().hys_abi_version() == 5
+    assert lib().hys_abi_version() == 6
     assert lib().hys_status_string(3) == b"HYS_ERR_WORKSPACE"
 
 
@@ -340,3 +340,30 @@ def test_decode_noalloc_validation_and_scratch_limit():
     assert nb.value > 64 << 20
     assert call(64, 4096, [4096] * 64, n_sparse=big) == WORKSPACE
     assert b"scratch" in L.hys_last_error()
+
+
+def test_attn_params_causal_and_q_offset():
+    """hys_attn_params carries causal (must be 1) and q_offset (row 0's absolute
+    position, q_offset + Lq <= Lk); the backward calls take q_offset 0 only."""
+    import ctypes as C
+    assert C.sizeof(HysAttnParams) == 24 and HysAttnParams.q_offset.offset == 16
+    q, kv = t4([1, 64, 8, 128]), t4([1, 256, 2, 128])
+    o = t4([1, 64, 8, 128], dtype=0)
+    assert _full(HysAttnParams(0.125, 1.0, 1.0, 1, 192), q, kv, kv, o) == 0          # chunk of a 256-token cache
+    assert _full(HysAttnParams(0.125, 1.0, 1.0, 1, 193), q, kv, kv, o) == INVALID    # 193 + 64 > 256
+    assert _full(HysAttnParams(0.125, 1.0, 1.0, 0, 0), q, kv, kv, o) == UNSUPPORTED  # non-causal
+    assert b"causal" in lib().hys_last_error()
+    assert _full(HysAttnParams(0.125, 1.0, 1.0, 1, -1), q, kv, kv, o) == INVALID
+    # score sizes follow the key length: BLOCK with 2 KV groups needs Hkv*B*Lq*ceil(Lk/64) floats
+    sp = HysScoreParams(1, 64)
+    nb = C.c_size_t(0)
+    assert _full(HysAttnParams(0.125, 1.0, 1.0, 1, 100), q, kv, kv, o, sp, C.c_void_p(FAKE), None, nb) == 0
+    assert nb.value == 2 * 1 * 64 * 4 * 4
+    # the backward pass refuses an offset
+    L = lib()
+    qb, kb = t4([1, 64, 8, 128]), t4([1, 64, 2, 128])
+    of = t4([1, 64, 8, 128], dtype=0)
+    kf = t4([1, 64, 2, 128], dtype=0)
+    args = [C.byref(HysAttnParams(0.125, 1.0, 1.0, 1, 3)), qb, kb, kb, qb, C.c_void_p(FAKE), qb, of, kf, kf, 0,
+            None, C.byref(nb), None]
+    assert L.hys_full_attn_bwd(*args) == UNSUPPORTED

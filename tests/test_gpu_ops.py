@@ -94,6 +94,7 @@ def test_full_attention_tile_token_scores(name, L, Hq, Hkv, D):
 
 @pytest.mark.parametrize("rows,cols,k", [(300, 16, 4), (257, 512, 16), (64, 2048, 64), (33, 3000, 100),
                                          (5, 65536, 1024), (3, 200001, 1024), (4, 32768, 1000), (2, 1048576, 1024),
+                                         (2, 1048576 + 4096, 1024), (1, 3000001, 2048),
                                          (7, 100, 0), (9, 40, 50), (6, 2048, 16), (6, 1000, 65), (5, 64, 64),
                                          (8, 700, 33)])
 def test_select_topk_exact(rows, cols, k):
