@@ -417,6 +417,7 @@ def bench_prefill(args, dev):
     timing = {"warm": stats_ms(warm), "cold_512MiB_flush": stats_ms(cold)}
     log(f"[bench] per step: warm median {timing['warm']['median_ms']} ms, "
         f"cold median {timing['cold_512MiB_flush']['median_ms']} ms")
+    timing["clocks_after_timed_steps"] = clock_state()
     tot = timer.totals_ms()
     per_step = {k: v / args.steps for k, v in tot.items()}
     launches = {k: c // args.steps for k, c in timer.counts().items()}
@@ -743,7 +744,7 @@ def main():
     if args.only_decode:
         print(json.dumps({"decode": bench_decode(args, dev)}), flush=True)
         return
-    clocks = clock_state()
+    clocks = clock_state()      # before any timed work (idle clocks)
     pre = bench_prefill(args, dev)
     w = pre["w"]
     dec = None if args.no_decode else bench_decode(args, dev)
@@ -785,7 +786,7 @@ def main():
         "stages": pre["stages"],
         "timing": pre.get("timing"),
         "measured_peaks": peaks,
-        "clocks": clocks,
+        "clocks_at_start": clocks,
         "decode": dec,
         "kv_bridge": bridge,
         "hs_decode": hs_dec,

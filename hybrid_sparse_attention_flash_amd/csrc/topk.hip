@@ -191,29 +191,55 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
   };
   const int nvalid = count_ge(1u);
   const bool all = !(nvalid > k && k > 0);
-  // ---- the k-th largest key T by radix selection: four rounds over the 8-bit
-  // digits from the top; each round histograms the digit of the keys that
-  // share the digits chosen so far and picks, scanning digits downward, the
-  // one whose bin holds the remaining rank.  need = how many keys equal to T
-  // are taken (the rest of k after all keys > T).
+  // ---- the k-th largest key T by radix selection.  The digits start below
+  // the leading bits that every valid key shares (those of the smallest and
+  // largest valid key): scores of one row mostly share sign and exponent, and
+  // a first digit taken from those bits would send nearly every key's atomic
+  // to one histogram bin, whose updates serialise.  Each round histograms
+  // the next (up to) 8-bit digit of the keys that match the digits chosen so
+  // far and picks, scanning digits downward, the one whose bin holds the
+  // remaining rank.  need = how many keys equal to T are taken (the rest of k
+  // after all keys > T).
   __shared__ __attribute__((aligned(16))) int histc[256 * 32];
   __shared__ int s_pick[2];
+  __shared__ uint32_t s_mm[2][16];
   uint32_t T = 0u;
   int need = 0;
   if (!all) {
-    uint32_t prefix = 0u, pmask = 0u;
+    // smallest and largest valid key of the chunk
+    uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      if (key[v] != 0u) { lo = min(lo, key[v]); hi = max(hi, key[v]); }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+      hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+    }
+    if (lane == 0) { s_mm[0][wave] = lo; s_mm[1][wave] = hi; }
+    __syncthreads();
+    lo = 0xffffffffu; hi = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { lo = min(lo, s_mm[0][i]); hi = max(hi, s_mm[1][i]); }
+    // bits [31, 32 - common] are shared by every valid key
+    const int common = (lo == hi) ? 32 : __clz(lo ^ hi);
+    uint32_t prefix = common == 0 ? 0u : (lo & (0xffffffffu << (32 - common)));
+    uint32_t pmask = common == 0 ? 0u : (0xffffffffu << (32 - common));
     int krem = k;
-    for (int round = 0; round < 4; ++round) {
-      const int shift = 24 - 8 * round;
+    for (int rem_bits = 32 - common; rem_bits > 0;) {
+      const int width = rem_bits < 8 ? rem_bits : 8;
+      const int shift = rem_bits - width;
+      const uint32_t dmask = (1u << width) - 1u;
 #pragma unroll
       for (int i = 0; i < 8; ++i) histc[tid + 1024 * i] = 0;
       __syncthreads();
       // 32 copies of each bin, lane l adding to copy l % 32, so lanes that
-      // share a digit (often all of them: the top digit is sign and
-      // exponent) do not serialise on one LDS address
+      // share a digit do not serialise on one LDS address
 #pragma unroll
       for (int v = 0; v < VPT; ++v)
-        if (key[v] != 0u && (key[v] & pmask) == prefix) atomicAdd(&histc[((key[v] >> shift) & 255u) * 32 + (tid & 31)], 1);
+        if (key[v] != 0u && (key[v] & pmask) == prefix)
+          atomicAdd(&histc[((key[v] >> shift) & dmask) * 32 + (tid & 31)], 1);
       __syncthreads();
       // thread t < 256 takes digit 255 - t; an inclusive scan over t counts
       // the keys with that digit or a larger one
@@ -232,8 +258,9 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
       }
       __syncthreads();
       prefix |= (uint32_t)s_pick[0] << shift;
-      pmask |= 0xFFu << shift;
+      pmask |= dmask << shift;
       krem -= s_pick[1];
+      rem_bits -= width;
       __syncthreads();                          // s_pick, shc and histc are rewritten next round
     }
     T = prefix;

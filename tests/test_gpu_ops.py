@@ -219,6 +219,12 @@ def test_swa_gate(name, L, Hq, Hkv, D, W):
     ("moe80b_32k", 512, 16, 2, 128, 6, 77, "f32"),
     ("moe80b_32k", 300, 8, 1, 128, 16, 128, "bf16"),
     ("dense7b_16k", 200, 4, 4, 64, 0, 1, "f32"),
+    # 16-row-block kernel (bf16, 2..16 heads per KV head): every head ratio,
+    # both head dims, an empty selection, ragged lengths
+    ("dense7b_16k", 200, 8, 4, 64, 0, 1, "f32"),
+    ("moe80b_32k", 150, 32, 2, 128, 5, 128, "bf16"),
+    ("moe80b_32k", 333, 16, 2, 64, 8, 100, "f32"),
+    ("dense7b_16k", 257, 16, 4, 128, 2, 40, "bf16"),
 ])
 def test_sparse_layer_fused(name, L, Hq, Hkv, D, k, W, out):
     """The one-pass sparse layer against the oracle's sparse branch, window branch and gate."""
