@@ -523,6 +523,9 @@ hys_status hys_sparse_layer_fwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     if ((s = setup_block_selection(a, sp, G, L, k.shape[1], B, Hkv, grid)) != HYS_OK) return s;
     if (L == 0) return ok();
     a.grid_used = grid;
+    // bf16 inputs: the dedicated kernel (LDS-direct tile loads); fp32 and fp8: the engine
+    if (q.dtype == HYS_BF16 && k.dtype == HYS_BF16)
+      return hip_status(hys::launch_sparse_layer((int)D, a, grid, (hipStream_t)stream), "sparse layer launch");
     return hip_status(hys::launch_attn(hys::M_SPARSE_SWA, et(q.dtype), et(k.dtype), (int)D, a, grid,
                                        (hipStream_t)stream),
                       "sparse layer launch");

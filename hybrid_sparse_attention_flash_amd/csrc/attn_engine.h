@@ -28,6 +28,7 @@
 #pragma once
 #include "common.h"
 #include "kernels.h"
+#include "block_union.h"
 #include <type_traits>
 
 namespace hys {
@@ -187,57 +188,9 @@ __global__ __launch_bounds__(256, (NB == 1) ? 2 : 1) void attn_tile_kernel(const
     kbase = max(0, qa0 - a.window + 1); kend = min(qa_last, a.Lk - 1);
     ntiles = (kend - kbase + 1 + 63) / 64;
   } else if (BLOCKSEL) {
-    const int nbw = (a.nblk + 31) >> 5;
-    for (int w = tid; w < nbw; w += 256) s_bitmap[w] = 0u;
-    for (int u = tid; u < UMAX; u += 256) s_member[u] = 0ull;
-    __syncthreads();
-    const int nent = a.BQ * a.topk;
     const int32_t* ib = a.idx + (int64_t)b * a.idx_sb + (int64_t)g * a.idx_sg;
-    for (int e = tid; e < nent; e += 256) {
-      const int qi = e / a.topk, s = e - qi * a.topk;
-      const int q = q0 + qi;
-      if (q < a.Lq) {
-        const int c = ib[(int64_t)q * a.idx_sr + s];
-        if (c >= 0 && c < a.nblk) atomicOr(&s_bitmap[c >> 5], 1u << (c & 31));
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      int carry = 0;
-      for (int w0 = 0; w0 < nbw; w0 += 64) {
-        const int w = w0 + lane;
-        const int cnt = (w < nbw) ? __popc(s_bitmap[w]) : 0;
-        int x = cnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) { const int y = __shfl_up(x, o); if (lane >= o) x += y; }
-        if (w < nbw) s_wpre[w] = carry + x - cnt;
-        carry += __shfl(x, 63);
-      }
-      if (lane == 0) s_misc[0] = carry;
-    }
-    __syncthreads();
-    for (int w = tid; w < nbw; w += 256) {
-      uint32_t bits = s_bitmap[w];
-      int pos = s_wpre[w];
-      while (bits) {
-        const int bit = __ffs(bits) - 1;
-        bits &= bits - 1;
-        s_ulist[pos++] = w * 32 + bit;
-      }
-    }
-    for (int e = tid; e < nent; e += 256) {
-      const int qi = e / a.topk, s = e - qi * a.topk;
-      const int q = q0 + qi;
-      if (q < a.Lq) {
-        const int c = ib[(int64_t)q * a.idx_sr + s];
-        if (c >= 0 && c < a.nblk) {
-          const int u = s_wpre[c >> 5] + __popc(s_bitmap[c >> 5] & ((1u << (c & 31)) - 1u));
-          atomicOr(&s_member[u], 1ull << qi);
-        }
-      }
-    }
-    __syncthreads();
-    ntiles = s_misc[0];
+    ntiles = build_block_union<UMAX, NBWMAX>(ib, a.idx_sr, a.topk, q0, a.BQ, a.Lq, a.nblk, s_bitmap, s_wpre,
+                                             s_ulist, s_member, &s_misc[0]);
     if (MODE == M_SPARSE_SWA) {
       // then the window [qa0 - window + 1, qa_last] of the layer's own K/V
       nsp = ntiles;
