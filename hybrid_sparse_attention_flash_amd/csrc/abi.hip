@@ -43,6 +43,24 @@ size_t elem_size(int32_t dt) { return dt == HYS_F32 ? 4 : (dt == HYS_BF16 ? 2 : 
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// ---------------------------------------------------------------------------
+// Launch-arithmetic checks of the debug build (compiled with -DHYS_DEBUG).
+// Before each launch the derived configuration (work decomposition, grid,
+// score and workspace layout, 32-bit offsets the kernels form) is re-derived
+// from the shapes and compared; a violation returns HYS_ERR_INTERNAL naming
+// the broken invariant.  In the normal build the checks compile to nothing.
+#ifdef HYS_DEBUG
+#define HYS_DCHECK(cond)                                                                                   \
+  do {                                                                                                     \
+    if (!(cond)) return fail(HYS_ERR_INTERNAL, "launch check failed: %s (line %d)", #cond, __LINE__);     \
+  } while (0)
+#else
+#define HYS_DCHECK(cond) \
+  do {                   \
+  } while (0)
+#endif
+
+
 // Shape/stride sanity of one [B, T, H, D] tensor.
 hys_status check_tensor(const hys_tensor4& t, const char* name, bool allow_fp8) {
   if (!t.ptr) return fail(HYS_ERR_INVALID_ARG, "%s: null pointer", name);
@@ -158,12 +176,55 @@ hys_status topk_launch(const float* scores, int64_t rows, int64_t cols, int64_t 
     a.cand_idx = (int32_t*)((char*)ws + n1 * sizeof(float));
     a.cand_val2 = (float*)((char*)ws + first);
     a.cand_idx2 = (int32_t*)((char*)ws + first + n2 * sizeof(float));
+    HYS_DCHECK(first <= total && first == n1 * (sizeof(float) + sizeof(int32_t)) &&
+               total - first == n2 * (sizeof(float) + sizeof(int32_t)));
+    HYS_DCHECK(n1 >= (size_t)rows * (size_t)k && (n2 == 0 || n2 >= (size_t)rows * (size_t)k));
   }
   return hip_status(hys::launch_topk(a, st), "top-k launch");
 }
 
 // Largest top-k grid: 1024-thread workgroups, grid x threads below 2^32.
 constexpr int64_t kMaxGrid = (int64_t)1 << 22;
+
+// every prefill attention launch (engine modes and the sparse-layer kernel)
+hys_status check_attn_launch(const hys::AttnArgs& a, int mode, int grid) {
+  const bool tile_mode = mode == hys::M_FULL_TILE || mode == hys::M_SPARSE_TOKEN;
+  const bool blocksel = mode == hys::M_SPARSE_BLOCK || mode == hys::M_SPARSE_SWA;
+  (void)tile_mode; (void)blocksel; (void)a; (void)grid;
+  HYS_DCHECK(grid >= 1 && grid == a.grid_used);
+  HYS_DCHECK(a.B >= 1 && a.Lq >= 1 && a.q_off >= 0 && (int64_t)a.q_off + a.Lq <= a.Lk && a.Lk < (1 << 30));
+  HYS_DCHECK(a.Hkv >= 1 && a.G >= 1 && a.Hq == a.G * a.Hkv);
+  HYS_DCHECK(a.BQ >= 1 && a.ntq == (a.Lq + a.BQ - 1) / a.BQ);
+  HYS_DCHECK(a.HC >= 1 && a.BQ * a.HC <= 128 && (int64_t)a.nhc * a.HC >= a.G && (int64_t)(a.nhc - 1) * a.HC < a.G);
+  if (tile_mode) {
+    HYS_DCHECK(a.BQ == 64);
+    HYS_DCHECK((int64_t)grid == ((int64_t)a.B * a.ntq + 7) / 8 * 8 * a.Hkv * a.nhc);
+  } else {
+    HYS_DCHECK(a.nhc == 1 && a.HC == a.G);
+    HYS_DCHECK((int64_t)grid == (int64_t)a.B * a.ntq * a.Hkv);
+  }
+  // the kernels address 64 key rows of an operand with 32-bit offsets
+  HYS_DCHECK(a.k_st >= 0 && a.v_st >= 0 && 64 * a.k_st < (1ll << 31) && 64 * a.v_st < (1ll << 31));
+  if (mode == hys::M_FULL_BLOCK)
+    HYS_DCHECK(a.scores && a.nblk == (a.Lk + 63) / 64 && a.sc_sr >= a.nblk && a.sc_sb >= (int64_t)a.Lq * a.sc_sr);
+  if (mode == hys::M_FULL_TILE) HYS_DCHECK(a.scores && a.sc_sr == a.Lk && a.sc_sb == (int64_t)a.ntq * a.Lk);
+  if (blocksel) {
+    HYS_DCHECK(a.nblk == (a.Lk + 63) / 64 && a.nblk <= 16384);
+    HYS_DCHECK(a.BQ <= 64 && a.topk >= 0 && a.topk <= 64 && a.BQ * a.topk <= 512 && a.idx_sr >= a.topk);
+  }
+  // token mode: the selected-token list and the window flags of one query tile fit their LDS arrays
+  if (mode == hys::M_SPARSE_TOKEN) HYS_DCHECK(a.topk >= 0 && a.topk <= 2048 && a.window >= 0 && a.window + a.BQ - 1 <= 2048);
+  if (mode == hys::M_SWA_GATE || mode == hys::M_SPARSE_SWA) HYS_DCHECK(a.window >= 1);
+  if (mode == hys::M_SPARSE_SWA) HYS_DCHECK(a.kw && a.vw && a.gate_w);
+  return HYS_OK;
+}
+
+// a workspace carved into consecutive parts: [p, p + bytes) inside [ws, ws + total)
+bool inside(const void* p, size_t bytes, const void* ws, size_t total) {
+  const char* c = (const char*)p;
+  const char* w = (const char*)ws;
+  return c >= w && (size_t)(c - w) <= total && bytes <= total - (size_t)(c - w);
+}
 
 
 }  // namespace
@@ -283,6 +344,7 @@ hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
       grid = (int)(B * a.ntq * Hkv);
     }
     a.grid_used = grid;
+    if ((s = check_attn_launch(a, mode, grid)) != HYS_OK) return s;
     hipError_t e;
     if (mode == hys::M_FULL_TILE) {
       e = hys::launch_tile_scores(a.scores, (int)B, a.ntq, a.BQ, (int)L, (int)Lk, a.q_off, a.sc_sb, a.sc_sr, 0, st);
@@ -439,6 +501,7 @@ hys_status hys_sparse_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tens
     }
     if (L == 0) return ok();
     a.grid_used = grid;
+    if ((s = check_attn_launch(a, mode, grid)) != HYS_OK) return s;
     return hip_status(hys::launch_attn(mode, et(q.dtype), et(k.dtype), (int)D, a, grid, (hipStream_t)stream),
                       "sparse attention launch");
   } catch (...) {
@@ -475,6 +538,7 @@ hys_status hys_swa_gate_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor4
     a.lse_sp = lse_sparse; a.gate_w = gate_w; a.gate_b = gate_b;
     const int grid = (int)(B * a.ntq * Hkv);
     a.grid_used = grid;
+    if ((s = check_attn_launch(a, hys::M_SWA_GATE, grid)) != HYS_OK) return s;
     return hip_status(hys::launch_attn(hys::M_SWA_GATE, et(q.dtype), et(k_win.dtype), (int)D, a, grid,
                                        (hipStream_t)stream),
                       "window+gate launch");
@@ -523,6 +587,7 @@ hys_status hys_sparse_layer_fwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     if ((s = setup_block_selection(a, sp, G, L, k.shape[1], B, Hkv, grid)) != HYS_OK) return s;
     if (L == 0) return ok();
     a.grid_used = grid;
+    if ((s = check_attn_launch(a, hys::M_SPARSE_SWA, grid)) != HYS_OK) return s;
     // bf16 inputs: the dedicated kernel (LDS-direct tile loads); fp32 and fp8: the engine
     if (q.dtype == HYS_BF16 && k.dtype == HYS_BF16)
       return hip_status(hys::launch_sparse_layer((int)D, a, grid, (hipStream_t)stream), "sparse layer launch");
@@ -602,6 +667,11 @@ static hys_status decode_step_impl(const hys_decode_params* p, hys_tensor4 q_ful
     float* ps_ml = ps_o + (size_t)((int64_t)n_sparse * B * nsplit_sp * Hq) * D;
     w += up(part_sp);
     void* tkws = w;
+    HYS_DCHECK(nsplit >= 1 && nsplit <= ntiles && (int64_t)nsplit * B <= 512 + B);
+    HYS_DCHECK(inside(pf_ml, (size_t)(B * nsplit * Hq) * 2 * sizeof(float), ws, up(part_full)));
+    HYS_DCHECK(inside(ps_ml, (size_t)((int64_t)n_sparse * B * nsplit_sp * Hq) * 2 * sizeof(float), ws,
+                      up(part_full) + up(part_sp)));
+    HYS_DCHECK(inside(tkws, tk, ws, need));
 
     hipStream_t st = (hipStream_t)stream;
     const float logit_scale = p->softmax_scale * p->k_scale;
@@ -953,6 +1023,7 @@ hys_status hys_window_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tens
     a.gate_w = nullptr;                       // no gate: the window branch alone, with its LSE
     const int grid = (int)(B * a.ntq * Hkv);
     a.grid_used = grid;
+    if ((s = check_attn_launch(a, hys::M_SWA_GATE, grid)) != HYS_OK) return s;
     return hip_status(hys::launch_attn(hys::M_SWA_GATE, et(q.dtype), et(k_win.dtype), (int)D, a, grid,
                                        (hipStream_t)stream),
                       "window launch");

@@ -219,13 +219,7 @@ __global__ __launch_bounds__(256, 2) void sparse_layer_kernel(const AttnArgs a) 
   const float lazy_raw = kLazyLog2 / c2;
   float m_run[2], l_run[2];
   f32x4 acc[2][P::NDB];
-#ifndef SL_SOFTMAX_BOTH
-#define SL_SOFTMAX_BOTH 0
-#endif
-#ifndef SL_PARK_REGS
-#define SL_PARK_REGS 1
-#endif
-  uint32_t osp[2][P::NDB][2];     // sparse branch, packed bf16 (bf16 outputs, SL_PARK_REGS)
+  uint32_t osp[2][P::NDB][2];     // sparse branch, packed bf16 (bf16 outputs)
   bool sp_live[2];
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
@@ -252,14 +246,9 @@ __global__ __launch_bounds__(256, 2) void sparse_layer_kernel(const AttnArgs a) 
         const f32x4 r = acc[gi][db] * inv;
         if (a.o_f32) {
           if (valid[gi]) *(f32x4*)((float*)a.o + row_off(gi) + 16 * db + 4 * lg) = r;
-        } else if (SL_PARK_REGS) {
+        } else {
           osp[gi][db][0] = pack_bf16x2(r[0], r[1]);
           osp[gi][db][1] = pack_bf16x2(r[2], r[3]);
-        } else if (valid[gi]) {
-          uint2 pk;
-          pk.x = pack_bf16x2(r[0], r[1]);
-          pk.y = pack_bf16x2(r[2], r[3]);
-          *(uint2*)((uint16_t*)a.o + row_off(gi) + 16 * db + 4 * lg) = pk;
         }
         acc[gi][db] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -352,9 +341,7 @@ __global__ __launch_bounds__(256, 2) void sparse_layer_kernel(const AttnArgs a) 
       bf16x8 pf[2][2];
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
-#if !SL_SOFTMAX_BOTH
         if (!ACT[gi]) continue;
-#endif
         if (emask[gi]) {
           const unsigned span = (unsigned)(hi[gi] - lo[gi]);
 #pragma unroll
@@ -395,8 +382,7 @@ __global__ __launch_bounds__(256, 2) void sparse_layer_kernel(const AttnArgs a) 
           pk4[kb4] = (s[gi][kb4][0] + s[gi][kb4][1]) + (s[gi][kb4][2] + s[gi][kb4][3]);
         }
         const float ps = (pk4[0] + pk4[1]) + (pk4[2] + pk4[3]);
-        // (an inactive group's S was not computed: its sum is not taken)
-        l_run[gi] = ACT[gi] ? fmaf(l_run[gi], alpha, ps) : l_run[gi];
+        l_run[gi] = fmaf(l_run[gi], alpha, ps);
         // PV k-step ks: k = 8lg + j <-> key 16(2ks + j/4) + 4lg + j%4
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -480,10 +466,6 @@ __global__ __launch_bounds__(256, 2) void sparse_layer_kernel(const AttnArgs a) 
         if (a.o_f32) {
           sp = *(const f32x4*)((const float*)a.o + ro + d);
         } else {
-          if (!SL_PARK_REGS) {
-            const uint2 pk = *(const uint2*)((const uint16_t*)a.o + ro + d);
-            osp[gi][db][0] = pk.x; osp[gi][db][1] = pk.y;
-          }
           sp[0] = bf16_to_f32((uint16_t)(osp[gi][db][0] & 0xffffu));
           sp[1] = bf16_to_f32((uint16_t)(osp[gi][db][0] >> 16));
           sp[2] = bf16_to_f32((uint16_t)(osp[gi][db][1] & 0xffffu));
