@@ -8,11 +8,12 @@
 //
 //   decode_kernel<full>   - split-K: each workgroup takes a contiguous share
 //                           of the 64-key tiles.  Two staging waves load fp8
-//                           tiles several ahead and write them, as bf16 (K
-//                           row-major, V transposed), into a two-stage LDS
-//                           ring; two compute waves (32 query heads each, the
-//                           MFMA N dimension) take S^T = K q^T and O^T = V^T
-//                           P^T from it with an online softmax.  The per-key
+//                           tiles several ahead and write them, as bf16 rows
+//                           (K and V row-major), into a two-stage LDS ring;
+//                           two compute waves (32 query heads each, the MFMA
+//                           N dimension) take S^T = K q^T and O^T = V^T P^T
+//                           from it with an online softmax, the V^T fragments
+//                           by transposing LDS reads.  The per-key
 //                           max over heads is the token score, written
 //                           directly; each compute wave leaves one (m, l, O)
 //                           partial per head.
@@ -33,27 +34,37 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
   // [32w, 32w+32) (one MFMA N-block) and both consume the same staged 64-key
   // tile, so every cache byte is read once per workgroup.  The other two
   // stage: they keep the loads of the next NSET tiles in flight in their own
-  // registers and write each tile, converted to bf16 (K row-major, V
-  // transposed), into a two-stage LDS ring one tile ahead of the compute
-  // waves, so these wait on LDS only, never on memory latency.  One barrier
-  // per tile.
+  // registers and write each tile, converted to bf16 rows, into a two-stage
+  // LDS ring one tile ahead of the compute waves, so these wait on LDS only,
+  // never on memory latency.  One barrier per tile.
+  //
+  // LDS: K rows padded to KROW (read as MFMA A fragments, ds_read_b128); V
+  // rows unpadded with the 16-byte chunks of key row r stored at chunk
+  // c ^ vswz(r), read as V^T fragments by ds_read_b64_tr_b16 (within each
+  // 16-lane slice, lane i receives element i of the four 4-element rows the
+  // slice addresses: four consecutive keys of one d); the swizzle keeps
+  // those reads free of bank conflicts.
   constexpr int KROW = D + 8;                 // bf16 LDS row stride of K
-  constexpr int VROW = 68;                    // bf16 LDS row stride of V^T
   constexpr int NDB = D / 32;
   constexpr int NQC = D / 16;
   constexpr int NST = 128;                    // staging threads
   constexpr int KU = 64 * (D / 8) / NST;      // K units (8 elements) per staging thread
-  constexpr int VU = (16 * (D / 8) + NST - 1) / NST;   // V units (4 keys x 8 d) per staging thread
+  constexpr int VU = KU;                      // V units (8 elements of one key) per staging thread
   constexpr int NSET = sizeof(KT) == 1 ? 3 : 1;   // tiles of loads in flight
   constexpr int TLMAX = 2048;
 
   __shared__ __attribute__((aligned(16))) uint16_t Kl[2][64 * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vl[2][D * VROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Vl[2][64 * D];
   __shared__ __attribute__((aligned(16))) float red[2][2][64];
   __shared__ int s_tlist[SPARSE ? TLMAX : 1];
   __shared__ int s_misc[4];
 
   __shared__ int s_simd[4];
+  // V row r: chunk c at c ^ vswz(r) (chosen by enumeration to keep the
+  // transposing reads below free of conflicts on 32- and 64-bank LDS)
+  auto vswz = [](int r) __attribute__((always_inline)) -> int {
+    return D == 128 ? (5 * (r & 3)) & 15 : 2 * (r & 3);
+  };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5, ln = lane & 31;
   const int bid = blockIdx.x;
   // Roles follow the SIMD a wave runs on.  The four waves of a workgroup sit
@@ -115,19 +126,18 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
   };
 
   // ---- staging (roles 2, 3) ----------------------------------------------------
-  // staging thread x, K unit u: key u*(NST/(D/8)) + x/(D/8), 8 elements from
-  // x%(D/8)*8; V unit u: keys 4(x%16) .. 4(x%16)+3, 8 elements from
-  // (u*NST/16 + x/16)*8
+  // staging thread x, K or V unit u: key u*(NST/(D/8)) + x/(D/8), 8 elements
+  // from x%(D/8)*8
   const KT* kb = (const KT*)a.k + (int64_t)b * a.k_sb;
   const KT* vb = (const KT*)a.v + (int64_t)b * a.v_sb;
   Raw8<KT> kreg[NSET][KU];
-  Raw8<KT> vreg[NSET][VU][4];
+  Raw8<KT> vreg[NSET][VU];
   uint32_t kmask[NSET], vmask[NSET];
   bool sfull[NSET];
   const int koff0 = (st / (D / 8)) * (int)a.k_st + (st % (D / 8)) * 8;
   const int kstep = (NST / (D / 8)) * (int)a.k_st;
-  const int voff0 = ((st % 16) * 4) * (int)a.v_st + (st / 16) * 8;
-  constexpr int VUN = 16 * (D / 8);
+  const int voff0 = (st / (D / 8)) * (int)a.v_st + (st % (D / 8)) * 8;
+  const int vstep = (NST / (D / 8)) * (int)a.v_st;
 
   auto stage_load = [&](auto set_tag, int t) __attribute__((always_inline)) {
     constexpr int S = decltype(set_tag)::value;
@@ -139,11 +149,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
 #pragma unroll
       for (int u = 0; u < KU; ++u) kreg[S][u] = load8<KT>(kt + koff0 + u * kstep);
 #pragma unroll
-      for (int u = 0; u < VU; ++u)
-        if (VUN % NST == 0 || u * NST + st < VUN) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) vreg[S][u][r] = load8<KT>(vt + voff0 + r * (int)a.v_st + u * (NST / 16) * 8);
-        }
+      for (int u = 0; u < VU; ++u) vreg[S][u] = load8<KT>(vt + voff0 + u * vstep);
       return;
     }
     // loads are unconditional from a clamped in-bounds key (key 0); empty
@@ -160,14 +166,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
       const int unit = u * NST + st;
-      if (VUN % NST != 0 && unit >= VUN) continue;
-      const int kg = unit % 16, dc = unit / 16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = keyof(t, kg * 4 + r);
-        vm |= (j >= 0 ? 1u : 0u) << (4 * u + r);
-        vreg[S][u][r] = load8<KT>(vb + (int64_t)(j >= 0 ? j : 0) * a.v_st + dc * 8);
-      }
+      const int key = unit / (D / 8), c8 = unit % (D / 8);
+      const int j = keyof(t, key);
+      vm |= (j >= 0 ? 1u : 0u) << u;
+      vreg[S][u] = load8<KT>(vb + (int64_t)(j >= 0 ? j : 0) * a.v_st + c8 * 8);
     }
     kmask[S] = km; vmask[S] = vm;
   };
@@ -184,22 +186,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
       const int unit = u * NST + st;
-      if (VUN % NST != 0 && unit >= VUN) continue;
-      const int kg = unit % 16, dc = unit / 16;     // one write covers a V^T row's 16 key groups
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (!full) keep_if(vreg[S][u][r], (vmask[S] >> (4 * u + r)) & 1u);
-      const uint4 r0 = to_ct(vreg[S][u][0]).a, r1 = to_ct(vreg[S][u][1]).a, r2 = to_ct(vreg[S][u][2]).a,
-                  r3 = to_ct(vreg[S][u][3]).a;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t w0 = u4get(r0, p), w1 = u4get(r1, p), w2 = u4get(r2, p), w3 = u4get(r3, p);
-        uint2 e, o;
-        e.x = __builtin_amdgcn_perm(w1, w0, 0x05040100u); e.y = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
-        o.x = __builtin_amdgcn_perm(w1, w0, 0x07060302u); o.y = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
-        *(uint2*)&Vl[stage][(dc * 8 + 2 * p) * VROW + kg * 4] = e;
-        *(uint2*)&Vl[stage][(dc * 8 + 2 * p + 1) * VROW + kg * 4] = o;
-      }
+      const int key = unit / (D / 8), c8 = unit % (D / 8);
+      if (!full) keep_if(vreg[S][u], (vmask[S] >> u) & 1u);
+      *(uint4*)&Vl[stage][key * D + ((c8 ^ vswz(key)) * 8)] = to_ct(vreg[S][u]).a;
     }
   };
 
@@ -213,6 +202,15 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
     const uint4 x = *(const uint4*)(qb + (int64_t)(hvalid ? head : 0) * a.q_sh + 16 * c + 8 * hh);
     const uint4 z = {0u, 0u, 0u, 0u};
     qf[c] = as_bf16x8(hvalid ? x : z);
+  }
+
+  // the lane's V^T read offset in a stage (d block 0, k-step 0)
+  int vbase;
+  {
+    const int i = lane & 15, g = (lane >> 4) & 1;
+    const int r = 4 * hh + (i >> 2), sv = vswz(r);
+    const int x = 2 * g + ((i >> 1) & 1);            // chunk among the d block's four
+    vbase = r * (2 * D) + 64 * (sv >> 2) + 16 * (x ^ (sv & 3)) + 8 * (i & 1);
   }
 
   float m_run = kNegInf, l_run = 0.f;
@@ -258,11 +256,19 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
     }
     // V^T fragments (A operand of O^T): the first d block is read now, under
     // the softmax; later blocks one d block ahead of their MFMAs
+    // k-step kc of d block db, lane (slice g = lane/16, i = lane%16): keys
+    // 16kc + 4hh + (0..3) (lo) and 16kc + 8 + 4hh + (0..3) (hi) at
+    // d = 32db + 16(g%2) + i.  The slice addresses rows 4hh + i/4 (+16kc, +8)
+    // at d = 32db + 16(g%2) + 4(i%4); vswz only flips the d-block bits and
+    // those below, so the swizzled offset is the lane's base XOR 64db.
     auto vfrag = [&](int db, int kc) __attribute__((always_inline)) {
-      const uint16_t* vr = &Vc[(db * 32 + ln) * VROW + 16 * kc + 4 * hh];
-      const uint2 lo = *(const uint2*)vr;
-      const uint2 hi = *(const uint2*)(vr + 8);
-      uint4 va; va.x = lo.x; va.y = lo.y; va.z = hi.x; va.w = hi.y;
+      typedef short v4i16 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+      const char* vr = (const char*)Vc + (vbase ^ (64 * db)) + (16 * kc) * (2 * D);
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)vr);
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vr + 8 * (2 * D)));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      uint4 va; va.x = l2.x; va.y = l2.y; va.z = h2.x; va.w = h2.y;
       return va;
     };
     uint4 vf[2][4];
