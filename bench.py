@@ -39,22 +39,23 @@ from hybrid_sparse_attention_flash_amd.block import (HySparse2Block, HySparse2De
 METRIC = ("hybrid-block prefill tokens/s at 32k (TFLOP/s, GB/s % peak); decode us/token at 1M")
 
 # HBM traffic of the dominant kernel (the one-pass sparse layer), measured
-# with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE over
-#   python3 bench.py --calibrate-copy --steps 1 --warmup 0 --no-cpu --no-decode
-# and scaled by the counters' reading for a plain copy of known size (the
-# profiles directory holds both summaries).  It is reported only while the
-# kernel sources still hash to the value they had when the counters were taken.
-TRAFFIC_SOURCES = ("attn_engine.h", "common.h", "kernels.h", "attn_sparse_swa.hip")
-TRAFFIC = {"sources_sha1": "4c9e9478bc1341f155f1c294d752786d104ce3e7", "bytes_per_launch": 2.088e9}
+# with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (one counter per pass) over
+#   python3 bench.py --no-decode --no-bridge --no-hs-decode --no-bwd --no-cpu --no-peaks --calibrate-copy --steps 2 --warmup 1
+# and scaled by the counters' reading for a plain 512 MiB copy in the same run
+# (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000; the profiles directory holds the
+# summaries).  It is reported only while the kernel sources still hash to the
+# value they had when the counters were taken.
+TRAFFIC_SOURCES = ("sparse_layer.hip", "block_union.h", "common.h", "kernels.h")
+TRAFFIC = {"sources_sha1": "6cbabb0d636f57e8ad5ab591530347e506630ce3", "bytes_per_launch": 1.4653e9}
 # The same two passes for the KV Bridging kernel, over
 #   python3 bench.py --only-bridge --calibrate-copy --steps 1 --warmup 0
 BRIDGE_TRAFFIC_SOURCES = ("bridge.hip", "common.h", "kernels.h")
 BRIDGE_TRAFFIC = {"sources_sha1": "0f3200bd622013cb90b006dafe13a157af9fc552", "bytes_per_launch": 575.7e6}
-# The same two passes for the decode step (all kernels of one hys_decode_step
-# call, per step), over
-#   python3 bench.py --only-decode --calibrate-copy --steps 2 --warmup 1
+# The same two passes for the decode step (every kernel of one hys_decode_step
+# call, summed per step), over
+#   python3 bench.py --only-decode --no-peaks --calibrate-copy --steps 2 --warmup 1
 DECODE_TRAFFIC_SOURCES = ("decode.hip", "topk.hip", "common.h", "kernels.h", "abi.hip")
-DECODE_TRAFFIC = None
+DECODE_TRAFFIC = {"sources_sha1": "7c1df2552e1980550e0a6c4acfdc8ca952e62cd6", "bytes_per_step": 1.1792e9}
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
@@ -141,8 +142,12 @@ def per_step_times(step, steps, flush=None):
 
 
 def clock_state():
-    """The GPU's clock readings as the driver tool reports them (raw text)."""
+    """The GPU's clock readings as the driver tool reports them (raw text).
+    Skipped under rocprofv3: its library attaches every child process to the
+    GPU before the tool (a Python script) can start."""
     import subprocess
+    if os.environ.get("ROCPROF_OUTPUT_PATH"):
+        return None
     for cmd in (["amd-smi", "metric", "--clock"], ["rocm-smi", "--showclocks"]):
         try:
             r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
