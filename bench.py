@@ -50,7 +50,7 @@ TRAFFIC = {"sources_sha1": "6cbabb0d636f57e8ad5ab591530347e506630ce3", "bytes_pe
 # The same two passes for the KV Bridging kernel, over
 #   python3 bench.py --only-bridge --calibrate-copy --steps 1 --warmup 0
 BRIDGE_TRAFFIC_SOURCES = ("bridge.hip", "common.h", "kernels.h")
-BRIDGE_TRAFFIC = {"sources_sha1": "0f3200bd622013cb90b006dafe13a157af9fc552", "bytes_per_launch": 575.7e6}
+BRIDGE_TRAFFIC = {"sources_sha1": "98ee99fa300645a3ebc8bc55242f8bcd03e94e95", "bytes_per_launch": 575.7e6}
 # The same two passes for the decode step (every kernel of one hys_decode_step
 # call, summed per step), over
 #   python3 bench.py --only-decode --no-peaks --calibrate-copy --steps 2 --warmup 1

@@ -9,6 +9,16 @@ oracle gives for exact - bound and exact + bound (the encoding is monotonic),
 which forces bit equality wherever the exact value is not within the bound of
 an fp8 rounding midpoint.  amax must lie within the bound of the exact
 maximum.  Bytes of the cache outside the written region must be untouched.
+
+How many codes may differ at all.  A code can move only where its exact value
+lies within the bound of a midpoint (the "ambiguous" codes, counted per case
+from the oracle), and there only if the kernel's actual error carries it
+across.  That error is a random walk over the d/32 fp32 accumulations of the
+MFMA chain, 2^-24 sqrt(d/96) |x| in size, while the bound is
+2^-18 sum|h_c w_c| ~ 2^-18 0.64 d |h||w| and |x| ~ sqrt(d) |h||w|: the ratio
+is about 1/400 whatever d is, so about one ambiguous code in 800 flips (the
+measured rate on these cases is 0.7-0.9 per 1000).  The test allows one in
+200, and at least 8.
 Widths that are and are not multiples of three 64-column chunks exercise the
 zero-padded tail of the chunk loop.
 """
@@ -50,7 +60,13 @@ def _check_codes(gpu, ref, exact, bound, scale, what):
     bad = (gv < lo) | (gv > hi)
     assert not bad.any(), (f"{what}: {int(bad.sum())} codes outside the accumulation bound, first at "
                            f"{np.argwhere(bad)[:3].tolist()}: gpu {gpu[bad][:3].tolist()} oracle {ref[bad][:3].tolist()}")
-    return int((gpu != ref).sum())
+    return int((gpu != ref).sum()), int((lo != hi).sum())
+
+
+def _cap(ambiguous):
+    """Most codes that may differ from the oracle, given how many lie within
+    the accumulation bound of a rounding midpoint."""
+    return max(8, ambiguous // 200)
 
 
 def _run(h, wk, wv, Hkv, D, ks, vs, k_cache=None, v_cache=None, with_amax=True):
@@ -90,10 +106,9 @@ def test_kv_bridge_parity(B, L, d_model, Hkv, D):
     k_cache, v_cache, amax = _run(h, wk, wv, Hkv, D, ks, vs)
     g_k = k_cache.cpu().numpy().reshape(B, L, n)
     g_v = v_cache.cpu().numpy().reshape(B, L, n)
-    mk = _check_codes(g_k, kc, kx, kb, ks, "K")
-    mv = _check_codes(g_v, vc, vx, vb, vs, "V")
-    # a handful of midpoint neighbours at most
-    assert mk + mv <= max(4, (kc.size + vc.size) // 200), (mk, mv)
+    mk, ak_n = _check_codes(g_k, kc, kx, kb, ks, "K")
+    mv, av_n = _check_codes(g_v, vc, vx, vb, vs, "V")
+    assert mk + mv <= _cap(ak_n + av_n), (mk, mv, ak_n + av_n)
     am = amax.cpu().numpy()
     assert abs(am[0] - ak) <= kb.max() and abs(am[1] - av) <= vb.max(), (am.tolist(), ak, av)
 
@@ -120,8 +135,9 @@ def test_kv_bridge_saturation_and_strided_views(d_model):
     ops.hys_kv_bridge_fwd(hd, wk.cuda(), wv.cuda(), kfull[:, t0:t0 + L], vfull[:, t0:t0 + L], ks, vs, amax)
     torch.cuda.synchronize()
     kf, vf = kfull.cpu().numpy(), vfull.cpu().numpy()
-    _check_codes(kf[:, t0:t0 + L].reshape(B, L, -1), kc, kx, kb, ks, "K")
-    _check_codes(vf[:, t0:t0 + L].reshape(B, L, -1), vc, vx, vb, vs, "V")
+    mk, ak_n = _check_codes(kf[:, t0:t0 + L].reshape(B, L, -1), kc, kx, kb, ks, "K")
+    mv, av_n = _check_codes(vf[:, t0:t0 + L].reshape(B, L, -1), vc, vx, vb, vs, "V")
+    assert mk + mv <= _cap(ak_n + av_n), (mk, mv, ak_n + av_n)
     sat = np.isin(kf[:, t0:t0 + L], [0x7E, 0xFE]).mean()
     assert sat > 0.5, sat
     for arr in (kf, vf):
@@ -137,8 +153,9 @@ def test_kv_bridge_empty_and_no_amax():
     h, wk, wv = _inputs(1, 70, 64, 128, seed=3)
     kc, vc, kx, vx, _, _, kb, vb = _oracle(h, wk, wv, 0.02, 0.02)
     k_cache, v_cache, _ = _run(h, wk, wv, 1, 128, 0.02, 0.02, with_amax=False)
-    _check_codes(k_cache.cpu().numpy().reshape(1, 70, 128), kc, kx, kb, 0.02, "K")
-    _check_codes(v_cache.cpu().numpy().reshape(1, 70, 128), vc, vx, vb, 0.02, "V")
+    mk, ak_n = _check_codes(k_cache.cpu().numpy().reshape(1, 70, 128), kc, kx, kb, 0.02, "K")
+    mv, av_n = _check_codes(v_cache.cpu().numpy().reshape(1, 70, 128), vc, vx, vb, 0.02, "V")
+    assert mk + mv <= _cap(ak_n + av_n), (mk, mv, ak_n + av_n)
 
 
 def test_kv_bridge_full_size():
@@ -150,8 +167,8 @@ def test_kv_bridge_full_size():
     ks = vs = 8.0 / 448.0
     kc, vc, kx, vx, ak, av, kb, vb = _oracle(h, wk, wv, ks, vs)
     k_cache, v_cache, amax = _run(h, wk, wv, Hkv, D, ks, vs)
-    mk = _check_codes(k_cache.cpu().numpy().reshape(B, L, -1), kc, kx, kb, ks, "K")
-    mv = _check_codes(v_cache.cpu().numpy().reshape(B, L, -1), vc, vx, vb, vs, "V")
-    assert mk + mv <= (kc.size + vc.size) // 200, (mk, mv)
+    mk, ak_n = _check_codes(k_cache.cpu().numpy().reshape(B, L, -1), kc, kx, kb, ks, "K")
+    mv, av_n = _check_codes(v_cache.cpu().numpy().reshape(B, L, -1), vc, vx, vb, vs, "V")
+    assert mk + mv <= _cap(ak_n + av_n), (mk, mv, ak_n + av_n)
     am = amax.cpu().numpy()
     assert abs(am[0] - ak) <= kb.max() and abs(am[1] - av) <= vb.max(), (am.tolist(), ak, av)
