@@ -350,7 +350,11 @@ hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
       e = hys::launch_tile_scores(a.scores, (int)B, a.ntq, a.BQ, (int)L, (int)Lk, a.q_off, a.sc_sb, a.sc_sr, 0, st);
       if (e != hipSuccess) return hip_status(e, "score clear launch");
     }
-    e = hys::launch_attn(mode, et(q.dtype), et(k.dtype), (int)D, a, grid, st);
+    if ((mode == hys::M_FULL || mode == hys::M_FULL_BLOCK) && et(q.dtype) == hys::ET_BF16 &&
+        et(k.dtype) == hys::ET_BF16 && hys::full_layer_supported((int)D, a, mode == hys::M_FULL_BLOCK))
+      e = hys::launch_full_layer((int)D, a, mode == hys::M_FULL_BLOCK, grid, st);
+    else
+      e = hys::launch_attn(mode, et(q.dtype), et(k.dtype), (int)D, a, grid, st);
     if (e != hipSuccess) return hip_status(e, "full attention launch");
     if (mode == hys::M_FULL_TILE) {
       e = hys::launch_tile_scores(a.scores, (int)B, a.ntq, a.BQ, (int)L, (int)Lk, a.q_off, a.sc_sb, a.sc_sr, 1, st);

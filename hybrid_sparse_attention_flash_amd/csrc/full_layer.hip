@@ -1,0 +1,411 @@
+// The HySparse full layer for bf16 Q/K/V on gfx950: exact causal attention
+// that also emits the block scores the sparse layers select from.
+//
+// What it computes (QbitAI HySparse article, method section; TechWalker
+// HySparse write-up, paragraph on the modified FlashAttention kernel): for
+// every query row, softmax(q K^T * scale) V over the keys at or before its
+// position, its log-sum-exp, and, with scores on, for every 64-key block c the
+// maximum over the block's visible keys of the scaled logit, reduced over the
+// query heads of the row's KV group (blocks past the query's own hold -inf).
+// The tiled engine's M_FULL / M_FULL_BLOCK modes compute the same for fp32
+// and fp8 inputs and for head groups this kernel does not take.
+//
+// Design:
+//  * A workgroup (4 waves) owns BQ queries x the G heads of one KV group, row
+//    r = query r / G, head r % G; each wave owns 32 consecutive rows, the N of
+//    v_mfma_f32_32x32x16_bf16.  It walks the 64-key tiles 0 .. its last
+//    query's block.
+//  * Key tiles go HBM -> LDS with global_load_lds_dwordx4 (each lane fetches
+//    any 16 bytes; the 64 lanes of one instruction fill 1 KiB of LDS in lane
+//    order): no staging registers and no VALU work.  Two LDS buffers; the
+//    loads of tile n+1 are in flight while tile n is computed; one barrier a
+//    tile.
+//  * K and V sit in LDS row-major, [64 keys][D], the 16-byte chunks of each
+//    row XOR-swizzled so the fragment reads below are free of bank conflicts.
+//    S^T = K Q^T takes K fragments (A) with ds_read_b128 and Q (B) from
+//    registers; each lane then holds one row's logits for 32 of the 64 keys,
+//    so the row maximum needs one cross-lane exchange.  O^T = V^T P^T takes
+//    the V^T fragments (A) from row-major V with ds_read_b64_tr_b16 and P^T
+//    (B) straight from the logit registers.
+//  * Online softmax in the base-2 domain on raw dot products with a lazily
+//    moved reference (the engine's rule); the block score is the row's tile
+//    maximum, reduced over a query's heads between adjacent lanes.
+//
+// v_mfma_f32_32x32x16_bf16 lane layout (wave64, lane l = 32h + n): lane l holds
+// A[m = l%32][k = 8h + j], B[k = 8h + j][n = l%32] (j = 0..7) and
+// C[m = 8(i/4) + 4h + i%4][n = l%32] (i = 0..15).
+#include "common.h"
+#include "kernels.h"
+
+namespace hys {
+namespace {
+
+typedef short fl_v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void fl_lds_void;
+typedef __attribute__((address_space(3))) fl_v4i16 fl_lds_v4i16;
+
+template <int D> struct FGeo {
+  static constexpr int ROWB = 2 * D;            // bytes per key row
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int RPI = 1024 / ROWB;       // rows filled by one load instruction
+  static constexpr int NU = 64 / (4 * RPI);     // load instructions per wave, operand and tile
+  static constexpr int TILEB = 64 * ROWB;       // bytes of one operand tile
+  static constexpr int NQC = D / 16;            // k-steps of S^T
+  static constexpr int NDB = D / 32;            // 32-wide d blocks of O^T
+};
+
+// chunk c of key row r is stored at chunk c ^ swz(r).  K: the 32 rows one
+// ds_read_b128 addresses (one chunk each) fall in distinct banks on 32- and
+// 64-bank LDS.  V: the transposing reads' four-row slices likewise.  Both
+// depend on the row mod 32 only (rows ln and ln + 32 share a swizzle).
+template <int D> __device__ __forceinline__ int fswz_k(int r) { return D == 128 ? (r & 15) : ((r ^ ((r >> 3) & 3)) & 7); }
+template <int D> __device__ __forceinline__ int fswz_v(int r) { return D == 128 ? (5 * (r & 3)) & 15 : 2 * (r & 3); }
+
+// all LDS reads and writes of this wave, and this wave's LDS loads, are done;
+// then the workgroup barrier (a compiler barrier for memory as well)
+__device__ __forceinline__ void fl_tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int D, bool SCORES>
+__global__ __launch_bounds__(256, 2) void full_layer_kernel(const AttnArgs a) {
+  using P = FGeo<D>;
+  // two stages, each operand and stage its own array: every LDS access below
+  // names one of them statically (the tile loop is unrolled by two), which is
+  // what lets the compiler tell the loads into one stage from the reads of
+  // the other and keep the loads in flight across a whole tile
+  __shared__ __attribute__((aligned(1024))) unsigned char K0[P::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char K1[P::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char V0[P::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char V1[P::TILEB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, ln = lane & 31;
+  if ((int)blockIdx.x >= a.grid_used) return;
+
+  // ---- work item: KV group fastest (the 8 XCDs take the workgroups round
+  // robin, so each XCD's L2 serves few KV heads), longest query tiles first --
+  const int g = (int)blockIdx.x % a.Hkv;
+  const int rest = (int)blockIdx.x / a.Hkv;
+  const int b = rest % a.B;
+  const int qt = a.ntq - 1 - rest / a.B;
+  const int q0 = qt * a.BQ;
+  const int nq = min(a.BQ, a.Lq - q0);
+  const int HC = a.HC;
+  // absolute position of the last query (row r of the call is q_off + r)
+  const int qa_last = q0 + nq - 1 + a.q_off;
+
+  // ---- this lane's row ---------------------------------------------------------
+  const int r = wave * 32 + ln;
+  const int qi = r / HC;
+  const int qpos = q0 + qi;
+  const int head = g * a.G + (r - qi * HC);
+  const bool valid = qi < nq;
+  const int qa = qpos + a.q_off;
+
+  // ---- Q fragments (B of S^T): q[row][16c + 8hh .. +7] ----------------------
+  const uint16_t* qbase = (const uint16_t*)a.q + (int64_t)b * a.q_sb;
+  bf16x8 qf[P::NQC];
+  {
+    const uint16_t* qr = qbase + (valid ? (int64_t)qpos * a.q_st + (int64_t)head * a.q_sh : 0);
+#pragma unroll
+    for (int c = 0; c < P::NQC; ++c) {
+      const uint4 x = *(const uint4*)(qr + 16 * c + 8 * hh);
+      const uint4 z = {0u, 0u, 0u, 0u};
+      qf[c] = as_bf16x8(valid ? x : z);
+    }
+  }
+
+  // ---- tiles 0 .. the last query's block ---------------------------------------
+  const int ntiles = qa_last / 64 + 1;
+  const int jlast = a.Lk - 1;
+  const uint16_t* kb = (const uint16_t*)a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh;
+  const uint16_t* vb = (const uint16_t*)a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh;
+  // instruction u of this wave fills tile rows (4u + wave) * RPI + (0..RPI-1);
+  // the swizzles depend on the row mod 4 * RPI (16 rows for D = 128, 32 for
+  // D = 64), so the chunk a lane fetches is the same for every u: one lane
+  // offset from a tile's first row, the rest of each address scalar
+  const int drow0 = wave * P::RPI + lane / P::CPR;
+  const uint32_t kstb = (uint32_t)a.k_st * 2u, vstb = (uint32_t)a.v_st * 2u;
+  const uint32_t chunk_k = (uint32_t)(((lane % P::CPR) ^ fswz_k<D>(drow0)) * 16);
+  const uint32_t chunk_v = (uint32_t)(((lane % P::CPR) ^ fswz_v<D>(drow0)) * 16);
+  const uint32_t lane_k = (uint32_t)drow0 * kstb + chunk_k;
+  const uint32_t lane_v = (uint32_t)drow0 * vstb + chunk_v;
+  // (64 rows of K or V span less than 2^32 bytes: checked at launch)
+  auto load_tile = [&](int j0, unsigned char* Kd, unsigned char* Vd, uint32_t lk, uint32_t lv, const uint16_t* Kg,
+                       const uint16_t* Vg) __attribute__((always_inline)) {
+    const char* kt = (const char*)Kg + (int64_t)j0 * a.k_st * 2;
+    const char* vt = (const char*)Vg + (int64_t)j0 * a.v_st * 2;
+    if (j0 + 63 <= jlast) {
+      // scalar row base per instruction + the lane's fixed offset: the two
+      // offset registers stay live through the loop, so no LDS read result is
+      // ever given a register an in-flight load still names
+#pragma unroll
+      for (int u = 0; u < P::NU; ++u) {
+        const char* ktu = kt + (int64_t)(4 * P::RPI * u) * a.k_st * 2;
+        const char* vtu = vt + (int64_t)(4 * P::RPI * u) * a.v_st * 2;
+        __builtin_amdgcn_global_load_lds((const void*)(ktu + lk), (fl_lds_void*)(Kd + (4 * u + wave) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vtu + lv), (fl_lds_void*)(Vd + (4 * u + wave) * 1024), 16, 0, 0);
+      }
+    } else {
+      // last tile of the keys: slots past the last key repeat the last key's
+      // row (their logits are masked, so their probabilities are exactly 0)
+      const int rmax = jlast - j0;
+#pragma unroll
+      for (int u = 0; u < P::NU; ++u) {
+        const uint32_t rr = (uint32_t)min(drow0 + 4 * P::RPI * u, rmax);
+        __builtin_amdgcn_global_load_lds((const void*)(kt + (rr * kstb + chunk_k)), (fl_lds_void*)(Kd + (4 * u + wave) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vt + (rr * vstb + chunk_v)), (fl_lds_void*)(Vd + (4 * u + wave) * 1024), 16, 0, 0);
+      }
+    }
+  };
+
+  // per-lane LDS byte offsets inside a tile.  K, k-step c, key ln (+32):
+  // row ln, chunk 2c + hh, stored at (2c + hh) ^ swz_k(ln); the swizzle only
+  // flips chunk bits, so step c is the base XOR 32c.  V^T, d block db, k-step
+  // kc: the lane's 16-lane slice (i = lane % 16, slice bit s = (lane / 16) % 2)
+  // addresses rows 4hh + i/4 (+16kc, +8) at d = 32db + 16s + 4(i%4); the
+  // swizzle flips only the d-block bits and those below, so block db is the
+  // base XOR 64db.
+  const int kbase_off = ln * P::ROWB + ((hh ^ fswz_k<D>(ln)) * 16);
+  int vbase_off;
+  {
+    const int i = lane & 15, s = (lane >> 4) & 1;
+    const int vr = 4 * hh + (i >> 2), sv = fswz_v<D>(vr);
+    const int x = 2 * s + ((i >> 1) & 1);            // chunk among the d block's four
+    vbase_off = vr * P::ROWB + 64 * (sv >> 2) + 16 * (x ^ (sv & 3)) + 8 * (i & 1);
+  }
+
+  // ---- softmax state -------------------------------------------------------
+  const float c2 = a.scale_log2;
+  const float lazy_raw = kLazyLog2 / c2;
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16 acc[P::NDB];
+#pragma unroll
+  for (int db = 0; db < P::NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  // block scores of this lane's query: a scalar base and a 32-bit lane offset
+  // (a KV group's score matrix spans less than 2^32 entries: checked at launch)
+  float* sc_base = nullptr;
+  if (SCORES) sc_base = a.scores + (int64_t)g * a.sc_sg + (int64_t)b * a.sc_sb;
+  const uint32_t sc_off = valid ? (uint32_t)qpos * (uint32_t)a.sc_sr : 0u;
+  const bool sc_lane = SCORES && valid && hh == 0 && (ln % HC) == 0;
+
+  // ---- one tile ---------------------------------------------------------------
+  // Kc/Vc: the tile being computed; Kn/Vn: the stage the next tile is loaded
+  // into; Kg/Vg: the K and V rows in global memory.  The loads of the next
+  // tile stay in flight across the whole tile; the barrier at its end waits
+  // for them.
+  auto step = [&](int n, const unsigned char* __restrict__ Kc, const unsigned char* __restrict__ Vc,
+                  unsigned char* __restrict__ Kn, unsigned char* __restrict__ Vn, const uint16_t* __restrict__ Kg,
+                  const uint16_t* __restrict__ Vg) __attribute__((always_inline)) {
+    // the per-step fragment offsets are a few XORs of these bases;
+    // recomputing them each tile keeps them out of the register budget the
+    // loop would otherwise hold them in
+    int kbo = kbase_off, vbo = vbase_off;
+    asm volatile("" : "+v"(kbo), "+v"(vbo));
+    if (n + 1 < ntiles) load_tile(64 * (n + 1), Kn, Vn, lane_k, lane_v, Kg, Vg);
+    const int j0 = 64 * n;
+    // (a wave none of whose rows sees this tile, possible only in the last
+    // tile when the rows start mid-block, runs it anyway: every row is off,
+    // so it adds nothing and its block scores come out -inf)
+    {
+      // S^T = K Q^T (M = 64 keys as two 32-blocks, N = rows, K = D); the K
+      // fragments are read two k-steps ahead of their MFMAs
+      f32x16 s[2];
+      const f32x16 zero16 = {};
+      uint4 kf[P::NQC][2];
+      auto kfrag = [&](int c) __attribute__((always_inline)) {
+        kf[c][0] = *(const uint4*)(Kc + (kbo ^ (32 * c)));
+        kf[c][1] = *(const uint4*)(Kc + (kbo ^ (32 * c)) + 32 * P::ROWB);
+      };
+      kfrag(0);
+      kfrag(1);
+#pragma unroll
+      for (int c = 0; c < P::NQC; ++c) {
+        if (c + 2 < P::NQC) kfrag(c + 2);
+        // keep the reads ahead: the scheduler would otherwise sink each read
+        // next to its MFMA and expose the LDS latency per step
+        __builtin_amdgcn_sched_barrier(0);
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[c][0]), qf[c], c == 0 ? zero16 : s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[c][1]), qf[c], c == 0 ? zero16 : s[1], 0, 0, 0);
+      }
+      // V^T fragments of k-step kc, d block db: keys 16kc + 4hh + (0..3) (lo)
+      // and 16kc + 8 + 4hh + (0..3) (hi) at d = 32db + ln
+      auto vfrag = [&](int db, int kc) __attribute__((always_inline)) {
+        const unsigned char* vr = Vc + (vbo ^ (64 * db)) + (16 * kc) * P::ROWB;
+        const fl_v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((fl_lds_v4i16*)vr);
+        const fl_v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((fl_lds_v4i16*)(vr + 8 * P::ROWB));
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        return make_uint4(l2.x, l2.y, h2.x, h2.y);
+      };
+      // the first d block's reads hide under the softmax
+      uint4 vf[2][4];
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) vf[0][kc] = vfrag(0, kc);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // causal mask, only where some row of the wave sees part of the tile.
+      // Register 16mb + i of lane (ln, hh) holds key j0 + 32mb + 8(i/4) + 4hh + i%4.
+      const bool row_on = valid && j0 <= qa;
+      const bool part = row_on && j0 + 63 > qa;
+      if (__ballot(part) != 0ull) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = j0 + 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
+            s[mb][i] = (row_on & (key <= qa)) ? s[mb][i] : kNegInf;
+          }
+      }
+      // row maximum over the tile (three-input maxima; no NaN quieting)
+      float mt;
+      {
+        float m8[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+          m8[x] = fmax_nc(fmax_nc(s[x >> 2][4 * (x & 3)], s[x >> 2][4 * (x & 3) + 1]),
+                          fmax_nc(s[x >> 2][4 * (x & 3) + 2], s[x >> 2][4 * (x & 3) + 3]));
+        mt = fmax_nc(fmax_nc(fmax_nc(m8[0], m8[1]), fmax_nc(m8[2], m8[3])),
+                     fmax_nc(fmax_nc(m8[4], m8[5]), fmax_nc(m8[6], m8[7])));
+      }
+      mt = xor32_max(mt);
+      if (!row_on) mt = kNegInf;
+      if (SCORES) {
+        // the query's heads are HC adjacent lanes: reduce them and let the
+        // group's first lane store the block score
+        // (HC is 1, 2, 4, 8, 16 or 32; wave-uniform branches)
+        float gm = mt;
+        if (HC >= 2)
+          gm = fmaxf(gm, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, gm), 0xB1, 0xF, 0xF, false)));
+        if (HC >= 4)
+          gm = fmaxf(gm, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, gm), 0x4E, 0xF, 0xF, false)));
+        if (HC >= 8)
+          gm = fmaxf(gm, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, gm), 0x141, 0xF, 0xF, false)));
+        if (HC >= 16)
+          gm = fmaxf(gm, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, gm), 0x140, 0xF, 0xF, false)));
+        if (HC >= 32) gm = xor16_max(gm);
+        if (sc_lane) sc_base[sc_off + n] = gm * a.logit_scale;
+      }
+      // lazily moved reference: O and l are rescaled only in the rare tiles
+      // where some row's maximum exceeds it by more than the slack
+      const bool need = mt > m_run + lazy_raw;
+      float alpha = 1.f;
+      if (__ballot(need) != 0ull) {
+        const float mref = need ? mt : m_run;
+        alpha = need ? __builtin_amdgcn_exp2f((m_run - mref) * c2) : 1.f;
+        m_run = mref;
+#pragma unroll
+        for (int db = 0; db < P::NDB; ++db) acc[db] *= alpha;
+      }
+      // rows that see nothing of this tile get probability 0 everywhere
+      const float mc = !row_on ? __builtin_huge_valf() : ((m_run == kNegInf) ? 0.f : m_run * c2);
+      float ps8[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int mb = x >> 2, i0 = 4 * (x & 3);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[mb][i0 + e] = __builtin_amdgcn_exp2f(fmaf(s[mb][i0 + e], c2, -mc));
+        ps8[x] = (s[mb][i0] + s[mb][i0 + 1]) + (s[mb][i0 + 2] + s[mb][i0 + 3]);
+      }
+      const float ps = ((ps8[0] + ps8[1]) + (ps8[2] + ps8[3])) + ((ps8[4] + ps8[5]) + (ps8[6] + ps8[7]));
+      l_run = fmaf(l_run, alpha, ps);
+
+      // O^T += V^T P^T; P^T k-step kc holds keys 16kc + {0, 8} + 4hh + (0..3)
+      bf16x8 pf[4];
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const int mb = kc >> 1, i0 = 8 * (kc & 1);
+        uint4 pk;
+        pk.x = pack_bf16x2(s[mb][i0 + 0], s[mb][i0 + 1]);
+        pk.y = pack_bf16x2(s[mb][i0 + 2], s[mb][i0 + 3]);
+        pk.z = pack_bf16x2(s[mb][i0 + 4], s[mb][i0 + 5]);
+        pk.w = pack_bf16x2(s[mb][i0 + 6], s[mb][i0 + 7]);
+        pf[kc] = as_bf16x8(pk);
+      }
+#pragma unroll
+      for (int db = 0; db < P::NDB; ++db) {
+        if (db + 1 < P::NDB) {
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) vf[(db + 1) & 1][kc] = vfrag(db + 1, kc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[db & 1][kc]), pf[kc], acc[db], 0, 0, 0);
+      }
+    }
+    fl_tile_barrier();
+  };
+
+  load_tile(0, K0, V0, lane_k, lane_v, kb, vb);
+  fl_tile_barrier();
+  for (int n = 0; n < ntiles; n += 2) {
+    step(n, K0, V0, K1, V1, kb, vb);
+    if (n + 1 < ntiles) step(n + 1, K1, V1, K0, V0, kb, vb);
+  }
+
+  // -inf for the blocks after each query's own
+  if (SCORES) {
+    float* sc = a.scores + (int64_t)g * a.sc_sg + (int64_t)b * a.sc_sb;
+    const int ncol = a.nblk - ntiles;
+    if (ncol > 0)
+      for (int e = tid; e < nq * ncol; e += 256) {
+        const int t = e / ncol, c = ntiles + (e - t * ncol);
+        sc[(int64_t)(q0 + t) * a.sc_sr + c] = kNegInf;
+      }
+  }
+
+  // ---- epilogue ----------------------------------------------------------------
+  const float lsum = l_run + __shfl_xor(l_run, 32);
+  const bool live = m_run != kNegInf;
+  if (!valid) return;
+  const float inv = live ? a.v_scale / lsum : 0.f;
+  if (a.lse && hh == 0)
+    a.lse[((int64_t)b * a.Hq + head) * a.Lq + qpos] = live ? (m_run * a.logit_scale + __logf(lsum)) : kNegInf;
+  const int64_t ro = (int64_t)b * a.o_sb + (int64_t)qpos * a.o_st + (int64_t)head * a.o_sh;
+#pragma unroll
+  for (int db = 0; db < P::NDB; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = db * 32 + 8 * i4 + 4 * hh;
+      const float r0 = acc[db][4 * i4] * inv, r1 = acc[db][4 * i4 + 1] * inv;
+      const float r2 = acc[db][4 * i4 + 2] * inv, r3 = acc[db][4 * i4 + 3] * inv;
+      if (a.o_f32) {
+        *(float4*)((float*)a.o + ro + d) = make_float4(r0, r1, r2, r3);
+      } else {
+        *(uint2*)((uint16_t*)a.o + ro + d) = make_uint2(pack_bf16x2(r0, r1), pack_bf16x2(r2, r3));
+      }
+    }
+}
+
+}  // namespace
+
+bool full_layer_supported(int D, const AttnArgs& a, bool scores) {
+  if (D != 64 && D != 128) return false;
+  if (a.HC != a.G || a.nhc != 1 || a.BQ * a.HC > 128 || a.BQ < 1) return false;
+  // block scores reduce a query's heads between adjacent lanes of one wave,
+  // and a lane addresses its query's scores with a 32-bit offset
+  if (scores && (a.HC > 32 || 32 % a.HC != 0)) return false;
+  if (scores && (int64_t)a.Lq * a.sc_sr >= (1ll << 32)) return false;
+  // 64 rows of K or V are addressed with 32-bit offsets
+  if (64 * a.k_st >= (1ll << 31) || 64 * a.v_st >= (1ll << 31)) return false;
+  return true;
+}
+
+hipError_t launch_full_layer(int D, const AttnArgs& a, bool scores, int grid, hipStream_t s) {
+  if (!full_layer_supported(D, a, scores)) return hipErrorInvalidValue;
+  if (D == 64) {
+    if (scores) hipLaunchKernelGGL((full_layer_kernel<64, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((full_layer_kernel<64, false>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (scores) hipLaunchKernelGGL((full_layer_kernel<128, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((full_layer_kernel<128, false>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hys

@@ -59,6 +59,11 @@ hipError_t launch_attn(int mode, int qt, int kt, int D, const AttnArgs& a, int g
 // or bf16 output; needs HC == G, BQ * topk <= 512, nblk <= 16384, D 64 or 128.
 hipError_t launch_sparse_layer(int D, const AttnArgs& a, int grid, hipStream_t s);
 
+// The full layer (M_FULL, or M_FULL_BLOCK with scores) for bf16 q/k/v, fp32
+// or bf16 output: D 64 or 128, HC == G, and with scores 32 % G == 0.
+bool full_layer_supported(int D, const AttnArgs& a, bool scores);
+hipError_t launch_full_layer(int D, const AttnArgs& a, bool scores, int grid, hipStream_t s);
+
 // M_FULL_TILE score rows [B, ntq, Lk] (row stride sr, batch stride sb):
 // decode = 0 clears them to atomic-max keys, decode = 1 turns keys into fp32
 hipError_t launch_tile_scores(float* sc, int B, int ntq, int BQ, int Lq, int Lk, int q_off, int64_t sb, int64_t sr,

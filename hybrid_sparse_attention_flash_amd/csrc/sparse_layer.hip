@@ -47,9 +47,6 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// source of the tile slots that hold no key
-__device__ __attribute__((aligned(16))) uint32_t g_zero16[4];
-
 template <int D> struct Geo {
   static constexpr int ROWB = 2 * D;            // bytes per key row
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
@@ -81,8 +78,14 @@ __global__ __launch_bounds__(256, 2) void sparse_layer_kernel(const AttnArgs a) 
   using P = Geo<D>;
   constexpr int UMAX = 512;      // union entries: BQ * topk <= 512 (host-checked)
   constexpr int NBWMAX = 512;    // bitmap words: nblk <= 16384 (host-checked)
-  __shared__ __attribute__((aligned(1024))) unsigned char Ks[2 * P::TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char Vs[2 * P::TILEB];
+  // two stages, each operand and stage its own array: every LDS access names
+  // one of them statically (the tile loops are unrolled by two), which is what
+  // lets the compiler tell the loads into one stage from the reads of the
+  // other and keep the loads in flight across a whole tile
+  __shared__ __attribute__((aligned(1024))) unsigned char K0[P::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char K1[P::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char V0[P::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char V1[P::TILEB];
   __shared__ uint32_t s_bitmap[NBWMAX];
   __shared__ int s_wpre[NBWMAX];
   __shared__ int s_ulist[UMAX];
@@ -158,18 +161,13 @@ __global__ __launch_bounds__(256, 2) void sparse_layer_kernel(const AttnArgs a) 
   // a swizzle depends on the row mod 16, and 4 * RPI is a multiple of 16, so
   // the chunk a lane fetches is the same for every u.  The lane's byte offset
   // from a tile's first key row is fixed; the rest of an address is scalar.
+  // (64 rows of K or V span less than 2^32 bytes: checked by the host.)
   const int drow0 = wave * P::RPI + lane / P::CPR;
-  const int64_t kstb = a.k_st * 2, vstb = a.v_st * 2;
-  const int64_t lane_k = (int64_t)drow0 * kstb + ((lane % P::CPR) ^ swz_k<D>(drow0)) * 16;
-  const int64_t lane_v = (int64_t)drow0 * vstb + ((lane % P::CPR) ^ swz_v<D>(drow0)) * 16;
-  // a tile's 64 rows span less than 2^31 bytes: 32-bit lane offsets from a scalar base
-  const bool off32 = kstb < (1ll << 25) && vstb < (1ll << 25);
-  const char* zero_src;
-  {
-    const uint64_t z = (uint64_t)(uintptr_t)g_zero16;
-    zero_src = (const char*)(uintptr_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(z >> 32)) << 32) |
-                                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)z));
-  }
+  const uint32_t kstb = (uint32_t)a.k_st * 2u, vstb = (uint32_t)a.v_st * 2u;
+  const uint32_t chunk_k = (uint32_t)(((lane % P::CPR) ^ swz_k<D>(drow0)) * 16);
+  const uint32_t chunk_v = (uint32_t)(((lane % P::CPR) ^ swz_v<D>(drow0)) * 16);
+  const uint32_t lane_k = (uint32_t)drow0 * kstb + chunk_k;
+  const uint32_t lane_v = (uint32_t)drow0 * vstb + chunk_v;
   // first key of tile n (scalar)
   auto tile_first = [&](int n) __attribute__((always_inline)) -> int {
     return n >= nsp ? wstart + (n - nsp) * 64 : __builtin_amdgcn_readfirstlane(s_ulist[n]) * 64;
@@ -177,26 +175,27 @@ __global__ __launch_bounds__(256, 2) void sparse_layer_kernel(const AttnArgs a) 
   auto load_tile = [&](int n, int j0, unsigned char* Kd, unsigned char* Vd) __attribute__((always_inline)) {
     const bool own = n >= nsp;
     const int jlast = own ? wend : a.Lk - 1;
-    const char* kt = (const char*)(own ? kwb : kb) + (int64_t)j0 * kstb;
-    const char* vt = (const char*)(own ? vwb : vb) + (int64_t)j0 * vstb;
-    if (j0 + 63 <= jlast && off32) {
-      // whole tile: scalar row base + 32-bit lane offset (the saddr form)
+    const char* kt = (const char*)(own ? kwb : kb) + (int64_t)j0 * a.k_st * 2;
+    const char* vt = (const char*)(own ? vwb : vb) + (int64_t)j0 * a.v_st * 2;
+    if (j0 + 63 <= jlast) {
+      // whole tile: a scalar base per instruction + the lane's fixed offset
+      // (the saddr form; the two offset registers stay live through the loops)
 #pragma unroll
       for (int u = 0; u < P::NU; ++u) {
-        const uint32_t ok_ = (uint32_t)lane_k + (uint32_t)(4 * P::RPI * u) * (uint32_t)kstb;
-        const uint32_t ov_ = (uint32_t)lane_v + (uint32_t)(4 * P::RPI * u) * (uint32_t)vstb;
-        __builtin_amdgcn_global_load_lds((const void*)(kt + ok_), (lds_void*)(Kd + (4 * u + wave) * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vt + ov_), (lds_void*)(Vd + (4 * u + wave) * 1024), 16, 0, 0);
+        const char* ktu = kt + (int64_t)(4 * P::RPI * u) * a.k_st * 2;
+        const char* vtu = vt + (int64_t)(4 * P::RPI * u) * a.v_st * 2;
+        __builtin_amdgcn_global_load_lds((const void*)(ktu + lane_k), (lds_void*)(Kd + (4 * u + wave) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vtu + lane_v), (lds_void*)(Vd + (4 * u + wave) * 1024), 16, 0, 0);
       }
     } else {
-      // partial tile: slots past the last key read 16 zero bytes
+      // partial tile: slots past the last key repeat the last key's row
+      // (their logits are masked, so their probabilities are exactly 0)
+      const int rmax = jlast - j0;
 #pragma unroll
       for (int u = 0; u < P::NU; ++u) {
-        const bool ok = j0 + drow0 + 4 * P::RPI * u <= jlast;
-        const char* sk = ok ? kt + (int64_t)(4 * P::RPI * u) * kstb + lane_k : zero_src;
-        const char* sv = ok ? vt + (int64_t)(4 * P::RPI * u) * vstb + lane_v : zero_src;
-        __builtin_amdgcn_global_load_lds((const void*)sk, (lds_void*)(Kd + (4 * u + wave) * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)sv, (lds_void*)(Vd + (4 * u + wave) * 1024), 16, 0, 0);
+        const uint32_t rr = (uint32_t)min(drow0 + 4 * P::RPI * u, rmax);
+        __builtin_amdgcn_global_load_lds((const void*)(kt + (rr * kstb + chunk_k)), (lds_void*)(Kd + (4 * u + wave) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vt + (rr * vstb + chunk_v)), (lds_void*)(Vd + (4 * u + wave) * 1024), 16, 0, 0);
       }
     }
   };
@@ -265,6 +264,10 @@ __global__ __launch_bounds__(256, 2) void sparse_layer_kernel(const AttnArgs a) 
   auto step = [&](auto own_tag, int n, const unsigned char* __restrict__ Kc, const unsigned char* __restrict__ Vc,
                   unsigned char* __restrict__ Kn, unsigned char* __restrict__ Vn) __attribute__((always_inline)) {
     constexpr bool own = decltype(own_tag)::value;
+    // the fragment offsets of the tile are XORs of these bases; recomputing
+    // them each tile keeps them out of the loops' register budget
+    int kbo = kbase_off, vbo = vbase_off;
+    asm volatile("" : "+v"(kbo), "+v"(vbo));
     const int j0 = tile_first(n);
     unsigned long long memb = 0ull;
     if (!own) {
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(256, 2) void sparse_layer_kernel(const AttnArgs a) 
       uint4 kf[2][4];
       auto kload = [&](int c, uint4(&dst)[4]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb4 = 0; kb4 < 4; ++kb4) dst[kb4] = *(const uint4*)(Kc + (kbase_off ^ (64 * c)) + kb4 * 16 * P::ROWB);
+        for (int kb4 = 0; kb4 < 4; ++kb4) dst[kb4] = *(const uint4*)(Kc + (kbo ^ (64 * c)) + kb4 * 16 * P::ROWB);
       };
       kload(0, kf[0]);
 #pragma unroll
@@ -325,9 +328,9 @@ __global__ __launch_bounds__(256, 2) void sparse_layer_kernel(const AttnArgs a) 
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const v4i16 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16*)(Vc + (vbase_off ^ (32 * db)) + (32 * ks) * P::ROWB));
+              (lds_v4i16*)(Vc + (vbo ^ (32 * db)) + (32 * ks) * P::ROWB));
           const v4i16 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16*)(Vc + (vbase_off ^ (32 * db)) + (32 * ks + 16) * P::ROWB));
+              (lds_v4i16*)(Vc + (vbo ^ (32 * db)) + (32 * ks + 16) * P::ROWB));
           const uint2 u0 = __builtin_bit_cast(uint2, t0), u1 = __builtin_bit_cast(uint2, t1);
           dst[ks] = as_bf16x8(make_uint4(u0.x, u0.y, u1.x, u1.y));
         }
@@ -415,18 +418,26 @@ __global__ __launch_bounds__(256, 2) void sparse_layer_kernel(const AttnArgs a) 
 
   // ---- tile loop ---------------------------------------------------------------
   // (two loops, so that the switch between the branches is not a branch inside one)
-  load_tile(0, tile_first(0), Ks, Vs);
+  load_tile(0, tile_first(0), K0, V0);
   tile_barrier();
-  for (int n = 0; n < nsp; ++n) {
-    const int cur = n & 1;
-    step(std::false_type{}, n, Ks + cur * P::TILEB, Vs + cur * P::TILEB, Ks + (cur ^ 1) * P::TILEB,
-         Vs + (cur ^ 1) * P::TILEB);
+  // tile n is computed from stage n & 1
+  int n = 0;
+  for (; n + 1 < nsp; n += 2) {
+    step(std::false_type{}, n, K0, V0, K1, V1);
+    step(std::false_type{}, n + 1, K1, V1, K0, V0);
+  }
+  if (n < nsp) {
+    step(std::false_type{}, n, K0, V0, K1, V1);
+    ++n;
   }
   finish_sparse();
-  for (int n = nsp; n < ntiles; ++n) {
-    const int cur = n & 1;
-    step(std::true_type{}, n, Ks + cur * P::TILEB, Vs + cur * P::TILEB, Ks + (cur ^ 1) * P::TILEB,
-         Vs + (cur ^ 1) * P::TILEB);
+  if ((n & 1) && n < ntiles) {
+    step(std::true_type{}, n, K1, V1, K0, V0);
+    ++n;
+  }
+  for (; n < ntiles; n += 2) {
+    step(std::true_type{}, n, K0, V0, K1, V1);
+    if (n + 1 < ntiles) step(std::true_type{}, n + 1, K1, V1, K0, V0);
   }
 
   // ---- epilogue: window branch, gate, one store per row ----------------------

@@ -66,6 +66,42 @@ def test_full_attention_block_scores(name, L, Hq, Hkv, D):
         check_scores(sc[b].cpu().numpy(), M)
 
 
+# Head groupings of the bf16 full layer: the query's heads reduced for the
+# block score across 2..32 adjacent lanes, a query spanning several waves
+# (G = 64), groups that do not divide 32 (G = 6: the heads of a query straddle
+# two waves), no scores, and bf16 outputs.
+FULL_GROUP_CASES = [
+    # L, Hq, Hkv, D, score mode, output dtype
+    (300, 16, 1, 128, "block", torch.float32),
+    (133, 32, 1, 128, "block", torch.bfloat16),
+    (200, 4, 2, 64, "block", torch.bfloat16),
+    (150, 6, 1, 128, "block", torch.float32),
+    (257, 8, 1, 128, "none", torch.bfloat16),
+    (97, 64, 1, 64, "none", torch.float32),
+    (64, 8, 2, 128, "block", torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("L,Hq,Hkv,D,mode,odt", FULL_GROUP_CASES)
+def test_full_attention_head_groups(L, Hq, Hkv, D, mode, odt):
+    w = _wl("dense7b_16k", L=L, Hq=Hq, Hkv=Hkv, D=D)
+    q, k, ks, v, vs = _qkv(w, seed=L + Hq)
+    print(f"full {mode} L={L} Hq={Hq} Hkv={Hkv} D={D} out={odt}", flush=True)
+    o = _nan_like((w.B, L, Hq, D), odt)
+    lse = _nan_like((w.B, Hq, L))
+    nblk = (L + 63) // 64
+    sc = _nan_like((w.B, L, nblk)) if mode == "block" else None
+    ops.hys_full_attn_fwd(dev(q), dev(k), dev(v), o, lse, mode, sc)
+    torch.cuda.synchronize()
+    for b in range(w.B):
+        qf, kf, vf = f64(q[b], w.q_dtype), f64(k[b], w.kv_dtype), f64(v[b], w.kv_dtype)
+        O, LSE = oracle.full_attention(qf, kf, vf, w.scale)
+        check_out(o[b].float().cpu().numpy(), O, "bf16", "o")
+        assert max_abs(lse[b].cpu().numpy(), LSE) <= 1e-3
+        if mode == "block":
+            check_scores(sc[b].cpu().numpy(), oracle.block_scores(qf, kf, w.scale, 64))
+
+
 TILE_CASES = [
     ("hysparse2_64k", 300, 8, 1, 128),
     ("hysparse2_64k", 128, 4, 1, 64),
