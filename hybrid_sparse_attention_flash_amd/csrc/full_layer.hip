@@ -36,6 +36,7 @@
 // C[m = 8(i/4) + 4h + i%4][n = l%32] (i = 0..15).
 #include "common.h"
 #include "kernels.h"
+#include <type_traits>
 
 namespace hys {
 namespace {
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void full_layer_kernel(const AttnArgs a) {
   // into; Kg/Vg: the K and V rows in global memory.  The loads of the next
   // tile stay in flight across the whole tile; the barrier at its end waits
   // for them.
-  auto step = [&](int n, const unsigned char* __restrict__ Kc, const unsigned char* __restrict__ Vc,
+  auto step = [&](auto mask_tag, int n, const unsigned char* __restrict__ Kc, const unsigned char* __restrict__ Vc,
                   unsigned char* __restrict__ Kn, unsigned char* __restrict__ Vn, const uint16_t* __restrict__ Kg,
                   const uint16_t* __restrict__ Vg) __attribute__((always_inline)) {
     // the per-step fragment offsets are a few XORs of these bases;
@@ -209,31 +210,30 @@ __global__ __launch_bounds__(256, 2) void full_layer_kernel(const AttnArgs a) {
     asm volatile("" : "+v"(kbo), "+v"(vbo));
     if (n + 1 < ntiles) load_tile(64 * (n + 1), Kn, Vn, lane_k, lane_v, Kg, Vg);
     const int j0 = 64 * n;
-    // (a wave none of whose rows sees this tile, possible only in the last
-    // tile when the rows start mid-block, runs it anyway: every row is off,
-    // so it adds nothing and its block scores come out -inf)
+    // MASK: the tile may hold keys past some row's position (the last one or
+    // two tiles of the workgroup); other tiles are whole for every row.  (A
+    // wave none of whose rows sees a tile, possible only in the last tile when
+    // the rows start mid-block, runs it anyway: every row is off, so it adds
+    // nothing and its block scores come out -inf.)
+    constexpr bool MASK = decltype(mask_tag)::value;
     {
-      // S^T = K Q^T (M = 64 keys as two 32-blocks, N = rows, K = D); the K
-      // fragments are read two k-steps ahead of their MFMAs
+      const bool row_on = MASK ? (valid && j0 <= qa) : valid;
+      // The tile runs as two 32-key halves h (keys j0 + 32h ..), each its own
+      // online-softmax step.  A wave issues in order, so the overlap of
+      // matrix and vector work is laid out by hand, in chunks the compiler
+      // may not reorder across (sched_barrier): the softmax of half 0 runs
+      // between the S MFMAs of half 1, that of half 1 between the PV MFMAs of
+      // half 0, the block-score reduction between those of half 1.  The
+      // reference moves branch-free (alpha = 1 unless it moves); only the
+      // rare rescale of O is a branch, between the PV MFMAs of the halves.
       f32x16 s[2];
       const f32x16 zero16 = {};
-      uint4 kf[P::NQC][2];
-      auto kfrag = [&](int c) __attribute__((always_inline)) {
-        kf[c][0] = *(const uint4*)(Kc + (kbo ^ (32 * c)));
-        kf[c][1] = *(const uint4*)(Kc + (kbo ^ (32 * c)) + 32 * P::ROWB);
+      // K fragment t: half t / NQC (rows 32h + ln), k-step t % NQC
+      constexpr int NT = 2 * P::NQC;
+      auto kfrag = [&](int t) __attribute__((always_inline)) {
+        return *(const uint4*)(Kc + (kbo ^ (32 * (t % P::NQC))) + (t / P::NQC) * 32 * P::ROWB);
       };
-      kfrag(0);
-      kfrag(1);
-#pragma unroll
-      for (int c = 0; c < P::NQC; ++c) {
-        if (c + 2 < P::NQC) kfrag(c + 2);
-        // keep the reads ahead: the scheduler would otherwise sink each read
-        // next to its MFMA and expose the LDS latency per step
-        __builtin_amdgcn_sched_barrier(0);
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[c][0]), qf[c], c == 0 ? zero16 : s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[c][1]), qf[c], c == 0 ? zero16 : s[1], 0, 0, 0);
-      }
-      // V^T fragments of k-step kc, d block db: keys 16kc + 4hh + (0..3) (lo)
+      // V^T fragments of d block db, k-step kc: keys 16kc + 4hh + (0..3) (lo)
       // and 16kc + 8 + 4hh + (0..3) (hi) at d = 32db + ln
       auto vfrag = [&](int db, int kc) __attribute__((always_inline)) {
         const unsigned char* vr = Vc + (vbo ^ (64 * db)) + (16 * kc) * P::ROWB;
@@ -242,110 +242,171 @@ __global__ __launch_bounds__(256, 2) void full_layer_kernel(const AttnArgs a) {
         const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
         return make_uint4(l2.x, l2.y, h2.x, h2.y);
       };
-      // the first d block's reads hide under the softmax
-      uint4 vf[2][4];
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) vf[0][kc] = vfrag(0, kc);
-      __builtin_amdgcn_sched_barrier(0);
-
-      // causal mask, only where some row of the wave sees part of the tile.
-      // Register 16mb + i of lane (ln, hh) holds key j0 + 32mb + 8(i/4) + 4hh + i%4.
-      const bool row_on = valid && j0 <= qa;
-      const bool part = row_on && j0 + 63 > qa;
-      if (__ballot(part) != 0ull) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+      // softmax of half h, in parts: head (mask, maximum, reference), the
+      // probabilities of elements [e0, e1), tail (row sum, P^T fragments)
+      float mt_h[2], alpha_h[2], mc_h[2], ps_h[2];
+      bool need_h[2];
+      auto soft_head = [&](int h) __attribute__((always_inline)) {
+        f32x16& x = s[h];
+        if (MASK) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = j0 + 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
-            s[mb][i] = (row_on & (key <= qa)) ? s[mb][i] : kNegInf;
+            const int key = j0 + 32 * h + 8 * (i >> 2) + 4 * hh + (i & 3);
+            x[i] = (row_on & (key <= qa)) ? x[i] : kNegInf;
           }
-      }
-      // row maximum over the tile (three-input maxima; no NaN quieting)
-      float mt;
-      {
-        float m8[8];
-#pragma unroll
-        for (int x = 0; x < 8; ++x)
-          m8[x] = fmax_nc(fmax_nc(s[x >> 2][4 * (x & 3)], s[x >> 2][4 * (x & 3) + 1]),
-                          fmax_nc(s[x >> 2][4 * (x & 3) + 2], s[x >> 2][4 * (x & 3) + 3]));
-        mt = fmax_nc(fmax_nc(fmax_nc(m8[0], m8[1]), fmax_nc(m8[2], m8[3])),
-                     fmax_nc(fmax_nc(m8[4], m8[5]), fmax_nc(m8[6], m8[7])));
-      }
-      mt = xor32_max(mt);
-      if (!row_on) mt = kNegInf;
-      if (SCORES) {
-        // the query's heads are HC adjacent lanes: reduce them and let the
-        // group's first lane store the block score
-        // (HC is 1, 2, 4, 8, 16 or 32; wave-uniform branches)
-        float gm = mt;
-        if (HC >= 2)
-          gm = fmaxf(gm, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, gm), 0xB1, 0xF, 0xF, false)));
-        if (HC >= 4)
-          gm = fmaxf(gm, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, gm), 0x4E, 0xF, 0xF, false)));
-        if (HC >= 8)
-          gm = fmaxf(gm, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, gm), 0x141, 0xF, 0xF, false)));
-        if (HC >= 16)
-          gm = fmaxf(gm, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, gm), 0x140, 0xF, 0xF, false)));
-        if (HC >= 32) gm = xor16_max(gm);
-        if (sc_lane) sc_base[sc_off + n] = gm * a.logit_scale;
-      }
-      // lazily moved reference: O and l are rescaled only in the rare tiles
-      // where some row's maximum exceeds it by more than the slack
-      const bool need = mt > m_run + lazy_raw;
-      float alpha = 1.f;
-      if (__ballot(need) != 0ull) {
-        const float mref = need ? mt : m_run;
-        alpha = need ? __builtin_amdgcn_exp2f((m_run - mref) * c2) : 1.f;
-        m_run = mref;
-#pragma unroll
-        for (int db = 0; db < P::NDB; ++db) acc[db] *= alpha;
-      }
-      // rows that see nothing of this tile get probability 0 everywhere
-      const float mc = !row_on ? __builtin_huge_valf() : ((m_run == kNegInf) ? 0.f : m_run * c2);
-      float ps8[8];
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const int mb = x >> 2, i0 = 4 * (x & 3);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[mb][i0 + e] = __builtin_amdgcn_exp2f(fmaf(s[mb][i0 + e], c2, -mc));
-        ps8[x] = (s[mb][i0] + s[mb][i0 + 1]) + (s[mb][i0 + 2] + s[mb][i0 + 3]);
-      }
-      const float ps = ((ps8[0] + ps8[1]) + (ps8[2] + ps8[3])) + ((ps8[4] + ps8[5]) + (ps8[6] + ps8[7]));
-      l_run = fmaf(l_run, alpha, ps);
-
-      // O^T += V^T P^T; P^T k-step kc holds keys 16kc + {0, 8} + 4hh + (0..3)
-      bf16x8 pf[4];
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const int mb = kc >> 1, i0 = 8 * (kc & 1);
-        uint4 pk;
-        pk.x = pack_bf16x2(s[mb][i0 + 0], s[mb][i0 + 1]);
-        pk.y = pack_bf16x2(s[mb][i0 + 2], s[mb][i0 + 3]);
-        pk.z = pack_bf16x2(s[mb][i0 + 4], s[mb][i0 + 5]);
-        pk.w = pack_bf16x2(s[mb][i0 + 6], s[mb][i0 + 7]);
-        pf[kc] = as_bf16x8(pk);
-      }
-#pragma unroll
-      for (int db = 0; db < P::NDB; ++db) {
-        if (db + 1 < P::NDB) {
-#pragma unroll
-          for (int kc = 0; kc < 4; ++kc) vf[(db + 1) & 1][kc] = vfrag(db + 1, kc);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        float m4[4];
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[db & 1][kc]), pf[kc], acc[db], 0, 0, 0);
+        for (int e = 0; e < 4; ++e)
+          m4[e] = fmax_nc(fmax_nc(x[4 * e], x[4 * e + 1]), fmax_nc(x[4 * e + 2], x[4 * e + 3]));
+        float mt = xor32_max(fmax_nc(fmax_nc(m4[0], m4[1]), fmax_nc(m4[2], m4[3])));
+        if (!row_on) mt = kNegInf;
+        mt_h[h] = mt;
+        const bool need = mt > m_run + lazy_raw;
+        const float mref = need ? mt : m_run;
+        // (exp2 of 0 when the reference stays; -inf, giving 0, when it moves
+        // off -inf; computed unconditionally so no branch splits the code)
+        alpha_h[h] = __builtin_amdgcn_exp2f(need ? (m_run - mref) * c2 : 0.f);
+        need_h[h] = need;
+        m_run = mref;
+        float mc = mref * c2;
+        mc = (mref == kNegInf) ? 0.f : mc;
+        mc_h[h] = row_on ? mc : __builtin_huge_valf();
+        ps_h[h] = 0.f;
+      };
+      auto soft_exp = [&](int h, int e0, int e1) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = e0; e < e1; ++e) {
+          s[h][e] = __builtin_amdgcn_exp2f(fmaf(s[h][e], c2, -mc_h[h]));
+          ps_h[h] += s[h][e];
+        }
+      };
+      auto soft_tail = [&](int h, bf16x8 (&pf)[2]) __attribute__((always_inline)) -> bool {
+        l_run = fmaf(l_run, alpha_h[h], ps_h[h]);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          uint4 pk;
+          pk.x = pack_bf16x2(s[h][8 * q + 0], s[h][8 * q + 1]);
+          pk.y = pack_bf16x2(s[h][8 * q + 2], s[h][8 * q + 3]);
+          pk.z = pack_bf16x2(s[h][8 * q + 4], s[h][8 * q + 5]);
+          pk.w = pack_bf16x2(s[h][8 * q + 6], s[h][8 * q + 7]);
+          pf[q] = as_bf16x8(pk);
+        }
+        return __ballot(need_h[h]) != 0ull;
+      };
+      // the 16 elements of a half exponentiated in NS chunks: chunk k covers
+      // [16k / NS, 16(k + 1) / NS)
+      auto soft_chunk = [&](int h, int k, int ns) __attribute__((always_inline)) {
+        soft_exp(h, 16 * k / ns, 16 * (k + 1) / ns);
+      };
+      constexpr int NSA = P::NQC - 2;       // half 0: after the 3rd S MFMA of half 1
+      constexpr int NSB = 2 * P::NDB - 1;   // half 1: after the 2nd PV MFMA of half 0
+
+      // ---- S^T = K Q^T; half 0's softmax between half 1's last 6 MFMAs ----
+      uint4 kf[NT];
+      kf[0] = kfrag(0);
+      kf[1] = kfrag(1);
+      kf[2] = kfrag(2);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t + 3 < NT) kf[t + 3] = kfrag(t + 3);
+        const int h = t / P::NQC, c = t % P::NQC;
+        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[t]), qf[c], c == 0 ? zero16 : s[h], 0, 0, 0);
+        if (t == P::NQC + 1) soft_head(0);            // S of half 0 has landed by now
+        if (t >= P::NQC + 2) soft_chunk(0, t - P::NQC - 2, NSA);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      bf16x8 pf0[2], pf1[2];
+      const bool moved0 = soft_tail(0, pf0);
+      // the probabilities are pinned ahead of the rescale branch (the
+      // compiler would otherwise sink them past it)
+      asm volatile("" : "+v"(pf0[0]), "+v"(pf0[1]), "+v"(l_run));
+      if (moved0) {
+#pragma unroll
+        for (int db = 0; db < P::NDB; ++db) acc[db] *= alpha_h[0];
+      }
+
+      // ---- O^T += V^T P^T_0 (k-steps 0, 1); half 1's softmax between -------
+      {
+        uint4 vf[2][2];
+        vf[0][0] = vfrag(0, 0);
+        vf[0][1] = vfrag(0, 1);
+#pragma unroll
+        for (int i = 0; i < 2 * P::NDB; ++i) {
+          const int db = i / 2, q = i % 2;
+          if (q == 0 && db + 1 < P::NDB) {
+            vf[(db + 1) & 1][0] = vfrag(db + 1, 0);
+            vf[(db + 1) & 1][1] = vfrag(db + 1, 1);
+          }
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[db & 1][q]), pf0[q], acc[db], 0, 0, 0);
+          if (i == 0) soft_head(1);
+          if (i >= 1) soft_chunk(1, i - 1, NSB);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      const bool moved1 = soft_tail(1, pf1);
+      asm volatile("" : "+v"(pf1[0]), "+v"(pf1[1]), "+v"(l_run));
+      if (moved1) {
+#pragma unroll
+        for (int db = 0; db < P::NDB; ++db) acc[db] *= alpha_h[1];
+      }
+
+      // ---- O^T += V^T P^T_1 (k-steps 2, 3); the block score between ----------
+      // (the row's tile maximum reduced over the query's HC adjacent lanes, HC
+      // in 1, 2, 4, 8, 16, 32: every step taken and selected, no branch)
+      float gm = fmax_nc(mt_h[0], mt_h[1]);
+      auto gstep = [&](int k) __attribute__((always_inline)) {
+        float t;
+        if (k == 0) t = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, gm), 0xB1, 0xF, 0xF, false));
+        else if (k == 1) t = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, gm), 0x4E, 0xF, 0xF, false));
+        else if (k == 2) t = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, gm), 0x141, 0xF, 0xF, false));
+        else if (k == 3) t = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, gm), 0x140, 0xF, 0xF, false));
+        else t = xor16_max(gm);
+        t = fmax_nc(gm, t);
+        gm = HC >= (2 << k) ? t : gm;
+      };
+      {
+        uint4 vf[2][2];
+        vf[0][0] = vfrag(0, 2);
+        vf[0][1] = vfrag(0, 3);
+#pragma unroll
+        for (int i = 0; i < 2 * P::NDB; ++i) {
+          const int db = i / 2, q = i % 2;
+          if (q == 0 && db + 1 < P::NDB) {
+            vf[(db + 1) & 1][0] = vfrag(db + 1, 2);
+            vf[(db + 1) & 1][1] = vfrag(db + 1, 3);
+          }
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[db & 1][q]), pf1[q], acc[db], 0, 0, 0);
+          if (SCORES && i < 5) gstep(i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (SCORES && sc_lane) sc_base[sc_off + n] = gm * a.logit_scale;
     }
     fl_tile_barrier();
   };
 
+  // tiles 0 .. nfull-1 are whole for every row of the workgroup (their last
+  // key precedes its first query); the rest need the causal mask
+  const int nfull = min((q0 + a.q_off + 1) / 64, ntiles);
   load_tile(0, K0, V0, lane_k, lane_v, kb, vb);
   fl_tile_barrier();
-  for (int n = 0; n < ntiles; n += 2) {
-    step(n, K0, V0, K1, V1, kb, vb);
-    if (n + 1 < ntiles) step(n + 1, K1, V1, K0, V0, kb, vb);
+  int n = 0;
+  for (; n + 1 < nfull; n += 2) {
+    step(std::false_type{}, n, K0, V0, K1, V1, kb, vb);
+    step(std::false_type{}, n + 1, K1, V1, K0, V0, kb, vb);
+  }
+  if (n < nfull) {
+    step(std::false_type{}, n, K0, V0, K1, V1, kb, vb);
+    ++n;
+  }
+  if ((n & 1) && n < ntiles) {
+    step(std::true_type{}, n, K1, V1, K0, V0, kb, vb);
+    ++n;
+  }
+  for (; n < ntiles; n += 2) {
+    step(std::true_type{}, n, K0, V0, K1, V1, kb, vb);
+    if (n + 1 < ntiles) step(std::true_type{}, n + 1, K1, V1, K0, V0, kb, vb);
   }
 
   // -inf for the blocks after each query's own
