@@ -195,7 +195,8 @@ hys_status check_attn_launch(const hys::AttnArgs& a, int mode, int grid) {
   HYS_DCHECK(a.B >= 1 && a.Lq >= 1 && a.q_off >= 0 && (int64_t)a.q_off + a.Lq <= a.Lk && a.Lk < (1 << 30));
   HYS_DCHECK(a.Hkv >= 1 && a.G >= 1 && a.Hq == a.G * a.Hkv);
   HYS_DCHECK(a.BQ >= 1 && a.ntq == (a.Lq + a.BQ - 1) / a.BQ);
-  HYS_DCHECK(a.HC >= 1 && a.BQ * a.HC <= 128 && (int64_t)a.nhc * a.HC >= a.G && (int64_t)(a.nhc - 1) * a.HC < a.G);
+  HYS_DCHECK(a.HC >= 1 && (int64_t)a.nhc * a.HC >= a.G && (int64_t)(a.nhc - 1) * a.HC < a.G);
+  HYS_DCHECK(a.BQ * a.HC <= ((mode == hys::M_FULL || mode == hys::M_FULL_BLOCK) ? hys::kFullLayerRows : 128));
   if (tile_mode) {
     HYS_DCHECK(a.BQ == 64);
     HYS_DCHECK((int64_t)grid == ((int64_t)a.B * a.ntq + 7) / 8 * 8 * a.Hkv * a.nhc);
@@ -314,6 +315,7 @@ hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
     hys::AttnArgs a = base_args(p, q, k, v, o, lse);
     hipStream_t st = (hipStream_t)stream;
     int mode, grid;
+    bool use_fl = false;
     a.nb = 1;
     const int rows = 128;                        // rows per workgroup
     if (mode_in == HYS_SCORE_TILE_TOKEN) {
@@ -331,9 +333,16 @@ hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
       mode = (mode_in == HYS_SCORE_BLOCK || mode_in == HYS_SCORE_BLOCK_GROUP) ? hys::M_FULL_BLOCK : hys::M_FULL;
       if (G > rows) return fail(HYS_ERR_UNSUPPORTED, "more than %d query heads per KV head", rows);
       a.HC = (int)G;
-      a.BQ = (int)(rows / G);
       a.nhc = 1;
+      // the bf16 full-layer kernel takes 256 rows per workgroup, the engine 128
+      a.BQ = (int)(hys::kFullLayerRows / G);
       a.ntq = (int)((L + a.BQ - 1) / a.BQ);
+      use_fl = et(q.dtype) == hys::ET_BF16 && et(k.dtype) == hys::ET_BF16 &&
+               hys::full_layer_supported((int)D, a, mode == hys::M_FULL_BLOCK);
+      if (!use_fl) {
+        a.BQ = (int)(rows / G);
+        a.ntq = (int)((L + a.BQ - 1) / a.BQ);
+      }
       if (mode == hys::M_FULL_BLOCK) {
         a.nblk = (int)nblk;
         a.sc_sb = L * nblk; a.sc_sr = nblk;
@@ -350,8 +359,7 @@ hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hys_tensor
       e = hys::launch_tile_scores(a.scores, (int)B, a.ntq, a.BQ, (int)L, (int)Lk, a.q_off, a.sc_sb, a.sc_sr, 0, st);
       if (e != hipSuccess) return hip_status(e, "score clear launch");
     }
-    if ((mode == hys::M_FULL || mode == hys::M_FULL_BLOCK) && et(q.dtype) == hys::ET_BF16 &&
-        et(k.dtype) == hys::ET_BF16 && hys::full_layer_supported((int)D, a, mode == hys::M_FULL_BLOCK))
+    if (use_fl)
       e = hys::launch_full_layer((int)D, a, mode == hys::M_FULL_BLOCK, grid, st);
     else
       e = hys::launch_attn(mode, et(q.dtype), et(k.dtype), (int)D, a, grid, st);

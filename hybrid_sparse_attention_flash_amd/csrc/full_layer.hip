@@ -11,14 +11,15 @@
 // and fp8 inputs and for head groups this kernel does not take.
 //
 // Design:
-//  * A workgroup (4 waves) owns BQ queries x the G heads of one KV group, row
-//    r = query r / G, head r % G; each wave owns 32 consecutive rows, the N of
-//    v_mfma_f32_32x32x16_bf16.  It walks the 64-key tiles 0 .. its last
-//    query's block.
+//  * A workgroup (8 waves, one per CU) owns BQ = 256 / G queries x the G
+//    heads of one KV group, row r = query r / G, head r % G; each wave owns
+//    32 consecutive rows, the N of v_mfma_f32_32x32x16_bf16.  It walks the
+//    64-key tiles 0 .. its last query's block.
 //  * Key tiles go HBM -> LDS with global_load_lds_dwordx4 (each lane fetches
 //    any 16 bytes; the 64 lanes of one instruction fill 1 KiB of LDS in lane
-//    order): no staging registers and no VALU work.  Two LDS buffers; the
-//    loads of tile n+1 are in flight while tile n is computed; one barrier a
+//    order): no staging registers and no VALU work.  Three LDS stages: the
+//    loads of tiles n+1 and n+2 are in flight while tile n is computed (one
+//    tile of lead left their latency exposed at every barrier); one barrier a
 //    tile.
 //  * K and V sit in LDS row-major, [64 keys][D], the 16-byte chunks of each
 //    row XOR-swizzled so the fragment reads below are free of bank conflicts.
@@ -45,11 +46,15 @@ typedef short fl_v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void fl_lds_void;
 typedef __attribute__((address_space(3))) fl_v4i16 fl_lds_v4i16;
 
+constexpr int kFlRows = kFullLayerRows;         // rows per workgroup
+constexpr int kFlWaves = kFlRows / 32;          // waves per workgroup
+static_assert(kFlWaves == 8, "the load placement assumes 8 waves");
+
 template <int D> struct FGeo {
   static constexpr int ROWB = 2 * D;            // bytes per key row
   static constexpr int CPR = D / 8;             // 16-byte chunks per row
   static constexpr int RPI = 1024 / ROWB;       // rows filled by one load instruction
-  static constexpr int NU = 64 / (4 * RPI);     // load instructions per wave, operand and tile
+  static constexpr int NU = 64 / (kFlWaves * RPI);   // load instructions per wave, operand and tile
   static constexpr int TILEB = 64 * ROWB;       // bytes of one operand tile
   static constexpr int NQC = D / 16;            // k-steps of S^T
   static constexpr int NDB = D / 32;            // 32-wide d blocks of O^T
@@ -62,24 +67,30 @@ template <int D> struct FGeo {
 template <int D> __device__ __forceinline__ int fswz_k(int r) { return D == 128 ? (r & 15) : ((r ^ ((r >> 3) & 3)) & 7); }
 template <int D> __device__ __forceinline__ int fswz_v(int r) { return D == 128 ? (5 * (r & 3)) & 15 : 2 * (r & 3); }
 
-// all LDS reads and writes of this wave, and this wave's LDS loads, are done;
-// then the workgroup barrier (a compiler barrier for memory as well)
+// this wave's LDS reads and writes are done and at most PENDING of its LDS
+// loads are still in flight (loads complete in issue order, so these are the
+// newest); then the workgroup barrier (a compiler barrier for memory as well)
+template <int PENDING>
 __device__ __forceinline__ void fl_tile_barrier() {
-  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+  static_assert(PENDING >= 0 && PENDING < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0070 | PENDING);   // vmcnt(PENDING) lgkmcnt(0)
   asm volatile("s_barrier" ::: "memory");
 }
 
 template <int D, bool SCORES>
-__global__ __launch_bounds__(256, 2) void full_layer_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(kFlRows * 2, 2) void full_layer_kernel(const AttnArgs a) {
   using P = FGeo<D>;
-  // two stages, each operand and stage its own array: every LDS access below
-  // names one of them statically (the tile loop is unrolled by two), which is
-  // what lets the compiler tell the loads into one stage from the reads of
-  // the other and keep the loads in flight across a whole tile
+  // three stages (tile n is computed while tiles n+1 and n+2 load), each
+  // operand and stage its own array: every LDS access below names one of
+  // them statically (the tile loop is unrolled by three), which is what lets
+  // the compiler tell the loads into one stage from the reads of another and
+  // keep the loads in flight across whole tiles
   __shared__ __attribute__((aligned(1024))) unsigned char K0[P::TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char K1[P::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char K2[P::TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char V0[P::TILEB];
   __shared__ __attribute__((aligned(1024))) unsigned char V1[P::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char V2[P::TILEB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -124,10 +135,11 @@ __global__ __launch_bounds__(256, 2) void full_layer_kernel(const AttnArgs a) {
   const int jlast = a.Lk - 1;
   const uint16_t* kb = (const uint16_t*)a.k + (int64_t)b * a.k_sb + (int64_t)g * a.k_sh;
   const uint16_t* vb = (const uint16_t*)a.v + (int64_t)b * a.v_sb + (int64_t)g * a.v_sh;
-  // instruction u of this wave fills tile rows (4u + wave) * RPI + (0..RPI-1);
-  // the swizzles depend on the row mod 4 * RPI (16 rows for D = 128, 32 for
-  // D = 64), so the chunk a lane fetches is the same for every u: one lane
-  // offset from a tile's first row, the rest of each address scalar
+  // instruction u of this wave fills tile rows (8u + wave) * RPI + (0..RPI-1);
+  // the swizzles depend on the row mod 16 (D = 128, where 8 * RPI = 32) and
+  // D = 64 takes one instruction, so the chunk a lane fetches is the same
+  // for every u: one lane offset from a tile's first row, the rest of each
+  // address scalar
   const int drow0 = wave * P::RPI + lane / P::CPR;
   const uint32_t kstb = (uint32_t)a.k_st * 2u, vstb = (uint32_t)a.v_st * 2u;
   const uint32_t chunk_k = (uint32_t)(((lane % P::CPR) ^ fswz_k<D>(drow0)) * 16);
@@ -145,10 +157,10 @@ __global__ __launch_bounds__(256, 2) void full_layer_kernel(const AttnArgs a) {
       // ever given a register an in-flight load still names
 #pragma unroll
       for (int u = 0; u < P::NU; ++u) {
-        const char* ktu = kt + (int64_t)(4 * P::RPI * u) * a.k_st * 2;
-        const char* vtu = vt + (int64_t)(4 * P::RPI * u) * a.v_st * 2;
-        __builtin_amdgcn_global_load_lds((const void*)(ktu + lk), (fl_lds_void*)(Kd + (4 * u + wave) * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vtu + lv), (fl_lds_void*)(Vd + (4 * u + wave) * 1024), 16, 0, 0);
+        const char* ktu = kt + (int64_t)(kFlWaves * P::RPI * u) * a.k_st * 2;
+        const char* vtu = vt + (int64_t)(kFlWaves * P::RPI * u) * a.v_st * 2;
+        __builtin_amdgcn_global_load_lds((const void*)(ktu + lk), (fl_lds_void*)(Kd + (kFlWaves * u + wave) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vtu + lv), (fl_lds_void*)(Vd + (kFlWaves * u + wave) * 1024), 16, 0, 0);
       }
     } else {
       // last tile of the keys: slots past the last key repeat the last key's
@@ -156,9 +168,9 @@ __global__ __launch_bounds__(256, 2) void full_layer_kernel(const AttnArgs a) {
       const int rmax = jlast - j0;
 #pragma unroll
       for (int u = 0; u < P::NU; ++u) {
-        const uint32_t rr = (uint32_t)min(drow0 + 4 * P::RPI * u, rmax);
-        __builtin_amdgcn_global_load_lds((const void*)(kt + (rr * kstb + chunk_k)), (fl_lds_void*)(Kd + (4 * u + wave) * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vt + (rr * vstb + chunk_v)), (fl_lds_void*)(Vd + (4 * u + wave) * 1024), 16, 0, 0);
+        const uint32_t rr = (uint32_t)min(drow0 + kFlWaves * P::RPI * u, rmax);
+        __builtin_amdgcn_global_load_lds((const void*)(kt + (rr * kstb + chunk_k)), (fl_lds_void*)(Kd + (kFlWaves * u + wave) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vt + (rr * vstb + chunk_v)), (fl_lds_void*)(Vd + (kFlWaves * u + wave) * 1024), 16, 0, 0);
       }
     }
   };
@@ -196,10 +208,10 @@ __global__ __launch_bounds__(256, 2) void full_layer_kernel(const AttnArgs a) {
   const bool sc_lane = SCORES && valid && hh == 0 && (ln % HC) == 0;
 
   // ---- one tile ---------------------------------------------------------------
-  // Kc/Vc: the tile being computed; Kn/Vn: the stage the next tile is loaded
-  // into; Kg/Vg: the K and V rows in global memory.  The loads of the next
-  // tile stay in flight across the whole tile; the barrier at its end waits
-  // for them.
+  // Kc/Vc: the tile being computed; Kn/Vn: the stage tile n+2 is loaded into
+  // (the one tile n-1 was read from); Kg/Vg: the K and V rows in global
+  // memory.  The barrier at the end waits for tile n+1's loads only, so each
+  // tile's loads have two tiles of compute to land in.
   auto step = [&](auto mask_tag, int n, const unsigned char* __restrict__ Kc, const unsigned char* __restrict__ Vc,
                   unsigned char* __restrict__ Kn, unsigned char* __restrict__ Vn, const uint16_t* __restrict__ Kg,
                   const uint16_t* __restrict__ Vg) __attribute__((always_inline)) {
@@ -208,7 +220,8 @@ __global__ __launch_bounds__(256, 2) void full_layer_kernel(const AttnArgs a) {
     // loop would otherwise hold them in
     int kbo = kbase_off, vbo = vbase_off;
     asm volatile("" : "+v"(kbo), "+v"(vbo));
-    if (n + 1 < ntiles) load_tile(64 * (n + 1), Kn, Vn, lane_k, lane_v, Kg, Vg);
+    const bool more = n + 2 < ntiles;
+    if (more) load_tile(64 * (n + 2), Kn, Vn, lane_k, lane_v, Kg, Vg);
     const int j0 = 64 * n;
     // MASK: the tile may hold keys past some row's position (the last one or
     // two tiles of the workgroup); other tiles are whole for every row.  (A
@@ -383,38 +396,45 @@ __global__ __launch_bounds__(256, 2) void full_layer_kernel(const AttnArgs a) {
       }
       if (SCORES && sc_lane) sc_base[sc_off + n] = gm * a.logit_scale;
     }
-    fl_tile_barrier();
+    if (more) fl_tile_barrier<2 * P::NU>();
+    else fl_tile_barrier<0>();
   };
 
   // tiles 0 .. nfull-1 are whole for every row of the workgroup (their last
   // key precedes its first query); the rest need the causal mask
   const int nfull = min((q0 + a.q_off + 1) / 64, ntiles);
   load_tile(0, K0, V0, lane_k, lane_v, kb, vb);
-  fl_tile_barrier();
+  if (ntiles > 1) {
+    load_tile(64, K1, V1, lane_k, lane_v, kb, vb);
+    fl_tile_barrier<2 * P::NU>();
+  } else {
+    fl_tile_barrier<0>();
+  }
+  // tile n is read from stage n % 3; step n loads tile n + 2 into stage
+  // (n + 2) % 3.  The main loop takes three mask-free tiles per trip; the
+  // rest go through a switch on the stage (a handful of tiles per workgroup).
+  auto one = [&](auto mask_tag, int n) __attribute__((always_inline)) {
+    switch (n % 3) {
+      case 0: step(mask_tag, n, K0, V0, K2, V2, kb, vb); break;
+      case 1: step(mask_tag, n, K1, V1, K0, V0, kb, vb); break;
+      default: step(mask_tag, n, K2, V2, K1, V1, kb, vb); break;
+    }
+  };
   int n = 0;
-  for (; n + 1 < nfull; n += 2) {
-    step(std::false_type{}, n, K0, V0, K1, V1, kb, vb);
+  for (; n + 2 < nfull; n += 3) {
+    step(std::false_type{}, n, K0, V0, K2, V2, kb, vb);
     step(std::false_type{}, n + 1, K1, V1, K0, V0, kb, vb);
+    step(std::false_type{}, n + 2, K2, V2, K1, V1, kb, vb);
   }
-  if (n < nfull) {
-    step(std::false_type{}, n, K0, V0, K1, V1, kb, vb);
-    ++n;
-  }
-  if ((n & 1) && n < ntiles) {
-    step(std::true_type{}, n, K1, V1, K0, V0, kb, vb);
-    ++n;
-  }
-  for (; n < ntiles; n += 2) {
-    step(std::true_type{}, n, K0, V0, K1, V1, kb, vb);
-    if (n + 1 < ntiles) step(std::true_type{}, n + 1, K1, V1, K0, V0, kb, vb);
-  }
+  for (; n < nfull; ++n) one(std::false_type{}, n);
+  for (; n < ntiles; ++n) one(std::true_type{}, n);
 
   // -inf for the blocks after each query's own
   if (SCORES) {
     float* sc = a.scores + (int64_t)g * a.sc_sg + (int64_t)b * a.sc_sb;
     const int ncol = a.nblk - ntiles;
     if (ncol > 0)
-      for (int e = tid; e < nq * ncol; e += 256) {
+      for (int e = tid; e < nq * ncol; e += kFlRows * 2) {
         const int t = e / ncol, c = ntiles + (e - t * ncol);
         sc[(int64_t)(q0 + t) * a.sc_sr + c] = kNegInf;
       }
@@ -447,7 +467,7 @@ __global__ __launch_bounds__(256, 2) void full_layer_kernel(const AttnArgs a) {
 
 bool full_layer_supported(int D, const AttnArgs& a, bool scores) {
   if (D != 64 && D != 128) return false;
-  if (a.HC != a.G || a.nhc != 1 || a.BQ * a.HC > 128 || a.BQ < 1) return false;
+  if (a.HC != a.G || a.nhc != 1 || a.BQ != kFlRows / a.G || a.BQ < 1) return false;
   // block scores reduce a query's heads between adjacent lanes of one wave,
   // and a lane addresses its query's scores with a 32-bit offset
   if (scores && (a.HC > 32 || 32 % a.HC != 0)) return false;
@@ -460,11 +480,11 @@ bool full_layer_supported(int D, const AttnArgs& a, bool scores) {
 hipError_t launch_full_layer(int D, const AttnArgs& a, bool scores, int grid, hipStream_t s) {
   if (!full_layer_supported(D, a, scores)) return hipErrorInvalidValue;
   if (D == 64) {
-    if (scores) hipLaunchKernelGGL((full_layer_kernel<64, true>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((full_layer_kernel<64, false>), dim3(grid), dim3(256), 0, s, a);
+    if (scores) hipLaunchKernelGGL((full_layer_kernel<64, true>), dim3(grid), dim3(2 * kFlRows), 0, s, a);
+    else hipLaunchKernelGGL((full_layer_kernel<64, false>), dim3(grid), dim3(2 * kFlRows), 0, s, a);
   } else {
-    if (scores) hipLaunchKernelGGL((full_layer_kernel<128, true>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((full_layer_kernel<128, false>), dim3(grid), dim3(256), 0, s, a);
+    if (scores) hipLaunchKernelGGL((full_layer_kernel<128, true>), dim3(grid), dim3(2 * kFlRows), 0, s, a);
+    else hipLaunchKernelGGL((full_layer_kernel<128, false>), dim3(grid), dim3(2 * kFlRows), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -60,7 +60,9 @@ hipError_t launch_attn(int mode, int qt, int kt, int D, const AttnArgs& a, int g
 hipError_t launch_sparse_layer(int D, const AttnArgs& a, int grid, hipStream_t s);
 
 // The full layer (M_FULL, or M_FULL_BLOCK with scores) for bf16 q/k/v, fp32
-// or bf16 output: D 64 or 128, HC == G, and with scores 32 % G == 0.
+// or bf16 output: D 64 or 128, HC == G, BQ == kFullLayerRows / G, and with
+// scores 32 % G == 0.
+constexpr int kFullLayerRows = 256;
 bool full_layer_supported(int D, const AttnArgs& a, bool scores);
 hipError_t launch_full_layer(int D, const AttnArgs& a, bool scores, int grid, hipStream_t s);
 
