@@ -48,16 +48,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
-// OCP e4m3fn -> bf16, exact.  v_cvt_pk_f32_fp8 decodes two e4m3fn bytes of a
-// dword to fp32 (checked against the format definition for all 256 codes on
-// gfx950); every finite e4m3 value has at most 4 significant bits, so the
-// round-to-nearest bf16 conversion that follows is exact.  (The pair goes
-// through __builtin_convertvector: extracting the two fp32 lanes as integers
-// and splicing their upper halves by hand was miscompiled by this toolchain,
-// which read the first lane twice.)
+// OCP e4m3fn -> bf16, exact: v_cvt_scalef32_pk_bf16_fp8 with scale 1
+// decodes two e4m3fn bytes of a dword (the low or the high half) straight to
+// two bf16 (one instruction; every finite e4m3 value has at most 4
+// significant bits and an exponent well inside bf16's range, so nothing
+// rounds).  Checked bit for bit against the format definition for every
+// finite code through the attention path.
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, bool hi_word) {
-  const f32x2 f = hi_word ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+  return __builtin_bit_cast(uint32_t, hi_word ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                                              : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
 }
 
 // Four fp8 bytes (one dword) -> four bf16 (two dwords).

@@ -25,8 +25,18 @@
 //                           window itself) and gathers its share of the tiles.
 #include "common.h"
 #include "kernels.h"
+#include <type_traits>
 
 namespace hys {
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void dec_static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    dec_static_for<N, I + 1>(f);
+  }
+}
 
 template <int SPARSE, typename KT, int D>
 __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
@@ -362,9 +372,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
   // neither keeps the other's registers live.
   const int niter = (t1 > t0) ? (t1 - t0 + 1) : 0;
   if (stager) {
-    if (t0 < t1) stage_load(std::integral_constant<int, 0>{}, t0);
-    if (NSET >= 2 && t0 + 1 < t1) stage_load(std::integral_constant<int, NSET >= 2 ? 1 : 0>{}, t0 + 1);
-    if (NSET >= 3 && t0 + 2 < t1) stage_load(std::integral_constant<int, NSET >= 3 ? 2 : 0>{}, t0 + 2);
+    dec_static_for<NSET>([&](auto set_tag) __attribute__((always_inline)) {
+      constexpr int S = decltype(set_tag)::value;
+      if (t0 + S < t1) stage_load(set_tag, t0 + S);
+    });
     auto step = [&](int i, auto set_tag) __attribute__((always_inline)) {
       const int t = t0 + i;
       if (t < t1) {
@@ -374,9 +385,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
       __syncthreads();
     };
     for (int i = 0; i < niter; i += NSET) {
-      step(i, std::integral_constant<int, 0>{});
-      if (NSET >= 2 && i + 1 < niter) step(i + 1, std::integral_constant<int, NSET >= 2 ? 1 : 0>{});
-      if (NSET >= 3 && i + 2 < niter) step(i + 2, std::integral_constant<int, NSET >= 3 ? 2 : 0>{});
+      dec_static_for<NSET>([&](auto set_tag) __attribute__((always_inline)) {
+        constexpr int S = decltype(set_tag)::value;
+        if (i + S < niter) step(i + S, set_tag);
+      });
     }
   } else {
     for (int i = 0; i < niter; ++i) {
