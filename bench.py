@@ -50,12 +50,12 @@ TRAFFIC = {"sources_sha1": "83caf5e53c26c550c057410450cda669e8ccda98", "bytes_pe
 # The same two passes for the KV Bridging kernel, over
 #   python3 bench.py --only-bridge --calibrate-copy --steps 1 --warmup 0
 BRIDGE_TRAFFIC_SOURCES = ("bridge.hip", "common.h", "kernels.h")
-BRIDGE_TRAFFIC = {"sources_sha1": "98ee99fa300645a3ebc8bc55242f8bcd03e94e95", "bytes_per_launch": 575.7e6}
+BRIDGE_TRAFFIC = {"sources_sha1": "2a72c8c8d8c9b6f4d25bc96e1f65349fe682411c", "bytes_per_launch": 575.7e6}
 # The same two passes for the decode step (every kernel of one hys_decode_step
 # call, summed per step), over
 #   python3 bench.py --only-decode --no-peaks --calibrate-copy --steps 2 --warmup 1
 DECODE_TRAFFIC_SOURCES = ("decode.hip", "topk.hip", "common.h", "kernels.h", "abi.hip")
-DECODE_TRAFFIC = {"sources_sha1": "7c1df2552e1980550e0a6c4acfdc8ca952e62cd6", "bytes_per_step": 1.1792e9}
+DECODE_TRAFFIC = {"sources_sha1": "0d7d4f3b8c8f13e12dd6a4a839531f39d2107213", "bytes_per_step": 1.1792e9}
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
