@@ -54,7 +54,7 @@ BRIDGE_TRAFFIC = {"sources_sha1": "2a72c8c8d8c9b6f4d25bc96e1f65349fe682411c", "b
 # The same two passes for the decode step (every kernel of one hys_decode_step
 # call, summed per step), over
 #   python3 bench.py --only-decode --no-peaks --calibrate-copy --steps 2 --warmup 1
-DECODE_TRAFFIC_SOURCES = ("decode.hip", "topk.hip", "common.h", "kernels.h", "abi.hip")
+DECODE_TRAFFIC_SOURCES = ("decode.hip", "decode_split.hip", "decode_split.h", "topk.hip", "common.h", "kernels.h", "abi.hip")
 DECODE_TRAFFIC = {"sources_sha1": "0d7d4f3b8c8f13e12dd6a4a839531f39d2107213", "bytes_per_step": 1.1792e9}
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0

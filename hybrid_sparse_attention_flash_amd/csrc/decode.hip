@@ -6,7 +6,11 @@
 // cache, so memory bandwidth dominates (QbitAI HySparse article, background
 // section).  The full layer therefore streams the cache once:
 //
-//   decode_kernel<full>   - split-K: each workgroup takes a contiguous share
+//   decode_kernel<full>   - split-K (bf16 caches, D = 64, and fp8 caches whose
+//                           layout does not suit 16-byte LDS-direct loads; the
+//                           fp8 D = 128 full layer otherwise runs the
+//                           all-compute kernel of decode_split.hip): each
+//                           workgroup takes a contiguous share
 //                           of the 64-key tiles.  Two staging waves load fp8
 //                           tiles several ahead and write them, as bf16 rows
 //                           (K and V row-major), into a two-stage LDS ring;
@@ -25,6 +29,7 @@
 //                           window itself) and gathers its share of the tiles.
 #include "common.h"
 #include "kernels.h"
+#include "decode_split.h"
 #include <type_traits>
 
 namespace hys {
@@ -493,6 +498,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const MergeArgs a) {
 }
 
 hipError_t launch_decode(int sparse, int kt, int D, const DecArgs& a, hipStream_t s) {
+  if (!sparse && kt == ET_FP8 && decode_split_fp8_supported(D, a)) return launch_decode_split_fp8(a, s);
   const unsigned grid = (unsigned)(a.nlayer * a.B * a.nsplit);
 #define HYS_DEC(SP, KT, DD) hipLaunchKernelGGL((decode_kernel<SP, KT, DD>), dim3(grid), dim3(256), 0, s, a)
   if (kt == ET_FP8) {
