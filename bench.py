@@ -46,7 +46,7 @@ METRIC = ("hybrid-block prefill tokens/s at 32k (TFLOP/s, GB/s % peak); decode u
 # summaries).  It is reported only while the kernel sources still hash to the
 # value they had when the counters were taken.
 TRAFFIC_SOURCES = ("sparse_layer.hip", "block_union.h", "common.h", "kernels.h")
-TRAFFIC = {"sources_sha1": "83caf5e53c26c550c057410450cda669e8ccda98", "bytes_per_launch": 1.4703e9}
+TRAFFIC = {"sources_sha1": "54063b6c7bf09af229384729e23633d8d207f21e", "bytes_per_launch": 1.4687e9}
 # The same two passes for the KV Bridging kernel, over
 #   python3 bench.py --only-bridge --calibrate-copy --steps 1 --warmup 0
 BRIDGE_TRAFFIC_SOURCES = ("bridge.hip", "common.h", "kernels.h")
@@ -55,7 +55,7 @@ BRIDGE_TRAFFIC = {"sources_sha1": "2a72c8c8d8c9b6f4d25bc96e1f65349fe682411c", "b
 # call, summed per step), over
 #   python3 bench.py --only-decode --no-peaks --calibrate-copy --steps 2 --warmup 1
 DECODE_TRAFFIC_SOURCES = ("decode.hip", "decode_split.hip", "decode_split.h", "topk.hip", "common.h", "kernels.h", "abi.hip")
-DECODE_TRAFFIC = {"sources_sha1": "0d7d4f3b8c8f13e12dd6a4a839531f39d2107213", "bytes_per_step": 1.1792e9}
+DECODE_TRAFFIC = {"sources_sha1": "4f1fc00adc302df213b30ccd68e4f49ff02bfcc3", "bytes_per_step": 1.1794e9}
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
