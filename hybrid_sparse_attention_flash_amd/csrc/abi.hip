@@ -167,18 +167,8 @@ hys_status topk_launch(const float* scores, int64_t rows, int64_t cols, int64_t 
   a.scores = scores; a.rows = rows; a.cols = cols; a.row_stride = row_stride; a.k = k;
   a.idx = idx; a.count = count;
   if (cols > hys::topk_chunk_cols()) {
-    // buffer 1: values then columns of level 0; buffer 2 likewise of level 1
-    const size_t first = hys::topk_workspace_first_bytes(rows, cols, k);
-    const size_t n1 = first / (sizeof(float) + sizeof(int32_t));
-    const size_t total = hys::topk_workspace_bytes(rows, cols, k);
-    const size_t n2 = (total - first) / (sizeof(float) + sizeof(int32_t));
-    a.cand_val = (float*)ws;
-    a.cand_idx = (int32_t*)((char*)ws + n1 * sizeof(float));
-    a.cand_val2 = (float*)((char*)ws + first);
-    a.cand_idx2 = (int32_t*)((char*)ws + first + n2 * sizeof(float));
-    HYS_DCHECK(first <= total && first == n1 * (sizeof(float) + sizeof(int32_t)) &&
-               total - first == n2 * (sizeof(float) + sizeof(int32_t)));
-    HYS_DCHECK(n1 >= (size_t)rows * (size_t)k && (n2 == 0 || n2 >= (size_t)rows * (size_t)k));
+    a.ws = ws;
+    HYS_DCHECK(ws != nullptr && ((uintptr_t)ws & 3) == 0 && hys::topk_workspace_bytes(rows, cols, k) > 0);
   }
   return hip_status(hys::launch_topk(a, st), "top-k launch");
 }
@@ -390,7 +380,7 @@ hys_status hys_select_topk(const float* scores, int64_t rows, int64_t cols, int6
     if (rows > 0 && row_stride < cols) return fail(HYS_ERR_INVALID_ARG, "row_stride < cols");
     if (rows > (1ll << 31) - 1) return fail(HYS_ERR_UNSUPPORTED, "rows >= 2^31");
     if (hys::topk_max_workgroups(rows, cols, k) > kMaxGrid)
-      return fail(HYS_ERR_UNSUPPORTED, "rows x ceil(cols / %lld) above %lld workgroups", (long long)hys::topk_chunk_cols(),
+      return fail(HYS_ERR_UNSUPPORTED, "rows x column chunks of the top-k launch above %lld workgroups",
                   (long long)kMaxGrid);
     const size_t need = hys::topk_workspace_bytes(rows, cols, k);
     if (!ws) { *ws_bytes = need; return ok(); }

@@ -78,16 +78,13 @@ struct TopkArgs {
   const float* scores; int64_t rows, cols, row_stride;
   int k;
   int32_t* idx; int32_t* count;
-  // long rows (cols > topk_chunk_cols()): the two candidate buffers of the
-  // level-by-level reduction (topk_workspace_bytes lays them out)
-  float* cand_val; int32_t* cand_idx;      // level 0's output (and levels 2, 4, ...)
-  float* cand_val2; int32_t* cand_idx2;    // level 1's output (and levels 3, 5, ...)
+  // long rows (cols > topk_chunk_cols()): topk_workspace_bytes of 4-byte
+  // aligned workspace for the row histograms, selection state and chunk counts
+  void* ws;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 // workspace of launch_topk for [rows, cols] and k; 0 when cols <= topk_chunk_cols()
 size_t topk_workspace_bytes(int64_t rows, int64_t cols, int k);
-// split of that workspace: bytes of the first candidate buffer (values then columns)
-size_t topk_workspace_first_bytes(int64_t rows, int64_t cols, int k);
 // largest grid (workgroups) launch_topk uses
 int64_t topk_max_workgroups(int64_t rows, int64_t cols, int k);
 int64_t topk_chunk_cols();

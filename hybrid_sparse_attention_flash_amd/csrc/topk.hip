@@ -18,8 +18,8 @@
 //
 //   short rows (cols <= 2048): one wave per row, up to 32 keys per lane
 //   long rows  (cols <= 32768): one 1024-thread workgroup per row, up to 32 keys per thread
-//   longer rows: each 32768-column chunk keeps its own top-k (exact superset of
-//   the row's top-k), then a second pass selects among the chunk winners.
+//   longer rows: the radix select runs over the whole row with many
+//   workgroups per row (a launch per digit, then a count and a write pass).
 #include "common.h"
 #include "kernels.h"
 
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// one 1024-thread workgroup per (row, chunk)
+// one 1024-thread workgroup per row (cols <= 32768)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int block_sum_1024(int v, int* sh) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -132,48 +132,34 @@ __device__ __forceinline__ int block_sum_1024(int v, int* sh) {
   return t;
 }
 
-// vals: row r, position p at vals[r*row_stride + p] (p < cols)
-// cmap: if non-null, the original column of position p is cmap[r*row_stride + p]
-//       (positions with cmap == -1 are empty); else the column is chunk_base + p.
-// Output for (row, chunk): out_idx[(r*nchunk + chunk)*k ...], out_val likewise (if non-null).
-//
-// Wave w owns positions [2048 w, 2048 w + 2048) of the chunk; lane L holds, in
-// slot v, position 2048 w + 64 v + L, so every load instruction reads 256
-// contiguous bytes and position order is (wave, slot, lane) order.
-template <int VPT, bool CMAP>
-__global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restrict__ vals,
-                                                          const int32_t* __restrict__ cmap, int64_t rows,
-                                                          int64_t cols, int64_t row_stride, int64_t chunk_cols,
-                                                          int nchunk, int k, int32_t* __restrict__ out_idx,
-                                                          float* __restrict__ out_val, int32_t* __restrict__ count) {
-  static_assert(VPT * 64 * 16 == 32768, "a workgroup covers 32768 positions");
+// Row r (one workgroup) is scores[r*row_stride + c], c < cols <= 32768.
+// Wave w owns columns [2048 w, 2048 w + 2048); lane L holds, in slot v,
+// column 2048 w + 64 v + L, so every load instruction reads 256 contiguous
+// bytes and column order is (wave, slot, lane) order.
+template <int VPT>
+__global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restrict__ vals, int64_t rows, int64_t cols,
+                                                          int64_t row_stride, int k, int32_t* __restrict__ out_idx,
+                                                          int32_t* __restrict__ count) {
+  static_assert(VPT * 64 * 16 == 32768, "a workgroup covers 32768 columns");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int64_t r = blockIdx.x / nchunk;
-  const int chunk = blockIdx.x % nchunk;
-  const int64_t cbase = (int64_t)chunk * chunk_cols;
-  const int ccols = (int)min(chunk_cols, cols - cbase);
-  const float* vr = vals + r * row_stride + cbase;
-  const int32_t* mr = CMAP ? cmap + r * row_stride + cbase : nullptr;
-  const int pos0 = wave * (64 * VPT) + lane;           // position of slot 0
-  // straight-line loads from clamped positions, masked afterwards
+  const int64_t r = blockIdx.x;
+  const int ccols = (int)cols;
+  const float* vr = vals + r * row_stride;
+  const int pos0 = wave * (64 * VPT) + lane;           // column of slot 0
+  // straight-line loads from clamped columns, masked afterwards
   uint32_t key[VPT];
-  int cmv[CMAP ? VPT : 1];      // original columns (cmap) of the positions
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     const int p = pos0 + 64 * v;
-    const int pc = min(p, ccols - 1);
-    key[v] = __builtin_bit_cast(uint32_t, vr[pc]);
-    if constexpr (CMAP) cmv[v] = mr[pc];
+    key[v] = __builtin_bit_cast(uint32_t, vr[min(p, ccols - 1)]);
   }
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     const int p = pos0 + 64 * v;
-    bool ok = p < ccols;
-    if constexpr (CMAP) ok = ok && cmv[v] >= 0;          // cmap -1: an empty candidate slot
-    key[v] = ok ? score_key(__builtin_bit_cast(float, key[v])) : 0u;
+    key[v] = p < ccols ? score_key(__builtin_bit_cast(float, key[v])) : 0u;
   }
-  // keys >= t in the chunk: per-lane counts, wave totals by DPP, the 16 wave
+  // keys >= t in the row: per-lane counts, wave totals by DPP, the 16 wave
   // totals through LDS
   __shared__ int shc[16];
   auto count_ge = [&](uint32_t t) {
@@ -206,7 +192,7 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
   uint32_t T = 0u;
   int need = 0;
   if (!all) {
-    // smallest and largest valid key of the chunk
+    // smallest and largest valid key of the row
     uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
@@ -279,7 +265,7 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
     if (lane == 0) { s_gt[wave] = ngt; s_eq[wave] = neq; }
   }
   __syncthreads();
-  // this wave's first tie rank and first output slot, and the chunk total:
+  // this wave's first tie rank and first output slot, and the row total:
   // wave w takes its keys > T and those of its ties whose rank is below need
   int tie0 = 0, out0 = 0, total = 0;
   {
@@ -292,7 +278,7 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
     }
     total = o0;
   }
-  const int64_t ob = (r * nchunk + chunk) * (int64_t)k;
+  const int64_t ob = r * (int64_t)k;
   int trun = tie0, orun = out0;
   // tie ranks are needed only in waves that hold keys equal to T (usually one)
   const bool has_eq = __builtin_amdgcn_readfirstlane(s_eq[wave]) != 0;
@@ -309,20 +295,10 @@ __global__ __launch_bounds__(1024) void topk_block_kernel(const float* __restric
     const unsigned long long bt = __ballot(tk);
     const int slot = orun + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bt >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bt, 0u));
     orun += __popcll(bt);
-    if (tk) {
-      // the score back from its (valid, hence nonzero) order key
-      const uint32_t kk = key[v];
-      const uint32_t bits = (kk & 0x80000000u) ? (kk & 0x7fffffffu) : ~kk;
-      if constexpr (CMAP) out_idx[ob + slot] = cmv[v];
-      else out_idx[ob + slot] = (int32_t)(cbase + pos0 + 64 * v);
-      if (out_val) out_val[ob + slot] = __builtin_bit_cast(float, bits);
-    }
+    if (tk) out_idx[ob + slot] = pos0 + 64 * v;
   }
-  for (int p = total + tid; p < k; p += 1024) {
-    out_idx[ob + p] = -1;
-    if (out_val) out_val[ob + p] = kNegInf;
-  }
-  if (count && tid == 0) count[r * nchunk + chunk] = total;
+  for (int p = total + tid; p < k; p += 1024) out_idx[ob + p] = -1;
+  if (count && tid == 0) count[r] = total;
 }
 
 // ---------------------------------------------------------------------------
@@ -340,58 +316,311 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Long rows (cols > 32768): a radix select over the whole row, run by many
+// workgroups per row.  The row is cut into chunks (one workgroup each, 8192
+// columns per pass over the chunk, chunks of several such pieces when a row
+// would otherwise need more than kGridMaxChunks of them).  T is found one digit
+// at a time from the top (bits 31..21, 20..10, 9..0 of the order key): every
+// workgroup adds its chunk's digit histogram of the keys that match the digits
+// chosen so far into the row's global histogram (LDS histogram first, then one
+// global atomic per nonzero bin), and the next launch picks the digit whose
+// bin holds the remaining rank.  A count pass records each chunk's keys > T
+// and keys == T; the write pass turns the preceding chunks' counts into the
+// chunk's first output slot and tie rank and places its chosen columns in
+// ascending order, exactly as the single-workgroup kernel does inside a chunk.
+// Compared with reducing each 32768-column chunk to its own top-k (a candidate
+// row of nchunk * k entries that must be reduced again by few workgroups),
+// every pass keeps the whole chip busy and no candidate row is built.
+// ---------------------------------------------------------------------------
 constexpr int kTopkVPT = 32;
-constexpr int64_t kTopkChunk = 1024 * kTopkVPT;      // columns per workgroup pass
-constexpr int kTopkMaxLevels = 8;
+constexpr int64_t kTopkChunk = 1024 * kTopkVPT;      // longest row of one workgroup
+constexpr int kGridThreads = 256;
+constexpr int kGridVPT = 32;
+constexpr int kGridPiece = kGridThreads * kGridVPT;  // 8192 columns per pass of a workgroup
+constexpr int64_t kGridMaxChunks = 1024;             // chunks per row at most
+constexpr int kGridBins1 = 2048, kGridBins2 = 2048, kGridBins3 = 1024;
+constexpr int kGridHist = kGridBins1 + kGridBins2 + kGridBins3;   // ints per row
+constexpr int kGridState = 8;                        // ints per row
 
-// Long rows are reduced level by level: level i cuts its input row into
-// 32768-column chunks and keeps each chunk's top-k (an exact superset of the
-// row's top-k), so its output row is nchunk_i * k candidates long, at most
-// 1/8 of its input for k <= 4096; the last level (<= 32768 columns) writes
-// the result.  Candidates stay in ascending column order at every level
-// (chunk outputs are ascending and chunks are concatenated in order), so a
-// tie still resolves to the lowest column.
-struct TopkPlan {
-  int nlev = 0;                 // reduction levels before the final one
-  int64_t nchunk[kTopkMaxLevels] = {};
-  int64_t cols[kTopkMaxLevels + 1] = {};   // input columns of each level
+struct GridTopkArgs {
+  const float* scores; int64_t rows, cols, row_stride;
+  int k;
+  int64_t chunk_cols;   // a multiple of kGridPiece
+  int nchunk;
+  int32_t* hist;        // [rows][kGridHist], zero before the first histogram pass
+  int32_t* state;       // [rows][kGridState]: after digit 1 and after digit 2 {mode (1 = take every
+                        // valid key), prefix, remaining rank}, then {T, keys == T to take}
+  int32_t* counts;      // [rows][nchunk][2]: keys > T, keys == T
+  int32_t* idx; int32_t* count;
 };
 
-static TopkPlan topk_plan(int64_t cols, int k) {
-  TopkPlan p;
-  int64_t c = cols;
-  while (c > kTopkChunk && p.nlev < kTopkMaxLevels) {
-    p.cols[p.nlev] = c;
-    p.nchunk[p.nlev] = (c + kTopkChunk - 1) / kTopkChunk;
-    c = p.nchunk[p.nlev] * (int64_t)k;
-    ++p.nlev;
+// digit round (0, 1, 2): its lowest key bit, its bin count, its histogram's offset in the row
+__device__ __forceinline__ int grid_shift(int round) { return round == 0 ? 21 : (round == 1 ? 10 : 0); }
+__device__ __forceinline__ int grid_bins(int round) { return round == 0 ? kGridBins1 : (round == 1 ? kGridBins2 : kGridBins3); }
+__device__ __forceinline__ int grid_hist_off(int round) { return round == 0 ? 0 : (round == 1 ? kGridBins1 : kGridBins1 + kGridBins2); }
+
+// Keys of the 8192 columns from col0 on, in the single-workgroup kernel's
+// layout: wave w owns columns col0 + [2048 w, 2048 w + 2048), lane L holds
+// column col0 + 2048 w + 64 v + L in slot v.  0 for columns past the row's end.
+__device__ __forceinline__ void grid_load_keys(const GridTopkArgs& a, int64_t r, int64_t col0, uint32_t (&key)[kGridVPT]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* vr = a.scores + r * a.row_stride;
+  const int64_t p0 = col0 + wave * (64 * kGridVPT) + lane;
+  const int64_t last = a.cols - 1;
+#pragma unroll
+  for (int v = 0; v < kGridVPT; ++v) {
+    const int64_t c = p0 + 64 * v;
+    key[v] = __builtin_bit_cast(uint32_t, vr[c < last ? c : last]);
   }
-  p.cols[p.nlev] = c;
-  return p;
+#pragma unroll
+  for (int v = 0; v < kGridVPT; ++v)
+    key[v] = (p0 + 64 * v <= last) ? score_key(__builtin_bit_cast(float, key[v])) : 0u;
 }
 
-// Two candidate buffers, used alternately by the levels: the first holds
-// level 0's output (the largest), the second level 1's.
+// Sum over the 256 threads (every thread gets it).  sh: 4 ints of LDS.
+__device__ __forceinline__ int grid_block_sum(int v, int* sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  v = wave_sum_i32(v);
+  __syncthreads();
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  return sh[0] + sh[1] + sh[2] + sh[3];
+}
+
+// Exclusive prefix over the 256 threads in thread order, and the total.
+__device__ __forceinline__ int grid_block_excl(int v, int* sh, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int incl = wave_incl_scan_i32(v);
+  __syncthreads();
+  if (lane == 63) sh[w] = incl;
+  __syncthreads();
+  int pre = 0;
+  for (int i = 0; i < w; ++i) pre += sh[i];
+  total = sh[0] + sh[1] + sh[2] + sh[3];
+  return pre + incl - v;
+}
+
+// The digit of row histogram h (nb bins) that holds rank krem counted from the
+// top, and the number of keys in higher bins; total = the histogram's sum.
+// Requires krem <= total for a meaningful digit.
+__device__ __forceinline__ void grid_pick(const int32_t* h, int nb, int krem, int* sh, int* s_pick, int& digit,
+                                          int& above, int& total) {
+  const int per = nb / kGridThreads;       // 8 or 4 bins per thread, thread 0 the highest
+  const int t = threadIdx.x;
+  const int top = nb - per * t;           // this thread's bins are [top - per, top)
+  int c = 0;
+  for (int i = 0; i < per; ++i) c += h[top - 1 - i];
+  const int ex = grid_block_excl(c, sh, total);
+  if (ex < krem && krem <= ex + c) {
+    int acc = ex;
+    for (int i = 0; i < per; ++i) {
+      const int hb = h[top - 1 - i];
+      if (acc + hb >= krem) { s_pick[0] = top - 1 - i; s_pick[1] = acc; break; }
+      acc += hb;
+    }
+  }
+  __syncthreads();
+  digit = s_pick[0];
+  above = s_pick[1];
+  __syncthreads();
+}
+
+// Histogram pass of digit ROUND over the keys that match the digits chosen so
+// far.  Round 0 also needs no state; rounds 1 and 2 first pick the previous
+// digit from the previous histogram (every workgroup of the row does, the
+// chunk-0 workgroup records it in the row's state).
+template <int ROUND>
+__global__ __launch_bounds__(kGridThreads) void topk_grid_hist_kernel(GridTopkArgs a) {
+  constexpr int NB = ROUND == 0 ? kGridBins1 : (ROUND == 1 ? kGridBins2 : kGridBins3);
+  constexpr int COPIES = ROUND == 0 ? 8 : 1;   // round 0 sees every key: spread each bin over 8 addresses
+  constexpr int SHIFT = ROUND == 0 ? 21 : (ROUND == 1 ? 10 : 0);
+  __shared__ __attribute__((aligned(16))) int hist[NB * COPIES];
+  __shared__ int sh[4], s_pick[2];
+  const int tid = threadIdx.x;
+  const int64_t r = blockIdx.x / a.nchunk;
+  const int chunk = (int)(blockIdx.x % a.nchunk);
+  int32_t* hrow = a.hist + r * kGridHist;
+  int32_t* st = a.state + r * kGridState;
+  uint32_t prefix = 0u, pmask = 0u;
+  if constexpr (ROUND > 0) {
+    // state after the previous round (round 1: nothing chosen yet, rank k)
+    int krem = a.k, mode = 0;
+    if constexpr (ROUND == 2) { mode = st[0]; prefix = (uint32_t)st[1]; krem = st[2]; }
+    if (mode == 0) {
+      int digit, above, total;
+      grid_pick(hrow + grid_hist_off(ROUND - 1), grid_bins(ROUND - 1), krem, sh, s_pick, digit, above, total);
+      if (ROUND == 1 && total <= a.k) mode = 1;   // no more valid keys than k: every one is taken
+      else { prefix |= (uint32_t)digit << grid_shift(ROUND - 1); krem -= above; }
+    }
+    // this round's slots; the other workgroups of this launch read the previous round's
+    if (chunk == 0 && tid == 0) {
+      int32_t* o = st + 3 * (ROUND - 1);
+      o[0] = mode; o[1] = (int)prefix; o[2] = krem;
+    }
+    if (mode != 0) return;
+    pmask = 0xffffffffu << (SHIFT + (ROUND == 1 ? 11 : 10));
+  }
+  for (int i = tid; i < NB * COPIES / 4; i += kGridThreads) ((int4*)hist)[i] = make_int4(0, 0, 0, 0);
+  __syncthreads();
+  const int copy = COPIES > 1 ? (tid & (COPIES - 1)) : 0;
+  const int64_t c0 = (int64_t)chunk * a.chunk_cols;
+  const int64_t c1 = min(a.cols, c0 + a.chunk_cols);
+  // chunk_cols is a multiple of the piece, so a piece never reaches into the
+  // next chunk; keys past the row's end are 0
+  for (int64_t col0 = c0; col0 < c1; col0 += kGridPiece) {
+    uint32_t key[kGridVPT];
+    grid_load_keys(a, r, col0, key);
+#pragma unroll
+    for (int v = 0; v < kGridVPT; ++v)
+      if (key[v] != 0u && (key[v] & pmask) == prefix)
+        atomicAdd(&hist[((key[v] >> SHIFT) & (NB - 1)) * COPIES + copy], 1);
+  }
+  __syncthreads();
+  int32_t* hg = hrow + grid_hist_off(ROUND);
+  for (int b = tid; b < NB; b += kGridThreads) {
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < COPIES; ++i) n += hist[b * COPIES + i];
+    if (n) atomicAdd(&hg[b], n);
+  }
+}
+
+// Count pass: T = the full key after the last digit, need = the keys equal to
+// T to take; each chunk's counts of keys > T and == T.
+__global__ __launch_bounds__(kGridThreads) void topk_grid_count_kernel(GridTopkArgs a) {
+  __shared__ int sh[4], s_pick[2];
+  const int tid = threadIdx.x;
+  const int64_t r = blockIdx.x / a.nchunk;
+  const int chunk = (int)(blockIdx.x % a.nchunk);
+  int32_t* st = a.state + r * kGridState;
+  const int mode = st[3];
+  uint32_t T = 0u;                               // mode 1: T = 0 and need = 0 take every valid key
+  int need = 0;
+  if (mode == 0) {
+    int digit, above, total;
+    const int krem = st[5];
+    grid_pick(a.hist + r * kGridHist + grid_hist_off(2), kGridBins3, krem, sh, s_pick, digit, above, total);
+    T = (uint32_t)st[4] | (uint32_t)digit;
+    need = krem - above;
+  }
+  if (chunk == 0 && tid == 0) { st[6] = (int)T; st[7] = need; }
+  const int64_t c0 = (int64_t)chunk * a.chunk_cols;
+  const int64_t c1 = min(a.cols, c0 + a.chunk_cols);
+  int ngt = 0, neq = 0;
+  for (int64_t col0 = c0; col0 < c1; col0 += kGridPiece) {
+    uint32_t key[kGridVPT];
+    grid_load_keys(a, r, col0, key);
+    // padding keys past the row's end are 0: never > T, and == T only when
+    // T = 0, where need = 0
+#pragma unroll
+    for (int v = 0; v < kGridVPT; ++v) { ngt += key[v] > T ? 1 : 0; neq += key[v] == T ? 1 : 0; }
+  }
+  ngt = grid_block_sum(ngt, sh);
+  neq = grid_block_sum(neq, sh);
+  if (tid == 0) {
+    int32_t* cn = a.counts + (r * a.nchunk + chunk) * 2;
+    cn[0] = ngt;
+    cn[1] = neq;
+  }
+}
+
+// Write pass: chunk j's first output slot is the number of keys taken by
+// chunks 0..j-1, its first tie rank the number of keys == T in them.
+__global__ __launch_bounds__(kGridThreads) void topk_grid_write_kernel(GridTopkArgs a) {
+  __shared__ int sh[4], s_gt[4], s_eq[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t r = blockIdx.x / a.nchunk;
+  const int chunk = (int)(blockIdx.x % a.nchunk);
+  const int32_t* st = a.state + r * kGridState;
+  const uint32_t T = (uint32_t)st[6];
+  const int need = st[7];
+  const int32_t* cn = a.counts + r * (int64_t)a.nchunk * 2;
+  // keys taken by the preceding chunks, 256 chunks at a time
+  int orun = 0, trun = 0;
+  for (int base = 0; base < chunk; base += kGridThreads) {
+    const int i = base + tid;
+    const int gt = i < chunk ? cn[2 * i] : 0;
+    const int eq = i < chunk ? cn[2 * i + 1] : 0;
+    int eqtot;
+    const int t0 = trun + grid_block_excl(eq, sh, eqtot);
+    const int taken = gt + min(max(need - t0, 0), eq);
+    orun += grid_block_sum(taken, sh);
+    trun += eqtot;
+  }
+  int32_t* out = a.idx + r * (int64_t)a.k;
+  const int64_t c0 = (int64_t)chunk * a.chunk_cols;
+  const int64_t c1 = min(a.cols, c0 + a.chunk_cols);
+  for (int64_t col0 = c0; col0 < c1; col0 += kGridPiece) {
+    uint32_t key[kGridVPT];
+    grid_load_keys(a, r, col0, key);
+    const int64_t pw = col0 + wave * (64 * kGridVPT) + lane;   // position of slot 0
+    {
+      int ngt = 0, neq = 0;
+#pragma unroll
+      for (int v = 0; v < kGridVPT; ++v) { ngt += key[v] > T ? 1 : 0; neq += key[v] == T ? 1 : 0; }
+      ngt = wave_sum_i32(ngt);
+      neq = wave_sum_i32(neq);
+      __syncthreads();                           // s_gt / s_eq of the previous piece are read
+      if (lane == 0) { s_gt[wave] = ngt; s_eq[wave] = neq; }
+    }
+    __syncthreads();
+    // this wave's first tie rank and output slot, and the piece's totals
+    int tie0 = trun, out0 = orun, o0 = orun, t0 = trun;
+    for (int w = 0; w < 4; ++w) {
+      const int eq = s_eq[w];
+      if (w == wave) { tie0 = t0; out0 = o0; }
+      o0 += s_gt[w] + min(max(need - t0, 0), eq);
+      t0 += eq;
+    }
+    orun = o0;
+    trun = t0;
+    int tr = tie0, orr = out0;
+    const bool has_eq = __builtin_amdgcn_readfirstlane(s_eq[wave]) != 0;
+#pragma unroll
+    for (int v = 0; v < kGridVPT; ++v) {
+      bool tk = key[v] > T;
+      if (has_eq) {
+        const bool eq = key[v] == T;
+        const unsigned long long be = __ballot(eq);
+        const int trank = tr + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+        tr += __popcll(be);
+        tk = tk || (eq && trank < need);
+      }
+      const unsigned long long bt = __ballot(tk);
+      const int slot = orr + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bt >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bt, 0u));
+      orr += __popcll(bt);
+      if (tk) out[slot] = (int32_t)(pw + 64 * v);
+    }
+  }
+  if (chunk == a.nchunk - 1) {
+    // orun = the row's total (at most k): pad the rest, record the count
+    for (int p = orun + tid; p < a.k; p += kGridThreads) out[p] = -1;
+    if (a.count && tid == 0) a.count[r] = orun;
+  }
+}
+
+struct GridPlan { int64_t chunk_cols; int nchunk; };
+static GridPlan grid_plan(int64_t cols) {
+  const int64_t pieces = (cols + kGridPiece - 1) / kGridPiece;
+  const int64_t per = (pieces + kGridMaxChunks - 1) / kGridMaxChunks;      // pieces per chunk
+  GridPlan g;
+  g.chunk_cols = per * kGridPiece;
+  g.nchunk = (int)((cols + g.chunk_cols - 1) / g.chunk_cols);
+  return g;
+}
+
 size_t topk_workspace_bytes(int64_t rows, int64_t cols, int k) {
+  (void)k;
   if (cols <= kTopkChunk) return 0;
-  const TopkPlan p = topk_plan(cols, k);
-  const size_t per = sizeof(float) + sizeof(int32_t);
-  size_t n = (size_t)(rows * p.cols[1]) * per;
-  if (p.nlev >= 2) n += (size_t)(rows * p.cols[2]) * per;
-  return n;
+  const GridPlan g = grid_plan(cols);
+  return (size_t)rows * ((size_t)kGridHist + kGridState + 2 * (size_t)g.nchunk) * sizeof(int32_t);
 }
 
-size_t topk_workspace_first_bytes(int64_t rows, int64_t cols, int k) {
-  if (cols <= kTopkChunk) return 0;
-  const TopkPlan p = topk_plan(cols, k);
-  return (size_t)(rows * p.cols[1]) * (sizeof(float) + sizeof(int32_t));
-}
-
-// Workgroups of the widest launch (rows x chunks of the input row).
+// Workgroups of the widest launch.
 int64_t topk_max_workgroups(int64_t rows, int64_t cols, int k) {
+  (void)k;
   if (cols <= kTopkChunk) return rows;
-  const TopkPlan p = topk_plan(cols, k);
-  return rows * p.nchunk[0];
+  return rows * grid_plan(cols).nchunk;
 }
 
 int64_t topk_chunk_cols() { return kTopkChunk; }
@@ -408,39 +637,28 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if (a.cols <= kTopkChunk) {
-    hipLaunchKernelGGL((topk_block_kernel<kTopkVPT, false>), dim3((unsigned)a.rows), dim3(1024), 0, s, a.scores,
-                       (const int32_t*)nullptr, a.rows, a.cols, a.row_stride, kTopkChunk, 1, a.k, a.idx,
-                       (float*)nullptr, a.count);
+    hipLaunchKernelGGL((topk_block_kernel<kTopkVPT>), dim3((unsigned)a.rows), dim3(1024), 0, s, a.scores, a.rows,
+                       a.cols, a.row_stride, a.k, a.idx, a.count);
     return hipGetLastError();
   }
-  const TopkPlan p = topk_plan(a.cols, a.k);
-  if (p.cols[p.nlev] > kTopkChunk) return hipErrorInvalidValue;   // excluded by validation
-  // candidate buffers: level i writes buffer i % 2
-  float* val[2] = {a.cand_val, a.cand_val2};
-  int32_t* col[2] = {a.cand_idx, a.cand_idx2};
-  for (int lev = 0; lev < p.nlev; ++lev) {
-    const int64_t nch = p.nchunk[lev];
-    const int64_t out_cols = nch * (int64_t)a.k;
-    int32_t* oi = col[lev & 1];
-    float* ov = val[lev & 1];
-    if (lev == 0) {
-      hipLaunchKernelGGL((topk_block_kernel<kTopkVPT, false>), dim3((unsigned)(a.rows * nch)), dim3(1024), 0, s,
-                         a.scores, (const int32_t*)nullptr, a.rows, a.cols, a.row_stride, kTopkChunk, (int)nch, a.k,
-                         oi, ov, (int32_t*)nullptr);
-    } else {
-      const int64_t in_cols = p.cols[lev];
-      hipLaunchKernelGGL((topk_block_kernel<kTopkVPT, true>), dim3((unsigned)(a.rows * nch)), dim3(1024), 0, s,
-                         (const float*)val[(lev - 1) & 1], (const int32_t*)col[(lev - 1) & 1], a.rows, in_cols,
-                         in_cols, kTopkChunk, (int)nch, a.k, oi, ov, (int32_t*)nullptr);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    (void)out_cols;
-  }
-  const int64_t fc = p.cols[p.nlev];
-  hipLaunchKernelGGL((topk_block_kernel<kTopkVPT, true>), dim3((unsigned)a.rows), dim3(1024), 0, s,
-                     (const float*)val[(p.nlev - 1) & 1], (const int32_t*)col[(p.nlev - 1) & 1], a.rows, fc, fc,
-                     kTopkChunk, 1, a.k, a.idx, (float*)nullptr, a.count);
+  if (a.k < 1 || !a.ws) return hipErrorInvalidValue;      // k = 0 never reaches here
+  const GridPlan g = grid_plan(a.cols);
+  GridTopkArgs ga{};
+  ga.scores = a.scores; ga.rows = a.rows; ga.cols = a.cols; ga.row_stride = a.row_stride; ga.k = a.k;
+  ga.chunk_cols = g.chunk_cols; ga.nchunk = g.nchunk;
+  int32_t* w = (int32_t*)a.ws;
+  ga.hist = w;
+  ga.state = w + a.rows * kGridHist;
+  ga.counts = ga.state + a.rows * kGridState;
+  ga.idx = a.idx; ga.count = a.count;
+  hipError_t e = launch_fill_i32(ga.hist, 0, a.rows * kGridHist, s);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)(a.rows * g.nchunk)), block(kGridThreads);
+  hipLaunchKernelGGL(topk_grid_hist_kernel<0>, grid, block, 0, s, ga);
+  hipLaunchKernelGGL(topk_grid_hist_kernel<1>, grid, block, 0, s, ga);
+  hipLaunchKernelGGL(topk_grid_hist_kernel<2>, grid, block, 0, s, ga);
+  hipLaunchKernelGGL(topk_grid_count_kernel, grid, block, 0, s, ga);
+  hipLaunchKernelGGL(topk_grid_write_kernel, grid, block, 0, s, ga);
   return hipGetLastError();
 }
 

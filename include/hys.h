@@ -212,11 +212,11 @@ HYS_API hys_status hys_full_attn_fwd(const hys_attn_params* p, hys_tensor4 q, hy
  *
  * scores: rows x cols fp32 with row_stride (elements, >= cols).
  * idx: rows x k int32, contiguous.  Limits: cols < 2^31; k <= 4096.  Rows
- * with more than 32768 columns are reduced level by level: each 32768-column
- * chunk keeps its own top-k (an exact superset of the row's), the winners are
- * concatenated in column order and reduced again until one chunk remains, so
- * any length is exact; rows * ceil(cols/32768) must stay below 2^22.  Those
- * rows need workspace (two candidate buffers).
+ * with more than 32768 columns are selected by a radix select over the whole
+ * row that many workgroups share (the row cut into at most 1024 chunks of a
+ * multiple of 8192 columns; rows * chunks must stay below 2^22).  Those rows
+ * need workspace: per row 5128 + 2 * chunks 32-bit words (row histograms,
+ * selection state, per-chunk counts), 4-byte aligned; the call overwrites it.
  */
 HYS_API hys_status hys_select_topk(const float* scores, int64_t rows, int64_t cols, int64_t row_stride, int32_t k,
                            int32_t* idx, int32_t* count, void* ws, size_t* ws_bytes, void* stream);

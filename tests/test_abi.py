@@ -83,7 +83,12 @@ def test_topk_validation():
     assert L.hys_select_topk(None, 4, 10, 5, 3, None, None, None, ctypes.byref(nb), None) == INVALID
     assert L.hys_select_topk(None, 4, 10, 10, 5000, None, None, None, ctypes.byref(nb), None) == UNSUPPORTED
     assert L.hys_select_topk(None, 4, 1 << 20, 1 << 20, 1024, None, None, None, ctypes.byref(nb), None) == 0
-    assert nb.value == 4 * 32 * 1024 * 8          # chunk winners (32768-column chunks): index + value
+    # per row: 5120 histogram bins + 8 state words + 2 counts per chunk (128 chunks of 8192 columns)
+    assert nb.value == 4 * (5120 + 8 + 2 * 128) * 4
+    assert L.hys_select_topk(None, 2, 3000001, 3000001, 16, None, None, None, ctypes.byref(nb), None) == 0
+    assert nb.value == 2 * (5120 + 8 + 2 * 367) * 4
+    assert L.hys_select_topk(None, 1, (1 << 31) - 1, (1 << 31) - 1, 16, None, None, None, ctypes.byref(nb), None) == 0
+    assert nb.value == (5120 + 8 + 2 * 1024) * 4        # at most 1024 chunks per row
     assert L.hys_select_topk(None, 4, 1 << 20, 1 << 20, 8192, None, None, None, ctypes.byref(nb), None) == UNSUPPORTED
     nb = ctypes.c_size_t(0)
     assert L.hys_select_topk(None, 4, 100, 100, 8, None, None, ctypes.c_void_p(FAKE), ctypes.byref(nb), None) == INVALID
