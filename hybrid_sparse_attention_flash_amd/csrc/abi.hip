@@ -1176,18 +1176,20 @@ hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     const int64_t B = q.shape[0], L = q.shape[1], Hq = q.shape[2], Hkv = k.shape[2], D = q.shape[3];
     const int64_t nblk = (L + 63) / 64;
     if (nblk > 16384) return fail(HYS_ERR_UNSUPPORTED, "more than 16384 key blocks");
-    const int64_t nwords = (nblk + 31) / 32, nrb = (L + 31) / 32;
+    const int64_t nwords = (nblk + 31) / 32;
     const int64_t ng = sp->idx_group_stride > 0 ? Hkv : 1;
     const size_t n_do = (size_t)(B * L * Hq * D) * 2, n_row = (size_t)(B * Hq * L) * 4;
-    const size_t n_rb = (size_t)(ng * B * L * nwords) * 4, n_tb = (size_t)(ng * B * nrb * nwords) * 4;
+    const int64_t ntk = (L + 127) / 128;
+    const size_t n_rb = (size_t)(ng * B * L * nwords) * 4;
+    const size_t n_rl = (size_t)(ng * B * ntk * L) * 4, n_rc = (size_t)(ng * B * ntk) * 4;
     const size_t n_tb16 = (size_t)(ng * B * ((L + 15) / 16) * nwords) * 4;
     const size_t n_gp = hys::bwd_gate_partial_floats((int)Hq, (int)D) * 4;
     int srb = 1, wsrb = 1;
     const int nsplit = hys::bwd_dkdv_plan(hys::BW_BLOCK, (int)L, 0, &srb);
     hys::bwd_dkdv_plan(hys::BW_WINDOW, (int)L, window, &wsrb);
     const size_t n_kv = hys::bwd_dkdv_ws_bytes(nsplit, (int)B, (int)L, (int)Hkv, (int)D);
-    const size_t need = 2 * up256(n_do) + 3 * up256(n_row) + up256(n_rb) + up256(n_tb) + up256(n_tb16) +
-                        up256(n_gp) + n_kv;
+    const size_t need = 2 * up256(n_do) + 3 * up256(n_row) + up256(n_rb) + up256(n_rl) + up256(n_rc) +
+                        up256(n_tb16) + up256(n_gp) + n_kv;
     if (!ws) { *ws_bytes = need; return ok(); }
     if (*ws_bytes < need) return fail(HYS_ERR_WORKSPACE, "workspace %zu < required %zu bytes", *ws_bytes, need);
     if (!aligned16(ws)) return fail(HYS_ERR_INVALID_ARG, "workspace not 16-byte aligned");
@@ -1199,7 +1201,8 @@ hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     float* Dd_w = (float*)w; w += up256(n_row);
     float* dz = (float*)w; w += up256(n_row);
     uint32_t* rowbits = (uint32_t*)w; w += up256(n_rb);
-    uint32_t* tilebits = (uint32_t*)w; w += up256(n_tb);
+    int32_t* rowlist = (int32_t*)w; w += up256(n_rl);
+    int32_t* rowcnt = (int32_t*)w; w += up256(n_rc);
     uint32_t* tilebits16 = (uint32_t*)w; w += up256(n_tb16);
     float* gpart = (float*)w; w += up256(n_gp);
     void* kvws = w;
@@ -1223,8 +1226,8 @@ hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
                                        (int)L, (int)Hq, (int)D, gpart, dgate_w, dgate_b, st)) != hipSuccess)
       return hip_status(e, "gate gradient launch");
     if ((e = hys::launch_bwd_selbits(idx, sp->idx_group_stride, sp->idx_batch_stride, sp->idx_row_stride, sp->k,
-                                     (int)ng, (int)B, (int)L, (int)nblk, (int)nwords, rowbits, tilebits, tilebits16,
-                                     st)) !=
+                                     (int)ng, (int)B, (int)L, (int)nblk, (int)nwords, rowbits, tilebits16, rowlist,
+                                     rowcnt, st)) !=
         hipSuccess)
       return hip_status(e, "selection bitmap launch");
 
@@ -1233,7 +1236,9 @@ hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     hys::BwdArgs a = bwd_args(p, q, k, v, dq, dk, (float*)dv.ptr);
     a.dO = do_sp; a.do_sb = do_sb; a.do_st = do_st; a.do_sh = D;
     a.lse = lse_sparse; a.Dd = Dd_sp;
-    a.rowbits = rowbits; a.tilebits = tilebits; a.tilebits16 = tilebits16; a.nwords = (int)nwords; a.ng = (int)ng;
+    a.rowbits = rowbits; a.rowlist = rowlist; a.rowcnt = rowcnt; a.tilebits16 = tilebits16;
+    a.nwords = (int)nwords; a.ng = (int)ng;
+    HYS_DCHECK(a.Lk == (int)L && (int64_t)srb * 32 * nsplit >= L);
     a.acc_q = 1; a.acc_kv = accumulate_kv;
     a.nsplit = nsplit; a.split_rb = srb;
     hys::bwd_dkdv_bind_ws(a, kvws, (int)D);

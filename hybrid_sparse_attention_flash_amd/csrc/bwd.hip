@@ -70,22 +70,13 @@ __device__ __forceinline__ void store_t8x2(uint16_t* t, int rp, int ch, bw_u32x4
   }
 }
 
-// Next row block of a dK/dV workgroup: blocks [base, rb_hi) in chunks of 64,
-// in block mode only those whose rows selected one of the tile's two 64-key
-// blocks (both bits sit in one word: the tile starts on an even block).
-template <int MODE>
-__device__ __forceinline__ bool next_row_block(const BwdArgs& a, int lane, int gs, int b, int nrb, int k0, int rb_hi,
-                                               uint64_t& mask, int& base, int& rb) {
+// Next row block of a dK/dV workgroup in the causal and window modes: blocks
+// [base, rb_hi) in chunks of 64.  (Block mode walks the tile's row list.)
+__device__ __forceinline__ bool next_row_block(int lane, int rb_hi, uint64_t& mask, int& base, int& rb) {
   while (mask == 0ull) {
     base += 64;
     if (base >= rb_hi) return false;
-    const int r = base + lane;
-    bool on = r < rb_hi;
-    if (MODE == BW_BLOCK && on) {
-      const uint32_t w = a.tilebits[((int64_t)(gs * a.B + b) * nrb + r) * a.nwords + (k0 >> 11)];
-      on = ((w >> ((k0 >> 6) & 31)) & 3u) != 0u;
-    }
-    mask = __ballot(on);
+    mask = __ballot(base + lane < rb_hi);
   }
   rb = base + __builtin_ctzll(mask);
   mask &= mask - 1ull;
@@ -106,6 +97,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_dot[D * TS];
   __shared__ __attribute__((aligned(16))) float s_lse[32];
   __shared__ __attribute__((aligned(16))) float s_dd[32];
+  // block mode: a window of the tile's row list, and the rows of the step
+  constexpr int NL = MODE == BW_BLOCK ? 2048 : 1;
+  __shared__ int s_list[NL];
+  __shared__ __attribute__((aligned(16))) int s_row[32];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -141,16 +136,45 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) { dk_acc[t][i] = 0.f; dv_acc[t][i] = 0.f; }
 
+  // Causal and window modes: this workgroup's share of the row blocks that can
+  // see the tile, absolute row blocks [split * split_rb, (split + 1) * split_rb).
+  // Block mode: a step is a chunk of 32 consecutive entries of the tile's
+  // row list (the rows that selected one of its two blocks), this workgroup's
+  // share the chunks [split * split_rb, (split + 1) * split_rb); rb is then
+  // the chunk index.
   int rb_hi = nrb;
-  if (MODE == BW_WINDOW) rb_hi = min(nrb, (k0 + 127 + a.window - 1) / 32 + 1);
-  // this workgroup's share of the row blocks that can see the tile: absolute
-  // row blocks [split * split_rb, (split + 1) * split_rb)
-  const int rb_first = max(k0 / 32, split * a.split_rb);
-  rb_hi = min(rb_hi, (split + 1) * a.split_rb);
   uint64_t mask = 0ull;
-  int base = rb_first - 64, rb = 0, h = 0;
-  bool have = rb_first < rb_hi && next_row_block<MODE>(a, lane, gs, b, nrb, k0, rb_hi, mask, base, rb);
+  int base = 0, rb = 0, h = 0;
+  bool have = false;
+  int rcnt = 0, win0 = -(NL + 32);        // the list window is loaded before the first step
+  const int32_t* rlist = nullptr;
+  if constexpr (MODE == BW_BLOCK) {
+    const int64_t tl = (int64_t)(gs * a.B + b) * ntk + kt;
+    rlist = a.rowlist + tl * a.L;
+    rcnt = __builtin_amdgcn_readfirstlane(a.rowcnt[tl]);
+    const int c_first = split * a.split_rb;
+    rb_hi = min((rcnt + 31) / 32, (split + 1) * a.split_rb);
+    rb = c_first;
+    have = c_first < rb_hi;
+  } else {
+    if (MODE == BW_WINDOW) rb_hi = min(nrb, (k0 + 127 + a.window - 1) / 32 + 1);
+    const int rb_first = max(k0 / 32, split * a.split_rb);
+    rb_hi = min(rb_hi, (split + 1) * a.split_rb);
+    base = rb_first - 64;
+    have = rb_first < rb_hi && next_row_block(lane, rb_hi, mask, base, rb);
+  }
   const bool did = have;
+  // block mode: list positions [p0, p0 + NL) into s_list (every thread calls it;
+  // issue() reads the window synchronously, so no read of the old one is pending)
+  auto load_window = [&](int p0) __attribute__((always_inline)) {
+    __syncthreads();
+    for (int e = tid; e < NL; e += 256) {
+      const int p = p0 + e;
+      s_list[e] = p < rcnt ? rlist[p] : 0;
+    }
+    __syncthreads();
+    win0 = p0;
+  };
 
   // staging item tid (when tid < NIT): rows 2rp, 2rp+1 of the block, 16-byte chunk ch.
   // Two register sets alternate (the loop is unrolled by two), so the loads of
@@ -160,6 +184,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   bw_u32x4 pq[2][2], pdo[2][2];
   float plse[2] = {kNegInf, kNegInf}, pdd[2] = {0.f, 0.f};
   uint32_t pbits[2] = {0u, 0u};
+  int prow[2] = {0, 0};                   // block mode: the query row of entry tid % 32 (L: none)
   uint32_t pok[2] = {0u, 0u};             // bit u: staging row u in range; 4: lse row; 8: bitmap row
   int srb[2] = {0, 0};
   bool shave[2] = {false, false};
@@ -172,10 +197,20 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     const int r0 = rbi * 32;
     const int ch = stager ? sch : 0;
     uint32_t okm = 0u;
+    // block mode: rows from the list window (which holds this chunk's entries;
+    // entries past the list's end read a 0 and are masked)
+    const int lw = r0 - win0;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int i = r0 + 2 * rp + u;
-      const bool ok = stager && i < a.L;
+      int i;
+      bool ok;
+      if constexpr (MODE == BW_BLOCK) {
+        ok = stager && r0 + 2 * rp + u < rcnt;
+        i = s_list[lw + 2 * rp + u];
+      } else {
+        i = r0 + 2 * rp + u;
+        ok = stager && i < a.L;
+      }
       const int ii = ok ? i : 0;
       okm |= (ok ? 1u : 0u) << u;
       pq[S][u] = *(const bw_u32x4*)(a.q + (int64_t)b * a.q_sb + (int64_t)ii * a.q_st + (int64_t)hq * a.q_sh + 8 * ch);
@@ -183,17 +218,25 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
                                      8 * ch);
     }
     {
-      const int i = r0 + (tid & 31);
-      const bool ok = i < a.L;
+      int i;
+      bool ok;
+      if constexpr (MODE == BW_BLOCK) {
+        ok = r0 + (tid & 31) < rcnt;
+        i = s_list[lw + (tid & 31)];
+      } else {
+        i = r0 + (tid & 31);
+        ok = i < a.L;
+      }
       okm |= (ok ? 4u : 0u);
       const int64_t o = ((int64_t)b * a.Hq + hq) * a.L + (ok ? i : 0);
       plse[S] = a.lse[o];
       pdd[S] = a.Dd[o];
-    }
-    if (MODE == BW_BLOCK) {
-      const int i = r0 + ln;
-      okm |= (i < a.L ? 8u : 0u);
-      pbits[S] = a.rowbits[((int64_t)(gs * a.B + b) * a.L + (i < a.L ? i : 0)) * a.nwords + (cw >> 5)];
+      if constexpr (MODE == BW_BLOCK) {
+        // the bitmap row is the same entry (ln = tid % 32)
+        okm |= (ok ? 8u : 0u);
+        prow[S] = ok ? i : a.L;
+        pbits[S] = a.rowbits[((int64_t)(gs * a.B + b) * a.nwords + (cw >> 5)) * a.L + (ok ? i : 0)];
+      }
     }
     pok[S] = okm;
   };
@@ -202,7 +245,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     if (!have) return;
     if (++h >= a.G) {
       h = 0;
-      have = next_row_block<MODE>(a, lane, gs, b, nrb, k0, rb_hi, mask, base, rb);
+      if constexpr (MODE == BW_BLOCK) have = ++rb < rb_hi;
+      else have = next_row_block(lane, rb_hi, mask, base, rb);
     }
   };
   // take the next step into set S and issue its loads (after finding the
@@ -213,7 +257,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     shave[S] = have;
     srb[S] = rb;
     advance();
-    if (shave[S]) issue(set_tag, srb[S], g * a.G + hs);
+    if (shave[S]) {
+      if constexpr (MODE == BW_BLOCK)
+        if ((srb[S] + 1) * 32 > win0 + NL) load_window(srb[S] * 32);
+      issue(set_tag, srb[S], g * a.G + hs);
+    }
   };
 
   auto step = [&](auto set_tag) __attribute__((always_inline)) {
@@ -237,6 +285,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     if (tid < 32) {
       s_lse[tid] = (okm & 4u) ? plse[S] * kLog2e : kNegInf;
       s_dd[tid] = (okm & 4u) ? pdd[S] : 0.f;
+      if constexpr (MODE == BW_BLOCK) s_row[tid] = prow[S];
     }
     uint32_t selmask = 0xffffffffu;
     if (MODE == BW_BLOCK)
@@ -245,7 +294,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     // this set now takes the step two ahead, whose loads overlap two steps of compute
     fill(set_tag);
 
-    bool any = kw0 <= cur_r0 + 31 && kw0 < a.Lk;
+    // block mode: the chunk's rows ascend, so its first row and its last valid
+    // row bound what the wave's keys can see
+    int r_first = cur_r0, r_last = cur_r0 + 31;
+    if constexpr (MODE == BW_BLOCK) {
+      r_first = s_row[0];
+      r_last = s_row[min(31, rcnt - cur_r0 - 1)];
+    }
+    bool any = kw0 <= r_last && kw0 < a.Lk;
     if (MODE == BW_WINDOW) any = any && kw0 + 31 > cur_r0 - a.window;
     if (MODE == BW_BLOCK) any = any && selmask != 0u;
     if (any) {
@@ -263,7 +319,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       // A block every one of whose rows sees all 32 keys skips the
       // per-element test (wave-uniform: away from the diagonal, the window
       // edges, partly selected blocks and the ragged ends).
-      bool full = kw0 + 31 <= cur_r0 && cur_r0 + 31 < a.L && kw0 + 31 < a.Lk;
+      bool full = kw0 + 31 <= r_first && cur_r0 + 31 < (MODE == BW_BLOCK ? rcnt : a.L) && kw0 + 31 < a.Lk;
       if (MODE == BW_WINDOW) full = full && kw0 > cur_r0 + 31 - a.window;
       if (MODE == BW_BLOCK) full = full && selmask == 0xffffffffu;
       float p[16], ds[16];
@@ -286,10 +342,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         for (int i4 = 0; i4 < 4; ++i4) {
           const f32x4 l4 = *(const f32x4*)&s_lse[8 * i4 + 4 * hh];
           const f32x4 d4 = *(const f32x4*)&s_dd[8 * i4 + 4 * hh];
+          int4 r4 = {0, 0, 0, 0};
+          if constexpr (MODE == BW_BLOCK) r4 = *(const int4*)&s_row[8 * i4 + 4 * hh];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * i4 + e, row = 8 * i4 + 4 * hh + e;
-            const bool vis = bw_visible<MODE>(cur_r0 + row, key, a.L, a.Lk, a.window, (selmask >> row) & 1u) &&
+            const int qrow = MODE == BW_BLOCK ? (e == 0 ? r4.x : e == 1 ? r4.y : e == 2 ? r4.z : r4.w) : cur_r0 + row;
+            const bool vis = bw_visible<MODE>(qrow, key, a.L, a.Lk, a.window, (selmask >> row) & 1u) &&
                              l4[e] != kNegInf;
             const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -l4[e])) : 0.f;
             p[i] = pv;
@@ -500,7 +559,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
       }
     }
     if (MODE == BW_BLOCK)
-      pbits = rowok ? a.rowbits[((int64_t)(gs * a.B + b) * a.L + qi) * a.nwords + (ct >> 5)] : 0u;
+      pbits = rowok ? a.rowbits[((int64_t)(gs * a.B + b) * a.nwords + (ct >> 5)) * a.L + qi] : 0u;
   };
   if (have) issue(c);
 
@@ -752,8 +811,7 @@ __global__ __launch_bounds__(256) void bwd_gate_reduce_kernel(const float* part,
 
 __global__ __launch_bounds__(256) void bwd_selbits_kernel(const int32_t* idx, int64_t idx_sg, int64_t idx_sb,
                                                           int64_t idx_sr, int k, int ng, int B, int L, int nblk,
-                                                          int nwords, uint32_t* rowbits, uint32_t* tilebits,
-                                                          uint32_t* tilebits16) {
+                                                          int nwords, uint32_t* rowbits, uint32_t* tilebits16) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t n = (int64_t)ng * B * L * k;
   if (e >= n) return;
@@ -765,10 +823,47 @@ __global__ __launch_bounds__(256) void bwd_selbits_kernel(const int32_t* idx, in
   const int c = idx[gs * idx_sg + b * idx_sb + (int64_t)i * idx_sr + j];
   if (c < 0 || c >= nblk) return;
   const uint32_t bit = 1u << (c & 31);
-  const int nrb = (L + 31) / 32;
-  atomicOr(&rowbits[((int64_t)(gs * B + b) * L + i) * nwords + (c >> 5)], bit);
-  atomicOr(&tilebits[((int64_t)(gs * B + b) * nrb + (i >> 5)) * nwords + (c >> 5)], bit);
+  atomicOr(&rowbits[((int64_t)(gs * B + b) * nwords + (c >> 5)) * L + i], bit);
   atomicOr(&tilebits16[((int64_t)(gs * B + b) * ((L + 15) / 16) + (i >> 4)) * nwords + (c >> 5)], bit);
+}
+
+// Row list of 128-key tile kt of selection set gb (= gs * B + b): the rows
+// i >= 128 kt, ascending, whose bitmap holds block 2kt or 2kt+1 (both bits in
+// one word, the tile starting on an even block), and their count.  One
+// workgroup per (gb, kt); thread t takes rows base + 16t .. base + 16t + 15 of
+// each 4096-row pass, so thread order is row order and an exclusive scan of
+// the per-thread counts places every row.
+__global__ __launch_bounds__(256) void bwd_rowlist_kernel(const uint32_t* rowbits, int L, int ntk, int nwords,
+                                                          int32_t* rowlist, int32_t* rowcnt) {
+  __shared__ int s_tot[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int kt = (int)(blockIdx.x % ntk);
+  const int64_t gb = blockIdx.x / ntk;
+  const int k0 = kt * 128, sh = (k0 >> 6) & 31;
+  const uint32_t* bits = rowbits + (gb * nwords + (k0 >> 11)) * (int64_t)L;
+  int32_t* out = rowlist + (gb * ntk + kt) * (int64_t)L;
+  int carry = 0;
+  for (int base = k0; base < L; base += 256 * 16) {
+    const int r0 = base + 16 * tid;
+    uint32_t wv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) wv[j] = bits[min(r0 + j, L - 1)];
+    uint32_t f = 0u;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) f |= (r0 + j < L && ((wv[j] >> sh) & 3u) != 0u) ? (1u << j) : 0u;
+    const int c = __popc(f);
+    const int incl = wave_incl_scan_i32(c);
+    __syncthreads();                      // the previous pass's totals are read
+    if (lane == 63) s_tot[w] = incl;
+    __syncthreads();
+    int pos = carry + incl - c;
+    for (int i = 0; i < w; ++i) pos += s_tot[i];
+    carry += s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if ((f >> j) & 1u) out[pos++] = r0 + j;
+  }
+  if (tid == 0) rowcnt[gb * ntk + kt] = carry;
 }
 
 template <int MODE, int D>
@@ -881,19 +976,22 @@ hipError_t launch_bwd_gate_grad(const float* dz, const uint16_t* q, int64_t q_sb
 }
 
 hipError_t launch_bwd_selbits(const int32_t* idx, int64_t idx_sg, int64_t idx_sb, int64_t idx_sr, int k, int ng,
-                              int B, int L, int nblk, int nwords, uint32_t* rowbits, uint32_t* tilebits,
-                              uint32_t* tilebits16, hipStream_t s) {
-  const int nrb = (L + 31) / 32, nrb16 = (L + 15) / 16;
+                              int B, int L, int nblk, int nwords, uint32_t* rowbits, uint32_t* tilebits16,
+                              int32_t* rowlist, int32_t* rowcnt, hipStream_t s) {
+  const int nrb16 = (L + 15) / 16, ntk = (L + 127) / 128;
+  if (L == 0) return hipSuccess;
   hipError_t e = launch_fill_i32((int32_t*)rowbits, 0, (int64_t)ng * B * L * nwords, s);
-  if (e != hipSuccess) return e;
-  e = launch_fill_i32((int32_t*)tilebits, 0, (int64_t)ng * B * nrb * nwords, s);
   if (e != hipSuccess) return e;
   e = launch_fill_i32((int32_t*)tilebits16, 0, (int64_t)ng * B * nrb16 * nwords, s);
   if (e != hipSuccess) return e;
   const int64_t n = (int64_t)ng * B * L * k;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_selbits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, idx_sg, idx_sb,
-                     idx_sr, k, ng, B, L, nblk, nwords, rowbits, tilebits, tilebits16);
+  if (n > 0) {
+    hipLaunchKernelGGL(bwd_selbits_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, idx, idx_sg, idx_sb,
+                       idx_sr, k, ng, B, L, nblk, nwords, rowbits, tilebits16);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(bwd_rowlist_kernel, dim3((unsigned)((int64_t)ng * B * ntk)), dim3(256), 0, s,
+                     (const uint32_t*)rowbits, L, ntk, nwords, rowlist, rowcnt);
   return hipGetLastError();
 }
 
