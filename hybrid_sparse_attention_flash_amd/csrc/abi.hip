@@ -1179,9 +1179,8 @@ hys_status hys_sparse_layer_bwd(const hys_attn_params* p, hys_tensor4 q, hys_ten
     const int64_t nwords = (nblk + 31) / 32;
     const int64_t ng = sp->idx_group_stride > 0 ? Hkv : 1;
     const size_t n_do = (size_t)(B * L * Hq * D) * 2, n_row = (size_t)(B * Hq * L) * 4;
-    const int64_t ntk = (L + 127) / 128;
     const size_t n_rb = (size_t)(ng * B * L * nwords) * 4;
-    const size_t n_rl = (size_t)(ng * B * ntk * L) * 4, n_rc = (size_t)(ng * B * ntk) * 4;
+    const size_t n_rl = (size_t)(ng * B * nblk * L) * 4, n_rc = (size_t)(ng * B * nblk) * 4;
     const size_t n_tb16 = (size_t)(ng * B * ((L + 15) / 16) * nwords) * 4;
     const size_t n_gp = hys::bwd_gate_partial_floats((int)Hq, (int)D) * 4;
     int srb = 1, wsrb = 1;

@@ -26,16 +26,16 @@ struct BwdArgs {
   int window;
   // BW_BLOCK: selection bitmaps (bit c of word c/32 = block c selected)
   const uint32_t* rowbits;    // [ng][B][nwords][L]: per query row (word-major)
-  // the query rows (ascending, rows >= the tile's first key) that selected
-  // block 2t or 2t+1, for every 128-key tile t: rowlist [ng][B][ntk][L],
-  // rowcnt [ng][B][ntk] entries used, ntk = ceil(Lk/128)
+  // the query rows (ascending, rows >= the block's first key) that selected
+  // 64-key block c: rowlist [ng][B][nblk][L], rowcnt [ng][B][nblk] entries
+  // used, nblk = ceil(Lk/64)
   const int32_t* rowlist; const int32_t* rowcnt;
   const uint32_t* tilebits16; // [ng][B][ceil(L/16)][nwords]: OR over the 16-row blocks
   int nwords, ng;             // ng = 1 (one set for every KV group) or Hkv
   int acc_q, acc_kv;          // 1: add into dq / dk, dv; 0: overwrite
   // dK/dV row split: the query rows a key tile sees are cut into nsplit ranges
-  // of split_rb 32-row blocks (block mode: of split_rb 32-entry chunks of the
-  // tile's row list), one workgroup each; with nsplit > 1 each writes
+  // of split_rb 32-row blocks (block mode: of split_rb * 32 entries of the
+  // block's row list), one workgroup each; with nsplit > 1 each writes
   // its partial sums (part_k, part_v: [nsplit][B][Lk][Hkv][D] fp32) and a flag
   // (flags: one per workgroup), and a reduce pass adds the flagged partials
   // into dk, dv in split order
@@ -90,7 +90,7 @@ hipError_t launch_bwd_gate_grad(const float* dz, const uint16_t* q, int64_t q_sb
                                 hipStream_t s);
 
 // selection bitmaps from block ids idx[g*idx_sg + b*idx_sb + i*idx_sr + j] (j < k; -1 = unused),
-// then the per-tile row lists of the dK/dV pass (ntk = ceil(L/128) tiles)
+// then the per-block row lists of the dK/dV pass (nblk blocks of 64 keys)
 hipError_t launch_bwd_selbits(const int32_t* idx, int64_t idx_sg, int64_t idx_sb, int64_t idx_sr, int k, int ng,
                               int B, int L, int nblk, int nwords, uint32_t* rowbits, uint32_t* tilebits16,
                               int32_t* rowlist, int32_t* rowcnt, hipStream_t s);

@@ -97,10 +97,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_dot[D * TS];
   __shared__ __attribute__((aligned(16))) float s_lse[32];
   __shared__ __attribute__((aligned(16))) float s_dd[32];
-  // block mode: a window of the tile's row list, and the rows of the step
-  constexpr int NL = MODE == BW_BLOCK ? 2048 : 1;
-  __shared__ int s_list[NL];
-  __shared__ __attribute__((aligned(16))) int s_row[32];
+  static_assert(MODE != BW_BLOCK, "the block-sparse branch runs bwd_dkdv_list_kernel");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -114,9 +111,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const int kt = tile / nbh, gb = tile - kt * nbh;
   const int g = gb % a.Hkv, b = gb / a.Hkv;
   const int k0 = kt * 128, kw0 = k0 + 32 * wave;
-  const int gs = a.ng > 1 ? g : 0;
   const int nrb = (a.L + 31) / 32;
-  const int cw = kw0 >> 6;                // this wave's 64-key block
 
   // this wave's 32 keys and values as B operands: lane (ln, hh) holds key ln, d = 16c + 8hh + [0, 8)
   bw_u32x4 kf[NC], vf[NC];
@@ -136,45 +131,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) { dk_acc[t][i] = 0.f; dv_acc[t][i] = 0.f; }
 
-  // Causal and window modes: this workgroup's share of the row blocks that can
-  // see the tile, absolute row blocks [split * split_rb, (split + 1) * split_rb).
-  // Block mode: a step is a chunk of 32 consecutive entries of the tile's
-  // row list (the rows that selected one of its two blocks), this workgroup's
-  // share the chunks [split * split_rb, (split + 1) * split_rb); rb is then
-  // the chunk index.
   int rb_hi = nrb;
+  if (MODE == BW_WINDOW) rb_hi = min(nrb, (k0 + 127 + a.window - 1) / 32 + 1);
+  // this workgroup's share of the row blocks that can see the tile: absolute
+  // row blocks [split * split_rb, (split + 1) * split_rb)
+  const int rb_first = max(k0 / 32, split * a.split_rb);
+  rb_hi = min(rb_hi, (split + 1) * a.split_rb);
   uint64_t mask = 0ull;
-  int base = 0, rb = 0, h = 0;
-  bool have = false;
-  int rcnt = 0, win0 = -(NL + 32);        // the list window is loaded before the first step
-  const int32_t* rlist = nullptr;
-  if constexpr (MODE == BW_BLOCK) {
-    const int64_t tl = (int64_t)(gs * a.B + b) * ntk + kt;
-    rlist = a.rowlist + tl * a.L;
-    rcnt = __builtin_amdgcn_readfirstlane(a.rowcnt[tl]);
-    const int c_first = split * a.split_rb;
-    rb_hi = min((rcnt + 31) / 32, (split + 1) * a.split_rb);
-    rb = c_first;
-    have = c_first < rb_hi;
-  } else {
-    if (MODE == BW_WINDOW) rb_hi = min(nrb, (k0 + 127 + a.window - 1) / 32 + 1);
-    const int rb_first = max(k0 / 32, split * a.split_rb);
-    rb_hi = min(rb_hi, (split + 1) * a.split_rb);
-    base = rb_first - 64;
-    have = rb_first < rb_hi && next_row_block(lane, rb_hi, mask, base, rb);
-  }
+  int base = rb_first - 64, rb = 0, h = 0;
+  bool have = rb_first < rb_hi && next_row_block(lane, rb_hi, mask, base, rb);
   const bool did = have;
-  // block mode: list positions [p0, p0 + NL) into s_list (every thread calls it;
-  // issue() reads the window synchronously, so no read of the old one is pending)
-  auto load_window = [&](int p0) __attribute__((always_inline)) {
-    __syncthreads();
-    for (int e = tid; e < NL; e += 256) {
-      const int p = p0 + e;
-      s_list[e] = p < rcnt ? rlist[p] : 0;
-    }
-    __syncthreads();
-    win0 = p0;
-  };
 
   // staging item tid (when tid < NIT): rows 2rp, 2rp+1 of the block, 16-byte chunk ch.
   // Two register sets alternate (the loop is unrolled by two), so the loads of
@@ -183,9 +149,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const bool stager = tid < NIT;
   bw_u32x4 pq[2][2], pdo[2][2];
   float plse[2] = {kNegInf, kNegInf}, pdd[2] = {0.f, 0.f};
-  uint32_t pbits[2] = {0u, 0u};
-  int prow[2] = {0, 0};                   // block mode: the query row of entry tid % 32 (L: none)
-  uint32_t pok[2] = {0u, 0u};             // bit u: staging row u in range; 4: lse row; 8: bitmap row
+  uint32_t pok[2] = {0u, 0u};             // bit u: staging row u in range; 4: lse row
   int srb[2] = {0, 0};
   bool shave[2] = {false, false};
   auto issue = [&](auto set_tag, int rbi, int hq) __attribute__((always_inline)) {
@@ -197,20 +161,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     const int r0 = rbi * 32;
     const int ch = stager ? sch : 0;
     uint32_t okm = 0u;
-    // block mode: rows from the list window (which holds this chunk's entries;
-    // entries past the list's end read a 0 and are masked)
-    const int lw = r0 - win0;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      int i;
-      bool ok;
-      if constexpr (MODE == BW_BLOCK) {
-        ok = stager && r0 + 2 * rp + u < rcnt;
-        i = s_list[lw + 2 * rp + u];
-      } else {
-        i = r0 + 2 * rp + u;
-        ok = stager && i < a.L;
-      }
+      const int i = r0 + 2 * rp + u;
+      const bool ok = stager && i < a.L;
       const int ii = ok ? i : 0;
       okm |= (ok ? 1u : 0u) << u;
       pq[S][u] = *(const bw_u32x4*)(a.q + (int64_t)b * a.q_sb + (int64_t)ii * a.q_st + (int64_t)hq * a.q_sh + 8 * ch);
@@ -218,25 +172,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
                                      8 * ch);
     }
     {
-      int i;
-      bool ok;
-      if constexpr (MODE == BW_BLOCK) {
-        ok = r0 + (tid & 31) < rcnt;
-        i = s_list[lw + (tid & 31)];
-      } else {
-        i = r0 + (tid & 31);
-        ok = i < a.L;
-      }
+      const int i = r0 + (tid & 31);
+      const bool ok = i < a.L;
       okm |= (ok ? 4u : 0u);
       const int64_t o = ((int64_t)b * a.Hq + hq) * a.L + (ok ? i : 0);
       plse[S] = a.lse[o];
       pdd[S] = a.Dd[o];
-      if constexpr (MODE == BW_BLOCK) {
-        // the bitmap row is the same entry (ln = tid % 32)
-        okm |= (ok ? 8u : 0u);
-        prow[S] = ok ? i : a.L;
-        pbits[S] = a.rowbits[((int64_t)(gs * a.B + b) * a.nwords + (cw >> 5)) * a.L + (ok ? i : 0)];
-      }
     }
     pok[S] = okm;
   };
@@ -245,8 +186,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     if (!have) return;
     if (++h >= a.G) {
       h = 0;
-      if constexpr (MODE == BW_BLOCK) have = ++rb < rb_hi;
-      else have = next_row_block(lane, rb_hi, mask, base, rb);
+      have = next_row_block(lane, rb_hi, mask, base, rb);
     }
   };
   // take the next step into set S and issue its loads (after finding the
@@ -257,11 +197,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     shave[S] = have;
     srb[S] = rb;
     advance();
-    if (shave[S]) {
-      if constexpr (MODE == BW_BLOCK)
-        if ((srb[S] + 1) * 32 > win0 + NL) load_window(srb[S] * 32);
-      issue(set_tag, srb[S], g * a.G + hs);
-    }
+    if (shave[S]) issue(set_tag, srb[S], g * a.G + hs);
   };
 
   auto step = [&](auto set_tag) __attribute__((always_inline)) {
@@ -285,25 +221,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     if (tid < 32) {
       s_lse[tid] = (okm & 4u) ? plse[S] * kLog2e : kNegInf;
       s_dd[tid] = (okm & 4u) ? pdd[S] : 0.f;
-      if constexpr (MODE == BW_BLOCK) s_row[tid] = prow[S];
     }
-    uint32_t selmask = 0xffffffffu;
-    if (MODE == BW_BLOCK)
-      selmask = (uint32_t)__ballot(hh == 0 && (okm & 8u) && ((pbits[S] >> (cw & 31)) & 1u));
     __syncthreads();
     // this set now takes the step two ahead, whose loads overlap two steps of compute
     fill(set_tag);
 
-    // block mode: the chunk's rows ascend, so its first row and its last valid
-    // row bound what the wave's keys can see
-    int r_first = cur_r0, r_last = cur_r0 + 31;
-    if constexpr (MODE == BW_BLOCK) {
-      r_first = s_row[0];
-      r_last = s_row[min(31, rcnt - cur_r0 - 1)];
-    }
-    bool any = kw0 <= r_last && kw0 < a.Lk;
+    bool any = kw0 <= cur_r0 + 31 && kw0 < a.Lk;
     if (MODE == BW_WINDOW) any = any && kw0 + 31 > cur_r0 - a.window;
-    if (MODE == BW_BLOCK) any = any && selmask != 0u;
     if (any) {
       f32x16 s, dp;
 #pragma unroll
@@ -319,9 +243,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       // A block every one of whose rows sees all 32 keys skips the
       // per-element test (wave-uniform: away from the diagonal, the window
       // edges, partly selected blocks and the ragged ends).
-      bool full = kw0 + 31 <= r_first && cur_r0 + 31 < (MODE == BW_BLOCK ? rcnt : a.L) && kw0 + 31 < a.Lk;
+      bool full = kw0 + 31 <= cur_r0 && cur_r0 + 31 < a.L && kw0 + 31 < a.Lk;
       if (MODE == BW_WINDOW) full = full && kw0 > cur_r0 + 31 - a.window;
-      if (MODE == BW_BLOCK) full = full && selmask == 0xffffffffu;
       float p[16], ds[16];
       const int key = kw0 + ln;
       if (full) {
@@ -342,14 +265,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         for (int i4 = 0; i4 < 4; ++i4) {
           const f32x4 l4 = *(const f32x4*)&s_lse[8 * i4 + 4 * hh];
           const f32x4 d4 = *(const f32x4*)&s_dd[8 * i4 + 4 * hh];
-          int4 r4 = {0, 0, 0, 0};
-          if constexpr (MODE == BW_BLOCK) r4 = *(const int4*)&s_row[8 * i4 + 4 * hh];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * i4 + e, row = 8 * i4 + 4 * hh + e;
-            const int qrow = MODE == BW_BLOCK ? (e == 0 ? r4.x : e == 1 ? r4.y : e == 2 ? r4.z : r4.w) : cur_r0 + row;
-            const bool vis = bw_visible<MODE>(qrow, key, a.L, a.Lk, a.window, (selmask >> row) & 1u) &&
-                             l4[e] != kNegInf;
+            const bool vis = bw_visible<MODE>(cur_r0 + row, key, a.L, a.Lk, a.window, true) && l4[e] != kNegInf;
             const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -l4[e])) : 0.f;
             p[i] = pv;
             ds[i] = pv * (dp[i] - d4[e]);
@@ -412,8 +331,277 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     }
 }
 
-// dk, dv (+)= the flagged partial sums of the row splits, in split order
-__global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdArgs a, int D) {
+// dK/dV of the block-sparse branch.  A workgroup owns one 64-key block of one
+// KV head and walks the list of query rows that selected the block (ascending,
+// built by bwd_rowlist_kernel), 64 list entries per step, once per head of the
+// group (heads fastest).  Wave w holds keys 32(w & 1) .. +31 of the block as B
+// operands, like the causal kernel, and computes rows 32(w >> 1) .. +31 of the
+// step; the two row halves' dK and dV are added through LDS at the end (fixed
+// order).  Every row of a step selected the block, so only causality and the
+// list's end are tested per element.  The list goes through an LDS window, so
+// a step's Q/dO loads, issued one step ahead, take their rows from LDS and
+// never wait on a global index load.  Row splits cut the list into ranges of
+// split_rb * 32 entries, one workgroup each, with the flagged partial sums of
+// the causal kernel's splits.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_list_kernel(BwdArgs a) {
+  constexpr int NC = D / 16;              // 16-wide d chunks of the S and dP contractions
+  constexpr int NT = D / 32;              // 32-wide d tiles of dK and dV
+  constexpr int RS = D + 8;               // row-major LDS row stride (elements)
+  constexpr int TS = 72;                  // transposed LDS row stride: 64 rows + 8
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int IPT = 32 * CPR / 256;     // staging items (row pair, chunk) per thread
+  constexpr int NL = 2048;                // list window (entries)
+  constexpr int QB = 64 * RS * 2, TB = D * TS * 2;   // bytes of a row-major and a transposed buffer
+  // the staging buffers, reused at the end for the row halves' dK/dV
+  __shared__ __attribute__((aligned(16))) unsigned char s_buf[2 * QB + 2 * TB];
+  static_assert(2 * QB + 2 * TB >= 2 * NT * 16 * 64 * 2 * 4, "dK/dV exchange fits the staging buffers");
+  uint16_t* s_q = (uint16_t*)s_buf;
+  uint16_t* s_do = (uint16_t*)(s_buf + QB);
+  uint16_t* s_qt = (uint16_t*)(s_buf + 2 * QB);
+  uint16_t* s_dot = (uint16_t*)(s_buf + 2 * QB + TB);
+  __shared__ __attribute__((aligned(16))) float s_lse[64];
+  __shared__ __attribute__((aligned(16))) float s_dd[64];
+  __shared__ __attribute__((aligned(16))) int s_row[64];
+  __shared__ int s_list[NL];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 31, hh = lane >> 5;
+  const int kh = wave & 1, rc = wave >> 1;
+  // blocks slowest within a split, split slowest (as in the causal kernel)
+  const int nbh = a.Hkv * a.B, nkb = (a.Lk + 63) / 64;
+  const int split = blockIdx.x / (nkb * nbh), tile = blockIdx.x - split * (nkb * nbh);
+  const int kb = tile / nbh, gb = tile - kb * nbh;
+  const int g = gb % a.Hkv, b = gb / a.Hkv;
+  const int kw0 = kb * 64 + 32 * kh;
+  const int gs = a.ng > 1 ? g : 0;
+
+  // this wave's 32 keys and values as B operands: lane (ln, hh) holds key ln, d = 16c + 8hh + [0, 8)
+  bw_u32x4 kf[NC], vf[NC];
+  {
+    const int key = kw0 + ln;
+    const bool ok = key < a.Lk;
+    const int64_t off = (int64_t)b * a.k_sb + (int64_t)(ok ? key : 0) * a.k_st + (int64_t)g * a.k_sh + 8 * hh;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kf[c] = ok ? *(const bw_u32x4*)(a.k + off + 16 * c) : zero4();
+      vf[c] = ok ? *(const bw_u32x4*)(a.v + off + 16 * c) : zero4();
+    }
+  }
+  f32x16 dk_acc[NT], dv_acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { dk_acc[t][i] = 0.f; dv_acc[t][i] = 0.f; }
+
+  // the block's list and this workgroup's share of it: entries [p_first, p_hi)
+  const int64_t tl = (int64_t)(gs * a.B + b) * nkb + kb;
+  const int32_t* rlist = a.rowlist + tl * a.L;
+  const int rcnt = __builtin_amdgcn_readfirstlane(a.rowcnt[tl]);
+  const int p_first = split * a.split_rb * 32;
+  const int p_hi = min(rcnt, p_first + a.split_rb * 32);
+  const bool did = p_first < p_hi;
+  int pos = p_first, h = 0;               // the next step to issue
+  bool have = did;
+  int win0 = -(NL + 64);                  // no window loaded yet
+  // list entries [p0, p0 + NL) into s_list; every thread calls it, and no read
+  // of the old window is pending (the issue reads it synchronously)
+  auto load_window = [&](int p0) __attribute__((always_inline)) {
+    __syncthreads();
+    for (int e = tid; e < NL; e += 256) {
+      const int p = p0 + e;
+      s_list[e] = p < p_hi ? rlist[p] : 0;
+    }
+    __syncthreads();
+    win0 = p0;
+  };
+
+  // the step in flight: Q and dO of 64 rows (item j of this thread: rows
+  // 2rp, 2rp + 1 of the step, 16-byte chunk ch), LSE and rowsum(dO O) of row
+  // tid (tid < 64), every load issued unconditionally from a clamped address
+  bw_u32x4 pq[IPT][2], pdo[IPT][2];
+  float plse = kNegInf, pdd = 0.f;
+  int prow = 0;
+  uint32_t pok = 0u;                      // bit 2j + u: staging row u of item j in range; 16: lse row
+  auto issue = [&](int p0, int hq) __attribute__((always_inline)) {
+    const int lw = p0 - win0;             // the step's first entry in the window
+    uint32_t okm = 0u;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int it = tid + 256 * j, rp = it & 31, ch = it >> 5;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bool ok = p0 + 2 * rp + u < p_hi;
+        const int i = s_list[lw + 2 * rp + u];
+        const int ii = ok ? i : 0;
+        okm |= (ok ? 1u : 0u) << (2 * j + u);
+        pq[j][u] = *(const bw_u32x4*)(a.q + (int64_t)b * a.q_sb + (int64_t)ii * a.q_st + (int64_t)hq * a.q_sh + 8 * ch);
+        pdo[j][u] = *(const bw_u32x4*)(a.dO + (int64_t)b * a.do_sb + (int64_t)ii * a.do_st + (int64_t)hq * a.do_sh +
+                                       8 * ch);
+      }
+    }
+    if (tid < 64) {
+      const bool ok = p0 + tid < p_hi;
+      const int i = s_list[lw + tid];
+      okm |= ok ? 16u : 0u;
+      prow = ok ? i : a.L;
+      const int64_t o = ((int64_t)b * a.Hq + hq) * a.L + (ok ? i : 0);
+      plse = a.lse[o];
+      pdd = a.Dd[o];
+    }
+    pok = okm;
+  };
+  // issue the next step (loading the window first when the step leaves it)
+  auto issue_next = [&]() __attribute__((always_inline)) {
+    if (pos + 64 > win0 + NL) load_window(pos);
+    issue(pos, g * a.G + h);
+    if (++h >= a.G) { h = 0; pos += 64; have = pos < p_hi; }
+  };
+
+  int cur_pos = pos;
+  if (have) issue_next();
+  while (did) {
+    const int step_pos = cur_pos;
+    const bool last = !have;
+    __syncthreads();                      // the previous step's LDS reads are done
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int it = tid + 256 * j, rp = it & 31, ch = it >> 5;
+      bw_u32x4 xq[2], xd[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bool ok = (pok >> (2 * j + u)) & 1u;
+        xq[u] = ok ? pq[j][u] : zero4();
+        xd[u] = ok ? pdo[j][u] : zero4();
+        *(bw_u32x4*)&s_q[(2 * rp + u) * RS + 8 * ch] = xq[u];
+        *(bw_u32x4*)&s_do[(2 * rp + u) * RS + 8 * ch] = xd[u];
+      }
+      store_t8x2<TS>(s_qt, rp, ch, xq[0], xq[1]);
+      store_t8x2<TS>(s_dot, rp, ch, xd[0], xd[1]);
+    }
+    if (tid < 64) {
+      s_lse[tid] = (pok & 16u) ? plse * kLog2e : kNegInf;
+      s_dd[tid] = (pok & 16u) ? pdd : 0.f;
+      s_row[tid] = prow;
+    }
+    __syncthreads();
+    // the next step's loads overlap this step's compute
+    cur_pos = pos;
+    if (have) issue_next();
+
+    // this wave's rows: entries step_pos + 32rc .. +31, ascending
+    const int nval = min(32, p_hi - (step_pos + 32 * rc));
+    const int r_first = s_row[32 * rc];
+    const int r_last = s_row[32 * rc + max(nval, 1) - 1];
+    const bool any = nval > 0 && kw0 <= r_last && kw0 < a.Lk;
+    if (any) {
+      f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { s[i] = 0.f; dp[i] = 0.f; }
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const bw_u32x4 aq = *(const bw_u32x4*)&s_q[(32 * rc + ln) * RS + 16 * c + 8 * hh];
+        const bw_u32x4 ad = *(const bw_u32x4*)&s_do[(32 * rc + ln) * RS + 16 * c + 8 * hh];
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(aq), bwf(kf[c]), s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(ad), bwf(vf[c]), dp, 0, 0, 0);
+      }
+      // element i: row 8(i/4) + 4hh + i%4 of the wave's 32, key kw0 + ln; a
+      // wave whose 32 rows all lie at or past its last key skips the test
+      const bool full = nval == 32 && kw0 + 31 <= r_first && kw0 + 31 < a.Lk;
+      float p[16], ds[16];
+      const int key = kw0 + ln;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int r0 = 32 * rc + 8 * i4 + 4 * hh;
+        const f32x4 l4 = *(const f32x4*)&s_lse[r0];
+        const f32x4 d4 = *(const f32x4*)&s_dd[r0];
+        const int4 q4 = *(const int4*)&s_row[r0];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * i4 + e;
+          const int qrow = e == 0 ? q4.x : e == 1 ? q4.y : e == 2 ? q4.z : q4.w;
+          // invalid entries carry row L and LSE -inf
+          const bool vis = full || (qrow < a.L && key <= qrow && key < a.Lk && l4[e] != kNegInf);
+          const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -l4[e])) : 0.f;
+          p[i] = pv;
+          ds[i] = pv * (dp[i] - d4[e]);
+        }
+      }
+      // A fragments: k-slot 8hh + j of chunk kc is row 16kc + 8(j/4) + 4hh + j%4, i.e. value 8kc + j
+      const bw_u32x4 pa0 = pack8(p), pa1 = pack8(p + 8);
+      const bw_u32x4 da0 = pack8(ds), da1 = pack8(ds + 8);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint16_t* td = &s_dot[(32 * t + ln) * TS + 32 * rc + 4 * hh];
+        const uint16_t* tq = &s_qt[(32 * t + ln) * TS + 32 * rc + 4 * hh];
+        const bw_u32x4 bd0 = cat2(*(const bw_u32x2*)(td), *(const bw_u32x2*)(td + 8));
+        const bw_u32x4 bd1 = cat2(*(const bw_u32x2*)(td + 16), *(const bw_u32x2*)(td + 24));
+        const bw_u32x4 bq0 = cat2(*(const bw_u32x2*)(tq), *(const bw_u32x2*)(tq + 8));
+        const bw_u32x4 bq1 = cat2(*(const bw_u32x2*)(tq + 16), *(const bw_u32x2*)(tq + 24));
+        dv_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(pa0), bwf(bd0), dv_acc[t], 0, 0, 0);
+        dv_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(pa1), bwf(bd1), dv_acc[t], 0, 0, 0);
+        dk_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(da0), bwf(bq0), dk_acc[t], 0, 0, 0);
+        dk_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(da1), bwf(bq1), dk_acc[t], 0, 0, 0);
+      }
+    }
+    if (last) break;
+  }
+
+  // the row halves' sums: waves 2, 3 hand theirs to waves 0, 1 through LDS
+  __syncthreads();                        // every wave is done with the staging buffers
+  float* red = (float*)s_buf;             // [kh][dk, dv][t][i][lane]
+  if (rc == 1) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        red[(((kh * 2 + 0) * NT + t) * 16 + i) * 64 + lane] = dk_acc[t][i];
+        red[(((kh * 2 + 1) * NT + t) * 16 + i) * 64 + lane] = dv_acc[t][i];
+      }
+  }
+  __syncthreads();
+  if (rc == 1) return;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dk_acc[t][i] += red[(((kh * 2 + 0) * NT + t) * 16 + i) * 64 + lane];
+      dv_acc[t][i] += red[(((kh * 2 + 1) * NT + t) * 16 + i) * 64 + lane];
+    }
+
+  // dK, dV in C layout: lane (ln, hh) holds d = 32t + ln of keys kw0 + 8(i/4) + 4hh + i%4
+  if (a.nsplit > 1) {
+    if (tid == 0) a.flags[blockIdx.x] = did ? 1 : 0;
+    if (!did) return;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kw0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if (key >= a.Lk) continue;
+        const int64_t o = ((((int64_t)split * a.B + b) * a.Lk + key) * a.Hkv + g) * D + 32 * t + ln;
+        a.part_k[o] = dk_acc[t][i] * a.scale;
+        a.part_v[o] = dv_acc[t][i];
+      }
+    return;
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = kw0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+      if (key >= a.Lk) continue;
+      const int64_t o = (int64_t)b * a.dk_sb + (int64_t)key * a.dk_st + (int64_t)g * a.dk_sh + 32 * t + ln;
+      const float kv = dk_acc[t][i] * a.scale, vv = dv_acc[t][i];
+      if (a.acc_kv) { a.dk[o] += kv; a.dv[o] += vv; }
+      else { a.dk[o] = kv; a.dv[o] = vv; }
+    }
+}
+
+// dk, dv (+)= the flagged partial sums of the row splits, in split order; the
+// dK/dV workgroups own tw keys (128 causal and window, 64 block-sparse)
+__global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdArgs a, int D, int tw) {
   const int n4 = D / 4;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t n = (int64_t)a.B * a.Lk * a.Hkv * n4;
@@ -423,8 +611,8 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdArgs a, int D) {
   const int g = (int)(t % a.Hkv);
   t /= a.Hkv;
   const int key = (int)(t % a.Lk), b = (int)(t / a.Lk);
-  const int nbh = a.Hkv * a.B, ntk = (a.Lk + 127) / 128;
-  const int64_t f0 = (int64_t)(key / 128) * nbh + (int64_t)b * a.Hkv + g;     // split s at f0 + s * ntk * nbh
+  const int nbh = a.Hkv * a.B, ntk = (a.Lk + tw - 1) / tw;
+  const int64_t f0 = (int64_t)(key / tw) * nbh + (int64_t)b * a.Hkv + g;      // split s at f0 + s * ntk * nbh
   const int64_t o = (int64_t)b * a.dk_sb + (int64_t)key * a.dk_st + (int64_t)g * a.dk_sh + 4 * d4;
   f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
   if (a.acc_kv) {
@@ -827,21 +1015,20 @@ __global__ __launch_bounds__(256) void bwd_selbits_kernel(const int32_t* idx, in
   atomicOr(&tilebits16[((int64_t)(gs * B + b) * ((L + 15) / 16) + (i >> 4)) * nwords + (c >> 5)], bit);
 }
 
-// Row list of 128-key tile kt of selection set gb (= gs * B + b): the rows
-// i >= 128 kt, ascending, whose bitmap holds block 2kt or 2kt+1 (both bits in
-// one word, the tile starting on an even block), and their count.  One
-// workgroup per (gb, kt); thread t takes rows base + 16t .. base + 16t + 15 of
+// Row list of 64-key block c of selection set gb (= gs * B + b): the rows
+// i >= 64 c, ascending, whose bitmap holds block c, and their count.  One
+// workgroup per (gb, c); thread t takes rows base + 16t .. base + 16t + 15 of
 // each 4096-row pass, so thread order is row order and an exclusive scan of
 // the per-thread counts places every row.
-__global__ __launch_bounds__(256) void bwd_rowlist_kernel(const uint32_t* rowbits, int L, int ntk, int nwords,
+__global__ __launch_bounds__(256) void bwd_rowlist_kernel(const uint32_t* rowbits, int L, int nblk, int nwords,
                                                           int32_t* rowlist, int32_t* rowcnt) {
   __shared__ int s_tot[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int kt = (int)(blockIdx.x % ntk);
-  const int64_t gb = blockIdx.x / ntk;
-  const int k0 = kt * 128, sh = (k0 >> 6) & 31;
-  const uint32_t* bits = rowbits + (gb * nwords + (k0 >> 11)) * (int64_t)L;
-  int32_t* out = rowlist + (gb * ntk + kt) * (int64_t)L;
+  const int c = (int)(blockIdx.x % nblk);
+  const int64_t gb = blockIdx.x / nblk;
+  const int k0 = c * 64, sh = c & 31;
+  const uint32_t* bits = rowbits + (gb * nwords + (c >> 5)) * (int64_t)L;
+  int32_t* out = rowlist + (gb * nblk + c) * (int64_t)L;
   int carry = 0;
   for (int base = k0; base < L; base += 256 * 16) {
     const int r0 = base + 16 * tid;
@@ -850,30 +1037,34 @@ __global__ __launch_bounds__(256) void bwd_rowlist_kernel(const uint32_t* rowbit
     for (int j = 0; j < 16; ++j) wv[j] = bits[min(r0 + j, L - 1)];
     uint32_t f = 0u;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) f |= (r0 + j < L && ((wv[j] >> sh) & 3u) != 0u) ? (1u << j) : 0u;
-    const int c = __popc(f);
-    const int incl = wave_incl_scan_i32(c);
+    for (int j = 0; j < 16; ++j) f |= (r0 + j < L && ((wv[j] >> sh) & 1u) != 0u) ? (1u << j) : 0u;
+    const int n = __popc(f);
+    const int incl = wave_incl_scan_i32(n);
     __syncthreads();                      // the previous pass's totals are read
     if (lane == 63) s_tot[w] = incl;
     __syncthreads();
-    int pos = carry + incl - c;
+    int pos = carry + incl - n;
     for (int i = 0; i < w; ++i) pos += s_tot[i];
     carry += s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
       if ((f >> j) & 1u) out[pos++] = r0 + j;
   }
-  if (tid == 0) rowcnt[gb * ntk + kt] = carry;
+  if (tid == 0) rowcnt[gb * nblk + c] = carry;
 }
 
 template <int MODE, int D>
 hipError_t dkdv_one(const BwdArgs& a, hipStream_t s) {
-  const int64_t grid = (int64_t)((a.Lk + 127) / 128) * a.Hkv * a.B * a.nsplit;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<MODE, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  const int tw = MODE == BW_BLOCK ? 64 : 128;
+  const int64_t grid = (int64_t)((a.Lk + tw - 1) / tw) * a.Hkv * a.B * a.nsplit;
+  if constexpr (MODE == BW_BLOCK)
+    hipLaunchKernelGGL((bwd_dkdv_list_kernel<D>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<MODE, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   const int64_t n = (int64_t)a.B * a.Lk * a.Hkv * (D / 4);
-  hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, D);
+  hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, D, tw);
   return hipGetLastError();
 }
 
@@ -905,7 +1096,8 @@ int bwd_dkdv_plan(int mode, int L, int window, int* split_rb) {
 size_t bwd_dkdv_ws_bytes(int nsplit, int B, int Lk, int Hkv, int D) {
   if (nsplit <= 1) return 0;
   const size_t part = (size_t)nsplit * B * Lk * Hkv * D * sizeof(float);
-  const size_t flags = (size_t)((Lk + 127) / 128) * Hkv * B * nsplit * sizeof(int32_t);
+  // one flag per workgroup: 64-key workgroups (block-sparse) bound the count
+  const size_t flags = (size_t)((Lk + 63) / 64) * Hkv * B * nsplit * sizeof(int32_t);
   return 2 * ((part + 255) & ~(size_t)255) + ((flags + 255) & ~(size_t)255);
 }
 
@@ -978,7 +1170,7 @@ hipError_t launch_bwd_gate_grad(const float* dz, const uint16_t* q, int64_t q_sb
 hipError_t launch_bwd_selbits(const int32_t* idx, int64_t idx_sg, int64_t idx_sb, int64_t idx_sr, int k, int ng,
                               int B, int L, int nblk, int nwords, uint32_t* rowbits, uint32_t* tilebits16,
                               int32_t* rowlist, int32_t* rowcnt, hipStream_t s) {
-  const int nrb16 = (L + 15) / 16, ntk = (L + 127) / 128;
+  const int nrb16 = (L + 15) / 16;
   if (L == 0) return hipSuccess;
   hipError_t e = launch_fill_i32((int32_t*)rowbits, 0, (int64_t)ng * B * L * nwords, s);
   if (e != hipSuccess) return e;
@@ -990,8 +1182,8 @@ hipError_t launch_bwd_selbits(const int32_t* idx, int64_t idx_sg, int64_t idx_sb
                        idx_sr, k, ng, B, L, nblk, nwords, rowbits, tilebits16);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(bwd_rowlist_kernel, dim3((unsigned)((int64_t)ng * B * ntk)), dim3(256), 0, s,
-                     (const uint32_t*)rowbits, L, ntk, nwords, rowlist, rowcnt);
+  hipLaunchKernelGGL(bwd_rowlist_kernel, dim3((unsigned)((int64_t)ng * B * nblk)), dim3(256), 0, s,
+                     (const uint32_t*)rowbits, L, nblk, nwords, rowlist, rowcnt);
   return hipGetLastError();
 }
 
