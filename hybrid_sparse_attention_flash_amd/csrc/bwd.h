@@ -33,9 +33,9 @@ struct BwdArgs {
   const uint32_t* tilebits16; // [ng][B][ceil(L/16)][nwords]: OR over the 16-row blocks
   int nwords, ng;             // ng = 1 (one set for every KV group) or Hkv
   int acc_q, acc_kv;          // 1: add into dq / dk, dv; 0: overwrite
-  // dK/dV row split: the query rows a key tile sees are cut into nsplit ranges
-  // of split_rb 32-row blocks (block mode: of split_rb * 32 entries of the
-  // block's row list), one workgroup each; with nsplit > 1 each writes
+  // dK/dV row split: the query rows a 64-key block sees (block mode: its row
+  // list) are cut into nsplit ranges of split_rb * 32 rows counted from the
+  // block's first, one workgroup each; with nsplit > 1 each writes
   // its partial sums (part_k, part_v: [nsplit][B][Lk][Hkv][D] fp32) and a flag
   // (flags: one per workgroup), and a reduce pass adds the flagged partials
   // into dk, dv in split order

@@ -1,4 +1,5 @@
-// Backward pass of the HySparse hybrid block on gfx950 (v_mfma_f32_32x32x16_bf16).
+// Backward pass of the HySparse hybrid block on gfx950 (v_mfma_f32_16x16x32_bf16
+// for dK/dV, v_mfma_f32_32x32x16_bf16 for dQ).
 //
 // HySparse is trained directly (QbitAI HySparse article, opening summary;
 // demingchina HySparse2 commentary, section 06).  With the selection held
@@ -8,12 +9,14 @@
 //   dQ = scale dS K,   dK = scale dS^T Q,
 // summed over the G query heads of a KV head for dK, dV.  Two kernels per
 // branch, neither with atomics:
-//   bwd_dkdv_kernel - key-stationary: a workgroup owns 128 keys of one KV head
-//     (32 per wave, held in registers as MFMA operands) and walks the 32-row
-//     query blocks of every head of the group that can see them, staging Q and
-//     dO through LDS both row-major (A operands of S and dP) and transposed
-//     (B operands of dK and dV); dK and dV stay in registers and are written
-//     once.
+//   bwd_dkdv_causal_kernel - the full layer's dK/dV: 128 keys of one KV head
+//     per workgroup, 32 per wave, over the 32-row query blocks that see them.
+//   bwd_dkdv_kernel - key-stationary: a workgroup owns 64 keys of one KV head
+//     (16 per wave, held in registers as MFMA operands) and walks the query
+//     rows that see them (block-sparse: the rows that selected the block) 32
+//     at a time for every head of the group, staging Q and dO through LDS both
+//     row-major (A operands of S and dP) and transposed (B operands of dK and
+//     dV); dK and dV stay in registers and are written once.
 //   bwd_dq_kernel - query-stationary: a workgroup owns 128 (query row, head)
 //     columns of one KV group (16 rows x 8 heads when the group has 8 or more
 //     heads, else 32-row blocks of up to 4 heads) and walks the 64-key tiles
@@ -23,8 +26,8 @@
 // the MFMA in its C layout (lane = one column, rows spread over the 16
 // values); they feed the next MFMA as A operands directly, with the other
 // operand read in the same permuted row order, so no transpose of P or dS is
-// needed.  The block-sparse branch reads per-row selection bitmaps and skips
-// whole row blocks (dK/dV) or key tiles (dQ) that no row selected.
+// needed.  The block-sparse branch walks per-block lists of the selecting rows
+// (dK/dV) and skips key tiles that no row of a 16-row block selected (dQ).
 
 #include <algorithm>
 
@@ -70,8 +73,7 @@ __device__ __forceinline__ void store_t8x2(uint16_t* t, int rp, int ch, bw_u32x4
   }
 }
 
-// Next row block of a dK/dV workgroup in the causal and window modes: blocks
-// [base, rb_hi) in chunks of 64.  (Block mode walks the tile's row list.)
+// Next row block of a causal dK/dV workgroup: blocks [base, rb_hi) in chunks of 64.
 __device__ __forceinline__ bool next_row_block(int lane, int rb_hi, uint64_t& mask, int& base, int& rb) {
   while (mask == 0ull) {
     base += 64;
@@ -83,8 +85,15 @@ __device__ __forceinline__ bool next_row_block(int lane, int rb_hi, uint64_t& ma
   return true;
 }
 
+// dK/dV of the full layer (causal).  A workgroup owns 128 keys of one KV head,
+// 32 per wave on v_mfma_f32_32x32x16_bf16, and walks the 32-row query blocks
+// from its first key on, once per head of the group, with Q/dO loads issued
+// two steps ahead over alternating register sets.  Every staged row serves
+// 128 keys here, twice as many as in the 64-key kernel below, which is what
+// the dense causal pass needs (its staging, not its latency, is the larger
+// cost); row splits are absolute ranges of split_rb 32-row blocks.
 template <int MODE, int D>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void bwd_dkdv_causal_kernel(BwdArgs a) {
   constexpr int NC = D / 16;              // 16-wide d chunks of the S and dP contractions
   constexpr int NT = D / 32;              // 32-wide d tiles of dK and dV
   constexpr int RS = D + 8;               // row-major LDS row stride (elements)
@@ -97,7 +106,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_dot[D * TS];
   __shared__ __attribute__((aligned(16))) float s_lse[32];
   __shared__ __attribute__((aligned(16))) float s_dd[32];
-  static_assert(MODE != BW_BLOCK, "the block-sparse branch runs bwd_dkdv_list_kernel");
+  static_assert(MODE == BW_CAUSAL, "the window and block-sparse branches run bwd_dkdv_kernel");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -132,7 +141,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     for (int i = 0; i < 16; ++i) { dk_acc[t][i] = 0.f; dv_acc[t][i] = 0.f; }
 
   int rb_hi = nrb;
-  if (MODE == BW_WINDOW) rb_hi = min(nrb, (k0 + 127 + a.window - 1) / 32 + 1);
   // this workgroup's share of the row blocks that can see the tile: absolute
   // row blocks [split * split_rb, (split + 1) * split_rb)
   const int rb_first = max(k0 / 32, split * a.split_rb);
@@ -227,7 +235,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     fill(set_tag);
 
     bool any = kw0 <= cur_r0 + 31 && kw0 < a.Lk;
-    if (MODE == BW_WINDOW) any = any && kw0 + 31 > cur_r0 - a.window;
     if (any) {
       f32x16 s, dp;
 #pragma unroll
@@ -244,7 +251,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       // per-element test (wave-uniform: away from the diagonal, the window
       // edges, partly selected blocks and the ragged ends).
       bool full = kw0 + 31 <= cur_r0 && cur_r0 + 31 < a.L && kw0 + 31 < a.Lk;
-      if (MODE == BW_WINDOW) full = full && kw0 > cur_r0 + 31 - a.window;
       float p[16], ds[16];
       const int key = kw0 + ln;
       if (full) {
@@ -331,80 +337,95 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     }
 }
 
-// dK/dV of the block-sparse branch.  A workgroup owns one 64-key block of one
-// KV head and walks the list of query rows that selected the block (ascending,
-// built by bwd_rowlist_kernel), 64 list entries per step, once per head of the
-// group (heads fastest).  Wave w holds keys 32(w & 1) .. +31 of the block as B
-// operands, like the causal kernel, and computes rows 32(w >> 1) .. +31 of the
-// step; the two row halves' dK and dV are added through LDS at the end (fixed
-// order).  Every row of a step selected the block, so only causality and the
-// list's end are tested per element.  The list goes through an LDS window, so
-// a step's Q/dO loads, issued one step ahead, take their rows from LDS and
-// never wait on a global index load.  Row splits cut the list into ranges of
-// split_rb * 32 entries, one workgroup each, with the flagged partial sums of
-// the causal kernel's splits.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dkdv_list_kernel(BwdArgs a) {
-  constexpr int NC = D / 16;              // 16-wide d chunks of the S and dP contractions
-  constexpr int NT = D / 32;              // 32-wide d tiles of dK and dV
+// dK/dV, key-stationary.  A workgroup owns one 64-key block of one KV head and
+// walks the query rows that see the block, 32 per step, once per head of the
+// group (heads fastest): in block mode the list of rows that selected the block
+// (ascending, built by bwd_rowlist_kernel), in the causal and window modes the
+// rows from the block's first key on (to the last row whose window reaches it).  Wave w holds keys 16w .. 16w + 15 of the block as B
+// operands of v_mfma_f32_16x16x32_bf16, so K/V fragments and dK/dV take half
+// the registers of the causal kernel's 32-key waves and two workgroups fit on
+// a CU (two waves per SIMD, each hiding the other's LDS, MFMA and barrier
+// latency).  Every row of a block-mode step selected the block, so only
+// causality (and the window) and the rows' end are tested per element.  The
+// list goes through an LDS window, so a step's Q/dO loads, issued one step
+// ahead, take their rows from LDS and never wait on a global index load.  Row
+// splits cut a block's rows into ranges of split_rb * 32, one workgroup each;
+// each writes flagged partial sums that bwd_kv_reduce_kernel adds in split
+// order.
+//
+// 16x16x32 lane layout (lane l, li = l % 16, lg = l / 16): A[m = li][k = 8lg + j],
+// B[k = 8lg + j][n = li], C[m = 4lg + i][n = li].  S = Q K^T and dP = dO V^T
+// come out as C[row][key] in two 16-row blocks, so lane (li, lg) holds key li
+// for rows 4lg + i and 16 + 4lg + i: those eight values are the lane's A
+// fragment of P^T (dV = P^T dO) and dS^T (dK = dS^T Q) with k-slot j standing
+// for row 4lg + j % 4 + 16 (j / 4), and the B operands (dO, Q) are read from
+// the transposed LDS copies in that row order.
+template <int MODE, int D>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NK = D / 32;              // 32-wide k-steps of S and dP
+  constexpr int NDB = D / 16;             // 16-wide d blocks of dK and dV
   constexpr int RS = D + 8;               // row-major LDS row stride (elements)
-  constexpr int TS = 72;                  // transposed LDS row stride: 64 rows + 8
+  constexpr int TS = 36;                  // transposed LDS row stride: 32 rows + 4
   constexpr int CPR = D / 8;              // 16-byte chunks per row
-  constexpr int IPT = 32 * CPR / 256;     // staging items (row pair, chunk) per thread
-  constexpr int NL = 2048;                // list window (entries)
-  constexpr int QB = 64 * RS * 2, TB = D * TS * 2;   // bytes of a row-major and a transposed buffer
-  // the staging buffers, reused at the end for the row halves' dK/dV
-  __shared__ __attribute__((aligned(16))) unsigned char s_buf[2 * QB + 2 * TB];
-  static_assert(2 * QB + 2 * TB >= 2 * NT * 16 * 64 * 2 * 4, "dK/dV exchange fits the staging buffers");
-  uint16_t* s_q = (uint16_t*)s_buf;
-  uint16_t* s_do = (uint16_t*)(s_buf + QB);
-  uint16_t* s_qt = (uint16_t*)(s_buf + 2 * QB);
-  uint16_t* s_dot = (uint16_t*)(s_buf + 2 * QB + TB);
-  __shared__ __attribute__((aligned(16))) float s_lse[64];
-  __shared__ __attribute__((aligned(16))) float s_dd[64];
-  __shared__ __attribute__((aligned(16))) int s_row[64];
+  constexpr int NIT = 16 * CPR;           // staging items: (row pair, chunk)
+  constexpr int NL = MODE == BW_BLOCK ? 2048 : 1;   // list window (entries)
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[32 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t s_do[32 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t s_qt[D * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t s_dot[D * TS];
+  __shared__ __attribute__((aligned(16))) float s_lse[32];
+  __shared__ __attribute__((aligned(16))) float s_dd[32];
+  __shared__ __attribute__((aligned(16))) int s_row[32];
   __shared__ int s_list[NL];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ln = lane & 31, hh = lane >> 5;
-  const int kh = wave & 1, rc = wave >> 1;
-  // blocks slowest within a split, split slowest (as in the causal kernel)
+  const int li = lane & 15, lg = lane >> 4;
+  // blocks slowest within a split, split slowest: the long causal blocks
+  // (small kb) are dispatched first
   const int nbh = a.Hkv * a.B, nkb = (a.Lk + 63) / 64;
   const int split = blockIdx.x / (nkb * nbh), tile = blockIdx.x - split * (nkb * nbh);
   const int kb = tile / nbh, gb = tile - kb * nbh;
   const int g = gb % a.Hkv, b = gb / a.Hkv;
-  const int kw0 = kb * 64 + 32 * kh;
+  const int kw0 = kb * 64 + 16 * wave;
   const int gs = a.ng > 1 ? g : 0;
 
-  // this wave's 32 keys and values as B operands: lane (ln, hh) holds key ln, d = 16c + 8hh + [0, 8)
-  bw_u32x4 kf[NC], vf[NC];
+  // B operands of S (K^T) and dP (V^T): lane (li, lg) holds key kw0 + li, d = 32c + 8lg + [0, 8)
+  bw_u32x4 kf[NK], vf[NK];
   {
-    const int key = kw0 + ln;
+    const int key = kw0 + li;
     const bool ok = key < a.Lk;
-    const int64_t off = (int64_t)b * a.k_sb + (int64_t)(ok ? key : 0) * a.k_st + (int64_t)g * a.k_sh + 8 * hh;
+    const int64_t off = (int64_t)b * a.k_sb + (int64_t)(ok ? key : 0) * a.k_st + (int64_t)g * a.k_sh + 8 * lg;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      kf[c] = ok ? *(const bw_u32x4*)(a.k + off + 16 * c) : zero4();
-      vf[c] = ok ? *(const bw_u32x4*)(a.v + off + 16 * c) : zero4();
+    for (int c = 0; c < NK; ++c) {
+      kf[c] = ok ? *(const bw_u32x4*)(a.k + off + 32 * c) : zero4();
+      vf[c] = ok ? *(const bw_u32x4*)(a.v + off + 32 * c) : zero4();
     }
   }
-  f32x16 dk_acc[NT], dv_acc[NT];
+  f32x4 dk_acc[NDB], dv_acc[NDB];
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { dk_acc[t][i] = 0.f; dv_acc[t][i] = 0.f; }
+  for (int t = 0; t < NDB; ++t) { dk_acc[t] = f32x4{0.f, 0.f, 0.f, 0.f}; dv_acc[t] = f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-  // the block's list and this workgroup's share of it: entries [p_first, p_hi)
-  const int64_t tl = (int64_t)(gs * a.B + b) * nkb + kb;
-  const int32_t* rlist = a.rowlist + tl * a.L;
-  const int rcnt = __builtin_amdgcn_readfirstlane(a.rowcnt[tl]);
+  // the block's rows and this workgroup's share of them: entries [p_first, p_hi)
+  // (causal and window: entry p is row 64kb + p)
+  const int row0 = kb * 64;
+  int rcnt;
+  const int32_t* rlist = nullptr;
+  if constexpr (MODE == BW_BLOCK) {
+    const int64_t tl = (int64_t)(gs * a.B + b) * nkb + kb;
+    rlist = a.rowlist + tl * a.L;
+    rcnt = __builtin_amdgcn_readfirstlane(a.rowcnt[tl]);
+  } else if constexpr (MODE == BW_WINDOW) {
+    rcnt = max(0, min(a.L - row0, 64 + a.window - 1));
+  } else {
+    rcnt = max(0, a.L - row0);
+  }
   const int p_first = split * a.split_rb * 32;
   const int p_hi = min(rcnt, p_first + a.split_rb * 32);
   const bool did = p_first < p_hi;
   int pos = p_first, h = 0;               // the next step to issue
   bool have = did;
-  int win0 = -(NL + 64);                  // no window loaded yet
+  int win0 = -(NL + 32);                  // no window loaded yet
   // list entries [p0, p0 + NL) into s_list; every thread calls it, and no read
   // of the old window is pending (the issue reads it synchronously)
   auto load_window = [&](int p0) __attribute__((always_inline)) {
@@ -417,34 +438,33 @@ __global__ __launch_bounds__(256) void bwd_dkdv_list_kernel(BwdArgs a) {
     win0 = p0;
   };
 
-  // the step in flight: Q and dO of 64 rows (item j of this thread: rows
-  // 2rp, 2rp + 1 of the step, 16-byte chunk ch), LSE and rowsum(dO O) of row
-  // tid (tid < 64), every load issued unconditionally from a clamped address
-  bw_u32x4 pq[IPT][2], pdo[IPT][2];
+  // the step in flight: staging item tid (when tid < NIT) holds rows 2rp,
+  // 2rp + 1 of the step, 16-byte chunk ch; thread tid < 32 the LSE and
+  // rowsum(dO O) of entry tid.  Every load is issued unconditionally from a
+  // clamped address.
+  const int rp = tid & 15, sch = tid >> 4;
+  const bool stager = tid < NIT;
+  bw_u32x4 pq[2], pdo[2];
   float plse = kNegInf, pdd = 0.f;
   int prow = 0;
-  uint32_t pok = 0u;                      // bit 2j + u: staging row u of item j in range; 16: lse row
+  uint32_t pok = 0u;                      // bit u: staging row u in range; 4: lse row
   auto issue = [&](int p0, int hq) __attribute__((always_inline)) {
     const int lw = p0 - win0;             // the step's first entry in the window
+    const int ch = stager ? sch : 0;
     uint32_t okm = 0u;
 #pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-      const int it = tid + 256 * j, rp = it & 31, ch = it >> 5;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bool ok = p0 + 2 * rp + u < p_hi;
-        const int i = s_list[lw + 2 * rp + u];
-        const int ii = ok ? i : 0;
-        okm |= (ok ? 1u : 0u) << (2 * j + u);
-        pq[j][u] = *(const bw_u32x4*)(a.q + (int64_t)b * a.q_sb + (int64_t)ii * a.q_st + (int64_t)hq * a.q_sh + 8 * ch);
-        pdo[j][u] = *(const bw_u32x4*)(a.dO + (int64_t)b * a.do_sb + (int64_t)ii * a.do_st + (int64_t)hq * a.do_sh +
-                                       8 * ch);
-      }
+    for (int u = 0; u < 2; ++u) {
+      const bool ok = stager && p0 + 2 * rp + u < p_hi;
+      const int i = MODE == BW_BLOCK ? s_list[lw + 2 * rp + u] : row0 + p0 + 2 * rp + u;
+      const int ii = ok ? i : 0;
+      okm |= (ok ? 1u : 0u) << u;
+      pq[u] = *(const bw_u32x4*)(a.q + (int64_t)b * a.q_sb + (int64_t)ii * a.q_st + (int64_t)hq * a.q_sh + 8 * ch);
+      pdo[u] = *(const bw_u32x4*)(a.dO + (int64_t)b * a.do_sb + (int64_t)ii * a.do_st + (int64_t)hq * a.do_sh + 8 * ch);
     }
-    if (tid < 64) {
+    if (tid < 32) {
       const bool ok = p0 + tid < p_hi;
-      const int i = s_list[lw + tid];
-      okm |= ok ? 16u : 0u;
+      const int i = MODE == BW_BLOCK ? s_list[lw + tid] : row0 + p0 + tid;
+      okm |= ok ? 4u : 0u;
       prow = ok ? i : a.L;
       const int64_t o = ((int64_t)b * a.Hq + hq) * a.L + (ok ? i : 0);
       plse = a.lse[o];
@@ -454,9 +474,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_list_kernel(BwdArgs a) {
   };
   // issue the next step (loading the window first when the step leaves it)
   auto issue_next = [&]() __attribute__((always_inline)) {
-    if (pos + 64 > win0 + NL) load_window(pos);
+    if constexpr (MODE == BW_BLOCK)
+      if (pos + 32 > win0 + NL) load_window(pos);
     issue(pos, g * a.G + h);
-    if (++h >= a.G) { h = 0; pos += 64; have = pos < p_hi; }
+    if (++h >= a.G) { h = 0; pos += 32; have = pos < p_hi; }
   };
 
   int cur_pos = pos;
@@ -465,24 +486,22 @@ __global__ __launch_bounds__(256) void bwd_dkdv_list_kernel(BwdArgs a) {
     const int step_pos = cur_pos;
     const bool last = !have;
     __syncthreads();                      // the previous step's LDS reads are done
-#pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-      const int it = tid + 256 * j, rp = it & 31, ch = it >> 5;
+    if (stager) {
       bw_u32x4 xq[2], xd[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const bool ok = (pok >> (2 * j + u)) & 1u;
-        xq[u] = ok ? pq[j][u] : zero4();
-        xd[u] = ok ? pdo[j][u] : zero4();
-        *(bw_u32x4*)&s_q[(2 * rp + u) * RS + 8 * ch] = xq[u];
-        *(bw_u32x4*)&s_do[(2 * rp + u) * RS + 8 * ch] = xd[u];
+        const bool ok = (pok >> u) & 1u;
+        xq[u] = ok ? pq[u] : zero4();
+        xd[u] = ok ? pdo[u] : zero4();
+        *(bw_u32x4*)&s_q[(2 * rp + u) * RS + 8 * sch] = xq[u];
+        *(bw_u32x4*)&s_do[(2 * rp + u) * RS + 8 * sch] = xd[u];
       }
-      store_t8x2<TS>(s_qt, rp, ch, xq[0], xq[1]);
-      store_t8x2<TS>(s_dot, rp, ch, xd[0], xd[1]);
+      store_t8x2<TS>(s_qt, rp, sch, xq[0], xq[1]);
+      store_t8x2<TS>(s_dot, rp, sch, xd[0], xd[1]);
     }
-    if (tid < 64) {
-      s_lse[tid] = (pok & 16u) ? plse * kLog2e : kNegInf;
-      s_dd[tid] = (pok & 16u) ? pdd : 0.f;
+    if (tid < 32) {
+      s_lse[tid] = (pok & 4u) ? plse * kLog2e : kNegInf;
+      s_dd[tid] = (pok & 4u) ? pdd : 0.f;
       s_row[tid] = prow;
     }
     __syncthreads();
@@ -490,117 +509,97 @@ __global__ __launch_bounds__(256) void bwd_dkdv_list_kernel(BwdArgs a) {
     cur_pos = pos;
     if (have) issue_next();
 
-    // this wave's rows: entries step_pos + 32rc .. +31, ascending
-    const int nval = min(32, p_hi - (step_pos + 32 * rc));
-    const int r_first = s_row[32 * rc];
-    const int r_last = s_row[32 * rc + max(nval, 1) - 1];
-    const bool any = nval > 0 && kw0 <= r_last && kw0 < a.Lk;
+    // the step's rows: entries step_pos .. step_pos + nval - 1, ascending
+    const int nval = min(32, p_hi - step_pos);
+    const int r_first = s_row[0];
+    const int r_last = s_row[nval - 1];
+    bool any = kw0 <= r_last && kw0 < a.Lk;
+    if (MODE == BW_WINDOW) any = any && r_first - a.window < kw0 + 15;
     if (any) {
-      f32x16 s, dp;
+      f32x4 s[2], dp[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) { s[i] = 0.f; dp[i] = 0.f; }
+      for (int rb = 0; rb < 2; ++rb) {
+        s[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const bw_u32x4 aq = *(const bw_u32x4*)&s_q[(32 * rc + ln) * RS + 16 * c + 8 * hh];
-        const bw_u32x4 ad = *(const bw_u32x4*)&s_do[(32 * rc + ln) * RS + 16 * c + 8 * hh];
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(aq), bwf(kf[c]), s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(ad), bwf(vf[c]), dp, 0, 0, 0);
+        for (int c = 0; c < NK; ++c) {
+          const bw_u32x4 aq = *(const bw_u32x4*)&s_q[(16 * rb + li) * RS + 32 * c + 8 * lg];
+          const bw_u32x4 ad = *(const bw_u32x4*)&s_do[(16 * rb + li) * RS + 32 * c + 8 * lg];
+          s[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bwf(aq), bwf(kf[c]), s[rb], 0, 0, 0);
+          dp[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bwf(ad), bwf(vf[c]), dp[rb], 0, 0, 0);
+        }
       }
-      // element i: row 8(i/4) + 4hh + i%4 of the wave's 32, key kw0 + ln; a
-      // wave whose 32 rows all lie at or past its last key skips the test
-      const bool full = nval == 32 && kw0 + 31 <= r_first && kw0 + 31 < a.Lk;
-      float p[16], ds[16];
-      const int key = kw0 + ln;
+      // element (rb, i): row 16rb + 4lg + i of the step, key kw0 + li; a step
+      // whose 32 rows all lie at or past the wave's last key skips the test
+      bool full = nval == 32 && kw0 + 15 <= r_first && kw0 + 15 < a.Lk;
+      if (MODE == BW_WINDOW) full = full && r_last - a.window < kw0;
+      const int key = kw0 + li;
+      float p[8], ds[8];
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int r0 = 32 * rc + 8 * i4 + 4 * hh;
+      for (int rb = 0; rb < 2; ++rb) {
+        const int r0 = 16 * rb + 4 * lg;
         const f32x4 l4 = *(const f32x4*)&s_lse[r0];
         const f32x4 d4 = *(const f32x4*)&s_dd[r0];
         const int4 q4 = *(const int4*)&s_row[r0];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int i = 4 * i4 + e;
           const int qrow = e == 0 ? q4.x : e == 1 ? q4.y : e == 2 ? q4.z : q4.w;
-          // invalid entries carry row L and LSE -inf
-          const bool vis = full || (qrow < a.L && key <= qrow && key < a.Lk && l4[e] != kNegInf);
-          const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -l4[e])) : 0.f;
-          p[i] = pv;
-          ds[i] = pv * (dp[i] - d4[e]);
+          // entries past the list's end carry row L and LSE -inf
+          bool vis = qrow < a.L && key <= qrow && key < a.Lk && l4[e] != kNegInf;
+          if (MODE == BW_WINDOW) vis = vis && key > qrow - a.window;
+          vis = vis || full;
+          const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(s[rb][e], a.scale_log2, -l4[e])) : 0.f;
+          p[4 * rb + e] = pv;
+          ds[4 * rb + e] = pv * (dp[rb][e] - d4[e]);
         }
       }
-      // A fragments: k-slot 8hh + j of chunk kc is row 16kc + 8(j/4) + 4hh + j%4, i.e. value 8kc + j
-      const bw_u32x4 pa0 = pack8(p), pa1 = pack8(p + 8);
-      const bw_u32x4 da0 = pack8(ds), da1 = pack8(ds + 8);
+      // A fragments of P^T and dS^T: k-slot j is row 4lg + j % 4 + 16 (j / 4)
+      const bw_u32x4 pa = pack8(p), da = pack8(ds);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const uint16_t* td = &s_dot[(32 * t + ln) * TS + 32 * rc + 4 * hh];
-        const uint16_t* tq = &s_qt[(32 * t + ln) * TS + 32 * rc + 4 * hh];
-        const bw_u32x4 bd0 = cat2(*(const bw_u32x2*)(td), *(const bw_u32x2*)(td + 8));
-        const bw_u32x4 bd1 = cat2(*(const bw_u32x2*)(td + 16), *(const bw_u32x2*)(td + 24));
-        const bw_u32x4 bq0 = cat2(*(const bw_u32x2*)(tq), *(const bw_u32x2*)(tq + 8));
-        const bw_u32x4 bq1 = cat2(*(const bw_u32x2*)(tq + 16), *(const bw_u32x2*)(tq + 24));
-        dv_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(pa0), bwf(bd0), dv_acc[t], 0, 0, 0);
-        dv_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(pa1), bwf(bd1), dv_acc[t], 0, 0, 0);
-        dk_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(da0), bwf(bq0), dk_acc[t], 0, 0, 0);
-        dk_acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwf(da1), bwf(bq1), dk_acc[t], 0, 0, 0);
+      for (int t = 0; t < NDB; ++t) {
+        // B fragments: d = 16t + li, rows 4lg .. 4lg + 3 and 16 + 4lg .. 16 + 4lg + 3
+        const uint16_t* td = &s_dot[(16 * t + li) * TS + 4 * lg];
+        const uint16_t* tq = &s_qt[(16 * t + li) * TS + 4 * lg];
+        const bw_u32x4 bd = cat2(*(const bw_u32x2*)(td), *(const bw_u32x2*)(td + 16));
+        const bw_u32x4 bq = cat2(*(const bw_u32x2*)(tq), *(const bw_u32x2*)(tq + 16));
+        dv_acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bwf(pa), bwf(bd), dv_acc[t], 0, 0, 0);
+        dk_acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bwf(da), bwf(bq), dk_acc[t], 0, 0, 0);
       }
     }
     if (last) break;
   }
 
-  // the row halves' sums: waves 2, 3 hand theirs to waves 0, 1 through LDS
-  __syncthreads();                        // every wave is done with the staging buffers
-  float* red = (float*)s_buf;             // [kh][dk, dv][t][i][lane]
-  if (rc == 1) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        red[(((kh * 2 + 0) * NT + t) * 16 + i) * 64 + lane] = dk_acc[t][i];
-        red[(((kh * 2 + 1) * NT + t) * 16 + i) * 64 + lane] = dv_acc[t][i];
-      }
-  }
-  __syncthreads();
-  if (rc == 1) return;
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dk_acc[t][i] += red[(((kh * 2 + 0) * NT + t) * 16 + i) * 64 + lane];
-      dv_acc[t][i] += red[(((kh * 2 + 1) * NT + t) * 16 + i) * 64 + lane];
-    }
-
-  // dK, dV in C layout: lane (ln, hh) holds d = 32t + ln of keys kw0 + 8(i/4) + 4hh + i%4
+  // dK, dV in C layout: lane (li, lg) holds d = 16t + li of keys kw0 + 4lg + i
   if (a.nsplit > 1) {
     if (tid == 0) a.flags[blockIdx.x] = did ? 1 : 0;
     if (!did) return;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NDB; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kw0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+      for (int i = 0; i < 4; ++i) {
+        const int key = kw0 + 4 * lg + i;
         if (key >= a.Lk) continue;
-        const int64_t o = ((((int64_t)split * a.B + b) * a.Lk + key) * a.Hkv + g) * D + 32 * t + ln;
+        const int64_t o = ((((int64_t)split * a.B + b) * a.Lk + key) * a.Hkv + g) * D + 16 * t + li;
         a.part_k[o] = dk_acc[t][i] * a.scale;
         a.part_v[o] = dv_acc[t][i];
       }
     return;
   }
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int t = 0; t < NDB; ++t)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = kw0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+    for (int i = 0; i < 4; ++i) {
+      const int key = kw0 + 4 * lg + i;
       if (key >= a.Lk) continue;
-      const int64_t o = (int64_t)b * a.dk_sb + (int64_t)key * a.dk_st + (int64_t)g * a.dk_sh + 32 * t + ln;
+      const int64_t o = (int64_t)b * a.dk_sb + (int64_t)key * a.dk_st + (int64_t)g * a.dk_sh + 16 * t + li;
       const float kv = dk_acc[t][i] * a.scale, vv = dv_acc[t][i];
       if (a.acc_kv) { a.dk[o] += kv; a.dv[o] += vv; }
       else { a.dk[o] = kv; a.dv[o] = vv; }
     }
 }
 
-// dk, dv (+)= the flagged partial sums of the row splits, in split order; the
-// dK/dV workgroups own tw keys (128 causal and window, 64 block-sparse)
+// dk, dv (+)= the flagged partial sums of the row splits, in split order (one
+// flag per dK/dV workgroup of tw keys: 128 causal, 64 window and block-sparse)
 __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdArgs a, int D, int tw) {
   const int n4 = D / 4;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1055,10 +1054,10 @@ __global__ __launch_bounds__(256) void bwd_rowlist_kernel(const uint32_t* rowbit
 
 template <int MODE, int D>
 hipError_t dkdv_one(const BwdArgs& a, hipStream_t s) {
-  const int tw = MODE == BW_BLOCK ? 64 : 128;
+  const int tw = MODE == BW_CAUSAL ? 128 : 64;
   const int64_t grid = (int64_t)((a.Lk + tw - 1) / tw) * a.Hkv * a.B * a.nsplit;
-  if constexpr (MODE == BW_BLOCK)
-    hipLaunchKernelGGL((bwd_dkdv_list_kernel<D>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  if constexpr (MODE == BW_CAUSAL)
+    hipLaunchKernelGGL((bwd_dkdv_causal_kernel<MODE, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<MODE, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
@@ -1080,8 +1079,8 @@ hipError_t dq_one(const BwdArgs& a, hipStream_t s) {
 }  // namespace
 
 // Rows per split: 64 row blocks (2048 rows) per workgroup, or more to keep at most 16
-// splits.  The window branch's tiles see at most (127 + window) / 32 + 1 row
-// blocks and are never split.
+// splits.  The window branch's 64-key blocks are seen by at most 63 + window
+// rows and are never split.
 int bwd_dkdv_plan(int mode, int L, int window, int* split_rb) {
   const int nrb = (L + 31) / 32;
   int srb = 64;
@@ -1090,8 +1089,9 @@ int bwd_dkdv_plan(int mode, int L, int window, int* split_rb) {
   *split_rb = srb;
   return (nrb + srb - 1) / srb;
 }
-// (splits are absolute row ranges: key tile kt's rows start at row block 4kt,
-// so its first split is the one holding that block and the earlier ones are empty)
+// (causal: absolute row ranges, so a key tile's first split is the one holding
+// its first row block and the earlier ones are empty; window and block-sparse:
+// ranges of a block's rows counted from its first row)
 
 size_t bwd_dkdv_ws_bytes(int nsplit, int B, int Lk, int Hkv, int D) {
   if (nsplit <= 1) return 0;
