@@ -155,7 +155,7 @@ hys_status check_params(const hys_attn_params* p) {
 
 // Launch the top-k kernels; arguments already validated, ws holds topk_workspace_bytes.
 hys_status topk_launch(const float* scores, int64_t rows, int64_t cols, int64_t row_stride, int32_t k, int32_t* idx,
-                       int32_t* count, void* ws, hipStream_t st) {
+                       int32_t* count, void* ws, hipStream_t st, bool hist_zeroed = false) {
   if (rows == 0) return ok();
   if (k == 0 || cols == 0) {
     hipError_t e = hipSuccess;
@@ -168,6 +168,7 @@ hys_status topk_launch(const float* scores, int64_t rows, int64_t cols, int64_t 
   a.idx = idx; a.count = count;
   if (cols > hys::topk_chunk_cols()) {
     a.ws = ws;
+    a.hist_zeroed = hist_zeroed;
     HYS_DCHECK(ws != nullptr && ((uintptr_t)ws & 3) == 0 && hys::topk_workspace_bytes(rows, cols, k) > 0);
   }
   return hip_status(hys::launch_topk(a, st), "top-k launch");
@@ -690,6 +691,11 @@ static hys_status decode_step_impl(const hys_decode_params* p, hys_tensor4 q_ful
       d.ncu = ncu;
     }
     d.scale_log2 = logit_scale * 1.4426950408889634f; d.logit_scale = logit_scale;
+    // the split launch also clears the top-k's row histograms (one launch fewer)
+    const int64_t tk_zero = hys::topk_zero_ints(B, Nmax);
+    HYS_DCHECK(tk_zero * (int64_t)sizeof(int32_t) <= (int64_t)tk);
+    d.zero = tk_zero > 0 ? (int32_t*)tkws : nullptr;
+    d.zero_n = tk_zero;
     // 1. full layer, split over the cache
     d.q[0] = q_full.ptr; d.q_sb = q_full.stride[0]; d.q_sh = q_full.stride[2];
     d.nsplit = nsplit; d.nlayer = 1;
@@ -702,26 +708,27 @@ static hys_status decode_step_impl(const hys_decode_params* p, hys_tensor4 q_ful
     m.scale_log2 = d.scale_log2;
     m.part_o = pf_o; m.part_ml = pf_ml; m.nsplit = nsplit; m.nlayer = 1;
     m.o[0] = o_full.ptr; m.o_sb = o_full.stride[0]; m.o_sh = o_full.stride[2]; m.o_f32 = o_full.dtype == HYS_F32;
-    e = hys::launch_decode_merge((int)D, m, st);
-    if (e != hipSuccess) return hip_status(e, "decode merge launch");
-    // 2. selection over the token scores
-    hys_status ts = topk_launch(token_scores, B, Nmax, Nmax, p->topk, idx, nullptr, tkws, st);
+    // 2. selection over the token scores (the full layer's merge waits for the
+    // sparse layers' and runs in the same launch)
+    hys_status ts = topk_launch(token_scores, B, Nmax, Nmax, p->topk, idx, nullptr, tkws, st, d.zero != nullptr);
     if (ts != HYS_OK) return ts;
+    if (n_sparse == 0) return hip_status(hys::launch_decode_merge((int)D, m, st), "decode merge launch");
     // 3. all sparse layers in one launch
     if (n_sparse > 0) {
       for (int l = 0; l < n_sparse; ++l) d.q[l] = q_sparse[l].ptr;
       d.q_sb = q_sparse[0].stride[0]; d.q_sh = q_sparse[0].stride[2];
       d.nsplit = nsplit_sp; d.nlayer = n_sparse;
-      d.scores = nullptr;
+      d.scores = nullptr; d.zero = nullptr; d.zero_n = 0;
       d.idx = idx; d.idx_sb = p->topk; d.topk = p->topk; d.window = p->window;
       d.part_o = ps_o; d.part_ml = ps_ml;
       e = hys::launch_decode(1, et(k_cache.dtype), (int)D, d, st);
       if (e != hipSuccess) return hip_status(e, "decode sparse launch");
-      m.part_o = ps_o; m.part_ml = ps_ml; m.nsplit = nsplit_sp; m.nlayer = n_sparse;
-      for (int l = 0; l < n_sparse; ++l) { m.o[l] = o_sparse[l].ptr; m.lse[l] = nullptr; }
-      m.o_sb = o_sparse[0].stride[0]; m.o_sh = o_sparse[0].stride[2]; m.o_f32 = o_sparse[0].dtype == HYS_F32;
-      e = hys::launch_decode_merge((int)D, m, st);
-      if (e != hipSuccess) return hip_status(e, "decode sparse merge launch");
+      hys::MergeArgs ms = m;
+      ms.part_o = ps_o; ms.part_ml = ps_ml; ms.nsplit = nsplit_sp; ms.nlayer = n_sparse;
+      for (int l = 0; l < n_sparse; ++l) { ms.o[l] = o_sparse[l].ptr; ms.lse[l] = nullptr; }
+      ms.o_sb = o_sparse[0].stride[0]; ms.o_sh = o_sparse[0].stride[2]; ms.o_f32 = o_sparse[0].dtype == HYS_F32;
+      e = hys::launch_decode_merge2((int)D, m, ms, st);
+      if (e != hipSuccess) return hip_status(e, "decode merge launch");
     }
     return ok();
   } catch (...) {

@@ -435,12 +435,11 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
 // loads of many partials are in flight together), and the NG group sums are
 // added in group order in LDS, so the result does not depend on scheduling.
 template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(const MergeArgs a) {
+__device__ __forceinline__ void decode_merge_one(const MergeArgs& a, int bid) {
   constexpr int NQ = D / 4;          // float4 column groups
   constexpr int NG = 256 / NQ;       // split groups
   __shared__ float sl[NG], smax[4];
   __shared__ float4 so[NG][NQ];
-  const int bid = blockIdx.x;
   const int h = bid % a.Hq;
   const int b = (bid / a.Hq) % a.B;
   const int layer = bid / (a.Hq * a.B);
@@ -497,8 +496,26 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const MergeArgs a) {
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge_kernel(const MergeArgs a) {
+  decode_merge_one<D>(a, blockIdx.x);
+}
+
+// two merges in one launch (the full layer's and the sparse layers')
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge2_kernel(const MergeArgs a, const MergeArgs b) {
+  const int na = a.nlayer * a.B * a.Hq;
+  if ((int)blockIdx.x < na) decode_merge_one<D>(a, blockIdx.x);
+  else decode_merge_one<D>(b, blockIdx.x - na);
+}
+
 hipError_t launch_decode(int sparse, int kt, int D, const DecArgs& a, hipStream_t s) {
   if (!sparse && kt == ET_FP8 && decode_split_fp8_supported(D, a)) return launch_decode_split_fp8(a, s);
+  // (the split kernel clears a.zero itself; the other paths clear it first)
+  if (!sparse && a.zero) {
+    hipError_t e = launch_fill_i32(a.zero, 0, a.zero_n, s);
+    if (e != hipSuccess) return e;
+  }
   const unsigned grid = (unsigned)(a.nlayer * a.B * a.nsplit);
 #define HYS_DEC(SP, KT, DD) hipLaunchKernelGGL((decode_kernel<SP, KT, DD>), dim3(grid), dim3(256), 0, s, a)
   if (kt == ET_FP8) {
@@ -513,6 +530,14 @@ hipError_t launch_decode(int sparse, int kt, int D, const DecArgs& a, hipStream_
     return hipErrorInvalidValue;
   }
 #undef HYS_DEC
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge2(int D, const MergeArgs& a, const MergeArgs& b, hipStream_t s) {
+  const unsigned grid = (unsigned)(a.nlayer * a.B * a.Hq + b.nlayer * b.B * b.Hq);
+  if (D == 128) hipLaunchKernelGGL(decode_merge2_kernel<128>, dim3(grid), dim3(256), 0, s, a, b);
+  else if (D == 64) hipLaunchKernelGGL(decode_merge2_kernel<64>, dim3(grid), dim3(256), 0, s, a, b);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

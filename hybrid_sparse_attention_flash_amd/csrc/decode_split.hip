@@ -169,6 +169,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_fp8_kernel(const DecArgs 
   const int ntiles = (n + 63) / 64;
   const int per = (ntiles + a.nsplit - 1) / a.nsplit;
   const int t0 = s * per, t1 = min(ntiles, t0 + per);
+  // the ints a later launch of the step needs cleared (the top-k's histograms)
+  if (bid == 0 && a.zero)
+    for (int64_t i = tid; i < a.zero_n; i += 256) a.zero[i] = 0;
 
   // ---- tile loads: instruction u of wave w fills rows 16w + 8u + (0..7), lane
   // L the row's chunk slot L%8 with source chunk (L%8) ^ swz(row) ----------

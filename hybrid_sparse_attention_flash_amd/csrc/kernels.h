@@ -79,12 +79,16 @@ struct TopkArgs {
   int k;
   int32_t* idx; int32_t* count;
   // long rows (cols > topk_chunk_cols()): topk_workspace_bytes of 4-byte
-  // aligned workspace for the row histograms, selection state and chunk counts
+  // aligned workspace for the row histograms, selection state and chunk counts;
+  // hist_zeroed: its first topk_zero_ints ints are already 0 (else cleared here)
   void* ws;
+  bool hist_zeroed;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 // workspace of launch_topk for [rows, cols] and k; 0 when cols <= topk_chunk_cols()
 size_t topk_workspace_bytes(int64_t rows, int64_t cols, int k);
+// ints at the start of that workspace that must be 0 when the selection starts
+int64_t topk_zero_ints(int64_t rows, int64_t cols);
 // largest grid (workgroups) launch_topk uses
 int64_t topk_max_workgroups(int64_t rows, int64_t cols, int k);
 int64_t topk_chunk_cols();
@@ -112,6 +116,7 @@ struct DecArgs {
   float* scores; int64_t sc_sb;                          // full mode: [B, Nmax] token scores
   const int32_t* idx; int64_t idx_sb; int topk; int window;   // sparse mode: [B, topk]
   float* part_o; float* part_ml;                         // [(layer*B + b)*nsplit + s][Hq][D], [..][Hq][2]
+  int32_t* zero; int64_t zero_n;                         // full mode: ints cleared for a later launch (or null)
 };
 
 struct MergeArgs {
@@ -124,6 +129,8 @@ struct MergeArgs {
 
 hipError_t launch_decode(int sparse, int kt, int D, const DecArgs& a, hipStream_t s);
 hipError_t launch_decode_merge(int D, const MergeArgs& a, hipStream_t s);
+// two merges in one launch: the workgroups of a, then those of b
+hipError_t launch_decode_merge2(int D, const MergeArgs& a, const MergeArgs& b, hipStream_t s);
 
 // HySparse (block-level) decode: block scores from the full layer's per-KV-head
 // token scores, and every sparse layer (block gather, ring window, gate).

@@ -625,6 +625,8 @@ int64_t topk_max_workgroups(int64_t rows, int64_t cols, int k) {
 
 int64_t topk_chunk_cols() { return kTopkChunk; }
 
+int64_t topk_zero_ints(int64_t rows, int64_t cols) { return cols <= kTopkChunk ? 0 : rows * kGridHist; }
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   if (a.cols <= 2048 && a.k <= 2048) {
@@ -651,8 +653,10 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   ga.state = w + a.rows * kGridHist;
   ga.counts = ga.state + a.rows * kGridState;
   ga.idx = a.idx; ga.count = a.count;
-  hipError_t e = launch_fill_i32(ga.hist, 0, a.rows * kGridHist, s);
-  if (e != hipSuccess) return e;
+  if (!a.hist_zeroed) {
+    hipError_t e = launch_fill_i32(ga.hist, 0, a.rows * kGridHist, s);
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid((unsigned)(a.rows * g.nchunk)), block(kGridThreads);
   hipLaunchKernelGGL(topk_grid_hist_kernel<0>, grid, block, 0, s, ga);
   hipLaunchKernelGGL(topk_grid_hist_kernel<1>, grid, block, 0, s, ga);
