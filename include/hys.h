@@ -233,7 +233,7 @@ HYS_API hys_status hys_select_topk(const float* scores, int64_t rows, int64_t co
  *   blocks' token positions [64c, min(cols, 64c+64)) in ascending block
  *   order, then -1.  The rows can feed hys_sparse_attn_fwd with granularity 1.
  * block must be 64; 1 <= k_blocks <= 32.  Workspace: the block maxima, the
- * block ids and top-k candidates (query with ws == NULL).
+ * block ids and the top-k workspace (query with ws == NULL).
  */
 HYS_API hys_status hys_select_topk_blocks(const float* scores, int64_t rows, int64_t cols, int64_t row_stride,
                                           int32_t block, int32_t k_blocks, int32_t* idx, void* ws, size_t* ws_bytes,
@@ -335,7 +335,7 @@ HYS_API hys_status hys_sparse_layer_fwd(const hys_attn_params* p, hys_tensor4 q,
  * o_full, o_sparse[l]: [B, 1, Hq, D] fp32 or bf16 (all of one type).
  * token_scores: [B, Nmax] fp32 (required).  idx: [B, topk] int32.
  * Limits: Hq <= 64, B <= 64, n_sparse <= 16, topk <= 2048.
- * Workspace: split partials, top-k candidates (query with ws == NULL).
+ * Workspace: split partials, the top-k's row histograms and counts (query with ws == NULL).
  */
 HYS_API hys_status hys_decode_step(const hys_decode_params* p, hys_tensor4 q_full, hys_tensor4 k_cache,
                            hys_tensor4 v_cache, const int64_t* cache_len, hys_tensor4 o_full, float* token_scores,
@@ -407,7 +407,7 @@ typedef struct {
  * is W = k_ring[0].shape[1].
  * Limits: Hq = Hkv*G with G in {1, 2, 4, 8, 16}, B <= 64, n_sparse <= 16,
  * topk <= 64.
- * Workspace: per-KV-head token scores and split partials, top-k candidates
+ * Workspace: per-KV-head token scores and split partials, the top-k workspace
  * (query with ws == NULL).
  */
 HYS_API hys_status hys_hysparse_decode_step(const hys_hs_decode_params* p, hys_tensor4 q_full, hys_tensor4 k_cache,
