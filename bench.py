@@ -46,16 +46,16 @@ METRIC = ("hybrid-block prefill tokens/s at 32k (TFLOP/s, GB/s % peak); decode u
 # summaries).  It is reported only while the kernel sources still hash to the
 # value they had when the counters were taken.
 TRAFFIC_SOURCES = ("sparse_layer.hip", "block_union.h", "common.h", "kernels.h")
-TRAFFIC = {"sources_sha1": "7325193e8c1fabd3252ac1f5d74e45d1221eb5ba", "bytes_per_launch": 1.4818e9}
+TRAFFIC = {"sources_sha1": "290adca7bbea8e9cd87f76e4cf211a8a0c925759", "bytes_per_launch": 1.4818e9}
 # The same two passes for the KV Bridging kernel, over
 #   python3 bench.py --only-bridge --calibrate-copy --steps 1 --warmup 0
 BRIDGE_TRAFFIC_SOURCES = ("bridge.hip", "common.h", "kernels.h")
-BRIDGE_TRAFFIC = {"sources_sha1": "ccc0d9a0d6f034cb763cccccb43755552dccc2f6", "bytes_per_launch": 575.8e6}
+BRIDGE_TRAFFIC = {"sources_sha1": "d353b349e2748a558fb7ad15af6be4f89ae8900a", "bytes_per_launch": 575.8e6}
 # The same two passes for the decode step (every kernel of one hys_decode_step
 # call, summed per step), over
 #   python3 bench.py --only-decode --no-peaks --calibrate-copy --steps 2 --warmup 1
 DECODE_TRAFFIC_SOURCES = ("decode.hip", "decode_split.hip", "decode_split.h", "topk.hip", "common.h", "kernels.h", "abi.hip")
-DECODE_TRAFFIC = {"sources_sha1": "8a2fc1a576531914bde7c3c739b09c62d7a57497", "bytes_per_step": 1.2456e9}
+DECODE_TRAFFIC = {"sources_sha1": "8a14bb9a6f7884d655b986e63fc4585a18b586a1", "bytes_per_step": 1.2456e9}
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
