@@ -942,20 +942,23 @@ hys_status hys_hysparse_decode_step(const hys_hs_decode_params* p, hys_tensor4 q
     hipStream_t st = (hipStream_t)stream;
     const float logit_scale = p->softmax_scale;
     const size_t oes = o_full.dtype == HYS_F32 ? 4 : 2;
-    for (int64_t g = 0; g < Hkv; ++g) {
-      float* po = po_all + (size_t)(g * B * nsplit * G) * D;
-      float* pml = pml_all + (size_t)(g * B * nsplit * G) * 2;
+    // the KV heads as the "layers" of one split launch (up to kMaxDecodeLayers at a time)
+    for (int64_t g0 = 0; g0 < Hkv; g0 += hys::kMaxDecodeLayers) {
+      const int nl = (int)std::min<int64_t>(hys::kMaxDecodeLayers, Hkv - g0);
       hys::DecArgs d{};
-      d.q[0] = (const uint16_t*)q_full.ptr + g * G * q_full.stride[2];
+      for (int l = 0; l < nl; ++l) d.q[l] = (const uint16_t*)q_full.ptr + (g0 + l) * G * q_full.stride[2];
       d.q_sb = q_full.stride[0]; d.q_sh = q_full.stride[2];
-      d.k = (const uint16_t*)k_cache.ptr + g * k_cache.stride[2]; d.k_sb = k_cache.stride[0]; d.k_st = k_cache.stride[1];
-      d.v = (const uint16_t*)v_cache.ptr + g * v_cache.stride[2]; d.v_sb = v_cache.stride[0]; d.v_st = v_cache.stride[1];
+      d.k = (const uint16_t*)k_cache.ptr + g0 * k_cache.stride[2]; d.k_sb = k_cache.stride[0]; d.k_st = k_cache.stride[1];
+      d.v = (const uint16_t*)v_cache.ptr + g0 * v_cache.stride[2]; d.v_sb = v_cache.stride[0]; d.v_st = v_cache.stride[1];
+      d.k_sl = k_cache.stride[2]; d.v_sl = v_cache.stride[2]; d.sc_sl = B * Nmax;
       for (int64_t b = 0; b < B; ++b) d.lens[b] = (int)cache_len[b];
       d.B = (int)B; d.Hq = (int)G; d.Nmax = (int)Nmax; d.ncu = ncu;
       d.scale_log2 = logit_scale * 1.4426950408889634f; d.logit_scale = logit_scale;
-      d.nsplit = nsplit; d.nlayer = 1;
-      d.scores = ts + (size_t)g * B * Nmax; d.sc_sb = Nmax;
-      d.part_o = po; d.part_ml = pml;
+      d.nsplit = nsplit; d.nlayer = nl;
+      d.scores = ts + (size_t)g0 * B * Nmax; d.sc_sb = Nmax;
+      d.part_o = po_all + (size_t)(g0 * B * nsplit * G) * D;
+      d.part_ml = pml_all + (size_t)(g0 * B * nsplit * G) * 2;
+      HYS_DCHECK((int64_t)nl * B * nsplit < ((int64_t)1 << 31));
       hipError_t e = hys::launch_decode(0, hys::ET_BF16, (int)D, d, st);
       if (e != hipSuccess) return hip_status(e, "decode split launch");
     }

@@ -103,6 +103,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
   const int b = rest % a.B;
   const int layer = rest / a.B;
   const int n = a.lens[b];
+  // full mode: layer l is the cache's KV head l (offsets 0 for one layer)
+  float* const scr = SPARSE ? nullptr : a.scores + (int64_t)layer * a.sc_sl;
 
   // ---- key list ------------------------------------------------------------
   int npre = 0, wstart = 0, nkeys = 0;
@@ -143,8 +145,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
   // ---- staging (roles 2, 3) ----------------------------------------------------
   // staging thread x, K or V unit u: key u*(NST/(D/8)) + x/(D/8), 8 elements
   // from x%(D/8)*8
-  const KT* kb = (const KT*)a.k + (int64_t)b * a.k_sb;
-  const KT* vb = (const KT*)a.v + (int64_t)b * a.v_sb;
+  const KT* kb = (const KT*)a.k + (int64_t)b * a.k_sb + (SPARSE ? 0 : (int64_t)layer * a.k_sl);
+  const KT* vb = (const KT*)a.v + (int64_t)b * a.v_sb + (SPARSE ? 0 : (int64_t)layer * a.v_sl);
   Raw8<KT> kreg[NSET][KU];
   Raw8<KT> vreg[NSET][VU];
   uint32_t kmask[NSET], vmask[NSET];
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
     if (!SPARSE && vw == 0) {
       const int j = t * 64 + lane;
       const float v = fmaxf(red[t & 1][0][lane], red[t & 1][1][lane]);
-      if (j < a.Nmax) a.scores[(int64_t)b * a.sc_sb + j] = (j < n) ? v * a.logit_scale : kNegInf;
+      if (j < a.Nmax) scr[(int64_t)b * a.sc_sb + j] = (j < n) ? v * a.logit_scale : kNegInf;
     }
   };
 
@@ -407,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(const DecArgs a) {
   // keys past the valid length: token scores are -inf (the workgroups of the
   // last split cover the tail of the score row)
   if (!SPARSE && s == a.nsplit - 1) {
-    for (int j = ntiles * 64 + tid; j < a.Nmax; j += 256) a.scores[(int64_t)b * a.sc_sb + j] = kNegInf;
+    for (int j = ntiles * 64 + tid; j < a.Nmax; j += 256) scr[(int64_t)b * a.sc_sb + j] = kNegInf;
   }
 
   // ---- this wave's partial (m, l, unnormalised O) ------------------------------

@@ -502,7 +502,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_fp8_kernel(const DecArgs 
 
 bool decode_split_fp8_supported(int D, const DecArgs& a) {
   const uintptr_t kp = (uintptr_t)a.k, vp = (uintptr_t)a.v;
-  return D == kDsD && (kp % 16) == 0 && (vp % 16) == 0 && a.k_sb % 16 == 0 && a.v_sb % 16 == 0 &&
+  return D == kDsD && a.nlayer == 1 && a.k_sl == 0 && a.v_sl == 0 && a.sc_sl == 0 && (kp % 16) == 0 && (vp % 16) == 0 && a.k_sb % 16 == 0 && a.v_sb % 16 == 0 &&
          a.k_st % 16 == 0 && a.v_st % 16 == 0 && a.k_st >= kDsD && a.v_st >= kDsD &&
          64 * a.k_st < ((int64_t)1 << 32) && 64 * a.v_st < ((int64_t)1 << 32);
 }

@@ -117,6 +117,9 @@ struct DecArgs {
   const int32_t* idx; int64_t idx_sb; int topk; int window;   // sparse mode: [B, topk]
   float* part_o; float* part_ml;                         // [(layer*B + b)*nsplit + s][Hq][D], [..][Hq][2]
   int32_t* zero; int64_t zero_n;                         // full mode: ints cleared for a later launch (or null)
+  // full mode with nlayer > 1 (one "layer" per KV head of a GQA cache): element
+  // offsets of layer l's K, V and score rows (0 for a single layer)
+  int64_t k_sl, v_sl, sc_sl;
 };
 
 struct MergeArgs {
