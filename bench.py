@@ -46,16 +46,21 @@ METRIC = ("hybrid-block prefill tokens/s at 32k (TFLOP/s, GB/s % peak); decode u
 # summaries).  It is reported only while the kernel sources still hash to the
 # value they had when the counters were taken.
 TRAFFIC_SOURCES = ("sparse_layer.hip", "block_union.h", "common.h", "kernels.h")
-TRAFFIC = {"sources_sha1": "290adca7bbea8e9cd87f76e4cf211a8a0c925759", "bytes_per_launch": 1.4818e9}
+TRAFFIC = {"sources_sha1": "1ad9e7ea641020f1db3c8cd14695a14ce84b82ab", "bytes_per_launch": 1.4688e9}
 # The same two passes for the KV Bridging kernel, over
 #   python3 bench.py --only-bridge --calibrate-copy --steps 1 --warmup 0
 BRIDGE_TRAFFIC_SOURCES = ("bridge.hip", "common.h", "kernels.h")
-BRIDGE_TRAFFIC = {"sources_sha1": "d353b349e2748a558fb7ad15af6be4f89ae8900a", "bytes_per_launch": 575.8e6}
+BRIDGE_TRAFFIC = {"sources_sha1": "6d6eba6b5f5e733c97373c3b33f4b1f406e1e599", "bytes_per_launch": 575.8e6}
 # The same two passes for the decode step (every kernel of one hys_decode_step
 # call, summed per step), over
 #   python3 bench.py --only-decode --no-peaks --calibrate-copy --steps 2 --warmup 1
 DECODE_TRAFFIC_SOURCES = ("decode.hip", "decode_split.hip", "decode_split.h", "topk.hip", "common.h", "kernels.h", "abi.hip")
-DECODE_TRAFFIC = {"sources_sha1": "8a14bb9a6f7884d655b986e63fc4585a18b586a1", "bytes_per_step": 1.2456e9}
+DECODE_TRAFFIC = {"sources_sha1": "66a5c7b9544150ee0b1db9e67897b352217c9420", "bytes_per_step": 1.2456e9}
+# The same two passes for the HySparse decode step at 128k (every kernel of one
+# hys_hysparse_decode_step call, summed per step), over
+#   python3 bench.py --only-hs-decode --calibrate-copy --steps 2 --warmup 1 --no-cpu
+HS_DECODE_TRAFFIC_SOURCES = ("hs_decode.hip", "decode.hip", "topk.hip", "common.h", "kernels.h", "abi.hip")
+HS_DECODE_TRAFFIC = {"sources_sha1": "1f81ea66ecd6a09580262f823fc28ca4a4e94515", "bytes_per_step": 1.1398e9}
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
@@ -574,7 +579,9 @@ def bench_hs_decode(args, dev):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "work_per_step": f"{kv_bytes + gathered:.4g} B (full-layer K+V, gathered blocks + windows)",
-                         "traffic": None}}
+                         "traffic": HS_DECODE_TRAFFIC["bytes_per_step"]
+                         if HS_DECODE_TRAFFIC["sources_sha1"] == kernel_sources_sha1(HS_DECODE_TRAFFIC_SOURCES)
+                         else None}}
 
 
 def bench_bridge(args, dev):
