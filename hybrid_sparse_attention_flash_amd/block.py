@@ -214,9 +214,20 @@ class HySparse2Decode:
         self.idx = torch.empty(B, topk, dtype=torch.int32, device=device)
         self.o_layers = [torch.empty(B, 1, Hq, D, dtype=out_dtype, device=device) for _ in range(n_sparse)]
         self.ws = None
+        self._call = None          # (key, marshalled arguments) of the last call
 
     def run(self, q_full, k_cache, v_cache, cache_len, q_sparse, k_scale=1.0, v_scale=1.0):
-        self.ws = ops.hys_decode_step(q_full, k_cache, v_cache, cache_len, self.o_full, self.scores, self.idx,
-                                      q_sparse, self.o_layers, self.topk, self.window, softmax_scale=self.scale,
-                                      k_scale=k_scale, v_scale=v_scale, workspace=self.ws)
+        # the arguments are marshalled again only when an input tensor, a
+        # length, a scale or the current stream changed since the last call
+        key = (tuple((t.data_ptr(), tuple(t.shape), tuple(t.stride()), t.dtype) for t in (q_full, k_cache, v_cache)),
+               tuple(int(x) for x in cache_len),
+               tuple((t.data_ptr(), tuple(t.shape), tuple(t.stride()), t.dtype) for t in q_sparse),
+               float(k_scale), float(v_scale), torch.cuda.current_stream(q_full.device).cuda_stream)
+        if self._call is None or self._call[0] != key:
+            args, self.ws, keep = ops.hys_decode_step_args(q_full, k_cache, v_cache, cache_len, self.o_full,
+                                                           self.scores, self.idx, q_sparse, self.o_layers, self.topk,
+                                                           self.window, softmax_scale=self.scale, k_scale=k_scale,
+                                                           v_scale=v_scale, workspace=self.ws)
+            self._call = (key, args, keep)
+        ops.check(ops._lib.load().hys_decode_step(*self._call[1]))
         return self

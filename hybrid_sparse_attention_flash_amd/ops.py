@@ -130,11 +130,14 @@ def hys_sparse_layer_fwd(q, k, v, idx, k_win, v_win, window: int, gate_w, o, gat
                                    _stream(q.device)))
 
 
-def hys_decode_step(q_full, k_cache, v_cache, cache_len: Sequence[int], o_full, token_scores, idx,
-                    q_sparse: Sequence[torch.Tensor], o_sparse: Sequence[torch.Tensor], topk: int, window: int,
-                    softmax_scale: float = None, k_scale: float = 1.0, v_scale: float = 1.0,
-                    workspace: Optional[torch.Tensor] = None):
-    """Returns the workspace tensor so callers can reuse it across steps."""
+def hys_decode_step_args(q_full, k_cache, v_cache, cache_len: Sequence[int], o_full, token_scores, idx,
+                         q_sparse: Sequence[torch.Tensor], o_sparse: Sequence[torch.Tensor], topk: int, window: int,
+                         softmax_scale: float = None, k_scale: float = 1.0, v_scale: float = 1.0,
+                         workspace: Optional[torch.Tensor] = None):
+    """The marshalled arguments of one hys_decode_step call and the workspace
+    they use (allocated here when `workspace` is missing or too small): the
+    call is lib.hys_decode_step(*args).  The ctypes objects the tuple refers
+    to live as long as the tuple."""
     lib = _lib.load()
     p = HysDecodeParams(softmax_scale or 1.0 / math.sqrt(q_full.shape[-1]), k_scale, v_scale, topk, window)
     lens = (ctypes.c_int64 * len(cache_len))(*[int(x) for x in cache_len])
@@ -148,7 +151,18 @@ def hys_decode_step(q_full, k_cache, v_cache, cache_len: Sequence[int], o_full, 
     if workspace is None or workspace.numel() < nb.value:
         workspace = _workspace(nb.value, q_full.device)
     nb2 = ctypes.c_size_t(workspace.numel())
-    check(lib.hys_decode_step(*args, _ptr(workspace), ctypes.byref(nb2), _stream(q_full.device)))
+    return tuple(args) + (_ptr(workspace), ctypes.byref(nb2), _stream(q_full.device)), workspace, (p, lens, qs, os_, nb2)
+
+
+def hys_decode_step(q_full, k_cache, v_cache, cache_len: Sequence[int], o_full, token_scores, idx,
+                    q_sparse: Sequence[torch.Tensor], o_sparse: Sequence[torch.Tensor], topk: int, window: int,
+                    softmax_scale: float = None, k_scale: float = 1.0, v_scale: float = 1.0,
+                    workspace: Optional[torch.Tensor] = None):
+    """Returns the workspace tensor so callers can reuse it across steps."""
+    args, workspace, _keep = hys_decode_step_args(q_full, k_cache, v_cache, cache_len, o_full, token_scores, idx,
+                                                  q_sparse, o_sparse, topk, window, softmax_scale, k_scale, v_scale,
+                                                  workspace)
+    check(_lib.load().hys_decode_step(*args))
     return workspace
 
 
